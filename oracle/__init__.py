@@ -1,0 +1,171 @@
+"""fp64 CPU oracle for exact softmax attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  It shares no code with the GPU library
+(``exact_attention_108_amd``) and neither imports the other.
+
+* ``attn_oracle.c``  -- the plain definition (scores and probabilities
+  materialised per row, fp64), built into ``liboracle.so`` with gcc + OpenMP.
+* ``blockwise.py``   -- an independent numpy fp64 re-statement of the
+  two-state online-softmax merge, used only to pin the C oracle.
+
+Every function follows page "Attention Kernel" (sections "问题与成本",
+"Online softmax", "Paged 与 ragged KV") and page "Attention 算子加速史"
+(section 1.1 for the materialised S and P, 1.2 for the safe softmax).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "attn_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+_DT = {"f32": 0, "bf16": 1}
+
+
+def build(src: str = SRC, out: str = LIB, werror: bool = True) -> str:
+    """Compile the C oracle with gcc (-O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-fno-fast-math", src, "-o", out + ".tmp", "-lm"] + (["-Werror"] if werror else [])
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes view of one build of ``attn_oracle.c``."""
+
+    def __init__(self, lib_path: str = LIB):
+        if not os.path.exists(lib_path):
+            build(out=lib_path)
+        self.lib = ctypes.CDLL(lib_path)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        self.lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                             vp, vp, vp, i64, vp, vp]
+        self.lib.oracle_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32,
+                                                    i32, vp, vp, vp, i64, vp, vp]
+        self.lib.oracle_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                 i32, f32, vp, i64, vp, vp]
+        for f in (self.lib.oracle_attn_fwd, self.lib.oracle_attn_fwd_varlen, self.lib.oracle_decode_paged):
+            f.restype = ctypes.c_int
+        self.lib.oracle_num_threads.restype = ctypes.c_int
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    @staticmethod
+    def _arr(x, dtype):
+        if dtype == "bf16":
+            return np.ascontiguousarray(x, dtype=np.uint16)
+        if dtype == "f32":
+            return np.ascontiguousarray(x, dtype=np.float32)
+        raise ValueError(f"unknown dtype {dtype!r}")
+
+    @staticmethod
+    def _rows(rows):
+        if rows is None:
+            return None, 0
+        r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        return r, r.size
+
+    def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, rows=None):
+        """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d].
+
+        Returns (o, lse): o [B,A,S_q,d] / lse [B,A,S_q] in fp64, or [n,d] / [n]
+        for the flattened row ids ``rows`` = (b*A + h)*S_q + i.
+        """
+        q, k, v = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype)
+        if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+            raise ValueError("q, k, v must be 4-D [B, heads, S, d]")
+        B, A, S_q, d = q.shape
+        if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+            raise ValueError("k and v must be [B, A_kv, S_k, d] matching q")
+        A_kv, S_k = k.shape[1], k.shape[2]
+        if A % A_kv:
+            raise ValueError("A must be a multiple of A_kv")
+        qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
+        kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
+        r, n = self._rows(rows)
+        n_out = B * A * S_q if r is None else n
+        o = np.empty((n_out, d), dtype=np.float64)
+        lse = np.empty(n_out, dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, A, A_kv, S_q, S_k, d,
+                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(r), n,
+                                      _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise ValueError("oracle_attn_fwd rejected its arguments")
+        if r is None:
+            return o.reshape(B, A, S_q, d), lse.reshape(B, A, S_q)
+        return o, lse
+
+    def attn_fwd_varlen(self, q, k, v, cu_seqlens, *, dtype, scale, causal=True, q_keep=None,
+                        k_keep=None, rows=None):
+        """Packed varlen attention.  q [A,T,d], k/v [A_kv,T,d]; rows = h*T + t."""
+        q, k, v = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype)
+        if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape != v.shape:
+            raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
+        A, T, d = q.shape
+        A_kv = k.shape[0]
+        if k.shape[1] != T or k.shape[2] != d or A % A_kv:
+            raise ValueError("k/v must be [A_kv, T, d] with A % A_kv == 0")
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        n_seq = cu.size - 1
+        qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(T)
+        kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(T)
+        r, n = self._rows(rows)
+        n_out = A * T if r is None else n
+        o = np.empty((n_out, d), dtype=np.float64)
+        lse = np.empty(n_out, dtype=np.float64)
+        rc = self.lib.oracle_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], _ptr(cu), n_seq, T, A,
+                                             A_kv, d, float(scale), int(bool(causal)), _ptr(qk), _ptr(kk),
+                                             _ptr(r), n, _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise ValueError("oracle_attn_fwd_varlen rejected its arguments")
+        if r is None:
+            return o.reshape(A, T, d), lse.reshape(A, T)
+        return o, lse
+
+    def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None):
+        """Paged decode.  q [B,A,d]; caches [P, page_size, A_kv, d]; rows = b*A + h."""
+        q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
+        if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
+            raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
+        B, A, d = q.shape
+        num_pages, page_size, A_kv, dk = kc.shape
+        if dk != d or A % A_kv:
+            raise ValueError("cache head dim / head count mismatch")
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        if bt.ndim != 2 or bt.shape[0] != B or sl.shape != (B,):
+            raise ValueError("block_table [B, max_pages], seq_lens [B]")
+        r, n = self._rows(rows)
+        n_out = B * A if r is None else n
+        o = np.empty((n_out, d), dtype=np.float64)
+        lse = np.empty(n_out, dtype=np.float64)
+        rc = self.lib.oracle_decode_paged(_ptr(q), _ptr(kc), _ptr(vc), _DT[dtype], _ptr(bt), _ptr(sl), B, A,
+                                          A_kv, d, page_size, bt.shape[1], num_pages, float(scale), _ptr(r), n,
+                                          _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise ValueError("oracle_decode_paged rejected its arguments")
+        if r is None:
+            return o.reshape(B, A, d), lse.reshape(B, A)
+        return o, lse
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,345 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU reference for exact softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg load this library.  It shares no code with the GPU library.
+ *
+ * What it computes (page "Attention Kernel", section "问题与成本", the
+ * definition P = softmax(QK^T/sqrt(d_h) + M), O = PV):
+ *
+ *   s_ij  = scale * sum_e q_ie k_je  (+ M_ij, M_ij in {0, -inf})
+ *   m_i   = max_j s_ij
+ *   l_i   = sum_j exp(s_ij - m_i)                 (safe softmax, page
+ *                                                  "Attention 算子加速史", 1.2)
+ *   P_ij  = exp(s_ij - m_i) / l_i
+ *   O_i   = sum_j P_ij v_j
+ *   LSE_i = m_i + ln l_i                          (natural log)
+ *
+ * Every row's score vector S_i and probability vector P_i are materialised in
+ * full, exactly as the standard (non-fused) attention does (page
+ * "Attention 算子加速史", 1.1, steps 1-3).  Arithmetic is fp64 throughout; the
+ * inputs (fp32 values or bf16 bits) are widened exactly.
+ *
+ * Mask M_ij = -inf when any of:
+ *   - causal and j > i + (S_k - S_q)   (query i sits at absolute position
+ *                                       S_k - S_q + i: bottom-right alignment)
+ *   - q_keep[i] == 0  or  k_keep[j] == 0
+ *   - j lies outside i's sequence (packed varlen)
+ * A row whose scores are all -inf (including S_k == 0) returns O = 0 and
+ * LSE = -inf (page "Attention Kernel", section "Online softmax": a fully
+ * masked row must yield an agreed zero output, never NaN).
+ *
+ * GQA: query head h reads KV head h / (A / A_kv) (contiguous groups; page
+ * "Attention Kernel", section "问题与成本", GQA paragraph).
+ *
+ * Paged decode: logical token t of sequence b lives in physical page
+ * block_table[b][t / page_size] at offset t % page_size (page "Attention
+ * Kernel", section "Paged 与 ragged KV").
+ *
+ * Return value: 0 on success, -1 on invalid arguments.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+
+static double ld(const void *p, int64_t idx, int dt)
+{
+    if (dt == OR_F32)
+        return (double)((const float *)p)[idx];
+    uint32_t u = (uint32_t)((const uint16_t *)p)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * One query row against n key/value rows.
+ * q_off: element offset of the query row; kv_off[j]: element offset of key j's
+ * row in k and of its value row in v; vis[j]: 1 where M_ij = 0, 0 where -inf.
+ * s, p: scratch of n doubles (the materialised score and probability rows).
+ */
+static void attend_row(const void *q, int64_t q_off, const void *k, const void *v, int dt,
+                       const int64_t *kv_off, const unsigned char *vis, int64_t n, int d,
+                       double scale, double *s, double *p, double *o, double *lse)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        if (!vis[j]) {
+            s[j] = -INFINITY;
+        } else {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += ld(q, q_off + e, dt) * ld(k, kv_off[j] + e, dt);
+            s[j] = scale * dot;
+        }
+        if (s[j] > m)
+            m = s[j];
+    }
+    if (m == -INFINITY) {
+        for (int e = 0; e < d; ++e)
+            o[e] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        p[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+        l += p[j];
+    }
+    for (int64_t j = 0; j < n; ++j)
+        p[j] /= l;
+    for (int e = 0; e < d; ++e) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j)
+            if (p[j] != 0.0)
+                acc += p[j] * ld(v, kv_off[j] + e, dt);
+        o[e] = acc;
+    }
+    *lse = m + log(l);
+}
+
+struct scratch {
+    int64_t *off;
+    unsigned char *vis;
+    double *s, *p;
+};
+
+static int scratch_alloc(struct scratch *w, int64_t n)
+{
+    size_t m = (size_t)(n > 0 ? n : 1);
+    w->off = malloc(m * sizeof *w->off);
+    w->vis = malloc(m);
+    w->s = malloc(m * sizeof *w->s);
+    w->p = malloc(m * sizeof *w->p);
+    return (w->off && w->vis && w->s && w->p) ? 0 : -1;
+}
+
+static void scratch_free(struct scratch *w)
+{
+    free(w->off);
+    free(w->vis);
+    free(w->s);
+    free(w->p);
+}
+
+/*
+ * Batched prefill.  q, o: [B, A, S_q, d]; k, v: [B, A_kv, S_k, d];
+ * q_keep: [B, S_q] or NULL; k_keep: [B, S_k] or NULL.
+ * rows: flattened row ids (b*A + h)*S_q + i to compute, or NULL for all rows
+ * in order.  o receives [n_rows, d] doubles, lse [n_rows].
+ */
+int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
+                    int B, int A, int A_kv, int S_q, int S_k, int d, float scale, int causal,
+                    const uint8_t *q_keep, const uint8_t *k_keep,
+                    const int64_t *rows, int64_t n_rows, double *o, double *lse)
+{
+    if (B <= 0 || A <= 0 || A_kv <= 0 || S_q < 0 || S_k < 0 || d <= 0 || A % A_kv != 0)
+        return -1;
+    if (dt != OR_F32 && dt != OR_BF16)
+        return -1;
+    int64_t total = (int64_t)B * A * S_q;
+    if (rows == NULL)
+        n_rows = total;
+    const int G = A / A_kv;
+    int err = 0;
+#pragma omp parallel
+    {
+        struct scratch w;
+        int bad = scratch_alloc(&w, S_k);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (bad)
+                continue;
+            int64_t id = rows ? rows[r] : r;
+            if (id < 0 || id >= total) {
+                bad = 1;
+                continue;
+            }
+            int i = (int)(id % S_q);
+            int64_t bh = id / S_q;
+            int h = (int)(bh % A), b = (int)(bh / A);
+            int hk = h / G;
+            int64_t kv_base = (((int64_t)b * A_kv + hk) * S_k) * d;
+            int row_masked = q_keep && !q_keep[(int64_t)b * S_q + i];
+            for (int j = 0; j < S_k; ++j) {
+                w.off[j] = kv_base + (int64_t)j * d;
+                int visible = !row_masked;
+                if (causal && (int64_t)j > (int64_t)i + (S_k - S_q))
+                    visible = 0;
+                if (k_keep && !k_keep[(int64_t)b * S_k + j])
+                    visible = 0;
+                w.vis[j] = (unsigned char)visible;
+            }
+            attend_row(q, id * d, k, v, dt, w.off, w.vis, S_k, d, (double)scale, w.s, w.p,
+                       o + r * d, lse + r);
+        }
+        if (bad) {
+#pragma omp atomic write
+            err = 1;
+        }
+        scratch_free(&w);
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Packed varlen prefill.  q, o: [A, T, d]; k, v: [A_kv, T, d];
+ * cu_seqlens: [n_seq + 1], non-decreasing, cu[0] = 0, cu[n_seq] = T.
+ * Query t of sequence s sees keys of the same sequence only; causal compares
+ * positions within the sequence.  q_keep, k_keep: [T] or NULL.
+ * rows: flattened ids h*T + t, or NULL for all.
+ */
+int oracle_attn_fwd_varlen(const void *q, const void *k, const void *v, int dt,
+                           const int32_t *cu, int n_seq, int T, int A, int A_kv, int d,
+                           float scale, int causal, const uint8_t *q_keep, const uint8_t *k_keep,
+                           const int64_t *rows, int64_t n_rows, double *o, double *lse)
+{
+    if (n_seq < 0 || T < 0 || A <= 0 || A_kv <= 0 || d <= 0 || A % A_kv != 0 || !cu)
+        return -1;
+    if (dt != OR_F32 && dt != OR_BF16)
+        return -1;
+    if (cu[0] != 0 || cu[n_seq] != T)
+        return -1;
+    for (int s = 0; s < n_seq; ++s)
+        if (cu[s + 1] < cu[s])
+            return -1;
+    int64_t total = (int64_t)A * T;
+    if (rows == NULL)
+        n_rows = total;
+    const int G = A / A_kv;
+    int64_t maxlen = 0;
+    for (int s = 0; s < n_seq; ++s)
+        if (cu[s + 1] - cu[s] > maxlen)
+            maxlen = cu[s + 1] - cu[s];
+    int err = 0;
+#pragma omp parallel
+    {
+        struct scratch w;
+        int bad = scratch_alloc(&w, maxlen);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (bad)
+                continue;
+            int64_t id = rows ? rows[r] : r;
+            if (id < 0 || id >= total) {
+                bad = 1;
+                continue;
+            }
+            int t = (int)(id % T), h = (int)(id / T);
+            int s = 0;
+            while (!(cu[s] <= t && t < cu[s + 1]))
+                ++s;
+            int start = cu[s], len = cu[s + 1] - cu[s];
+            int i = t - start;
+            int64_t kv_base = ((int64_t)(h / G) * T + start) * d;
+            int row_masked = q_keep && !q_keep[t];
+            /* keys outside the sequence carry M = -inf and contribute exactly
+               zero, so only the sequence's own keys are listed */
+            for (int j = 0; j < len; ++j) {
+                w.off[j] = kv_base + (int64_t)j * d;
+                int visible = !row_masked;
+                if (causal && j > i)
+                    visible = 0;
+                if (k_keep && !k_keep[start + j])
+                    visible = 0;
+                w.vis[j] = (unsigned char)visible;
+            }
+            attend_row(q, id * d, k, v, dt, w.off, w.vis, len, d, (double)scale, w.s, w.p,
+                       o + r * d, lse + r);
+        }
+        if (bad) {
+#pragma omp atomic write
+            err = 1;
+        }
+        scratch_free(&w);
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Single-query decode over a paged KV cache.  q, o: [B, A, d];
+ * k_cache, v_cache: [num_pages, page_size, A_kv, d];
+ * block_table: [B, max_pages]; seq_lens: [B].
+ * rows: flattened ids b*A + h, or NULL for all.
+ */
+int oracle_decode_paged(const void *q, const void *k_cache, const void *v_cache, int dt,
+                        const int32_t *block_table, const int32_t *seq_lens,
+                        int B, int A, int A_kv, int d, int page_size, int max_pages,
+                        int num_pages, float scale,
+                        const int64_t *rows, int64_t n_rows, double *o, double *lse)
+{
+    if (B <= 0 || A <= 0 || A_kv <= 0 || d <= 0 || A % A_kv != 0 || page_size <= 0 ||
+        max_pages < 0 || num_pages < 0)
+        return -1;
+    if (dt != OR_F32 && dt != OR_BF16)
+        return -1;
+    int64_t maxlen = 0;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size)
+            return -1;
+        for (int64_t t = 0; t < seq_lens[b]; t += page_size) {
+            int32_t pg = block_table[(int64_t)b * max_pages + t / page_size];
+            if (pg < 0 || pg >= num_pages)
+                return -1;
+        }
+        if (seq_lens[b] > maxlen)
+            maxlen = seq_lens[b];
+    }
+    int64_t total = (int64_t)B * A;
+    if (rows == NULL)
+        n_rows = total;
+    const int G = A / A_kv;
+    int err = 0;
+#pragma omp parallel
+    {
+        struct scratch w;
+        int bad = scratch_alloc(&w, maxlen);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (bad)
+                continue;
+            int64_t id = rows ? rows[r] : r;
+            if (id < 0 || id >= total) {
+                bad = 1;
+                continue;
+            }
+            int h = (int)(id % A), b = (int)(id / A);
+            int hk = h / G;
+            int n = seq_lens[b];
+            for (int t = 0; t < n; ++t) {
+                int64_t page = block_table[(int64_t)b * max_pages + t / page_size];
+                int off = t % page_size;
+                w.off[t] = ((page * page_size + off) * A_kv + hk) * (int64_t)d;
+                w.vis[t] = 1;
+            }
+            attend_row(q, id * d, k_cache, v_cache, dt, w.off, w.vis, n, d, (double)scale,
+                       w.s, w.p, o + r * d, lse + r);
+        }
+        if (bad) {
+#pragma omp atomic write
+            err = 1;
+        }
+        scratch_free(&w);
+    }
+    return err ? -1 : 0;
+}
+
+/* Number of threads an OpenMP region will use (for reporting). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

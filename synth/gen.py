@@ -1,0 +1,309 @@
+"""Seeded synthetic inputs for fused exact attention (prefill, varlen, paged decode).
+
+Nothing here computes attention.  The module draws numbers, rounds them to the
+storage dtype once, and builds the index structures (cu_seqlens, block tables)
+that describe where each sequence lives.  Both sides of a parity check read the
+same arrays: the CPU oracle widens the stored bf16 bits to fp64, the GPU reads
+the bits.
+
+Random streams.  Every tensor is drawn from its own stream, identified by
+``(seed, stream)``; a tensor is filled in chunks of ``CHUNK`` elements and chunk
+``c`` comes from ``PCG64(SeedSequence([seed, stream, c]))``.  The values are
+therefore fixed by (seed, stream, position) and do not depend on how many
+threads fill the array.
+
+Workload shapes follow the pages' workloads (dense causal prefill, GQA prefill,
+long-context paged decode, ragged packed prefill); the five named recipes are in
+``CONFIGS``.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CHUNK = 1 << 22
+
+# stream ids, in drawing order
+S_Q, S_K, S_V, S_LENS, S_PERM, S_QKEEP, S_KKEEP = 0, 1, 2, 3, 4, 5, 6
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _fill(out: np.ndarray, seed: int, stream: int, kind: str, lo: float = 0.0, hi: float = 1.0) -> None:
+    flat = out.reshape(-1)
+    n = flat.size
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def work(c: int) -> None:
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, c])))
+        view = flat[c * CHUNK: min(n, (c + 1) * CHUNK)]
+        if kind == "normal":
+            rng.standard_normal(out=view, dtype=np.float32)
+        elif kind == "uniform":
+            rng.random(out=view, dtype=np.float32)
+            view *= np.float32(hi - lo)
+            view += np.float32(lo)
+        else:  # pragma: no cover
+            raise ValueError(kind)
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            work(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, round-to-nearest-even, returned as uint16 bits.
+
+    Inputs are finite draws, so the NaN special case is not needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    src = x.reshape(-1).view(np.uint32)
+    dst = out.reshape(-1)
+    n = src.size
+
+    def work(c: int) -> None:
+        s = src[c * CHUNK: min(n, (c + 1) * CHUNK)]
+        lsb = (s >> np.uint32(16)) & np.uint32(1)
+        dst[c * CHUNK: min(n, (c + 1) * CHUNK)] = ((s + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+    nchunks = (n + CHUNK - 1) // CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            work(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bits to float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def draw(shape, seed: int, stream: int, kind: str = "normal", dtype: str = "bf16",
+         lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    """Draw a tensor; bf16 tensors are returned as uint16 bits, fp32 as float32."""
+    x = np.empty(shape, dtype=np.float32)
+    _fill(x, seed, stream, kind, lo, hi)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f32":
+        return x
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def as_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored tensor (bits or float32) as float32 values."""
+    return bf16_bits_to_f32(x) if dtype == "bf16" else np.asarray(x, dtype=np.float32)
+
+
+def keep_mask(n: int, n_masked: int, seed: int, stream: int) -> np.ndarray:
+    """uint8 keep vector with exactly ``n_masked`` zeros at seeded positions."""
+    keep = np.ones(n, dtype=np.uint8)
+    if n_masked > 0:
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
+        keep[rng.choice(n, size=n_masked, replace=False)] = 0
+    return keep
+
+
+@dataclass
+class Dense:
+    """Batched prefill problem: q/o [B, A, S_q, d], k/v [B, A_kv, S_k, d]."""
+    B: int
+    A: int
+    A_kv: int
+    S_q: int
+    S_k: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_keep: np.ndarray | None = None   # [B, S_q] uint8
+    k_keep: np.ndarray | None = None   # [B, S_k] uint8
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs, 4*B*A*S_q*S_k*d, halved when causal."""
+        f = 4.0 * self.B * self.A * self.S_q * self.S_k * self.d
+        return f / 2 if self.causal else f
+
+
+@dataclass
+class Varlen:
+    """Packed ragged prefill: q/o [A, T, d], k/v [A_kv, T, d], sequences by cu_seqlens."""
+    lens: np.ndarray
+    cu_seqlens: np.ndarray     # int32 [n_seq + 1]
+    A: int
+    A_kv: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_keep: np.ndarray | None = None   # [T]
+    k_keep: np.ndarray | None = None   # [T]
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def n_seq(self) -> int:
+        return int(self.lens.size)
+
+    def flops(self) -> float:
+        f = float(np.sum(4.0 * self.A * self.lens.astype(np.float64) ** 2 * self.d))
+        return f / 2 if self.causal else f
+
+
+@dataclass
+class Paged:
+    """Single-query decode over a paged KV cache.
+
+    q/o [B, A, d]; k_cache/v_cache [num_pages, page_size, A_kv, d];
+    block_table int32 [B, max_pages] (-1 past a sequence's last page);
+    seq_lens int32 [B].
+    """
+    B: int
+    A: int
+    A_kv: int
+    d: int
+    page_size: int
+    dtype: str
+    scale: float
+    seq_lens: np.ndarray
+    block_table: np.ndarray
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    num_pages: int = field(default=0)
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def kv_bytes(self) -> float:
+        """Algorithmic KV bytes: every valid token's K and V row of every KV head."""
+        esz = 2 if self.dtype == "bf16" else 4
+        return float(2 * self.A_kv * self.d * esz * int(np.sum(self.seq_lens, dtype=np.int64)))
+
+
+def make_dense(B, A, A_kv, S_q, S_k, d, *, dtype="bf16", causal=False, seed=0,
+               v_kind="normal", scale=None, q_masked=0, k_masked=0) -> Dense:
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    q = draw((B, A, S_q, d), seed, S_Q, "normal", dtype)
+    k = draw((B, A_kv, S_k, d), seed, S_K, "normal", dtype)
+    if v_kind == "uniform":
+        v = draw((B, A_kv, S_k, d), seed, S_V, "uniform", dtype, -1.0, 1.0)
+    else:
+        v = draw((B, A_kv, S_k, d), seed, S_V, "normal", dtype)
+    qk = keep_mask(B * S_q, q_masked, seed, S_QKEEP).reshape(B, S_q) if q_masked else None
+    kk = keep_mask(B * S_k, k_masked, seed, S_KKEEP).reshape(B, S_k) if k_masked else None
+    return Dense(B, A, A_kv, S_q, S_k, d, dtype, causal, scale, q, k, v, qk, kk)
+
+
+def lognormal_lengths(n: int, median: float, sigma: float, lo: int, hi: int, seed: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, S_LENS])))
+    x = np.exp(rng.normal(math.log(median), sigma, size=n))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+def make_varlen(lens, A, A_kv, d, *, dtype="bf16", causal=True, seed=0, q_mask_frac=0.0,
+                k_mask_frac=0.0, scale=None) -> Varlen:
+    lens = np.asarray(lens, dtype=np.int64)
+    cu = np.zeros(lens.size + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    q = draw((A, T, d), seed, S_Q, "normal", dtype)
+    k = draw((A_kv, T, d), seed, S_K, "normal", dtype)
+    v = draw((A_kv, T, d), seed, S_V, "normal", dtype)
+    qk = keep_mask(T, int(round(q_mask_frac * T)), seed, S_QKEEP) if q_mask_frac > 0 else None
+    kk = keep_mask(T, int(round(k_mask_frac * T)), seed, S_KKEEP) if k_mask_frac > 0 else None
+    return Varlen(lens, cu, A, A_kv, d, dtype, causal, scale, q, k, v, qk, kk)
+
+
+def make_paged(lens, A, A_kv, d, page_size, *, dtype="bf16", seed=0, scale=None,
+               max_pages=None, extra_pages=0) -> Paged:
+    """Paged KV cache whose physical pages are a seeded permutation of the pool.
+
+    The pool holds exactly sum(ceil(len/page_size)) pages (plus ``extra_pages``
+    spare ones), assigned to (sequence, logical page) in order through the
+    permutation.  Unused block-table entries are -1.
+    """
+    lens = np.asarray(lens, dtype=np.int32)
+    B = lens.size
+    npg = (lens.astype(np.int64) + page_size - 1) // page_size
+    pool = int(npg.sum()) + int(extra_pages)
+    if max_pages is None:
+        max_pages = max(1, int(npg.max()) if B else 1)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, S_PERM])))
+    perm = rng.permutation(pool).astype(np.int32)
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = int(npg[b])
+        bt[b, :n] = perm[off: off + n]
+        off += n
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    q = draw((B, A, d), seed, S_Q, "normal", dtype)
+    kc = draw((pool, page_size, A_kv, d), seed, S_K, "normal", dtype)
+    vc = draw((pool, page_size, A_kv, d), seed, S_V, "normal", dtype)
+    return Paged(B, A, A_kv, d, page_size, dtype, scale, lens, bt, q, kc, vc, pool)
+
+
+# --- the five named workloads -------------------------------------------------
+
+CONFIG_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}
+
+CONFIGS = {
+    1: "fp32 single head, B=1 A=A_kv=1 S_q=S_k=128 d=64, non-causal, no mask",
+    2: "bf16 MHA causal prefill, B=4 A=A_kv=32 S_q=S_k=2048 d=128",
+    3: "bf16 GQA causal prefill, B=1 A=32 A_kv=8 S_q=S_k=16384 d=128, V~U(-1,1)",
+    4: "bf16 paged decode, 64 seqs, A=32 A_kv=8 d=128, lens~U{512..32768}, page 16",
+    5: "bf16 varlen causal, 16 seqs log-normal(median 1024, sigma 1, clip [64,8192]), A=A_kv=16 d=64, 5% rows fully masked",
+}
+
+
+def config_lengths_decode(seed: int = CONFIG_SEEDS[4], n: int = 64) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, S_LENS])))
+    return rng.integers(512, 32768, size=n, endpoint=True).astype(np.int32)
+
+
+def make_config(k: int, seed: int | None = None):
+    seed = CONFIG_SEEDS[k] if seed is None else seed
+    if k == 1:
+        return make_dense(1, 1, 1, 128, 128, 64, dtype="f32", causal=False, seed=seed)
+    if k == 2:
+        return make_dense(4, 32, 32, 2048, 2048, 128, dtype="bf16", causal=True, seed=seed)
+    if k == 3:
+        return make_dense(1, 32, 8, 16384, 16384, 128, dtype="bf16", causal=True, seed=seed,
+                          v_kind="uniform")
+    if k == 4:
+        return make_paged(config_lengths_decode(seed), 32, 8, 128, 16, dtype="bf16", seed=seed)
+    if k == 5:
+        lens = lognormal_lengths(16, 1024.0, 1.0, 64, 8192, seed)
+        return make_varlen(lens, 16, 16, 64, dtype="bf16", causal=True, seed=seed, q_mask_frac=0.05)
+    raise ValueError(f"no config {k}")

@@ -1,0 +1,412 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with something other than itself: the worked example of page
+"Attention Kernel" (section "Blockwise reference"), closed forms, invariants,
+library routines on special cases, an independent blockwise recurrence, and
+brute force with ``math.fsum`` on tiny inputs.  The same battery runs against
+mutated copies of the oracle (tests/test_oracle_mutants.py) to show that a
+plausible mistake in the oracle fails at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+from scipy.special import expit, logsumexp, softmax
+
+from oracle import blockwise
+from synth import gen
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _row_problem(scores, values):
+    """Dense f32 problem whose single query row has exactly the given scores.
+
+    q = e_0 and k_j = scores_j * e_0 (scale 1), so q.k_j = scores_j; entries
+    equal to -inf are produced by k_keep = 0 instead.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    n, d = values.shape
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, n, d), np.float32)
+    fin = np.isfinite(scores)
+    k[0, 0, fin, 0] = scores[fin]
+    keep = fin.astype(np.uint8).reshape(1, n)
+    v = _f32(values).reshape(1, 1, n, d)
+    return q, k, v, keep
+
+
+# --- the page's worked example --------------------------------------------------
+
+def pin_worked_example(orc):
+    fx = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    scores = np.array([float(s) for s in fx["scores"]])
+    values = np.arange(15, dtype=np.float64).reshape(fx["values_rows"], fx["values_cols"])
+    q, k, v, keep = _row_problem(scores, values)
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=1.0, k_keep=keep)
+    want = softmax(scores) @ values
+    assert np.allclose(o[0, 0, 0], want, rtol=0, atol=1e-12), (o[0, 0, 0], want)
+    assert abs(lse[0, 0, 0] - logsumexp(scores)) < 1e-12
+    # sum(P) = 1 and value columns differ by exactly 1, so consecutive outputs do too
+    assert abs((o[0, 0, 0, 1] - o[0, 0, 0, 0]) - 1.0) < 1e-12
+    assert abs((o[0, 0, 0, 2] - o[0, 0, 0, 1]) - 1.0) < 1e-12
+    # the page's blockwise procedure with block size 2 agrees
+    ob, lb = blockwise.online_attention_row(scores, values, block_size=fx["block_size"])
+    assert np.allclose(ob, want, rtol=0, atol=1e-12) and abs(lb - lse[0, 0, 0]) < 1e-12
+
+
+def pin_all_masked_row(orc):
+    values = np.arange(15, dtype=np.float64).reshape(5, 3)
+    q, k, v, keep = _row_problem(np.full(5, -np.inf), values)
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=1.0, k_keep=keep)
+    assert np.array_equal(o[0, 0, 0], np.zeros(3)) and not np.isnan(o).any()
+    assert lse[0, 0, 0] == -np.inf
+    ob, lb = blockwise.online_attention_row(np.full(5, -np.inf), values, block_size=2)
+    assert np.array_equal(ob, np.zeros(3)) and lb == -np.inf
+    # S_k = 0: every row is fully masked
+    o0, l0 = orc.attn_fwd(np.ones((1, 2, 3, 4), np.float32), np.ones((1, 1, 0, 4), np.float32),
+                          np.ones((1, 1, 0, 4), np.float32), dtype="f32", scale=0.5)
+    assert np.array_equal(o0, np.zeros_like(o0)) and np.all(l0 == -np.inf)
+
+
+def pin_shape_rejection(orc):
+    values = np.zeros((6, 3))
+    for bad in (
+        lambda: orc.attn_fwd(np.zeros((1, 1, 1, 3), np.float32), np.zeros((1, 1, 5, 3), np.float32),
+                             _f32(values).reshape(1, 1, 6, 3), dtype="f32", scale=1.0),
+        lambda: blockwise.online_attention_row(np.zeros(5), values, block_size=2),
+        lambda: orc.attn_fwd(np.zeros((1, 3, 1, 3), np.float32), np.zeros((1, 2, 5, 3), np.float32),
+                             np.zeros((1, 2, 5, 3), np.float32), dtype="f32", scale=1.0),
+    ):
+        try:
+            bad()
+        except ValueError:
+            continue
+        raise AssertionError("misaligned inputs must be rejected")
+
+
+# --- closed forms -----------------------------------------------------------------
+
+def pin_single_key(orc):
+    rng = np.random.default_rng(11)
+    q = _f32(rng.standard_normal((2, 3, 4, 16)))
+    k = _f32(rng.standard_normal((2, 3, 1, 16)))
+    v = _f32(rng.standard_normal((2, 3, 1, 16)))
+    scale = 0.3125
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=scale)
+    for b in range(2):
+        for h in range(3):
+            for i in range(4):
+                assert np.array_equal(o[b, h, i], v[b, h, 0].astype(np.float64))
+                s = scale * math.fsum(float(a) * float(c) for a, c in zip(q[b, h, i], k[b, h, 0]))
+                assert abs(lse[b, h, i] - s) < 1e-12
+
+
+def pin_causal_first_row(orc):
+    """Causal row 0 sees key 0 only, so O = v_0 exactly, for every head (GQA)."""
+    p = gen.make_dense(2, 4, 2, 9, 9, 8, dtype="bf16", causal=True, seed=5)
+    o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True)
+    vf = gen.as_f32(p.v, "bf16")
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(o[b, h, 0], vf[b, h // 2, 0].astype(np.float64))
+
+
+def pin_two_keys(orc):
+    rng = np.random.default_rng(12)
+    q = _f32(rng.standard_normal((1, 1, 5, 8)))
+    k = _f32(rng.standard_normal((1, 1, 2, 8)))
+    v = _f32(rng.standard_normal((1, 1, 2, 8)))
+    scale = 0.6875
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=scale)
+    for i in range(5):
+        s1 = scale * math.fsum(float(a) * float(c) for a, c in zip(q[0, 0, i], k[0, 0, 0]))
+        s2 = scale * math.fsum(float(a) * float(c) for a, c in zip(q[0, 0, i], k[0, 0, 1]))
+        want = expit(s1 - s2) * v[0, 0, 0].astype(np.float64) + expit(s2 - s1) * v[0, 0, 1].astype(np.float64)
+        assert np.allclose(o[0, 0, i], want, rtol=0, atol=1e-12)
+        assert abs(lse[0, 0, i] - np.logaddexp(s1, s2)) < 1e-12
+
+
+def pin_uniform_scores(orc):
+    """q = 0 makes every score 0: O = mean of the visible values, LSE = ln n."""
+    rng = np.random.default_rng(13)
+    n, d = 37, 16
+    q = np.zeros((1, 2, 3, d), np.float32)
+    k = _f32(rng.standard_normal((1, 2, n, d)))
+    v = _f32(rng.standard_normal((1, 2, n, d)))
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=1.0)
+    for h in range(2):
+        for i in range(3):
+            assert np.allclose(o[0, h, i], v[0, h].astype(np.float64).mean(axis=0), rtol=0, atol=1e-12)
+            assert abs(lse[0, h, i] - math.log(n)) < 1e-12
+
+
+def pin_rows_are_distributions(orc):
+    """With V = identity (S_k = d), O is the probability row itself."""
+    rng = np.random.default_rng(14)
+    n = 24
+    q = _f32(rng.standard_normal((1, 1, 6, n)) * 2)
+    k = _f32(rng.standard_normal((1, 1, n, n)))
+    v = np.eye(n, dtype=np.float32).reshape(1, 1, n, n)
+    keep = np.ones((1, n), np.uint8)
+    keep[0, [3, 7, 20]] = 0
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.25, k_keep=keep)
+    s = 0.25 * (q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T)
+    s[:, keep[0] == 0] = -np.inf
+    for i in range(6):
+        assert abs(math.fsum(o[0, 0, i]) - 1.0) < 1e-12 and np.all(o[0, 0, i] >= 0)
+        assert np.allclose(o[0, 0, i], softmax(s[i]), rtol=0, atol=1e-12)
+        assert np.all(o[0, 0, i, keep[0] == 0] == 0)
+        assert abs(lse[0, 0, i] - logsumexp(s[i])) < 1e-12
+
+
+# --- invariants -----------------------------------------------------------------------
+
+def pin_masked_keys_inert(orc):
+    p = gen.make_dense(1, 2, 2, 10, 30, 8, dtype="f32", causal=True, seed=15, k_masked=9)
+    o1, l1 = orc.attn_fwd(p.q, p.k, p.v, dtype="f32", scale=p.scale, causal=True, k_keep=p.k_keep)
+    k2, v2 = p.k.copy(), p.v.copy()
+    dead = p.k_keep[0] == 0
+    k2[:, :, dead] = 1e30
+    v2[:, :, dead] = -7e29
+    o2, l2 = orc.attn_fwd(p.q, k2, v2, dtype="f32", scale=p.scale, causal=True, k_keep=p.k_keep)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_shift_invariance(orc):
+    """Adding c to every score leaves O unchanged and shifts LSE by c (|c| up to 1e4)."""
+    rng = np.random.default_rng(16)
+    n = 19
+    x = rng.standard_normal(4)
+    y = rng.standard_normal(n)
+    v = _f32(rng.standard_normal((1, 1, n, 2)))
+    base = None
+    for c in (0.0, 1e4, -1e4, 37.5):
+        q = np.zeros((1, 1, 4, 2), np.float32)
+        q[0, 0, :, 0] = x
+        q[0, 0, :, 1] = 1.0
+        k = np.zeros((1, 1, n, 2), np.float32)
+        k[0, 0, :, 0] = y
+        k[0, 0, :, 1] = c
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=1.0)
+        if base is None:
+            base = (o, lse)
+            continue
+        assert np.allclose(o, base[0], rtol=0, atol=1e-10)
+        assert np.allclose(lse - base[1], c, rtol=0, atol=1e-9)
+
+
+def pin_gqa_equals_repeated_heads(orc):
+    p = gen.make_dense(2, 8, 2, 7, 11, 16, dtype="bf16", causal=True, seed=17)
+    o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True)
+    kr = np.repeat(p.k, 4, axis=1)
+    vr = np.repeat(p.v, 4, axis=1)
+    o2, l2 = orc.attn_fwd(p.q, kr, vr, dtype="bf16", scale=p.scale, causal=True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def pin_varlen_equals_separate(orc):
+    lens = [5, 0, 13, 1, 8]
+    p = gen.make_varlen(lens, 4, 2, 8, dtype="bf16", causal=True, seed=18, q_mask_frac=0.1, k_mask_frac=0.1)
+    o, lse = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=True,
+                                 q_keep=p.q_keep, k_keep=p.k_keep)
+    for s, n in enumerate(lens):
+        a, b = int(p.cu_seqlens[s]), int(p.cu_seqlens[s + 1])
+        if n == 0:
+            continue
+        qs = p.q[:, a:b][None]
+        ks = p.k[:, a:b][None]
+        vs = p.v[:, a:b][None]
+        o1, l1 = orc.attn_fwd(qs, ks, vs, dtype="bf16", scale=p.scale, causal=True,
+                              q_keep=p.q_keep[a:b][None], k_keep=p.k_keep[a:b][None])
+        assert np.array_equal(o[:, a:b], o1[0]) and np.array_equal(lse[:, a:b], l1[0])
+
+
+def pin_decode_is_last_causal_row(orc):
+    n, d = 23, 16
+    p = gen.make_dense(1, 4, 2, n, n, d, dtype="bf16", causal=True, seed=19)
+    o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True)
+    # S_q = 1 < S_k: bottom-right alignment lets the single query see every key
+    o1, l1 = orc.attn_fwd(p.q[:, :, n - 1:], p.k, p.v, dtype="bf16", scale=p.scale, causal=True)
+    assert np.array_equal(o1[:, :, 0], o[:, :, n - 1]) and np.array_equal(l1[:, :, 0], lse[:, :, n - 1])
+    # the same through a paged cache (page size 4, identity page order)
+    ps = 4
+    npg = (n + ps - 1) // ps
+    kc = np.zeros((npg, ps, 2, d), np.uint16)
+    vc = np.zeros((npg, ps, 2, d), np.uint16)
+    for t in range(n):
+        kc[t // ps, t % ps] = p.k[0, :, t]
+        vc[t // ps, t % ps] = p.v[0, :, t]
+    bt = np.arange(npg, dtype=np.int32)[None]
+    o2, l2 = orc.decode_paged(p.q[:, :, n - 1], kc, vc, bt, np.array([n], np.int32), dtype="bf16",
+                              scale=p.scale)
+    assert np.array_equal(o2[0], o[0, :, n - 1]) and np.array_equal(l2[0], lse[0, :, n - 1])
+
+
+def pin_paged_equals_contiguous(orc):
+    lens = [1, 16, 17, 40, 0, 33]
+    p = gen.make_paged(lens, 8, 2, 16, 16, dtype="bf16", seed=20, extra_pages=3)
+    o, lse = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="bf16",
+                              scale=p.scale)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(o[b], np.zeros_like(o[b])) and np.all(lse[b] == -np.inf)
+            continue
+        t = np.arange(n)
+        pages = p.block_table[b, t // 16]
+        kc = p.k_cache[pages, t % 16].transpose(1, 0, 2)[None]  # [1, A_kv, n, d]
+        vc = p.v_cache[pages, t % 16].transpose(1, 0, 2)[None]
+        o1, l1 = orc.attn_fwd(p.q[b][None, :, None], np.ascontiguousarray(kc), np.ascontiguousarray(vc),
+                              dtype="bf16", scale=p.scale)
+        assert np.array_equal(o1[0, :, 0], o[b]) and np.array_equal(l1[0, :, 0], lse[b])
+    # cache rows no sequence owns (page tails past seq_len, spare pages) are never read
+    kc, vc = p.k_cache.copy(), p.v_cache.copy()
+    owned = np.zeros(p.k_cache.shape[:2], bool)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            owned[p.block_table[b, t // 16], t % 16] = True
+    kc[~owned] = 0x7FC0  # bf16 NaN
+    vc[~owned] = 0x7FC0
+    o3, l3 = orc.decode_paged(p.q, kc, vc, p.block_table, p.seq_lens, dtype="bf16", scale=p.scale)
+    assert np.array_equal(o3, o) and np.array_equal(l3, lse)
+
+
+def pin_causal_offset(orc):
+    """Bottom-right alignment: S_q > S_k masks the leading S_q - S_k rows entirely;
+    S_q < S_k lets row i see keys 0 .. i + S_k - S_q."""
+    p = gen.make_dense(1, 1, 1, 9, 5, 8, dtype="f32", causal=True, seed=21)
+    o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="f32", scale=p.scale, causal=True)
+    assert np.array_equal(o[0, 0, :4], np.zeros((4, 8))) and np.all(lse[0, 0, :4] == -np.inf)
+    assert np.all(np.isfinite(lse[0, 0, 4:]))
+    p = gen.make_dense(1, 1, 1, 4, 10, 8, dtype="f32", causal=True, seed=22)
+    o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="f32", scale=p.scale, causal=True)
+    for i in range(4):
+        n = i + 10 - 4 + 1
+        o1, l1 = orc.attn_fwd(p.q[:, :, i:i + 1], p.k[:, :, :n], p.v[:, :, :n], dtype="f32", scale=p.scale)
+        assert np.array_equal(o1[0, 0, 0], o[0, 0, i]) and l1[0, 0, 0] == lse[0, 0, i]
+
+
+def pin_bf16_widening(orc):
+    """bf16 bits are widened exactly: same result as feeding the widened fp32 values."""
+    p = gen.make_dense(1, 2, 1, 6, 9, 8, dtype="bf16", causal=False, seed=23)
+    o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale)
+    o2, l2 = orc.attn_fwd(gen.as_f32(p.q, "bf16"), gen.as_f32(p.k, "bf16"), gen.as_f32(p.v, "bf16"),
+                          dtype="f32", scale=p.scale)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # and the widening is the textbook one: 1.0 = 0x3f80, -2.0 = 0xc000, 0.5 = 0x3f00
+    q = np.array([0x3F80, 0, 0, 0], np.uint16).reshape(1, 1, 1, 4)
+    k = np.array([[0xC000, 0, 0, 0], [0x3F00, 0, 0, 0]], np.uint16).reshape(1, 1, 2, 4)
+    v = np.array([[0x3F80, 0, 0, 0], [0, 0x3F80, 0, 0]], np.uint16).reshape(1, 1, 2, 4)
+    o3, l3 = orc.attn_fwd(q, k, v, dtype="bf16", scale=1.0)
+    assert abs(l3[0, 0, 0] - np.logaddexp(-2.0, 0.5)) < 1e-12
+    assert abs(o3[0, 0, 0, 0] - expit(-2.5)) < 1e-12
+
+
+# --- independent recurrence and brute force ---------------------------------------
+
+def pin_blockwise_recurrence(orc):
+    rng = np.random.default_rng(24)
+    for trial in range(4):
+        S_q, S_k, d = 6, int(rng.integers(1, 60)), 8
+        causal = bool(trial % 2)
+        p = gen.make_dense(1, 2, 1, S_q, S_k, d, dtype="bf16", causal=causal, seed=100 + trial, k_masked=S_k // 5)
+        o, lse = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal, k_keep=p.k_keep)
+        qf, kf, vf = (gen.as_f32(x, "bf16").astype(np.float64) for x in (p.q, p.k, p.v))
+        for h in range(2):
+            s = blockwise.dense_scores(qf[0, h], kf[0, 0], p.scale)
+            s[:, p.k_keep[0] == 0] = -np.inf
+            if causal:
+                for i in range(S_q):
+                    s[i, np.arange(S_k) > i + S_k - S_q] = -np.inf
+            for i in range(S_q):
+                cuts = sorted(set([0, S_k] + list(rng.integers(0, S_k + 1, size=int(rng.integers(0, 6))))))
+                order = list(rng.permutation(len(cuts) - 1))
+                ob, lb = blockwise.online_attention_row(s[i], vf[0, 0], bounds=cuts, order=order)
+                assert np.allclose(ob, o[0, h, i], rtol=1e-12, atol=1e-12)
+                assert (lb == -np.inf and lse[0, h, i] == -np.inf) or abs(lb - lse[0, h, i]) < 1e-12
+
+
+def _brute(q, k, v, scale, vis):
+    """Pure-Python softmax attention for one row with math.fsum."""
+    s = [scale * math.fsum(a * b for a, b in zip(q, kj)) if ok else -math.inf for kj, ok in zip(k, vis)]
+    m = max(s) if s else -math.inf
+    if m == -math.inf:
+        return [0.0] * len(q), -math.inf
+    w = [math.exp(x - m) if x != -math.inf else 0.0 for x in s]
+    lsum = math.fsum(w)
+    out = [math.fsum(wj * vj[e] for wj, vj in zip(w, v)) / lsum for e in range(len(v[0]) if v else len(q))]
+    return out, m + math.log(lsum)
+
+
+def pin_brute_force(orc):
+    rng = np.random.default_rng(25)
+    for S_q, S_k, d, A, A_kv, causal in [(3, 5, 4, 2, 1, True), (5, 3, 2, 4, 2, True), (4, 4, 3, 3, 3, False),
+                                         (1, 8, 4, 2, 2, True), (6, 7, 1, 2, 1, False)]:
+        q = _f32(rng.standard_normal((2, A, S_q, d)))
+        k = _f32(rng.standard_normal((2, A_kv, S_k, d)))
+        v = _f32(rng.standard_normal((2, A_kv, S_k, d)))
+        qk = (rng.random((2, S_q)) > 0.2).astype(np.uint8)
+        kk = (rng.random((2, S_k)) > 0.2).astype(np.uint8)
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.875, causal=causal, q_keep=qk, k_keep=kk)
+        G = A // A_kv
+        for b in range(2):
+            for h in range(A):
+                for i in range(S_q):
+                    vis = [bool(qk[b, i]) and bool(kk[b, j]) and (not causal or j <= i + S_k - S_q)
+                           for j in range(S_k)]
+                    want, wl = _brute([float(x) for x in q[b, h, i]],
+                                      [[float(x) for x in row] for row in k[b, h // G]],
+                                      [[float(x) for x in row] for row in v[b, h // G]], 0.875, vis)
+                    assert np.allclose(o[b, h, i], want, rtol=0, atol=1e-13), (S_q, S_k, b, h, i)
+                    assert (wl == -math.inf and lse[b, h, i] == -np.inf) or abs(lse[b, h, i] - wl) < 1e-13
+
+
+def pin_varlen_brute_force(orc):
+    rng = np.random.default_rng(26)
+    lens = [3, 0, 5, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, A, A_kv, d = int(cu[-1]), 2, 1, 3
+    q = _f32(rng.standard_normal((A, T, d)))
+    k = _f32(rng.standard_normal((A_kv, T, d)))
+    v = _f32(rng.standard_normal((A_kv, T, d)))
+    kk = (rng.random(T) > 0.25).astype(np.uint8)
+    o, lse = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=1.125, causal=True, k_keep=kk)
+    for h in range(A):
+        for t in range(T):
+            s = int(np.searchsorted(cu, t, side="right") - 1)
+            a = int(cu[s])
+            vis = [bool(kk[j]) and cu[s] <= j < cu[s + 1] and j <= t for j in range(T)]
+            want, wl = _brute([float(x) for x in q[h, t]], [[float(x) for x in r] for r in k[0]],
+                              [[float(x) for x in r] for r in v[0]], 1.125, vis)
+            assert np.allclose(o[h, t], want, rtol=0, atol=1e-13), (h, t, a)
+            assert (wl == -math.inf and lse[h, t] == -np.inf) or abs(lse[h, t] - wl) < 1e-13
+
+
+def pin_paged_brute_force(orc):
+    rng = np.random.default_rng(27)
+    lens = [5, 0, 9]
+    p = gen.make_paged(lens, 4, 2, 3, 4, dtype="f32", seed=28, extra_pages=2)
+    o, lse = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="f32", scale=p.scale)
+    for b, n in enumerate(lens):
+        for h in range(4):
+            ks = [[float(x) for x in p.k_cache[p.block_table[b, t // 4], t % 4, h // 2]] for t in range(n)]
+            vs = [[float(x) for x in p.v_cache[p.block_table[b, t // 4], t % 4, h // 2]] for t in range(n)]
+            want, wl = _brute([float(x) for x in p.q[b, h]], ks, vs, p.scale, [True] * n)
+            if n == 0:
+                want = [0.0] * 3
+            assert np.allclose(o[b, h], want, rtol=0, atol=1e-13)
+            assert (wl == -math.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - wl) < 1e-13
+    del rng
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,88 @@
+"""Each plausible mistake planted in a copy of the oracle must fail a pin.
+
+The mutants are textual edits of ``oracle/attn_oracle.c`` compiled into a
+temporary directory (CPU only); the pin battery of ``tests/oracle_pins.py`` runs
+against each one in a child process.  The real oracle source is never changed.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, text to find, replacement, which occurrence (0 = all))
+MUTANTS = [
+    ("scale dropped", "s[j] = scale * dot;", "s[j] = dot;", 0),
+    ("max subtracted with wrong sign", "exp(s[j] - m)", "exp(m - s[j])", 0),
+    ("normalisation dropped", "p[j] /= l;", "p[j] /= 1.0;", 0),
+    ("max missing from LSE", "*lse = m + log(l);", "*lse = log(l);", 0),
+    ("log2 instead of ln in LSE", "*lse = m + log(l);", "*lse = m + log2(l);", 0),
+    ("GQA head taken modulo", "int hk = h / G;", "int hk = h % A_kv;", 1),
+    ("causal diagonal excluded", "(int64_t)j > (int64_t)i + (S_k - S_q)", "(int64_t)j >= (int64_t)i + (S_k - S_q)", 0),
+    ("causal aligned top-left", "(int64_t)j > (int64_t)i + (S_k - S_q)", "(int64_t)j > (int64_t)i", 0),
+    ("V read from K", "acc += p[j] * ld(v, kv_off[j] + e, dt);", "acc += p[j] * ld(k, kv_off[j] + e, dt);", 0),
+    ("q_keep ignored (dense)", "int row_masked = q_keep && !q_keep[(int64_t)b * S_q + i];", "int row_masked = 0;", 0),
+    ("k_keep ignored (dense)", "if (k_keep && !k_keep[(int64_t)b * S_k + j])", "if (0)", 0),
+    ("k_keep ignored (varlen)", "if (k_keep && !k_keep[start + j])", "if (0)", 0),
+    ("varlen causal diagonal excluded", "if (causal && j > i)", "if (causal && j >= i)", 0),
+    ("varlen keys not offset to sequence", "int64_t kv_base = ((int64_t)(h / G) * T + start) * d;",
+     "int64_t kv_base = ((int64_t)(h / G) * T) * d;", 0),
+    ("paged head stride dropped", "w.off[t] = ((page * page_size + off) * A_kv + hk) * (int64_t)d;",
+     "w.off[t] = ((page * page_size + off) * A_kv) * (int64_t)d;", 0),
+    ("paged offset uses page index", "int off = t % page_size;", "int off = (t / page_size) % page_size;", 0),
+    ("bf16 widened with wrong shift", "<< 16;", "<< 15;", 0),
+    ("last head-dim term dropped", "for (int e = 0; e < d; ++e)\n                dot +=", "for (int e = 0; e < d - 1; ++e)\n                dot +=", 0),
+    ("fully masked row not guarded", "if (m == -INFINITY) {", "if (0) {", 0),
+    ("row max taken as first score", "if (s[j] > m)\n            m = s[j];", "if (j == 0)\n            m = s[j];", 0),
+]
+
+BATTERY = r"""
+import sys
+sys.path.insert(0, {root!r})
+import oracle
+from tests import oracle_pins
+orc = oracle.Oracle({lib!r})
+failed = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(orc)
+    except Exception as e:  # a pin that fails or cannot run counts
+        failed.append(pin.__name__)
+print("FAILED_PINS", ",".join(failed))
+"""
+
+
+def _mutate(src, old, new, which):
+    assert old in src, f"mutation anchor not found: {old!r}"
+    if which == 0:
+        return src.replace(old, new)
+    parts = src.split(old)
+    assert len(parts) > which
+    return old.join(parts[:which]) + new + old.join(parts[which:])
+
+
+def test_mutants_fail_a_pin(tmp_path):
+    src = open(oracle.SRC).read()
+    # the unmutated source must pass every pin (control)
+    results = {}
+    for name, old, new, which in [("control", "", "", -1)] + MUTANTS:
+        msrc = src if which == -1 else _mutate(src, old, new, which)
+        c = tmp_path / f"m{len(results)}.c"
+        c.write_text(msrc)
+        lib = str(tmp_path / f"m{len(results)}.so")
+        oracle.build(str(c), lib, werror=False)
+        r = subprocess.run([sys.executable, "-c", BATTERY.format(root=ROOT, lib=lib)],
+                           capture_output=True, text=True, timeout=300, cwd=ROOT)
+        line = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED_PINS")]
+        failed = line[0].split(" ", 1)[1].split(",") if line and line[0].strip() != "FAILED_PINS" else []
+        crashed = r.returncode != 0
+        results[name] = (failed, crashed)
+    assert results["control"] == ([], False), results["control"]
+    undetected = [n for n, (f, crashed) in results.items() if n != "control" and not f and not crashed]
+    for n, (f, crashed) in results.items():
+        print(f"{n:40s} caught by {len(f):2d} pins{' (crashed)' if crashed else ''}: {','.join(f)}")
+    assert not undetected, f"mutants no pin catches: {undetected}"
