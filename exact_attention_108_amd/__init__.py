@@ -1,0 +1,20 @@
+"""MI355X (gfx950) fused exact attention: Python binding of libattn_mi355x.so.
+
+The functions here only marshal arguments (tensor pointers, sizes, the current
+HIP stream) into the C ABI of ``include/attn.h``; every step of the computation
+runs in the library's HIP kernels.  Importing fails if the library has not been
+built (``python -m exact_attention_108_amd.build``): there is no fallback path.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_F32,
+    AttnError,
+    LIB_PATH,
+    attn_abi_version,
+    attn_decode_paged,
+    attn_decode_paged_workspace_bytes,
+    attn_fwd,
+    attn_fwd_varlen,
+    attn_status_string,
+    exported_symbols,
+)

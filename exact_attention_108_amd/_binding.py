@@ -1,0 +1,203 @@
+"""ctypes marshalling for libattn_mi355x.so (argument checks + pointers only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_mi355x.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_108_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ATTN_OK, ATTN_ERR_INVAL, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p)]
+
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, ctypes.POINTER(_Mask), _i, _vp]
+_lib.attn_fwd.restype = _i
+_lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                 ctypes.POINTER(_Mask), _i, _vp]
+_lib.attn_fwd_varlen.restype = _i
+_lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                                   _vp, _sz, _vp]
+_lib.attn_decode_paged.restype = _i
+_lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _vp]
+_lib.attn_decode_paged_workspace_bytes.restype = _sz
+_lib.attn_status_string.argtypes = [_i]
+_lib.attn_status_string.restype = ctypes.c_char_p
+_lib.attn_abi_version.argtypes = []
+_lib.attn_abi_version.restype = _i
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
+        self.status = status
+
+
+def attn_status_string(status: int) -> str:
+    return _lib.attn_status_string(int(status)).decode()
+
+
+def attn_abi_version() -> int:
+    return int(_lib.attn_abi_version())
+
+
+def exported_symbols():
+    """Names of the C entry points this binding resolves (one per header declaration)."""
+    return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
+            "attn_status_string", "attn_abi_version"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must share one device")
+    return dev
+
+
+def _stream(stream, dev):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _mask(q_keep, k_keep):
+    torch = _torch()
+    for t in (q_keep, k_keep):
+        if t is not None and t.dtype != torch.uint8:
+            raise ValueError("keep-masks must be uint8")
+    if q_keep is None and k_keep is None:
+        return None
+    return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep)))
+
+
+def _check(status: int, where: str) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None, k_keep=None, stream=None):
+    """O, LSE of softmax(Q K^T * scale + M) V.  q/o [B,A,S_q,d], k/v [B,A_kv,S_k,d], lse [B,A,S_q] fp32."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, heads, S, d]")
+    B, A, S_q, d = q.shape
+    _, A_kv, S_k, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k, v must be [B, A_kv, S_k, d]")
+    if o.shape != q.shape or o.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("o must match q; k, v must share q's dtype")
+    if lse.shape != (B, A, S_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, A, S_q]")
+    if q_keep is not None and q_keep.shape != (B, S_q):
+        raise ValueError("q_keep must be [B, S_q]")
+    if k_keep is not None and k_keep.shape != (B, S_k):
+        raise ValueError("k_keep must be [B, S_k]")
+    dev = _dev(q, k, v, o, lse, q_keep, k_keep)
+    st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, A, A_kv, S_q, S_k, d, float(scale),
+                       int(bool(causal)), _mask(q_keep, k_keep), _dtype_code(q), _stream(stream, dev))
+    _check(st, "attn_fwd")
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: float, causal: bool = True,
+                    q_keep=None, k_keep=None, stream=None):
+    """Packed varlen prefill.  q/o [A,T,d], k/v [A_kv,T,d], lse [A,T]; cu_seqlens int32 device,
+    cu_seqlens_host the same values on the host (numpy int32)."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
+    A, T, d = q.shape
+    A_kv = k.shape[0]
+    if k.shape[1] != T or k.shape[2] != d or o.shape != q.shape or lse.shape != (A, T):
+        raise ValueError("shape mismatch")
+    if lse.dtype != torch.float32 or o.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("dtype mismatch")
+    cu_host = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    n_seq = cu_host.size - 1
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.numel() != cu_host.size:
+        raise ValueError("cu_seqlens must be int32 [n_seq + 1] matching cu_seqlens_host")
+    for t in (q_keep, k_keep):
+        if t is not None and t.shape != (T,):
+            raise ValueError("keep-masks must be [T]")
+    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep)
+    st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                              cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d, float(scale), int(bool(causal)),
+                              _mask(q_keep, k_keep), _dtype_code(q), _stream(stream, dev))
+    _check(st, "attn_fwd_varlen")
+
+
+def attn_decode_paged_workspace_bytes(B: int, A: int, A_kv: int, d: int, page_size: int, seq_lens_host) -> int:
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if sl.shape != (B,):
+        raise ValueError("seq_lens_host must be [B]")
+    return int(_lib.attn_decode_paged_workspace_bytes(B, A, A_kv, d, page_size, sl.ctypes.data_as(_vp)))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, workspace, *,
+                      scale: float, stream=None):
+    """Paged decode.  q/o [B,A,d]; caches [num_pages, page_size, A_kv, d]; block_table int32 [B, max_pages];
+    seq_lens int32 [B] (device) and seq_lens_host (numpy); workspace a uint8 device tensor of at least
+    attn_decode_paged_workspace_bytes(...) bytes."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
+    B, A, d = q.shape
+    num_pages, page_size, A_kv, dk = k_cache.shape
+    if dk != d or o.shape != q.shape or lse.shape != (B, A) or lse.dtype != torch.float32:
+        raise ValueError("shape mismatch")
+    if o.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("dtype mismatch")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if sl.shape != (B,):
+        raise ValueError("seq_lens_host must be [B]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace)
+    st = _lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                sl.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), B, A, A_kv, d,
+                                block_table.shape[1], num_pages, float(scale), _dtype_code(q),
+                                _ptr(workspace), ws_bytes, _stream(stream, dev))
+    _check(st, "attn_decode_paged")

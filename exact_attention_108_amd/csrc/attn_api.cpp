@@ -1,0 +1,202 @@
+// attn_api.cpp -- the extern "C" boundary of libattn_mi355x.so: argument
+// validation, launch planning and kernel dispatch.  Semantics of every entry
+// point are documented in include/attn.h.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_kernels.h"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+attn_status launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int A, int A_kv, int d_h, float scale, int causal, const attn_mask* mask) {
+  attn::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_keep = mask ? mask->q_keep : nullptr;
+  p.k_keep = mask ? mask->k_keep : nullptr;
+  p.A = A;
+  p.A_kv = A_kv;
+  p.G = A / A_kv;
+  p.d = d_h;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return p;
+}
+
+// dtype / head-dim combinations the kernels are built for
+attn_status check_prefill_support(attn_dtype dtype, int d_h) {
+  if (dtype == ATTN_BF16) return (d_h == 64 || d_h == 128) ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32) return (d_h >= 1 && d_h <= 128) ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+  return ATTN_ERR_INVAL;
+}
+
+}  // namespace
+
+ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int A, int A_kv, int S_q, int S_k, int d_h, float scale,
+                                 int causal, const attn_mask* mask, attn_dtype dtype, void* stream) {
+  if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (S_q > 0 && (!q || !o || !lse)) return ATTN_ERR_INVAL;
+  if (S_k > 0 && (!k || !v)) return ATTN_ERR_INVAL;
+  attn_status sup = check_prefill_support(dtype, d_h);
+  if (sup != ATTN_OK) return sup;
+  if (S_q == 0) return ATTN_OK;
+  const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
+  const long long n_qt = (S_q + rows - 1) / rows;
+  if (n_qt * (long long)A * (long long)B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  // element offsets inside the kernels are size_t; per-(b,h) row counts are int
+  if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask);
+  p.B = B;
+  p.S_q = S_q;
+  p.S_k = S_k;
+  p.n_qt = (int)n_qt;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, false, st) : attn::launch_prefill_f32(p, false, st);
+  return launch_status(e);
+}
+
+ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                        int n_seq, int total_tokens, int A, int A_kv, int d_h, float scale,
+                                        int causal, const attn_mask* mask, attn_dtype dtype, void* stream) {
+  if (n_seq < 0 || total_tokens < 0 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (!cu_seqlens || !cu_seqlens_host) return ATTN_ERR_INVAL;
+  if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seq] != total_tokens) return ATTN_ERR_INVAL;
+  for (int s = 0; s < n_seq; ++s)
+    if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return ATTN_ERR_INVAL;
+  if (total_tokens > 0 && (!q || !k || !v || !o || !lse)) return ATTN_ERR_INVAL;
+  attn_status sup = check_prefill_support(dtype, d_h);
+  if (sup != ATTN_OK) return sup;
+  if (total_tokens == 0) return ATTN_OK;
+  if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
+  long long total_tiles = 0;
+  int max_tiles = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int len = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+    const int nt = (len + rows - 1) / rows;
+    total_tiles += nt;
+    if (nt > max_tiles) max_tiles = nt;
+  }
+  if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask);
+  p.cu_seqlens = cu_seqlens;
+  p.n_seq = n_seq;
+  p.T = total_tokens;
+  p.B = 1;
+  p.n_qt = max_tiles;
+  p.total_tiles = (int)total_tiles;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, true, st) : attn::launch_prefill_f32(p, true, st);
+  return launch_status(e);
+}
+
+namespace {
+
+attn_status check_decode(int B, int A, int A_kv, int d_h, int page_size, const int32_t* seq_lens_host,
+                         int max_pages, bool check_pages) {
+  if (B < 1 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0 || page_size < 1) return ATTN_ERR_INVAL;
+  if (!seq_lens_host) return ATTN_ERR_INVAL;
+  for (int b = 0; b < B; ++b) {
+    if (seq_lens_host[b] < 0) return ATTN_ERR_INVAL;
+    if (check_pages && (long long)seq_lens_host[b] > (long long)max_pages * page_size) return ATTN_ERR_INVAL;
+  }
+  if (d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
+  if (page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (A / A_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_EXPORT size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int page_size,
+                                                     const int32_t* seq_lens_host) {
+  if (check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, 0, false) != ATTN_OK) return 0;
+  const attn::DecodePlan plan = attn::plan_decode(B, A_kv, page_size, seq_lens_host);
+  return attn::decode_workspace_bytes(B, A, d_h, plan);
+}
+
+ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                          int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                          float scale, attn_dtype dtype, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
+  attn_status st = check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, max_pages, true);
+  if (st != ATTN_OK) return st;
+  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (!q || !o || !lse || !seq_lens) return ATTN_ERR_INVAL;
+  long long total_tokens = 0;
+  for (int b = 0; b < B; ++b) total_tokens += seq_lens_host[b];
+  if (total_tokens > 0 && (!k_cache || !v_cache || !block_table || num_pages < 1)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const attn::DecodePlan plan = attn::plan_decode(B, A_kv, page_size, seq_lens_host);
+  const size_t need = attn::decode_workspace_bytes(B, A, d_h, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  long long units = 0;
+  for (int b = 0; b < B; ++b) units += (seq_lens_host[b] + plan.split_tokens - 1) / plan.split_tokens;
+  if (units * A_kv > INT_MAX || (long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  attn::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.o = o;
+  p.lse = lse;
+  const size_t slots = (size_t)B * (size_t)plan.n_split * (size_t)A;
+  const size_t o_bytes = ((slots * (size_t)d_h * 4) + 255) / 256 * 256;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + o_bytes);
+  p.B = B;
+  p.A = A;
+  p.A_kv = A_kv;
+  p.G = A / A_kv;
+  p.d = d_h;
+  p.page_size = page_size;
+  p.max_pages = max_pages;
+  p.split_tokens = plan.split_tokens;
+  p.n_split = plan.n_split;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return launch_status(attn::launch_decode_bf16(p, (int)units, (hipStream_t)stream));
+}
+
+ATTN_EXPORT const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVAL: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+ATTN_EXPORT int attn_abi_version(void) { return kAbiVersion; }

@@ -1,0 +1,71 @@
+// attn_device.h -- device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) (v_log_f32).
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane l ^ 32, combined with this lane's: v_permlane32_swap
+// exchanges the upper half of the first operand with the lower half of the
+// second, so with both operands = x the pair is {x[l], x[l ^ 32]} in every lane.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i & 3) of the 4-element chunk addressed by lane
+// 4*r + (i >> 2), for r = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 concat(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// LDS row swizzle over 16-byte chunks (chunk c of row `row` lives at chunk
+// c ^ sigma(row)).  sigma is chosen so that (a) 16 consecutive rows read at one
+// logical chunk hit 16 distinct bank groups, and (b) 4 consecutive rows (row %
+// 4 == 0 at the first) x 4 consecutive chunks (first % 4 == 0) also do -- the
+// two access shapes of the K-operand reads and the transposing V reads.
+template <int D>
+__device__ __forceinline__ int lds_chunk(int row, int c) {
+  if constexpr (D == 128) {
+    return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  } else {
+    static_assert(D == 64, "head dim 64 or 128");
+    return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  }
+}
+
+}  // namespace attn

@@ -1,0 +1,113 @@
+// attn_rowblock.h -- which query rows (and which K/V) a prefill workgroup owns.
+#pragma once
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+
+struct RowBlock {
+  const char* q;   // row 0 of this (sequence, head); rows are d elements apart
+  const char* k;   // key 0 of the KV head
+  const char* v;
+  char* o;
+  float* lse;
+  const uint8_t* q_keep;  // or null
+  const uint8_t* k_keep;  // or null
+  int S_q, S_k;
+  int q0;                 // first query row of this workgroup
+};
+
+// Dense batch: query tile index descending (heaviest causal tiles first),
+// then batch*head.
+template <int kRows>
+__device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_bytes) {
+  const int lin = blockIdx.x;
+  const int bh_n = p.A * p.B;
+  const int qt = p.n_qt - 1 - lin / bh_n;
+  const int bh = lin % bh_n;
+  const int h = bh % p.A, b = bh / p.A;
+  const int hk = h / p.G;
+  RowBlock r;
+  const size_t qoff = (size_t)(b * p.A + h) * p.S_q;
+  const size_t koff = (size_t)(b * p.A_kv + hk) * p.S_k;
+  r.q = (const char*)p.q + qoff * row_bytes;
+  r.o = (char*)p.o + qoff * row_bytes;
+  r.lse = p.lse + qoff;
+  r.k = (const char*)p.k + koff * row_bytes;
+  r.v = (const char*)p.v + koff * row_bytes;
+  r.q_keep = p.q_keep ? p.q_keep + (size_t)b * p.S_q : nullptr;
+  r.k_keep = p.k_keep ? p.k_keep + (size_t)b * p.S_k : nullptr;
+  r.S_q = p.S_q;
+  r.S_k = p.S_k;
+  r.q0 = qt * kRows;
+  return r;
+}
+
+// Wave-wide sum of an int.
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Packed varlen: workgroups ordered by query-tile index descending across all
+// sequences (tile t of any sequence sees about t+1 key tiles when causal),
+// then sequence, then head.  C(t) = A * sum_s max(0, n_s - t) counts the
+// workgroups whose tile index is >= t; a binary search finds this workgroup's
+// tile index, a ballot finds its sequence.
+template <int kRows>
+__device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, RowBlock& r) {
+  const int lin = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  auto ntiles = [&](int s) -> int {
+    int len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
+    return (len + kRows - 1) / kRows;
+  };
+  auto count_ge = [&](int t) -> int {  // workgroups (per head) with tile index >= t
+    int c = 0;
+    for (int s = lane; s < p.n_seq; s += 64) c += max(0, ntiles(s) - t);
+    return wave_sum(c);
+  };
+  const int per_head = lin / p.A;  // rank among tiles, heaviest first
+  const int h = lin % p.A;
+  // largest t with count_ge(t) > per_head
+  int lo = 0, hi = p.n_qt;  // count_ge(lo) > per_head, count_ge(hi) == 0
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (count_ge(mid) > per_head) lo = mid; else hi = mid;
+  }
+  const int t = lo;
+  int k = per_head - count_ge(t + 1);  // k-th sequence (in order) with n_s > t
+  int seq = -1;
+  for (int base = 0; base < p.n_seq && seq < 0; base += 64) {
+    int s = base + lane;
+    bool has = s < p.n_seq && ntiles(s) > t;
+    uint64_t m = __ballot(has);
+    int c = __popcll(m);
+    if (k < c) {
+      uint64_t below = m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+      bool mine = has && __popcll(below) == k;
+      uint64_t w = __ballot(mine);
+      seq = base + __ffsll((long long)w) - 1;
+    } else {
+      k -= c;
+    }
+  }
+  if (seq < 0) return false;
+  const int start = p.cu_seqlens[seq];
+  const int len = p.cu_seqlens[seq + 1] - start;
+  const int hk = h / p.G;
+  r.q = (const char*)p.q + ((size_t)h * p.T + start) * row_bytes;
+  r.o = (char*)p.o + ((size_t)h * p.T + start) * row_bytes;
+  r.lse = p.lse + (size_t)h * p.T + start;
+  r.k = (const char*)p.k + ((size_t)hk * p.T + start) * row_bytes;
+  r.v = (const char*)p.v + ((size_t)hk * p.T + start) * row_bytes;
+  r.q_keep = p.q_keep ? p.q_keep + start : nullptr;
+  r.k_keep = p.k_keep ? p.k_keep + start : nullptr;
+  r.S_q = len;
+  r.S_k = len;
+  r.q0 = t * kRows;
+  return true;
+}
+
+}  // namespace attn

@@ -1,0 +1,147 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused exact-attention library
+ *           (libattn_mi355x.so).
+ *
+ * Operation (page "Attention Kernel", section "问题与成本"):
+ *
+ *     P = softmax(Q K^T * scale + M),   O = P V,   LSE_i = ln sum_j exp(s_ij)
+ *
+ * computed without writing the S_q x S_k score matrix anywhere: K/V tiles
+ * stream through on-chip memory against a resident Q tile and the running
+ * (max, normaliser, unnormalised output) state of every query row is
+ * rescaled as each tile arrives (page "Attention 算子加速史", sections 1.1-1.3
+ * and 2.1-2.2; page "Attention Kernel", section "Online softmax").
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library neither allocates nor frees memory and keeps no global state.
+ *     Pointers named *_host are HOST pointers read synchronously during the
+ *     call.  Everything is contiguous row-major.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise.  Inputs are read-only; o/lse are fully
+ *     overwritten (including masked rows) and must not alias the inputs.
+ *   - dtype ATTN_BF16: q/k/v/o hold bfloat16 (uint16 bits); products are
+ *     accumulated in fp32; o is rounded once to bf16 (round-to-nearest-even).
+ *     ATTN_F32: q/k/v/o are fp32.  lse is always fp32, natural log.
+ *   - GQA: query head h reads KV head h / (A / A_kv) (contiguous groups; page
+ *     "Attention Kernel", section "问题与成本", GQA paragraph).
+ *   - Mask M_ij in {0, -inf} only.  M_ij = -inf when: causal and
+ *     j > i + (S_k - S_q) (bottom-right alignment), q_keep[i] == 0, or
+ *     k_keep[j] == 0.  A row with every key masked (including S_k == 0)
+ *     returns O = 0 and LSE = -inf (page "Attention Kernel", section
+ *     "Online softmax", fully-masked-row contract), never NaN.
+ *   - scale must be finite and > 0.  Inputs must be finite.
+ *   - Errors are reported before any launch: ATTN_ERR_INVAL for bad
+ *     arguments (NULL required pointer, negative size, A % A_kv != 0,
+ *     scale not finite and positive, inconsistent lengths, workspace too
+ *     small), ATTN_ERR_UNSUPPORTED for a valid request outside the built
+ *     kernels (see each entry point), ATTN_ERR_LAUNCH when the runtime
+ *     rejects a launch.  Device-side contract violations (a block-table
+ *     entry outside [0, num_pages), cu_seqlens that differ from
+ *     cu_seqlens_host) are the caller's responsibility.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVAL = 1,
+    ATTN_ERR_UNSUPPORTED = 2,
+    ATTN_ERR_LAUNCH = 3
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Optional keep-masks (uint8, 1 = keep, 0 = mask to -inf); either may be NULL.
+ * Layout: attn_fwd q_keep [B, S_q], k_keep [B, S_k]; attn_fwd_varlen [T]. */
+typedef struct {
+    const uint8_t *q_keep;
+    const uint8_t *k_keep;
+} attn_mask;
+
+/*
+ * Batched prefill attention (page "Attention Kernel", section "问题与成本";
+ * causal tile skipping and the saved log-sum-exp: section "FlashAttention 的
+ * 稳定基础"; outer loop over query tiles, inner over key/value tiles with a
+ * single deferred division: page "Attention 算子加速史", sections 2.1-2.2).
+ *
+ *   q, o : [B, A, S_q, d_h]        k, v : [B, A_kv, S_k, d_h]
+ *   lse  : [B, A, S_q] fp32        mask : NULL or keep-masks as above
+ *
+ * Supported: bf16 with d_h in {64, 128}; fp32 with 1 <= d_h <= 128.
+ * B, A, A_kv >= 1; S_q, S_k >= 0.
+ */
+attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int A, int A_kv, int S_q, int S_k, int d_h, float scale,
+                     int causal, const attn_mask *mask, attn_dtype dtype, void *stream);
+
+/*
+ * Packed variable-length prefill (page "Attention Kernel", section
+ * "Paged 与 ragged KV", ragged batches described by cumulative lengths).
+ * Sequence s occupies tokens [cu_seqlens[s], cu_seqlens[s+1]); a query only
+ * sees keys of its own sequence, and causal compares positions within it.
+ *
+ *   q, o : [A, T, d_h]      k, v : [A_kv, T, d_h]      lse : [A, T]
+ *   cu_seqlens      : device int32 [n_seq + 1], cu[0] = 0, non-decreasing,
+ *                     cu[n_seq] = T (= total_tokens); empty sequences allowed
+ *   cu_seqlens_host : host copy of the same values (used for launch planning)
+ *   mask            : NULL or q_keep [T], k_keep [T]
+ *
+ * Supported: as attn_fwd.
+ */
+attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                            int n_seq, int total_tokens, int A, int A_kv, int d_h, float scale,
+                            int causal, const attn_mask *mask, attn_dtype dtype, void *stream);
+
+/*
+ * Single-query decode over a paged KV cache, split along the KV length and
+ * merged by log-sum-exp (page "Attention Kernel", section "Paged 与 ragged
+ * KV": token t of a sequence lives in physical page block_table[t / page_size]
+ * at offset t % page_size; page "Attention 算子加速史", section 4.2: each
+ * split emits a partial output plus its LSE and a reduction merges them with
+ * the two-state rule of page "Attention Kernel", section "Online softmax").
+ *
+ *   q, o        : [B, A, d_h]            lse : [B, A] fp32
+ *   k_cache,
+ *   v_cache     : [num_pages, page_size, A_kv, d_h]
+ *   block_table : device int32 [B, max_pages]; entries past
+ *                 ceil(seq_lens[b] / page_size) are never read
+ *   seq_lens    : device int32 [B]; seq_lens_host: host copy (split planning)
+ *   workspace   : device buffer of at least
+ *                 attn_decode_paged_workspace_bytes(...) bytes, 256-byte
+ *                 aligned; its contents on entry are ignored
+ *
+ * The split boundaries depend only on seq_lens, so the result does not
+ * depend on which physical pages the block table names.
+ * Supported: bf16, d_h in {64, 128}, page_size a multiple of 16.
+ */
+attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              const int32_t *seq_lens_host, int page_size, void *o, float *lse,
+                              int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                              float scale, attn_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_decode_paged needs for these lengths (0 on bad input). */
+size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int page_size,
+                                         const int32_t *seq_lens_host);
+
+/* Static text for a status code. */
+const char *attn_status_string(attn_status s);
+
+/* ABI version of this header (incremented on incompatible change). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,190 @@
+"""GPU parity: prefill kernels (dense, GQA, causal, masks, varlen) vs the fp64 oracle.
+
+Small cases are compared element by element over every row; the full-size
+workloads are compared on sampled rows plus properties that hold at any size.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import exact_attention_108_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def run_dense(ea, p, q_keep=None, k_keep=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, p.dtype), gu.dev(p.k, p.dtype), gu.dev(p.v, p.dtype)
+    o = gu.empty_out(q.shape, p.dtype)
+    lse = t.empty((p.B, p.A, p.S_q), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    qk = None if q_keep is None else gu.dev(q_keep, "u8")
+    kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+DENSE_CASES = [
+    # B, A, A_kv, S_q, S_k, d, causal
+    (1, 1, 1, 1, 1, 128, False),
+    (1, 2, 1, 17, 17, 128, True),
+    (2, 4, 4, 64, 64, 128, True),
+    (1, 2, 2, 65, 65, 128, True),
+    (1, 2, 2, 127, 129, 128, True),
+    (1, 2, 2, 129, 127, 128, True),
+    (2, 8, 2, 200, 200, 128, True),
+    (1, 4, 1, 300, 300, 64, True),
+    (1, 3, 3, 128, 1000, 64, False),
+    (1, 2, 2, 1000, 1000, 128, False),
+    (2, 4, 2, 257, 384, 64, True),
+    (1, 1, 1, 1, 700, 128, True),
+    (1, 2, 1, 5, 0, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n"))
+def test_dense_bf16_small(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal = case
+    _say("dense bf16", case)
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=hash(case) % 10000)
+    o, lse = run_dense(ea, p)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal)
+    gu.check(o, lse, o_ref, l_ref, "bf16", str(case))
+
+
+@pytest.mark.parametrize("case", [(1, 1, 1, 128, 128, 64, False), (2, 4, 2, 33, 70, 128, True),
+                                  (1, 2, 2, 100, 100, 37, False), (1, 2, 1, 48, 16, 64, True)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_dense_f32_small(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal = case
+    _say("dense f32", case)
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="f32", causal=causal, seed=7 + S_q)
+    o, lse = run_dense(ea, p)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="f32", scale=p.scale, causal=causal)
+    gu.check(o, lse, o_ref, l_ref, "f32", str(case))
+
+
+def test_config1_fp32(ea, orc):
+    _say("config 1 fp32 full")
+    p = gen.make_config(1)
+    o, lse = run_dense(ea, p)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="f32", scale=p.scale, causal=False)
+    gu.check(o, lse, o_ref, l_ref, "f32", "config1")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_keep_masks(ea, orc, dtype):
+    _say("keep masks", dtype)
+    p = gen.make_dense(2, 4, 2, 150, 190, 128 if dtype == "bf16" else 64, dtype=dtype, causal=True, seed=31,
+                       q_masked=30, k_masked=60)
+    # one batch row with every key masked
+    kk = p.k_keep.copy()
+    kk[1, :] = 0
+    o, lse = run_dense(ea, p, q_keep=p.q_keep, k_keep=kk)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype=dtype, scale=p.scale, causal=True, q_keep=p.q_keep,
+                                k_keep=kk)
+    assert np.all(np.isneginf(l_ref[1]))
+    gu.check(o, lse, o_ref, l_ref, dtype, "keep masks")
+
+
+def _sample_rows(rng, B, A, S_q, n):
+    ids = rng.choice(B * A * S_q, size=n, replace=False)
+    # always include the first and last row of a few heads
+    extra = [(b * A + h) * S_q + i for b in range(B) for h in range(0, A, max(1, A // 4)) for i in (0, S_q - 1)]
+    return np.unique(np.concatenate([ids, np.array(extra, np.int64)]))
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_configs(ea, orc, cfg):
+    _say("config", cfg, "full size (sampled rows)")
+    p = gen.make_config(cfg)
+    o, lse = run_dense(ea, p)
+    rng = np.random.default_rng(cfg)
+    rows = _sample_rows(rng, p.B, p.A, p.S_q, 1500 if cfg == 2 else 600)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True, rows=rows)
+    o_flat = o.reshape(-1, p.d)[rows]
+    l_flat = lse.reshape(-1)[rows]
+    stats = gu.check(o_flat, l_flat, o_ref, l_ref, "bf16", f"config{cfg}")
+    _say("config", cfg, stats)
+    # any size: outputs finite, every LSE finite (no row is masked)
+    assert np.all(np.isfinite(lse)) and np.all(np.isfinite(o))
+    # causal row 0 sees only key 0: O equals V[b, h_kv, 0] bit for bit
+    vf = gen.as_f32(p.v, "bf16").astype(np.float64)
+    G = p.A // p.A_kv
+    for b in range(p.B):
+        for h in range(p.A):
+            assert np.array_equal(o[b, h, 0], vf[b, h // G, 0]), (b, h)
+
+
+def run_varlen(ea, p, k_keep=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, p.dtype), gu.dev(p.k, p.dtype), gu.dev(p.v, p.dtype)
+    o = gu.empty_out(q.shape, p.dtype)
+    lse = t.empty((p.A, p.T), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    cu = gu.dev(p.cu_seqlens, "i32")
+    qk = None if p.q_keep is None else gu.dev(p.q_keep, "u8")
+    kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    ea.attn_fwd_varlen(q, k, v, o, lse, cu, p.cu_seqlens, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_varlen_small(ea, orc, dtype, d):
+    lens = [1, 0, 130, 17, 256, 0, 64, 300, 5]
+    _say("varlen small", dtype, d, lens)
+    p = gen.make_varlen(lens, 4, 2, d, dtype=dtype, causal=True, seed=41, q_mask_frac=0.05, k_mask_frac=0.1)
+    o, lse = run_varlen(ea, p, k_keep=p.k_keep)
+    o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype=dtype, scale=p.scale, causal=True,
+                                       q_keep=p.q_keep, k_keep=p.k_keep)
+    gu.check(o, lse, o_ref, l_ref, dtype, "varlen small")
+
+
+def test_varlen_noncausal_small(ea, orc):
+    lens = [70, 129, 3]
+    _say("varlen non-causal", lens)
+    p = gen.make_varlen(lens, 2, 1, 128, dtype="bf16", causal=False, seed=43)
+    o, lse = run_varlen(ea, p)
+    o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=False)
+    gu.check(o, lse, o_ref, l_ref, "bf16", "varlen non-causal")
+
+
+def test_config5_full(ea, orc):
+    _say("config 5 varlen full size (sampled rows)")
+    p = gen.make_config(5)
+    o, lse = run_varlen(ea, p)
+    # every query row the keep-mask drops: exactly zero output and -inf LSE, in every head
+    dead = p.q_keep == 0
+    assert dead.sum() == round(0.05 * p.T)
+    assert np.all(o[:, dead] == 0) and np.all(np.isneginf(lse[:, dead]))
+    assert np.all(np.isfinite(lse[:, ~dead]))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(p.A * p.T, size=1500, replace=False),
+                                     np.nonzero(np.tile(dead, p.A))[0][:50]]))
+    o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=True,
+                                       q_keep=p.q_keep, rows=rows)
+    stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "config5")
+    _say("config 5", stats)
