@@ -5,6 +5,12 @@ import ctypes
 import os
 
 import numpy as np
+# torch first: its wheel carries its own libamdhip64.so.7.  Loading torch before
+# the library makes the library's libamdhip64.so.7 dependency resolve to that
+# same, already-loaded runtime, so device pointers and streams handed over from
+# torch belong to the runtime that launches the kernels.  Loading the library
+# first would bring in a second HIP runtime for torch.
+import torch  # noqa: F401
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_mi355x.so")
 
