@@ -27,9 +27,9 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
+    out = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -40,17 +40,20 @@ def _compile(src: str) -> str:
     return out
 
 
-def build() -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(lib: str = LIB, extra_flags=()) -> str:
+    """Compile and link; ``lib``/``extra_flags`` select another output and
+    additional hipcc flags (e.g. -D tuning switches) for side-by-side builds."""
+    obj_dir = OBJ if lib == LIB else os.path.join(os.path.dirname(os.path.abspath(lib)), "_build")
+    os.makedirs(obj_dir, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra_flags), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

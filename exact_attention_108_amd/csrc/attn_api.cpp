@@ -136,8 +136,8 @@ attn_status check_decode(int B, int A, int A_kv, int d_h, int page_size, const i
 ATTN_EXPORT size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int page_size,
                                                      const int32_t* seq_lens_host) {
   if (check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, 0, false) != ATTN_OK) return 0;
-  const attn::DecodePlan plan = attn::plan_decode(B, A_kv, page_size, seq_lens_host);
-  return attn::decode_workspace_bytes(B, A, d_h, plan);
+  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
+  return attn::decode_workspace_bytes(A, d_h, plan);
 }
 
 ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -156,13 +156,11 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   for (int b = 0; b < B; ++b) total_tokens += seq_lens_host[b];
   if (total_tokens > 0 && (!k_cache || !v_cache || !block_table || num_pages < 1)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const attn::DecodePlan plan = attn::plan_decode(B, A_kv, page_size, seq_lens_host);
-  const size_t need = attn::decode_workspace_bytes(B, A, d_h, plan);
+  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
+  const size_t need = attn::decode_workspace_bytes(A, d_h, plan);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
     return ATTN_ERR_INVAL;
-  long long units = 0;
-  for (int b = 0; b < B; ++b) units += (seq_lens_host[b] + plan.split_tokens - 1) / plan.split_tokens;
-  if (units * A_kv > INT_MAX || (long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   attn::DecodeParams p{};
   p.q = q;
   p.k_cache = k_cache;
@@ -171,10 +169,8 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   p.seq_lens = seq_lens;
   p.o = o;
   p.lse = lse;
-  const size_t slots = (size_t)B * (size_t)plan.n_split * (size_t)A;
-  const size_t o_bytes = ((slots * (size_t)d_h * 4) + 255) / 256 * 256;
   p.part_o = (float*)workspace;
-  p.part_lse = (float*)((char*)workspace + o_bytes);
+  p.part_lse = (float*)((char*)workspace + attn::decode_workspace_lse_offset(A, d_h, plan));
   p.B = B;
   p.A = A;
   p.A_kv = A_kv;
@@ -182,11 +178,10 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   p.d = d_h;
   p.page_size = page_size;
   p.max_pages = max_pages;
-  p.split_tokens = plan.split_tokens;
-  p.n_split = plan.n_split;
+  p.n_chunks = plan.n_chunks;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  return launch_status(attn::launch_decode_bf16(p, (int)units, (hipStream_t)stream));
+  return launch_status(attn::launch_decode_bf16(p, (hipStream_t)stream));
 }
 
 ATTN_EXPORT const char* attn_status_string(attn_status s) {

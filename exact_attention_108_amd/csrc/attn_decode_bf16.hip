@@ -6,35 +6,28 @@
 // at offset t % page_size; a cache row is [page][offset][kv head][d].
 //
 // Split-KV (page "Attention 算子加速史", section 4.2; page "快速Transformer
-// （续）", section "Stream-K", split-K with a fix-up pass): every sequence's
-// keys are cut into splits of `split_tokens`; one wavefront handles one
-// (sequence, split, KV head) unit for all G = A / A_kv query heads that share
-// the KV head (page "Attention Kernel", GQA paragraph), and writes a partial
-// output normalised within its split plus the split's log-sum-exp.  The merge
-// kernel combines the partials of a (sequence, head) with the two-state rule
-// of page "Attention Kernel", section "Online softmax":
+// （续）", section "Stream-K"): the KV length is divided among workgroups and
+// each emits a partial output normalised within its range plus the range's
+// log-sum-exp; a second kernel merges the partials of a (sequence, head) with
+// the two-state rule of page "Attention Kernel", section "Online softmax":
 //     lse = log sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) O_s.
-// Splits depend only on seq_lens, so the result is the same for any choice of
-// physical pages.
+// The ranges depend only on seq_lens (and the device's CU count), so the
+// result is the same for any choice of physical pages.  The G = A / A_kv query
+// heads that share a KV head (page "Attention Kernel", GQA paragraph) are
+// processed together, so each KV byte is read once.
 //
-// Matrix-core mapping (v_mfma_f32_16x16x32_bf16), per 32-token chunk:
-//   S^T[token, head] = K_chunk . Q^T     (A = K straight from global memory:
-//                                         lane holds 8 consecutive d of one
-//                                         token row; B = Q^T, heads >= G are 0)
-//   O^T[d, head]    += V^T . P^T         (B = P^T from the S^T registers;
-//                                         A = V^T from the transposing LDS
-//                                         read of the row-major V chunk)
 // Decode is bound by HBM bandwidth (each KV byte feeds ~4 flops, page
-// "Attention Kernel", section "Prefill 与 decode 是两种 kernel"), so the
-// design goal is many 16-byte loads in flight per CU; the matrix cores only
-// keep the arithmetic off the critical path.
+// "Attention Kernel", section "Prefill 与 decode 是两种 kernel").  The design
+// goal is long, contiguous, row-sized reads with many in flight per CU; the
+// matrix cores only keep the arithmetic off the critical path.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
 namespace attn {
 namespace {
 
-constexpr int kChunk = 32;  // tokens per inner step (two 16-token blocks)
+constexpr int kChunk = 16;       // tokens per inner step (one MFMA M block)
+constexpr int kWavesPerGroup = 4;  // waves per workgroup, each with its own KV heads
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -45,211 +38,335 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
-  constexpr int NCH = D / 8;
-  constexpr int KSTEPS = D / 32;  // k-steps of the 16x16x32 QK MFMA
-  constexpr int MB = D / 16;      // 16-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * D];
+// LDS swizzle of the 16-byte chunks of a token row (row = token % 16): keeps
+// both the K-operand reads (16 tokens, one chunk) and the transposing V reads
+// (4 tokens x two adjacent chunks per 16 lanes) free of bank conflicts.
+__device__ __forceinline__ int tok_swz(int tok) { return ((tok & 7) << 1) | ((tok >> 3) & 1); }
 
-  const int lane = threadIdx.x;
+// Work split (Stream-K, page "快速Transformer（续）", section Stream-K): the
+// sequences' 16-token chunks are concatenated into one list of n_chunks and
+// workgroup i of n_wg takes chunks [i*n_chunks/n_wg, (i+1)*n_chunks/n_wg), so
+// every workgroup streams the same amount of KV whatever the length mix.  A
+// range may cover the tail of one sequence, whole sequences and the head of
+// another; the workgroup emits one partial per (workgroup i, sequence b) it
+// touches, in slot i + b (the touched pairs form a staircase in (i, b), so
+// i + b is unique), and the merge kernel combines a sequence's partials.
+//
+// Wave w of the workgroup owns KV heads 4*HPW*blockIdx.y + HPW*w + [0, HPW).
+// A 16-token chunk of the wave's heads is copied global -> LDS with
+// global_load_lds (rows of HPW*d contiguous elements, so each load
+// instruction reads whole rows), then
+//   S^T[token, n] = sum_hh K_hh . Q^T_hh     (16x16x32 MFMA; column n = query
+//                                             head n of the wave; block
+//                                             diagonal: columns of other KV
+//                                             heads see a zero B operand)
+//   O^T[d, n]    += sum_hh V_hh^T . P^T_hh   (16x16x16 MFMA, same masking)
+template <int D, int HPW>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(DecodeParams p) {
+  constexpr int RC = HPW * D / 8;            // 16-byte chunks per token row
+  constexpr int TOK_PER_LD = 64 / RC;        // tokens per load instruction
+  constexpr int N_LD = kChunk / TOK_PER_LD;  // load instructions per chunk (K or V)
+  constexpr int KSTEPS = D / 32;             // QK k-steps per head
+  constexpr int MB = D / 16;                 // 16-row blocks of O^T
+  constexpr int WAVE_LDS = 2 * kChunk * RC * 16;  // bytes: K then V
+  static_assert(64 % RC == 0 && kChunk % TOK_PER_LD == 0, "row split");
+  __shared__ __attribute__((aligned(16))) char smem[kWavesPerGroup * WAVE_LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int g = blockIdx.x % p.A_kv;
-  int unit = blockIdx.x / p.A_kv;
-
-  // ---- locate (sequence b, split s) of this unit: units are numbered
-  // sequence-major, sequence b owning ceil(len_b / split_tokens) of them.
-  const int C = p.split_tokens;
-  int b = -1, s = 0, len = 0;
-  for (int base = 0; base < p.B; base += 64) {
-    const int bb = base + lane;
-    const int lb = bb < p.B ? p.seq_lens[bb] : 0;
-    const int ns = (lb + C - 1) / C;
-    const int incl = wave_incl_scan(ns, lane);
-    const int total = __shfl(incl, 63);
-    if (unit < total) {
-      const uint64_t m = __ballot(incl > unit);
-      const int src = __ffsll((long long)m) - 1;
-      b = base + src;
-      s = unit - (__shfl(incl, src) - __shfl(ns, src));
-      len = __shfl(lb, src);
-      break;
-    }
-    unit -= total;
-  }
-  if (b < 0) return;
-
   const int G = p.G;
-  const int t_begin = s * C;
-  const int t_end = min(len, t_begin + C);
+  const int kv0 = (blockIdx.y * kWavesPerGroup + wave) * HPW;  // first KV head of this wave
+  if (kv0 >= p.A_kv) return;  // no barrier below: waves are independent
+  const int nh = min(HPW, p.A_kv - kv0);  // KV heads of this wave
+  char* sK = smem + wave * WAVE_LDS;
+  char* sV = sK + kChunk * RC * 16;
 
-  // ---- Q^T operand: lane holds Q[head l16][32t + 8 grp .. +7]; heads >= G are 0
-  const uint16_t* qb = (const uint16_t*)p.q + ((size_t)b * p.A + (size_t)g * G) * D;
-  bf16x8 qf[KSTEPS];
-#pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    qf[t] = l16 < G ? *(const bf16x8*)(qb + (size_t)l16 * D + 32 * t + 8 * grp) : bf16x8{};
+  // ---- this workgroup's chunk range
+  const long long NC = p.n_chunks;
+  const int wg = blockIdx.x;
+  const long long c_lo = (long long)wg * NC / p.n_wg;
+  const long long c_hi = (long long)(wg + 1) * NC / p.n_wg;
+  if (c_lo >= c_hi) return;
+
+  // ---- sequence holding chunk c_lo: prefix sums of ceil(len / 16), 64 at a time
+  int b = -1, len = 0;
+  long long cex = 0;  // chunks of all sequences before b
+  {
+    long long base_chunks = 0;
+    for (int base = 0; base < p.B; base += 64) {
+      const int bb = base + lane;
+      const int lb = bb < p.B ? p.seq_lens[bb] : 0;
+      const int nc = (lb + kChunk - 1) / kChunk;
+      const long long incl = base_chunks + wave_incl_scan(nc, lane);
+      const long long total = __shfl(incl, 63);
+      if (c_lo < total) {
+        const uint64_t m = __ballot(incl > c_lo);
+        const int src = __ffsll((long long)m) - 1;
+        b = base + src;
+        len = __shfl(lb, src);
+        cex = __shfl(incl, src) - __shfl(nc, src);
+        break;
+      }
+      base_chunks = total;
+    }
   }
+  if (b < 0) return;  // unreachable when n_chunks matches seq_lens
 
+  const int ps = p.page_size;
   const uint16_t* kc = (const uint16_t*)p.k_cache;
   const uint16_t* vc = (const uint16_t*)p.v_cache;
-  const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-  const size_t row_stride = (size_t)p.A_kv * D;  // elements between tokens of a page
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{};
+  const size_t tok_stride = (size_t)p.A_kv * D;  // elements between tokens of a page
+  // this lane's slot in a load instruction: token row (ld_tok), head, physical chunk
+  const int ld_tok = lane / RC, ld_pc = lane % RC;
+  const int ld_hh = min(ld_pc / (D / 8), nh - 1);
+  const int ld_c = ld_pc % (D / 8);
+  const int n_col = l16;
+  const int hh_col = n_col / G;  // which of the wave's KV heads this column belongs to
+  const bool col_live = n_col < nh * G;
   const float cs = p.scale_log2;
+  const int tr_r = l16 >> 2, tr_q = l16 & 3;
 
-  for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
-    // ---- gather: lane reads token (c0 + 16 tb + l16), d chunk (4 t + grp)
-    uint4 kr[2][KSTEPS], vr[2][KSTEPS];
+  int k = (int)(c_lo - cex);     // chunk index within sequence b
+  long long remaining = c_hi - c_lo;
+  while (true) {
+    const int nch = (len + kChunk - 1) / kChunk;
+    const int k_end = (int)min((long long)nch, k + remaining);
+    const int t_begin = k * kChunk, t_end = min(len, k_end * kChunk);
+
+    // ---- Q^T operand: column n = query head kv0*G + n (n < nh*G), 8 d per lane
+    const uint16_t* qb = (const uint16_t*)p.q + ((size_t)b * p.A + (size_t)kv0 * G) * D;
+    bf16x8 qf[KSTEPS];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int tok = c0 + 16 * tb + l16;
-      if (tok < t_end) {
-        const int page = bt[tok / p.page_size];
-        const size_t row = ((size_t)page * p.page_size + (tok % p.page_size)) * row_stride + (size_t)g * D;
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = col_live ? *(const bf16x8*)(qb + (size_t)n_col * D + 32 * t + 8 * grp) : bf16x8{};
+    }
+    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+    const int last_page = (t_end - 1) / ps;
+    int pbase = t_begin / ps;  // lane i holds block-table entry pbase + i
+    int page_of_lane = pbase + lane <= last_page ? bt[pbase + lane] : 0;
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{};
+
+    for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
+      // a 16-token chunk lies inside one page (page_size is a multiple of 16)
+      int pidx = c0 / ps - pbase;
+      if (pidx >= 64) {
+        pbase += 64;
+        pidx -= 64;
+        page_of_lane = pbase + lane <= last_page ? bt[pbase + lane] : 0;
+      }
+      const int page = __builtin_amdgcn_readlane(page_of_lane, pidx);
+      const size_t page_row0 = ((size_t)page * ps + (c0 % ps)) * tok_stride + (size_t)kv0 * D;
+      const int n_valid = min(kChunk, t_end - c0);
+      // ---- global -> LDS: instruction i fills token rows i*TOK_PER_LD + [0, TOK_PER_LD);
+      //      lane slot (ld_tok, ld_pc) holds logical chunk ld_c ^ swz of head ld_hh.
+      //      Rows past the end re-read the last valid row (finite, weight 0).
+#pragma unroll
+      for (int i = 0; i < N_LD; ++i) {
+        const int tl = i * TOK_PER_LD + ld_tok;
+        const int tr = min(tl, n_valid - 1);
+        const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
+        const size_t e = page_row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)(kc + e),
+                                         (__attribute__((address_space(3))) void*)(sK + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vc + e),
+                                         (__attribute__((address_space(3))) void*)(sV + i * 1024), 16, 0, 0);
+      }
+      // The copies land in LDS asynchronously (tracked by vmcnt).  Wait for all
+      // of them explicitly: the compiler's own wait for LDS written this way is
+      // not placed before every read.  The empty asm keeps LDS accesses from
+      // moving across the wait.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      asm volatile("" ::: "memory");
+      // ---- S^T = sum_hh K_hh . Q^T_hh (block diagonal over the wave's heads)
+      f32x4 sc = f32x4{};
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
-          kr[tb][t] = *(const uint4*)(kc + row + 32 * t + 8 * grp);
-          vr[tb][t] = *(const uint4*)(vc + row + 32 * t + 8 * grp);
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          kr[tb][t] = uint4{0, 0, 0, 0};
-          vr[tb][t] = uint4{0, 0, 0, 0};
+          const int c = 4 * t + grp;  // logical chunk of lane's 8 d
+          const char* ka = sK + (l16 * RC + hh * (D / 8) + (c ^ (tok_swz(l16) & (D / 8 - 1)))) * 16;
+          const bf16x8 a = *(const bf16x8*)ka;
+          const bf16x8 bq = (col_live && hh_col == hh) ? qf[t] : bf16x8{};
+          sc = mfma16(a, bq, sc);
         }
       }
-    }
-    // ---- V chunk to LDS, row-major [token][d] with a 16-byte-chunk swizzle
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int row = 16 * tb + l16;
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        const int c = 4 * t + grp;
-        *(uint4*)(sV + row * D + (c ^ (row & (NCH - 1))) * 8) = vr[tb][t];
-      }
-    }
-    // ---- S^T = K . Q^T
-    f32x4 sc[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      sc[tb] = f32x4{};
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        sc[tb] = mfma16(__builtin_bit_cast(bf16x8, kr[tb][t]), qf[t], sc[tb]);
-      }
-    }
-    // lane holds tokens c0 + 16 tb + 4 grp + r of head l16
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+      // lane holds tokens c0 + 4 grp + r of column n_col
+      float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tok = c0 + 16 * tb + 4 * grp + r;
-        if (tok >= t_end) sc[tb][r] = -INFINITY;
-        mx = fmaxf(mx, sc[tb][r]);
+        if (4 * grp + r >= n_valid) sc[r] = -INFINITY;
+        mx = fmaxf(mx, sc[r]);
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m_run, mx * cs);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
-    bf16x8 pb;
-    float rs = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = max_with_other_half(mx);
+      const float m_new = fmaxf(m_run, mx * cs);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+      bf16x4 pb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = exp2_fast(fmaf(sc[tb][r], cs, -m_use));
+        const float e = exp2_fast(fmaf(sc[r], cs, -m_use));
         rs += e;
-        pb[4 * tb + r] = (__bf16)e;
+        pb[r] = (__bf16)e;
       }
-    }
-    l_run = fmaf(l_run, alpha, rs);
-    // ---- O^T += V^T . P^T ; V^T slot s of lane group grp = token
-    // (s < 4 ? 4 grp + s : 16 + 4 grp + s - 4), matching pb
-    const int tr_r = l16 >> 2, tr_q = l16 & 3;
+      l_run = fmaf(l_run, alpha, rs);
+      // ---- O^T += sum_hh V_hh^T . P^T_hh ; V^T slot s of lane group grp = token 4 grp + s
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      acc[mb] *= alpha;
-      const int c = 2 * mb + (tr_q >> 1);
-      const int r0 = 4 * grp + tr_r, r1 = r0 + 16;
-      const uint16_t* a0 = sV + r0 * D + (c ^ (r0 & (NCH - 1))) * 8 + (tr_q & 1) * 4;
-      const uint16_t* a1 = sV + r1 * D + (c ^ (r1 & (NCH - 1))) * 8 + (tr_q & 1) * 4;
-      acc[mb] = mfma16(concat(lds_read_tr16(a0), lds_read_tr16(a1)), pb, acc[mb]);
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const bf16x4 bp = (col_live && hh_col == hh) ? pb : bf16x4{};
+        const int row = 4 * grp + tr_r;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int c = 2 * mb + (tr_q >> 1);
+          const char* va =
+              sV + (row * RC + hh * (D / 8) + (c ^ (tok_swz(row) & (D / 8 - 1)))) * 16 + (tr_q & 1) * 8;
+          acc[mb] = mfma16_k16(__builtin_bit_cast(bf16x4, lds_read_tr16(va)), bp, acc[mb]);
+        }
+      }
+      // the next chunk's copies overwrite this chunk's LDS rows: all reads above
+      // must have returned first
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
     }
-  }
 
-  // ---- partial (normalised within the split) and its base-2 LSE
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot = sum_with_other_half(l_tot);
-  const bool ok = l_tot > 0.f;
-  const float inv = ok ? 1.f / l_tot : 0.f;
-  if (l16 < G) {
-    const int h = g * G + l16;
-    const size_t slot = ((size_t)b * p.n_split + s) * p.A + h;
-    float* po = p.part_o + slot * D;
+    // ---- partial of (workgroup, sequence b): normalised O and base-2 LSE per column
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot = sum_with_other_half(l_tot);
+    const bool ok = l_tot > 0.f;
+    const float inv = ok ? 1.f / l_tot : 0.f;
+    if (col_live) {
+      const int h = kv0 * G + n_col;
+      const size_t slot = (size_t)(wg + b) * p.A + h;
+      float* po = p.part_o + slot * D;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      f32x4 w = acc[mb] * inv;
-      *(f32x4*)(po + 16 * mb + 4 * grp) = w;
+      for (int mb = 0; mb < MB; ++mb) *(f32x4*)(po + 16 * mb + 4 * grp) = acc[mb] * inv;
+      if (grp == 0) p.part_lse[slot] = ok ? m_run + log2_fast(l_tot) : -INFINITY;
     }
-    if (grp == 0) p.part_lse[slot] = ok ? m_run + log2_fast(l_tot) : -INFINITY;
+
+    remaining -= k_end - k;
+    if (remaining <= 0) break;
+    do {  // next sequence with at least one chunk (exists while chunks remain)
+      if (++b >= p.B) return;  // device lengths disagree with the host copy
+      len = p.seq_lens[b];
+    } while (len <= 0);
+    k = 0;
   }
 }
 
-// One wavefront per (sequence, head): combine the sequence's split partials.
+// One wavefront per (sequence, head): combine the sequence's partials.  The
+// workgroups that touched sequence b are the owners of its first and last
+// chunk and everything between; their partials sit in slots wg + b.  Lanes
+// turn the partial LSEs into weights 2^(lse - max); the output loop then
+// broadcasts one weight at a time (v_readlane) and keeps several independent
+// partial-row loads in flight.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+  constexpr int PER = D / 64;  // output elements per lane (contiguous)
+  typedef float fvec __attribute__((ext_vector_type(PER)));
   const int lane = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / p.A, h = bh % p.A;
   const int len = p.seq_lens[b];
-  const int ns = (len + p.split_tokens - 1) / p.split_tokens;
-  const size_t base = (size_t)b * p.n_split * p.A + h;  // slot of split 0
-  float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, p.part_lse[base + (size_t)s * p.A]);
+  uint16_t* o = (uint16_t*)p.o + ((size_t)b * p.A + h) * D + lane * PER;
+  fvec acc = {};
+  float wsum = 0.f, mx = -INFINITY;
+  if (len > 0) {
+    // chunks before sequence b
+    long long cex = 0;
+    for (int base = 0; base < b; base += 64) {
+      const int bb = base + lane;
+      const int lb = bb < b ? p.seq_lens[bb] : 0;
+      long long nc = (lb + kChunk - 1) / kChunk;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  constexpr int PER = D / 64;
-  float acc[PER];
+      for (int off = 32; off >= 1; off >>= 1) nc += __shfl_xor(nc, off);
+      cex += nc;
+    }
+    const long long nch = (len + kChunk - 1) / kChunk;
+    const long long NC = p.n_chunks, P = p.n_wg;
+    // owner of chunk c: the largest i with floor(i * NC / P) <= c
+    const int first = (int)(((cex + 1) * P - 1) / NC);
+    const int last = (int)(((cex + nch) * P - 1) / NC);
+    const int np = last - first + 1;
+    const size_t slot0 = (size_t)(first + b) * p.A + h;
+    for (int j = lane; j < np; j += 64) mx = fmaxf(mx, p.part_lse[slot0 + (size_t)j * p.A]);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const size_t slot = base + (size_t)s * p.A;
-      const float ls = p.part_lse[slot];
-      if (ls == -INFINITY) continue;
-      const float w = exp2_fast(ls - mx);
-      wsum += w;
-      const float* po = p.part_o + slot * D;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, po[lane + 64 * i], acc[i]);
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (mx != -INFINITY) {
+      for (int j0 = 0; j0 < np; j0 += 64) {
+        const int j = j0 + lane;
+        const float ls = j < np ? p.part_lse[slot0 + (size_t)j * p.A] : -INFINITY;
+        const float w = ls == -INFINITY ? 0.f : exp2_fast(ls - mx);
+        wsum += w;
+        const int cnt = min(64, np - j0);
+        const float* po = p.part_o + (slot0 + (size_t)j0 * p.A) * D + lane * PER;
+        const size_t step = (size_t)p.A * D;
+        auto wl = [&](int jj) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), jj)); };
+        int jj = 0;
+        for (; jj + 4 <= cnt; jj += 4) {  // four independent row loads in flight
+          const fvec r0 = *(const fvec*)(po + (jj + 0) * step);
+          const fvec r1 = *(const fvec*)(po + (jj + 1) * step);
+          const fvec r2 = *(const fvec*)(po + (jj + 2) * step);
+          const fvec r3 = *(const fvec*)(po + (jj + 3) * step);
+          acc += wl(jj) * r0;
+          acc += wl(jj + 1) * r1;
+          acc += wl(jj + 2) * r2;
+          acc += wl(jj + 3) * r3;
+        }
+        for (; jj < cnt; ++jj) acc += wl(jj) * *(const fvec*)(po + jj * step);
+      }
     }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   const bool ok = wsum > 0.f;
   const float inv = ok ? 1.f / wsum : 0.f;
-  uint16_t* o = (uint16_t*)p.o + ((size_t)b * p.A + h) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    o[lane + 64 * i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] * inv));
-  }
+  for (int i = 0; i < PER; ++i) o[i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] * inv));
   if (lane == 0) p.lse[(size_t)b * p.A + h] = ok ? (mx + log2_fast(wsum)) * kLn2 : -INFINITY;
 }
 
+template <int D, int HPW>
+hipError_t launch_split(const DecodeParams& p, int groups, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, HPW>), dim3(p.n_wg, groups), dim3(64 * kWavesPerGroup), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int HPW>
+int resident_groups(int cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, HPW>, 64 * kWavesPerGroup, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return cus * per_cu;
+}
+
 template <int D>
-hipError_t launch_decode_d(const DecodeParams& p, int total_units, hipStream_t stream) {
-  if (total_units > 0) {
-    hipLaunchKernelGGL(decode_split_kernel<D>, dim3(total_units * p.A_kv), dim3(64), 0, stream, p);
-    hipError_t e = hipGetLastError();
+hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
+  if (p.n_chunks > 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus < 1)
+      cus = 1;
+    const bool two = p.G <= 8;  // two KV heads per wave when 2G <= 16 MFMA columns
+    const int heads_per_group = (two ? 2 : 1) * kWavesPerGroup;
+    const int groups = (p.A_kv + heads_per_group - 1) / heads_per_group;
+    // one resident wave of workgroups covers the chunk list once
+    long long want = (two ? resident_groups<D, 2>(cus) : resident_groups<D, 1>(cus)) / groups;
+    if (want < 1) want = 1;
+    if (want > kMaxDecodeGroups) want = kMaxDecodeGroups;
+    if (want > p.n_chunks) want = p.n_chunks;
+    p.n_wg = (int)want;
+    hipError_t e = two ? launch_split<D, 2>(p, groups, stream) : launch_split<D, 1>(p, groups, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.B * p.A), dim3(64), 0, stream, p);
@@ -258,40 +375,31 @@ hipError_t launch_decode_d(const DecodeParams& p, int total_units, hipStream_t s
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int A_kv, int page_size, const int32_t* seq_lens_host) {
-  // Split size: aim for ~32k (unit, KV head) wavefronts over the whole batch
-  // (>= 100 per CU, so the last round of waves is a small tail), in whole
-  // 32-token chunks and whole pages, between 64 and 4096 tokens.
-  long long total = 0;
-  int max_len = 0;
-  for (int b = 0; b < B; ++b) {
-    total += seq_lens_host[b];
-    max_len = seq_lens_host[b] > max_len ? seq_lens_host[b] : max_len;
-  }
-  const long long target_units = 32768;
-  long long c = (total * A_kv + target_units - 1) / target_units;
-  const int quantum = page_size > kChunk ? page_size : kChunk;  // page_size % 16 == 0
-  int lcm = quantum;
-  while (lcm % kChunk != 0 || lcm % page_size != 0) lcm += quantum;
-  if (c < 64) c = 64;
-  if (c > 4096) c = 4096;
-  c = ((c + lcm - 1) / lcm) * lcm;
+DecodePlan plan_decode(int B, const int32_t* seq_lens_host) {
   DecodePlan plan;
-  plan.split_tokens = (int)c;
-  plan.n_split = max_len > 0 ? (int)((max_len + c - 1) / c) : 0;
+  long long nc = 0;
+  for (int b = 0; b < B; ++b) nc += (seq_lens_host[b] + kChunk - 1) / kChunk;
+  plan.n_chunks = nc;
+  plan.n_slots = kMaxDecodeGroups + B;  // slot wg + b < n_wg + B
   return plan;
 }
 
-size_t decode_workspace_bytes(int B, int A, int d, const DecodePlan& plan) {
-  const size_t slots = (size_t)B * (size_t)plan.n_split * (size_t)A;
+size_t decode_workspace_bytes(int A, int d, const DecodePlan& plan) {
+  if (plan.n_chunks == 0) return 0;
+  const size_t slots = (size_t)plan.n_slots * (size_t)A;
   const size_t o_bytes = ((slots * (size_t)d * 4) + 255) / 256 * 256;
   const size_t l_bytes = ((slots * 4) + 255) / 256 * 256;
   return o_bytes + l_bytes;
 }
 
-hipError_t launch_decode_bf16(const DecodeParams& p, int total_units, hipStream_t stream) {
-  if (p.d == 128) return launch_decode_d<128>(p, total_units, stream);
-  if (p.d == 64) return launch_decode_d<64>(p, total_units, stream);
+size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan) {
+  const size_t slots = (size_t)plan.n_slots * (size_t)A;
+  return ((slots * (size_t)d * 4) + 255) / 256 * 256;
+}
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+  if (p.d == 128) return launch_decode_d<128>(p, stream);
+  if (p.d == 64) return launch_decode_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

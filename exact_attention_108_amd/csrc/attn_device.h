@@ -39,6 +39,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// 16x16x16 (K = 16): lane l holds A[l % 16][4 (l / 16) + s], B[4 (l / 16) + s][l % 16]
+__device__ __forceinline__ f32x4 mfma16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                   0, 0, 0);
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element (i & 3) of the 4-element chunk addressed by lane

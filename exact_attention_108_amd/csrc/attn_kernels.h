@@ -36,7 +36,7 @@ hipError_t launch_prefill_f32(const FwdParams& p, bool varlen, hipStream_t strea
 constexpr int kPrefillRows = 128;
 constexpr int kPrefillRowsF32 = 16;
 
-// Paged decode, split along the KV length.
+// Paged decode, split along the KV length (Stream-K over 16-token chunks).
 struct DecodeParams {
   const void* q;
   const void* k_cache;
@@ -45,24 +45,26 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* o;
   float* lse;
-  float* part_o;    // workspace [B, A, n_split, d] fp32 (normalised partial outputs)
-  float* part_lse;  // workspace [B, A, n_split] fp32 (natural-log LSE of each split)
+  float* part_o;    // workspace [n_slots, A, d] fp32: partial outputs, normalised within the partial
+  float* part_lse;  // workspace [n_slots, A] fp32: base-2 LSE of each partial
   int B, A, A_kv, G, d;
   int page_size, max_pages;
-  int split_tokens;  // tokens per split (multiple of the page size)
-  int n_split;       // splits per sequence = ceil(max seq_len / split_tokens)
+  long long n_chunks;  // sum over sequences of ceil(len / 16)
+  int n_wg;            // workgroups along the chunk list (set at launch)
   float scale, scale_log2;
 };
 
-// Split plan shared by the workspace query and the launch.
-struct DecodePlan {
-  int split_tokens;
-  int n_split;
-};
-DecodePlan plan_decode(int B, int A_kv, int page_size, const int32_t* seq_lens_host);
-size_t decode_workspace_bytes(int B, int A, int d, const DecodePlan& plan);
+// upper bound on workgroups along the chunk list; sizes the workspace
+constexpr int kMaxDecodeGroups = 2048;
 
-// total_units = sum_b ceil(seq_lens[b] / split_tokens)
-hipError_t launch_decode_bf16(const DecodeParams& p, int total_units, hipStream_t stream);
+struct DecodePlan {
+  long long n_chunks;
+  int n_slots;  // partial slots: workgroup + sequence < kMaxDecodeGroups + B
+};
+DecodePlan plan_decode(int B, const int32_t* seq_lens_host);
+size_t decode_workspace_bytes(int A, int d, const DecodePlan& plan);
+size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan);
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace attn
