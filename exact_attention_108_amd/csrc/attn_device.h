@@ -52,6 +52,32 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane L's 16 bytes land
+// at LDS byte lds_wave_base + 16 * L.  The copy is issued from inline assembly
+// so the compiler does not add its own (whole-queue) wait before later LDS
+// reads; the caller orders it with lds_copy_wait_all() and a barrier.  M0
+// carries the wave-uniform LDS base; no other code in these kernels uses M0.
+__device__ __forceinline__ void lds_copy16(const void* gptr, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_wave_base), "v"(gptr)
+               : "memory");
+}
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order, so every older LDS copy has landed).
+template <int N>
+__device__ __forceinline__ void lds_copy_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);  // vmcnt(N)
+  asm volatile("" ::: "memory");
+}
+// Wait until every vector-memory load of this wave (including the LDS copies)
+// has completed.
+__device__ __forceinline__ void lds_copy_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 concat(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

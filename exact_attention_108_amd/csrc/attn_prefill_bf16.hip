@@ -38,6 +38,8 @@
 // 稳定基础").  Query tiles are issued heaviest first (most key tiles) so the
 // tail of the grid holds the short ones (page "快速Transformer（续）",
 // section "Stream-K", wave quantisation).
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 #include "attn_rowblock.h"
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
   constexpr int MB = D / 32;               // 32-row blocks of O^T
   constexpr int TILE_CH = kBc * NCH;       // chunks per K (or V) tile
-  constexpr int LD_PER_T = TILE_CH / kThreads;
+  constexpr int LD_PER_T = TILE_CH / kThreads;  // 16-byte copies per thread per K (or V) tile
   static_assert(TILE_CH % kThreads == 0, "tile load split");
 
   // [K buf 0 | K buf 1 | V buf 0 | V buf 1]; the epilogue reuses it for staging
@@ -103,45 +105,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // ---- tile loader: thread handles LD_PER_T chunks of K and of V
-  uint4 kr[LD_PER_T], vr[LD_PER_T];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) {
-      const int cid = tid + i * kThreads;
-      const int row = cid / NCH, c = cid % NCH;
-      const int key = j * kBc + row;
-      if (key < S_k) {
-        kr[i] = *(const uint4*)(gk + (size_t)key * D + c * 8);
-        vr[i] = *(const uint4*)(gv + (size_t)key * D + c * 8);
-      } else {
-        kr[i] = uint4{0, 0, 0, 0};
-        vr[i] = uint4{0, 0, 0, 0};
-      }
-    }
+  // ---- tile loader: global -> LDS copies (global_load_lds_dwordx4) that do
+  // not pass through registers.  One copy round of the workgroup fills RPC
+  // tile rows: lane L of wave w the 16 bytes of slot w*64 + L, i.e. row
+  // i*RPC + rowc, physical chunk pcc; the global address is chosen so that
+  // those bytes hold the row's swizzled chunk.  Only the last tile can reach
+  // past S_k; its missing rows re-read row S_k - 1 (finite, masked to weight 0).
+  constexpr int RPC = kThreads / NCH;  // rows per copy round (a multiple of 16)
+  constexpr int TILE_BYTES = kBc * D * 2;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+  const int rowc = (wave * 64 + lane) / NCH, pcc = (wave * 64 + lane) % NCH;
+  const int cc = lds_chunk<D>(rowc, pcc);  // the swizzle is an involution; it depends on row % 16 only
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index in a scalar register
+  // Copy part `part` (of LD_PER_T) of tile j into buffer buf: one K and one V
+  // 16-byte copy per lane.  The parts are issued at spread-out points of the
+  // previous tile's computation, so the waves of a CU do not all queue their
+  // copies on the load path at the same moment.
+  auto copy_part = [&](int j, int buf, int i) {
+    const int key = min(j * kBc + i * RPC + rowc, S_k - 1);
+    const uint16_t* src = gk + (size_t)key * D + cc * 8;
+    const size_t vdiff = (size_t)(gv - gk);
+    const uint32_t lk = lds_base + (uint32_t)(buf * TILE_BYTES + i * RPC * D * 2) + (uint32_t)wave_u * 1024u;
+    lds_copy16(src, lk);
+    lds_copy16(src + vdiff, lk + 2 * TILE_BYTES);
   };
-  uint8_t keep_r = 1;
-  auto load_keep = [&](int j) {
+  auto copy_keep = [&](int j, int buf) {
     if (rb.k_keep && tid < kBc) {
       const int key = j * kBc + tid;
-      keep_r = key < S_k ? rb.k_keep[key] : 0;
+      sKeep[buf][tid] = key < S_k ? rb.k_keep[key] : 0;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto copy_tile = [&](int j, int buf) {
 #pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) {
-      const int cid = tid + i * kThreads;
-      const int row = cid / NCH, c = cid % NCH;
-      const int pc = lds_chunk<D>(row, c);
-      *(uint4*)(sK(buf) + row * D + pc * 8) = kr[i];
-      *(uint4*)(sV(buf) + row * D + pc * 8) = vr[i];
-    }
-    if (rb.k_keep && tid < kBc) sKeep[buf][tid] = keep_r;
+    for (int i = 0; i < LD_PER_T; ++i) copy_part(j, buf, i);
+    copy_keep(j, buf);
   };
 
-  // ---- online-softmax state: m (base-2 scaled running max), l (this half's
-  // partial normaliser), o (O^T accumulators: d = 32mb + 8(r/4) + 4g + r%4)
-  float m_run = -INFINITY;
+  // ---- online-softmax state.  m_ref: the base-2 reference the exponentials
+  // of this row are taken against (-inf until the row has seen a key); l: this
+  // lane-half's partial normaliser; acc_o: O^T accumulators (d = 32mb +
+  // 8(r/4) + 4g + r%4 of this lane's query).  m_ref only moves when a tile's
+  // max exceeds it by more than kLazy (so p <= 2^kLazy); o and l always share
+  // the same reference, so the final o / l is the exact softmax average
+  // whatever reference was used (page "Attention Kernel", Online softmax:
+  // the state may be rescaled by any common factor).
+  constexpr float kLazy = 8.f;
+  float m_ref = -INFINITY;
   float l_run = 0.f;
   f32x16 acc_o[MB];
 #pragma unroll
@@ -151,108 +160,172 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wave_q0 = rb.q0 + wave * 32;
   const bool wave_live = wave_q0 < S_q;
 
-  // per-lane LDS byte offsets (within a tile buffer) for the K-operand reads
-  // and the transposing V reads; the swizzle depends only on row % 16.
-  const int kt_row = l32;  // + 32*kb
+  // ---- per-lane LDS byte offsets of the operand reads inside a tile buffer.
+  // The swizzle depends on row % 16 only, so the row blocks (32 rows per kb,
+  // 16 per h) and the buffer choice are compile-time immediates.
+  int koff[KSTEPS];  // K operand of k-step t: row l32, chunk 2t + g
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) koff[t] = (l32 * D + lds_chunk<D>(l32, 2 * t + g) * 8) * 2;
   const int j16 = lane & 15, tr_r = j16 >> 2, tr_q = j16 & 3, half16 = (lane >> 4) & 1;
-  const int v_row = 4 * g + tr_r;  // + 32kb + 16h (+8 for the second read)
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    load_keep(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) {
-      load_tile(j + 1);
-      load_keep(j + 1);
+  const int v_row = 4 * g + tr_r;
+  int voff[MB][2];  // transposing V read rd of block mb: row v_row + 8 rd, chunk 4mb + 2 half16 + tr_q/2
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = v_row + 8 * rd;
+      const int c = 4 * mb + 2 * half16 + (tr_q >> 1);
+      voff[mb][rd] = (row * D + lds_chunk<D>(row, c) * 8 + (tr_q & 1) * 4) * 2;
     }
-    const int k0 = j * kBc;
-    // skip tiles no row of this wave can see
-    const bool wave_active = wave_live && !(causal && k0 > wave_q0 + 31 + off);
-    if (wave_active) {
-      const uint16_t* tK = sK(buf);
-      const uint16_t* tV = sV(buf);
-      // ---- S^T = K . Q^T : two 32-key blocks
-      f32x16 s[2];
+  }
+  const char* lds = (const char*)smem;
+
+  // One key tile for this wave.  BUF is the tile's LDS buffer (compile time).
+  // MASKED selects the per-element predicate (keys past S_k, the causal
+  // diagonal, the key keep-mask); interior tiles take the unmasked instance.
+  // Operand reads run PF steps ahead of the MFMAs that consume them.
+  auto tile = [&](auto masked_tag, auto buf_tag, int k0, auto&& issue_copy) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int KB = BUF * TILE_BYTES;            // K tile of this buffer
+    constexpr int VB = (2 + BUF) * TILE_BYTES;      // V tile of this buffer
+    constexpr int PF = 3;
+    // ---- S^T = K . Q^T : two 32-key blocks, k-steps interleaved across them
+    constexpr int NQ = 2 * KSTEPS;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    bf16x8 ka[NQ];
+    auto kread = [&](int p) {  // step p: kb = p % 2, t = p / 2
+      ka[p] = *(const bf16x8*)(lds + KB + (p % 2) * 32 * D * 2 + koff[p / 2]);
+    };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int row = 32 * kb + kt_row;
+    for (int p = 0; p < PF; ++p) kread(p);
+    issue_copy(0);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          const bf16x8 a = *(const bf16x8*)(tK + row * D + lds_chunk<D>(row, 2 * t + g) * 8);
-          s[kb] = mfma32(a, qf[t], s[kb]);
-        }
-      }
-      // ---- mask: keys past S_k, causal diagonal, key keep-mask
-      const bool need_mask = (k0 + kBc > S_k) || (causal && k0 + kBc - 1 > wave_q0 + off) ||
-                             (rb.k_keep != nullptr);
-      if (need_mask) {
-        const int qpos = qrow + off;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const int key = k0 + kl;
-            bool dead = key >= S_k || (causal && key > qpos);
-            if (rb.k_keep) dead = dead || sKeep[buf][kl] == 0;
-            if (dead) s[kb][r] = -INFINITY;
-          }
-        }
-      }
-      // ---- online softmax (base 2)
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = max_with_other_half(mx);
-      const float m_new = fmaxf(m_run, mx * cs);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
-      const float neg = -m_use;
-      float rs = 0.f;
-      bf16x8 pb[2][2];
+    for (int p = 0; p < NQ; ++p) {
+      if (p + PF < NQ) kread(p + PF);
+      s[p % 2] = mfma32(ka[p], qf[p / 2], s[p % 2]);
+      if (p == NQ / 2) issue_copy(1);
+    }
+    if constexpr (MASKED) {
+      // bit k of kvalid: key k0 + k exists and is kept (same for every lane)
+      bool valid = k0 + lane < S_k;
+      if (rb.k_keep) valid = valid && sKeep[BUF][lane] != 0;
+      const uint64_t kvalid = __ballot(valid) >> (4 * g);
+      // element (kb, r) holds key k0 + kl, kl = 32kb + 8(r/4) + 4g + r%4;
+      // causal: dead when kl > qrow + off - k0
+      const int lim = causal ? qrow + off - k0 - 4 * g : (1 << 30);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(fmaf(s[kb][r], cs, neg));
-          rs += e;
-          pb[kb][r >> 3][r & 7] = (__bf16)e;
-        }
-      }
-      l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc_o[mb] *= alpha;
-      // ---- O^T += V^T . P^T
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int c = 4 * mb + 2 * half16 + (tr_q >> 1);
-            const int r0 = 32 * kb + 16 * h + v_row;
-            const int r1 = r0 + 8;
-            const uint16_t* a0 = tV + r0 * D + lds_chunk<D>(r0, c) * 8 + (tr_q & 1) * 4;
-            const uint16_t* a1 = tV + r1 * D + lds_chunk<D>(r1, c) * 8 + (tr_q & 1) * 4;
-            const bf16x8 a = concat(lds_read_tr16(a0), lds_read_tr16(a1));
-            acc_o[mb] = mfma32(a, pb[kb][h], acc_o[mb]);
-          }
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);  // kl - 4g
+          const bool live = ((kvalid >> c) & 1) && c <= lim;
+          s[kb][r] = live ? s[kb][r] : -INFINITY;
         }
       }
     }
-    if (has_next) store_tile(buf ^ 1);
+    // ---- row max of the tile (raw scores), both lane halves
+    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      mx0 = fmaxf(mx0, fmaxf(s[0][r], s[0][r + 1]));
+      mx1 = fmaxf(mx1, fmaxf(s[1][r], s[1][r + 1]));
+    }
+    const float mxs = max_with_other_half(fmaxf(mx0, mx1)) * cs;  // scale > 0
+    // ---- move the reference only when some row of the wave needs it
+    if (__builtin_amdgcn_ballot_w64(mxs > m_ref + kLazy) != 0) {
+      const float m_new = fmaxf(m_ref, mxs);
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc_o[mb] *= alpha;
+    }
+    issue_copy(2);
+    const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    float rs0 = 0.f, rs1 = 0.f, rs2 = 0.f, rs3 = 0.f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const float e0 = exp2_fast(fmaf(s[kb][r + 0], cs, neg));
+        const float e1 = exp2_fast(fmaf(s[kb][r + 1], cs, neg));
+        const float e2 = exp2_fast(fmaf(s[kb][r + 2], cs, neg));
+        const float e3 = exp2_fast(fmaf(s[kb][r + 3], cs, neg));
+        rs0 += e0;
+        rs1 += e1;
+        rs2 += e2;
+        rs3 += e3;
+        pb[kb][r >> 3][(r & 7) + 0] = (__bf16)e0;
+        pb[kb][r >> 3][(r & 7) + 1] = (__bf16)e1;
+        pb[kb][r >> 3][(r & 7) + 2] = (__bf16)e2;
+        pb[kb][r >> 3][(r & 7) + 3] = (__bf16)e3;
+      }
+    }
+    l_run += (rs0 + rs1) + (rs2 + rs3);
+    // ---- O^T += V^T . P^T ; steps (kb, h, mb) with mb innermost: MB
+    // independent accumulator chains
+    constexpr int NV = 4 * MB;
+    bf16x8 va[NV];
+    auto vread = [&](int q) {  // step q: mb = q % MB, (kb, h) = q / MB
+      const int mb = q % MB, kh = q / MB, kb = kh >> 1, h = kh & 1;
+      const char* base = lds + VB + (32 * kb + 16 * h) * D * 2;
+      va[q] = concat(lds_read_tr16(base + voff[mb][0]), lds_read_tr16(base + voff[mb][1]));
+    };
+#pragma unroll
+    for (int q = 0; q < PF; ++q) vread(q);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      if (q + PF < NV) vread(q + PF);
+      const int mb = q % MB, kh = q / MB;
+      acc_o[mb] = mfma32(va[q], pb[kh >> 1][kh & 1], acc_o[mb]);
+      if (q == NV / 2) issue_copy(3);
+    }
+  };
+
+  // ---- main loop, unrolled by the two buffers: tile j sits in buffer j % 2
+  auto step = [&](auto buf_tag, int j) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    // tile j has landed in LDS for this thread's copies; after the barrier,
+    // for everyone's -- and every wave is done with tile j-1, whose buffer
+    // the copy of tile j+1 below overwrites
+    lds_copy_wait_all();
     __syncthreads();
+    // the copies of tile j+1 are issued in LD_PER_T parts spread over the
+    // computation of tile j (four issue points in tile()).  After the last
+    // tile they re-copy it into the idle buffer (harmless, and it keeps the
+    // tile body free of branches).
+    const int jn = min(j + 1, n_tiles - 1);
+    if (j + 1 < n_tiles) copy_keep(j + 1, BUF ^ 1);
+    auto issue = [&](int at) {
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i)
+        if (i * 4 / LD_PER_T == at) copy_part(jn, BUF ^ 1, i);
+    };
+    const int k0 = j * kBc;
+    // skip tiles no row of this wave can see
+    const bool wave_active = wave_live && !(causal && k0 > wave_q0 + 31 + off);
+    if (wave_active) {
+      const bool need_mask = (k0 + kBc > S_k) || (causal && k0 + kBc - 1 > wave_q0 + off) ||
+                             (rb.k_keep != nullptr);
+      if (need_mask) {
+        tile(std::integral_constant<bool, true>{}, buf_tag, k0, issue);
+      } else {
+        tile(std::integral_constant<bool, false>{}, buf_tag, k0, issue);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) copy_part(jn, BUF ^ 1, i);
+    }
+  };
+  if (n_tiles > 0) copy_tile(0, 0);
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
+  lds_copy_wait_all();  // the trailing copies have landed ...
+  __syncthreads();      // ... and all reads of the last tile are done before the epilogue reuses LDS
 
   // ---- epilogue: O = o / l (0 for an empty row), LSE = ln 2 * (m + log2 l)
   const float l_tot = sum_with_other_half(l_run);
@@ -276,7 +349,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   if (g == 0 && qrow < S_q) {
-    rb.lse[qrow] = row_ok ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
+    rb.lse[qrow] = row_ok ? (m_ref + log2_fast(l_tot)) * kLn2 : -INFINITY;
   }
   __syncthreads();
 #pragma unroll
@@ -317,3 +390,4 @@ hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stre
 }
 
 }  // namespace attn
+
