@@ -10,6 +10,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -61,6 +63,28 @@ __device__ __forceinline__ void lds_copy16(const void* gptr, uint32_t lds_wave_b
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds_wave_base), "v"(gptr)
+               : "memory");
+}
+// Buffer resource (V#) for raw byte-addressed loads from `base`: stride 0, so
+// a lane's access is in range iff its byte offset < num_bytes; out-of-range
+// lanes touch no memory and read zeros.  Every field is wave-uniform (SGPRs).
+__device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;  // 32-bit data format, no swizzle (gfx9 family)
+  return r;
+}
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane L's 16 bytes
+// at byte `voff` of the resource land at LDS byte lds_wave_base + 16 * L; a
+// lane whose offset is out of the resource's range writes 16 zero bytes.
+// Ordered like lds_copy16 (explicit waits, M0 holds the LDS base).
+__device__ __forceinline__ void lds_copy16_buf(i32x4 rsrc, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
                : "memory");
 }
 // Wait until at most N vector-memory loads of this wave are outstanding

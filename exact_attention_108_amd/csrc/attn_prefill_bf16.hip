@@ -65,8 +65,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // [K buf 0 | K buf 1 | V buf 0 | V buf 1]; the epilogue reuses it for staging
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kBc * D];
   __shared__ uint8_t sKeep[2][kBc];
-  auto sK = [&](int buf) { return smem + buf * (kBc * D); };
-  auto sV = [&](int buf) { return smem + (2 + buf) * (kBc * D); };
 
   RowBlock rb;
   if constexpr (kVarlen) {
@@ -105,40 +103,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // ---- tile loader: global -> LDS copies (global_load_lds_dwordx4) that do
-  // not pass through registers.  One copy round of the workgroup fills RPC
+  // ---- tile loader: buffer -> LDS copies (buffer_load_dwordx4 ... lds) that
+  // do not pass through registers.  One copy round of the workgroup fills RPC
   // tile rows: lane L of wave w the 16 bytes of slot w*64 + L, i.e. row
-  // i*RPC + rowc, physical chunk pcc; the global address is chosen so that
-  // those bytes hold the row's swizzled chunk.  Only the last tile can reach
-  // past S_k; its missing rows re-read row S_k - 1 (finite, masked to weight 0).
+  // i*RPC + rowc, physical chunk pcc; the source offset is chosen so that
+  // those bytes hold the row's swizzled chunk.  Each tile gets its own buffer
+  // resource covering exactly its rows that exist, so the rows of a ragged
+  // last tile past S_k arrive as zeros (finite, and masked to weight 0)
+  // without any per-lane address arithmetic in the loop.
+  //
+  // LDS holds [K buf 0 | K buf 1 | V buf 0 | V buf 1]; tile t's K sits in K
+  // buffer t % 2 and its V in V buffer t % 2.  K runs one tile ahead of V:
+  // iteration j multiplies Q by K of tile j+1 while it applies P of tile j to
+  // V of tile j, and meanwhile copies K of tile j+2 and V of tile j+1 into the
+  // buffers iteration j-1 finished with.
   constexpr int RPC = kThreads / NCH;  // rows per copy round (a multiple of 16)
   constexpr int TILE_BYTES = kBc * D * 2;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const int rowc = (wave * 64 + lane) / NCH, pcc = (wave * 64 + lane) % NCH;
   const int cc = lds_chunk<D>(rowc, pcc);  // the swizzle is an involution; it depends on row % 16 only
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index in a scalar register
-  // Copy part `part` (of LD_PER_T) of tile j into buffer buf: one K and one V
-  // 16-byte copy per lane.  The parts are issued at spread-out points of the
-  // previous tile's computation, so the waves of a CU do not all queue their
-  // copies on the load path at the same moment.
-  auto copy_part = [&](int j, int buf, int i) {
-    const int key = min(j * kBc + i * RPC + rowc, S_k - 1);
-    const uint16_t* src = gk + (size_t)key * D + cc * 8;
-    const size_t vdiff = (size_t)(gv - gk);
-    const uint32_t lk = lds_base + (uint32_t)(buf * TILE_BYTES + i * RPC * D * 2) + (uint32_t)wave_u * 1024u;
-    lds_copy16(src, lk);
-    lds_copy16(src + vdiff, lk + 2 * TILE_BYTES);
-  };
-  auto copy_keep = [&](int j, int buf) {
-    if (rb.k_keep && tid < kBc) {
-      const int key = j * kBc + tid;
-      sKeep[buf][tid] = key < S_k ? rb.k_keep[key] : 0;
-    }
-  };
-  auto copy_tile = [&](int j, int buf) {
+  uint32_t coff[LD_PER_T];  // byte offset of this lane's copy of part i inside a tile
 #pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) copy_part(j, buf, i);
-    copy_keep(j, buf);
+  for (int i = 0; i < LD_PER_T; ++i) coff[i] = (uint32_t)((i * RPC + rowc) * D * 2 + cc * 16);
+  auto tile_rsrc = [&](const uint16_t* gsrc, int t) {
+    const int rows = min(max(S_k - t * kBc, 0), kBc);
+    return make_buffer_rsrc(gsrc + (size_t)t * kBc * D, (uint32_t)(rows * D * 2));
+  };
+  // part i (of LD_PER_T) of one tile of K (or V) into LDS byte offset `dst`
+  auto copy_part = [&](const i32x4& rsrc, uint32_t dst, int i) {
+    lds_copy16_buf(rsrc, coff[i], lds_base + dst + (uint32_t)(i * RPC * D * 2) + (uint32_t)wave_u * 1024u);
+  };
+  auto copy_keep = [&](int t) {
+    if (rb.k_keep && tid < kBc && t < n_tiles) {
+      const int key = t * kBc + tid;
+      sKeep[t & 1][tid] = key < S_k ? rb.k_keep[key] : 0;
+    }
   };
 
   // ---- online-softmax state.  m_ref: the base-2 reference the exponentials
@@ -158,7 +158,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const float cs = p.scale_log2;
   const int wave_q0 = rb.q0 + wave * 32;
-  const bool wave_live = wave_q0 < S_q;
 
   // ---- per-lane LDS byte offsets of the operand reads inside a tile buffer.
   // The swizzle depends on row % 16 only, so the row blocks (32 rows per kb,
@@ -179,60 +178,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   const char* lds = (const char*)smem;
+  constexpr int PF = 3;  // operand reads run PF MFMA steps ahead of their use
 
-  // One key tile for this wave.  BUF is the tile's LDS buffer (compile time).
-  // MASKED selects the per-element predicate (keys past S_k, the causal
-  // diagonal, the key keep-mask); interior tiles take the unmasked instance.
-  // Operand reads run PF steps ahead of the MFMAs that consume them.
-  auto tile = [&](auto masked_tag, auto buf_tag, int k0, auto&& issue_copy) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int BUF = decltype(buf_tag)::value;
-    constexpr int KB = BUF * TILE_BYTES;            // K tile of this buffer
-    constexpr int VB = (2 + BUF) * TILE_BYTES;      // V tile of this buffer
-    constexpr int PF = 3;
-    // ---- S^T = K . Q^T : two 32-key blocks, k-steps interleaved across them
+  // S^T = K . Q^T for the K tile in LDS buffer KBUF: two 32-key blocks, the
+  // k-steps interleaved across them.  `issue` is called at two points.
+  auto qk = [&](auto kbuf_tag, f32x16 (&s)[2], auto&& issue) {
+    constexpr int KB = decltype(kbuf_tag)::value * TILE_BYTES;
     constexpr int NQ = 2 * KSTEPS;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
     bf16x8 ka[NQ];
     auto kread = [&](int p) {  // step p: kb = p % 2, t = p / 2
       ka[p] = *(const bf16x8*)(lds + KB + (p % 2) * 32 * D * 2 + koff[p / 2]);
     };
 #pragma unroll
     for (int p = 0; p < PF; ++p) kread(p);
-    issue_copy(0);
+    issue(0);
 #pragma unroll
     for (int p = 0; p < NQ; ++p) {
       if (p + PF < NQ) kread(p + PF);
       s[p % 2] = mfma32(ka[p], qf[p / 2], s[p % 2]);
-      if (p == NQ / 2) issue_copy(1);
+      if (p == NQ / 2) issue(1);
     }
-    if constexpr (MASKED) {
-      // bit k of kvalid: key k0 + k exists and is kept (same for every lane)
-      bool valid = k0 + lane < S_k;
-      if (rb.k_keep) valid = valid && sKeep[BUF][lane] != 0;
-      const uint64_t kvalid = __ballot(valid) >> (4 * g);
-      // element (kb, r) holds key k0 + kl, kl = 32kb + 8(r/4) + 4g + r%4;
-      // causal: dead when kl > qrow + off - k0
-      const int lim = causal ? qrow + off - k0 - 4 * g : (1 << 30);
+  };
+  // per-element predicate of tile t (keys past S_k, the causal diagonal, the
+  // key keep-mask): dead scores become -inf
+  auto mask = [&](f32x16 (&s)[2], int t) {
+    const int k0 = t * kBc;
+    // bit k of kvalid: key k0 + k exists and is kept (same for every lane)
+    bool valid = k0 + lane < S_k;
+    if (rb.k_keep) valid = valid && sKeep[t & 1][lane] != 0;
+    const uint64_t kvalid = __ballot(valid) >> (4 * g);
+    // element (kb, r) holds key k0 + kl, kl = 32kb + 8(r/4) + 4g + r%4;
+    // causal: dead when kl > qrow + off - k0
+    const int lim = causal ? qrow + off - k0 - 4 * g : (1 << 30);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);  // kl - 4g
-          const bool live = ((kvalid >> c) & 1) && c <= lim;
-          s[kb][r] = live ? s[kb][r] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * kb + 8 * (r >> 2) + (r & 3);  // kl - 4g
+        const bool live = ((kvalid >> c) & 1) && c <= lim;
+        s[kb][r] = live ? s[kb][r] : -INFINITY;
       }
     }
-    // ---- row max of the tile (raw scores), both lane halves
-    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
+  };
+  // row max of a tile in base-2 units (scale > 0), both lane halves: four
+  // chains of three-input maxima
+  auto rowmax = [&](const f32x16 (&s)[2]) {
+    float mx[4];
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      mx0 = fmaxf(mx0, fmaxf(s[0][r], s[0][r + 1]));
-      mx1 = fmaxf(mx1, fmaxf(s[1][r], s[1][r + 1]));
+    for (int c = 0; c < 4; ++c) {
+      const int kb = c >> 1, r0 = (c & 1) * 8;
+      float m = fmaxf(s[kb][r0], fmaxf(s[kb][r0 + 1], s[kb][r0 + 2]));
+      m = fmaxf(m, fmaxf(s[kb][r0 + 3], s[kb][r0 + 4]));
+      m = fmaxf(m, fmaxf(s[kb][r0 + 5], s[kb][r0 + 6]));
+      mx[c] = fmaxf(m, s[kb][r0 + 7]);
     }
-    const float mxs = max_with_other_half(fmaxf(mx0, mx1)) * cs;  // scale > 0
-    // ---- move the reference only when some row of the wave needs it
+    return max_with_other_half(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * cs;
+  };
+  // move the reference only when some row of the wave needs it
+  auto rescale = [&](float mxs) {
     if (__builtin_amdgcn_ballot_w64(mxs > m_ref + kLazy) != 0) {
       const float m_new = fmaxf(m_ref, mxs);
       const float alpha = (m_ref == -INFINITY) ? 0.f : exp2_fast(m_ref - m_new);
@@ -241,9 +246,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc_o[mb] *= alpha;
     }
-    issue_copy(2);
+  };
+  // P = 2^(S * scale * log2 e - m) and O^T += V^T . P^T for the V tile in
+  // LDS buffer VBUF; the normaliser sums p in fp32, the product takes p
+  // rounded to bf16.  PV steps (kb, h, mb) with mb innermost: MB independent
+  // accumulator chains.  `issue` is called at two points.
+  auto softmax_pv = [&](auto vbuf_tag, const f32x16 (&s)[2], auto&& issue) {
+    constexpr int VB = (2 + decltype(vbuf_tag)::value) * TILE_BYTES;
     const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
-    float rs0 = 0.f, rs1 = 0.f, rs2 = 0.f, rs3 = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -253,19 +264,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float e1 = exp2_fast(fmaf(s[kb][r + 1], cs, neg));
         const float e2 = exp2_fast(fmaf(s[kb][r + 2], cs, neg));
         const float e3 = exp2_fast(fmaf(s[kb][r + 3], cs, neg));
-        rs0 += e0;
-        rs1 += e1;
-        rs2 += e2;
-        rs3 += e3;
+        rs[0] += e0;
+        rs[1] += e1;
+        rs[2] += e2;
+        rs[3] += e3;
         pb[kb][r >> 3][(r & 7) + 0] = (__bf16)e0;
         pb[kb][r >> 3][(r & 7) + 1] = (__bf16)e1;
         pb[kb][r >> 3][(r & 7) + 2] = (__bf16)e2;
         pb[kb][r >> 3][(r & 7) + 3] = (__bf16)e3;
       }
     }
-    l_run += (rs0 + rs1) + (rs2 + rs3);
-    // ---- O^T += V^T . P^T ; steps (kb, h, mb) with mb innermost: MB
-    // independent accumulator chains
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     constexpr int NV = 4 * MB;
     bf16x8 va[NV];
     auto vread = [&](int q) {  // step q: mb = q % MB, (kb, h) = q / MB
@@ -275,54 +284,115 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 #pragma unroll
     for (int q = 0; q < PF; ++q) vread(q);
+    issue(2);
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       if (q + PF < NV) vread(q + PF);
       const int mb = q % MB, kh = q / MB;
       acc_o[mb] = mfma32(va[q], pb[kh >> 1][kh & 1], acc_o[mb]);
-      if (q == NV / 2) issue_copy(3);
+      if (q == NV / 2) issue(3);
     }
   };
 
-  // ---- main loop, unrolled by the two buffers: tile j sits in buffer j % 2
-  auto step = [&](auto buf_tag, int j) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    // tile j has landed in LDS for this thread's copies; after the barrier,
-    // for everyone's -- and every wave is done with tile j-1, whose buffer
-    // the copy of tile j+1 below overwrites
+  // ---- tiles 0 .. n_full-1 need no per-element predicate for any row of the
+  // workgroup (below the causal diagonal, inside S_k, no key mask)
+  int n_full = 0;
+  if (rb.k_keep == nullptr) {
+    n_full = S_k / kBc;
+    if (causal) n_full = min(n_full, max(rb.q0 + off + 1, 0) / kBc);
+  }
+
+  // ---- prologue: K, V of tile 0 and K of tile 1 in flight; S of tile 0
+  f32x16 s_cur[2];
+  float mx_cur = -INFINITY;
+  if (n_tiles > 0) {
+    const i32x4 rk0 = tile_rsrc(gk, 0), rv0 = tile_rsrc(gv, 0);
+    const i32x4 rk1 = tile_rsrc(gk, min(1, n_tiles - 1));
+#pragma unroll
+    for (int i = 0; i < LD_PER_T; ++i) {
+      copy_part(rk0, 0, i);
+      copy_part(rv0, 2 * TILE_BYTES, i);
+      copy_part(rk1, TILE_BYTES, i);
+    }
+    copy_keep(0);
+    copy_keep(1);
     lds_copy_wait_all();
     __syncthreads();
-    // the copies of tile j+1 are issued in LD_PER_T parts spread over the
-    // computation of tile j (four issue points in tile()).  After the last
-    // tile they re-copy it into the idle buffer (harmless, and it keeps the
-    // tile body free of branches).
-    const int jn = min(j + 1, n_tiles - 1);
-    if (j + 1 < n_tiles) copy_keep(j + 1, BUF ^ 1);
+    qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
+    if (n_full == 0) mask(s_cur, 0);
+    mx_cur = rowmax(s_cur);
+  }
+
+  // ---- iteration j (tile j in buffers BUF = j % 2): S of tile j+1, softmax
+  // and PV of tile j.  Iterations whose next tile every row sees whole run
+  // first, in pairs, through the predicate-free body; the rest (the causal
+  // diagonal, a ragged tail, a key mask, the last tile, an odd leftover)
+  // follow in a second loop.  Keeping the two bodies in separate loops lets
+  // the accumulators stay in one register set.
+  auto iteration = [&](auto buf_tag, auto masked_tag, int j) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // K of tile j+1 and V of tile j have landed for this thread's copies;
+    // after the barrier, for everyone's -- and every wave is done with
+    // iteration j-1, whose buffers (K of tile j, V of tile j-1) the copies
+    // below overwrite
+    lds_copy_wait_all();
+    __syncthreads();
+    // copies of K of tile j+2 (into K buffer BUF) and V of tile j+1 (into V
+    // buffer BUF^1), issued in parts at four points of the iteration.  Past
+    // the last tile they re-copy the last tile into an idle buffer (harmless,
+    // and it keeps the body free of branches).
+    const i32x4 rk = tile_rsrc(gk, min(j + 2, n_tiles - 1));
+    const i32x4 rv = tile_rsrc(gv, min(j + 1, n_tiles - 1));
+    if constexpr (MASKED) copy_keep(j + 2);
     auto issue = [&](int at) {
 #pragma unroll
-      for (int i = 0; i < LD_PER_T; ++i)
-        if (i * 4 / LD_PER_T == at) copy_part(jn, BUF ^ 1, i);
-    };
-    const int k0 = j * kBc;
-    // skip tiles no row of this wave can see
-    const bool wave_active = wave_live && !(causal && k0 > wave_q0 + 31 + off);
-    if (wave_active) {
-      const bool need_mask = (k0 + kBc > S_k) || (causal && k0 + kBc - 1 > wave_q0 + off) ||
-                             (rb.k_keep != nullptr);
-      if (need_mask) {
-        tile(std::integral_constant<bool, true>{}, buf_tag, k0, issue);
-      } else {
-        tile(std::integral_constant<bool, false>{}, buf_tag, k0, issue);
+      for (int i = 0; i < LD_PER_T; ++i) {
+        if (i * 4 / LD_PER_T == at) {
+          copy_part(rk, BUF * TILE_BYTES, i);
+          copy_part(rv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
+        }
       }
+    };
+    rescale(mx_cur);
+    f32x16 s_next[2];
+    if constexpr (!MASKED) {
+      qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
+      softmax_pv(buf_tag, s_cur, issue);
+      mx_cur = rowmax(s_next);
+      s_cur[0] = s_next[0];
+      s_cur[1] = s_next[1];
     } else {
-#pragma unroll
-      for (int i = 0; i < LD_PER_T; ++i) copy_part(jn, BUF ^ 1, i);
+      const bool has_next = j + 1 < n_tiles;
+      if (has_next) {
+        qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
+      } else {
+        issue(0);
+        issue(1);
+      }
+      softmax_pv(buf_tag, s_cur, issue);
+      if (has_next) {
+        mask(s_next, j + 1);
+        mx_cur = rowmax(s_next);
+        s_cur[0] = s_next[0];
+        s_cur[1] = s_next[1];
+      }
     }
   };
-  if (n_tiles > 0) copy_tile(0, 0);
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
+  constexpr std::integral_constant<int, 0> B0{};
+  constexpr std::integral_constant<int, 1> B1{};
+  constexpr std::integral_constant<bool, false> UNMASKED{};
+  constexpr std::integral_constant<bool, true> MASKED_T{};
+  // iteration j is predicate-free when tile j+1 < n_full
+  const int n_pair_end = max(n_full - 1, 0) & ~1;
+  int j = 0;
+  for (; j < n_pair_end; j += 2) {
+    iteration(B0, UNMASKED, j);
+    iteration(B1, UNMASKED, j + 1);
+  }
+  for (; j < n_tiles; j += 2) {
+    iteration(B0, MASKED_T, j);
+    if (j + 1 < n_tiles) iteration(B1, MASKED_T, j + 1);
   }
   lds_copy_wait_all();  // the trailing copies have landed ...
   __syncthreads();      // ... and all reads of the last tile are done before the epilogue reuses LDS

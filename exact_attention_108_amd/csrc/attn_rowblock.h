@@ -94,6 +94,10 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
     }
   }
   if (seq < 0) return false;
+  // t and seq are wave-uniform by construction; say so, so that everything
+  // derived from them lives in scalar registers
+  const int t_u = __builtin_amdgcn_readfirstlane(t);
+  seq = __builtin_amdgcn_readfirstlane(seq);
   const int start = p.cu_seqlens[seq];
   const int len = p.cu_seqlens[seq + 1] - start;
   const int hk = h / p.G;
@@ -106,7 +110,7 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
   r.k_keep = p.k_keep ? p.k_keep + start : nullptr;
   r.S_q = len;
   r.S_k = len;
-  r.q0 = t * kRows;
+  r.q0 = t_u * kRows;
   return true;
 }
 
