@@ -13,10 +13,27 @@ by HIP events recorded on the stream the library launches on.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Prints one JSON line.
+
+HBM traffic of each kernel comes from hardware-counter runs over a fixed
+workload, scaled by what the same counters read for a plain device-to-device
+copy of known size.  Reads are the L2-to-fabric read requests priced by their
+size (TCC_EA0_RDREQ_32B/_64B/_128B: on gfx950 the FETCH_SIZE expression counts
+128-byte requests as 64 bytes); writes are WRITE_SIZE; FETCH_SIZE itself is
+reported beside them:
+
+    rocprofv3 --pmc TCC_EA0_RDREQ_32B TCC_EA0_RDREQ_64B TCC_EA0_RDREQ_128B -f csv -d <dir_r> -o p -- python3 bench.py --traffic-workload
+    rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o p -- python3 bench.py --traffic-workload
+    rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o p -- python3 bench.py --traffic-workload
+    python3 bench.py --traffic-summary <dir_r> <dir_w> <dir_f> > profiles/traffic_<...>.md
+
+The summary records a hash of each kernel's sources; a later bench run reports
+`traffic` only while those sources are unchanged (null otherwise).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +47,13 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (causal-adjusted) + paged-decode KV GB/s, % roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+CSRC = os.path.join(ROOT, "exact_attention_108_amd", "csrc")
+# sources that determine each timed kernel's memory traffic
+KERNEL_SOURCES = {
+    "prefill": ["attn_prefill_bf16.hip", "attn_device.h", "attn_kernels.h", "attn_rowblock.h"],
+    "decode": ["attn_decode_bf16.hip", "attn_device.h", "attn_kernels.h"],
+}
+COPY_BYTES = 1 << 30  # the reference copy kernel moves this many bytes each way
 
 
 def log(*a):
@@ -43,34 +67,39 @@ def to_dev(x, kind):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on a single device "
-              "and no multi-GPU path is built.", file=sys.stderr)
-        sys.exit(2)
+def source_hash(part: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[part]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
+
+def committed_traffic(part: str):
+    """HBM bytes per launch of `part`'s kernel from the newest traffic summary
+    under profiles/ whose recorded source hash matches the current sources."""
+    want = source_hash(part)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")), reverse=True):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    ent = rec.get(part)
+                    if ent and ent.get("source_hash") == want:
+                        return ent["bytes_per_launch"], os.path.basename(path)
+    return None, None
+
+
+def load_inputs(log_fn=lambda *a: None):
     import torch
     import exact_attention_108_amd as ea
     from synth import gen
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
-
-    # ---------------- inputs (host -> HBM, outside the timed region)
     t0 = time.time()
     p2 = gen.make_config(2)
     q2, k2, v2 = to_dev(p2.q, "bf16"), to_dev(p2.k, "bf16"), to_dev(p2.v, "bf16")
     o2 = torch.empty_like(q2)
     l2 = torch.empty((p2.B, p2.A, p2.S_q), dtype=torch.float32, device="cuda")
-    log(f"prefill inputs ready ({time.time() - t0:.1f}s)")
+    log_fn(f"prefill inputs ready ({time.time() - t0:.1f}s)")
 
     t0 = time.time()
     p4 = gen.make_config(4)
@@ -82,8 +111,8 @@ def main():
     ws_bytes = ea.attn_decode_paged_workspace_bytes(p4.B, p4.A, p4.A_kv, p4.d, p4.page_size, p4.seq_lens)
     ws4 = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     kv_bytes = p4.kv_bytes()
-    log(f"decode inputs ready ({time.time() - t0:.1f}s): {kv_bytes / 1e9:.2f} GB of KV, "
-        f"workspace {ws_bytes / 1e6:.1f} MB")
+    log_fn(f"decode inputs ready ({time.time() - t0:.1f}s): {kv_bytes / 1e9:.2f} GB of KV, "
+           f"workspace {ws_bytes / 1e6:.1f} MB")
     p4.k_cache = p4.v_cache = None  # host copies no longer needed
 
     t0 = time.time()
@@ -93,8 +122,9 @@ def main():
     l5 = torch.empty((p5.A, p5.T), dtype=torch.float32, device="cuda")
     cu5 = to_dev(p5.cu_seqlens, "i32")
     qk5 = to_dev(p5.q_keep, "u8")
-    log(f"varlen inputs ready ({time.time() - t0:.1f}s): T={p5.T}")
+    log_fn(f"varlen inputs ready ({time.time() - t0:.1f}s): T={p5.T}")
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
 
     def prefill():
         ea.attn_fwd(q2, k2, v2, o2, l2, scale=p2.scale, causal=True, stream=stream)
@@ -106,7 +136,141 @@ def main():
         ea.attn_fwd_varlen(q5, k5, v5, o5, l5, cu5, p5.cu_seqlens, scale=p5.scale, causal=True, q_keep=qk5,
                            stream=stream)
 
-    parts = [("prefill", prefill), ("decode", decode), ("varlen", varlen)]
+    return dict(p2=p2, p4=p4, p5=p5, kv_bytes=kv_bytes, ws_bytes=ws_bytes, stream=stream,
+                parts=[("prefill", prefill), ("decode", decode), ("varlen", varlen)])
+
+
+def traffic_workload():
+    """Each timed kernel three times, then a plain copy of COPY_BYTES three
+    times (the counter scale reference); nothing is timed."""
+    import torch
+    torch.cuda.set_device(0)
+    w = load_inputs()
+    for name, fn in w["parts"]:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("traffic workload done", flush=True)
+
+
+def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
+    """Markdown summary of three counter runs of --traffic-workload."""
+    import csv
+
+    def per_kernel(d, value_of):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert files, f"no counter_collection.csv under {d}"
+        by = {}
+        for path in files:
+            with open(path) as fh:
+                for r in csv.DictReader(fh):
+                    w = value_of(r["Counter_Name"])
+                    if w is None:
+                        continue
+                    key = (r["Kernel_Name"], r["Dispatch_Id"])
+                    by[key] = by.get(key, 0.0) + w * float(r["Counter_Value"])
+        out = {}
+        for (kname, _), v in by.items():
+            out.setdefault(kname, []).append(v)
+        return out
+
+    def mean(tab):
+        return {k: sum(v) / len(v) for k, v in tab.items()}
+
+    sizes = {"TCC_EA0_RDREQ_32B": 32.0, "TCC_EA0_RDREQ_64B": 64.0, "TCC_EA0_RDREQ_128B": 128.0}
+    read_d = per_kernel(dir_read, lambda c: sizes.get(c))                          # bytes
+    write_d = per_kernel(dir_write, lambda c: 1024.0 if c == "WRITE_SIZE" else None)  # KiB -> bytes
+    fetch_d = per_kernel(dir_fetch, lambda c: 1024.0 if c == "FETCH_SIZE" else None)
+    read, write, fetch = mean(read_d), mean(write_d), mean(fetch_d)
+    nr = {k: len(v) for k, v in read_d.items()}
+
+    def pick(tab, pred):
+        ks = [k for k in tab if pred(k)]
+        assert len(ks) == 1, ks
+        return ks[0]
+
+    # the reference copy: the largest dispatches of the runtime's copy kernel
+    # (the small ones are the input uploads)
+    is_copy = lambda k: "copybuffer" in k.lower()
+    cr, cw, cf = pick(read, is_copy), pick(write, is_copy), pick(fetch, is_copy)
+    read[cr], write[cw], fetch[cf] = max(read_d[cr]), max(write_d[cw]), max(fetch_d[cf])
+    r_scale, w_scale, f_scale = COPY_BYTES / read[cr], COPY_BYTES / write[cw], COPY_BYTES / fetch[cf]
+    kernels = {
+        "prefill": lambda k: "prefill_bf16_kernel<128, false>" in k,
+        "varlen": lambda k: "prefill_bf16_kernel<64, true>" in k,
+        "decode_split": lambda k: "decode_split_kernel" in k,
+        "decode_merge": lambda k: "decode_merge_kernel" in k,
+    }
+    rows, rec = [], {}
+    for part, pred in kernels.items():
+        kr, kw, kf = pick(read, pred), pick(write, pred), pick(fetch, pred)
+        rb, wb, fb = read[kr] * r_scale, write[kw] * w_scale, fetch[kf] * f_scale
+        rows.append((part, kr, nr[kr], read[kr], write[kw], fetch[kf], rb, wb, fb))
+        rec[part] = (rb, wb)
+    out = {"copy_read_scale": r_scale, "copy_write_scale": w_scale, "copy_fetch_size_scale": f_scale,
+           "prefill": {"bytes_per_launch": sum(rec["prefill"]), "read_bytes": rec["prefill"][0],
+                       "write_bytes": rec["prefill"][1], "source_hash": source_hash("prefill")},
+           "decode": {"bytes_per_launch": sum(rec["decode_split"]) + sum(rec["decode_merge"]),
+                      "source_hash": source_hash("decode")}}
+    print("# HBM traffic per launch (L2-to-fabric read requests by size, WRITE_SIZE)\n")
+    print("Commands (repository root, one MI355X):\n")
+    print("    rocprofv3 --pmc TCC_EA0_RDREQ_32B TCC_EA0_RDREQ_64B TCC_EA0_RDREQ_128B -f csv -d <dir_r> -o p "
+          "-- python3 bench.py --traffic-workload")
+    print("    rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o p -- python3 bench.py --traffic-workload")
+    print("    rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o p -- python3 bench.py --traffic-workload")
+    print("    python3 bench.py --traffic-summary <dir_r> <dir_w> <dir_f>\n")
+    print(f"Scale reference: a {COPY_BYTES >> 20} MiB device copy (`{cr[:60]}`) reads "
+          f"{read[cr] / 2**20:.1f} MiB by request size ({r_scale:.4f}x to the true {COPY_BYTES >> 20} MiB), "
+          f"writes {write[cw] / 2**20:.1f} MiB by WRITE_SIZE ({w_scale:.4f}x) and shows "
+          f"{fetch[cf] / 2**20:.1f} MiB by FETCH_SIZE ({f_scale:.4f}x).\n")
+    print("| part | kernel | launches | read req. MiB | WRITE_SIZE MiB | FETCH_SIZE MiB | read MB (scaled) "
+          "| write MB (scaled) | FETCH_SIZE MB (scaled) |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for part, k, n, r, w, f, rb, wb, fb in rows:
+        print(f"| {part} | `{k[:60]}` | {n} | {r / 2**20:.1f} | {w / 2**20:.1f} | {f / 2**20:.1f} | {rb / 1e6:.1f} "
+              f"| {wb / 1e6:.1f} | {fb / 1e6:.1f} |")
+    print()
+    print("traffic-json: " + json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--traffic-workload", action="store_true", help="run the counter workload and exit")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("READ_DIR", "WRITE_DIR", "FETCH_DIR"),
+                    help="summarise three counter runs of --traffic-workload and exit")
+    args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.traffic_workload:
+        traffic_workload()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on a single device "
+              "and no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    # ---------------- inputs (host -> HBM, outside the timed region)
+    w = load_inputs(log)
+    p2, p4, p5, kv_bytes, ws_bytes, stream = w["p2"], w["p4"], w["p5"], w["kv_bytes"], w["ws_bytes"], w["stream"]
+    parts = w["parts"]
 
     for _ in range(args.warmup):
         for _, fn in parts:
@@ -138,6 +302,8 @@ def main():
     tf2 = f2 / (avg["prefill"] * 1e-3) / 1e12
     tf5 = f5 / (avg["varlen"] * 1e-3) / 1e12
     gbs4 = kv_bytes / (avg["decode"] * 1e-3) / 1e9
+    traffic_prefill, traffic_src = committed_traffic("prefill")
+    traffic_decode, _ = committed_traffic("decode")
 
     out = {
         "metric": METRIC,
@@ -159,12 +325,17 @@ def main():
                         "causal": True, "flops_causal_adjusted": f2},
         },
         "roofline": {"bound": "mfma", "achieved": round(tf2, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf2 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tf2 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic_prefill is None else round(traffic_prefill),
+                     "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
+                     "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
                      "kernel": "prefill_bf16_kernel<128,false>", "avg_launch_ms": round(avg["prefill"], 5),
                      "median_launch_ms": round(med["prefill"], 5)},
         "decode": {"metric": "paged-decode KV GB/s", "value": round(gbs4, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs4, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                "frac": round(gbs4 / PEAK_HBM_GBPS, 4), "traffic": None},
+                                "frac": round(gbs4 / PEAK_HBM_GBPS, 4),
+                                "traffic": None if traffic_decode is None else round(traffic_decode),
+                                "traffic_unit": "bytes per launch (split + merge, HBM, counter-scaled)"},
                    "avg_ms": round(avg["decode"], 5), "median_ms": round(med["decode"], 5),
                    "kv_bytes": kv_bytes, "total_tokens": int(np.sum(p4.seq_lens, dtype=np.int64)),
                    "workspace_bytes": ws_bytes},

@@ -144,6 +144,13 @@ class Dense:
         f = 4.0 * self.B * self.A * self.S_q * self.S_k * self.d
         return f / 2 if self.causal else f
 
+    def io_bytes(self) -> int:
+        """Bytes each launch must move at least once: Q, K, V read, O written
+        (element size of `dtype`) and the fp32 LSE written."""
+        e = 2 if self.dtype == "bf16" else 4
+        return (e * self.d * (2 * self.B * self.A * self.S_q + 2 * self.B * self.A_kv * self.S_k)
+                + 4 * self.B * self.A * self.S_q)
+
 
 @dataclass
 class Varlen:
