@@ -72,6 +72,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   p.S_q = S_q;
   p.S_k = S_k;
   p.n_qt = (int)n_qt;
+  attn::plan_dense_order(p);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, false, st) : attn::launch_prefill_f32(p, false, st);
   return launch_status(e);

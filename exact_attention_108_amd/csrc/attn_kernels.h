@@ -26,7 +26,32 @@ struct FwdParams {
   int causal;
   float scale;                // softmax scale (> 0)
   float scale_log2;           // scale * log2(e)
+  int xcd_heads;              // dense: (batch, head) pairs per XCD block, 0 = plain order
+  int xcd_group;              // dense: heads whose query tiles are issued together
 };
+
+// Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin
+// by index, and each XCD has its own L2.  When B*A is a multiple of 8, XCD x
+// is given the contiguous (batch, head) block [x*H, (x+1)*H), H = B*A/8
+// (query heads that share a KV head stay together), and it takes its heads
+// in groups of `group` (up to 8), each group's query tiles heaviest first, so
+// the tiles of a head stream the same K/V at about the same time and the
+// XCD's L2 serves most re-reads.  Groups of 8 keep enough heavy tiles at the
+// head of each XCD's queue that the grid still ends evenly (groups of 4 fetch
+// less but leave a tail of long tiles).  Otherwise: query tiles heaviest
+// first across all heads.
+constexpr int kXcds = 8;
+inline void plan_dense_order(FwdParams& p) {
+  const int bh = p.B * p.A;
+  p.xcd_heads = 0;
+  p.xcd_group = 0;
+  if (bh % kXcds != 0) return;
+  const int h = bh / kXcds;
+  int g = 8;
+  while (g > 1 && h % g != 0) g >>= 1;
+  p.xcd_heads = h;
+  p.xcd_group = g;
+}
 
 // bf16 prefill (d in {64, 128}).  Returns hipSuccess or the launch error.
 hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stream);

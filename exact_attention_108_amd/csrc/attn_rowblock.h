@@ -23,8 +23,18 @@ template <int kRows>
 __device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_bytes) {
   const int lin = blockIdx.x;
   const int bh_n = p.A * p.B;
-  const int qt = p.n_qt - 1 - lin / bh_n;
-  const int bh = lin % bh_n;
+  int qt, bh;
+  if (p.xcd_heads > 0) {
+    // XCD-blocked order (see plan_dense_order)
+    const int x = lin % kXcds, i = lin / kXcds;
+    const int per_group = p.xcd_group * p.n_qt;
+    const int grp = i / per_group, r = i % per_group;
+    qt = p.n_qt - 1 - r / p.xcd_group;
+    bh = x * p.xcd_heads + grp * p.xcd_group + r % p.xcd_group;
+  } else {
+    qt = p.n_qt - 1 - lin / bh_n;
+    bh = lin % bh_n;
+  }
   const int h = bh % p.A, b = bh / p.A;
   const int hk = h / p.G;
   RowBlock r;
