@@ -28,6 +28,11 @@ reported beside them:
 
 The summary records a hash of each kernel's sources; a later bench run reports
 `traffic` only while those sources are unchanged (null otherwise).
+
+Matrix-core utilisation of the prefill kernels, from one counter run:
+
+    rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY -f csv -d <dir_m> -o p -- python3 bench.py --traffic-workload
+    python3 bench.py --counter-summary <dir_m> > profiles/mfma_<...>.md
 """
 from __future__ import annotations
 
@@ -113,7 +118,6 @@ def load_inputs(log_fn=lambda *a: None):
     kv_bytes = p4.kv_bytes()
     log_fn(f"decode inputs ready ({time.time() - t0:.1f}s): {kv_bytes / 1e9:.2f} GB of KV, "
            f"workspace {ws_bytes / 1e6:.1f} MB")
-    p4.k_cache = p4.v_cache = None  # host copies no longer needed
 
     t0 = time.time()
     p5 = gen.make_config(5)
@@ -240,6 +244,52 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
     print("traffic-json: " + json.dumps(out))
 
 
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def counter_summary(d: str):
+    """Markdown summary of one SQ counter run of --traffic-workload."""
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert files, f"no counter_collection.csv under {d}"
+    by, span = {}, {}
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                by.setdefault(key, {})
+                by[key][r["Counter_Name"]] = by[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                span[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    kernels = {"prefill": "prefill_bf16_kernel<128, false>", "varlen": "prefill_bf16_kernel<64, true>",
+               "decode_split": "decode_split_kernel"}
+    print("# Matrix-core utilisation per launch (SQ / GRBM counters)\n")
+    print("Commands (repository root, one MI355X):\n")
+    print("    rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
+          "SQ_INSTS_VALU_TRANS_F32 SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY -f csv -d <dir_m> -o p "
+          "-- python3 bench.py --traffic-workload")
+    print("    python3 bench.py --counter-summary <dir_m>\n")
+    print("Definitions: kernel cycles = GRBM_GUI_ACTIVE / 8 (one value per XCD); MFMA busy = "
+          "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles); clock = kernel cycles / dispatch duration; "
+          "waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles).\n")
+    print("| part | launches | duration us | kernel cycles | clock GHz | MFMA instr | MFMA busy | VALU instr / MFMA "
+          "| exp / MFMA | wave time waiting |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for part, pat in kernels.items():
+        rows = [(v, span[k]) for k, v in by.items() if pat in k[0]]
+        if not rows:
+            continue
+        n = len(rows)
+        avg = lambda c: sum(v.get(c, 0.0) for v, _ in rows) / n
+        dur = sum(t for _, t in rows) / n
+        cyc = avg("GRBM_GUI_ACTIVE") / N_XCD
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (N_SIMD * cyc) if cyc else 0.0
+        mf = avg("SQ_INSTS_MFMA")
+        print(f"| {part} | {n} | {dur / 1e3:.1f} | {cyc:.0f} | {cyc / dur:.2f} | {mf:.3g} | {100 * busy:.1f}% "
+              f"| {(avg('SQ_INSTS_VALU') - mf) / max(mf, 1):.2f} | {avg('SQ_INSTS_VALU_TRANS_F32') / max(mf, 1):.2f} "
+              f"| {100 * avg('SQ_WAIT_ANY') / max(avg('SQ_WAVE_CYCLES'), 1):.1f}% |")
+    print("\n(SQ_INSTS_VALU counts the MFMA instructions too; they are subtracted above.)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,7 +300,11 @@ def main():
     ap.add_argument("--traffic-workload", action="store_true", help="run the counter workload and exit")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("READ_DIR", "WRITE_DIR", "FETCH_DIR"),
                     help="summarise three counter runs of --traffic-workload and exit")
+    ap.add_argument("--counter-summary", metavar="DIR", help="summarise one SQ counter run and exit")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
@@ -296,6 +350,8 @@ def main():
     ms = {name: np.array([a.elapsed_time(b) for a, b in evs]) for name, evs in events.items()}
     avg = {k: float(v.mean()) for k, v in ms.items()}
     med = {k: float(np.median(v)) for k, v in ms.items()}
+    mn = {k: float(v.min()) for k, v in ms.items()}
+    ceil = measured_ceilings(w["stream"])
 
     f2 = p2.flops()
     f5 = p5.flops()
@@ -330,23 +386,135 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
                      "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
                      "kernel": "prefill_bf16_kernel<128,false>", "avg_launch_ms": round(avg["prefill"], 5),
-                     "median_launch_ms": round(med["prefill"], 5)},
+                     "median_launch_ms": round(med["prefill"], 5), "min_launch_ms": round(mn["prefill"], 5),
+                     "measured_ceiling": {"what": "torch.matmul bf16 8192^3 on the same GPU",
+                                          "TFLOP/s": ceil["gemm_tflops"],
+                                          "frac": round(tf2 / ceil["gemm_tflops"], 4)}},
         "decode": {"metric": "paged-decode KV GB/s", "value": round(gbs4, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs4, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": round(gbs4 / PEAK_HBM_GBPS, 4),
                                 "traffic": None if traffic_decode is None else round(traffic_decode),
                                 "traffic_unit": "bytes per launch (split + merge, HBM, counter-scaled)"},
+                   "measured_ceiling": {"what": "torch sum over 4 GiB of fp32 (read-only stream) on the same GPU",
+                                        "GB/s": ceil["read_gbps"], "frac": round(gbs4 / ceil["read_gbps"], 4),
+                                        "copy_GB/s": ceil["copy_gbps"]},
                    "avg_ms": round(avg["decode"], 5), "median_ms": round(med["decode"], 5),
+                   "min_ms": round(mn["decode"], 5),
                    "kv_bytes": kv_bytes, "total_tokens": int(np.sum(p4.seq_lens, dtype=np.int64)),
                    "workspace_bytes": ws_bytes},
         "varlen": {"metric": "varlen causal prefill TFLOP/s", "value": round(tf5, 2), "unit": "TFLOP/s",
                    "frac_of_bf16_peak": round(tf5 / PEAK_BF16_TFLOPS, 4), "avg_ms": round(avg["varlen"], 5),
+                   "median_ms": round(med["varlen"], 5), "min_ms": round(mn["varlen"], 5),
                    "T": p5.T, "flops_causal_adjusted": f5, "masked_rows": int((p5.q_keep == 0).sum())},
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
+        out["decode"]["cpu_baseline"] = cpu_baseline_decode(p4, kv_bytes, args.cpu_seconds / 3)
+        out["varlen"]["cpu_baseline"] = cpu_baseline_varlen(p5, args.cpu_seconds / 3)
     print(json.dumps(out), flush=True)
+
+
+def measured_ceilings(stream) -> dict:
+    """What this GPU sustains on plain library work, as a second reference
+    beside the spec peaks: a bf16 GEMM through torch.matmul, a 2 GiB
+    device-to-device copy and a read-only 4 GiB reduction."""
+    import torch
+    out = {}
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["gemm_tflops"] = round(2.0 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    del a, b
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["copy_gbps"] = round(2.0 * src.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    # read-only stream: a sum over 4 GiB of fp32 (what decode does: read, little written)
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        x.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["read_gbps"] = round(4.0 * x.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del x
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_decode(p4, kv_bytes: float, target_s: float) -> dict:
+    """The fp64 oracle on uniformly drawn (sequence, head) rows of the paged
+    decode workload, extrapolated by the rows' share of the KV tokens."""
+    import oracle
+    orc = oracle.default()
+    total_rows = p4.B * p4.A
+    rng = np.random.default_rng(2025)
+    order = rng.permutation(total_rows)
+    lens = np.repeat(p4.seq_lens.astype(np.float64), p4.A)
+    spent, done, work = 0.0, 0, 0.0
+    while done < total_rows and spent < target_s:
+        rows = order[done:done + 16]
+        t0 = time.perf_counter()
+        orc.decode_paged(p4.q, p4.k_cache, p4.v_cache, p4.block_table, p4.seq_lens, dtype="bf16",
+                         scale=p4.scale, rows=rows)
+        spent += time.perf_counter() - t0
+        done += len(rows)
+        work += lens[rows].sum()
+    est = spent * lens.sum() / work
+    log(f"oracle decode: {done} rows in {spent:.1f}s")
+    return {"value": round(kv_bytes / est / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{done} uniformly drawn (sequence, head) rows of the paged decode ({spent:.1f}s), "
+                      f"extrapolated by their share of KV tokens to all {total_rows} rows ({est:.0f}s)"}
+
+
+def cpu_baseline_varlen(p5, target_s: float) -> dict:
+    """The fp64 oracle on uniformly drawn query rows of the varlen workload,
+    extrapolated by the rows' share of visible keys (causal within a sequence)."""
+    import oracle
+    orc = oracle.default()
+    cu = p5.cu_seqlens.astype(np.int64)
+    pos = np.arange(p5.T, dtype=np.int64) - np.repeat(cu[:-1], np.diff(cu))  # position within the sequence
+    cost = np.tile((pos + 1).astype(np.float64), p5.A)  # keys each (head, row) sees
+    total_rows = p5.A * p5.T
+    rng = np.random.default_rng(2026)
+    order = rng.permutation(total_rows)
+    spent, done, work = 0.0, 0, 0.0
+    while done < total_rows and spent < target_s:
+        rows = order[done:done + 256]
+        t0 = time.perf_counter()
+        orc.attn_fwd_varlen(p5.q, p5.k, p5.v, p5.cu_seqlens, dtype="bf16", scale=p5.scale, causal=True,
+                            q_keep=p5.q_keep, rows=rows)
+        spent += time.perf_counter() - t0
+        done += len(rows)
+        work += cost[rows].sum()
+    est = spent * cost.sum() / work
+    log(f"oracle varlen: {done} rows in {spent:.1f}s")
+    return {"value": round(p5.flops() / est / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} uniformly drawn query rows of the varlen workload ({spent:.1f}s), extrapolated "
+                      f"by their share of visible keys to all {total_rows} rows ({est:.0f}s)"}
 
 
 def cpu_baseline(p2, target_s: float) -> dict:
