@@ -60,6 +60,12 @@ DENSE_CASES = [
     (2, 4, 2, 257, 384, 64, True),
     (1, 1, 1, 1, 700, 128, True),
     (1, 2, 1, 5, 0, 128, True),
+    # B*A a multiple of 8: each XCD gets a contiguous block of (batch, head)
+    # pairs, taken in head groups of 8 (first), 2 (with 16 query heads per KV
+    # head) and 1 (three heads per XCD)
+    (2, 32, 8, 200, 200, 128, True),
+    (1, 16, 1, 130, 130, 128, True),
+    (3, 8, 8, 150, 150, 64, True),
 ]
 
 
