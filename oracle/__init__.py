@@ -25,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "attn_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-_DT = {"f32": 0, "bf16": 1}
+_DT = {"f32": 0, "bf16": 1, "f64": 2}  # f64: test inputs for the finite-difference gradient pins
 
 
 def build(src: str = SRC, out: str = LIB, werror: bool = True) -> str:
@@ -55,7 +55,10 @@ class Oracle:
                                                     i32, vp, vp, vp, i64, vp, vp]
         self.lib.oracle_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                                  i32, f32, vp, i64, vp, vp]
-        for f in (self.lib.oracle_attn_fwd, self.lib.oracle_attn_fwd_varlen, self.lib.oracle_decode_paged):
+        self.lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                             vp, vp, vp, vp, vp]
+        for f in (self.lib.oracle_attn_fwd, self.lib.oracle_attn_fwd_varlen, self.lib.oracle_decode_paged,
+                  self.lib.oracle_attn_bwd):
             f.restype = ctypes.c_int
         self.lib.oracle_num_threads.restype = ctypes.c_int
 
@@ -68,6 +71,8 @@ class Oracle:
             return np.ascontiguousarray(x, dtype=np.uint16)
         if dtype == "f32":
             return np.ascontiguousarray(x, dtype=np.float32)
+        if dtype == "f64":
+            return np.ascontiguousarray(x, dtype=np.float64)
         raise ValueError(f"unknown dtype {dtype!r}")
 
     @staticmethod
@@ -133,6 +138,28 @@ class Oracle:
         if r is None:
             return o.reshape(A, T, d), lse.reshape(A, T)
         return o, lse
+
+    def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None):
+        """Gradient of attn_fwd: q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d].
+        Returns (dq, dk, dv) in fp64 with the shapes of q, k and v."""
+        q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
+        if q.ndim != 4 or k.shape != v.shape or do.shape != q.shape:
+            raise ValueError("q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d]")
+        B, A, S_q, d = q.shape
+        A_kv, S_k = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != d or A % A_kv:
+            raise ValueError("k/v must be [B, A_kv, S_k, d] with A % A_kv == 0")
+        qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
+        kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
+        dq = np.empty((B, A, S_q, d), dtype=np.float64)
+        dk = np.empty((B, A_kv, S_k, d), dtype=np.float64)
+        dv = np.empty((B, A_kv, S_k, d), dtype=np.float64)
+        rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _DT[dtype], B, A, A_kv, S_q, S_k, d,
+                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(dq), _ptr(dk),
+                                      _ptr(dv))
+        if rc != 0:
+            raise ValueError("oracle_attn_bwd rejected its arguments")
+        return dq, dk, dv
 
     def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None):
         """Paged decode.  q [B,A,d]; caches [P, page_size, A_kv, d]; rows = b*A + h."""

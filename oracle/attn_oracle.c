@@ -36,6 +36,23 @@
  * block_table[b][t / page_size] at offset t % page_size (page "Attention
  * Kernel", section "Paged 与 ragged KV").
  *
+ * Gradient (oracle_attn_bwd): the exact derivative of the batched prefill
+ * above with respect to q, k and v, for an incoming output gradient dO.  The
+ * probabilities are recomputed from Q and K, as the backward pass of page
+ * "Attention 算子加速史" (FAQ Q1) and page "Attention Kernel" (section
+ * "Backward 与重计算") describe; the chain rule through O = P V,
+ * P = softmax(S), S = scale Q K^T + M, row by row:
+ *
+ *   dV_j  += P_ij dO_i
+ *   dP_ij  = dO_i . v_j
+ *   D_i    = sum_j P_ij dP_ij
+ *   dS_ij  = P_ij (dP_ij - D_i)
+ *   dQ_i   = scale * sum_j dS_ij k_j
+ *   dK_j  += scale * dS_ij q_i
+ *
+ * Masked entries (P_ij = 0) pass no gradient; a fully masked row has dQ_i = 0.
+ * Under GQA, dK and dV of a KV head sum over the query heads that read it.
+ *
  * Return value: 0 on success, -1 on invalid arguments.
  */
 #include <math.h>
@@ -43,10 +60,16 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+/* element types of the inputs; OR_F64 exists for the finite-difference pins
+ * of the gradient, which need inputs perturbed below fp32 resolution */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
+
+static int dt_ok(int dt) { return dt == OR_F32 || dt == OR_BF16 || dt == OR_F64; }
 
 static double ld(const void *p, int64_t idx, int dt)
 {
+    if (dt == OR_F64)
+        return ((const double *)p)[idx];
     if (dt == OR_F32)
         return (double)((const float *)p)[idx];
     uint32_t u = (uint32_t)((const uint16_t *)p)[idx] << 16;
@@ -138,7 +161,7 @@ int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
 {
     if (B <= 0 || A <= 0 || A_kv <= 0 || S_q < 0 || S_k < 0 || d <= 0 || A % A_kv != 0)
         return -1;
-    if (dt != OR_F32 && dt != OR_BF16)
+    if (!dt_ok(dt))
         return -1;
     int64_t total = (int64_t)B * A * S_q;
     if (rows == NULL)
@@ -186,6 +209,98 @@ int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
 }
 
 /*
+ * Gradient of the batched prefill (see the header).  do_ has q's layout and
+ * element type.  dq: [B, A, S_q, d]; dk, dv: [B, A_kv, S_k, d]; all doubles,
+ * fully written.  One thread owns one (batch, KV head) and every query row
+ * that reads it, so the dK / dV sums need no synchronisation.
+ */
+int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *do_, int dt,
+                    int B, int A, int A_kv, int S_q, int S_k, int d, float scale, int causal,
+                    const uint8_t *q_keep, const uint8_t *k_keep,
+                    double *dq, double *dk, double *dv)
+{
+    if (B <= 0 || A <= 0 || A_kv <= 0 || S_q < 0 || S_k < 0 || d <= 0 || A % A_kv != 0)
+        return -1;
+    if (!dt_ok(dt))
+        return -1;
+    const int G = A / A_kv;
+    const double sc = (double)scale;
+    int err = 0;
+#pragma omp parallel
+    {
+        struct scratch w;
+        int bad = scratch_alloc(&w, S_k);
+        double *dp = malloc((size_t)(S_k > 0 ? S_k : 1) * sizeof *dp);
+        double *o = malloc((size_t)d * sizeof *o);
+        if (!dp || !o)
+            bad = 1;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bk = 0; bk < (int64_t)B * A_kv; ++bk) {
+            int b = (int)(bk / A_kv), hk = (int)(bk % A_kv);
+            int64_t kv_base = bk * S_k * (int64_t)d;
+            double *dkg = dk + kv_base, *dvg = dv + kv_base;
+            for (int64_t x = 0; x < (int64_t)S_k * d; ++x)
+                dkg[x] = dvg[x] = 0.0;
+            if (bad)
+                continue;
+            for (int g = 0; g < G; ++g) {
+                int h = hk * G + g;
+                for (int i = 0; i < S_q; ++i) {
+                    int64_t id = ((int64_t)b * A + h) * S_q + i;
+                    double *dqi = dq + id * d;
+                    for (int e = 0; e < d; ++e)
+                        dqi[e] = 0.0;
+                    int row_masked = q_keep && !q_keep[(int64_t)b * S_q + i];
+                    for (int j = 0; j < S_k; ++j) {
+                        w.off[j] = kv_base + (int64_t)j * d;
+                        int visible = !row_masked;
+                        if (causal && (int64_t)j > (int64_t)i + (S_k - S_q))
+                            visible = 0;
+                        if (k_keep && !k_keep[(int64_t)b * S_k + j])
+                            visible = 0;
+                        w.vis[j] = (unsigned char)visible;
+                    }
+                    double lse;
+                    attend_row(q, id * d, k, v, dt, w.off, w.vis, S_k, d, sc, w.s, w.p, o, &lse);
+                    if (lse == -INFINITY)
+                        continue;  /* fully masked row: no gradient anywhere */
+                    double D = 0.0;
+                    for (int j = 0; j < S_k; ++j) {
+                        if (!w.vis[j] || w.p[j] == 0.0) {
+                            dp[j] = 0.0;
+                            continue;
+                        }
+                        double acc = 0.0;
+                        for (int e = 0; e < d; ++e)
+                            acc += ld(do_, id * d + e, dt) * ld(v, w.off[j] + e, dt);
+                        dp[j] = acc;
+                        D += w.p[j] * acc;
+                    }
+                    for (int j = 0; j < S_k; ++j) {
+                        if (!w.vis[j] || w.p[j] == 0.0)
+                            continue;
+                        double ds = w.p[j] * (dp[j] - D);
+                        for (int e = 0; e < d; ++e) {
+                            dqi[e] += sc * ds * ld(k, w.off[j] + e, dt);
+                            dkg[(int64_t)j * d + e] += sc * ds * ld(q, id * d + e, dt);
+                            dvg[(int64_t)j * d + e] += w.p[j] * ld(do_, id * d + e, dt);
+                        }
+                    }
+                }
+            }
+        }
+        if (bad) {
+#pragma omp atomic write
+            err = 1;
+        }
+        free(dp);
+        free(o);
+        scratch_free(&w);
+    }
+    return err ? -1 : 0;
+}
+
+/*
  * Packed varlen prefill.  q, o: [A, T, d]; k, v: [A_kv, T, d];
  * cu_seqlens: [n_seq + 1], non-decreasing, cu[0] = 0, cu[n_seq] = T.
  * Query t of sequence s sees keys of the same sequence only; causal compares
@@ -199,7 +314,7 @@ int oracle_attn_fwd_varlen(const void *q, const void *k, const void *v, int dt,
 {
     if (n_seq < 0 || T < 0 || A <= 0 || A_kv <= 0 || d <= 0 || A % A_kv != 0 || !cu)
         return -1;
-    if (dt != OR_F32 && dt != OR_BF16)
+    if (!dt_ok(dt))
         return -1;
     if (cu[0] != 0 || cu[n_seq] != T)
         return -1;
@@ -274,7 +389,7 @@ int oracle_decode_paged(const void *q, const void *k_cache, const void *v_cache,
     if (B <= 0 || A <= 0 || A_kv <= 0 || d <= 0 || A % A_kv != 0 || page_size <= 0 ||
         max_pages < 0 || num_pages < 0)
         return -1;
-    if (dt != OR_F32 && dt != OR_BF16)
+    if (!dt_ok(dt))
         return -1;
     int64_t maxlen = 0;
     for (int b = 0; b < B; ++b) {

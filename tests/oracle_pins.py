@@ -409,4 +409,130 @@ def pin_paged_brute_force(orc):
     del rng
 
 
+# ---- gradient (oracle_attn_bwd): the exact derivative of the forward above.
+# Pinned against central finite differences of the (already pinned) forward
+# in fp64, closed forms and invariants of the softmax Jacobian.
+
+def _bwd_problem(B, A, A_kv, S_q, S_k, d, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, A, S_q, d))
+    k = rng.standard_normal((B, A_kv, S_k, d))
+    v = rng.standard_normal((B, A_kv, S_k, d))
+    do = rng.standard_normal((B, A, S_q, d))
+    return q, k, v, do
+
+
+def _loss(orc, q, k, v, do, scale, causal, q_keep=None, k_keep=None):
+    o, _ = orc.attn_fwd(q, k, v, dtype="f64", scale=scale, causal=causal, q_keep=q_keep, k_keep=k_keep)
+    return float(np.sum(o.reshape(do.shape) * do))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every entry of dQ, dK, dV equals the central difference of
+    L = sum(O * dO) computed with the forward oracle (h = 1e-6, fp64)."""
+    cases = [  # B, A, A_kv, S_q, S_k, d, causal, masks
+        (1, 2, 1, 3, 4, 3, True, False),
+        (1, 2, 2, 4, 3, 2, False, True),
+        (2, 2, 1, 3, 3, 2, True, True),
+    ]
+    h = 1e-6
+    for n, (B, A, A_kv, S_q, S_k, d, causal, masks) in enumerate(cases):
+        q, k, v, do = _bwd_problem(B, A, A_kv, S_q, S_k, d, 100 + n)
+        scale = 0.6875  # exact in fp32
+        qk = kk = None
+        if masks:
+            qk = np.ones((B, S_q), np.uint8)
+            qk[0, 1] = 0
+            kk = np.ones((B, S_k), np.uint8)
+            kk[-1, 0] = 0
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=scale, causal=causal, q_keep=qk, k_keep=kk)
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (_loss(orc, *args_p, do, scale, causal, qk, kk) -
+                            _loss(orc, *args_m, do, scale, causal, qk, kk)) / (2 * h)
+            err = np.max(np.abs(num - g))
+            assert err <= 1e-7, (n, name, err)
+
+
+def pin_bwd_two_keys(orc):
+    """One query, two keys: with a = s_1 - s_2, dS_1 = -dS_2 =
+    sigmoid(a) sigmoid(-a) (dP_1 - dP_2), dV_1 = sigmoid(a) dO, dV_2 = sigmoid(-a) dO."""
+    q, k, v, do = _bwd_problem(1, 1, 1, 1, 2, 3, 7)
+    scale = 0.875  # exact in fp32, the oracle's scale type
+    s = scale * (k[0, 0] @ q[0, 0, 0])
+    a = s[0] - s[1]
+    p1, p2 = expit(a), expit(-a)
+    dp = v[0, 0] @ do[0, 0, 0]
+    ds1 = p1 * p2 * (dp[0] - dp[1])
+    dq_ref = scale * (ds1 * k[0, 0, 0] - ds1 * k[0, 0, 1])
+    dk_ref = np.stack([scale * ds1 * q[0, 0, 0], -scale * ds1 * q[0, 0, 0]])
+    dv_ref = np.stack([p1 * do[0, 0, 0], p2 * do[0, 0, 0]])
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=scale)
+    assert np.allclose(dq[0, 0, 0], dq_ref, rtol=0, atol=1e-13)
+    assert np.allclose(dk[0, 0], dk_ref, rtol=0, atol=1e-13)
+    assert np.allclose(dv[0, 0], dv_ref, rtol=0, atol=1e-13)
+
+
+def pin_bwd_single_key(orc):
+    """A single visible key: O = v, so dV = dO and dQ = dK = 0."""
+    q, k, v, do = _bwd_problem(1, 2, 1, 1, 1, 4, 8)
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.5)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    assert np.allclose(dv[0, 0, 0], do[0, 0, 0] + do[0, 1, 0], rtol=0, atol=1e-15)
+
+
+def pin_bwd_uniform_values(orc):
+    """All value rows equal: O does not depend on the scores, so dQ = dK = 0,
+    and dV_j = sum_i P_ij dO_i with P from a library softmax."""
+    q, k, v, do = _bwd_problem(1, 1, 1, 3, 5, 2, 9)
+    v[:] = v[0, 0, 0]
+    scale = 0.625  # exact in fp32, the oracle's scale type
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=scale)
+    assert np.max(np.abs(dq)) < 1e-14 and np.max(np.abs(dk)) < 1e-14
+    P = softmax(scale * q[0, 0] @ k[0, 0].T, axis=1)
+    assert np.allclose(dv[0, 0], P.T @ do[0, 0], rtol=0, atol=1e-13)
+
+
+def pin_bwd_key_gradients_sum_to_zero(orc):
+    """Each row of dS sums to zero (softmax Jacobian), so sum_j dK_j = 0 for
+    every (batch, KV head), with masks too."""
+    q, k, v, do = _bwd_problem(2, 4, 2, 6, 7, 3, 10)
+    kk = np.ones((2, 7), np.uint8)
+    kk[1, 3] = 0
+    _, dk, _ = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.8, causal=True, k_keep=kk)
+    assert np.max(np.abs(dk.sum(axis=2))) < 1e-12
+    assert np.max(np.abs(dk)) > 1e-3
+
+
+def pin_bwd_gqa_equals_repeated_heads(orc):
+    """GQA gradients equal those of the MHA problem with each KV head repeated
+    G times, dK and dV summed over the repeats."""
+    q, k, v, do = _bwd_problem(1, 4, 2, 5, 6, 3, 11)
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.7, causal=True)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    dq2, dk2, dv2 = orc.attn_bwd(q, kr, vr, do, dtype="f64", scale=0.7, causal=True)
+    assert np.allclose(dq, dq2, rtol=0, atol=1e-13)
+    assert np.allclose(dk, dk2.reshape(1, 2, 2, 6, 3).sum(axis=2), rtol=0, atol=1e-13)
+    assert np.allclose(dv, dv2.reshape(1, 2, 2, 6, 3).sum(axis=2), rtol=0, atol=1e-13)
+
+
+def pin_bwd_masked_row_inert(orc):
+    """A query row whose keep flag is 0 has dQ = 0 and its dO moves nothing."""
+    q, k, v, do = _bwd_problem(1, 2, 2, 4, 4, 3, 12)
+    qk = np.ones((1, 4), np.uint8)
+    qk[0, 2] = 0
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.5, q_keep=qk)
+    assert np.all(dq[:, :, 2] == 0)
+    do2 = do.copy()
+    do2[:, :, 2] += 5.0
+    _, dk2, dv2 = orc.attn_bwd(q, k, v, do2, dtype="f64", scale=0.5, q_keep=qk)
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,12 @@ MUTANTS = [
     ("last head-dim term dropped", "for (int e = 0; e < d; ++e)\n                dot +=", "for (int e = 0; e < d - 1; ++e)\n                dot +=", 0),
     ("fully masked row not guarded", "if (m == -INFINITY) {", "if (0) {", 0),
     ("row max taken as first score", "if (s[j] > m)\n            m = s[j];", "if (j == 0)\n            m = s[j];", 0),
+    ("gradient: D term dropped", "double ds = w.p[j] * (dp[j] - D);", "double ds = w.p[j] * dp[j];", 0),
+    ("gradient: dK scale dropped", "dkg[(int64_t)j * d + e] += sc * ds", "dkg[(int64_t)j * d + e] += ds", 0),
+    ("gradient: dV weighted by dS", "dvg[(int64_t)j * d + e] += w.p[j] *", "dvg[(int64_t)j * d + e] += ds *", 0),
+    ("gradient: dQ built from V", "dqi[e] += sc * ds * ld(k,", "dqi[e] += sc * ds * ld(v,", 0),
+    ("gradient: dP built from K", "acc += ld(do_, id * d + e, dt) * ld(v, w.off[j] + e, dt);",
+     "acc += ld(do_, id * d + e, dt) * ld(k, w.off[j] + e, dt);", 0),
 ]
 
 BATTERY = r"""
