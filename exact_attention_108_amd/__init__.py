@@ -3,7 +3,7 @@
 The functions here only marshal arguments (tensor pointers, sizes, the current
 HIP stream) into the C ABI of ``include/attn.h``; every step of the computation
 runs in the library's HIP kernels.  Importing fails if the library has not been
-built (``python -m exact_attention_108_amd.build``): there is no fallback path.
+built (``python exact_attention_108_amd/build.py``): there is no fallback path.
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
@@ -11,6 +11,8 @@ from ._binding import (  # noqa: F401
     AttnError,
     LIB_PATH,
     attn_abi_version,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
     attn_decode_paged,
     attn_decode_paged_workspace_bytes,
     attn_fwd,

@@ -15,7 +15,7 @@ import torch  # noqa: F401
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_mi355x.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_108_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python exact_attention_108_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -38,6 +38,11 @@ _lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _
 _lib.attn_decode_paged.restype = _i
 _lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _vp]
 _lib.attn_decode_paged_workspace_bytes.restype = _sz
+_lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                          ctypes.POINTER(_Mask), _i, _vp, _sz, _vp]
+_lib.attn_bwd.restype = _i
+_lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
+_lib.attn_bwd_workspace_bytes.restype = _sz
 _lib.attn_status_string.argtypes = [_i]
 _lib.attn_status_string.restype = ctypes.c_char_p
 _lib.attn_abi_version.argtypes = []
@@ -61,7 +66,7 @@ def attn_abi_version() -> int:
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
-            "attn_status_string", "attn_abi_version"]
+            "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version"]
 
 
 def _torch():
@@ -207,3 +212,40 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host,
                                 block_table.shape[1], num_pages, float(scale), _dtype_code(q),
                                 _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_decode_paged")
+
+
+def attn_bwd_workspace_bytes(B: int, A: int, S_q: int) -> int:
+    return int(_lib.attn_bwd_workspace_bytes(B, A, S_q))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, causal: bool = False, q_keep=None,
+             k_keep=None, stream=None):
+    """dQ, dK, dV of attn_fwd.  q/o/dout/dq [B,A,S_q,d], k/v/dk/dv [B,A_kv,S_k,d], lse [B,A,S_q] fp32 (the
+    forward's); workspace a uint8 device tensor of at least attn_bwd_workspace_bytes(B, A, S_q) bytes."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, heads, S, d]")
+    B, A, S_q, d = q.shape
+    _, A_kv, S_k, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k, v must be [B, A_kv, S_k, d]")
+    for t in (o, dout, dq):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("o, dout, dq must match q")
+    for t in (dk, dv):
+        if t.shape != k.shape or t.dtype != q.dtype:
+            raise ValueError("dk, dv must match k")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k, v must share q's dtype")
+    if lse.shape != (B, A, S_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, A, S_q]")
+    if q_keep is not None and q_keep.shape != (B, S_q):
+        raise ValueError("q_keep must be [B, S_q]")
+    if k_keep is not None and k_keep.shape != (B, S_k):
+        raise ValueError("k_keep must be [B, S_k]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, workspace, q_keep, k_keep)
+    st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                       B, A, A_kv, S_q, S_k, d, float(scale), int(bool(causal)), _mask(q_keep, k_keep),
+                       _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    _check(st, "attn_bwd")

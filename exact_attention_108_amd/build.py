@@ -1,6 +1,6 @@
 """Build libattn_mi355x.so (gfx950) in-tree with hipcc.
 
-    python -m exact_attention_108_amd.build
+    python exact_attention_108_amd/build.py
 
 Every HIP translation unit is compiled for gfx950 only, with packed-fp32
 instruction selection disabled, and linked into one shared library whose only
@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libattn_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_prefill_bf16.hip", "attn_prefill_f32.hip", "attn_decode_bf16.hip", "attn_api.cpp"]
+SOURCES = ["attn_prefill_bf16.hip", "attn_prefill_f32.hip", "attn_decode_bf16.hip", "attn_bwd_bf16.hip",
+           "attn_api.cpp"]
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]

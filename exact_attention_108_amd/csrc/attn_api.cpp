@@ -185,6 +185,68 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   return launch_status(attn::launch_decode_bf16(p, (hipStream_t)stream));
 }
 
+namespace {
+
+size_t bwd_workspace_bytes(int B, int A, int S_q) {
+  const size_t n = (size_t)B * (size_t)A * (size_t)S_q * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int A, int S_q) {
+  if (B < 1 || A < 1 || S_q < 0) return 0;
+  return bwd_workspace_bytes(B, A, S_q);
+}
+
+ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, int B, int A, int A_kv, int S_q,
+                                 int S_k, int d_h, float scale, int causal, const attn_mask* mask,
+                                 attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (S_q > 0 && (!q || !o || !dout || !lse || !dq)) return ATTN_ERR_INVAL;
+  if (S_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(t)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  const long long n_qt = (S_q + attn::kBwdQRows - 1) / attn::kBwdQRows;
+  const long long n_kt = (S_k + attn::kBwdKRows - 1) / attn::kBwdKRows;
+  if (n_qt * A * B > INT_MAX || n_kt * A_kv * B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = S_q > 0 ? bwd_workspace_bytes(B, A, S_q) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  attn::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = (float*)workspace;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.q_keep = mask ? mask->q_keep : nullptr;
+  p.k_keep = mask ? mask->k_keep : nullptr;
+  p.B = B;
+  p.A = A;
+  p.A_kv = A_kv;
+  p.G = A / A_kv;
+  p.S_q = S_q;
+  p.S_k = S_k;
+  p.d = d_h;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
+}
+
 ATTN_EXPORT const char* attn_status_string(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ok";

@@ -134,6 +134,40 @@ attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_
 size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int page_size,
                                          const int32_t *seq_lens_host);
 
+/*
+ * Backward of attn_fwd (dense batch): dQ, dK, dV of O = softmax(Q K^T *
+ * scale + M) V for an incoming dO, with the probabilities recomputed tile by
+ * tile from Q, K and the forward's LSE instead of being stored (page
+ * "Attention 算子加速史", FAQ Q1; page "Attention Kernel", section
+ * "Backward 与重计算": same scale, same mask, same GQA mapping as the
+ * forward).  Per row i and key j, with D_i = sum_e dO_ie O_ie:
+ *   dV_j = sum_i P_ij dO_i,    dS_ij = P_ij (dO_i . v_j - D_i),
+ *   dQ_i = scale sum_j dS_ij k_j,    dK_j = scale sum_i dS_ij q_i,
+ * and for GQA dK, dV of a KV head sum over the query heads that read it.
+ *
+ *   q, o, dout, dq : [B, A, S_q, d_h]     k, v, dk, dv : [B, A_kv, S_k, d_h]
+ *   lse       : [B, A, S_q] fp32, as attn_fwd wrote it for the same q, k, v,
+ *               scale, causal and mask; rows with lse = -inf take no part
+ *   o         : attn_fwd's output for the same call
+ *   mask      : NULL or keep-masks [B, S_q] / [B, S_k], as given to attn_fwd
+ *   workspace : device buffer of at least attn_bwd_workspace_bytes(B, A, S_q)
+ *               bytes, 256-byte aligned (per-row D_i, fp32); contents on
+ *               entry are ignored
+ *
+ * dq, dk, dv are fully overwritten (zero where no element contributes) and
+ * must not alias the inputs or each other.  Every output element is written
+ * by one thread with a fixed summation order: the result is deterministic.
+ * All tensor pointers must be 16-byte aligned (ATTN_ERR_INVAL otherwise).
+ * Supported: bf16 with d_h in {64, 128}.  B, A, A_kv >= 1; S_q, S_k >= 0.
+ */
+attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, void *dq, void *dk, void *dv, int B, int A, int A_kv, int S_q,
+                     int S_k, int d_h, float scale, int causal, const attn_mask *mask,
+                     attn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_bwd needs (0 on bad input). */
+size_t attn_bwd_workspace_bytes(int B, int A, int S_q);
+
 /* Static text for a status code. */
 const char *attn_status_string(attn_status s);
 

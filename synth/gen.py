@@ -28,7 +28,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # stream ids, in drawing order
-S_Q, S_K, S_V, S_LENS, S_PERM, S_QKEEP, S_KKEEP = 0, 1, 2, 3, 4, 5, 6
+S_Q, S_K, S_V, S_LENS, S_PERM, S_QKEEP, S_KKEEP, S_DOUT = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def _threads() -> int:
@@ -227,6 +227,11 @@ def make_dense(B, A, A_kv, S_q, S_k, d, *, dtype="bf16", causal=False, seed=0,
     qk = keep_mask(B * S_q, q_masked, seed, S_QKEEP).reshape(B, S_q) if q_masked else None
     kk = keep_mask(B * S_k, k_masked, seed, S_KKEEP).reshape(B, S_k) if k_masked else None
     return Dense(B, A, A_kv, S_q, S_k, d, dtype, causal, scale, q, k, v, qk, kk)
+
+
+def make_dout(p: Dense, seed: int) -> np.ndarray:
+    """Incoming output gradient dO for a dense problem: N(0, 1), shaped like Q."""
+    return draw((p.B, p.A, p.S_q, p.d), seed, S_DOUT, "normal", p.dtype)
 
 
 def lognormal_lengths(n: int, median: float, sigma: float, lo: int, hi: int, seed: int) -> np.ndarray:

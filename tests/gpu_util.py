@@ -64,3 +64,46 @@ def check(o, lse, o_ref, lse_ref, dtype: str, what: str = "") -> dict:
         assert stats["max_abs"] <= F32_MAX_ABS, f"{what}: O max-abs {stats}"
     assert stats["lse_max_abs"] <= LSE_ABS, f"{what}: LSE {stats}"
     return stats
+
+
+# Gradients (dQ, dK, dV against the fp64 oracle's exact gradient).  Each
+# gradient element is a sum x = sum_t a_t b_t over bf16 operands with fp32
+# accumulation; its error has three parts, with u = 2^-8 the bf16 unit roundoff:
+#   - the final rounding of x to bf16: at most u |x|, about u/3 |x| on average;
+#   - the rounding to bf16 of the recomputed operand (P for dV, dS for dQ and
+#     dK), u/2 per term at most; the terms have random signs, so the sum's error
+#     is about 0.4 u sqrt(sum_t (a_t b_t)^2), i.e. about 0.4 u |x|;
+#   - D_i = rowsum(dO_i * O_i) taken from the forward's bf16 O rather than the
+#     exact O: |dD_i| <= u sum_e |dO_ie O_ie|, which moves dS_ij by P_ij dD_i.
+# Relative to the tensor's scale (max |x|, mean |x|) these stay under 2u for
+# the largest element and under u/2 on average; the bounds below allow 4u and
+# u.  Elements to which nothing contributes (fully masked rows, masked or
+# never-seen keys) must be exactly zero.
+GRAD_MAX_REL = 2.0 ** -6
+GRAD_MEAN_REL = 2.0 ** -8
+
+
+def check_grad(got, ref, what: str = "", zero_rows=None) -> dict:
+    """Compare a gradient with the oracle's; ``zero_rows`` (bool over the rows of
+    the last axis) marks rows no element contributes to, which must be exactly 0."""
+    got = np.asarray(got, np.float64).reshape(ref.shape)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    if ref.size == 0:
+        return {"max_rel": 0.0, "mean_rel": 0.0}
+    if zero_rows is not None:
+        zr = np.asarray(zero_rows, bool).reshape(-1)
+        rows_got = got.reshape(-1, ref.shape[-1])
+        assert np.all(ref.reshape(-1, ref.shape[-1])[zr] == 0.0), f"{what}: oracle disagrees on zero rows"
+        assert np.all(rows_got[zr] == 0.0), f"{what}: rows with no contribution must be exactly 0"
+    scale_max = float(np.abs(ref).max())
+    scale_mean = float(np.abs(ref).mean())
+    if scale_max == 0.0:
+        assert np.all(got == 0.0), f"{what}: expected all zeros"
+        return {"max_rel": 0.0, "mean_rel": 0.0}
+    err = np.abs(got - ref)
+    stats = {"max_rel": float(err.max()) / scale_max, "mean_rel": float(err.mean()) / scale_mean,
+             "scale_max": scale_max}
+    assert stats["max_rel"] <= GRAD_MAX_REL, f"{what}: max error {stats}"
+    assert stats["mean_rel"] <= GRAD_MEAN_REL, f"{what}: mean error {stats}"
+    return stats

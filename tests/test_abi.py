@@ -19,7 +19,8 @@ def header_functions():
 
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_varlen", "attn_decode_paged",
-                                         "attn_decode_paged_workspace_bytes", "attn_status_string",
+                                         "attn_decode_paged_workspace_bytes", "attn_bwd",
+                                         "attn_bwd_workspace_bytes", "attn_status_string",
                                          "attn_abi_version"])
 
 
@@ -67,6 +68,10 @@ def _lib():
     lib.attn_decode_paged.restype = i
     lib.attn_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, vp]
     lib.attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, i, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -164,3 +169,31 @@ def test_workspace_bytes():
     assert lib.attn_decode_paged_workspace_bytes(4, 32, 7, 128, 16, lp) == 0   # invalid: A % A_kv
     zero = np.zeros(3, np.int32)
     assert lib.attn_decode_paged_workspace_bytes(3, 8, 8, 64, 16, zero.ctypes.data_as(ctypes.c_void_p)) == 0
+
+
+def test_attn_bwd_rejects_bad_arguments():
+    lib = _lib()
+    INVAL, UNSUP, OK = 1, 2, 0
+
+    def bwd(**kw):
+        a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, A=4, A_kv=2, S_q=8, S_k=8, d=128,
+                 scale=0.1, causal=1, dt=1, ws=P, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                            a["A"], a["A_kv"], a["S_q"], a["S_k"], a["d"], a["scale"], a["causal"], None, a["dt"],
+                            a["ws"], a["ws_bytes"], None)
+    assert bwd(A=3) == INVAL                       # A % A_kv
+    assert bwd(B=0) == INVAL
+    assert bwd(S_k=-1) == INVAL
+    assert bwd(scale=float("nan")) == INVAL
+    assert bwd(do=None) == INVAL
+    assert bwd(dk=None) == INVAL
+    assert bwd(dq=ctypes.c_void_p(4096 + 8)) == INVAL   # not 16-byte aligned
+    assert bwd(ws_bytes=64) == INVAL               # workspace too small
+    assert bwd(ws=ctypes.c_void_p(4096 + 16)) == INVAL  # workspace not 256-byte aligned
+    assert bwd(ws=None) == INVAL
+    assert bwd(d=96) == UNSUP
+    assert bwd(dt=0) == UNSUP                      # the backward is bf16 only
+    assert lib.attn_bwd_workspace_bytes(2, 8, 100) == 6400
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1) == 256
+    assert lib.attn_bwd_workspace_bytes(0, 8, 100) == 0
