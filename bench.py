@@ -10,6 +10,10 @@ One step = one pass of the whole path over one batch of synthetic inputs:
 Inputs are resident in HBM before the timed region.  Each launch is bracketed
 by HIP events recorded on the stream the library launches on.
 
+After the timed steps, the backward of workload 1 (dQ, dK, dV recomputed from
+the forward's LSE) is timed on its own and reported under "backward"; it is
+not part of a step.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Prints one JSON line.
@@ -57,6 +61,7 @@ CSRC = os.path.join(ROOT, "exact_attention_108_amd", "csrc")
 KERNEL_SOURCES = {
     "prefill": ["attn_prefill_bf16.hip", "attn_device.h", "attn_kernels.h", "attn_rowblock.h"],
     "decode": ["attn_decode_bf16.hip", "attn_device.h", "attn_kernels.h"],
+    "backward": ["attn_bwd_bf16.hip", "attn_bwd.h", "attn_device.h"],
 }
 COPY_BYTES = 1 << 30  # the reference copy kernel moves this many bytes each way
 
@@ -141,6 +146,7 @@ def load_inputs(log_fn=lambda *a: None):
                            stream=stream)
 
     return dict(p2=p2, p4=p4, p5=p5, kv_bytes=kv_bytes, ws_bytes=ws_bytes, stream=stream,
+                dev2=(q2, k2, v2, o2, l2),
                 parts=[("prefill", prefill), ("decode", decode), ("varlen", varlen)])
 
 
@@ -154,6 +160,10 @@ def traffic_workload():
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
+    bwd = backward_setup(w)
+    for _ in range(3):
+        bwd()
+    torch.cuda.synchronize()
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -211,6 +221,8 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
         "varlen": lambda k: "prefill_bf16_kernel<64, true>" in k,
         "decode_split": lambda k: "decode_split_kernel" in k,
         "decode_merge": lambda k: "decode_merge_kernel" in k,
+        "bwd_dq": lambda k: "bwd_dq_kernel<128>" in k,
+        "bwd_dkdv": lambda k: "bwd_dkdv_kernel<128>" in k,
     }
     rows, rec = [], {}
     for part, pred in kernels.items():
@@ -222,7 +234,10 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
            "prefill": {"bytes_per_launch": sum(rec["prefill"]), "read_bytes": rec["prefill"][0],
                        "write_bytes": rec["prefill"][1], "source_hash": source_hash("prefill")},
            "decode": {"bytes_per_launch": sum(rec["decode_split"]) + sum(rec["decode_merge"]),
-                      "source_hash": source_hash("decode")}}
+                      "source_hash": source_hash("decode")},
+           "backward": {"bytes_per_launch": sum(rec["bwd_dq"]) + sum(rec["bwd_dkdv"]),
+                        "dq_bytes": sum(rec["bwd_dq"]), "dkdv_bytes": sum(rec["bwd_dkdv"]),
+                        "source_hash": source_hash("backward")}}
     print("# HBM traffic per launch (L2-to-fabric read requests by size, WRITE_SIZE)\n")
     print("Commands (repository root, one MI355X):\n")
     print("    rocprofv3 --pmc TCC_EA0_RDREQ_32B TCC_EA0_RDREQ_64B TCC_EA0_RDREQ_128B -f csv -d <dir_r> -o p "
@@ -261,7 +276,8 @@ def counter_summary(d: str):
                 by[key][r["Counter_Name"]] = by[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
                 span[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     kernels = {"prefill": "prefill_bf16_kernel<128, false>", "varlen": "prefill_bf16_kernel<64, true>",
-               "decode_split": "decode_split_kernel"}
+               "decode_split": "decode_split_kernel", "bwd_dq": "bwd_dq_kernel<128>",
+               "bwd_dkdv": "bwd_dkdv_kernel<128>"}
     print("# Matrix-core utilisation per launch (SQ / GRBM counters)\n")
     print("Commands (repository root, one MI355X):\n")
     print("    rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
@@ -408,11 +424,75 @@ def main():
                    "T": p5.T, "flops_causal_adjusted": f5, "masked_rows": int((p5.q_keep == 0).sum())},
     }
 
+    out["backward"] = bench_backward(w, args.steps, args.warmup)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(p4, kv_bytes, args.cpu_seconds / 3)
         out["varlen"]["cpu_baseline"] = cpu_baseline_varlen(p5, args.cpu_seconds / 3)
     print(json.dumps(out), flush=True)
+
+
+def backward_setup(w):
+    """The backward call over the prefill workload: O and LSE are whatever the
+    forward last wrote into the workload's buffers, dO is seeded N(0, 1)."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p2, stream = w["p2"], w["stream"]
+    q, k, v, o, lse = w["dev2"]
+    ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, stream=stream)
+    do = to_dev(gen.make_dout(p2, 2002), "bf16")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(p2.B, p2.A, p2.S_q), dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p2.scale, causal=True, stream=stream)
+    return bwd
+
+
+def bench_backward(w, steps: int, warmup: int) -> dict:
+    """Backward of the causal prefill workload (dQ, dK, dV recomputed from the
+    forward's LSE), timed on its own after the forward steps.
+
+    FLOPs follow the usual convention for an attention backward: five
+    S x S x d products (S, dP, dV, dQ, dK) against the forward's two, i.e. 2.5x
+    the forward's causal-adjusted count.  The kernels execute seven (the dQ
+    pass recomputes S and dP), reported as `executed_tflops`.  Algorithmic
+    bytes: Q, K, V, O, dO and LSE read once, dQ, dK, dV written once."""
+    import torch
+    p2, stream = w["p2"], w["stream"]
+    bwd = backward_setup(w)
+    for _ in range(warmup):
+        bwd()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bwd()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    flops = 2.5 * p2.flops()
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    traffic, src = committed_traffic("backward")
+    elem = p2.B * p2.A * p2.S_q * p2.d * 2
+    alg_bytes = 8 * elem + p2.B * p2.A * p2.S_q * 4
+    return {"metric": "attention bwd TFLOP/s (causal-adjusted, 2.5x forward FLOPs)", "value": round(tf, 2),
+            "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None if traffic is None else round(traffic),
+                         "traffic_unit": "bytes per call (dQ + dK/dV launches, HBM, counter-scaled)",
+                         "traffic_source": src, "algorithmic_bytes": alg_bytes},
+            "executed_tflops": round(tf * 7 / 5, 2), "avg_ms": round(float(ms.mean()), 5),
+            "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5),
+            "flops": flops,
+            "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 (the prefill workload)",
+            "kernels": "bwd_dq_kernel<128> then bwd_dkdv_kernel<128> (one call)"}
 
 
 def measured_ceilings(stream) -> dict:

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "attn_bwd.h"
 #include "attn_kernels.h"
 
 #define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
@@ -188,7 +189,7 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
 namespace {
 
 size_t bwd_workspace_bytes(int B, int A, int S_q) {
-  const size_t n = (size_t)B * (size_t)A * (size_t)S_q * sizeof(float);
+  const size_t n = (size_t)B * (size_t)A * (size_t)S_q * 2 * sizeof(float);
   return (n + 255) & ~(size_t)255;
 }
 
@@ -228,7 +229,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   p.o = o;
   p.dout = dout;
   p.lse = lse;
-  p.delta = (float*)workspace;
+  p.row_stats = (float*)workspace;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;

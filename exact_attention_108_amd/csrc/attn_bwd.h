@@ -1,0 +1,34 @@
+// attn_bwd.h -- host/device interface of the backward-pass kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Backward pass of the dense prefill (bf16, d in {64, 128}).
+struct BwdParams {
+  const void* q;    // [B, A, S_q, d]
+  const void* k;    // [B, A_kv, S_k, d]
+  const void* v;
+  const void* o;    // forward output, [B, A, S_q, d]
+  const void* dout;  // incoming gradient of o
+  const float* lse;  // forward LSE (natural log), [B, A, S_q]
+  float* row_stats;  // workspace [B, A, S_q, 2]: (LSE * log2 e, or +inf for a row that
+                     // takes no part; rowsum(dO * O)), written by the dQ pass
+  void* dq;          // [B, A, S_q, d]
+  void* dk;          // [B, A_kv, S_k, d]
+  void* dv;
+  const uint8_t* q_keep;  // [B, S_q] or null
+  const uint8_t* k_keep;  // [B, S_k] or null
+  int B, A, A_kv, G, S_q, S_k, d;
+  int causal;
+  float scale, scale_log2;
+  // XCD-blocked grid orders (0 = plain order), set by launch_bwd_bf16
+  int dq_units_per_xcd, dq_group;  // units: (batch, query head)
+  int kv_units_per_xcd, kv_group;  // units: (batch, KV head)
+};
+constexpr int kBwdQRows = 128;   // query rows per dQ workgroup
+constexpr int kBwdKRows = 128;   // keys per dK/dV workgroup
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+
+}  // namespace attn

@@ -13,17 +13,20 @@
 //   dK_j += scale sum_i dS_ij q_i.
 // (D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.)
 //
-// Three launches, none of which writes the same output element twice, so the
+// Two launches, neither of which writes an output element twice, so the
 // result is deterministic and needs no atomics (the "no race in accumulation"
 // requirement of the same section):
-//   1. delta: D_i = rowsum(dO_i * O_i) into the caller's workspace;
-//   2. dQ: one workgroup per 128 query rows of one (batch, head), streaming the
-//      K/V tiles of its KV head -- the forward's layout (one query per lane):
+//   1. dQ: one workgroup per 128 query rows of one (batch, head), four waves
+//      of 32 rows, streaming double-buffered 64-key K/V tiles of its KV head in
+//      the forward's layout (one query per lane):
 //        S^T = K . Q^T,  dP^T = V . dO^T  (Q and dO rows resident),
 //        dQ^T += K^T . dS^T  (K^T through the transposing LDS read);
-//   3. dK/dV: one workgroup per 128 keys of one (batch, KV head), four waves
-//      of 32 keys each, streaming 32-row blocks of Q and dO of every query
-//      head that reads this KV head (this is the GQA sum), one key per lane:
+//      its prologue also forms D_i and the base-2 LSE of each row and stores
+//      both in the workspace for the second launch;
+//   2. dK/dV: one workgroup per 128 keys of one (batch, KV head), four waves
+//      of 32 keys, streaming triple-buffered 32-row blocks of Q, dO and the row
+//      statistics of every query head that reads this KV head (this is the GQA
+//      sum), one key per lane:
 //        S = Q . K^T,  dP = dO . V^T  (K and V rows resident),
 //        dV^T += dO^T . P,  dK^T += Q^T . dS  (transposing reads of Q, dO).
 // The per-element predicate (causal bottom-right diagonal, keep masks, rows
@@ -31,39 +34,22 @@
 // masked) take no part.
 #include <type_traits>
 
+#include "attn_bwd.h"
 #include "attn_device.h"
-#include "attn_kernels.h"
 
 namespace attn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kXcdCount = 8;
 constexpr int kKeyTile = 64;  // keys per tile in the dQ kernel
 constexpr int kQBlock = 32;   // query rows per block in the dK/dV kernel
 static_assert(kBwdQRows == 128 && kBwdKRows == 128, "four waves of 32");
 
-// ---------------------------------------------------------------- delta
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdParams p, int n_rows) {
-  constexpr int LPR = D / 8;              // lanes per row, 8 elements each
-  constexpr int RPW = kThreads / LPR;     // rows per workgroup
-  const int row = blockIdx.x * RPW + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < n_rows) {
-    const bf16x8 a = *(const bf16x8*)((const uint16_t*)p.dout + (size_t)row * D + 8 * c);
-    const bf16x8 b = *(const bf16x8*)((const uint16_t*)p.o + (size_t)row * D + 8 * c);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)b[i], acc);
-  }
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row < n_rows && c == 0) p.delta[row] = acc;
-}
-
 // Copy rows [r0, r0 + NROWS) of a row-major [rows_total, D] bf16 tensor into an
 // LDS tile with the forward's chunk swizzle; rows past rows_total arrive as
-// zeros (range-checked buffer resource).  All kThreads threads take part.
+// zeros (range-checked buffer resource).  All kThreads threads take part; each
+// wave issues NROWS * D / 2048 copy instructions.
 template <int D, int NROWS>
 __device__ __forceinline__ void copy_rows(const uint16_t* base, int rows_total, int r0, uint32_t lds_dst) {
   constexpr int NCH = D / 8;
@@ -82,6 +68,35 @@ __device__ __forceinline__ void copy_rows(const uint16_t* base, int rows_total, 
     lds_copy16_buf(rsrc, (uint32_t)((i * RPC + rowc) * D * 2 + cc * 16), wave_base + (uint32_t)(i * RPC * D * 2));
 }
 
+// Scheduling hint for the blocks that hold both a score pass and a gradient
+// pass: LLVM's interleaving strategy 0 for MFMA-heavy code spreads the LDS
+// reads and vector ALU work between the matrix instructions (measured: 6-11%
+// faster than the default schedule, bitwise identical results).
+__device__ __forceinline__ void interleave_hint() { __builtin_amdgcn_iglp_opt(0); }
+
+// Grid order.  Workgroups are dealt to the 8 XCDs round-robin by index and
+// each XCD has its own L2.  With `group` > 0, XCD x owns the units (batch,
+// head pairs) [x * per, (x + 1) * per) and takes them `group` at a time, each
+// group's tiles heaviest first (rank 0 first), so the workgroups that stream
+// the same K/V (dQ pass) or the same Q/dO (dK/dV pass) run at about the same
+// time on one XCD.  Otherwise: rank-major over all units.
+__device__ __forceinline__ void grid_order(int lin, int n_tiles, int n_units, int per, int group, int& rank,
+                                           int& unit) {
+  if (group > 0) {
+    const int x = lin % kXcdCount, i = lin / kXcdCount;
+    const int per_group = group * n_tiles;
+    const int grp = i / per_group, r = i % per_group;
+    rank = r / group;
+    unit = x * per + grp * group + r % group;
+  } else {
+    rank = lin / n_units;
+    unit = lin % n_units;
+  }
+}
+
+template <int N>
+using Slot = std::integral_constant<int, N>;
+
 // ---------------------------------------------------------------- dQ
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void bwd_dq_kernel(BwdParams p,
@@ -89,14 +104,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int TILE_BYTES = kKeyTile * D * 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kKeyTile * D];  // [K tile | V tile]
-  __shared__ uint8_t sKeep[kKeyTile];
+  constexpr int SLOT_BYTES = 2 * TILE_BYTES;  // [K tile | V tile]
+  constexpr int NSLOT = 4;
+  constexpr int COPIES = 2 * (kKeyTile * D / 8 / kThreads);  // copy instructions per wave per tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * SLOT_BYTES / 2];
 
-  // heaviest query tiles first (most causal key tiles), then batch * head
-  const int lin = blockIdx.x;
-  const int bh_n = p.A * p.B;
-  const int qt = n_qt - 1 - lin / bh_n;
-  const int bh = lin % bh_n;
+  // heaviest query tiles first (most causal key tiles)
+  int rank, bh;
+  grid_order(blockIdx.x, n_qt, p.A * p.B, p.dq_units_per_xcd, p.dq_group, rank, bh);
+  const int qt = n_qt - 1 - rank;
   const int h = bh % p.A, b = bh / p.A, hk = h / p.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int S_q = p.S_q, S_k = p.S_k, off = S_k - S_q;
@@ -107,20 +123,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const int qrow = q0 + wave * 32 + l32;
   const bool row_in = qrow < S_q;
 
-  // resident Q and dO rows of this lane's query; its base-2 LSE (+inf when the
-  // row takes no part, so that every p of it is exactly 0) and delta
+  // resident Q and dO halves of this lane's query row (lanes l and l ^ 32
+  // hold the two halves); D = rowsum(dO * O) in fp32
   bf16x8 qf[KSTEPS], dof[KSTEPS];
+  float dsum = 0.f;
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) {
-    qf[t] = row_in ? *(const bf16x8*)((const uint16_t*)p.q + (q_row0 + qrow) * D + 16 * t + 8 * g) : bf16x8{};
-    dof[t] = row_in ? *(const bf16x8*)((const uint16_t*)p.dout + (q_row0 + qrow) * D + 16 * t + 8 * g) : bf16x8{};
+    const size_t e = (q_row0 + qrow) * D + 16 * t + 8 * g;
+    qf[t] = row_in ? *(const bf16x8*)((const uint16_t*)p.q + e) : bf16x8{};
+    dof[t] = row_in ? *(const bf16x8*)((const uint16_t*)p.dout + e) : bf16x8{};
+    const bf16x8 of = row_in ? *(const bf16x8*)((const uint16_t*)p.o + e) : bf16x8{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dsum = fmaf((float)dof[t][i], (float)of[i], dsum);
   }
-  float lrow = INFINITY, drow = 0.f;
+  const float drow = sum_with_other_half(dsum);
+  // base-2 LSE, +inf when the row takes no part (every p of it is then 0)
+  float lrow = INFINITY;
   if (row_in) {
     const float lse = p.lse[q_row0 + qrow];
     const bool keep = p.q_keep == nullptr || p.q_keep[(size_t)b * S_q + qrow] != 0;
     if (keep && lse != -INFINITY) lrow = lse * kLog2e;
-    drow = p.delta[q_row0 + qrow];
+    if (g == 0) *(float2*)(p.row_stats + 2 * (q_row0 + qrow)) = make_float2(lrow, drow);
   }
 
   int kend = S_k;
@@ -142,30 +165,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       voff[mb][rd] = (row * D + lds_chunk<D>(row, c) * 8 + (tr_q & 1) * 4) * 2;
     }
   }
-  const char* lds = (const char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const float cs = p.scale_log2;
+  const uint16_t* kbase = (const uint16_t*)p.k + k_row0 * D;
+  const uint16_t* vbase = (const uint16_t*)p.v + k_row0 * D;
+  const uint8_t* kkeep = p.k_keep ? p.k_keep + (size_t)b * S_k : nullptr;
 
   f32x16 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int k0 = j * kKeyTile;
-    __syncthreads();  // every wave is done with the previous tile
-    copy_rows<D, kKeyTile>((const uint16_t*)p.k + k_row0 * D, S_k, k0, lds_base);
-    copy_rows<D, kKeyTile>((const uint16_t*)p.v + k_row0 * D, S_k, k0, lds_base + TILE_BYTES);
-    if (p.k_keep && tid < kKeyTile) {
-      const int key = k0 + tid;
-      sKeep[tid] = key < S_k ? p.k_keep[(size_t)b * S_k + key] : 0;
-    }
-    lds_copy_wait_all();
-    __syncthreads();
+  auto issue = [&](int j, int slot) {
+    const uint32_t dst = lds_base + slot * SLOT_BYTES;
+    copy_rows<D, kKeyTile>(kbase, S_k, j * kKeyTile, dst);
+    copy_rows<D, kKeyTile>(vbase, S_k, j * kKeyTile, dst + TILE_BYTES);
+  };
+  // key k0 + lane is in range and kept.  The keep byte is an ordinary load,
+  // so with a key mask each step also waits for the copies in flight.
+  auto key_ok = [&](int j) -> bool {
+    const int key = j * kKeyTile + lane;
+    return key < S_k && (kkeep == nullptr || kkeep[key] != 0);
+  };
 
-    // S^T = K . Q^T and dP^T = V . dO^T: two 32-key blocks
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  // S^T and dP^T of the tile in `lds` (two 32-key blocks each)
+  auto scores = [&](const char* lds, f32x16 (&s)[2], f32x16 (&dp)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
         const bf16x8 ka = *(const bf16x8*)(lds + kb * 32 * D * 2 + koff[t]);
@@ -174,34 +201,105 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         dp[kb] = mfma32(va, dof[t], dp[kb]);
       }
     }
-    // element (kb, r) holds key k0 + kl, kl = 32kb + 8(r/4) + 4g + r%4
-    bool valid = k0 + lane < S_k;
-    if (p.k_keep) valid = valid && sKeep[lane] != 0;
-    const uint64_t kvalid = __ballot(valid) >> (4 * g);
+  };
+  // P, dS = P (dP - D) of tile j, then dQ^T += K^T . dS^T.  A dead row has
+  // lrow = +inf, so its p = 2^-inf = 0 without a mask.  MASKED adds the
+  // per-element predicate (keys past S_k, dropped keys, causal diagonal).
+  auto grad = [&](const char* lds, int j, bool ok, const f32x16 (&s)[2], const f32x16 (&dp)[2], auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = j * kKeyTile;
+    // element r of 32-key block kb holds key k0 + 32 kb + 8(r/4) + 4g + r%4
+    const uint64_t kvalid = __ballot(ok) >> (4 * g);
     const int lim = causal ? qrow + off - k0 - 4 * g : (1 << 30);
-    bf16x8 dsb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 dsb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-        const bool live = ((kvalid >> c) & 1) && c <= lim;
-        const float pr = live ? exp2_fast(fmaf(s[kb][r], cs, -lrow)) : 0.f;
-        dsb[kb][r >> 3][r & 7] = (__bf16)(pr * (dp[kb][r] - drow));
+        float x = fmaf(s[kb][r], cs, -lrow);
+        if constexpr (MASKED) {
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+          x = (((kvalid >> c) & 1) && c <= lim) ? x : -INFINITY;
+        }
+        const float pr = exp2_fast(x);
+        dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[kb][r] - drow));
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const char* base = lds + (32 * kb + 16 * hh) * D * 2;
+          const bf16x8 kt = concat(lds_read_tr16(base + voff[mb][0]), lds_read_tr16(base + voff[mb][1]));
+          acc[mb] = mfma32(kt, dsb[hh], acc[mb]);
+        }
       }
     }
-    // dQ^T += K^T . dS^T
-#pragma unroll
-    for (int kh = 0; kh < 4; ++kh) {
-      const int kb = kh >> 1, hh = kh & 1;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const char* base = lds + (32 * kb + 16 * hh) * D * 2;
-        const bf16x8 kt = concat(lds_read_tr16(base + voff[mb][0]), lds_read_tr16(base + voff[mb][1]));
-        acc[mb] = mfma32(kt, dsb[kb][hh], acc[mb]);
-      }
+  };
+  // whether tile j needs the per-element predicate in this wave (uniform)
+  const int wave_row0 = q0 + wave * 32;
+  auto tile_masked = [&](int j, bool ok) -> bool {
+    const int k0 = j * kKeyTile;
+    bool full = k0 + kKeyTile <= S_k && __ballot(ok) == ~0ull;
+    if (causal) full = full && k0 + kKeyTile - 1 <= wave_row0 + off;
+    return !full;
+  };
+
+  // Software pipeline over key tiles: step j waits for tile j + 1, issues the
+  // copy of tile j + 3 into the slot tile j - 1 used, and computes, in one
+  // basic block so that the two interleave, S^T and dP^T of tile j + 1 and the
+  // gradient of tile j (from the S^T and dP^T the previous step computed).
+  // Slot of tile j: j % 4; the two register sets alternate.
+  struct SD {
+    f32x16 s[2], dp[2];
+  };
+  SD ra, rb;
+  auto step = [&](int j, auto slot_tag, SD& cur, SD& nxt) {
+    constexpr int SC = decltype(slot_tag)::value;
+    constexpr int SN = (SC + 1) % NSLOT, SI = (SC + 3) % NSLOT;
+    if (j + 2 < n_tiles)
+      lds_copy_wait<COPIES>();  // tile j + 1 has landed; j + 2 may still be in flight
+    else
+      lds_copy_wait_all();
+    __syncthreads();  // and for every wave; every wave is done with tile j - 1
+    if (j + 3 < n_tiles) issue(j + 3, SI);
+    const char* lc = (const char*)smem + SC * SLOT_BYTES;
+    // at the last tile this reads a stale (in-bounds) slot; the result is unused
+    const char* ln = (const char*)smem + SN * SLOT_BYTES;
+    const bool ok = key_ok(j);
+    if (tile_masked(j, ok)) {
+      interleave_hint();
+      scores(ln, nxt.s, nxt.dp);
+      grad(lc, j, ok, cur.s, cur.dp, std::true_type{});
+    } else {
+      interleave_hint();
+      scores(ln, nxt.s, nxt.dp);
+      grad(lc, j, ok, cur.s, cur.dp, std::false_type{});
     }
+  };
+
+  if (n_tiles > 0) {
+    issue(0, 0);
+    if (n_tiles > 1) issue(1, 1);
+    if (n_tiles > 2) issue(2, 2);
+    if (n_tiles > 2)
+      lds_copy_wait<2 * COPIES>();
+    else if (n_tiles > 1)
+      lds_copy_wait<COPIES>();
+    else
+      lds_copy_wait_all();
+    __syncthreads();
+    scores((const char*)smem, ra.s, ra.dp);
   }
+  int j = 0;
+  for (; j + 4 <= n_tiles; j += 4) {
+    step(j, Slot<0>{}, ra, rb);
+    step(j + 1, Slot<1>{}, rb, ra);
+    step(j + 2, Slot<2>{}, ra, rb);
+    step(j + 3, Slot<3>{}, rb, ra);
+  }
+  if (j < n_tiles) step(j, Slot<0>{}, ra, rb);
+  if (j + 1 < n_tiles) step(j + 1, Slot<1>{}, rb, ra);
+  if (j + 2 < n_tiles) step(j + 2, Slot<2>{}, ra, rb);
 
   // dQ = scale * (dQ^T)^T: lane holds d = 32mb + 8(r/4) + 4g + r%4 of its row
   if (row_in) {
@@ -226,23 +324,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kQBlock * D];  // [Q block | dO block]
-  __shared__ __attribute__((aligned(16))) float sL[kQBlock];  // base-2 LSE (+inf: row takes no part)
-  __shared__ __attribute__((aligned(16))) float sD[kQBlock];  // delta
+  constexpr int STATS_BYTES = kQBlock * 8;                    // (L2, D) per row
+  constexpr int SLOT_BYTES = 2 * BLOCK_BYTES + STATS_BYTES;   // [Q block | dO block | stats]
+  constexpr int NSLOT = 4;
+  constexpr int COPIES = 2 * (kQBlock * D / 8 / kThreads) + 1;  // copy instructions per wave per block
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * SLOT_BYTES / 2];
 
-  // key tiles in order (the first ones see the most query rows when causal),
-  // then batch * KV head
-  const int lin = blockIdx.x;
-  const int bk_n = p.A_kv * p.B;
-  const int kt = lin / bk_n;
-  const int bk = lin % bk_n;
+  // key tiles in order (the first ones see the most query rows when causal)
+  int kt, bk;
+  grid_order(blockIdx.x, n_kt, p.A_kv * p.B, p.kv_units_per_xcd, p.kv_group, kt, bk);
   const int hk = bk % p.A_kv, b = bk / p.A_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int S_q = p.S_q, S_k = p.S_k, off = S_k - S_q;
   const bool causal = p.causal != 0;
   const size_t k_row0 = (size_t)(b * p.A_kv + hk) * S_k;
-  const int kw0 = kt * kBwdKRows + wave * 32;  // this wave's first key
-  const int key = kw0 + l32;                   // this lane's key
+  const int key = kt * kBwdKRows + wave * 32 + l32;  // this lane's key
   bool key_live = key < S_k;
   if (key_live && p.k_keep) key_live = p.k_keep[(size_t)b * S_k + key] != 0;
 
@@ -268,7 +364,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       voff[mb][rd] = (row * D + lds_chunk<D>(row, c) * 8 + (tr_q & 1) * 4) * 2;
     }
   }
-  const char* lds = (const char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const float cs = p.scale_log2;
 
@@ -276,78 +371,149 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc_dk[mb] = acc_dv[mb] = f32x16{};
 
-  // query rows that can see a key of this workgroup: i + off >= first key
+  // query rows that can see a key of this workgroup: i + off >= first key;
+  // blocks run over (query head of the group, 32-row block)
   const int k_first = kt * kBwdKRows;
   const int i_first = causal ? max(k_first - off, 0) : 0;
   const int qb_first = i_first / kQBlock;
   const int n_qb = (S_q + kQBlock - 1) / kQBlock;
+  const int nq = max(n_qb - qb_first, 0);
+  const int n_blocks = p.G * nq;
 
-  for (int gh = 0; gh < p.G; ++gh) {
-    const int h = hk * p.G + gh;
-    const size_t q_row0 = (size_t)(b * p.A + h) * S_q;
-    for (int qb = qb_first; qb < n_qb; ++qb) {
-      const int r0 = qb * kQBlock;
-      __syncthreads();  // every wave is done with the previous block
-      copy_rows<D, kQBlock>((const uint16_t*)p.q + q_row0 * D, S_q, r0, lds_base);
-      copy_rows<D, kQBlock>((const uint16_t*)p.dout + q_row0 * D, S_q, r0, lds_base + BLOCK_BYTES);
-      if (tid < kQBlock) {
-        const int row = r0 + tid;
-        float lv = INFINITY, dv = 0.f;
-        if (row < S_q) {
-          const float lse = p.lse[q_row0 + row];
-          const bool keep = p.q_keep == nullptr || p.q_keep[(size_t)b * S_q + row] != 0;
-          if (keep && lse != -INFINITY) lv = lse * kLog2e;
-          dv = p.delta[q_row0 + row];
-        }
-        sL[tid] = lv;
-        sD[tid] = dv;
-      }
-      lds_copy_wait_all();
-      __syncthreads();
+  auto issue = [&](int idx, int slot) {
+    const int gh = idx / nq, qb = qb_first + idx % nq;
+    const size_t q_row0 = (size_t)(b * p.A + hk * p.G + gh) * S_q;
+    const int r0 = qb * kQBlock;
+    const uint32_t dst = lds_base + slot * SLOT_BYTES;
+    copy_rows<D, kQBlock>((const uint16_t*)p.q + q_row0 * D, S_q, r0, dst);
+    copy_rows<D, kQBlock>((const uint16_t*)p.dout + q_row0 * D, S_q, r0, dst + BLOCK_BYTES);
+    // (L2, D) of rows r0 + 8 wave .. + 7: four lanes of 16 bytes per wave
+    const int rows = min(S_q - r0, kQBlock);
+    const i32x4 rsrc = make_buffer_rsrc(p.row_stats + 2 * (q_row0 + r0), (uint32_t)(rows * 8));
+    const uint32_t sdst = dst + 2 * BLOCK_BYTES + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
+    if (lane < 4) lds_copy16_buf(rsrc, (uint32_t)(wave * 64 + lane * 16), sdst);
+  };
 
-      // S = Q . K^T, dP = dO . V^T for this wave's 32 keys
-      f32x16 s = f32x16{}, dp = f32x16{};
+  // S and dP of the block in `lds` for this wave's 32 keys
+  auto scores = [&](const char* lds, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        const bf16x8 qa = *(const bf16x8*)(lds + koff[t]);
-        const bf16x8 da = *(const bf16x8*)(lds + BLOCK_BYTES + koff[t]);
-        s = mfma32(qa, kres[t], s);
-        dp = mfma32(da, vres[t], dp);
-      }
-      // element r holds query row r0 + m, m = 8(r/4) + 4g + r%4, of this lane's key
-      bf16x8 pb[2], dsb[2];
+    for (int t = 0; t < KSTEPS; ++t) {
+      const bf16x8 qa = *(const bf16x8*)(lds + koff[t]);
+      const bf16x8 da = *(const bf16x8*)(lds + BLOCK_BYTES + koff[t]);
+      s = mfma32(qa, kres[t], s);
+      dp = mfma32(da, vres[t], dp);
+    }
+  };
+  // P and dS of block idx, then dV^T += dO^T . P and dK^T += Q^T . dS.  A
+  // dead row has L2 = +inf, so its p is 0 without a mask; MASKED adds the
+  // per-element predicate (rows past S_q, which arrive zero-filled with L2 =
+  // 0, dropped or absent keys, causal diagonal).
+  auto grad = [&](const char* lds, int idx, const f32x16& s, const f32x16& dp, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const float* st = (const float*)(lds + 2 * BLOCK_BYTES);
+    const int r0 = (qb_first + idx % nq) * kQBlock;
+    // element r holds query row r0 + m, m = 8(r/4) + 4g + r%4, of this lane's key
+    const int m_lo = causal ? key - off - r0 - 4 * g : -(1 << 30);
+    const int m_hi = key_live ? S_q - r0 - 4 * g : -(1 << 30);
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int m0 = 8 * r4 + 4 * g;
-        const float4 lv = *(const float4*)(sL + m0);
-        const float4 dv = *(const float4*)(sD + m0);
-        const float lvv[4] = {lv.x, lv.y, lv.z, lv.w}, dvv[4] = {dv.x, dv.y, dv.z, dv.w};
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 a = *(const f32x4*)(st + 2 * (8 * r4 + 4 * g));
+      const f32x4 c = *(const f32x4*)(st + 2 * (8 * r4 + 4 * g) + 4);
+      const float lv[4] = {a[0], a[2], c[0], c[2]}, dv[4] = {a[1], a[3], c[1], c[3]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * r4 + i;
-          const int row = r0 + m0 + i;
-          bool live = key_live;
-          if (causal) live = live && key <= row + off;
-          const float pr = live ? exp2_fast(fmaf(s[r], cs, -lvv[i])) : 0.f;
-          pb[r >> 3][r & 7] = (__bf16)pr;
-          dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dvv[i]));
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * r4 + i;
+        float x = fmaf(s[r], cs, -lv[i]);
+        if constexpr (MASKED) {
+          const int m = 8 * r4 + i;
+          x = (m >= m_lo && m < m_hi) ? x : -INFINITY;
         }
-      }
-      // dV^T += dO^T . P and dK^T += Q^T . dS: two 16-row k-steps
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const char* qbase = lds + 16 * kk * D * 2;
-          const char* dbase = lds + BLOCK_BYTES + 16 * kk * D * 2;
-          const bf16x8 dt = concat(lds_read_tr16(dbase + voff[mb][0]), lds_read_tr16(dbase + voff[mb][1]));
-          const bf16x8 qt_ = concat(lds_read_tr16(qbase + voff[mb][0]), lds_read_tr16(qbase + voff[mb][1]));
-          acc_dv[mb] = mfma32(dt, pb[kk], acc_dv[mb]);
-          acc_dk[mb] = mfma32(qt_, dsb[kk], acc_dk[mb]);
-        }
+        const float pr = exp2_fast(x);
+        pb[r >> 3][r & 7] = (__bf16)pr;
+        dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dv[i]));
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const char* qbase = lds + 16 * kk * D * 2;
+        const char* dbase = lds + BLOCK_BYTES + 16 * kk * D * 2;
+        const bf16x8 dt = concat(lds_read_tr16(dbase + voff[mb][0]), lds_read_tr16(dbase + voff[mb][1]));
+        const bf16x8 qt_ = concat(lds_read_tr16(qbase + voff[mb][0]), lds_read_tr16(qbase + voff[mb][1]));
+        acc_dv[mb] = mfma32(dt, pb[kk], acc_dv[mb]);
+        acc_dk[mb] = mfma32(qt_, dsb[kk], acc_dk[mb]);
+      }
+    }
+  };
+  // whether block idx needs the per-element predicate in this wave (uniform)
+  const bool wave_keys_live = __ballot(key_live) == ~0ull;
+  const int wave_key_last = kt * kBwdKRows + wave * 32 + 31;
+  auto block_masked = [&](int idx) -> bool {
+    const int r0 = (qb_first + idx % nq) * kQBlock;
+    bool full = wave_keys_live && r0 + kQBlock <= S_q;
+    if (causal) full = full && wave_key_last <= r0 + off;
+    return !full;
+  };
+
+  // Software pipeline over blocks: step idx waits for block idx + 1, issues
+  // the copy of block idx + 3 into the slot block idx - 1 used, and computes,
+  // in one basic block so that the two interleave, S and dP of block idx + 1
+  // and the gradient of block idx.  Slot of block idx: idx % 4; the two
+  // register sets alternate.
+  struct SD {
+    f32x16 s, dp;
+  };
+  SD ra, rb;
+  auto step = [&](int idx, auto slot_tag, SD& cur, SD& nxt) {
+    constexpr int SC = decltype(slot_tag)::value;
+    constexpr int SN = (SC + 1) % NSLOT, SI = (SC + 3) % NSLOT;
+    if (idx + 2 < n_blocks)
+      lds_copy_wait<COPIES>();  // block idx + 1 has landed; idx + 2 may still be in flight
+    else
+      lds_copy_wait_all();
+    __syncthreads();  // and for every wave; every wave is done with block idx - 1
+    if (idx + 3 < n_blocks) issue(idx + 3, SI);
+    const char* lc = (const char*)smem + SC * SLOT_BYTES;
+    // at the last block this reads a stale (in-bounds) slot; the result is unused
+    const char* ln = (const char*)smem + SN * SLOT_BYTES;
+    if (block_masked(idx)) {
+      interleave_hint();
+      scores(ln, nxt.s, nxt.dp);
+      grad(lc, idx, cur.s, cur.dp, std::true_type{});
+    } else {
+      interleave_hint();
+      scores(ln, nxt.s, nxt.dp);
+      grad(lc, idx, cur.s, cur.dp, std::false_type{});
+    }
+  };
+
+  if (n_blocks > 0) {
+    issue(0, 0);
+    if (n_blocks > 1) issue(1, 1);
+    if (n_blocks > 2) issue(2, 2);
+    if (n_blocks > 2)
+      lds_copy_wait<2 * COPIES>();
+    else if (n_blocks > 1)
+      lds_copy_wait<COPIES>();
+    else
+      lds_copy_wait_all();
+    __syncthreads();
+    scores((const char*)smem, ra.s, ra.dp);
   }
+  int idx = 0;
+  for (; idx + 4 <= n_blocks; idx += 4) {
+    step(idx, Slot<0>{}, ra, rb);
+    step(idx + 1, Slot<1>{}, rb, ra);
+    step(idx + 2, Slot<2>{}, ra, rb);
+    step(idx + 3, Slot<3>{}, rb, ra);
+  }
+  if (idx < n_blocks) step(idx, Slot<0>{}, ra, rb);
+  if (idx + 1 < n_blocks) step(idx + 1, Slot<1>{}, rb, ra);
+  if (idx + 2 < n_blocks) step(idx + 2, Slot<2>{}, ra, rb);
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds d = 32mb + 8(r/4) + 4g + r%4
   if (key < S_k) {
@@ -370,12 +536,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
+// Groups of 8 query heads for the dQ pass (as in the forward); groups of 2
+// KV heads for the dK/dV pass, whose 16 key tiles per head already keep an
+// XCD busy (measured: the order moves the time by a few percent at most).
+constexpr int kDqGroupMax = 8;
+constexpr int kKvGroupMax = 2;
+// XCD blocking of `units` (see grid_order): a multiple of 8 units is split
+// into 8 contiguous blocks taken in groups of up to `group_max`.
+void plan_order(int units, int group_max, int& per, int& group) {
+  per = group = 0;
+  if (units % kXcdCount != 0) return;
+  per = units / kXcdCount;
+  int g = group_max;
+  while (g > 1 && per % g != 0) g >>= 1;
+  group = g;
+}
+
 template <int D>
-hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  const int n_rows = p.B * p.A * p.S_q;
-  if (n_rows > 0) {
-    constexpr int RPW = kThreads / (D / 8);
-    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((n_rows + RPW - 1) / RPW), dim3(kThreads), 0, stream, p, n_rows);
+hipError_t launch_bwd_d(const BwdParams& p_in, hipStream_t stream) {
+  BwdParams p = p_in;
+  plan_order(p.A * p.B, kDqGroupMax, p.dq_units_per_xcd, p.dq_group);
+  plan_order(p.A_kv * p.B, kKvGroupMax, p.kv_units_per_xcd, p.kv_group);
+  // the dQ pass writes the row statistics the dK/dV pass reads: same stream, in order
+  if (p.S_q > 0) {
     const int n_qt = (p.S_q + kBwdQRows - 1) / kBwdQRows;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_qt * p.A * p.B), dim3(kThreads), 0, stream, p, n_qt);
   }

@@ -92,26 +92,4 @@ size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan);
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 
-// Backward pass of the dense prefill (bf16, d in {64, 128}).
-struct BwdParams {
-  const void* q;    // [B, A, S_q, d]
-  const void* k;    // [B, A_kv, S_k, d]
-  const void* v;
-  const void* o;    // forward output, [B, A, S_q, d]
-  const void* dout;  // incoming gradient of o
-  const float* lse;  // forward LSE (natural log), [B, A, S_q]
-  float* delta;      // workspace [B, A, S_q]: rowsum(dO * O)
-  void* dq;          // [B, A, S_q, d]
-  void* dk;          // [B, A_kv, S_k, d]
-  void* dv;
-  const uint8_t* q_keep;  // [B, S_q] or null
-  const uint8_t* k_keep;  // [B, S_k] or null
-  int B, A, A_kv, G, S_q, S_k, d;
-  int causal;
-  float scale, scale_log2;
-};
-constexpr int kBwdQRows = 128;   // query rows per dQ workgroup
-constexpr int kBwdKRows = 128;   // keys per dK/dV workgroup
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
-
 }  // namespace attn

@@ -151,8 +151,8 @@ size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int pa
  *   o         : attn_fwd's output for the same call
  *   mask      : NULL or keep-masks [B, S_q] / [B, S_k], as given to attn_fwd
  *   workspace : device buffer of at least attn_bwd_workspace_bytes(B, A, S_q)
- *               bytes, 256-byte aligned (per-row D_i, fp32); contents on
- *               entry are ignored
+ *               bytes, 256-byte aligned (two fp32 per query row: the base-2
+ *               LSE and D_i); contents on entry are ignored
  *
  * dq, dk, dv are fully overwritten (zero where no element contributes) and
  * must not alias the inputs or each other.  Every output element is written

@@ -194,6 +194,6 @@ def test_attn_bwd_rejects_bad_arguments():
     assert bwd(ws=None) == INVAL
     assert bwd(d=96) == UNSUP
     assert bwd(dt=0) == UNSUP                      # the backward is bf16 only
-    assert lib.attn_bwd_workspace_bytes(2, 8, 100) == 6400
+    assert lib.attn_bwd_workspace_bytes(2, 8, 100) == 12800
     assert lib.attn_bwd_workspace_bytes(1, 1, 1) == 256
     assert lib.attn_bwd_workspace_bytes(0, 8, 100) == 0
