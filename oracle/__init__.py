@@ -50,13 +50,13 @@ class Oracle:
         self.lib = ctypes.CDLL(lib_path)
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         self.lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                             vp, vp, vp, i64, vp, vp]
+                                             vp, vp, vp, vp, i64, vp, vp]
         self.lib.oracle_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32,
                                                     i32, vp, vp, vp, i64, vp, vp]
         self.lib.oracle_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                                  i32, f32, vp, i64, vp, vp]
         self.lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                             vp, vp, vp, vp, vp]
+                                             vp, vp, vp, vp, vp, vp]
         for f in (self.lib.oracle_attn_fwd, self.lib.oracle_attn_fwd_varlen, self.lib.oracle_decode_paged,
                   self.lib.oracle_attn_bwd):
             f.restype = ctypes.c_int
@@ -82,8 +82,9 @@ class Oracle:
         r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
         return r, r.size
 
-    def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, rows=None):
-        """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d].
+    def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None, rows=None):
+        """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d]; m_keep an
+        optional dense keep matrix [B,S_q,S_k] (see window_keep).
 
         Returns (o, lse): o [B,A,S_q,d] / lse [B,A,S_q] in fp64, or [n,d] / [n]
         for the flattened row ids ``rows`` = (b*A + h)*S_q + i.
@@ -99,12 +100,13 @@ class Oracle:
             raise ValueError("A must be a multiple of A_kv")
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
+        mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
         r, n = self._rows(rows)
         n_out = B * A * S_q if r is None else n
         o = np.empty((n_out, d), dtype=np.float64)
         lse = np.empty(n_out, dtype=np.float64)
         rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, A, A_kv, S_q, S_k, d,
-                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(r), n,
+                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(r), n,
                                       _ptr(o), _ptr(lse))
         if rc != 0:
             raise ValueError("oracle_attn_fwd rejected its arguments")
@@ -139,7 +141,7 @@ class Oracle:
             return o.reshape(A, T, d), lse.reshape(A, T)
         return o, lse
 
-    def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None):
+    def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None):
         """Gradient of attn_fwd: q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d].
         Returns (dq, dk, dv) in fp64 with the shapes of q, k and v."""
         q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
@@ -151,12 +153,13 @@ class Oracle:
             raise ValueError("k/v must be [B, A_kv, S_k, d] with A % A_kv == 0")
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
+        mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
         dq = np.empty((B, A, S_q, d), dtype=np.float64)
         dk = np.empty((B, A_kv, S_k, d), dtype=np.float64)
         dv = np.empty((B, A_kv, S_k, d), dtype=np.float64)
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _DT[dtype], B, A, A_kv, S_q, S_k, d,
-                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(dq), _ptr(dk),
-                                      _ptr(dv))
+                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(dq),
+                                      _ptr(dk), _ptr(dv))
         if rc != 0:
             raise ValueError("oracle_attn_bwd rejected its arguments")
         return dq, dk, dv
@@ -189,6 +192,23 @@ class Oracle:
 
 
 _default = None
+
+
+def window_keep(B: int, S_q: int, S_k: int, left: int, right: int) -> np.ndarray:
+    """Dense keep matrix [B, S_q, S_k] of a sliding window around each query's
+    position i + (S_k - S_q) (bottom-right alignment, as for causal): key j is
+    kept when i + off - left <= j <= i + off + right; -1 leaves that side
+    unbounded.  Page "Attention Kernel", section "可编程 mask" (sliding window
+    as an element rule)."""
+    off = S_k - S_q
+    i = np.arange(S_q, dtype=np.int64)[:, None] + off
+    j = np.arange(S_k, dtype=np.int64)[None, :]
+    keep = np.ones((S_q, S_k), dtype=bool)
+    if left >= 0:
+        keep &= j >= i - left
+    if right >= 0:
+        keep &= j <= i + right
+    return np.broadcast_to(keep.astype(np.uint8), (B, S_q, S_k)).copy()
 
 
 def default() -> Oracle:

@@ -24,6 +24,11 @@
  *   - causal and j > i + (S_k - S_q)   (query i sits at absolute position
  *                                       S_k - S_q + i: bottom-right alignment)
  *   - q_keep[i] == 0  or  k_keep[j] == 0
+ *   - m_keep[i][j] == 0  (a dense keep matrix per batch row, dense prefill
+ *     and its gradient only: any element rule -- sliding window, block
+ *     sparsity, document boundaries -- is handed to the oracle in this form,
+ *     built from the rule's definition; page "Attention Kernel", section
+ *     "可编程 mask")
  *   - j lies outside i's sequence (packed varlen)
  * A row whose scores are all -inf (including S_k == 0) returns O = 0 and
  * LSE = -inf (page "Attention Kernel", section "Online softmax": a fully
@@ -150,13 +155,14 @@ static void scratch_free(struct scratch *w)
 
 /*
  * Batched prefill.  q, o: [B, A, S_q, d]; k, v: [B, A_kv, S_k, d];
- * q_keep: [B, S_q] or NULL; k_keep: [B, S_k] or NULL.
+ * q_keep: [B, S_q] or NULL; k_keep: [B, S_k] or NULL; m_keep: [B, S_q, S_k]
+ * or NULL (shared by every head).
  * rows: flattened row ids (b*A + h)*S_q + i to compute, or NULL for all rows
  * in order.  o receives [n_rows, d] doubles, lse [n_rows].
  */
 int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
                     int B, int A, int A_kv, int S_q, int S_k, int d, float scale, int causal,
-                    const uint8_t *q_keep, const uint8_t *k_keep,
+                    const uint8_t *q_keep, const uint8_t *k_keep, const uint8_t *m_keep,
                     const int64_t *rows, int64_t n_rows, double *o, double *lse)
 {
     if (B <= 0 || A <= 0 || A_kv <= 0 || S_q < 0 || S_k < 0 || d <= 0 || A % A_kv != 0)
@@ -194,6 +200,8 @@ int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
                     visible = 0;
                 if (k_keep && !k_keep[(int64_t)b * S_k + j])
                     visible = 0;
+                if (m_keep && !m_keep[((int64_t)b * S_q + i) * S_k + j])
+                    visible = 0;
                 w.vis[j] = (unsigned char)visible;
             }
             attend_row(q, id * d, k, v, dt, w.off, w.vis, S_k, d, (double)scale, w.s, w.p,
@@ -216,7 +224,7 @@ int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
  */
 int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *do_, int dt,
                     int B, int A, int A_kv, int S_q, int S_k, int d, float scale, int causal,
-                    const uint8_t *q_keep, const uint8_t *k_keep,
+                    const uint8_t *q_keep, const uint8_t *k_keep, const uint8_t *m_keep,
                     double *dq, double *dk, double *dv)
 {
     if (B <= 0 || A <= 0 || A_kv <= 0 || S_q < 0 || S_k < 0 || d <= 0 || A % A_kv != 0)
@@ -257,6 +265,8 @@ int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *do_
                         if (causal && (int64_t)j > (int64_t)i + (S_k - S_q))
                             visible = 0;
                         if (k_keep && !k_keep[(int64_t)b * S_k + j])
+                            visible = 0;
+                        if (m_keep && !m_keep[((int64_t)b * S_q + i) * S_k + j])
                             visible = 0;
                         w.vis[j] = (unsigned char)visible;
                     }

@@ -409,6 +409,75 @@ def pin_paged_brute_force(orc):
     del rng
 
 
+# ---- dense keep matrix and sliding windows (page "Attention Kernel", section
+# "可编程 mask": element rules given to the oracle as a keep matrix)
+
+def pin_dense_keep_brute_force(orc):
+    rng = np.random.default_rng(41)
+    for S_q, S_k, d, A, A_kv, causal in [(4, 6, 3, 2, 1, True), (5, 5, 2, 2, 2, False), (6, 4, 2, 2, 1, True)]:
+        q = _f32(rng.standard_normal((2, A, S_q, d)))
+        k = _f32(rng.standard_normal((2, A_kv, S_k, d)))
+        v = _f32(rng.standard_normal((2, A_kv, S_k, d)))
+        kk = (rng.random((2, S_k)) > 0.2).astype(np.uint8)
+        mk = (rng.random((2, S_q, S_k)) > 0.35).astype(np.uint8)
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.75, causal=causal, k_keep=kk, m_keep=mk)
+        G = A // A_kv
+        for b in range(2):
+            for h in range(A):
+                for i in range(S_q):
+                    vis = [bool(kk[b, j]) and bool(mk[b, i, j]) and (not causal or j <= i + S_k - S_q)
+                           for j in range(S_k)]
+                    want, wl = _brute([float(x) for x in q[b, h, i]],
+                                      [[float(x) for x in row] for row in k[b, h // G]],
+                                      [[float(x) for x in row] for row in v[b, h // G]], 0.75, vis)
+                    assert np.allclose(o[b, h, i], want, rtol=0, atol=1e-13), (S_q, S_k, b, h, i)
+                    assert (wl == -math.inf and lse[b, h, i] == -np.inf) or abs(lse[b, h, i] - wl) < 1e-13
+
+
+def pin_dense_keep_matches_flag_masks(orc):
+    """The causal pattern, and the outer product of q_keep and k_keep, given as
+    a keep matrix reproduce the flags bit for bit."""
+    rng = np.random.default_rng(42)
+    B, A, A_kv, S_q, S_k, d = 2, 2, 1, 5, 7, 3
+    q = _f32(rng.standard_normal((B, A, S_q, d)))
+    k = _f32(rng.standard_normal((B, A_kv, S_k, d)))
+    v = _f32(rng.standard_normal((B, A_kv, S_k, d)))
+    o1, l1 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=True)
+    causal_pattern = np.tril(np.ones((S_q, S_k), np.uint8), S_k - S_q)
+    o2, l2 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, m_keep=np.broadcast_to(causal_pattern, (B, S_q, S_k)))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    qk = (rng.random((B, S_q)) > 0.3).astype(np.uint8)
+    kk = (rng.random((B, S_k)) > 0.3).astype(np.uint8)
+    o3, l3 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, q_keep=qk, k_keep=kk)
+    o4, l4 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, m_keep=qk[:, :, None] * kk[:, None, :])
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+
+
+def pin_window_equals_key_slice(orc):
+    """A sliding-window row equals plain attention over the contiguous slice of
+    keys the window keeps (same keys in the same order: bit for bit); a row
+    whose window holds no key is fully masked."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(43)
+    for S_q, S_k, left, right in [(6, 9, 2, 1), (7, 7, 3, 0), (5, 8, 0, 0), (4, 6, -1, 1), (6, 6, 2, -1),
+                                  (8, 5, 1, 0)]:
+        q = _f32(rng.standard_normal((1, 2, S_q, 4)))
+        k = _f32(rng.standard_normal((1, 1, S_k, 4)))
+        v = _f32(rng.standard_normal((1, 1, S_k, 4)))
+        mk = oracle_pkg.window_keep(1, S_q, S_k, left, right)
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.625, m_keep=mk)
+        off = S_k - S_q
+        for i in range(S_q):
+            lo = max(0, i + off - left) if left >= 0 else 0
+            hi = min(S_k - 1, i + off + right) if right >= 0 else S_k - 1
+            if lo > hi:
+                assert np.all(o[0, :, i] == 0) and np.all(np.isneginf(lse[0, :, i])), (S_q, S_k, left, right, i)
+                continue
+            os_, ls = orc.attn_fwd(q[:, :, i:i + 1], k[:, :, lo:hi + 1], v[:, :, lo:hi + 1], dtype="f32", scale=0.625)
+            assert np.array_equal(o[0, :, i], os_[0, :, 0]), (S_q, S_k, left, right, i)
+            assert np.array_equal(lse[0, :, i], ls[0, :, 0]), (S_q, S_k, left, right, i)
+
+
 # ---- gradient (oracle_attn_bwd): the exact derivative of the forward above.
 # Pinned against central finite differences of the (already pinned) forward
 # in fp64, closed forms and invariants of the softmax Jacobian.
@@ -422,30 +491,36 @@ def _bwd_problem(B, A, A_kv, S_q, S_k, d, seed):
     return q, k, v, do
 
 
-def _loss(orc, q, k, v, do, scale, causal, q_keep=None, k_keep=None):
-    o, _ = orc.attn_fwd(q, k, v, dtype="f64", scale=scale, causal=causal, q_keep=q_keep, k_keep=k_keep)
+def _loss(orc, q, k, v, do, scale, causal, q_keep=None, k_keep=None, m_keep=None):
+    o, _ = orc.attn_fwd(q, k, v, dtype="f64", scale=scale, causal=causal, q_keep=q_keep, k_keep=k_keep,
+                        m_keep=m_keep)
     return float(np.sum(o.reshape(do.shape) * do))
 
 
 def pin_bwd_finite_differences(orc):
     """Every entry of dQ, dK, dV equals the central difference of
     L = sum(O * dO) computed with the forward oracle (h = 1e-6, fp64)."""
-    cases = [  # B, A, A_kv, S_q, S_k, d, causal, masks
-        (1, 2, 1, 3, 4, 3, True, False),
-        (1, 2, 2, 4, 3, 2, False, True),
-        (2, 2, 1, 3, 3, 2, True, True),
+    cases = [  # B, A, A_kv, S_q, S_k, d, causal, masks (1: keep flags, 2: a dense keep matrix)
+        (1, 2, 1, 3, 4, 3, True, 0),
+        (1, 2, 2, 4, 3, 2, False, 1),
+        (2, 2, 1, 3, 3, 2, True, 1),
+        (1, 2, 1, 4, 5, 2, False, 2),
     ]
     h = 1e-6
     for n, (B, A, A_kv, S_q, S_k, d, causal, masks) in enumerate(cases):
         q, k, v, do = _bwd_problem(B, A, A_kv, S_q, S_k, d, 100 + n)
         scale = 0.6875  # exact in fp32
-        qk = kk = None
-        if masks:
+        qk = kk = mk = None
+        if masks == 1:
             qk = np.ones((B, S_q), np.uint8)
             qk[0, 1] = 0
             kk = np.ones((B, S_k), np.uint8)
             kk[-1, 0] = 0
-        dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=scale, causal=causal, q_keep=qk, k_keep=kk)
+        elif masks == 2:
+            mk = (np.random.default_rng(200 + n).random((B, S_q, S_k)) > 0.4).astype(np.uint8)
+            mk[0, 2, :] = 0  # one row fully masked
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=scale, causal=causal, q_keep=qk, k_keep=kk,
+                                  m_keep=mk)
         for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
             num = np.zeros_like(x)
             for idx in np.ndindex(x.shape):
@@ -454,8 +529,8 @@ def pin_bwd_finite_differences(orc):
                 xm[idx] -= h
                 args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
                 args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
-                num[idx] = (_loss(orc, *args_p, do, scale, causal, qk, kk) -
-                            _loss(orc, *args_m, do, scale, causal, qk, kk)) / (2 * h)
+                num[idx] = (_loss(orc, *args_p, do, scale, causal, qk, kk, mk) -
+                            _loss(orc, *args_m, do, scale, causal, qk, kk, mk)) / (2 * h)
             err = np.max(np.abs(num - g))
             assert err <= 1e-7, (n, name, err)
 

@@ -44,6 +44,10 @@ MUTANTS = [
     ("gradient: dQ built from V", "dqi[e] += sc * ds * ld(k,", "dqi[e] += sc * ds * ld(v,", 0),
     ("gradient: dP built from K", "acc += ld(do_, id * d + e, dt) * ld(v, w.off[j] + e, dt);",
      "acc += ld(do_, id * d + e, dt) * ld(k, w.off[j] + e, dt);", 0),
+    ("keep matrix ignored (dense)", "if (m_keep && !m_keep[((int64_t)b * S_q + i) * S_k + j])", "if (0)", 1),
+    ("keep matrix transposed (dense)", "m_keep[((int64_t)b * S_q + i) * S_k + j]",
+     "m_keep[((int64_t)b * S_k + j) * S_q + i]", 1),
+    ("gradient: keep matrix ignored", "if (m_keep && !m_keep[((int64_t)b * S_q + i) * S_k + j])", "if (0)", 2),
 ]
 
 BATTERY = r"""
