@@ -425,6 +425,7 @@ def main():
     }
 
     out["backward"] = bench_backward(w, args.steps, args.warmup)
+    out["window"] = bench_window(args.steps, args.warmup, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
@@ -493,6 +494,55 @@ def bench_backward(w, steps: int, warmup: int) -> dict:
             "flops": flops,
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 (the prefill workload)",
             "kernels": "bwd_dq_kernel<128> then bwd_dkdv_kernel<128> (one call)"}
+
+
+def window_pairs(S: int, left: int) -> int:
+    """(row, key) pairs a causal sliding window of `left` keys before the
+    diagonal keeps in one S x S head: sum_i min(i + 1, left + 1)."""
+    w = left + 1
+    if S <= w:
+        return S * (S + 1) // 2
+    return w * (w + 1) // 2 + (S - w) * w
+
+
+def bench_window(steps: int, warmup: int, stream) -> dict:
+    """Causal sliding-window prefill, GQA B=1 A=32 A_kv=8 S=16384 d=128, each
+    query sees its own key and the 4095 before it: key tiles outside every
+    row's window are skipped whole.  FLOPs = 4 d A x (kept pairs per head),
+    the window analogue of the causal-adjusted count."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    B, A, A_kv, S, d, left = 1, 32, 8, 16384, 128, 4095
+    p = gen.make_dense(B, A, A_kv, S, S, d, dtype="bf16", causal=True, seed=1006)
+    q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, A, S), dtype=torch.float32, device="cuda")
+
+    def run():
+        ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=True, window=(left, -1), stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    flops = 4.0 * d * A * B * window_pairs(S, left)
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    return {"metric": "sliding-window causal prefill TFLOP/s (kept pairs)", "value": round(tf, 2),
+            "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "avg_ms": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
+            "min_ms": round(float(ms.min()), 5), "flops": flops,
+            "workload": f"GQA causal B={B} A={A} A_kv={A_kv} S={S} d={d} bf16, window: {left} keys before the "
+                        "diagonal"}
 
 
 def measured_ceilings(stream) -> dict:

@@ -27,11 +27,17 @@ class _Mask(ctypes.Structure):
     _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p)]
 
 
+class _Window(ctypes.Structure):
+    _fields_ = [("left", ctypes.c_int), ("right", ctypes.c_int)]
+
+
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-_lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, ctypes.POINTER(_Mask), _i, _vp]
+_WP = ctypes.POINTER(_Window)
+_lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, ctypes.POINTER(_Mask), _WP, _i,
+                          _vp]
 _lib.attn_fwd.restype = _i
 _lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
-                                 ctypes.POINTER(_Mask), _i, _vp]
+                                 ctypes.POINTER(_Mask), _WP, _i, _vp]
 _lib.attn_fwd_varlen.restype = _i
 _lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                    _vp, _sz, _vp]
@@ -39,7 +45,7 @@ _lib.attn_decode_paged.restype = _i
 _lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _vp]
 _lib.attn_decode_paged_workspace_bytes.restype = _sz
 _lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
-                          ctypes.POINTER(_Mask), _i, _vp, _sz, _vp]
+                          ctypes.POINTER(_Mask), _WP, _i, _vp, _sz, _vp]
 _lib.attn_bwd.restype = _i
 _lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.attn_bwd_workspace_bytes.restype = _sz
@@ -122,13 +128,23 @@ def _mask(q_keep, k_keep):
     return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep)))
 
 
+def _window(window):
+    """None, or (left, right) with -1 for an unbounded side."""
+    if window is None:
+        return None
+    left, right = window
+    return ctypes.byref(_Window(int(left), int(right)))
+
+
 def _check(status: int, where: str) -> None:
     if status != ATTN_OK:
         raise AttnError(status, where)
 
 
-def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None, k_keep=None, stream=None):
-    """O, LSE of softmax(Q K^T * scale + M) V.  q/o [B,A,S_q,d], k/v [B,A_kv,S_k,d], lse [B,A,S_q] fp32."""
+def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None, k_keep=None, window=None,
+             stream=None):
+    """O, LSE of softmax(Q K^T * scale + M) V.  q/o [B,A,S_q,d], k/v [B,A_kv,S_k,d], lse [B,A,S_q] fp32;
+    window = (left, right) sliding window around each query's position, -1 = unbounded side."""
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, heads, S, d]")
@@ -146,12 +162,13 @@ def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None
         raise ValueError("k_keep must be [B, S_k]")
     dev = _dev(q, k, v, o, lse, q_keep, k_keep)
     st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, A, A_kv, S_q, S_k, d, float(scale),
-                       int(bool(causal)), _mask(q_keep, k_keep), _dtype_code(q), _stream(stream, dev))
+                       int(bool(causal)), _mask(q_keep, k_keep), _window(window), _dtype_code(q),
+                       _stream(stream, dev))
     _check(st, "attn_fwd")
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: float, causal: bool = True,
-                    q_keep=None, k_keep=None, stream=None):
+                    q_keep=None, k_keep=None, window=None, stream=None):
     """Packed varlen prefill.  q/o [A,T,d], k/v [A_kv,T,d], lse [A,T]; cu_seqlens int32 device,
     cu_seqlens_host the same values on the host (numpy int32)."""
     torch = _torch()
@@ -173,7 +190,7 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: floa
     dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep)
     st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                               cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d, float(scale), int(bool(causal)),
-                              _mask(q_keep, k_keep), _dtype_code(q), _stream(stream, dev))
+                              _mask(q_keep, k_keep), _window(window), _dtype_code(q), _stream(stream, dev))
     _check(st, "attn_fwd_varlen")
 
 
@@ -219,7 +236,7 @@ def attn_bwd_workspace_bytes(B: int, A: int, S_q: int) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, causal: bool = False, q_keep=None,
-             k_keep=None, stream=None):
+             k_keep=None, window=None, stream=None):
     """dQ, dK, dV of attn_fwd.  q/o/dout/dq [B,A,S_q,d], k/v/dk/dv [B,A_kv,S_k,d], lse [B,A,S_q] fp32 (the
     forward's); workspace a uint8 device tensor of at least attn_bwd_workspace_bytes(B, A, S_q) bytes."""
     torch = _torch()
@@ -247,5 +264,5 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, caus
     dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, workspace, q_keep, k_keep)
     st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                        B, A, A_kv, S_q, S_k, d, float(scale), int(bool(causal)), _mask(q_keep, k_keep),
-                       _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
+                       _window(window), _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_bwd")

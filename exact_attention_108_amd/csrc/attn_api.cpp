@@ -16,14 +16,25 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 attn_status launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+bool valid_window(const attn_window* w) { return w == nullptr || (w->left >= -1 && w->right >= -1); }
+
+// window edges as the kernels take them: -1 = unbounded; causal makes the
+// right edge min(right, 0), which is 0 for every valid right (>= -1)
+void window_edges(const attn_window* w, int causal, int& left, int& right) {
+  left = w ? w->left : -1;
+  right = w ? w->right : -1;
+  if (causal) right = 0;
+}
+
 attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int A, int A_kv, int d_h, float scale, int causal, const attn_mask* mask) {
+                            int A, int A_kv, int d_h, float scale, int causal, const attn_mask* mask,
+                            const attn_window* window) {
   attn::FwdParams p{};
   p.q = q;
   p.k = k;
@@ -39,6 +50,7 @@ attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  window_edges(window, causal, p.win_left, p.win_right);
   return p;
 }
 
@@ -53,9 +65,10 @@ attn_status check_prefill_support(attn_dtype dtype, int d_h) {
 
 ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int A, int A_kv, int S_q, int S_k, int d_h, float scale,
-                                 int causal, const attn_mask* mask, attn_dtype dtype, void* stream) {
+                                 int causal, const attn_mask* mask, const attn_window* window,
+                                 attn_dtype dtype, void* stream) {
   if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
-  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
   if (S_q > 0 && (!q || !o || !lse)) return ATTN_ERR_INVAL;
   if (S_k > 0 && (!k || !v)) return ATTN_ERR_INVAL;
@@ -68,7 +81,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   // element offsets inside the kernels are size_t; per-(b,h) row counts are int
   if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
     return ATTN_ERR_UNSUPPORTED;
-  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask);
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window);
   p.B = B;
   p.S_q = S_q;
   p.S_k = S_k;
@@ -82,9 +95,10 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
 ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                         const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                                         int n_seq, int total_tokens, int A, int A_kv, int d_h, float scale,
-                                        int causal, const attn_mask* mask, attn_dtype dtype, void* stream) {
+                                        int causal, const attn_mask* mask, const attn_window* window,
+                                        attn_dtype dtype, void* stream) {
   if (n_seq < 0 || total_tokens < 0 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
-  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
   if (!cu_seqlens || !cu_seqlens_host) return ATTN_ERR_INVAL;
   if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seq] != total_tokens) return ATTN_ERR_INVAL;
@@ -105,7 +119,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
     if (nt > max_tiles) max_tiles = nt;
   }
   if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
-  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask);
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window);
   p.cu_seqlens = cu_seqlens;
   p.n_seq = n_seq;
   p.T = total_tokens;
@@ -205,9 +219,10 @@ ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int A, int S_q) {
 ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                  const float* lse, void* dq, void* dk, void* dv, int B, int A, int A_kv, int S_q,
                                  int S_k, int d_h, float scale, int causal, const attn_mask* mask,
-                                 attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                                 const attn_window* window, attn_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
-  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
   if (S_q > 0 && (!q || !o || !dout || !lse || !dq)) return ATTN_ERR_INVAL;
   if (S_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVAL;
@@ -245,6 +260,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  window_edges(window, causal, p.win_left, p.win_right);
   return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
 }
 

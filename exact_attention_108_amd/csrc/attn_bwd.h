@@ -23,6 +23,10 @@ struct BwdParams {
   int B, A, A_kv, G, S_q, S_k, d;
   int causal;
   float scale, scale_log2;
+  // sliding window around query i's position i + S_k - S_q: key j is kept
+  // when i + off - win_left <= j <= i + off + win_right; -1 leaves a side
+  // unbounded.  The causal flag is folded into win_right (<= 0).
+  int win_left, win_right;
   // XCD-blocked grid orders (0 = plain order), set by launch_bwd_bf16
   int dq_units_per_xcd, dq_group;  // units: (batch, query head)
   int kv_units_per_xcd, kv_group;  // units: (batch, KV head)

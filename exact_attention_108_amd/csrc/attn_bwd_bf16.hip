@@ -29,8 +29,9 @@
 //      sum), one key per lane:
 //        S = Q . K^T,  dP = dO . V^T  (K and V rows resident),
 //        dV^T += dO^T . P,  dK^T += Q^T . dS  (transposing reads of Q, dO).
-// The per-element predicate (causal bottom-right diagonal, keep masks, rows
-// and keys past the ends) is the forward's; rows whose LSE is -inf (fully
+// The per-element predicate (sliding window whose right edge is the causal
+// bottom-right diagonal, keep masks, rows and keys past the ends) is the
+// forward's; rows whose LSE is -inf (fully
 // masked) take no part.
 #include <type_traits>
 
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const int h = bh % p.A, b = bh / p.A, hk = h / p.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int S_q = p.S_q, S_k = p.S_k, off = S_k - S_q;
-  const bool causal = p.causal != 0;
+  const int wl = p.win_left, wr = p.win_right;
   const size_t q_row0 = (size_t)(b * p.A + h) * S_q;
   const size_t k_row0 = (size_t)(b * p.A_kv + hk) * S_k;
   const int q0 = qt * kBwdQRows;
@@ -146,9 +147,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     if (g == 0) *(float2*)(p.row_stats + 2 * (q_row0 + qrow)) = make_float2(lrow, drow);
   }
 
-  int kend = S_k;
-  if (causal) kend = min(kend, q0 + kBwdQRows - 1 + off + 1);
-  const int n_tiles = kend > 0 ? (kend + kKeyTile - 1) / kKeyTile : 0;
+  // key tiles some row of the workgroup keeps: j_lo + [0, n_tiles)
+  int kbeg = 0, kend = S_k;
+  if (wr >= 0) kend = min(kend, q0 + kBwdQRows - 1 + off + wr + 1);
+  if (wl >= 0) kbeg = max(q0 + off - wl, 0);
+  const int j_lo = kbeg / kKeyTile;
+  const int n_tiles = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile - j_lo : 0;
 
   int koff[KSTEPS];  // row-major operand read: row l32, chunk 2t + g
 #pragma unroll
@@ -177,13 +181,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   auto issue = [&](int j, int slot) {
     const uint32_t dst = lds_base + slot * SLOT_BYTES;
-    copy_rows<D, kKeyTile>(kbase, S_k, j * kKeyTile, dst);
-    copy_rows<D, kKeyTile>(vbase, S_k, j * kKeyTile, dst + TILE_BYTES);
+    copy_rows<D, kKeyTile>(kbase, S_k, (j_lo + j) * kKeyTile, dst);
+    copy_rows<D, kKeyTile>(vbase, S_k, (j_lo + j) * kKeyTile, dst + TILE_BYTES);
   };
   // key k0 + lane is in range and kept.  The keep byte is an ordinary load,
   // so with a key mask each step also waits for the copies in flight.
   auto key_ok = [&](int j) -> bool {
-    const int key = j * kKeyTile + lane;
+    const int key = (j_lo + j) * kKeyTile + lane;
     return key < S_k && (kkeep == nullptr || kkeep[key] != 0);
   };
 
@@ -204,13 +208,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   };
   // P, dS = P (dP - D) of tile j, then dQ^T += K^T . dS^T.  A dead row has
   // lrow = +inf, so its p = 2^-inf = 0 without a mask.  MASKED adds the
-  // per-element predicate (keys past S_k, dropped keys, causal diagonal).
+  // per-element predicate (keys past S_k, dropped keys, the window's edges).
   auto grad = [&](const char* lds, int j, bool ok, const f32x16 (&s)[2], const f32x16 (&dp)[2], auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const int k0 = j * kKeyTile;
+    const int k0 = (j_lo + j) * kKeyTile;
     // element r of 32-key block kb holds key k0 + 32 kb + 8(r/4) + 4g + r%4
     const uint64_t kvalid = __ballot(ok) >> (4 * g);
-    const int lim = causal ? qrow + off - k0 - 4 * g : (1 << 30);
+    const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
+    const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 dsb[2];
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         float x = fmaf(s[kb][r], cs, -lrow);
         if constexpr (MASKED) {
           const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-          x = (((kvalid >> c) & 1) && c <= lim) ? x : -INFINITY;
+          x = (((kvalid >> c) & 1) && c <= lim && c >= lo) ? x : -INFINITY;
         }
         const float pr = exp2_fast(x);
         dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[kb][r] - drow));
@@ -238,9 +243,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // whether tile j needs the per-element predicate in this wave (uniform)
   const int wave_row0 = q0 + wave * 32;
   auto tile_masked = [&](int j, bool ok) -> bool {
-    const int k0 = j * kKeyTile;
+    const int k0 = (j_lo + j) * kKeyTile;
     bool full = k0 + kKeyTile <= S_k && __ballot(ok) == ~0ull;
-    if (causal) full = full && k0 + kKeyTile - 1 <= wave_row0 + off;
+    if (wr >= 0) full = full && k0 + kKeyTile - 1 <= wave_row0 + off + wr;
+    if (wl >= 0) full = full && k0 >= wave_row0 + 31 + off - wl;
     return !full;
   };
 
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int hk = bk % p.A_kv, b = bk / p.A_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
   const int S_q = p.S_q, S_k = p.S_k, off = S_k - S_q;
-  const bool causal = p.causal != 0;
+  const int wl = p.win_left, wr = p.win_right;
   const size_t k_row0 = (size_t)(b * p.A_kv + hk) * S_k;
   const int key = kt * kBwdKRows + wave * 32 + l32;  // this lane's key
   bool key_live = key < S_k;
@@ -373,11 +379,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // query rows that can see a key of this workgroup: i + off >= first key;
   // blocks run over (query head of the group, 32-row block)
-  const int k_first = kt * kBwdKRows;
-  const int i_first = causal ? max(k_first - off, 0) : 0;
+  // (row i keeps key j when i + off - wl <= j <= i + off + wr)
+  const int k_first = kt * kBwdKRows, k_last = k_first + kBwdKRows - 1;
+  const int i_first = wr >= 0 ? max(k_first - off - wr, 0) : 0;
+  const int i_end = wl >= 0 ? min(k_last - off + wl + 1, S_q) : S_q;
   const int qb_first = i_first / kQBlock;
-  const int n_qb = (S_q + kQBlock - 1) / kQBlock;
-  const int nq = max(n_qb - qb_first, 0);
+  const int qb_end = i_end > i_first ? (i_end + kQBlock - 1) / kQBlock : qb_first;
+  const int nq = qb_end - qb_first;
   const int n_blocks = p.G * nq;
 
   auto issue = [&](int idx, int slot) {
@@ -409,14 +417,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // P and dS of block idx, then dV^T += dO^T . P and dK^T += Q^T . dS.  A
   // dead row has L2 = +inf, so its p is 0 without a mask; MASKED adds the
   // per-element predicate (rows past S_q, which arrive zero-filled with L2 =
-  // 0, dropped or absent keys, causal diagonal).
+  // 0, dropped or absent keys, the window's edges).
   auto grad = [&](const char* lds, int idx, const f32x16& s, const f32x16& dp, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const float* st = (const float*)(lds + 2 * BLOCK_BYTES);
     const int r0 = (qb_first + idx % nq) * kQBlock;
     // element r holds query row r0 + m, m = 8(r/4) + 4g + r%4, of this lane's key
-    const int m_lo = causal ? key - off - r0 - 4 * g : -(1 << 30);
-    const int m_hi = key_live ? S_q - r0 - 4 * g : -(1 << 30);
+    const int m_lo = wr >= 0 ? key - off - wr - r0 - 4 * g : -(1 << 30);
+    int m_hi = key_live ? S_q - r0 - 4 * g : -(1 << 30);
+    if (wl >= 0) m_hi = min(m_hi, key - off + wl - r0 - 4 * g + 1);
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -451,11 +460,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   // whether block idx needs the per-element predicate in this wave (uniform)
   const bool wave_keys_live = __ballot(key_live) == ~0ull;
-  const int wave_key_last = kt * kBwdKRows + wave * 32 + 31;
+  const int wave_key_first = kt * kBwdKRows + wave * 32, wave_key_last = wave_key_first + 31;
   auto block_masked = [&](int idx) -> bool {
     const int r0 = (qb_first + idx % nq) * kQBlock;
     bool full = wave_keys_live && r0 + kQBlock <= S_q;
-    if (causal) full = full && wave_key_last <= r0 + off;
+    if (wr >= 0) full = full && wave_key_last <= r0 + off + wr;
+    if (wl >= 0) full = full && wave_key_first >= r0 + kQBlock - 1 + off - wl;
     return !full;
   };
 

@@ -28,6 +28,10 @@ struct FwdParams {
   float scale_log2;           // scale * log2(e)
   int xcd_heads;              // dense: (batch, head) pairs per XCD block, 0 = plain order
   int xcd_group;              // dense: heads whose query tiles are issued together
+  // sliding window around query i's position i + off (off = S_k - S_q): key
+  // j is kept when i + off - win_left <= j <= i + off + win_right; -1 leaves
+  // a side unbounded.  The causal flag is folded into win_right (<= 0).
+  int win_left, win_right;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin

@@ -85,12 +85,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int S_q = rb.S_q, S_k = rb.S_k;
   const int off = S_k - S_q;                 // causal: query i sits at position i + off
   const int qrow = rb.q0 + wave * 32 + l32;  // this lane's query row
-  const bool causal = p.causal != 0;
 
-  // ---- number of key tiles this workgroup needs
-  int kend = S_k;
-  if (causal) kend = min(kend, rb.q0 + kRows - 1 + off + 1);
-  const int n_tiles = kend > 0 ? (kend + kBc - 1) / kBc : 0;
+  // ---- key tiles this workgroup needs: [j_lo, j_hi), the keys some row of
+  // it keeps under the window (the causal diagonal is its right edge)
+  const int wl = p.win_left, wr = p.win_right;
+  const int q_first = rb.q0, q_last = rb.q0 + kRows - 1;
+  int kbeg = 0, kend = S_k;
+  if (wr >= 0) kend = min(kend, q_last + off + wr + 1);
+  if (wl >= 0) kbeg = max(q_first + off - wl, 0);
+  const int j_lo = kbeg / kBc;
+  const int n_tiles = kend > kbeg ? (kend + kBc - 1) / kBc - j_lo : 0;
+
+  // ---- tile order.  The tiles [j_ul, j_uh) need no per-element predicate for
+  // any row of the workgroup (inside S_k, inside every row's window, no key
+  // mask); they run first, the masked tiles [j_lo, j_ul) and [j_uh, j_hi)
+  // after them (the online softmax does not depend on the order).  Logical
+  // tile t is physical tile phys(t).
+  int j_ul = j_lo, j_uh = j_lo;
+  if (rb.k_keep == nullptr && n_tiles > 0) {
+    int ul = wl >= 0 ? (max(q_last + off - wl, 0) + kBc - 1) / kBc : 0;
+    int uh = S_k / kBc;
+    if (wr >= 0) uh = min(uh, max(q_first + off + wr + 1, 0) / kBc);
+    ul = max(ul, j_lo);
+    uh = min(uh, j_lo + n_tiles);
+    if (ul < uh) {
+      j_ul = ul;
+      j_uh = uh;
+    }
+  }
+  const int n_mid = j_uh - j_ul;
+  const int n_left = j_ul - j_lo;
+  // (written with 0/1 factors: selects here became branches at the top of
+  // every iteration.  Without a left edge n_left = 0 and phys(t) = j_ul + t.)
+  auto phys = [=](int t) -> int {
+    const int u = t - n_mid;
+    const int in_left = (unsigned)u < (unsigned)n_left;  // u in [0, n_left): left edge tiles
+    const int past = u >= n_left;                         // right edge tiles
+    const int base = j_ul + t - past * n_left;            // middle, then [j_uh, j_hi)
+    return base + in_left * (j_lo + u - base);
+  };
 
   // ---- resident Q operand: lane holds Q[qrow][16t + 8g .. +7] for each t
   bf16x8 qf[KSTEPS];
@@ -127,8 +160,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int i = 0; i < LD_PER_T; ++i) coff[i] = (uint32_t)((i * RPC + rowc) * D * 2 + cc * 16);
   auto tile_rsrc = [&](const uint16_t* gsrc, int t) {
-    const int rows = min(max(S_k - t * kBc, 0), kBc);
-    return make_buffer_rsrc(gsrc + (size_t)t * kBc * D, (uint32_t)(rows * D * 2));
+    const int k0 = phys(t) * kBc;
+    const int rows = min(max(S_k - k0, 0), kBc);
+    return make_buffer_rsrc(gsrc + (size_t)k0 * D, (uint32_t)(rows * D * 2));
   };
   // part i (of LD_PER_T) of one tile of K (or V) into LDS byte offset `dst`
   auto copy_part = [&](const i32x4& rsrc, uint32_t dst, int i) {
@@ -136,7 +170,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   auto copy_keep = [&](int t) {
     if (rb.k_keep && tid < kBc && t < n_tiles) {
-      const int key = t * kBc + tid;
+      const int key = phys(t) * kBc + tid;
       sKeep[t & 1][tid] = key < S_k ? rb.k_keep[key] : 0;
     }
   };
@@ -201,23 +235,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (p == NQ / 2) issue(1);
     }
   };
-  // per-element predicate of tile t (keys past S_k, the causal diagonal, the
-  // key keep-mask): dead scores become -inf
+  // per-element predicate of tile t (keys past S_k, the window's edges -- the
+  // causal diagonal is its right edge --, the key keep-mask): dead scores
+  // become -inf
   auto mask = [&](f32x16 (&s)[2], int t) {
-    const int k0 = t * kBc;
+    const int k0 = phys(t) * kBc;
     // bit k of kvalid: key k0 + k exists and is kept (same for every lane)
     bool valid = k0 + lane < S_k;
     if (rb.k_keep) valid = valid && sKeep[t & 1][lane] != 0;
     const uint64_t kvalid = __ballot(valid) >> (4 * g);
     // element (kb, r) holds key k0 + kl, kl = 32kb + 8(r/4) + 4g + r%4;
-    // causal: dead when kl > qrow + off - k0
-    const int lim = causal ? qrow + off - k0 - 4 * g : (1 << 30);
+    // dead when kl > qrow + off + wr - k0 or kl < qrow + off - wl - k0
+    const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
+    const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 32 * kb + 8 * (r >> 2) + (r & 3);  // kl - 4g
-        const bool live = ((kvalid >> c) & 1) && c <= lim;
+        const bool live = ((kvalid >> c) & 1) && c <= lim && c >= lo;
         s[kb][r] = live ? s[kb][r] : -INFINITY;
       }
     }
@@ -294,13 +330,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // ---- tiles 0 .. n_full-1 need no per-element predicate for any row of the
-  // workgroup (below the causal diagonal, inside S_k, no key mask)
-  int n_full = 0;
-  if (rb.k_keep == nullptr) {
-    n_full = S_k / kBc;
-    if (causal) n_full = min(n_full, max(rb.q0 + off + 1, 0) / kBc);
-  }
 
   // ---- prologue: K, V of tile 0 and K of tile 1 in flight; S of tile 0
   f32x16 s_cur[2];
@@ -319,7 +348,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     lds_copy_wait_all();
     __syncthreads();
     qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
-    if (n_full == 0) mask(s_cur, 0);
+    if (n_mid == 0) mask(s_cur, 0);
     mx_cur = rowmax(s_cur);
   }
 
@@ -383,8 +412,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr std::integral_constant<int, 1> B1{};
   constexpr std::integral_constant<bool, false> UNMASKED{};
   constexpr std::integral_constant<bool, true> MASKED_T{};
-  // iteration j is predicate-free when tile j+1 < n_full
-  const int n_pair_end = max(n_full - 1, 0) & ~1;
+  // iteration j is predicate-free when tile j+1 < n_mid
+  const int n_pair_end = max(n_mid - 1, 0) & ~1;
   int j = 0;
   for (; j < n_pair_end; j += 2) {
     iteration(B0, UNMASKED, j);

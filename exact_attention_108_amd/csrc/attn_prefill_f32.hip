@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S_q = rb.S_q, S_k = rb.S_k, off = S_k - S_q;
-  const bool causal = p.causal != 0;
+  const int wl = p.win_left, wr = p.win_right;  // window edges (causal folded into wr)
   const float cs = p.scale_log2;
 
   for (int idx = tid; idx < kRows * D; idx += kThreads) {
@@ -62,9 +62,12 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
     sQ[r][e] = row < S_q ? gq[(size_t)row * D + e] : 0.f;
   }
 
-  int kend = S_k;
-  if (causal) kend = min(kend, rb.q0 + kRows + off);
-  const int n_tiles = kend > 0 ? (kend + kBc - 1) / kBc : 0;
+  // keys some row of the workgroup keeps: [kbeg, kend)
+  int kbeg = 0, kend = S_k;
+  if (wr >= 0) kend = min(kend, rb.q0 + kRows - 1 + off + wr + 1);
+  if (wl >= 0) kbeg = max(rb.q0 + off - wl, 0);
+  const int j_lo = kbeg / kBc;
+  const int j_hi = kend > kbeg ? (kend + kBc - 1) / kBc : j_lo;
 
   float m_run[kRowsPerWave], l_run[kRowsPerWave], acc[kRowsPerWave][2];
 #pragma unroll
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
     acc[rr][0] = acc[rr][1] = 0.f;
   }
 
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = j_lo; j < j_hi; ++j) {
     const int k0 = j * kBc;
     __syncthreads();  // previous tile fully consumed (and sQ written)
     for (int idx = tid; idx < kBc * D; idx += kThreads) {
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
       const int row = rb.q0 + qr;
       float s = 0.f;
       for (int e = 0; e < D; ++e) s = fmaf(sQ[qr][e], sK[lane][e], s);
-      const bool dead = sKeep[lane] == 0 || (causal && key > row + off);
+      const bool dead = sKeep[lane] == 0 || (wr >= 0 && key > row + off + wr) || (wl >= 0 && key < row + off - wl);
       s = dead ? -INFINITY : s;
       const float mx = wave_max(s);
       const float m_new = fmaxf(m_run[rr], mx * cs);

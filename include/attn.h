@@ -66,6 +66,18 @@ typedef struct {
     const uint8_t *k_keep;
 } attn_mask;
 
+/* Optional sliding window (page "Attention Kernel", section "可编程 mask":
+ * a window is an element rule, and key tiles outside every row's window are
+ * skipped whole).  Query i sits at position p_i = i + (S_k - S_q) (within its
+ * sequence for varlen); key j is kept when p_i - left <= j <= p_i + right.
+ * -1 leaves a side unbounded; other negative values are ATTN_ERR_INVAL.  With
+ * causal = 1 the right edge is min(right, 0) (right = -1 gives the causal
+ * diagonal).  NULL = no window. */
+typedef struct {
+    int left;
+    int right;
+} attn_window;
+
 /*
  * Batched prefill attention (page "Attention Kernel", section "问题与成本";
  * causal tile skipping and the saved log-sum-exp: section "FlashAttention 的
@@ -74,13 +86,15 @@ typedef struct {
  *
  *   q, o : [B, A, S_q, d_h]        k, v : [B, A_kv, S_k, d_h]
  *   lse  : [B, A, S_q] fp32        mask : NULL or keep-masks as above
+ *   window : NULL or a sliding window as above
  *
  * Supported: bf16 with d_h in {64, 128}; fp32 with 1 <= d_h <= 128.
  * B, A, A_kv >= 1; S_q, S_k >= 0.
  */
 attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                      int B, int A, int A_kv, int S_q, int S_k, int d_h, float scale,
-                     int causal, const attn_mask *mask, attn_dtype dtype, void *stream);
+                     int causal, const attn_mask *mask, const attn_window *window,
+                     attn_dtype dtype, void *stream);
 
 /*
  * Packed variable-length prefill (page "Attention Kernel", section
@@ -93,13 +107,15 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
  *                     cu[n_seq] = T (= total_tokens); empty sequences allowed
  *   cu_seqlens_host : host copy of the same values (used for launch planning)
  *   mask            : NULL or q_keep [T], k_keep [T]
+ *   window          : NULL or a sliding window (positions within a sequence)
  *
  * Supported: as attn_fwd.
  */
 attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                             const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                             int n_seq, int total_tokens, int A, int A_kv, int d_h, float scale,
-                            int causal, const attn_mask *mask, attn_dtype dtype, void *stream);
+                            int causal, const attn_mask *mask, const attn_window *window,
+                            attn_dtype dtype, void *stream);
 
 /*
  * Single-query decode over a paged KV cache, split along the KV length and
@@ -150,6 +166,7 @@ size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int pa
  *               scale, causal and mask; rows with lse = -inf take no part
  *   o         : attn_fwd's output for the same call
  *   mask      : NULL or keep-masks [B, S_q] / [B, S_k], as given to attn_fwd
+ *   window    : NULL or the sliding window given to attn_fwd
  *   workspace : device buffer of at least attn_bwd_workspace_bytes(B, A, S_q)
  *               bytes, 256-byte aligned (two fp32 per query row: the base-2
  *               LSE and D_i); contents on entry are ignored
@@ -163,7 +180,8 @@ size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int pa
 attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                      const float *lse, void *dq, void *dk, void *dv, int B, int A, int A_kv, int S_q,
                      int S_k, int d_h, float scale, int causal, const attn_mask *mask,
-                     attn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+                     const attn_window *window, attn_dtype dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* Workspace bytes attn_bwd needs (0 on bad input). */
 size_t attn_bwd_workspace_bytes(int B, int A, int S_q);

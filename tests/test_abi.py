@@ -38,7 +38,7 @@ def test_library_exports_exactly_the_header():
 
 def test_status_strings_and_version():
     import exact_attention_108_amd as ea
-    assert ea.attn_abi_version() == 1
+    assert ea.attn_abi_version() == 2
     assert ea.attn_status_string(0) == "ok"
     assert ea.attn_status_string(1) == "invalid argument"
     assert ea.attn_status_string(2) == "unsupported configuration"
@@ -59,16 +59,16 @@ def _lib():
     import exact_attention_108_amd as ea
     lib = ctypes.CDLL(ea.LIB_PATH)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp]
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp]
     lib.attn_fwd.restype = i
-    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, i, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, i, vp,
                                       ctypes.c_size_t, vp]
     lib.attn_decode_paged.restype = i
     lib.attn_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, vp]
     lib.attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
-    lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, i, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, vp, i, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -80,10 +80,10 @@ P = ctypes.c_void_p(4096)  # never dereferenced: every call below is rejected (o
 
 def fwd(lib, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, A=4, A_kv=2, S_q=8, S_k=8, d=128, scale=0.1, causal=1, mask=None,
-             dt=1, stream=None)
+             window=None, dt=1, stream=None)
     a.update(kw)
     return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["A"], a["A_kv"], a["S_q"], a["S_k"],
-                        a["d"], a["scale"], a["causal"], a["mask"], a["dt"], a["stream"])
+                        a["d"], a["scale"], a["causal"], a["mask"], a["window"], a["dt"], a["stream"])
 
 
 def test_attn_fwd_rejects_bad_arguments():
@@ -104,6 +104,13 @@ def test_attn_fwd_rejects_bad_arguments():
     assert fwd(lib, d=96) == UNSUP                 # bf16 kernels: d in {64, 128}
     assert fwd(lib, d=200, dt=0) == UNSUP          # fp32: d <= 128
     assert fwd(lib, S_q=0, q=None, o=None, lse=None) == OK   # nothing to do, no launch
+    import ctypes as ct
+
+    class W(ct.Structure):
+        _fields_ = [("left", ct.c_int), ("right", ct.c_int)]
+    assert fwd(lib, window=ct.byref(W(-2, 0))) == INVAL     # window sides are >= -1
+    assert fwd(lib, window=ct.byref(W(3, -5))) == INVAL
+    assert fwd(lib, S_q=0, q=None, o=None, lse=None, window=ct.byref(W(3, -1))) == OK
     # the page's shape-mismatch example has no analogue here: sizes are explicit,
     # and the Python binding rejects tensors whose shapes disagree
     import pytest
@@ -119,7 +126,7 @@ def test_attn_fwd_varlen_rejects_bad_arguments():
     cu = np.array([0, 5, 3, 9], np.int32)  # decreasing
     cup = cu.ctypes.data_as(ctypes.c_void_p)
     args = lambda cu_host, n, T, **kw: lib.attn_fwd_varlen(P, P, P, P, P, P, cu_host, n, T, kw.get("A", 4), 2, 64,
-                                                           kw.get("scale", 0.1), 1, None, 1, None)
+                                                           kw.get("scale", 0.1), 1, None, None, 1, None)
     assert args(cup, 3, 9) == 1
     good = np.array([0, 5, 5, 9], np.int32)
     gp = good.ctypes.data_as(ctypes.c_void_p)
@@ -180,8 +187,8 @@ def test_attn_bwd_rejects_bad_arguments():
                  scale=0.1, causal=1, dt=1, ws=P, ws_bytes=1 << 20)
         a.update(kw)
         return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
-                            a["A"], a["A_kv"], a["S_q"], a["S_k"], a["d"], a["scale"], a["causal"], None, a["dt"],
-                            a["ws"], a["ws_bytes"], None)
+                            a["A"], a["A_kv"], a["S_q"], a["S_k"], a["d"], a["scale"], a["causal"], None,
+                            a.get("window"), a["dt"], a["ws"], a["ws_bytes"], None)
     assert bwd(A=3) == INVAL                       # A % A_kv
     assert bwd(B=0) == INVAL
     assert bwd(S_k=-1) == INVAL

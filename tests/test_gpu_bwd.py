@@ -168,3 +168,65 @@ def test_bwd_full_size_sampled(ea, orc, shape):
         ref = orc.attn_bwd(qs, ks, vs, dout[b:b + 1, hs], dtype="bf16", scale=p.scale, causal=True)
         got = (dq[b:b + 1, hs], dk[b:b + 1, hk:hk + 1], dv[b:b + 1, hk:hk + 1])
         _say("slice", (b, hk), compare(got, ref, f"{shape} slice {(b, hk)}"))
+
+
+def run_bwd_window(ea, p, dout, window, k_keep=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    do = gu.dev(dout, "bf16")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A, p.S_q), dtype=t.float32, device="cuda")
+    kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, k_keep=kk, window=window)
+    dq, dk, dv = (gu.empty_out(x.shape, "bf16") for x in (q, k, v))
+    for x in (dq, dk, dv):
+        x.fill_(float("nan"))
+    ws = t.empty(max(ea.attn_bwd_workspace_bytes(p.B, p.A, p.S_q), 1), dtype=t.uint8, device="cuda")
+    ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p.scale, causal=p.causal, k_keep=kk, window=window)
+    t.cuda.synchronize()
+    return gu.host_f64(dq), gu.host_f64(dk), gu.host_f64(dv)
+
+
+BWD_WINDOW_CASES = [
+    # B, A, A_kv, S_q, S_k, d, causal, (left, right)
+    (1, 2, 1, 300, 300, 128, True, (0, -1)),
+    (2, 4, 2, 500, 500, 128, True, (100, -1)),
+    (1, 2, 2, 300, 420, 128, True, (63, -1)),
+    (1, 2, 2, 420, 300, 128, True, (200, -1)),
+    (1, 2, 2, 400, 400, 128, False, (40, 90)),
+    (1, 4, 1, 350, 350, 64, True, (129, -1)),
+]
+
+
+@pytest.mark.parametrize("case", BWD_WINDOW_CASES,
+                         ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n") + f"w{c[7][0]}_{c[7][1]}")
+def test_bwd_window(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal, (left, right) = case
+    _say("bwd window", case)
+    seed = 800 + S_q + left
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=seed)
+    dout = gen.make_dout(p, seed)
+    got = run_bwd_window(ea, p, dout, (left, right))
+    mk = oracle.window_keep(B, S_q, S_k, left, 0 if causal else right)
+    ref = orc.attn_bwd(p.q, p.k, p.v, dout, dtype="bf16", scale=p.scale, causal=causal, m_keep=mk)
+    vis = visibility(B, S_q, S_k, causal) & (mk != 0)
+    if left == 0 and causal:
+        # every row sees one key: p = 1 and dS = dP - D = 0 exactly, so the
+        # exact dQ and dK vanish by cancellation.  The GPU's dS is the
+        # rounding difference of two fp32 sums (dP by MFMA, D from the bf16
+        # O = v): |dS_i| <= 2 u sum_e |dO_ie v_ie| with u = 2^-8 (bounding both
+        # sums' fp32 errors generously); dQ_i = scale dS_i k_i and
+        # dK_i = scale sum over the query heads of dS_i q_i
+        assert S_q == S_k and np.all(ref[0] == 0) and np.all(ref[1] == 0)
+        q_, k_, v_ = (gen.as_f32(x, "bf16").astype(np.float64) for x in (p.q, p.k, p.v))
+        do_ = gen.as_f32(dout, "bf16").astype(np.float64)
+        G = A // A_kv
+        kv, vv = np.repeat(k_, G, axis=1), np.repeat(v_, G, axis=1)
+        ds_bound = 2 * 2.0 ** -8 * np.abs(do_ * vv).sum(axis=-1, keepdims=True)   # [B, A, S, 1]
+        assert np.all(np.abs(got[0]) <= 1.01 * p.scale * ds_bound * np.abs(kv))
+        dk_bound = (p.scale * ds_bound * np.abs(q_)).reshape(B, A_kv, G, S_q, d).sum(axis=2)
+        assert np.all(np.abs(got[1]) <= 1.01 * dk_bound)
+        _say({"dv": gu.check_grad(got[2], ref[2], f"{case} dv"), "dq_max": float(np.abs(got[0]).max()),
+              "dk_max": float(np.abs(got[1]).max())})
+        return
+    _say(compare(got, ref, str(case), vis, A, A_kv))

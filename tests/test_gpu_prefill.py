@@ -194,3 +194,99 @@ def test_config5_full(ea, orc):
                                        q_keep=p.q_keep, rows=rows)
     stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "config5")
     _say("config 5", stats)
+
+
+# ---- sliding windows (page "Attention Kernel", section "可编程 mask"): the
+# oracle takes the window as a dense keep matrix built from its definition
+
+def run_dense_window(ea, p, window, k_keep=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, p.dtype), gu.dev(p.k, p.dtype), gu.dev(p.v, p.dtype)
+    o = gu.empty_out(q.shape, p.dtype)
+    lse = t.empty((p.B, p.A, p.S_q), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, k_keep=kk, window=window)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+WINDOW_CASES = [
+    # B, A, A_kv, S_q, S_k, d, causal, (left, right)
+    (1, 2, 1, 300, 300, 128, True, (0, -1)),       # each row sees only its own key
+    (1, 2, 2, 300, 300, 128, True, (37, -1)),      # window inside one tile
+    (2, 4, 2, 700, 700, 128, True, (255, -1)),     # several tiles, masked edges on both sides
+    (1, 4, 1, 513, 700, 128, True, (100, -1)),     # S_q < S_k (bottom-right alignment)
+    (1, 2, 2, 700, 400, 128, True, (64, -1)),      # S_q > S_k: leading rows see nothing
+    (1, 2, 2, 600, 600, 128, False, (50, 70)),     # two-sided, non-causal
+    (1, 2, 2, 600, 600, 128, False, (-1, 0)),      # right edge only = causal
+    (1, 2, 2, 600, 600, 128, False, (200, -1)),    # left edge only
+    (2, 4, 4, 400, 400, 64, True, (129, -1)),      # d = 64
+    (1, 2, 1, 300, 300, 128, True, (5000, -1)),    # window wider than the sequence = causal
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n")
+                         + f"w{c[7][0]}_{c[7][1]}")
+def test_window_bf16(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal, (left, right) = case
+    _say("window bf16", case)
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=700 + S_q + left)
+    o, lse = run_dense_window(ea, p, (left, right))
+    mk = oracle.window_keep(B, S_q, S_k, left, 0 if causal else right)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal, m_keep=mk)
+    gu.check(o, lse, o_ref, l_ref, "bf16", str(case))
+
+
+def test_window_key_mask_and_f32(ea, orc):
+    _say("window + key mask (bf16) and fp32 window")
+    p = gen.make_dense(2, 4, 2, 333, 333, 128, dtype="bf16", causal=True, seed=771, k_masked=50)
+    o, lse = run_dense_window(ea, p, (90, -1), k_keep=p.k_keep)
+    mk = oracle.window_keep(2, 333, 333, 90, 0)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True, k_keep=p.k_keep, m_keep=mk)
+    gu.check(o, lse, o_ref, l_ref, "bf16", "window + key mask")
+    p = gen.make_dense(1, 2, 1, 150, 170, 64, dtype="f32", causal=False, seed=772)
+    o, lse = run_dense_window(ea, p, (20, 9))
+    mk = oracle.window_keep(1, 150, 170, 20, 9)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="f32", scale=p.scale, m_keep=mk)
+    gu.check(o, lse, o_ref, l_ref, "f32", "fp32 window")
+
+
+def test_window_varlen(ea, orc):
+    lens = [1, 0, 130, 17, 400, 64, 300]
+    left = 70
+    _say("varlen window", lens, left)
+    p = gen.make_varlen(lens, 4, 2, 128, dtype="bf16", causal=True, seed=773)
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.A, p.T), dtype=t.float32, device="cuda")
+    cu = gu.dev(p.cu_seqlens, "i32")
+    ea.attn_fwd_varlen(q, k, v, o, lse, cu, p.cu_seqlens, scale=p.scale, causal=True, window=(left, -1))
+    t.cuda.synchronize()
+    o, lse = gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+    # a packed sequence is an independent dense problem (pinned for the oracle)
+    for s in range(len(lens)):
+        a, b = int(p.cu_seqlens[s]), int(p.cu_seqlens[s + 1])
+        if a == b:
+            continue
+        L = b - a
+        mk = oracle.window_keep(1, L, L, left, 0)
+        o_ref, l_ref = orc.attn_fwd(p.q[None, :, a:b], p.k[None, :, a:b], p.v[None, :, a:b], dtype="bf16",
+                                    scale=p.scale, causal=True, m_keep=mk)
+        gu.check(o[None, :, a:b], lse[None, :, a:b], o_ref, l_ref, "bf16", f"varlen window seq {s}")
+
+
+def test_window_full_size_sampled(ea, orc):
+    """The MHA workload's shape with a 512-key causal window, sampled rows."""
+    _say("window full size 4x32x2048x128, left 511")
+    p = gen.make_dense(4, 32, 32, 2048, 2048, 128, dtype="bf16", causal=True, seed=774)
+    o, lse = run_dense_window(ea, p, (511, -1))
+    rng = np.random.default_rng(774)
+    rows = _sample_rows(rng, p.B, p.A, p.S_q, 1000)
+    mk = oracle.window_keep(p.B, p.S_q, p.S_k, 511, 0)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True, m_keep=mk, rows=rows)
+    stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "window full size")
+    _say(stats)
+    assert np.all(np.isfinite(lse)) and np.all(np.isfinite(o))
