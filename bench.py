@@ -146,7 +146,7 @@ def load_inputs(log_fn=lambda *a: None):
                            stream=stream)
 
     return dict(p2=p2, p4=p4, p5=p5, kv_bytes=kv_bytes, ws_bytes=ws_bytes, stream=stream,
-                dev2=(q2, k2, v2, o2, l2),
+                dev2=(q2, k2, v2, o2, l2), dev4=(kc4, vc4, bt4, sl4),
                 parts=[("prefill", prefill), ("decode", decode), ("varlen", varlen)])
 
 
@@ -426,6 +426,7 @@ def main():
 
     out["backward"] = bench_backward(w, args.steps, args.warmup)
     out["window"] = bench_window(args.steps, args.warmup, stream)
+    out["paged_prefill"] = bench_paged_prefill(w, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
@@ -543,6 +544,57 @@ def bench_window(steps: int, warmup: int, stream) -> dict:
             "min_ms": round(float(ms.min()), 5), "flops": flops,
             "workload": f"GQA causal B={B} A={A} A_kv={A_kv} S={S} d={d} bf16, window: {left} keys before the "
                         "diagonal"}
+
+
+PAGED_CHUNK = 256
+
+
+def bench_paged_prefill(w, steps: int, warmup: int) -> dict:
+    """Chunked prefill over the paged decode cache: each of the 64 sequences
+    (A=32, A_kv=8, d=128, page 16, lengths ~U{512..32768}) gets its last 256
+    tokens as a new query chunk, all in one call.  FLOPs = 4 d A x (causal
+    (row, key) pairs): row i of a chunk of q rows over L keys sees L - q + i + 1."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p4, stream = w["p4"], w["stream"]
+    kc, vc, bt, sl = w["dev4"]
+    n = p4.B
+    q_lens = np.full(n, PAGED_CHUNK, np.int32)
+    cu = np.zeros(n + 1, np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    q = to_dev(gen.draw((p4.A, int(cu[-1]), p4.d), 1007, 0, "normal", "bf16"), "bf16")
+    cud = to_dev(cu, "i32")
+    o = torch.empty_like(q)
+    lse = torch.empty((p4.A, int(cu[-1])), dtype=torch.float32, device="cuda")
+
+    def run():
+        ea.attn_prefill_paged(q, kc, vc, bt, sl, p4.seq_lens, cud, cu, o, lse, scale=p4.scale, causal=True,
+                              stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    L = p4.seq_lens.astype(np.int64)
+    ql = q_lens.astype(np.int64)
+    pairs = int(np.sum(ql * (L - ql) + ql * (ql + 1) // 2))
+    flops = 4.0 * p4.d * p4.A * pairs
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    return {"metric": "paged chunked prefill TFLOP/s (causal pairs)", "value": round(tf, 2), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(float(ms.mean()), 5),
+            "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5), "flops": flops,
+            "workload": f"{n} sequences of the paged decode cache (A=32 A_kv=8 d=128 page 16, lengths "
+                        f"~U{{512..32768}}), each with its last {PAGED_CHUNK} tokens as the query chunk"}
 
 
 def measured_ceilings(stream) -> dict:

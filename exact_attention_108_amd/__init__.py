@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     attn_decode_paged_workspace_bytes,
     attn_fwd,
     attn_fwd_varlen,
+    attn_prefill_paged,
     attn_status_string,
     exported_symbols,
 )

@@ -48,6 +48,9 @@ _lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _
                           ctypes.POINTER(_Mask), _WP, _i, _vp, _sz, _vp]
 _lib.attn_bwd.restype = _i
 _lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
+_lib.attn_prefill_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                    _f, _i, _WP, _i, _vp]
+_lib.attn_prefill_paged.restype = _i
 _lib.attn_bwd_workspace_bytes.restype = _sz
 _lib.attn_status_string.argtypes = [_i]
 _lib.attn_status_string.restype = ctypes.c_char_p
@@ -72,7 +75,8 @@ def attn_abi_version() -> int:
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
-            "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version"]
+            "attn_bwd", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_status_string",
+            "attn_abi_version"]
 
 
 def _torch():
@@ -266,3 +270,35 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, caus
                        B, A, A_kv, S_q, S_k, d, float(scale), int(bool(causal)), _mask(q_keep, k_keep),
                        _window(window), _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_bwd")
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host,
+                       o, lse, *, scale: float, causal: bool = True, window=None, stream=None):
+    """Prefill of packed query chunks q/o [A,T_q,d] (lse [A,T_q]) over a paged cache [num_pages, page_size,
+    A_kv, d]; block_table int32 [n_seq, max_pages]; seq_lens int32 [n_seq] (device) with seq_lens_host; chunk
+    boundaries cu_seqlens_q int32 [n_seq+1] (device) with cu_seqlens_q_host."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
+    A, T_q, d = q.shape
+    num_pages, page_size, A_kv, dk = k_cache.shape
+    if dk != d or o.shape != q.shape or lse.shape != (A, T_q) or lse.dtype != torch.float32:
+        raise ValueError("shape mismatch")
+    if o.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("dtype mismatch")
+    cu_host = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
+    n_seq = cu_host.size - 1
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if sl.shape != (n_seq,) or seq_lens.dtype != torch.int32 or seq_lens.shape != (n_seq,):
+        raise ValueError("seq_lens must be int32 [n_seq]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_q.numel() != cu_host.size:
+        raise ValueError("cu_seqlens_q must be int32 [n_seq + 1]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != n_seq:
+        raise ValueError("block_table must be int32 [n_seq, max_pages]")
+    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse)
+    st = _lib.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                 sl.ctypes.data_as(_vp), _ptr(cu_seqlens_q), cu_host.ctypes.data_as(_vp), page_size,
+                                 _ptr(o), _ptr(lse), n_seq, T_q, A, A_kv, d, block_table.shape[1], num_pages,
+                                 float(scale), int(bool(causal)), _window(window), _dtype_code(q),
+                                 _stream(stream, dev))
+    _check(st, "attn_prefill_paged")

@@ -126,6 +126,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   p.B = 1;
   p.n_qt = max_tiles;
   p.total_tiles = (int)total_tiles;
+  if (dtype == ATTN_BF16) attn::plan_varlen_order(p);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, true, st) : attn::launch_prefill_f32(p, true, st);
   return launch_status(e);
@@ -198,6 +199,61 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return launch_status(attn::launch_decode_bf16(p, (hipStream_t)stream));
+}
+
+ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table, const int32_t* seq_lens,
+                                           const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_q_host, int page_size, void* o, float* lse,
+                                           int n_seq, int total_q, int A, int A_kv, int d_h, int max_pages,
+                                           int num_pages, float scale, int causal, const attn_window* window,
+                                           attn_dtype dtype, void* stream) {
+  if (n_seq < 0 || total_q < 0 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (page_size < 1 || max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (!cu_seqlens_q || !cu_seqlens_q_host || !seq_lens || (n_seq > 0 && !seq_lens_host)) return ATTN_ERR_INVAL;
+  if (cu_seqlens_q_host[0] != 0 || cu_seqlens_q_host[n_seq] != total_q) return ATTN_ERR_INVAL;
+  long long total_kv = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int q_len = cu_seqlens_q_host[s + 1] - cu_seqlens_q_host[s];
+    if (q_len < 0 || seq_lens_host[s] < q_len) return ATTN_ERR_INVAL;
+    if ((long long)seq_lens_host[s] > (long long)max_pages * page_size) return ATTN_ERR_INVAL;
+    total_kv += seq_lens_host[s];
+  }
+  if (total_q > 0 && (!q || !o || !lse)) return ATTN_ERR_INVAL;
+  if (total_kv > 0 && (!k_cache || !v_cache || !block_table || num_pages < 1)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
+  const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
+  if ((page_size & (page_size - 1)) != 0 || page_size % rows_per_part != 0) return ATTN_ERR_UNSUPPORTED;
+  if (total_q == 0) return ATTN_OK;
+  if ((long long)A * total_q > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  // the cache's byte offsets must fit the kernels' 32-bit buffer ranges per page row
+  if ((long long)page_size * A_kv * d_h * 2 > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  long long total_tiles = 0;
+  int max_tiles = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int len = cu_seqlens_q_host[s + 1] - cu_seqlens_q_host[s];
+    const int nt = (len + attn::kPrefillRows - 1) / attn::kPrefillRows;
+    total_tiles += nt;
+    if (nt > max_tiles) max_tiles = nt;
+  }
+  if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdParams p = base_params(q, k_cache, v_cache, o, lse, A, A_kv, d_h, scale, causal, nullptr, window);
+  p.cu_seqlens = cu_seqlens_q;
+  p.n_seq = n_seq;
+  p.T = total_q;
+  p.B = 1;
+  p.n_qt = max_tiles;
+  p.total_tiles = (int)total_tiles;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.max_pages = max_pages;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  p.page_shift = shift;
+  attn::plan_varlen_order(p);
+  return launch_status(attn::launch_prefill_paged_bf16(p, (hipStream_t)stream));
 }
 
 namespace {

@@ -102,6 +102,18 @@ __device__ __forceinline__ void lds_copy_wait_all() {
   asm volatile("" ::: "memory");
 }
 
+// Wave-uniform load of one int32 (base[idx], both uniform): the address is
+// made scalar and read through the constant address space, so the load is an
+// s_load_dword, counted by lgkmcnt.  A vector load would be counted by vmcnt,
+// and waiting for it would also wait for every asynchronous LDS copy in flight.
+__device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
+  const uint64_t a = (uint64_t)(uintptr_t)(base + idx);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  return *(const_i32_ptr)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ bf16x8 concat(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

@@ -26,12 +26,19 @@ struct FwdParams {
   int causal;
   float scale;                // softmax scale (> 0)
   float scale_log2;           // scale * log2(e)
-  int xcd_heads;              // dense: (batch, head) pairs per XCD block, 0 = plain order
+  int xcd_heads;              // dense: (batch, head) pairs per XCD block; varlen/paged: heads per XCD block; 0 = plain order
   int xcd_group;              // dense: heads whose query tiles are issued together
   // sliding window around query i's position i + off (off = S_k - S_q): key
   // j is kept when i + off - win_left <= j <= i + off + win_right; -1 leaves
   // a side unbounded.  The causal flag is folded into win_right (<= 0).
   int win_left, win_right;
+  // paged KV (prefill over a paged cache): k, v are the caches [num_pages,
+  // page_size, A_kv, d]; sequence s's token t lives in page
+  // block_table[s * max_pages + t / page_size]; seq_lens[s] = its KV length
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int page_shift;  // log2(page_size)
+  int max_pages;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin
@@ -57,8 +64,21 @@ inline void plan_dense_order(FwdParams& p) {
   p.xcd_group = g;
 }
 
+// Packed (varlen or paged) prefill grid order: heads dealt to the XCDs in
+// contiguous blocks of A/8 when those blocks hold whole GQA groups, so the
+// query heads of one KV head share an XCD's L2 (GQA only: measured 2% slower
+// without heads to share); otherwise plain order.
+inline void plan_varlen_order(FwdParams& p) {
+  p.xcd_heads = 0;
+  p.xcd_group = 0;
+  if (p.G > 1 && p.A % kXcds == 0 && (p.A / kXcds) % p.G == 0) p.xcd_heads = p.A / kXcds;
+}
+
 // bf16 prefill (d in {64, 128}).  Returns hipSuccess or the launch error.
 hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stream);
+// bf16 prefill of packed query chunks over a paged KV cache (d in {64, 128};
+// page_size a power of two and a multiple of 2048 / d).
+hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream);
 // fp32 prefill (1 <= d <= 128).
 hipError_t launch_prefill_f32(const FwdParams& p, bool varlen, hipStream_t stream);
 // query rows per workgroup of the bf16 prefill kernel

@@ -53,7 +53,7 @@ constexpr int kBc = 64;             // keys per tile
 constexpr int kThreads = 64 * kWaves;
 static_assert(kRows == kPrefillRows, "row tile");
 
-template <int D, bool kVarlen>
+template <int D, bool kVarlen, bool kPaged = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(FwdParams p) {
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ uint8_t sKeep[2][kBc];
 
   RowBlock rb;
-  if constexpr (kVarlen) {
+  if constexpr (kPaged) {
+    if (!setup_paged<kRows>(p, D * 2, rb)) return;
+  } else if constexpr (kVarlen) {
     if (!setup_varlen<kRows>(p, D * 2, rb)) return;
   } else {
     rb = setup_dense<kRows>(p, D * 2);
@@ -167,6 +169,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // part i (of LD_PER_T) of one tile of K (or V) into LDS byte offset `dst`
   auto copy_part = [&](const i32x4& rsrc, uint32_t dst, int i) {
     lds_copy16_buf(rsrc, coff[i], lds_base + dst + (uint32_t)(i * RPC * D * 2) + (uint32_t)wave_u * 1024u);
+  };
+  // Paged KV: part i of a tile is RPC consecutive tokens, which the page size
+  // (a power of two, a multiple of RPC) keeps inside one page.  Its resource
+  // starts at the part's first token row in that page (rows are A_kv * D
+  // elements apart) and covers only tokens < S_k, so the block table is never
+  // read past the sequence and absent rows arrive as zeros.
+  [[maybe_unused]] const uint32_t kv_stride = (uint32_t)(kPaged ? p.A_kv * D * 2 : D * 2);
+  [[maybe_unused]] const uint32_t poff = (uint32_t)rowc * kv_stride + (uint32_t)cc * 16;
+  [[maybe_unused]] auto part_rsrc = [&](const char* gbase, int t, int i) -> i32x4 {
+    const int row0 = phys(t) * kBc + i * RPC;
+    const int page = load_uniform_i32(rb.bt, min(row0, S_k - 1) >> p.page_shift);
+    const int in_page = row0 & ((1 << p.page_shift) - 1);
+    const int rows = min(max(S_k - row0, 0), RPC);
+    return make_buffer_rsrc(gbase + ((size_t)page << p.page_shift | (size_t)in_page) * kv_stride,
+                            (uint32_t)rows * kv_stride);
+  };
+  [[maybe_unused]] auto copy_part_paged = [&](const char* gbase, int t, uint32_t dst, int i) {
+    lds_copy16_buf(part_rsrc(gbase, t, i), poff,
+                   lds_base + dst + (uint32_t)(i * RPC * D * 2) + (uint32_t)wave_u * 1024u);
   };
   auto copy_keep = [&](int t) {
     if (rb.k_keep && tid < kBc && t < n_tiles) {
@@ -335,13 +356,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 s_cur[2];
   float mx_cur = -INFINITY;
   if (n_tiles > 0) {
-    const i32x4 rk0 = tile_rsrc(gk, 0), rv0 = tile_rsrc(gv, 0);
-    const i32x4 rk1 = tile_rsrc(gk, min(1, n_tiles - 1));
+    if constexpr (kPaged) {
+      const int t1 = min(1, n_tiles - 1);
 #pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) {
-      copy_part(rk0, 0, i);
-      copy_part(rv0, 2 * TILE_BYTES, i);
-      copy_part(rk1, TILE_BYTES, i);
+      for (int i = 0; i < LD_PER_T; ++i) {
+        copy_part_paged(rb.k, 0, 0, i);
+        copy_part_paged(rb.v, 0, 2 * TILE_BYTES, i);
+        copy_part_paged(rb.k, t1, TILE_BYTES, i);
+      }
+    } else {
+      const i32x4 rk0 = tile_rsrc(gk, 0), rv0 = tile_rsrc(gv, 0);
+      const i32x4 rk1 = tile_rsrc(gk, min(1, n_tiles - 1));
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        copy_part(rk0, 0, i);
+        copy_part(rv0, 2 * TILE_BYTES, i);
+        copy_part(rk1, TILE_BYTES, i);
+      }
     }
     copy_keep(0);
     copy_keep(1);
@@ -371,15 +402,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // buffer BUF^1), issued in parts at four points of the iteration.  Past
     // the last tile they re-copy the last tile into an idle buffer (harmless,
     // and it keeps the body free of branches).
-    const i32x4 rk = tile_rsrc(gk, min(j + 2, n_tiles - 1));
-    const i32x4 rv = tile_rsrc(gv, min(j + 1, n_tiles - 1));
+    const int tk = min(j + 2, n_tiles - 1), tv = min(j + 1, n_tiles - 1);
+    [[maybe_unused]] i32x4 rk, rv;
+    if constexpr (!kPaged) {
+      rk = tile_rsrc(gk, tk);
+      rv = tile_rsrc(gv, tv);
+    }
     if constexpr (MASKED) copy_keep(j + 2);
     auto issue = [&](int at) {
 #pragma unroll
       for (int i = 0; i < LD_PER_T; ++i) {
         if (i * 4 / LD_PER_T == at) {
-          copy_part(rk, BUF * TILE_BYTES, i);
-          copy_part(rv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
+          if constexpr (kPaged) {
+            copy_part_paged(rb.k, tk, BUF * TILE_BYTES, i);
+            copy_part_paged(rb.v, tv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
+          } else {
+            copy_part(rk, BUF * TILE_BYTES, i);
+            copy_part(rv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
+          }
         }
       }
     };
@@ -486,6 +526,19 @@ hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stre
   if (p.d == 128) return launch_d<128>(p, varlen, stream);
   if (p.d == 64) return launch_d<64>(p, varlen, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream) {
+  const int grid = p.total_tiles * p.A;
+  if (grid <= 0) return hipSuccess;
+  if (p.d == 128) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (p.d == 64) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace attn

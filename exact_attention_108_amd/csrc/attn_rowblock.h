@@ -7,8 +7,9 @@ namespace attn {
 
 struct RowBlock {
   const char* q;   // row 0 of this (sequence, head); rows are d elements apart
-  const char* k;   // key 0 of the KV head
+  const char* k;   // key 0 of the KV head (paged: the head's offset in a cache row)
   const char* v;
+  const int32_t* bt;  // paged: this sequence's block-table row
   char* o;
   float* lse;
   const uint8_t* q_keep;  // or null
@@ -64,9 +65,13 @@ __device__ __forceinline__ int wave_sum(int x) {
 // sequences (tile t of any sequence sees about t+1 key tiles when causal),
 // then sequence, then head.  C(t) = A * sum_s max(0, n_s - t) counts the
 // workgroups whose tile index is >= t; a binary search finds this workgroup's
-// tile index, a ballot finds its sequence.
+// tile index, a ballot finds its sequence.  With xcd_heads > 0 the heads are
+// dealt to the XCDs in contiguous blocks of xcd_heads (whole GQA groups), so
+// the query heads that read one KV head run on one XCD, next to each other,
+// and share its L2.
 template <int kRows>
-__device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, RowBlock& r) {
+__device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, RowBlock& r, int* seq_out = nullptr,
+                                             int* head_out = nullptr) {
   const int lin = blockIdx.x;
   const int lane = threadIdx.x & 63;
   auto ntiles = [&](int s) -> int {
@@ -78,8 +83,15 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
     for (int s = lane; s < p.n_seq; s += 64) c += max(0, ntiles(s) - t);
     return wave_sum(c);
   };
-  const int per_head = lin / p.A;  // rank among tiles, heaviest first
-  const int h = lin % p.A;
+  int per_head, h;  // rank among tiles (heaviest first), head
+  if (p.xcd_heads > 0) {
+    const int x = lin % kXcds, i = lin / kXcds;
+    per_head = i / p.xcd_heads;
+    h = x * p.xcd_heads + i % p.xcd_heads;
+  } else {
+    per_head = lin / p.A;
+    h = lin % p.A;
+  }
   // largest t with count_ge(t) > per_head
   int lo = 0, hi = p.n_qt;  // count_ge(lo) > per_head, count_ge(hi) == 0
   while (hi - lo > 1) {
@@ -121,6 +133,25 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
   r.S_q = len;
   r.S_k = len;
   r.q0 = t_u * kRows;
+  if (seq_out) *seq_out = seq;
+  if (head_out) *head_out = h;
+  return true;
+}
+
+// Packed query chunks over a paged KV cache: the query side is the varlen
+// one (cu_seqlens over the chunks); sequence s's keys are its seq_lens[s]
+// cached tokens, the chunk being the last of them (bottom-right alignment).
+template <int kRows>
+__device__ __forceinline__ bool setup_paged(const FwdParams& p, int row_bytes, RowBlock& r) {
+  int seq = 0, h = 0;
+  if (!setup_varlen<kRows>(p, row_bytes, r, &seq, &h)) return false;
+  const int hk = h / p.G;
+  r.k = (const char*)p.k + (size_t)hk * row_bytes;
+  r.v = (const char*)p.v + (size_t)hk * row_bytes;
+  r.bt = p.block_table + (size_t)seq * p.max_pages;
+  r.S_k = p.seq_lens[seq];
+  r.q_keep = nullptr;
+  r.k_keep = nullptr;
   return true;
 }
 

@@ -151,6 +151,41 @@ size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int pa
                                          const int32_t *seq_lens_host);
 
 /*
+ * Prefill of new query chunks over a paged KV cache, as one batched call
+ * (page "Attention 算子加速史", section 4.2: paged KV addressed through the
+ * block table inside the kernel, and one scheduling abstraction for a batch
+ * that mixes prefill chunks with decode rows; page "Attention Kernel",
+ * section "Paged 与 ragged KV").
+ *
+ *   q, o        : [A, T_q, d_h] packed chunks; lse : [A, T_q] fp32
+ *   cu_seqlens_q: device int32 [n_seq + 1], chunk s = rows [cu[s], cu[s+1]);
+ *                 cu_seqlens_q_host: host copy (launch planning)
+ *   k_cache,
+ *   v_cache     : [num_pages, page_size, A_kv, d_h], already holding every
+ *                 sequence's tokens including its chunk
+ *   block_table : device int32 [n_seq, max_pages]; token t of sequence s is in
+ *                 page block_table[s][t / page_size] at offset t % page_size;
+ *                 entries past ceil(seq_lens[s] / page_size) are never read
+ *   seq_lens    : device int32 [n_seq] (KV length of each sequence, chunk
+ *                 included); seq_lens_host: host copy (validation)
+ *
+ * Chunk s holds the last q_s = cu[s+1] - cu[s] tokens of its sequence: row i
+ * of the chunk sits at position seq_lens[s] - q_s + i (the bottom-right
+ * alignment of attn_fwd).  causal and window apply to these positions.  A
+ * decode step is a chunk of length 1, so prefill chunks and decode rows can
+ * share one call.  Requires q_s <= seq_lens[s] <= max_pages * page_size.
+ * Supported: bf16, d_h in {64, 128}, page_size a power of two and a multiple
+ * of 16 (d_h = 128) or 32 (d_h = 64).
+ */
+attn_status attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               const int32_t *seq_lens_host, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_q_host, int page_size, void *o, float *lse,
+                               int n_seq, int total_q, int A, int A_kv, int d_h, int max_pages,
+                               int num_pages, float scale, int causal, const attn_window *window,
+                               attn_dtype dtype, void *stream);
+
+/*
  * Backward of attn_fwd (dense batch): dQ, dK, dV of O = softmax(Q K^T *
  * scale + M) V for an incoming dO, with the probabilities recomputed tile by
  * tile from Q, K and the forward's LSE instead of being stored (page

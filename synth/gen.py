@@ -286,6 +286,27 @@ def make_paged(lens, A, A_kv, d, page_size, *, dtype="bf16", seed=0, scale=None,
     return Paged(B, A, A_kv, d, page_size, dtype, scale, lens, bt, q, kc, vc, pool)
 
 
+def make_paged_prefill(lens, q_lens, A, A_kv, d, page_size, *, dtype="bf16", seed=0, extra_pages=0):
+    """Query chunks over a paged cache: the cache, block table and lengths of
+    make_paged (``lens`` = KV length per sequence, chunk included) plus packed
+    chunk queries q [A, sum(q_lens), d] and cu_seqlens_q [n_seq + 1]."""
+    pg = make_paged(lens, A, A_kv, d, page_size, dtype=dtype, seed=seed, extra_pages=extra_pages)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    cu = np.zeros(q_lens.size + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    q = draw((A, int(cu[-1]), d), seed, S_DOUT + 1, "normal", dtype)
+    return pg, q, cu
+
+
+def gather_paged(cache: np.ndarray, block_table: np.ndarray, b: int, length: int) -> np.ndarray:
+    """Tokens 0..length-1 of sequence b as a contiguous [A_kv, length, d] array
+    (token t in page block_table[b, t // page_size] at offset t % page_size)."""
+    ps = cache.shape[1]
+    t = np.arange(length)
+    rows = cache[block_table[b, t // ps], t % ps]       # [length, A_kv, d]
+    return np.ascontiguousarray(rows.transpose(1, 0, 2))
+
+
 # --- the five named workloads -------------------------------------------------
 
 CONFIG_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}

@@ -20,7 +20,7 @@ def header_functions():
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd",
-                                         "attn_bwd_workspace_bytes", "attn_status_string",
+                                         "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_status_string",
                                          "attn_abi_version"])
 
 
@@ -204,3 +204,27 @@ def test_attn_bwd_rejects_bad_arguments():
     assert lib.attn_bwd_workspace_bytes(2, 8, 100) == 12800
     assert lib.attn_bwd_workspace_bytes(1, 1, 1) == 256
     assert lib.attn_bwd_workspace_bytes(0, 8, 100) == 0
+
+
+def test_attn_prefill_paged_rejects_bad_arguments():
+    lib = _lib()
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_prefill_paged.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 7 + [f, i, vp, i, vp]
+    lib.attn_prefill_paged.restype = i
+    INVAL, UNSUP, OK = 1, 2, 0
+    cu = np.array([0, 5, 6], np.int32)
+    lens = np.array([40, 9], np.int32)
+
+    def call(cu=cu, lens=lens, ps=16, T=6, A=8, A_kv=2, d=128, mp=3, np_=6, dt=1):
+        return lib.attn_prefill_paged(P, P, P, P, P, lens.ctypes.data_as(vp), P, cu.ctypes.data_as(vp), ps, P, P,
+                                      cu.size - 1, T, A, A_kv, d, mp, np_, 0.1, 1, None, dt, None)
+    assert call(T=7) == INVAL                                    # cu[n_seq] != total
+    assert call(lens=np.array([4, 9], np.int32)) == INVAL        # chunk longer than the sequence
+    assert call(mp=2) == INVAL                                   # 40 tokens need 3 pages of 16
+    assert call(A=6, A_kv=4) == INVAL
+    assert call(ps=24, mp=2) == UNSUP                            # not a power of two
+    assert call(ps=16, d=64) == UNSUP                            # d = 64 needs pages of 32 tokens
+    assert call(d=96) == UNSUP
+    assert call(dt=0) == UNSUP
+    zero = np.array([0, 0, 0], np.int32)
+    assert call(cu=zero, T=0) == OK                              # no query rows: nothing to launch

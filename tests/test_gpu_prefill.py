@@ -290,3 +290,95 @@ def test_window_full_size_sampled(ea, orc):
     stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "window full size")
     _say(stats)
     assert np.all(np.isfinite(lse)) and np.all(np.isfinite(o))
+
+
+# ---- prefill of query chunks over a paged KV cache, mixing prefill chunks
+# and single-row decode steps in one call (the reference gathers each
+# sequence's tokens through the block table and runs the dense oracle with the
+# bottom-right causal alignment)
+
+def run_paged_prefill(ea, pg, q, cu, window=None, causal=True):
+    t = gu.torch()
+    qd = gu.dev(q, pg.dtype)
+    kc, vc = gu.dev(pg.k_cache, pg.dtype), gu.dev(pg.v_cache, pg.dtype)
+    bt, sl, cud = gu.dev(pg.block_table, "i32"), gu.dev(pg.seq_lens, "i32"), gu.dev(cu, "i32")
+    o = gu.empty_out(qd.shape, pg.dtype)
+    lse = t.empty((qd.shape[0], qd.shape[1]), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    ea.attn_prefill_paged(qd, kc, vc, bt, sl, pg.seq_lens, cud, cu, o, lse, scale=pg.scale, causal=causal,
+                          window=window)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def check_paged_prefill(orc, pg, q, cu, o, lse, what, window=None, causal=True):
+    for s in range(cu.size - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            continue
+        L = int(pg.seq_lens[s])
+        k = gen.gather_paged(pg.k_cache, pg.block_table, s, L)[None]
+        v = gen.gather_paged(pg.v_cache, pg.block_table, s, L)[None]
+        mk = None if window is None else oracle.window_keep(1, b - a, L, window[0], 0 if causal else window[1])
+        o_ref, l_ref = orc.attn_fwd(q[None, :, a:b], k, v, dtype=pg.dtype, scale=pg.scale, causal=causal,
+                                    m_keep=mk)
+        gu.check(o[None, :, a:b], lse[None, :, a:b], o_ref, l_ref, pg.dtype, f"{what} seq {s}")
+
+
+@pytest.mark.parametrize("d,ps", [(128, 16), (128, 64), (64, 32)])
+def test_paged_prefill_mixed(ea, orc, d, ps):
+    lens = [300, 1, 129, 700, 64, 5, 1000, 17]       # KV length per sequence (chunk included)
+    q_lens = [300, 1, 1, 200, 64, 5, 129, 0]         # full prefill, decode rows, chunks, an empty chunk
+    _say("paged prefill", d, ps, lens, q_lens)
+    pg, q, cu = gen.make_paged_prefill(lens, q_lens, 8, 2, d, ps, seed=900 + d + ps, extra_pages=3)
+    o, lse = run_paged_prefill(ea, pg, q, cu)
+    check_paged_prefill(orc, pg, q, cu, o, lse, f"paged d={d} ps={ps}")
+
+
+def test_paged_prefill_window_and_noncausal(ea, orc):
+    lens = [400, 260, 33]
+    q_lens = [150, 260, 3]
+    _say("paged prefill window / non-causal", lens, q_lens)
+    pg, q, cu = gen.make_paged_prefill(lens, q_lens, 4, 4, 128, 16, seed=931)
+    o, lse = run_paged_prefill(ea, pg, q, cu, window=(77, -1))
+    check_paged_prefill(orc, pg, q, cu, o, lse, "paged window", window=(77, -1))
+    o, lse = run_paged_prefill(ea, pg, q, cu, causal=False)
+    check_paged_prefill(orc, pg, q, cu, o, lse, "paged non-causal", causal=False)
+
+
+def test_paged_prefill_equals_varlen_bitwise(ea):
+    """With identity pages and the whole sequence as the chunk, the paged call
+    computes exactly the packed varlen prefill (same tiles, same order)."""
+    t = gu.torch()
+    lens = [256, 77, 513]
+    _say("paged == varlen", lens)
+    pv = gen.make_varlen(lens, 4, 2, 128, dtype="bf16", causal=True, seed=932)
+    ps = 16
+    npg = [(L + ps - 1) // ps for L in lens]
+    pool = sum(npg)
+    kc = np.zeros((pool, ps, 2, 128), np.uint16)
+    vc = np.zeros_like(kc)
+    bt = np.full((len(lens), max(npg)), -1, np.int32)
+    page = 0
+    for s, L in enumerate(lens):
+        a = int(pv.cu_seqlens[s])
+        for j in range(npg[s]):
+            n = min(ps, L - j * ps)
+            kc[page, :n] = pv.k[:, a + j * ps: a + j * ps + n].transpose(1, 0, 2)
+            vc[page, :n] = pv.v[:, a + j * ps: a + j * ps + n].transpose(1, 0, 2)
+            bt[s, j] = page
+            page += 1
+    qd = gu.dev(pv.q, "bf16")
+    o1 = gu.empty_out(qd.shape, "bf16")
+    l1 = t.empty((4, pv.T), dtype=t.float32, device="cuda")
+    cu = gu.dev(pv.cu_seqlens, "i32")
+    ea.attn_fwd_varlen(qd, gu.dev(pv.k, "bf16"), gu.dev(pv.v, "bf16"), o1, l1, cu, pv.cu_seqlens, scale=pv.scale,
+                       causal=True)
+    o2 = gu.empty_out(qd.shape, "bf16")
+    l2 = t.empty((4, pv.T), dtype=t.float32, device="cuda")
+    sl = np.array(lens, np.int32)
+    ea.attn_prefill_paged(qd, gu.dev(kc, "bf16"), gu.dev(vc, "bf16"), gu.dev(bt, "i32"), gu.dev(sl, "i32"), sl,
+                          cu, pv.cu_seqlens, o2, l2, scale=pv.scale, causal=True)
+    t.cuda.synchronize()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
