@@ -164,6 +164,32 @@ class Oracle:
             raise ValueError("oracle_attn_bwd rejected its arguments")
         return dq, dk, dv
 
+    def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
+                         seqs=None):
+        """Paged decode over FP8 caches (E4M3 codes [P, page_size, A_kv, d] with
+        per-(page, KV head) scales [P, A_kv]); q bf16 bits [B, A, d].  The cache
+        values code value * scale are formed in fp64 for the pages each sequence
+        uses, and the sequence runs through decode_paged.  Returns (o [n, A, d],
+        lse [n, A]) for the sequences ``seqs`` (default: all)."""
+        B, A, d = q.shape
+        bt = np.asarray(block_table)
+        sl = np.asarray(seq_lens)
+        ps = k_codes.shape[1]
+        seqs = range(B) if seqs is None else list(seqs)
+        qb = self._arr(q, "bf16").astype(np.uint32) << np.uint32(16)   # bf16 bits -> fp32 bits
+        qf = qb.view(np.float32).astype(np.float64)
+        outs, lses = [], []
+        for b in seqs:
+            n = int((int(sl[b]) + ps - 1) // ps)
+            pages = bt[b, :max(n, 1)].astype(np.int64) if n else np.zeros(1, np.int64)
+            kc = fp8_e4m3_value(k_codes[pages]) * np.asarray(k_scale, np.float64)[pages][:, None, :, None]
+            vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale, np.float64)[pages][:, None, :, None]
+            o, lse = self.decode_paged(qf[b:b + 1], kc, vc, np.arange(pages.size, dtype=np.int32)[None],
+                                       np.array([sl[b]], np.int32), dtype="f64", scale=scale)
+            outs.append(o.reshape(A, d))
+            lses.append(lse.reshape(A))
+        return np.stack(outs), np.stack(lses)
+
     def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None):
         """Paged decode.  q [B,A,d]; caches [P, page_size, A_kv, d]; rows = b*A + h."""
         q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
@@ -192,6 +218,17 @@ class Oracle:
 
 
 _default = None
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8) in fp64: sign bit 7, exponent bits
+    6..3 with bias 7, mantissa bits 2..0; exponent 0 is subnormal
+    (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN; there is no infinity."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
 
 
 def window_keep(B: int, S_q: int, S_k: int, left: int, right: int) -> np.ndarray:

@@ -307,6 +307,69 @@ def gather_paged(cache: np.ndarray, block_table: np.ndarray, b: int, length: int
     return np.ascontiguousarray(rows.transpose(1, 0, 2))
 
 
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the E4M3 codes 0x00..0x7E (sign bit clear, NaN excluded), by
+    the OCP FP8 definition: bias 7, 3 mantissa bits, subnormals at exponent 0."""
+    c = np.arange(0x7F)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def quantize_e4m3(y: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 code (ties to the even code), saturating at
+    448; returns uint8 codes.  Used only to build FP8 test caches."""
+    tab = _e4m3_positive_values()
+    a = np.minimum(np.abs(np.asarray(y, dtype=np.float64)), tab[-1])
+    hi = np.clip(np.searchsorted(tab, a), 1, tab.size - 1)
+    lo = hi - 1
+    dl, dh = a - tab[lo], tab[hi] - a
+    pick_hi = (dh < dl) | ((dh == dl) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(y) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+@dataclass
+class PagedFp8:
+    """Paged decode over FP8 caches: ``base`` holds q, block table and lengths
+    (its bf16 caches are not used); k/v_codes uint8 [num_pages, page_size,
+    A_kv, d]; k/v_scale fp32 [num_pages, A_kv]."""
+    base: Paged
+    k_codes: np.ndarray
+    v_codes: np.ndarray
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+
+
+def make_paged_fp8(lens, A, A_kv, d, page_size, *, seed=0, extra_pages=0) -> PagedFp8:
+    """FP8 caches quantised per (page, KV head): N(0, 1) values drawn in fp32,
+    scale = max |x| / 448 over the page's tokens and dims, codes =
+    round-to-nearest-even of x / scale."""
+    lens = np.asarray(lens, dtype=np.int32)
+    npg = (lens.astype(np.int64) + page_size - 1) // page_size
+    pool = int(npg.sum()) + int(extra_pages)
+    # block table, q and lengths exactly as make_paged draws them (caches drawn below in fp32)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, S_PERM])))
+    perm = rng.permutation(pool).astype(np.int32)
+    max_pages = max(1, int(npg.max()) if lens.size else 1)
+    bt = np.full((lens.size, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(lens.size):
+        n = int(npg[b])
+        bt[b, :n] = perm[off: off + n]
+        off += n
+    q = draw((lens.size, A, d), seed, S_Q, "normal", "bf16")
+    base = Paged(lens.size, A, A_kv, d, page_size, "bf16", float(np.float32(1.0 / math.sqrt(d))), lens, bt, q,
+                 np.zeros((0,), np.uint16), np.zeros((0,), np.uint16), pool)
+    out = []
+    for stream in (S_K, S_V):
+        x = draw((pool, page_size, A_kv, d), seed, stream, "normal", "f32")
+        amax = np.abs(x).max(axis=(1, 3))                              # [pool, A_kv]
+        sc = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+        codes = quantize_e4m3(x / sc[:, None, :, None])
+        out += [codes, sc]
+    return PagedFp8(base, out[0], out[2], out[1], out[3])
+
+
 # --- the five named workloads -------------------------------------------------
 
 CONFIG_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}

@@ -478,6 +478,54 @@ def pin_window_equals_key_slice(orc):
             assert np.array_equal(lse[0, :, i], ls[0, :, 0]), (S_q, S_k, left, right, i)
 
 
+# ---- FP8 (OCP E4M3) caches: code values, and decode over dequantised pages
+
+def pin_fp8_e4m3_published_values(orc):
+    """Values the OCP FP8 specification lists for E4M3: zero, the smallest
+    subnormal 2^-9, the largest subnormal 7 * 2^-9, the smallest normal 2^-6,
+    one, the largest finite 448, negative zero, and NaN at S.1111.111."""
+    import oracle as oracle_pkg
+    v = oracle_pkg.fp8_e4m3_value
+    assert v(0x00) == 0.0 and v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9 and v(0x08) == 2.0 ** -6
+    assert v(0x38) == 1.0 and v(0x7E) == 448.0 and v(0xFE) == -448.0
+    assert v(0x80) == 0.0 and np.signbit(v(0x80))
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+    vals = v(np.arange(0x7F))
+    assert np.all(np.diff(vals) > 0)                         # codes 0..126 increase strictly
+    assert np.array_equal(v(np.arange(0x80, 0xFF)), -vals)   # the sign bit only negates
+
+
+def pin_fp8_decode_brute_force(orc):
+    """Tiny FP8 paged decode against math.fsum over K = code value * k_scale and
+    V = code value * v_scale, scales per (page, KV head)."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(51)
+    ps, A, A_kv, d = 4, 4, 2, 3
+    lens = np.array([6, 1, 0], np.int32)
+    bt = np.array([[2, 0], [1, -1], [-1, -1]], np.int32)
+    kc = rng.integers(0, 0x7F, size=(3, ps, A_kv, d)).astype(np.uint8) | (rng.integers(0, 2, size=(3, ps, A_kv, d)) * 0x80).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, size=(3, ps, A_kv, d)).astype(np.uint8)
+    ksc = rng.uniform(0.001, 0.01, size=(3, A_kv)).astype(np.float32)
+    vsc = rng.uniform(0.001, 0.01, size=(3, A_kv)).astype(np.float32)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((3, A, d)).astype(np.float32))
+    o, lse = orc.decode_paged_fp8(q, kc, vc, ksc, vsc, bt, lens, scale=0.75)
+    qv = gen.bf16_bits_to_f32(q).astype(np.float64)
+    G = A // A_kv
+    for b in range(3):
+        for h in range(A):
+            hk = h // G
+            keys, vals = [], []
+            for t in range(int(lens[b])):
+                pg, off = int(bt[b, t // ps]), t % ps
+                keys.append([float(x) * float(ksc[pg, hk]) for x in oracle_pkg.fp8_e4m3_value(kc[pg, off, hk])])
+                vals.append([float(x) * float(vsc[pg, hk]) for x in oracle_pkg.fp8_e4m3_value(vc[pg, off, hk])])
+            want, wl = _brute([float(x) for x in qv[b, h]], keys, vals, 0.75, [True] * len(keys))
+            if not keys:
+                want = [0.0] * d
+            assert np.allclose(o[b, h], want, rtol=0, atol=1e-13), (b, h)
+            assert (wl == -math.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - wl) < 1e-13
+
+
 # ---- gradient (oracle_attn_bwd): the exact derivative of the forward above.
 # Pinned against central finite differences of the (already pinned) forward
 # in fp64, closed forms and invariants of the softmax Jacobian.
