@@ -427,6 +427,7 @@ def main():
     out["backward"] = bench_backward(w, args.steps, args.warmup)
     out["window"] = bench_window(args.steps, args.warmup, stream)
     out["paged_prefill"] = bench_paged_prefill(w, args.steps, args.warmup)
+    out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
@@ -544,6 +545,58 @@ def bench_window(steps: int, warmup: int, stream) -> dict:
             "min_ms": round(float(ms.min()), 5), "flops": flops,
             "workload": f"GQA causal B={B} A={A} A_kv={A_kv} S={S} d={d} bf16, window: {left} keys before the "
                         "diagonal"}
+
+
+def bench_decode_fp8(w, steps: int, warmup: int, bf16_ms: float) -> dict:
+    """The paged decode workload (same lengths, block table and q) over FP8
+    (E4M3) caches with per-(page, KV head) fp32 scales.  Algorithmic bytes:
+    each valid token's K and V row of every KV head once (1 byte per element)
+    plus the scales of the pages in use."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p4, stream = w["p4"], w["stream"]
+    t0 = time.time()
+    pf = gen.make_paged_fp8(p4.seq_lens, p4.A, p4.A_kv, p4.d, p4.page_size, seed=1008)
+    log(f"fp8 decode inputs ready ({time.time() - t0:.1f}s)")
+    p = pf.base
+    q = to_dev(p.q, "bf16")
+    kc, vc = torch.from_numpy(pf.k_codes).cuda(), torch.from_numpy(pf.v_codes).cuda()
+    ks, vs = torch.from_numpy(pf.k_scale).cuda(), torch.from_numpy(pf.v_scale).cuda()
+    bt, sl = to_dev(p.block_table, "i32"), to_dev(p.seq_lens, "i32")
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.A), dtype=torch.float32, device="cuda")
+    nbytes = ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def run():
+        ea.attn_decode_paged_fp8(q, kc, vc, ks, vs, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale, stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    tokens = int(np.sum(p.seq_lens, dtype=np.int64))
+    pages = int(np.sum((p.seq_lens.astype(np.int64) + p.page_size - 1) // p.page_size))
+    kv_bytes = 2.0 * p.A_kv * p.d * tokens + 2.0 * 4 * p.A_kv * pages
+    gbs = kv_bytes / (ms.mean() * 1e-3) / 1e9
+    return {"metric": "paged-decode FP8 KV GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBPS, 4)},
+            "avg_ms": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
+            "min_ms": round(float(ms.min()), 5), "kv_bytes": kv_bytes, "total_tokens": tokens,
+            "speedup_vs_bf16_cache": round(bf16_ms / float(ms.mean()), 3),
+            "workload": "the paged decode workload (64 seqs, A=32 A_kv=8 d=128, page 16) with E4M3 caches "
+                        "quantised per (page, KV head)"}
 
 
 PAGED_CHUNK = 256

@@ -52,6 +52,9 @@ _lib.attn_prefill_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, 
                                     _f, _i, _WP, _i, _vp]
 _lib.attn_prefill_paged.restype = _i
 _lib.attn_bwd_workspace_bytes.restype = _sz
+_lib.attn_decode_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                       _f, _vp, _sz, _vp]
+_lib.attn_decode_paged_fp8.restype = _i
 _lib.attn_status_string.argtypes = [_i]
 _lib.attn_status_string.restype = ctypes.c_char_p
 _lib.attn_abi_version.argtypes = []
@@ -75,8 +78,8 @@ def attn_abi_version() -> int:
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
-            "attn_bwd", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_status_string",
-            "attn_abi_version"]
+            "attn_bwd", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
+            "attn_status_string", "attn_abi_version"]
 
 
 def _torch():
@@ -302,3 +305,37 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host
                                  float(scale), int(bool(causal)), _window(window), _dtype_code(q),
                                  _stream(stream, dev))
     _check(st, "attn_prefill_paged")
+
+
+def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse,
+                          workspace, *, scale: float, stream=None):
+    """Paged decode over FP8 (E4M3) caches: q/o bf16 [B,A,d]; caches uint8 [num_pages, page_size, A_kv, d];
+    k_scale/v_scale fp32 [num_pages, A_kv]; the rest as attn_decode_paged."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
+    B, A, d = q.shape
+    num_pages, page_size, A_kv, dk = k_cache.shape
+    if dk != d or o.shape != q.shape or lse.shape != (B, A) or lse.dtype != torch.float32:
+        raise ValueError("shape mismatch")
+    if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
+        raise ValueError("q and o must be bf16")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches are passed as uint8 tensors of E4M3 bytes")
+    for sc in (k_scale, v_scale):
+        if sc.dtype != torch.float32 or sc.shape != (num_pages, A_kv):
+            raise ValueError("scales must be fp32 [num_pages, A_kv]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if sl.shape != (B,):
+        raise ValueError("seq_lens_host must be [B]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse, workspace)
+    st = _lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp), page_size, _ptr(o),
+                                    _ptr(lse), B, A, A_kv, d, block_table.shape[1], num_pages, float(scale),
+                                    _ptr(workspace), ws_bytes, _stream(stream, dev))
+    _check(st, "attn_decode_paged_fp8")

@@ -320,6 +320,52 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
 }
 
+ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                              const float* k_scale, const float* v_scale,
+                                              const int32_t* block_table, const int32_t* seq_lens,
+                                              const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                              int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
+  attn_status st = check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, max_pages, true);
+  if (st != ATTN_OK) return st;
+  if (!valid_scale(scale)) return ATTN_ERR_INVAL;
+  if (!q || !o || !lse || !seq_lens) return ATTN_ERR_INVAL;
+  long long total_tokens = 0;
+  for (int b = 0; b < B; ++b) total_tokens += seq_lens_host[b];
+  if (total_tokens > 0 && (!k_cache || !v_cache || !k_scale || !v_scale || !block_table || num_pages < 1))
+    return ATTN_ERR_INVAL;
+  if (((uintptr_t)k_cache & 7) != 0 || ((uintptr_t)v_cache & 7) != 0) return ATTN_ERR_INVAL;
+  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
+  const size_t need = attn::decode_workspace_bytes(A, d_h, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  if ((long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  attn::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.o = o;
+  p.lse = lse;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + attn::decode_workspace_lse_offset(A, d_h, plan));
+  p.B = B;
+  p.A = A;
+  p.A_kv = A_kv;
+  p.G = A / A_kv;
+  p.d = d_h;
+  p.page_size = page_size;
+  p.max_pages = max_pages;
+  p.n_chunks = plan.n_chunks;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return launch_status(attn::launch_decode_fp8(p, (hipStream_t)stream));
+}
+
 ATTN_EXPORT const char* attn_status_string(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ok";

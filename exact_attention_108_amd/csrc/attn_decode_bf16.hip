@@ -61,7 +61,16 @@ __device__ __forceinline__ int tok_swz(int tok) { return ((tok & 7) << 1) | ((to
 //                                             diagonal: columns of other KV
 //                                             heads see a zero B operand)
 //   O^T[d, n]    += sum_hh V_hh^T . P^T_hh   (16x16x16 MFMA, same masking)
-template <int D, int HPW>
+//
+// FP8 caches (kFp8): element e of the cache is one OCP E4M3 byte, and the
+// value is byte(e) * scale[page, kv head] (page "Attention Kernel", section
+// "Paged 与 ragged KV": cache dtype and scale metadata are part of the
+// contract).  Each lane loads the 8 bytes of its slot, widens them exactly to
+// bf16 (every E4M3 value is a bf16 value) and stores them where the bf16
+// path's copy would have put them, so the MFMA code is shared.  The scales
+// stay in fp32: a key's scale multiplies its scores, a value's scale its
+// probabilities before the PV product (the normaliser sums the unscaled ones).
+template <int D, int HPW, bool kFp8 = false>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(DecodeParams p) {
   constexpr int RC = HPW * D / 8;            // 16-byte chunks per token row
   constexpr int TOK_PER_LD = 64 / RC;        // tokens per load instruction
@@ -165,23 +174,56 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
       // ---- global -> LDS: instruction i fills token rows i*TOK_PER_LD + [0, TOK_PER_LD);
       //      lane slot (ld_tok, ld_pc) holds logical chunk ld_c ^ swz of head ld_hh.
       //      Rows past the end re-read the last valid row (finite, weight 0).
+      [[maybe_unused]] float ksc = 1.f, vsc = 1.f;
+      if constexpr (kFp8) {
+        // 8 E4M3 bytes per lane and slot, widened to bf16 into the same LDS slot
+        const uint8_t* kc8 = (const uint8_t*)p.k_cache;
+        const uint8_t* vc8 = (const uint8_t*)p.v_cache;
+        uint2 kr[N_LD], vr[N_LD];
 #pragma unroll
-      for (int i = 0; i < N_LD; ++i) {
-        const int tl = i * TOK_PER_LD + ld_tok;
-        const int tr = min(tl, n_valid - 1);
-        const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
-        const size_t e = page_row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
-        __builtin_amdgcn_global_load_lds((const void*)(kc + e),
-                                         (__attribute__((address_space(3))) void*)(sK + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vc + e),
-                                         (__attribute__((address_space(3))) void*)(sV + i * 1024), 16, 0, 0);
+        for (int i = 0; i < N_LD; ++i) {
+          const int tl = i * TOK_PER_LD + ld_tok;
+          const int tr = min(tl, n_valid - 1);
+          const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
+          const size_t e = page_row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
+          kr[i] = *(const uint2*)(kc8 + e);
+          vr[i] = *(const uint2*)(vc8 + e);
+        }
+        const size_t srow = (size_t)page * p.A_kv + kv0 + min(hh_col, nh - 1);
+        ksc = p.k_scale[srow];
+        vsc = p.v_scale[srow];
+        auto widen = [](uint2 w) {
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+          const b2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false);
+          const b2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true);
+          const b2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false);
+          const b2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true);
+          return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+        };
+#pragma unroll
+        for (int i = 0; i < N_LD; ++i) {
+          *(bf16x8*)(sK + i * 1024 + lane * 16) = widen(kr[i]);
+          *(bf16x8*)(sV + i * 1024 + lane * 16) = widen(vr[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < N_LD; ++i) {
+          const int tl = i * TOK_PER_LD + ld_tok;
+          const int tr = min(tl, n_valid - 1);
+          const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
+          const size_t e = page_row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
+          __builtin_amdgcn_global_load_lds((const void*)(kc + e),
+                                           (__attribute__((address_space(3))) void*)(sK + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(vc + e),
+                                           (__attribute__((address_space(3))) void*)(sV + i * 1024), 16, 0, 0);
+        }
+        // The copies land in LDS asynchronously (tracked by vmcnt).  Wait for all
+        // of them explicitly: the compiler's own wait for LDS written this way is
+        // not placed before every read.  The empty asm keeps LDS accesses from
+        // moving across the wait.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        asm volatile("" ::: "memory");
       }
-      // The copies land in LDS asynchronously (tracked by vmcnt).  Wait for all
-      // of them explicitly: the compiler's own wait for LDS written this way is
-      // not placed before every read.  The empty asm keeps LDS accesses from
-      // moving across the wait.
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      asm volatile("" ::: "memory");
       // ---- S^T = sum_hh K_hh . Q^T_hh (block diagonal over the wave's heads)
       f32x4 sc = f32x4{};
 #pragma unroll
@@ -199,6 +241,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        if constexpr (kFp8) sc[r] *= ksc;
         if (4 * grp + r >= n_valid) sc[r] = -INFINITY;
         mx = fmaxf(mx, sc[r]);
       }
@@ -214,7 +257,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
       for (int r = 0; r < 4; ++r) {
         const float e = exp2_fast(fmaf(sc[r], cs, -m_use));
         rs += e;
-        pb[r] = (__bf16)e;
+        if constexpr (kFp8)
+          pb[r] = (__bf16)(e * vsc);
+        else
+          pb[r] = (__bf16)e;
       }
       l_run = fmaf(l_run, alpha, rs);
       // ---- O^T += sum_hh V_hh^T . P^T_hh ; V^T slot s of lane group grp = token 4 grp + s
@@ -334,23 +380,24 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   if (lane == 0) p.lse[(size_t)b * p.A + h] = ok ? (mx + log2_fast(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool kFp8>
 hipError_t launch_split(const DecodeParams& p, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, HPW>), dim3(p.n_wg, groups), dim3(64 * kWavesPerGroup), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, HPW, kFp8>), dim3(p.n_wg, groups), dim3(64 * kWavesPerGroup), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool kFp8>
 int resident_groups(int cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, HPW>, 64 * kWavesPerGroup, 0) !=
-          hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, HPW, kFp8>, 64 * kWavesPerGroup,
+                                                   0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   return cus * per_cu;
 }
 
-template <int D>
+template <int D, bool kFp8>
 hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
   if (p.n_chunks > 0) {
     int dev = 0, cus = 0;
@@ -361,12 +408,12 @@ hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
     const int heads_per_group = (two ? 2 : 1) * kWavesPerGroup;
     const int groups = (p.A_kv + heads_per_group - 1) / heads_per_group;
     // one resident wave of workgroups covers the chunk list once
-    long long want = (two ? resident_groups<D, 2>(cus) : resident_groups<D, 1>(cus)) / groups;
+    long long want = (two ? resident_groups<D, 2, kFp8>(cus) : resident_groups<D, 1, kFp8>(cus)) / groups;
     if (want < 1) want = 1;
     if (want > kMaxDecodeGroups) want = kMaxDecodeGroups;
     if (want > p.n_chunks) want = p.n_chunks;
     p.n_wg = (int)want;
-    hipError_t e = two ? launch_split<D, 2>(p, groups, stream) : launch_split<D, 1>(p, groups, stream);
+    hipError_t e = two ? launch_split<D, 2, kFp8>(p, groups, stream) : launch_split<D, 1, kFp8>(p, groups, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.B * p.A), dim3(64), 0, stream, p);
@@ -398,8 +445,14 @@ size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan) {
 }
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
-  if (p.d == 128) return launch_decode_d<128>(p, stream);
-  if (p.d == 64) return launch_decode_d<64>(p, stream);
+  if (p.d == 128) return launch_decode_d<128, false>(p, stream);
+  if (p.d == 64) return launch_decode_d<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream) {
+  if (p.d == 128) return launch_decode_d<128, true>(p, stream);
+  if (p.d == 64) return launch_decode_d<64, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

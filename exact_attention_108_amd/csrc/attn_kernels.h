@@ -96,6 +96,8 @@ struct DecodeParams {
   float* lse;
   float* part_o;    // workspace [n_slots, A, d] fp32: partial outputs, normalised within the partial
   float* part_lse;  // workspace [n_slots, A] fp32: base-2 LSE of each partial
+  const float* k_scale;  // fp8 caches: [num_pages, A_kv] dequantisation scales (else null)
+  const float* v_scale;
   int B, A, A_kv, G, d;
   int page_size, max_pages;
   long long n_chunks;  // sum over sequences of ceil(len / 16)
@@ -115,5 +117,7 @@ size_t decode_workspace_bytes(int A, int d, const DecodePlan& plan);
 size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan);
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+// Same, over FP8 (OCP E4M3) caches with per-(page, KV head) scales.
+hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace attn

@@ -146,6 +146,29 @@ attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_
                               float scale, attn_dtype dtype, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/*
+ * attn_decode_paged over an FP8 KV cache (page "Attention Kernel", sections
+ * "Paged 与 ragged KV" and "正确性契约": the cache dtype and its scale
+ * metadata are part of the contract; page "Attention 算子加速史", section
+ * 3.3: FP8 attention with block-wise scales).  The caches hold one OCP FP8 E4M3
+ * byte per element (4 exponent bits, bias 7, 3 mantissa bits, largest finite
+ * value 448, no infinities; 0x7F / 0xFF are NaN and must not occur), with
+ * the layout [num_pages, page_size, A_kv, d_h]; element value =
+ * byte value * scale[page, kv head]:
+ *
+ *   k_scale, v_scale : device fp32 [num_pages, A_kv], finite
+ *
+ * q, o, lse, block table, lengths and workspace are as in attn_decode_paged
+ * (q, o bf16; same workspace size, from attn_decode_paged_workspace_bytes).
+ * Supported: d_h in {64, 128}, page_size a multiple of 16.
+ */
+attn_status attn_decode_paged_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                  const float *k_scale, const float *v_scale,
+                                  const int32_t *block_table, const int32_t *seq_lens,
+                                  const int32_t *seq_lens_host, int page_size, void *o, float *lse,
+                                  int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                  float scale, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace bytes attn_decode_paged needs for these lengths (0 on bad input). */
 size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int page_size,
                                          const int32_t *seq_lens_host);

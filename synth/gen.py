@@ -315,9 +315,9 @@ def _e4m3_positive_values() -> np.ndarray:
     return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
 
 
-def quantize_e4m3(y: np.ndarray) -> np.ndarray:
+def quantize_e4m3_reference(y: np.ndarray) -> np.ndarray:
     """Round to the nearest E4M3 code (ties to the even code), saturating at
-    448; returns uint8 codes.  Used only to build FP8 test caches."""
+    448, by searching the table of code values; returns uint8 codes."""
     tab = _e4m3_positive_values()
     a = np.minimum(np.abs(np.asarray(y, dtype=np.float64)), tab[-1])
     hi = np.clip(np.searchsorted(tab, a), 1, tab.size - 1)
@@ -326,6 +326,35 @@ def quantize_e4m3(y: np.ndarray) -> np.ndarray:
     pick_hi = (dh < dl) | ((dh == dl) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
     return np.where(np.signbit(y) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def quantize_e4m3(y: np.ndarray) -> np.ndarray:
+    """quantize_e4m3_reference for fp32 input, with integer arithmetic: below
+    2^-6 the code is round-half-even(|y| * 2^9); above, the fp32 mantissa is
+    rounded to 3 bits (ties to even) and the exponent rebiased from 127 to 7.
+    Runs in chunks on a thread pool (the FP8 decode workload has 1e9 values)."""
+    y = np.ascontiguousarray(y, dtype=np.float32).reshape(-1)
+    out = np.empty(y.size, dtype=np.uint8)
+    step = CHUNK
+
+    def work(c: int) -> None:
+        v = y[c * step: (c + 1) * step]
+        a = np.minimum(np.abs(v), np.float32(448.0))
+        bits = a.view(np.uint32)
+        lsb = (bits >> np.uint32(20)) & np.uint32(1)
+        normal = ((bits + np.uint32(0x7FFFF) + lsb) >> np.uint32(20)).astype(np.int64) - 960
+        sub = np.rint(a.astype(np.float64) * 512.0).astype(np.int64)
+        code = np.where(a < np.float32(2.0 ** -6), sub, normal).astype(np.uint8)
+        out[c * step: (c + 1) * step] = np.where((v < 0) & (code != 0), code | np.uint8(0x80), code)
+
+    n = (y.size + step - 1) // step
+    if n <= 1:
+        for c in range(n):
+            work(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(n)))
+    return out
 
 
 @dataclass
@@ -364,8 +393,10 @@ def make_paged_fp8(lens, A, A_kv, d, page_size, *, seed=0, extra_pages=0) -> Pag
     for stream in (S_K, S_V):
         x = draw((pool, page_size, A_kv, d), seed, stream, "normal", "f32")
         amax = np.abs(x).max(axis=(1, 3))                              # [pool, A_kv]
-        sc = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
-        codes = quantize_e4m3(x / sc[:, None, :, None])
+        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        x /= sc[:, None, :, None]
+        codes = quantize_e4m3(x).reshape(x.shape)
+        del x
         out += [codes, sc]
     return PagedFp8(base, out[0], out[2], out[1], out[3])
 

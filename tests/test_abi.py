@@ -20,7 +20,8 @@ def header_functions():
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd",
-                                         "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_status_string",
+                                         "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
+                                         "attn_status_string",
                                          "attn_abi_version"])
 
 

@@ -121,3 +121,57 @@ def test_config4_full(ea, orc):
                                     scale=p.scale, rows=rows)
     stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "config4")
     _say("config 4", stats)
+
+
+# ---- FP8 (E4M3) caches with per-(page, KV head) scales.  The tolerance is the
+# bf16 path's: the E4M3 values widen exactly to bf16 and the scales stay fp32,
+# so the rounding budget (bf16 P, bf16 O) is the same; the oracle decodes the
+# same codes exactly.
+
+def run_decode_fp8(ea, pf):
+    t = gu.torch()
+    p = pf.base
+    q = gu.dev(p.q, "bf16")
+    kc = t.from_numpy(pf.k_codes).cuda()
+    vc = t.from_numpy(pf.v_codes).cuda()
+    ks = t.from_numpy(pf.k_scale).cuda()
+    vs = t.from_numpy(pf.v_scale).cuda()
+    bt = gu.dev(p.block_table, "i32")
+    sl = gu.dev(p.seq_lens, "i32")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    nbytes = ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens)
+    ws = t.empty(max(nbytes, 1), dtype=t.uint8, device="cuda")
+    ws.fill_(0xFF)
+    ea.attn_decode_paged_fp8(q, kc, vc, ks, vs, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{len(c[0])}seq-A{c[1]}-kv{c[2]}-d{c[3]}-ps{c[4]}")
+def test_decode_fp8_small(ea, orc, case):
+    lens, A, A_kv, d, ps = case
+    _say("decode fp8", case)
+    pf = gen.make_paged_fp8(lens, A, A_kv, d, ps, seed=61 + sum(lens), extra_pages=2)
+    o, lse = run_decode_fp8(ea, pf)
+    p = pf.base
+    o_ref, l_ref = orc.decode_paged_fp8(p.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, p.block_table,
+                                        p.seq_lens, scale=p.scale)
+    gu.check(o, lse, o_ref, l_ref, "bf16", f"fp8 {case}")
+
+
+def test_decode_fp8_full_size_sampled(ea, orc):
+    """The paged decode workload's lengths and shape with FP8 caches; sampled
+    sequences against the oracle, every output finite."""
+    p4 = gen.make_config(4)
+    lens = p4.seq_lens
+    _say("decode fp8 full size", int(lens.sum()), "tokens")
+    pf = gen.make_paged_fp8(lens, 32, 8, 128, 16, seed=1008)
+    o, lse = run_decode_fp8(ea, pf)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    seqs = [0, int(np.argmax(lens)), int(np.argmin(lens)), 63]
+    o_ref, l_ref = orc.decode_paged_fp8(pf.base.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale,
+                                        pf.base.block_table, lens, scale=pf.base.scale, seqs=seqs)
+    _say(gu.check(o[seqs], lse[seqs], o_ref, l_ref, "bf16", "fp8 full size"))
