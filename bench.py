@@ -427,6 +427,7 @@ def main():
     out["backward"] = bench_backward(w, args.steps, args.warmup)
     out["window"] = bench_window(args.steps, args.warmup, stream)
     out["paged_prefill"] = bench_paged_prefill(w, args.steps, args.warmup)
+    out["block_sparse"] = bench_block_sparse(w, args.steps, args.warmup)
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
 
     if not args.no_cpu_baseline:
@@ -597,6 +598,49 @@ def bench_decode_fp8(w, steps: int, warmup: int, bf16_ms: float) -> dict:
             "speedup_vs_bf16_cache": round(bf16_ms / float(ms.mean()), 3),
             "workload": "the paged decode workload (64 seqs, A=32 A_kv=8 d=128, page 16) with E4M3 caches "
                         "quantised per (page, KV head)"}
+
+
+def bench_block_sparse(w, steps: int, warmup: int) -> dict:
+    """The MHA causal prefill workload with a block mask: half of the 128 x 128
+    blocks kept (seeded, one mask per batch row shared by the heads).  FLOPs =
+    4 d A x (causal (row, key) pairs inside kept blocks)."""
+    import torch
+    import exact_attention_108_amd as ea
+    p2, stream = w["p2"], w["stream"]
+    q, k, v, o, lse = w["dev2"]
+    nb = (p2.S_q + 127) // 128
+    rng = np.random.default_rng(1009)
+    bk = (rng.random((p2.B, 1, nb, nb)) < 0.5).astype(np.uint8)
+    bkd = torch.from_numpy(bk).cuda()
+
+    def run():
+        ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, block_keep=bkd, stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # causal pairs per block: below-diagonal blocks 128^2, diagonal blocks 128 * 129 / 2 (S = 2048 = 16 blocks)
+    bi, bj = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    per_block = np.where(bj < bi, 128 * 128, np.where(bj == bi, 128 * 129 // 2, 0))
+    pairs = int(sum((bk[b, 0] * per_block).sum() for b in range(p2.B)))
+    flops = 4.0 * p2.d * p2.A * pairs
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    return {"metric": "block-sparse causal prefill TFLOP/s (kept causal pairs)", "value": round(tf, 2),
+            "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "avg_ms": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
+            "min_ms": round(float(ms.min()), 5), "flops": flops, "blocks_kept": int(bk.sum()),
+            "blocks_total": int(bk.size),
+            "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 with a seeded 50% block mask (128 x 128 blocks)"}
 
 
 PAGED_CHUNK = 256

@@ -24,7 +24,8 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 
 class _Mask(ctypes.Structure):
-    _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p)]
+    _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p), ("block_keep", ctypes.c_void_p),
+                ("block_heads", ctypes.c_int)]
 
 
 class _Window(ctypes.Structure):
@@ -125,14 +126,15 @@ def _stream(stream, dev):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _mask(q_keep, k_keep):
+def _mask(q_keep, k_keep, block_keep=None):
     torch = _torch()
-    for t in (q_keep, k_keep):
+    for t in (q_keep, k_keep, block_keep):
         if t is not None and t.dtype != torch.uint8:
             raise ValueError("keep-masks must be uint8")
-    if q_keep is None and k_keep is None:
+    if q_keep is None and k_keep is None and block_keep is None:
         return None
-    return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep)))
+    heads = 0 if block_keep is None else int(block_keep.shape[1])
+    return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep), _ptr(block_keep), heads))
 
 
 def _window(window):
@@ -149,9 +151,10 @@ def _check(status: int, where: str) -> None:
 
 
 def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None, k_keep=None, window=None,
-             stream=None):
+             block_keep=None, stream=None):
     """O, LSE of softmax(Q K^T * scale + M) V.  q/o [B,A,S_q,d], k/v [B,A_kv,S_k,d], lse [B,A,S_q] fp32;
-    window = (left, right) sliding window around each query's position, -1 = unbounded side."""
+    window = (left, right) sliding window around each query's position, -1 = unbounded side;
+    block_keep = uint8 [B, 1 or A, ceil(S_q/128), ceil(S_k/128)] block mask (bf16 only)."""
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, heads, S, d]")
@@ -167,9 +170,13 @@ def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None
         raise ValueError("q_keep must be [B, S_q]")
     if k_keep is not None and k_keep.shape != (B, S_k):
         raise ValueError("k_keep must be [B, S_k]")
-    dev = _dev(q, k, v, o, lse, q_keep, k_keep)
+    if block_keep is not None and (block_keep.dim() != 4 or block_keep.shape[0] != B or
+                                   block_keep.shape[1] not in (1, A) or
+                                   tuple(block_keep.shape[2:]) != ((S_q + 127) // 128, (S_k + 127) // 128)):
+        raise ValueError("block_keep must be [B, 1 or A, ceil(S_q/128), ceil(S_k/128)]")
+    dev = _dev(q, k, v, o, lse, q_keep, k_keep, block_keep)
     st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, A, A_kv, S_q, S_k, d, float(scale),
-                       int(bool(causal)), _mask(q_keep, k_keep), _window(window), _dtype_code(q),
+                       int(bool(causal)), _mask(q_keep, k_keep, block_keep), _window(window), _dtype_code(q),
                        _stream(stream, dev))
     _check(st, "attn_fwd")
 

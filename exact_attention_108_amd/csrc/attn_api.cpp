@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
@@ -74,6 +74,11 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   if (S_k > 0 && (!k || !v)) return ATTN_ERR_INVAL;
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
+  const bool blocks = mask && mask->block_keep;
+  if (blocks) {
+    if (mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
+    if (dtype != ATTN_BF16 || S_k > 262144) return ATTN_ERR_UNSUPPORTED;
+  }
   if (S_q == 0) return ATTN_OK;
   const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
   const long long n_qt = (S_q + rows - 1) / rows;
@@ -86,6 +91,11 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   p.S_q = S_q;
   p.S_k = S_k;
   p.n_qt = (int)n_qt;
+  if (blocks) {
+    p.block_keep = mask->block_keep;
+    p.block_heads = mask->block_heads;
+    p.n_kb = (S_k + 127) / 128;
+  }
   attn::plan_dense_order(p);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, false, st) : attn::launch_prefill_f32(p, false, st);
@@ -105,6 +115,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   for (int s = 0; s < n_seq; ++s)
     if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return ATTN_ERR_INVAL;
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse)) return ATTN_ERR_INVAL;
+  if (mask && mask->block_keep) return ATTN_ERR_UNSUPPORTED;  // block masks: dense attn_fwd only
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
   if (total_tokens == 0) return ATTN_OK;
@@ -285,6 +296,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(t)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
+  if (mask && mask->block_keep) return ATTN_ERR_UNSUPPORTED;  // block masks: forward only
   if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
     return ATTN_ERR_UNSUPPORTED;
   const long long n_qt = (S_q + attn::kBwdQRows - 1) / attn::kBwdQRows;

@@ -39,6 +39,11 @@ struct FwdParams {
   const int32_t* seq_lens;
   int page_shift;  // log2(page_size)
   int max_pages;
+  // block sparsity (dense prefill): block_keep[b][hm][qb][kb] (hm = 0 when
+  // block_heads == 1, else the head) says whether the 128 x 128 block of query
+  // rows qb*128.. and keys kb*128.. is computed at all; n_kb = ceil(S_k / 128)
+  const uint8_t* block_keep;
+  int block_heads, n_kb;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin

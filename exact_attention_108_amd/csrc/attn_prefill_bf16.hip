@@ -53,7 +53,10 @@ constexpr int kBc = 64;             // keys per tile
 constexpr int kThreads = 64 * kWaves;
 static_assert(kRows == kPrefillRows, "row tile");
 
-template <int D, bool kVarlen, bool kPaged = false>
+// Key tiles one workgroup can list under a block mask (S_k up to 262144).
+constexpr int kMaxListedTiles = 4096;
+
+template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(FwdParams p) {
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
@@ -65,6 +68,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // [K buf 0 | K buf 1 | V buf 0 | V buf 1]; the epilogue reuses it for staging
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kBc * D];
   __shared__ uint8_t sKeep[2][kBc];
+  // block-sparse mode: the physical index of each listed key tile, and the
+  // per-wave counts of the list-building scans
+  __shared__ uint16_t sTiles[kBlocks ? kMaxListedTiles : 1];
+  __shared__ int sCnt[kBlocks ? kWaves : 1];
 
   RowBlock rb;
   if constexpr (kPaged) {
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (wr >= 0) kend = min(kend, q_last + off + wr + 1);
   if (wl >= 0) kbeg = max(q_first + off - wl, 0);
   const int j_lo = kbeg / kBc;
-  const int n_tiles = kend > kbeg ? (kend + kBc - 1) / kBc - j_lo : 0;
+  const int n_range = kend > kbeg ? (kend + kBc - 1) / kBc - j_lo : 0;
 
   // ---- tile order.  The tiles [j_ul, j_uh) need no per-element predicate for
   // any row of the workgroup (inside S_k, inside every row's window, no key
@@ -104,27 +111,82 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // after them (the online softmax does not depend on the order).  Logical
   // tile t is physical tile phys(t).
   int j_ul = j_lo, j_uh = j_lo;
-  if (rb.k_keep == nullptr && n_tiles > 0) {
+  if (rb.k_keep == nullptr && n_range > 0) {
     int ul = wl >= 0 ? (max(q_last + off - wl, 0) + kBc - 1) / kBc : 0;
     int uh = S_k / kBc;
     if (wr >= 0) uh = min(uh, max(q_first + off + wr + 1, 0) / kBc);
     ul = max(ul, j_lo);
-    uh = min(uh, j_lo + n_tiles);
+    uh = min(uh, j_lo + n_range);
     if (ul < uh) {
       j_ul = ul;
       j_uh = uh;
     }
   }
-  const int n_mid = j_uh - j_ul;
+  int n_tiles = n_range, n_mid = j_uh - j_ul;
   const int n_left = j_ul - j_lo;
+  if constexpr (kBlocks) {
+    // Block sparsity (page "Attention Kernel", section "可编程 mask": the
+    // block level decides which tiles are skipped whole).  List the tiles of
+    // [j_lo, j_lo + n_range) whose 128-key block this row block keeps, the
+    // predicate-free ones ([j_ul, j_uh)) first, each group in ascending order
+    // (workgroup-wide prefix sums, so the order -- and the result -- is fixed).
+    const uint8_t* brow = p.block_keep +
+        (((size_t)rb.b * p.block_heads + (p.block_heads == 1 ? 0 : rb.h)) * p.n_qt + rb.qt) * p.n_kb;
+    auto scan = [&](bool f, int& total) -> int {  // exclusive prefix of f over the workgroup
+      const uint64_t m = __ballot(f);
+      const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) sCnt[wave] = __popcll(m);
+      __syncthreads();
+      int before = 0;
+      total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        before += w < wave ? sCnt[w] : 0;
+        total += sCnt[w];
+      }
+      __syncthreads();
+      return before + in_wave;
+    };
+    auto classify = [&](int base, bool& keep, bool& free) {
+      const int jj = j_lo + base + tid;
+      keep = base + tid < n_range && brow[jj >> 1] != 0;
+      free = keep && jj >= j_ul && jj < j_uh;
+    };
+    int n_free = 0;
+    for (int base = 0; base < n_range; base += kThreads) {
+      bool keep, free;
+      classify(base, keep, free);
+      int t;
+      scan(free, t);
+      n_free += t;
+    }
+    int at_free = 0, at_rest = n_free;
+    for (int base = 0; base < n_range; base += kThreads) {
+      bool keep, free;
+      classify(base, keep, free);
+      int tf, tr;
+      const int pf = scan(free, tf), pr = scan(keep && !free, tr);
+      if (free) sTiles[at_free + pf] = (uint16_t)(j_lo + base + tid);
+      if (keep && !free) sTiles[at_rest + pr] = (uint16_t)(j_lo + base + tid);
+      at_free += tf;
+      at_rest += tr;
+    }
+    __syncthreads();
+    n_tiles = __builtin_amdgcn_readfirstlane(at_rest);
+    n_mid = __builtin_amdgcn_readfirstlane(n_free);
+  }
   // (written with 0/1 factors: selects here became branches at the top of
   // every iteration.  Without a left edge n_left = 0 and phys(t) = j_ul + t.)
   auto phys = [=](int t) -> int {
-    const int u = t - n_mid;
-    const int in_left = (unsigned)u < (unsigned)n_left;  // u in [0, n_left): left edge tiles
-    const int past = u >= n_left;                         // right edge tiles
-    const int base = j_ul + t - past * n_left;            // middle, then [j_uh, j_hi)
-    return base + in_left * (j_lo + u - base);
+    if constexpr (kBlocks) {
+      return __builtin_amdgcn_readfirstlane((int)sTiles[t]);
+    } else {
+      const int u = t - n_mid;
+      const int in_left = (unsigned)u < (unsigned)n_left;  // u in [0, n_left): left edge tiles
+      const int past = u >= n_left;                         // right edge tiles
+      const int base = j_ul + t - past * n_left;            // middle, then [j_uh, j_hi)
+      return base + in_left * (j_lo + u - base);
+    }
   };
 
   // ---- resident Q operand: lane holds Q[qrow][16t + 8g .. +7] for each t
@@ -512,7 +574,9 @@ hipError_t launch_d(const FwdParams& p, bool varlen, hipStream_t stream) {
     grid = p.n_qt * p.A * p.B;
   }
   if (grid <= 0) return hipSuccess;
-  if (varlen) {
+  if (!varlen && p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (varlen) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);

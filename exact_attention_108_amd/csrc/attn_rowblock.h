@@ -16,6 +16,7 @@ struct RowBlock {
   const uint8_t* k_keep;  // or null
   int S_q, S_k;
   int q0;                 // first query row of this workgroup
+  int b, h, qt;           // dense: batch, head and query tile of this workgroup
 };
 
 // Dense batch: query tile index descending (heaviest causal tiles first),
@@ -51,6 +52,9 @@ __device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_byte
   r.S_q = p.S_q;
   r.S_k = p.S_k;
   r.q0 = qt * kRows;
+  r.b = b;
+  r.h = h;
+  r.qt = qt;
   return r;
 }
 

@@ -59,11 +59,21 @@ typedef enum {
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 
-/* Optional keep-masks (uint8, 1 = keep, 0 = mask to -inf); either may be NULL.
- * Layout: attn_fwd q_keep [B, S_q], k_keep [B, S_k]; attn_fwd_varlen [T]. */
+/* Optional keep-masks (uint8, 1 = keep, 0 = mask to -inf); any may be NULL.
+ * Layout: attn_fwd q_keep [B, S_q], k_keep [B, S_k]; attn_fwd_varlen [T].
+ *
+ * block_keep (attn_fwd only, bf16): block sparsity (page "Attention Kernel",
+ * section "可编程 mask": the block level decides which tiles are skipped
+ * whole).  uint8 [B, block_heads, ceil(S_q / 128), ceil(S_k / 128)];
+ * block_keep[b][h'][i][j] = 0 masks every (row, key) pair with row in
+ * [128 i, 128 i + 128) and key in [128 j, 128 j + 128) (h' = 0 when
+ * block_heads == 1, else the query head); those key tiles are never loaded.
+ * block_heads is 1 or A.  Requires S_k <= 262144. */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
+    const uint8_t *block_keep;
+    int block_heads;
 } attn_mask;
 
 /* Optional sliding window (page "Attention Kernel", section "可编程 mask":

@@ -39,7 +39,7 @@ def test_library_exports_exactly_the_header():
 
 def test_status_strings_and_version():
     import exact_attention_108_amd as ea
-    assert ea.attn_abi_version() == 2
+    assert ea.attn_abi_version() == 3
     assert ea.attn_status_string(0) == "ok"
     assert ea.attn_status_string(1) == "invalid argument"
     assert ea.attn_status_string(2) == "unsupported configuration"
@@ -112,6 +112,13 @@ def test_attn_fwd_rejects_bad_arguments():
     assert fwd(lib, window=ct.byref(W(-2, 0))) == INVAL     # window sides are >= -1
     assert fwd(lib, window=ct.byref(W(3, -5))) == INVAL
     assert fwd(lib, S_q=0, q=None, o=None, lse=None, window=ct.byref(W(3, -1))) == OK
+
+    class M(ct.Structure):
+        _fields_ = [("q_keep", ct.c_void_p), ("k_keep", ct.c_void_p), ("block_keep", ct.c_void_p),
+                    ("block_heads", ct.c_int)]
+    assert fwd(lib, mask=ct.byref(M(None, None, 4096, 3))) == INVAL           # block_heads must be 1 or A
+    assert fwd(lib, mask=ct.byref(M(None, None, 4096, 1)), dt=0) == UNSUP     # block masks: bf16 only
+    assert fwd(lib, mask=ct.byref(M(None, None, 4096, 1)), S_k=300000) == UNSUP
     # the page's shape-mismatch example has no analogue here: sizes are explicit,
     # and the Python binding rejects tensors whose shapes disagree
     import pytest

@@ -382,3 +382,88 @@ def test_paged_prefill_equals_varlen_bitwise(ea):
                           cu, pv.cu_seqlens, o2, l2, scale=pv.scale, causal=True)
     t.cuda.synchronize()
     assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
+
+
+# ---- block sparsity (page "Attention Kernel", section "可编程 mask"): the
+# oracle receives the block mask expanded to the dense keep matrix it defines
+
+def block_dense(bk_b, S_q, S_k):
+    """[nqb, nkb] block mask -> [S_q, S_k] keep matrix (block (i, j) covers rows
+    128 i .. and keys 128 j ..)."""
+    return np.repeat(np.repeat(bk_b, 128, axis=0), 128, axis=1)[:S_q, :S_k]
+
+
+def run_block_sparse(ea, p, bk, window=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A, p.S_q), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, window=window, block_keep=gu.dev(bk, "u8"))
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def check_block_sparse(orc, p, bk, o, lse, what, window=None, heads=None):
+    G = p.A // p.A_kv
+    for h in (range(p.A) if heads is None else heads):
+        hm = 0 if bk.shape[1] == 1 else h
+        mk = np.stack([block_dense(bk[b, hm], p.S_q, p.S_k) for b in range(p.B)]).astype(np.uint8)
+        if window is not None:
+            mk &= oracle.window_keep(p.B, p.S_q, p.S_k, window[0], 0 if p.causal else window[1])
+        o_ref, l_ref = orc.attn_fwd(p.q[:, h:h + 1], p.k[:, h // G:h // G + 1], p.v[:, h // G:h // G + 1],
+                                    dtype="bf16", scale=p.scale, causal=p.causal, m_keep=mk)
+        gu.check(o[:, h:h + 1], lse[:, h:h + 1], o_ref, l_ref, "bf16", f"{what} head {h}")
+
+
+BLOCK_CASES = [
+    # B, A, A_kv, S_q, S_k, d, causal, block_heads, density, window
+    (2, 4, 2, 700, 700, 128, True, 1, 0.5, None),
+    (1, 4, 4, 513, 900, 128, False, 4, 0.4, None),     # a different mask per head, ragged sizes
+    (1, 2, 1, 640, 640, 64, True, 2, 0.6, None),
+    (1, 2, 2, 600, 600, 128, True, 1, 0.7, (200, -1)),  # with a sliding window
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n")
+                         + f"h{c[7]}d{c[8]}" + ("w" if c[9] else ""))
+def test_block_sparse(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal, bh, dens, window = case
+    _say("block sparse", case)
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=950 + S_q)
+    rng = np.random.default_rng(S_q + S_k)
+    bk = (rng.random((B, bh, (S_q + 127) // 128, (S_k + 127) // 128)) < dens).astype(np.uint8)
+    bk[0, 0, 1, :] = 0                                   # a row block with every block off
+    o, lse = run_block_sparse(ea, p, bk, window)
+    check_block_sparse(orc, p, bk, o, lse, str(case), window)
+
+
+def test_block_sparse_all_on_equals_dense_bitwise(ea):
+    """Every block kept: the listed tiles are the plain tile range in the same
+    order, so the output equals the plain causal call bit for bit."""
+    t = gu.torch()
+    p = gen.make_dense(1, 4, 2, 777, 777, 128, dtype="bf16", causal=True, seed=960)
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    o1, o2 = gu.empty_out(q.shape, "bf16"), gu.empty_out(q.shape, "bf16")
+    l1 = t.empty((1, 4, 777), dtype=t.float32, device="cuda")
+    l2 = t.empty_like(l1)
+    ea.attn_fwd(q, k, v, o1, l1, scale=p.scale, causal=True)
+    bk = t.ones((1, 1, 7, 7), dtype=t.uint8, device="cuda")
+    ea.attn_fwd(q, k, v, o2, l2, scale=p.scale, causal=True, block_keep=bk)
+    t.cuda.synchronize()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
+
+
+def test_block_sparse_full_size_sampled(ea, orc):
+    """The MHA workload's shape, causal, half of the blocks kept (per batch row),
+    sampled heads against the oracle."""
+    p = gen.make_dense(4, 32, 32, 2048, 2048, 128, dtype="bf16", causal=True, seed=961)
+    rng = np.random.default_rng(961)
+    bk = (rng.random((4, 1, 16, 16)) < 0.5).astype(np.uint8)
+    _say("block sparse full size", int(bk.sum()), "blocks kept")
+    o, lse = run_block_sparse(ea, p, bk)
+    dead = np.stack([block_dense(bk[b, 0], 2048, 2048) & np.tril(np.ones((2048, 2048), np.uint8))
+                     for b in range(4)]).sum(axis=2) == 0
+    assert np.all(np.isneginf(lse[dead[:, None, :].repeat(32, 1)]))
+    check_block_sparse(orc, p, bk, o, lse, "block sparse full size", heads=[0, 17, 31])
