@@ -24,7 +24,7 @@
 //      its prologue also forms D_i and the base-2 LSE of each row and stores
 //      both in the workspace for the second launch;
 //   2. dK/dV: one workgroup per 128 keys of one (batch, KV head), four waves
-//      of 32 keys, streaming triple-buffered 32-row blocks of Q, dO and the row
+//      of 32 keys, streaming 32-row blocks of Q, dO and the row
 //      statistics of every query head that reads this KV head (this is the GQA
 //      sum), one key per lane:
 //        S = Q . K^T,  dP = dO . V^T  (K and V rows resident),
@@ -100,14 +100,13 @@ using Slot = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------- dQ
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void bwd_dq_kernel(BwdParams p,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p,
                                                                                                     int n_qt) {
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int TILE_BYTES = kKeyTile * D * 2;
   constexpr int SLOT_BYTES = 2 * TILE_BYTES;  // [K tile | V tile]
-  constexpr int NSLOT = 4;
-  constexpr int COPIES = 2 * (kKeyTile * D / 8 / kThreads);  // copy instructions per wave per tile
+  constexpr int NSLOT = 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * SLOT_BYTES / 2];
 
   // heaviest query tiles first (most causal key tiles)
@@ -191,56 +190,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     return key < S_k && (kkeep == nullptr || kkeep[key] != 0);
   };
 
-  // S^T and dP^T of the tile in `lds` (two 32-key blocks each)
-  auto scores = [&](const char* lds, f32x16 (&s)[2], f32x16 (&dp)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        const bf16x8 ka = *(const bf16x8*)(lds + kb * 32 * D * 2 + koff[t]);
-        const bf16x8 va = *(const bf16x8*)(lds + TILE_BYTES + kb * 32 * D * 2 + koff[t]);
-        s[kb] = mfma32(ka, qf[t], s[kb]);
-        dp[kb] = mfma32(va, dof[t], dp[kb]);
-      }
-    }
-  };
-  // P, dS = P (dP - D) of tile j, then dQ^T += K^T . dS^T.  A dead row has
-  // lrow = +inf, so its p = 2^-inf = 0 without a mask.  MASKED adds the
-  // per-element predicate (keys past S_k, dropped keys, the window's edges).
-  auto grad = [&](const char* lds, int j, bool ok, const f32x16 (&s)[2], const f32x16 (&dp)[2], auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int k0 = (j_lo + j) * kKeyTile;
-    // element r of 32-key block kb holds key k0 + 32 kb + 8(r/4) + 4g + r%4
-    const uint64_t kvalid = __ballot(ok) >> (4 * g);
-    const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
-    const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fmaf(s[kb][r], cs, -lrow);
-        if constexpr (MASKED) {
-          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-          x = (((kvalid >> c) & 1) && c <= lim && c >= lo) ? x : -INFINITY;
-        }
-        const float pr = exp2_fast(x);
-        dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[kb][r] - drow));
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const char* base = lds + (32 * kb + 16 * hh) * D * 2;
-          const bf16x8 kt = concat(lds_read_tr16(base + voff[mb][0]), lds_read_tr16(base + voff[mb][1]));
-          acc[mb] = mfma32(kt, dsb[hh], acc[mb]);
-        }
-      }
-    }
-  };
-  // whether tile j needs the per-element predicate in this wave (uniform)
+  // 32-key half kb of tile j in `lds`: S^T, dP^T, then P, dS and dQ^T += K^T . dS^T
   const int wave_row0 = q0 + wave * 32;
   auto tile_masked = [&](int j, bool ok) -> bool {
     const int k0 = (j_lo + j) * kKeyTile;
@@ -249,63 +199,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     if (wl >= 0) full = full && k0 >= wave_row0 + 31 + off - wl;
     return !full;
   };
-
-  // Software pipeline over key tiles: step j waits for tile j + 1, issues the
-  // copy of tile j + 3 into the slot tile j - 1 used, and computes, in one
-  // basic block so that the two interleave, S^T and dP^T of tile j + 1 and the
-  // gradient of tile j (from the S^T and dP^T the previous step computed).
-  // Slot of tile j: j % 4; the two register sets alternate.
-  struct SD {
-    f32x16 s[2], dp[2];
-  };
-  SD ra, rb;
-  auto step = [&](int j, auto slot_tag, SD& cur, SD& nxt) {
-    constexpr int SC = decltype(slot_tag)::value;
-    constexpr int SN = (SC + 1) % NSLOT, SI = (SC + 3) % NSLOT;
-    if (j + 2 < n_tiles)
-      lds_copy_wait<COPIES>();  // tile j + 1 has landed; j + 2 may still be in flight
-    else
-      lds_copy_wait_all();
-    __syncthreads();  // and for every wave; every wave is done with tile j - 1
-    if (j + 3 < n_tiles) issue(j + 3, SI);
-    const char* lc = (const char*)smem + SC * SLOT_BYTES;
-    // at the last tile this reads a stale (in-bounds) slot; the result is unused
-    const char* ln = (const char*)smem + SN * SLOT_BYTES;
-    const bool ok = key_ok(j);
-    if (tile_masked(j, ok)) {
-      interleave_hint();
-      scores(ln, nxt.s, nxt.dp);
-      grad(lc, j, ok, cur.s, cur.dp, std::true_type{});
-    } else {
-      interleave_hint();
-      scores(ln, nxt.s, nxt.dp);
-      grad(lc, j, ok, cur.s, cur.dp, std::false_type{});
+  auto half = [&](const char* lds, int j, bool ok, int kb, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      const bf16x8 ka = *(const bf16x8*)(lds + kb * 32 * D * 2 + koff[t]);
+      const bf16x8 va = *(const bf16x8*)(lds + TILE_BYTES + kb * 32 * D * 2 + koff[t]);
+      s = mfma32(ka, qf[t], s);
+      dp = mfma32(va, dof[t], dp);
+    }
+    const int k0 = (j_lo + j) * kKeyTile;
+    const uint64_t kvalid = __ballot(ok) >> (4 * g);
+    const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
+    const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = fmaf(s[r], cs, -lrow);
+      if constexpr (MASKED) {
+        const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+        x = (((kvalid >> c) & 1) && c <= lim && c >= lo) ? x : -INFINITY;
+      }
+      const float pr = exp2_fast(x);
+      dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - drow));
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const char* base = lds + (32 * kb + 16 * hh) * D * 2;
+        const bf16x8 kt = concat(lds_read_tr16(base + voff[mb][0]), lds_read_tr16(base + voff[mb][1]));
+        acc[mb] = mfma32(kt, dsb[hh], acc[mb]);
+      }
     }
   };
-
-  if (n_tiles > 0) {
-    issue(0, 0);
-    if (n_tiles > 1) issue(1, 1);
-    if (n_tiles > 2) issue(2, 2);
-    if (n_tiles > 2)
-      lds_copy_wait<2 * COPIES>();
-    else if (n_tiles > 1)
-      lds_copy_wait<COPIES>();
-    else
-      lds_copy_wait_all();
-    __syncthreads();
-    scores((const char*)smem, ra.s, ra.dp);
-  }
+  auto step = [&](int j, auto slot_tag) {
+    constexpr int SC = decltype(slot_tag)::value;
+    lds_copy_wait_all();
+    __syncthreads();  // tile j has landed; every wave is done with tile j - 1
+    if (j + 1 < n_tiles) issue(j + 1, SC ^ 1);
+    const char* lc = (const char*)smem + SC * SLOT_BYTES;
+    const bool ok = key_ok(j);
+    if (tile_masked(j, ok)) {
+      half(lc, j, ok, 0, std::true_type{});
+      half(lc, j, ok, 1, std::true_type{});
+    } else {
+      half(lc, j, ok, 0, std::false_type{});
+      half(lc, j, ok, 1, std::false_type{});
+    }
+  };
+  if (n_tiles > 0) issue(0, 0);
   int j = 0;
-  for (; j + 4 <= n_tiles; j += 4) {
-    step(j, Slot<0>{}, ra, rb);
-    step(j + 1, Slot<1>{}, rb, ra);
-    step(j + 2, Slot<2>{}, ra, rb);
-    step(j + 3, Slot<3>{}, rb, ra);
+  for (; j + 2 <= n_tiles; j += 2) {
+    step(j, Slot<0>{});
+    step(j + 1, Slot<1>{});
   }
-  if (j < n_tiles) step(j, Slot<0>{}, ra, rb);
-  if (j + 1 < n_tiles) step(j + 1, Slot<1>{}, rb, ra);
-  if (j + 2 < n_tiles) step(j + 2, Slot<2>{}, ra, rb);
+  if (j < n_tiles) step(j, Slot<0>{});
 
   // dQ = scale * (dQ^T)^T: lane holds d = 32mb + 8(r/4) + 4g + r%4 of its row
   if (row_in) {
