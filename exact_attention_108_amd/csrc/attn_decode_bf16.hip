@@ -160,38 +160,59 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{};
 
-    for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
-      // a 16-token chunk lies inside one page (page_size is a multiple of 16)
-      int pidx = c0 / ps - pbase;
+    // first token row of chunk c in the cache (for this wave's first KV head).
+    // A 16-token chunk lies inside one page (page_size is a multiple of 16);
+    // chunks are looked up in increasing order, each at most one page past
+    // the previous, so the 64-entry block-table window only moves forward.
+    auto chunk_row0 = [&](int c, int& page) -> size_t {
+      int pidx = c / ps - pbase;
       if (pidx >= 64) {
         pbase += 64;
         pidx -= 64;
         page_of_lane = pbase + lane <= last_page ? bt[pbase + lane] : 0;
       }
-      const int page = __builtin_amdgcn_readlane(page_of_lane, pidx);
-      const size_t page_row0 = ((size_t)page * ps + (c0 % ps)) * tok_stride + (size_t)kv0 * D;
+      page = __builtin_amdgcn_readlane(page_of_lane, pidx);
+      return ((size_t)page * ps + (c % ps)) * tok_stride + (size_t)kv0 * D;
+    };
+    // global offset of lane slot (ld_tok, ld_pc) of load instruction i: token
+    // row i*TOK_PER_LD + ld_tok (rows past the end re-read the last valid row:
+    // finite, weight 0), logical chunk ld_c ^ swz of head ld_hh
+    auto slot_elem = [&](size_t row0, int n_valid, int i) -> size_t {
+      const int tl = i * TOK_PER_LD + ld_tok;
+      const int tr = min(tl, n_valid - 1);
+      const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
+      return row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
+    };
+    // FP8: the 8 E4M3 bytes of each lane slot of a chunk, and its scales, are
+    // loaded one chunk ahead into registers (the loads of chunk c + 16 are in
+    // flight while chunk c is computed)
+    [[maybe_unused]] uint2 kr[N_LD], vr[N_LD];
+    [[maybe_unused]] float ksc_n = 1.f, vsc_n = 1.f;
+    [[maybe_unused]] auto fp8_load = [&](int c) {
+      int page;
+      const size_t row0 = chunk_row0(c, page);
+      const int nv = min(kChunk, t_end - c);
+      const uint8_t* kc8 = (const uint8_t*)p.k_cache;
+      const uint8_t* vc8 = (const uint8_t*)p.v_cache;
+#pragma unroll
+      for (int i = 0; i < N_LD; ++i) {
+        const size_t e = slot_elem(row0, nv, i);
+        kr[i] = *(const uint2*)(kc8 + e);
+        vr[i] = *(const uint2*)(vc8 + e);
+      }
+      const size_t srow = (size_t)page * p.A_kv + kv0 + min(hh_col, nh - 1);
+      ksc_n = p.k_scale[srow];
+      vsc_n = p.v_scale[srow];
+    };
+    if constexpr (kFp8) {
+      if (t_begin < t_end) fp8_load(t_begin);
+    }
+
+    for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
       const int n_valid = min(kChunk, t_end - c0);
-      // ---- global -> LDS: instruction i fills token rows i*TOK_PER_LD + [0, TOK_PER_LD);
-      //      lane slot (ld_tok, ld_pc) holds logical chunk ld_c ^ swz of head ld_hh.
-      //      Rows past the end re-read the last valid row (finite, weight 0).
       [[maybe_unused]] float ksc = 1.f, vsc = 1.f;
       if constexpr (kFp8) {
-        // 8 E4M3 bytes per lane and slot, widened to bf16 into the same LDS slot
-        const uint8_t* kc8 = (const uint8_t*)p.k_cache;
-        const uint8_t* vc8 = (const uint8_t*)p.v_cache;
-        uint2 kr[N_LD], vr[N_LD];
-#pragma unroll
-        for (int i = 0; i < N_LD; ++i) {
-          const int tl = i * TOK_PER_LD + ld_tok;
-          const int tr = min(tl, n_valid - 1);
-          const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
-          const size_t e = page_row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
-          kr[i] = *(const uint2*)(kc8 + e);
-          vr[i] = *(const uint2*)(vc8 + e);
-        }
-        const size_t srow = (size_t)page * p.A_kv + kv0 + min(hh_col, nh - 1);
-        ksc = p.k_scale[srow];
-        vsc = p.v_scale[srow];
+        // widen to bf16 (exact) into the LDS slots the bf16 copy would fill
         auto widen = [](uint2 w) {
           typedef __bf16 b2 __attribute__((ext_vector_type(2)));
           const b2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false);
@@ -205,13 +226,16 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
           *(bf16x8*)(sK + i * 1024 + lane * 16) = widen(kr[i]);
           *(bf16x8*)(sV + i * 1024 + lane * 16) = widen(vr[i]);
         }
+        ksc = ksc_n;
+        vsc = vsc_n;
+        if (c0 + kChunk < t_end) fp8_load(c0 + kChunk);
       } else {
+        // ---- global -> LDS: instruction i fills token rows i*TOK_PER_LD + [0, TOK_PER_LD)
+        int page;
+        const size_t page_row0 = chunk_row0(c0, page);
 #pragma unroll
         for (int i = 0; i < N_LD; ++i) {
-          const int tl = i * TOK_PER_LD + ld_tok;
-          const int tr = min(tl, n_valid - 1);
-          const int c = ld_c ^ (tok_swz(tl) & (D / 8 - 1));
-          const size_t e = page_row0 + (size_t)tr * tok_stride + (size_t)ld_hh * D + c * 8;
+          const size_t e = slot_elem(page_row0, n_valid, i);
           __builtin_amdgcn_global_load_lds((const void*)(kc + e),
                                            (__attribute__((address_space(3))) void*)(sK + i * 1024), 16, 0, 0);
           __builtin_amdgcn_global_load_lds((const void*)(vc + e),
