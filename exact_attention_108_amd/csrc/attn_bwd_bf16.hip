@@ -69,12 +69,6 @@ __device__ __forceinline__ void copy_rows(const uint16_t* base, int rows_total, 
     lds_copy16_buf(rsrc, (uint32_t)((i * RPC + rowc) * D * 2 + cc * 16), wave_base + (uint32_t)(i * RPC * D * 2));
 }
 
-// Scheduling hint for the blocks that hold both a score pass and a gradient
-// pass: LLVM's interleaving strategy 0 for MFMA-heavy code spreads the LDS
-// reads and vector ALU work between the matrix instructions (measured: 6-11%
-// faster than the default schedule, bitwise identical results).
-__device__ __forceinline__ void interleave_hint() { __builtin_amdgcn_iglp_opt(0); }
-
 // Grid order.  Workgroups are dealt to the 8 XCDs round-robin by index and
 // each XCD has its own L2.  With `group` > 0, XCD x owns the units (batch,
 // head pairs) [x * per, (x + 1) * per) and takes them `group` at a time, each

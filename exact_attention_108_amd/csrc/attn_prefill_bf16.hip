@@ -487,6 +487,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     rescale(mx_cur);
     f32x16 s_next[2];
+    interleave_hint();
     if constexpr (!MASKED) {
       qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
       softmax_pv(buf_tag, s_cur, issue);
