@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = ATTN_ABI_VERSION;
 
 bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 

@@ -46,6 +46,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The value attn_abi_version() returns for this header. */
+#define ATTN_ABI_VERSION 3
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -68,7 +71,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * block_keep[b][h'][i][j] = 0 masks every (row, key) pair with row in
  * [128 i, 128 i + 128) and key in [128 j, 128 j + 128) (h' = 0 when
  * block_heads == 1, else the query head); those key tiles are never loaded.
- * block_heads is 1 or A.  Requires S_k <= 262144. */
+ * block_heads is 1 or A (ignored when block_keep is NULL).  Requires
+ * S_k <= 262144.  attn_fwd_varlen and attn_bwd return ATTN_ERR_UNSUPPORTED
+ * for a non-NULL block_keep. */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
