@@ -275,6 +275,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const float cs = p.scale_log2;
   const int wave_q0 = rb.q0 + wave * 32;
+  // keys [kbeg_w, kend_w) hold every key some row of this wave keeps; a
+  // tile outside them is dead for the whole wave (only edge tiles can be:
+  // the predicate-free ones lie inside every row's range)
+  int kbeg_w = 0, kend_w = S_k;
+  if (wr >= 0) kend_w = min(kend_w, wave_q0 + 31 + off + wr + 1);
+  if (wl >= 0) kbeg_w = max(wave_q0 + off - wl, 0);
+  kbeg_w = __builtin_amdgcn_readfirstlane(kbeg_w);
+  kend_w = __builtin_amdgcn_readfirstlane(kend_w);
+  auto wave_sees = [&](int t) -> bool {
+    const int k0 = phys(t) * kBc;
+    return k0 < kend_w && k0 + kBc > kbeg_w;
+  };
 
   // ---- per-lane LDS byte offsets of the operand reads inside a tile buffer.
   // The swizzle depends on row % 16 only, so the row blocks (32 rows per kb,
@@ -370,11 +382,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // LDS buffer VBUF; the normaliser sums p in fp32, the product takes p
   // rounded to bf16.  PV steps (kb, h, mb) with mb innermost: MB independent
   // accumulator chains.  `issue` is called at two points.
-  auto softmax_pv = [&](auto vbuf_tag, const f32x16 (&s)[2], auto&& issue) {
-    constexpr int VB = (2 + decltype(vbuf_tag)::value) * TILE_BYTES;
+  auto exps = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) -> float {
     const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -393,7 +403,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         pb[kb][r >> 3][(r & 7) + 3] = (__bf16)e3;
       }
     }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+  auto softmax_pv = [&](auto vbuf_tag, const f32x16 (&s)[2], auto&& issue) {
+    constexpr int VB = (2 + decltype(vbuf_tag)::value) * TILE_BYTES;
+    bf16x8 pb[2][2];
+    l_run += exps(s, pb);
     constexpr int NV = 4 * MB;
     bf16x8 va[NV];
     auto vread = [&](int q) {  // step q: mb = q % MB, (kb, h) = q / MB
@@ -495,14 +510,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];
     } else {
-      const bool has_next = j + 1 < n_tiles;
+      // a wave skips the work of a tile none of its rows can see (it still
+      // takes part in the copies and barriers)
+      const bool has_next = j + 1 < n_tiles && wave_sees(j + 1);
       if (has_next) {
         qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
       } else {
         issue(0);
         issue(1);
       }
-      softmax_pv(buf_tag, s_cur, issue);
+      if (wave_sees(j)) {
+        softmax_pv(buf_tag, s_cur, issue);
+      } else {
+        issue(2);
+        issue(3);
+      }
       if (has_next) {
         mask(s_next, j + 1);
         mx_cur = rowmax(s_next);
