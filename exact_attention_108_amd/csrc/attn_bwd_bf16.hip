@@ -268,23 +268,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One wave per SIMD at d = 128 (the resident K/V rows and the fp32 dK/dV
-// accumulators take about 380 registers); two at d = 64, where they fit in
-// 256 (measured +8-29% on causal batches).
-template <int D>
-constexpr int kDkdvWavesPerSimd = D == 64 ? 2 : 1;
+// Two forms.  KLDS = false: the K and V rows of a wave's keys stay in
+// registers and the loop is software-pipelined over 4 LDS slots; at d = 128
+// that takes about 380 registers, so one wave per SIMD (two at d = 64).
+// KLDS = true (d = 128): the workgroup's 128 K rows live in LDS (32 KB, read as
+// the B operand of S), V stays in registers and the Q/dO blocks are
+// double-buffered, which fits 256 registers: two waves per SIMD, twice the
+// resident workgroups.  The launch picks it when the grid has enough
+// workgroups to fill those slots several times over.
+template <int D, bool KLDS>
+constexpr int kDkdvWavesPerSimd = (D == 64 || KLDS) ? 2 : 1;
 
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D>, kDkdvWavesPerSimd<D>))) void bwd_dkdv_kernel(BwdParams p,
+template <int D, bool KLDS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS>, kDkdvWavesPerSimd<D, KLDS>))) void bwd_dkdv_kernel(BwdParams p,
                                                                                                       int n_kt) {
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
   constexpr int STATS_BYTES = kQBlock * 8;                    // (L2, D) per row
   constexpr int SLOT_BYTES = 2 * BLOCK_BYTES + STATS_BYTES;   // [Q block | dO block | stats]
-  constexpr int NSLOT = 4;
+  constexpr int NSLOT = KLDS ? 2 : 4;
+  constexpr int KTILE_BYTES = KLDS ? kBwdKRows * D * 2 : 0;  // [slots | K tile]
   constexpr int COPIES = 2 * (kQBlock * D / 8 / kThreads) + 1;  // copy instructions per wave per block
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * SLOT_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(NSLOT * SLOT_BYTES + KTILE_BYTES) / 2];
 
   // key tiles in order (the first ones see the most query rows when causal)
   int kt, bk;
@@ -298,10 +304,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   bool key_live = key < S_k;
   if (key_live && p.k_keep) key_live = p.k_keep[(size_t)b * S_k + key] != 0;
 
-  bf16x8 kres[KSTEPS], vres[KSTEPS];
+  bf16x8 kres[KLDS ? 1 : KSTEPS], vres[KSTEPS];
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) {
-    kres[t] = key < S_k ? *(const bf16x8*)((const uint16_t*)p.k + (k_row0 + key) * D + 16 * t + 8 * g) : bf16x8{};
+    if constexpr (!KLDS)
+      kres[t] = key < S_k ? *(const bf16x8*)((const uint16_t*)p.k + (k_row0 + key) * D + 16 * t + 8 * g) : bf16x8{};
     vres[t] = key < S_k ? *(const bf16x8*)((const uint16_t*)p.v + (k_row0 + key) * D + 16 * t + 8 * g) : bf16x8{};
   }
 
@@ -353,6 +360,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   };
 
   // S and dP of the block in `lds` for this wave's 32 keys
+  // (K tile in LDS: this wave's rows 32 wave + l32 have the swizzle of rows l32)
+  const char* lds_k = (const char*)smem + NSLOT * SLOT_BYTES + wave * 32 * D * 2;
   auto scores = [&](const char* lds, f32x16& s, f32x16& dp) {
     s = f32x16{};
     dp = f32x16{};
@@ -360,7 +369,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     for (int t = 0; t < KSTEPS; ++t) {
       const bf16x8 qa = *(const bf16x8*)(lds + koff[t]);
       const bf16x8 da = *(const bf16x8*)(lds + BLOCK_BYTES + koff[t]);
-      s = mfma32(qa, kres[t], s);
+      if constexpr (KLDS) {
+        s = mfma32(qa, *(const bf16x8*)(lds_k + koff[t]), s);
+      } else {
+        s = mfma32(qa, kres[t], s);
+      }
       dp = mfma32(da, vres[t], dp);
     }
   };
@@ -451,29 +464,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     }
   };
 
-  if (n_blocks > 0) {
-    issue(0, 0);
-    if (n_blocks > 1) issue(1, 1);
-    if (n_blocks > 2) issue(2, 2);
-    if (n_blocks > 2)
-      lds_copy_wait<2 * COPIES>();
-    else if (n_blocks > 1)
-      lds_copy_wait<COPIES>();
-    else
+  if constexpr (KLDS) {
+    // Two slots: step idx waits for block idx (and, at the first step, the K
+    // tile), issues the copy of block idx + 1 into the other slot and computes
+    // block idx; the other workgroup's waves on the SIMD fill the gaps.
+    auto step2 = [&](int idx, auto slot_tag) {
+      constexpr int SC = decltype(slot_tag)::value;
       lds_copy_wait_all();
-    __syncthreads();
-    scores((const char*)smem, ra.s, ra.dp);
+      __syncthreads();  // block idx has landed for every wave; all are done with block idx - 1
+      if (idx + 1 < n_blocks) issue(idx + 1, SC ^ 1);
+      const char* lc = (const char*)smem + SC * SLOT_BYTES;
+      SD cur;
+      if (block_masked(idx)) {
+        interleave_hint();
+        scores(lc, cur.s, cur.dp);
+        grad(lc, idx, cur.s, cur.dp, std::true_type{});
+      } else {
+        interleave_hint();
+        scores(lc, cur.s, cur.dp);
+        grad(lc, idx, cur.s, cur.dp, std::false_type{});
+      }
+    };
+    if (n_blocks > 0) {
+      // the workgroup's K rows (rows past S_k arrive as zeros)
+      copy_rows<D, kBwdKRows>((const uint16_t*)p.k + k_row0 * D, S_k, kt * kBwdKRows,
+                              lds_base + NSLOT * SLOT_BYTES);
+      issue(0, 0);
+    }
+    for (int idx = 0; idx < n_blocks; idx += 2) {
+      step2(idx, Slot<0>{});
+      if (idx + 1 < n_blocks) step2(idx + 1, Slot<1>{});
+    }
+  } else {
+    if (n_blocks > 0) {
+      issue(0, 0);
+      if (n_blocks > 1) issue(1, 1);
+      if (n_blocks > 2) issue(2, 2);
+      if (n_blocks > 2)
+        lds_copy_wait<2 * COPIES>();
+      else if (n_blocks > 1)
+        lds_copy_wait<COPIES>();
+      else
+        lds_copy_wait_all();
+      __syncthreads();
+      scores((const char*)smem, ra.s, ra.dp);
+    }
+    int idx = 0;
+    for (; idx + 4 <= n_blocks; idx += 4) {
+      step(idx, Slot<0>{}, ra, rb);
+      step(idx + 1, Slot<1>{}, rb, ra);
+      step(idx + 2, Slot<2>{}, ra, rb);
+      step(idx + 3, Slot<3>{}, rb, ra);
+    }
+    if (idx < n_blocks) step(idx, Slot<0>{}, ra, rb);
+    if (idx + 1 < n_blocks) step(idx + 1, Slot<1>{}, rb, ra);
+    if (idx + 2 < n_blocks) step(idx + 2, Slot<2>{}, ra, rb);
   }
-  int idx = 0;
-  for (; idx + 4 <= n_blocks; idx += 4) {
-    step(idx, Slot<0>{}, ra, rb);
-    step(idx + 1, Slot<1>{}, rb, ra);
-    step(idx + 2, Slot<2>{}, ra, rb);
-    step(idx + 3, Slot<3>{}, rb, ra);
-  }
-  if (idx < n_blocks) step(idx, Slot<0>{}, ra, rb);
-  if (idx + 1 < n_blocks) step(idx + 1, Slot<1>{}, rb, ra);
-  if (idx + 2 < n_blocks) step(idx + 2, Slot<2>{}, ra, rb);
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds d = 32mb + 8(r/4) + 4g + r%4
   if (key < S_k) {
@@ -501,6 +547,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
 // XCD busy (measured: the order moves the time by a few percent at most).
 constexpr int kDqGroupMax = 8;
 constexpr int kKvGroupMax = 2;
+// workgroups from which the dK/dV pass takes its two-wave form at d = 128
+// (four per resident slot of that form: 256 CUs x 2)
+constexpr int kKlDsMinWorkgroups = 2048;
 // XCD blocking of `units` (see grid_order): a multiple of 8 units is split
 // into 8 contiguous blocks taken in groups of up to `group_max`.
 void plan_order(int units, int group_max, int& per, int& group) {
@@ -525,7 +574,20 @@ hipError_t launch_bwd_d(const BwdParams& p_in, hipStream_t stream) {
   if (p.S_k > 0) {
     // with no query row every key gradient is zero; the kernel still writes them
     const int n_kt = (p.S_k + kBwdKRows - 1) / kBwdKRows;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(n_kt * p.A_kv * p.B), dim3(kThreads), 0, stream, p, n_kt);
+    const int n_wg = n_kt * p.A_kv * p.B;
+    // The K-in-LDS form doubles the resident workgroups but halves what one
+    // of them gets of its SIMD.  Causal key tiles differ in length (the first
+    // sees every query row), so with few workgroups per slot the longest one
+    // sets the time and the one-wave form is faster (GQA B=1 S=8192: 512
+    // workgroups); with several per slot the two-wave form wins (MHA B=4
+    // S=2048: 2048 workgroups, +18%).
+    bool two_wave = false;
+    if constexpr (D == 128) two_wave = n_wg >= kKlDsMinWorkgroups;
+    if (two_wave) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
+    }
   }
   return hipGetLastError();
 }

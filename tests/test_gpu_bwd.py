@@ -34,7 +34,7 @@ def orc():
     return oracle.default()
 
 
-def run_bwd(ea, p, dout, q_keep=None, k_keep=None):
+def run_bwd(ea, p, dout, q_keep=None, k_keep=None, window=None):
     """GPU forward then backward; returns (dq, dk, dv) as float64 arrays."""
     t = gu.torch()
     q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
@@ -43,12 +43,13 @@ def run_bwd(ea, p, dout, q_keep=None, k_keep=None):
     lse = t.empty((p.B, p.A, p.S_q), dtype=t.float32, device="cuda")
     qk = None if q_keep is None else gu.dev(q_keep, "u8")
     kk = None if k_keep is None else gu.dev(k_keep, "u8")
-    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk)
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk, window=window)
     dq, dk, dv = (gu.empty_out(x.shape, "bf16") for x in (q, k, v))
     for x in (dq, dk, dv):
         x.fill_(float("nan"))
     ws = t.empty(max(ea.attn_bwd_workspace_bytes(p.B, p.A, p.S_q), 1), dtype=t.uint8, device="cuda")
-    ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk)
+    ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk,
+                window=window)
     t.cuda.synchronize()
     return gu.host_f64(dq), gu.host_f64(dk), gu.host_f64(dv)
 
@@ -230,3 +231,48 @@ def test_bwd_window(ea, orc, case):
               "dk_max": float(np.abs(got[1]).max())})
         return
     _say(compare(got, ref, str(case), vis, A, A_kv))
+
+
+# Grids of at least 2048 dK/dV workgroups (key tiles x KV heads x batch) at
+# d = 128 run the form of the dK/dV pass that keeps the workgroup's K rows in
+# LDS; these cases give it ragged key tiles, keep masks, GQA sums and both
+# window shapes, checked on sampled (batch, KV head) slices.
+MANY_WG_CASES = [
+    # B, A, A_kv, S_q, S_k, causal, window, masked
+    (4, 256, 256, 200, 200, True, None, True),         # 2 key tiles (one ragged): 2048 workgroups
+    (4, 512, 256, 300, 300, True, (100, -1), False),   # GQA 2:1, 3 key tiles: 3072
+    (4, 128, 128, 130, 390, False, (40, 90), False),   # 4 key tiles: 2048
+]
+
+
+@pytest.mark.parametrize("case", MANY_WG_CASES, ids=["mha-masks", "gqa-window", "noncausal-window"])
+def test_bwd_many_workgroups_sampled(ea, orc, case):
+    B, A, A_kv, S_q, S_k, causal, window, masked = case
+    _say("bwd many workgroups", case)
+    seed = 900 + S_q + A
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, 128, dtype="bf16", causal=causal, seed=seed,
+                       q_masked=20 if masked else 0, k_masked=40 if masked else 0)
+    dout = gen.make_dout(p, seed)
+    q_keep = p.q_keep if masked else None
+    k_keep = p.k_keep if masked else None
+    dq, dk, dv = run_bwd(ea, p, dout, q_keep=q_keep, k_keep=k_keep, window=window)
+    for x in (dq, dk, dv):
+        assert np.all(np.isfinite(x))
+    mk = None
+    vis = visibility(B, S_q, S_k, causal, q_keep, k_keep)
+    if window is not None:
+        mk = oracle.window_keep(B, S_q, S_k, window[0], 0 if causal else window[1])
+        vis &= mk != 0
+    G = A // A_kv
+    rng = np.random.default_rng(seed)
+    picks = [(0, 0), (B - 1, A_kv - 1), (int(rng.integers(B)), int(rng.integers(A_kv)))]
+    for b, hk in picks:
+        (qs, ks, vs), hs = _slice(p, b, hk)
+        kw = {}
+        if masked:
+            kw.update(q_keep=q_keep[b:b + 1], k_keep=k_keep[b:b + 1])
+        if mk is not None:
+            kw.update(m_keep=mk[b:b + 1])
+        ref = orc.attn_bwd(qs, ks, vs, dout[b:b + 1, hs], dtype="bf16", scale=p.scale, causal=causal, **kw)
+        got = (dq[b:b + 1, hs], dk[b:b + 1, hk:hk + 1], dv[b:b + 1, hk:hk + 1])
+        _say("slice", (b, hk), compare(got, ref, f"{case} slice {(b, hk)}", vis[b:b + 1], G, 1))
