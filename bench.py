@@ -222,7 +222,7 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
         "decode_split": lambda k: "decode_split_kernel" in k,
         "decode_merge": lambda k: "decode_merge_kernel" in k,
         "bwd_dq": lambda k: "bwd_dq_kernel<128>" in k,
-        "bwd_dkdv": lambda k: "bwd_dkdv_kernel<128>" in k,
+        "bwd_dkdv": lambda k: "bwd_dkdv_kernel<128," in k,
     }
     rows, rec = [], {}
     for part, pred in kernels.items():
@@ -277,7 +277,7 @@ def counter_summary(d: str):
                 span[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     kernels = {"prefill": "prefill_bf16_kernel<128, false, false, false>", "varlen": "prefill_bf16_kernel<64, true, false, false>",
                "decode_split": "decode_split_kernel", "bwd_dq": "bwd_dq_kernel<128>",
-               "bwd_dkdv": "bwd_dkdv_kernel<128>"}
+               "bwd_dkdv": "bwd_dkdv_kernel<128,"}
     print("# Matrix-core utilisation per launch (SQ / GRBM counters)\n")
     print("Commands (repository root, one MI355X):\n")
     print("    rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
@@ -496,7 +496,7 @@ def bench_backward(w, steps: int, warmup: int) -> dict:
             "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5),
             "flops": flops,
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 (the prefill workload)",
-            "kernels": "bwd_dq_kernel<128> then bwd_dkdv_kernel<128> (one call)"}
+            "kernels": "bwd_dq_kernel<128> then bwd_dkdv_kernel<128, true> (K rows in LDS; one call)"}
 
 
 def window_pairs(S: int, left: int) -> int:
