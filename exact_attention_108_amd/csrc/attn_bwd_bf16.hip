@@ -27,12 +27,13 @@
 //      of 32 keys, streaming 32-row blocks of Q, dO and the row
 //      statistics of every query head that reads this KV head (this is the GQA
 //      sum), one key per lane:
-//        S = Q . K^T,  dP = dO . V^T  (K and V rows resident),
+//        S = Q . K^T,  dP = dO . V^T  (V rows in registers; K rows in
+//                                      registers, or in LDS for the two-wave
+//                                      form at d = 128),
 //        dV^T += dO^T . P,  dK^T += Q^T . dS  (transposing reads of Q, dO).
 // The per-element predicate (sliding window whose right edge is the causal
 // bottom-right diagonal, keep masks, rows and keys past the ends) is the
-// forward's; rows whose LSE is -inf (fully
-// masked) take no part.
+// forward's; rows whose LSE is -inf (fully masked) take no part.
 #include <type_traits>
 
 #include "attn_bwd.h"
