@@ -77,11 +77,38 @@ def to_dev(x, kind):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+def code_text(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so that
+    an edit of comments or layout leaves the hash of the code unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # string or character literal, copied whole
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(part: str) -> str:
+    """Hash of the code (comments and layout excluded) of the sources that
+    determine `part`'s kernels."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[part]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
