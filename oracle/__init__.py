@@ -50,7 +50,7 @@ class Oracle:
         self.lib = ctypes.CDLL(lib_path)
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         self.lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                             vp, vp, vp, vp, i64, vp, vp]
+                                             vp, vp, vp, vp, i32, vp, i64, vp, vp]
         self.lib.oracle_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32,
                                                     i32, vp, vp, vp, i64, vp, vp]
         self.lib.oracle_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -82,9 +82,12 @@ class Oracle:
         r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
         return r, r.size
 
-    def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None, rows=None):
+    def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None, bias=None,
+                 rows=None):
         """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d]; m_keep an
-        optional dense keep matrix [B,S_q,S_k] (see window_keep).
+        optional dense keep matrix [B,S_q,S_k] (see window_keep); bias an optional
+        dense additive term M, fp32 [B,1,S_q,S_k] (every head) or [B,A,S_q,S_k],
+        finite or -inf.
 
         Returns (o, lse): o [B,A,S_q,d] / lse [B,A,S_q] in fp64, or [n,d] / [n]
         for the flattened row ids ``rows`` = (b*A + h)*S_q + i.
@@ -101,13 +104,19 @@ class Oracle:
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
         mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
+        bh = 0
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+            if bias.ndim != 4 or bias.shape[0] != B or bias.shape[1] not in (1, A) or bias.shape[2:] != (S_q, S_k):
+                raise ValueError("bias must be [B, 1 or A, S_q, S_k]")
+            bh = bias.shape[1]
         r, n = self._rows(rows)
         n_out = B * A * S_q if r is None else n
         o = np.empty((n_out, d), dtype=np.float64)
         lse = np.empty(n_out, dtype=np.float64)
         rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, A, A_kv, S_q, S_k, d,
-                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(r), n,
-                                      _ptr(o), _ptr(lse))
+                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(bias),
+                                      bh, _ptr(r), n, _ptr(o), _ptr(lse))
         if rc != 0:
             raise ValueError("oracle_attn_fwd rejected its arguments")
         if r is None:

@@ -7,7 +7,7 @@
  * What it computes (page "Attention Kernel", section "问题与成本", the
  * definition P = softmax(QK^T/sqrt(d_h) + M), O = PV):
  *
- *   s_ij  = scale * sum_e q_ie k_je  (+ M_ij, M_ij in {0, -inf})
+ *   s_ij  = scale * sum_e q_ie k_je + M_ij   (M_ij finite or -inf)
  *   m_i   = max_j s_ij
  *   l_i   = sum_j exp(s_ij - m_i)                 (safe softmax, page
  *                                                  "Attention 算子加速史", 1.2)
@@ -20,7 +20,10 @@
  * "Attention 算子加速史", 1.1, steps 1-3).  Arithmetic is fp64 throughout; the
  * inputs (fp32 values or bf16 bits) are widened exactly.
  *
- * Mask M_ij = -inf when any of:
+ * M_ij is the sum of an optional dense additive term bias[i][j] (dense
+ * prefill only: any finite value or -inf, e.g. a relative-position bias, or
+ * 0 / -inf for an arbitrary pattern -- page "Attention Kernel", section
+ * "可编程 mask", general dense M) and of -inf when any of:
  *   - causal and j > i + (S_k - S_q)   (query i sits at absolute position
  *                                       S_k - S_q + i: bottom-right alignment)
  *   - q_keep[i] == 0  or  k_keep[j] == 0
@@ -90,8 +93,8 @@ static double ld(const void *p, int64_t idx, int dt)
  * s, p: scratch of n doubles (the materialised score and probability rows).
  */
 static void attend_row(const void *q, int64_t q_off, const void *k, const void *v, int dt,
-                       const int64_t *kv_off, const unsigned char *vis, int64_t n, int d,
-                       double scale, double *s, double *p, double *o, double *lse)
+                       const int64_t *kv_off, const unsigned char *vis, const float *bias_row,
+                       int64_t n, int d, double scale, double *s, double *p, double *o, double *lse)
 {
     double m = -INFINITY;
     for (int64_t j = 0; j < n; ++j) {
@@ -102,6 +105,8 @@ static void attend_row(const void *q, int64_t q_off, const void *k, const void *
             for (int e = 0; e < d; ++e)
                 dot += ld(q, q_off + e, dt) * ld(k, kv_off[j] + e, dt);
             s[j] = scale * dot;
+            if (bias_row)
+                s[j] += (double)bias_row[j];
         }
         if (s[j] > m)
             m = s[j];
@@ -156,16 +161,20 @@ static void scratch_free(struct scratch *w)
 /*
  * Batched prefill.  q, o: [B, A, S_q, d]; k, v: [B, A_kv, S_k, d];
  * q_keep: [B, S_q] or NULL; k_keep: [B, S_k] or NULL; m_keep: [B, S_q, S_k]
- * or NULL (shared by every head).
+ * or NULL (shared by every head); bias: [B, bias_heads, S_q, S_k] fp32 or
+ * NULL, bias_heads 1 (shared by every head) or A.
  * rows: flattened row ids (b*A + h)*S_q + i to compute, or NULL for all rows
  * in order.  o receives [n_rows, d] doubles, lse [n_rows].
  */
 int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
                     int B, int A, int A_kv, int S_q, int S_k, int d, float scale, int causal,
                     const uint8_t *q_keep, const uint8_t *k_keep, const uint8_t *m_keep,
+                    const float *bias, int bias_heads,
                     const int64_t *rows, int64_t n_rows, double *o, double *lse)
 {
     if (B <= 0 || A <= 0 || A_kv <= 0 || S_q < 0 || S_k < 0 || d <= 0 || A % A_kv != 0)
+        return -1;
+    if (bias && bias_heads != 1 && bias_heads != A)
         return -1;
     if (!dt_ok(dt))
         return -1;
@@ -204,7 +213,9 @@ int oracle_attn_fwd(const void *q, const void *k, const void *v, int dt,
                     visible = 0;
                 w.vis[j] = (unsigned char)visible;
             }
-            attend_row(q, id * d, k, v, dt, w.off, w.vis, S_k, d, (double)scale, w.s, w.p,
+            const float *bias_row =
+                bias ? bias + (((int64_t)b * bias_heads + (bias_heads == 1 ? 0 : h)) * S_q + i) * S_k : NULL;
+            attend_row(q, id * d, k, v, dt, w.off, w.vis, bias_row, S_k, d, (double)scale, w.s, w.p,
                        o + r * d, lse + r);
         }
         if (bad) {
@@ -271,7 +282,7 @@ int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *do_
                         w.vis[j] = (unsigned char)visible;
                     }
                     double lse;
-                    attend_row(q, id * d, k, v, dt, w.off, w.vis, S_k, d, sc, w.s, w.p, o, &lse);
+                    attend_row(q, id * d, k, v, dt, w.off, w.vis, NULL, S_k, d, sc, w.s, w.p, o, &lse);
                     if (lse == -INFINITY)
                         continue;  /* fully masked row: no gradient anywhere */
                     double D = 0.0;
@@ -372,7 +383,7 @@ int oracle_attn_fwd_varlen(const void *q, const void *k, const void *v, int dt,
                     visible = 0;
                 w.vis[j] = (unsigned char)visible;
             }
-            attend_row(q, id * d, k, v, dt, w.off, w.vis, len, d, (double)scale, w.s, w.p,
+            attend_row(q, id * d, k, v, dt, w.off, w.vis, NULL, len, d, (double)scale, w.s, w.p,
                        o + r * d, lse + r);
         }
         if (bad) {
@@ -440,7 +451,7 @@ int oracle_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                 w.off[t] = ((page * page_size + off) * A_kv + hk) * (int64_t)d;
                 w.vis[t] = 1;
             }
-            attend_row(q, id * d, k_cache, v_cache, dt, w.off, w.vis, n, d, (double)scale,
+            attend_row(q, id * d, k_cache, v_cache, dt, w.off, w.vis, NULL, n, d, (double)scale,
                        w.s, w.p, o + r * d, lse + r);
         }
         if (bad) {

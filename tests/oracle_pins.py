@@ -453,6 +453,100 @@ def pin_dense_keep_matches_flag_masks(orc):
     assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
 
 
+# ---- general dense M (page "Attention Kernel", section "可编程 mask"; the
+# definition P = softmax(Q K^T / sqrt(d_h) + M) of section "问题与成本"): an
+# additive fp32 term per (row, key), finite or -inf
+
+def _brute_bias(q, k, v, scale, bias_row, vis):
+    """Pure-Python softmax attention for one row with an additive term."""
+    s = [scale * math.fsum(a * b for a, b in zip(q, kj)) + mj if ok else -math.inf
+         for kj, mj, ok in zip(k, bias_row, vis)]
+    m = max(s) if s else -math.inf
+    if m == -math.inf:
+        return [0.0] * len(q), -math.inf
+    w = [math.exp(x - m) if x != -math.inf else 0.0 for x in s]
+    lsum = math.fsum(w)
+    out = [math.fsum(wj * vj[e] for wj, vj in zip(w, v)) / lsum for e in range(len(v[0]))]
+    return out, m + math.log(lsum)
+
+
+def pin_bias_brute_force(orc):
+    rng = np.random.default_rng(61)
+    for S_q, S_k, d, A, A_kv, causal, heads in [(4, 6, 3, 2, 1, True, 1), (5, 5, 2, 2, 2, False, 2),
+                                                (3, 7, 2, 4, 2, True, 4)]:
+        q = _f32(rng.standard_normal((2, A, S_q, d)))
+        k = _f32(rng.standard_normal((2, A_kv, S_k, d)))
+        v = _f32(rng.standard_normal((2, A_kv, S_k, d)))
+        bias = _f32(3.0 * rng.standard_normal((2, heads, S_q, S_k)))
+        bias[rng.random(bias.shape) < 0.25] = -np.inf
+        bias[1, 0, 0, :] = -np.inf  # a row with every key masked by the term alone
+        kk = (rng.random((2, S_k)) > 0.2).astype(np.uint8)
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.625, causal=causal, k_keep=kk, bias=bias)
+        G = A // A_kv
+        for b in range(2):
+            for h in range(A):
+                for i in range(S_q):
+                    vis = [bool(kk[b, j]) and (not causal or j <= i + S_k - S_q) for j in range(S_k)]
+                    row = [float(x) for x in bias[b, h if heads > 1 else 0, i]]
+                    want, wl = _brute_bias([float(x) for x in q[b, h, i]],
+                                           [[float(x) for x in r] for r in k[b, h // G]],
+                                           [[float(x) for x in r] for r in v[b, h // G]], 0.625, row, vis)
+                    assert np.allclose(o[b, h, i], want, rtol=0, atol=1e-13), (S_q, S_k, b, h, i)
+                    assert (wl == -math.inf and lse[b, h, i] == -np.inf) or abs(lse[b, h, i] - wl) < 1e-13
+
+
+def pin_bias_zero_and_keep(orc):
+    """M = 0 is no mask, and M in {0, -inf} is the keep matrix of the same
+    pattern, bit for bit."""
+    rng = np.random.default_rng(62)
+    B, A, A_kv, S_q, S_k, d = 2, 2, 1, 5, 6, 3
+    q = _f32(rng.standard_normal((B, A, S_q, d)))
+    k = _f32(rng.standard_normal((B, A_kv, S_k, d)))
+    v = _f32(rng.standard_normal((B, A_kv, S_k, d)))
+    o0, l0 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=True)
+    o1, l1 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=True, bias=np.zeros((B, 1, S_q, S_k), np.float32))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    mk = (rng.random((B, S_q, S_k)) > 0.4).astype(np.uint8)
+    o2, l2 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, m_keep=mk)
+    bias = np.where(mk[:, None] != 0, 0.0, -np.inf).astype(np.float32)
+    o3, l3 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, bias=bias)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+
+
+def pin_bias_row_shift(orc):
+    """Softmax ignores a constant added to a whole row: O is unchanged and the
+    log-sum-exp moves by exactly that constant."""
+    rng = np.random.default_rng(63)
+    B, A, S_q, S_k, d = 2, 3, 4, 9, 5
+    q = _f32(rng.standard_normal((B, A, S_q, d)))
+    k = _f32(rng.standard_normal((B, A, S_k, d)))
+    v = _f32(rng.standard_normal((B, A, S_k, d)))
+    c = _f32(rng.uniform(-20, 20, (B, A, S_q, 1)))
+    o0, l0 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.4)
+    o1, l1 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.4, bias=np.broadcast_to(c, (B, A, S_q, S_k)))
+    assert np.allclose(o0, o1, rtol=0, atol=1e-12)
+    assert np.allclose(l1 - l0, c[..., 0].astype(np.float64), rtol=0, atol=1e-12)
+
+
+def pin_bias_log_weights(orc):
+    """M = ln w weights each key's exponential by w: O_i = sum_j w_ij e^{s_ij} v_j
+    / sum_j w_ij e^{s_ij}, evaluated directly in numpy."""
+    rng = np.random.default_rng(64)
+    B, A, S_q, S_k, d, scale = 1, 2, 3, 8, 4, 0.7
+    q = _f32(rng.standard_normal((B, A, S_q, d)))
+    k = _f32(rng.standard_normal((B, A, S_k, d)))
+    v = _f32(rng.standard_normal((B, A, S_k, d)))
+    w = _f32(rng.uniform(0.05, 4.0, (B, A, S_q, S_k)))
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=scale, bias=np.log(w.astype(np.float64)).astype(np.float32))
+    lw = np.log(w.astype(np.float64)).astype(np.float32).astype(np.float64)  # the term as the oracle reads it
+    sc = float(np.float32(scale))  # the scale is an fp32 argument
+    s = sc * np.einsum("bhid,bhjd->bhij", q.astype(np.float64), k.astype(np.float64))
+    e = np.exp(s) * np.exp(lw)
+    want = np.einsum("bhij,bhjd->bhid", e, v.astype(np.float64)) / e.sum(-1, keepdims=True)
+    assert np.allclose(o, want, rtol=0, atol=1e-12)
+    assert np.allclose(lse, np.log(e.sum(-1)), rtol=0, atol=1e-12)
+
+
 def pin_window_equals_key_slice(orc):
     """A sliding-window row equals plain attention over the contiguous slice of
     keys the window keeps (same keys in the same order: bit for bit); a row

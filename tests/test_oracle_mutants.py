@@ -48,6 +48,11 @@ MUTANTS = [
     ("keep matrix transposed (dense)", "m_keep[((int64_t)b * S_q + i) * S_k + j]",
      "m_keep[((int64_t)b * S_k + j) * S_q + i]", 1),
     ("gradient: keep matrix ignored", "if (m_keep && !m_keep[((int64_t)b * S_q + i) * S_k + j])", "if (0)", 2),
+    ("additive term scaled by the softmax scale", "s[j] += (double)bias_row[j];",
+     "s[j] += scale * (double)bias_row[j];", 0),
+    ("additive term subtracted", "s[j] += (double)bias_row[j];", "s[j] -= (double)bias_row[j];", 0),
+    ("additive term: head ignored", "(bias_heads == 1 ? 0 : h)", "0", 0),
+    ("additive term: row ignored", "* S_q + i) * S_k : NULL;", "* S_q + 0) * S_k : NULL;", 0),
 ]
 
 BATTERY = r"""
