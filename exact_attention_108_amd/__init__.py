@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     LIB_PATH,
     attn_abi_version,
+    attn_block_keep_from_bias,
     attn_bwd,
     attn_bwd_workspace_bytes,
     attn_decode_paged,
@@ -21,4 +22,5 @@ from ._binding import (  # noqa: F401
     attn_prefill_paged,
     attn_status_string,
     exported_symbols,
+    pad_bias,
 )

@@ -25,7 +25,8 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 class _Mask(ctypes.Structure):
     _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p), ("block_keep", ctypes.c_void_p),
-                ("block_heads", ctypes.c_int)]
+                ("block_heads", ctypes.c_int), ("bias", ctypes.c_void_p), ("bias_heads", ctypes.c_int),
+                ("bias_ld", ctypes.c_int)]
 
 
 class _Window(ctypes.Structure):
@@ -60,6 +61,8 @@ _lib.attn_status_string.argtypes = [_i]
 _lib.attn_status_string.restype = ctypes.c_char_p
 _lib.attn_abi_version.argtypes = []
 _lib.attn_abi_version.restype = _i
+_lib.attn_block_keep_from_bias.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
+_lib.attn_block_keep_from_bias.restype = _i
 
 
 class AttnError(RuntimeError):
@@ -80,7 +83,7 @@ def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
-            "attn_status_string", "attn_abi_version"]
+            "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
 
 
 def _torch():
@@ -105,6 +108,13 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
 
 
+def _view_ptr(t):
+    """Data pointer of a strided view whose layout the caller has checked."""
+    if t is None or t.numel() == 0:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _dev(*ts):
     dev = None
     for t in ts:
@@ -126,15 +136,35 @@ def _stream(stream, dev):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _mask(q_keep, k_keep, block_keep=None):
+def _bias_view(bias, B, A, S_q, S_k):
+    """(heads, row stride) of a dense additive mask: an fp32 [B, 1 or A, S_q, S_k]
+    tensor whose rows are unit-stride and ld elements apart (ld a multiple of
+    4, e.g. a [..., :S_k] slice of a padded tensor) and whose heads and batch
+    rows are packed at that stride."""
+    torch = _torch()
+    if bias.dtype != torch.float32 or bias.dim() != 4:
+        raise ValueError("bias must be fp32 [B, 1 or A, S_q, S_k]")
+    if bias.shape[0] != B or bias.shape[1] not in (1, A) or tuple(bias.shape[2:]) != (S_q, S_k):
+        raise ValueError("bias must be [B, 1 or A, S_q, S_k]")
+    heads = int(bias.shape[1])
+    ld = int(bias.stride(2))
+    if (S_k > 1 and bias.stride(3) != 1) or ld % 4 or ld < S_k:
+        raise ValueError("bias rows must be unit-stride, ld >= S_k apart with ld a multiple of 4")
+    if (heads > 1 and bias.stride(1) != S_q * ld) or (B > 1 and bias.stride(0) != heads * S_q * ld):
+        raise ValueError("bias heads and batch rows must be packed at the row stride")
+    return heads, ld
+
+
+def _mask(q_keep, k_keep, block_keep=None, bias=None, bias_heads=0, bias_ld=0):
     torch = _torch()
     for t in (q_keep, k_keep, block_keep):
         if t is not None and t.dtype != torch.uint8:
             raise ValueError("keep-masks must be uint8")
-    if q_keep is None and k_keep is None and block_keep is None:
+    if q_keep is None and k_keep is None and block_keep is None and bias is None:
         return None
     heads = 0 if block_keep is None else int(block_keep.shape[1])
-    return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep), _ptr(block_keep), heads))
+    return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep), _ptr(block_keep), heads, _view_ptr(bias), bias_heads,
+                             bias_ld))
 
 
 def _window(window):
@@ -151,10 +181,12 @@ def _check(status: int, where: str) -> None:
 
 
 def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None, k_keep=None, window=None,
-             block_keep=None, stream=None):
+             block_keep=None, bias=None, stream=None):
     """O, LSE of softmax(Q K^T * scale + M) V.  q/o [B,A,S_q,d], k/v [B,A_kv,S_k,d], lse [B,A,S_q] fp32;
     window = (left, right) sliding window around each query's position, -1 = unbounded side;
-    block_keep = uint8 [B, 1 or A, ceil(S_q/128), ceil(S_k/128)] block mask (bf16 only)."""
+    block_keep = uint8 [B, 1 or A, ceil(S_q/128), ceil(S_k/128)] block mask (bf16 only);
+    bias = the dense additive term M, fp32 [B, 1 or A, S_q, S_k] (finite or -inf; rows unit-stride and
+    a multiple of 4 elements apart, see pad_bias)."""
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, heads, S, d]")
@@ -174,11 +206,41 @@ def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None
                                    block_keep.shape[1] not in (1, A) or
                                    tuple(block_keep.shape[2:]) != ((S_q + 127) // 128, (S_k + 127) // 128)):
         raise ValueError("block_keep must be [B, 1 or A, ceil(S_q/128), ceil(S_k/128)]")
-    dev = _dev(q, k, v, o, lse, q_keep, k_keep, block_keep)
+    bh, ld = _bias_view(bias, B, A, S_q, S_k) if bias is not None else (0, 0)
+    dev = _dev(q, k, v, o, lse, q_keep, k_keep, block_keep, bias)
     st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, A, A_kv, S_q, S_k, d, float(scale),
-                       int(bool(causal)), _mask(q_keep, k_keep, block_keep), _window(window), _dtype_code(q),
-                       _stream(stream, dev))
+                       int(bool(causal)), _mask(q_keep, k_keep, block_keep, bias, bh, ld), _window(window),
+                       _dtype_code(q), _stream(stream, dev))
     _check(st, "attn_fwd")
+
+
+def pad_bias(bias):
+    """An fp32 [B, H, S_q, S_k] tensor as the [..., :S_k] view of a zero-padded copy whose rows are a
+    multiple of 4 elements long (the layout attn_fwd and attn_block_keep_from_bias read)."""
+    torch = _torch()
+    B, H, S_q, S_k = bias.shape
+    ld = max(4, (S_k + 3) // 4 * 4)
+    out = torch.zeros((B, H, S_q, ld), dtype=torch.float32, device=bias.device)
+    out[..., :S_k] = bias
+    return out[..., :S_k]
+
+
+def attn_block_keep_from_bias(bias, block_keep, *, stream=None):
+    """block_keep uint8 [B, H, ceil(S_q/128), ceil(S_k/128)] = whether each 128 x 128 block of the fp32
+    bias [B, H, S_q, S_k] (layout as attn_fwd's bias) holds an entry greater than -inf."""
+    torch = _torch()
+    if bias.dim() != 4:
+        raise ValueError("bias must be [B, H, S_q, S_k]")
+    B, H, S_q, S_k = bias.shape
+    bh, ld = _bias_view(bias, B, H, S_q, S_k)
+    if block_keep.dtype != torch.uint8 or tuple(block_keep.shape) != (B, bh, (S_q + 127) // 128,
+                                                                      (S_k + 127) // 128):
+        raise ValueError("block_keep must be uint8 [B, H, ceil(S_q/128), ceil(S_k/128)]")
+    if not block_keep.is_contiguous():
+        raise ValueError("block_keep must be contiguous")
+    dev = _dev(bias, block_keep)
+    st = _lib.attn_block_keep_from_bias(_view_ptr(bias), B, bh, S_q, S_k, ld, _ptr(block_keep), _stream(stream, dev))
+    _check(st, "attn_block_keep_from_bias")
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: float, causal: bool = True,

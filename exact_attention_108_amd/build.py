@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libattn_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_prefill_bf16.hip", "attn_prefill_f32.hip", "attn_decode_bf16.hip", "attn_bwd_bf16.hip",
+SOURCES = ["attn_prefill_bf16.hip", "attn_prefill_f32.hip", "attn_decode_bf16.hip", "attn_bwd_bf16.hip", "attn_bias.hip",
            "attn_api.cpp"]
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -54,6 +54,16 @@ attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   return p;
 }
 
+// a dense additive mask the kernels can read: [B, heads, S_q, ld] fp32 with
+// ld >= S_k a multiple of 4 and 16-byte rows (the kernels load 4 keys at once)
+bool valid_bias(const float* bias, int heads, int A, int S_q, int S_k, int ld) {
+  if (heads != 1 && heads != A) return false;
+  if (ld < S_k || ld < 1 || ld % 4 != 0) return false;
+  if (((uintptr_t)bias & 15u) != 0) return false;
+  (void)S_q;
+  return true;
+}
+
 // dtype / head-dim combinations the kernels are built for
 attn_status check_prefill_support(attn_dtype dtype, int d_h) {
   if (dtype == ATTN_BF16) return (d_h == 64 || d_h == 128) ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
@@ -79,6 +89,8 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
     if (mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
     if (dtype != ATTN_BF16 || S_k > 262144) return ATTN_ERR_UNSUPPORTED;
   }
+  const bool bias = mask && mask->bias;
+  if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
   if (S_q == 0) return ATTN_OK;
   const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
   const long long n_qt = (S_q + rows - 1) / rows;
@@ -96,10 +108,27 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
     p.block_heads = mask->block_heads;
     p.n_kb = (S_k + 127) / 128;
   }
+  if (bias) {
+    p.bias = mask->bias;
+    p.bias_heads = mask->bias_heads;
+    p.bias_ld = mask->bias_ld;
+    p.inv_scale = (float)(1.0 / (double)scale);
+  }
   attn::plan_dense_order(p);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, false, st) : attn::launch_prefill_f32(p, false, st);
   return launch_status(e);
+}
+
+ATTN_EXPORT attn_status attn_block_keep_from_bias(const float* bias, int B, int bias_heads, int S_q, int S_k,
+                                                  int bias_ld, uint8_t* block_keep, void* stream) {
+  if (B < 1 || S_q < 0 || S_k < 0 || bias_heads < 1) return ATTN_ERR_INVAL;
+  if (!bias || !block_keep || !valid_bias(bias, bias_heads, bias_heads, S_q, S_k, bias_ld)) return ATTN_ERR_INVAL;
+  if (S_q == 0 || S_k == 0) return ATTN_OK;  // the block mask is empty
+  const long long n_qb = (S_q + 127) / 128, n_kb = (S_k + 127) / 128;
+  if ((long long)B * bias_heads * n_qb > INT_MAX || n_kb > 65535) return ATTN_ERR_UNSUPPORTED;
+  return launch_status(attn::launch_block_keep_from_bias(bias, B, bias_heads, S_q, S_k, bias_ld, block_keep,
+                                                         (hipStream_t)stream));
 }
 
 ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -115,7 +144,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   for (int s = 0; s < n_seq; ++s)
     if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return ATTN_ERR_INVAL;
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse)) return ATTN_ERR_INVAL;
-  if (mask && mask->block_keep) return ATTN_ERR_UNSUPPORTED;  // block masks: dense attn_fwd only
+  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // dense attn_fwd only
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
   if (total_tokens == 0) return ATTN_OK;
@@ -296,7 +325,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(t)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
-  if (mask && mask->block_keep) return ATTN_ERR_UNSUPPORTED;  // block masks: forward only
+  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // forward only
   if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
     return ATTN_ERR_UNSUPPORTED;
   const long long n_qt = (S_q + attn::kBwdQRows - 1) / attn::kBwdQRows;

@@ -44,6 +44,12 @@ struct FwdParams {
   // rows qb*128.. and keys kb*128.. is computed at all; n_kb = ceil(S_k / 128)
   const uint8_t* block_keep;
   int block_heads, n_kb;
+  // dense additive mask (dense prefill): bias[((b * bias_heads + hm) * S_q +
+  // i) * bias_ld + j] is added to scale * q_i . k_j (hm = 0 when bias_heads
+  // == 1, else the head); inv_scale = 1 / scale
+  const float* bias;
+  int bias_heads, bias_ld;
+  float inv_scale;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin
@@ -86,6 +92,10 @@ hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stre
 hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream);
 // fp32 prefill (1 <= d <= 128).
 hipError_t launch_prefill_f32(const FwdParams& p, bool varlen, hipStream_t stream);
+// block_keep[b][h][qb][kb] = whether some bias entry of the 128 x 128 block is
+// greater than -inf (n_kb <= 65535)
+hipError_t launch_block_keep_from_bias(const float* bias, int B, int heads, int S_q, int S_k, int ld,
+                                       uint8_t* block_keep, hipStream_t stream);
 // query rows per workgroup of the bf16 prefill kernel
 constexpr int kPrefillRows = 128;
 constexpr int kPrefillRowsF32 = 16;

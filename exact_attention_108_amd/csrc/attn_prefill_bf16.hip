@@ -59,13 +59,13 @@ constexpr int kMaxListedTiles = 4096;
 // Waves per SIMD: two at d = 128 (the kernel needs up to 256 VGPRs); three
 // at d = 64, whose accumulators and operands fit the 168-VGPR budget that
 // needs, with three workgroups' 32 KB of tiles in LDS (measured +9% on a
-// causal S = 2048 batch, +16% on ragged varlen batches).  The paged variant
-// stays at two: at three it spills.
-template <int D, bool kPaged>
-constexpr int kWavesPerSimd = (D == 64 && !kPaged) ? 3 : 2;
+// causal S = 2048 batch, +16% on ragged varlen batches).  The paged and
+// dense-additive-mask variants stay at two: at three they spill.
+template <int D, bool kPaged, bool kBias>
+constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias) ? 3 : 2;
 
-template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged>, kWavesPerSimd<D, kPaged>))) void prefill_bf16_kernel(FwdParams p) {
+template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias>, kWavesPerSimd<D, kPaged, kBias>))) void prefill_bf16_kernel(FwdParams p) {
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
   constexpr int MB = D / 32;               // 32-row blocks of O^T
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // after them (the online softmax does not depend on the order).  Logical
   // tile t is physical tile phys(t).
   int j_ul = j_lo, j_uh = j_lo;
-  if (rb.k_keep == nullptr && n_range > 0) {
+  if (rb.k_keep == nullptr && !kBias && n_range > 0) {
     int ul = wl >= 0 ? (max(q_last + off - wl, 0) + kBc - 1) / kBc : 0;
     int uh = S_k / kBc;
     if (wr >= 0) uh = min(uh, max(q_first + off + wr + 1, 0) / kBc);
@@ -341,8 +341,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // per-element predicate of tile t (keys past S_k, the window's edges -- the
   // causal diagonal is its right edge --, the key keep-mask): dead scores
   // become -inf
-  auto mask = [&](f32x16 (&s)[2], int t) {
+  // Dense additive mask: this lane's row of M, and the 32 terms of its keys
+  // in tile t (element (kb, r) of the score tile is key k0 + 32kb + 8(r/4) +
+  // 4g + r%4, so keys come in runs of 4: one 16-byte load per run).  Keys at
+  // or past S_k are not read (their scores are masked below).  The term is
+  // added to the raw product as M / scale, so that the base-2 scaling by
+  // scale * log2(e) applies to both.
+  [[maybe_unused]] const float* brow = nullptr;
+  if constexpr (kBias) {
+    const int hm = p.bias_heads == 1 ? 0 : rb.h;
+    brow = p.bias + ((size_t)(rb.b * p.bias_heads + hm) * S_q + min(qrow, S_q - 1)) * p.bias_ld;
+  }
+  auto bias_load = [&](int t, f32x4 (&m)[2][4]) {
+    if constexpr (kBias) {
+      const int k0 = phys(t) * kBc;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kk = k0 + 32 * kb + 8 * q4 + 4 * g;
+          m[kb][q4] = kk < S_k ? *(const f32x4*)(brow + kk) : f32x4{};
+        }
+      }
+    }
+  };
+  auto mask = [&](f32x16 (&s)[2], int t, const f32x4 (&m)[2][4]) {
     const int k0 = phys(t) * kBc;
+    if constexpr (kBias) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(m[kb][r >> 2][r & 3], p.inv_scale, s[kb][r]);
+      }
+    }
     // bit k of kvalid: key k0 + k exists and is kept (same for every lane)
     bool valid = k0 + lane < S_k;
     if (rb.k_keep) valid = valid && sKeep[t & 1][lane] != 0;
@@ -461,10 +492,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     copy_keep(0);
     copy_keep(1);
+    f32x4 m0[2][4];
+    bias_load(0, m0);
     lds_copy_wait_all();
     __syncthreads();
     qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
-    if (n_mid == 0) mask(s_cur, 0);
+    if (n_mid == 0) mask(s_cur, 0, m0);
     mx_cur = rowmax(s_cur);
   }
 
@@ -521,12 +554,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       // a wave skips the work of a tile none of its rows can see (it still
       // takes part in the copies and barriers)
       const bool has_next = j + 1 < n_tiles && wave_sees(j + 1);
+      f32x4 m_next[2][4];
       if (has_next) {
         qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
       } else {
         issue(0);
         issue(1);
       }
+      if (has_next) bias_load(j + 1, m_next);  // in flight during the softmax and PV of tile j
       if (wave_sees(j)) {
         softmax_pv(buf_tag, s_cur, issue);
       } else {
@@ -534,7 +569,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         issue(3);
       }
       if (has_next) {
-        mask(s_next, j + 1);
+        mask(s_next, j + 1, m_next);
         mx_cur = rowmax(s_next);
         s_cur[0] = s_next[0];
         s_cur[1] = s_next[1];
@@ -605,7 +640,11 @@ hipError_t launch_d(const FwdParams& p, bool varlen, hipStream_t stream) {
     grid = p.n_qt * p.A * p.B;
   }
   if (grid <= 0) return hipSuccess;
-  if (!varlen && p.block_keep) {
+  if (!varlen && p.bias && p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (!varlen && p.bias) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (!varlen && p.block_keep) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else if (varlen) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);

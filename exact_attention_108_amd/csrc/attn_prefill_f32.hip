@@ -7,6 +7,9 @@
 // the division by l happens once at the end.  Scores and products use scalar
 // fp32 FMAs on the vector ALUs, so this path is exact to fp32 rounding.
 //
+// A dense additive mask M (dense batches) enters each score as M / scale
+// before the scaling, i.e. s * scale + M.
+//
 // A workgroup owns 16 query rows; wave w owns rows 4w..4w+3.  In the score
 // step lane j computes the scores of key j of the tile for the wave's 4 rows;
 // in the output step lane j accumulates output dimensions j and j + 64.
@@ -69,6 +72,17 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
   const int j_lo = kbeg / kBc;
   const int j_hi = kend > kbeg ? (kend + kBc - 1) / kBc : j_lo;
 
+  // dense additive mask (dense batches only): row (b, head, i) of M, added to
+  // the raw product as M / scale so that the scaling by scale * log2(e)
+  // applies to both
+  const float* bias_rows = nullptr;
+  if constexpr (!kVarlen) {
+    if (p.bias) {
+      const int hm = p.bias_heads == 1 ? 0 : rb.h;
+      bias_rows = p.bias + (size_t)(rb.b * p.bias_heads + hm) * S_q * p.bias_ld;
+    }
+  }
+
   float m_run[kRowsPerWave], l_run[kRowsPerWave], acc[kRowsPerWave][2];
 #pragma unroll
   for (int rr = 0; rr < kRowsPerWave; ++rr) {
@@ -101,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
       const int row = rb.q0 + qr;
       float s = 0.f;
       for (int e = 0; e < D; ++e) s = fmaf(sQ[qr][e], sK[lane][e], s);
+      if (bias_rows && key < S_k && row < S_q) s = fmaf(bias_rows[(size_t)row * p.bias_ld + key], p.inv_scale, s);
       const bool dead = sKeep[lane] == 0 || (wr >= 0 && key > row + off + wr) || (wl >= 0 && key < row + off - wl);
       s = dead ? -INFINITY : s;
       const float mx = wave_max(s);

@@ -25,11 +25,12 @@
  *     ATTN_F32: q/k/v/o are fp32.  lse is always fp32, natural log.
  *   - GQA: query head h reads KV head h / (A / A_kv) (contiguous groups; page
  *     "Attention Kernel", section "问题与成本", GQA paragraph).
- *   - Mask M_ij in {0, -inf} only.  M_ij = -inf when: causal and
- *     j > i + (S_k - S_q) (bottom-right alignment), q_keep[i] == 0, or
- *     k_keep[j] == 0.  A row with every key masked (including S_k == 0)
- *     returns O = 0 and LSE = -inf (page "Attention Kernel", section
- *     "Online softmax", fully-masked-row contract), never NaN.
+ *   - Mask: M_ij is the optional dense additive term bias[i][j] (attn_fwd
+ *     only, see attn_mask) plus -inf when: causal and j > i + (S_k - S_q)
+ *     (bottom-right alignment), q_keep[i] == 0, k_keep[j] == 0, a window or
+ *     a block mask excludes (i, j).  A row with every key masked (including
+ *     S_k == 0) returns O = 0 and LSE = -inf (page "Attention Kernel",
+ *     section "Online softmax", fully-masked-row contract), never NaN.
  *   - scale must be finite and > 0.  Inputs must be finite.
  *   - Errors are reported before any launch: ATTN_ERR_INVAL for bad
  *     arguments (NULL required pointer, negative size, A % A_kv != 0,
@@ -47,7 +48,7 @@
 #include <stdint.h>
 
 /* The value attn_abi_version() returns for this header. */
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 #ifdef __cplusplus
 extern "C" {
@@ -73,12 +74,29 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * block_heads == 1, else the query head); those key tiles are never loaded.
  * block_heads is 1 or A (ignored when block_keep is NULL).  Requires
  * S_k <= 262144.  attn_fwd_varlen and attn_bwd return ATTN_ERR_UNSUPPORTED
- * for a non-NULL block_keep. */
+ * for a non-NULL block_keep.
+ *
+ * bias (attn_fwd only): the general dense additive mask M of the operation
+ * (page "Attention Kernel", section "可编程 mask"; the term "+ M" of section
+ * "问题与成本").  fp32 [B, bias_heads, S_q, bias_ld], row (b, h', i) holding
+ * M_ij for keys j < S_k (h' = 0 when bias_heads == 1, else the query head).
+ * Rows are read in 16-byte groups, so entries S_k .. bias_ld - 1 of a row
+ * may be read; their values are ignored.  Each entry j < S_k is finite or
+ * -inf (-inf masks the pair; +inf and NaN are contract violations).  The
+ * term is added to scale * q_i . k_j, so it is not multiplied by scale.
+ * Requires bias_heads in {1, A}, bias_ld >= S_k and a multiple of 4, and
+ * bias 16-byte aligned.  It combines with every other mask; key tiles are
+ * skipped only through block_keep, which attn_block_keep_from_bias derives
+ * from a bias.  attn_fwd_varlen and attn_bwd return ATTN_ERR_UNSUPPORTED for
+ * a non-NULL bias. */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
     const uint8_t *block_keep;
     int block_heads;
+    const float *bias;
+    int bias_heads;
+    int bias_ld;
 } attn_mask;
 
 /* Optional sliding window (page "Attention Kernel", section "可编程 mask":
@@ -110,6 +128,19 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                      int B, int A, int A_kv, int S_q, int S_k, int d_h, float scale,
                      int causal, const attn_mask *mask, const attn_window *window,
                      attn_dtype dtype, void *stream);
+
+/*
+ * Block mask of a dense additive mask (page "Attention Kernel", section
+ * "可编程 mask": the block level of a mask decides which tiles are skipped
+ * whole).  Writes block_keep [B, bias_heads, ceil(S_q / 128), ceil(S_k / 128)]
+ * uint8 (device, caller-owned): 1 when some entry bias[b][h'][i][j] with i in
+ * [128 qb, 128 qb + 128) ∩ [0, S_q) and j in [128 kb, 128 kb + 128) ∩ [0, S_k)
+ * is greater than -inf, else 0.  Passed to attn_fwd with the same bias (and
+ * block_heads = bias_heads) it changes no result and skips the key tiles the
+ * bias masks whole.  bias: as in attn_mask.  Asynchronous on stream.
+ */
+attn_status attn_block_keep_from_bias(const float *bias, int B, int bias_heads, int S_q, int S_k, int bias_ld,
+                                      uint8_t *block_keep, void *stream);
 
 /*
  * Packed variable-length prefill (page "Attention Kernel", section

@@ -28,7 +28,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # stream ids, in drawing order
-S_Q, S_K, S_V, S_LENS, S_PERM, S_QKEEP, S_KKEEP, S_DOUT = 0, 1, 2, 3, 4, 5, 6, 7
+S_Q, S_K, S_V, S_LENS, S_PERM, S_QKEEP, S_KKEEP, S_DOUT, S_BIAS = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def _threads() -> int:
@@ -434,3 +434,45 @@ def make_config(k: int, seed: int | None = None):
         lens = lognormal_lengths(16, 1024.0, 1.0, 64, 8192, seed)
         return make_varlen(lens, 16, 16, 64, dtype="bf16", causal=True, seed=seed, q_mask_frac=0.05)
     raise ValueError(f"no config {k}")
+
+
+def make_bias(B: int, H: int, S_q: int, S_k: int, kind: str, seed: int, *, doc_median: int = 200) -> np.ndarray:
+    """A dense additive mask M, fp32 [B, H, S_q, S_k] (query i at position
+    i + S_k - S_q, as for causal alignment).
+
+    kind "document": packed documents with log-normal lengths (median
+        doc_median) drawn per batch row; 0 inside a document, -inf across
+        (H must be 1).
+    kind "alibi": a linear distance penalty -slope_h |pos_i - j| with
+        slope_h = 2^(-8 (h + 1) / H) (finite everywhere).
+    kind "random": N(0, 2^2) entries, a seeded quarter of them -inf, and query
+        row 0 of batch row 0 all -inf (a row the term alone masks).
+    """
+    off = S_k - S_q
+    pos = np.arange(S_q)[:, None] + off
+    j = np.arange(S_k)[None, :]
+    out = np.empty((B, H, S_q, S_k), np.float32)
+    if kind == "document":
+        assert H == 1
+        for b in range(B):
+            lens = lognormal_lengths(max(1, S_k // max(doc_median // 4, 1)) + 1, doc_median, 0.8, 1, S_k,
+                                     seed * 1000 + b)
+            edges = np.cumsum(lens)
+            doc = np.searchsorted(edges, np.arange(S_k), side="right")
+            same = doc[np.clip(pos, 0, S_k - 1)] == doc[j]
+            same &= (pos >= 0)
+            out[b, 0] = np.where(same, 0.0, -np.inf).astype(np.float32)
+    elif kind == "alibi":
+        for h in range(H):
+            slope = 2.0 ** (-8.0 * (h + 1) / H)
+            out[:, h] = (-slope * np.abs(pos - j)).astype(np.float32)
+    elif kind == "random":
+        x = draw((B, H, S_q, S_k), seed, S_BIAS, "normal", "f32").astype(np.float32) * 2.0
+        u = draw((B, H, S_q, S_k), seed, S_BIAS + 100, "uniform", "f32")
+        x[u < 0.25] = -np.inf
+        if S_q > 0:
+            x[0, :, 0, :] = -np.inf
+        out[...] = x
+    else:
+        raise ValueError(kind)
+    return out

@@ -467,3 +467,127 @@ def test_block_sparse_full_size_sampled(ea, orc):
                      for b in range(4)]).sum(axis=2) == 0
     assert np.all(np.isneginf(lse[dead[:, None, :].repeat(32, 1)]))
     check_block_sparse(orc, p, bk, o, lse, "block sparse full size", heads=[0, 17, 31])
+
+
+# ---- general dense additive mask M (page "Attention Kernel", section "可编程
+# mask"): fp32 [B, 1 or A, S_q, S_k], alone or with the flag masks, windows and
+# the block mask attn_block_keep_from_bias derives from it
+
+def run_bias(ea, p, bias_np, *, window=None, blocks=False, q_keep=None, k_keep=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, p.dtype), gu.dev(p.k, p.dtype), gu.dev(p.v, p.dtype)
+    o = gu.empty_out(q.shape, p.dtype)
+    lse = t.empty((p.B, p.A, p.S_q), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    bias = ea.pad_bias(t.from_numpy(bias_np).cuda())
+    bk = None
+    if blocks:
+        bk = t.full((p.B, bias_np.shape[1], (p.S_q + 127) // 128, (p.S_k + 127) // 128), 7, dtype=t.uint8,
+                    device="cuda")
+        ea.attn_block_keep_from_bias(bias, bk)
+    qk = None if q_keep is None else gu.dev(q_keep, "u8")
+    kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk, window=window,
+                block_keep=bk, bias=bias)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64), None if bk is None else bk.cpu().numpy()
+
+
+def bias_oracle(orc, p, bias_np, *, window=None, q_keep=None, k_keep=None, rows=None):
+    mk = None
+    if window is not None:
+        mk = oracle.window_keep(p.B, p.S_q, p.S_k, window[0], 0 if p.causal else window[1])
+    return orc.attn_fwd(p.q, p.k, p.v, dtype=p.dtype, scale=p.scale, causal=p.causal, q_keep=q_keep,
+                        k_keep=k_keep, m_keep=mk, bias=bias_np, rows=rows)
+
+
+def block_keep_reference(bias_np):
+    """[B, H, ceil(S_q/128), ceil(S_k/128)]: some entry of the block > -inf."""
+    B, H, S_q, S_k = bias_np.shape
+    nq, nk = (S_q + 127) // 128, (S_k + 127) // 128
+    pad = np.full((B, H, nq * 128, nk * 128), -np.inf, np.float32)
+    pad[:, :, :S_q, :S_k] = bias_np
+    return (pad.reshape(B, H, nq, 128, nk, 128) > -np.inf).any(axis=(3, 5)).astype(np.uint8)
+
+
+BIAS_CASES = [
+    # B, A, A_kv, S_q, S_k, d, causal, window, heads, kind, blocks, keep masks
+    (2, 4, 2, 300, 300, 128, True, None, 1, "document", True, False),
+    (1, 4, 4, 257, 390, 64, False, None, 4, "alibi", False, False),
+    (2, 2, 1, 200, 333, 128, True, None, 2, "random", True, True),
+    (1, 2, 2, 130, 130, 128, True, (40, -1), 1, "random", False, False),
+    (1, 8, 2, 500, 500, 64, True, None, 1, "document", True, True),
+    (2, 2, 2, 1, 70, 128, False, None, 1, "random", False, False),
+    (1, 2, 1, 64, 1000, 128, False, (100, 100), 2, "alibi", True, False),
+]
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n")
+                         + f"_{c[9]}{c[8]}" + ("_blk" if c[10] else "") + ("_keep" if c[11] else "")
+                         + ("" if c[7] is None else f"_w{c[7][0]}_{c[7][1]}"))
+def test_bias_bf16(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal, window, heads, kind, blocks, keeps = case
+    _say("dense additive mask", case)
+    seed = 1100 + S_q + S_k
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=seed,
+                       q_masked=S_q // 10 if keeps else 0, k_masked=S_k // 8 if keeps else 0)
+    bias = gen.make_bias(B, heads, S_q, S_k, kind, seed)
+    qk = p.q_keep if keeps else None
+    kk = p.k_keep if keeps else None
+    o, lse, bk = run_bias(ea, p, bias, window=window, blocks=blocks, q_keep=qk, k_keep=kk)
+    if blocks:
+        assert np.array_equal(bk, block_keep_reference(bias))
+    o_ref, l_ref = bias_oracle(orc, p, bias, window=window, q_keep=qk, k_keep=kk)
+    _say(gu.check(o, lse, o_ref, l_ref, "bf16", str(case)))
+
+
+def test_bias_f32(ea, orc):
+    """The fp32 path with a per-head distance penalty (the single-head fp32
+    workload's shape) and with a random term plus keep masks on a ragged shape."""
+    p = gen.make_config(1)
+    bias = gen.make_bias(p.B, p.A, p.S_q, p.S_k, "alibi", 1200)
+    o, lse, _ = run_bias(ea, p, bias)
+    o_ref, l_ref = bias_oracle(orc, p, bias)
+    _say("f32 alibi", gu.check(o, lse, o_ref, l_ref, "f32", "f32 alibi"))
+    p = gen.make_dense(2, 3, 1, 45, 77, 40, dtype="f32", causal=True, seed=1201, q_masked=4, k_masked=9)
+    bias = gen.make_bias(2, 1, 45, 77, "random", 1201)
+    o, lse, _ = run_bias(ea, p, bias, q_keep=p.q_keep, k_keep=p.k_keep)
+    o_ref, l_ref = bias_oracle(orc, p, bias, q_keep=p.q_keep, k_keep=p.k_keep)
+    _say("f32 random", gu.check(o, lse, o_ref, l_ref, "f32", "f32 random"))
+
+
+def test_bias_block_skip_bitwise(ea):
+    """The block mask derived from the bias skips only tiles the bias masks
+    whole: with and without it the outputs agree bit for bit."""
+    t = gu.torch()
+    p = gen.make_dense(2, 4, 2, 700, 900, 128, dtype="bf16", causal=True, seed=1202)
+    bias_np = gen.make_bias(2, 1, 700, 900, "document", 1202, doc_median=150)
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    bias = ea.pad_bias(t.from_numpy(bias_np).cuda())
+    bk = t.empty((2, 1, 6, 8), dtype=t.uint8, device="cuda")
+    ea.attn_block_keep_from_bias(bias, bk)
+    o1, o2 = gu.empty_out(q.shape, "bf16"), gu.empty_out(q.shape, "bf16")
+    l1 = t.empty((2, 4, 700), dtype=t.float32, device="cuda")
+    l2 = t.empty_like(l1)
+    ea.attn_fwd(q, k, v, o1, l1, scale=p.scale, causal=True, bias=bias)
+    ea.attn_fwd(q, k, v, o2, l2, scale=p.scale, causal=True, bias=bias, block_keep=bk)
+    t.cuda.synchronize()
+    kept = int(bk.sum().item())
+    _say("blocks kept", kept, "of", bk.numel())
+    assert kept < bk.numel()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
+
+
+def test_bias_full_size_sampled(ea, orc):
+    """The MHA workload's shape, causal, with a packed-document mask given as
+    the additive term (and its block mask), sampled rows against the oracle."""
+    p = gen.make_config(2)
+    bias = gen.make_bias(p.B, 1, p.S_q, p.S_k, "document", 1203)
+    o, lse, bk = run_bias(ea, p, bias, blocks=True)
+    assert np.array_equal(bk, block_keep_reference(bias))
+    rng = np.random.default_rng(1203)
+    rows = _sample_rows(rng, p.B, p.A, p.S_q, 1200)
+    o_ref, l_ref = bias_oracle(orc, p, bias, rows=rows)
+    _say("bias full size", int(bk.sum()), "blocks kept",
+         gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "bias full size"))
