@@ -10,9 +10,14 @@ One step = one pass of the whole path over one batch of synthetic inputs:
 Inputs are resident in HBM before the timed region.  Each launch is bracketed
 by HIP events recorded on the stream the library launches on.
 
-After the timed steps, the backward of workload 1 (dQ, dK, dV recomputed from
-the forward's LSE) is timed on its own and reported under "backward"; it is
-not part of a step.
+After the timed steps, the next-step variants are timed on their own, each
+under its own key (none is part of a step): "backward" (dQ, dK, dV of
+workload 1 recomputed from the forward's LSE), "window" (GQA causal S=16384
+with a 4096-key sliding window), "paged_prefill" (256-token chunks over the
+decode workload's paged cache), "block_sparse" (workload 1 with a 50% block
+mask), "dense_mask" (workload 1 with a general dense additive mask: packed
+documents with their derived block mask, and a per-head distance penalty) and
+"decode_fp8" (workload 2 over E4M3 caches with per-(page, head) scales).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -30,8 +35,9 @@ reported beside them:
     rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o p -- python3 bench.py --traffic-workload
     python3 bench.py --traffic-summary <dir_r> <dir_w> <dir_f> > profiles/traffic_<...>.md
 
-The summary records a hash of each kernel's sources; a later bench run reports
-`traffic` only while those sources are unchanged (null otherwise).
+The summary records a hash of the code of each kernel's sources (comments and
+layout excluded); a later bench run reports `traffic` only while that code is
+unchanged (null otherwise).
 
 Matrix-core utilisation of the prefill kernels, from one counter run:
 
@@ -455,6 +461,7 @@ def main():
     out["window"] = bench_window(args.steps, args.warmup, stream)
     out["paged_prefill"] = bench_paged_prefill(w, args.steps, args.warmup)
     out["block_sparse"] = bench_block_sparse(w, args.steps, args.warmup)
+    out["dense_mask"] = bench_dense_mask(w, args.steps, args.warmup)
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
 
     if not args.no_cpu_baseline:
@@ -668,6 +675,76 @@ def bench_block_sparse(w, steps: int, warmup: int) -> dict:
             "min_ms": round(float(ms.min()), 5), "flops": flops, "blocks_kept": int(bk.sum()),
             "blocks_total": int(bk.size),
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 with a seeded 50% block mask (128 x 128 blocks)"}
+
+
+def _event_times(run, steps: int, warmup: int, stream) -> np.ndarray:
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def bench_dense_mask(w, steps: int, warmup: int) -> dict:
+    """The MHA causal prefill workload with a general dense additive mask M
+    (fp32 [B, heads, S, S]), two ways:
+      - packed documents (log-normal lengths, median 200 tokens) given as M in
+        {0, -inf} shared by the heads, with the block mask derived from it
+        (attn_block_keep_from_bias, timed separately) so that tiles the
+        documents exclude are skipped; FLOPs = 4 d A x (kept causal pairs);
+      - a finite per-head distance penalty -2^(-8(h+1)/A) |i - j| (every pair
+        kept, 2.1 GB of fp32 terms read once per launch); FLOPs = the causal
+        count, and the term's bytes / time as a bandwidth."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p2, stream = w["p2"], w["stream"]
+    q, k, v, o, lse = w["dev2"]
+    B, A, S, d = p2.B, p2.A, p2.S_q, p2.d
+    doc = gen.make_bias(B, 1, S, S, "document", 1011)
+    causal_pairs = np.tril(np.ones((S, S), bool))
+    kept = int(sum(((doc[b, 0] == 0) & causal_pairs).sum() for b in range(B)))
+    bias_doc = ea.pad_bias(torch.from_numpy(doc).cuda())
+    bk = torch.empty((B, 1, (S + 127) // 128, (S + 127) // 128), dtype=torch.uint8, device="cuda")
+    ms_blk = _event_times(lambda: ea.attn_block_keep_from_bias(bias_doc, bk, stream=stream), steps, warmup, stream)
+    ms_doc = _event_times(lambda: ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, bias=bias_doc,
+                                              block_keep=bk, stream=stream), steps, warmup, stream)
+    flops_doc = 4.0 * d * A * kept
+    tf_doc = flops_doc / (ms_doc.mean() * 1e-3) / 1e12
+    del bias_doc
+    pos = torch.arange(S, device="cuda", dtype=torch.float32)
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / A) for h in range(A)], device="cuda")
+    dist = (pos[:, None] - pos[None, :]).abs()
+    bias_pen = (-slopes[:, None, None] * dist[None]).unsqueeze(0).expand(B, A, S, S).contiguous()
+    ms_pen = _event_times(lambda: ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, bias=bias_pen,
+                                              stream=stream), steps, warmup, stream)
+    flops_pen = 4.0 * d * A * B * (S * (S + 1) // 2)
+    tf_pen = flops_pen / (ms_pen.mean() * 1e-3) / 1e12
+    pen_bytes = 4.0 * B * A * (S * (S + 1) // 2)  # the causal part of M is what the kernel reads
+    del bias_pen
+    torch.cuda.empty_cache()
+    return {"metric": "dense additive mask causal prefill TFLOP/s (kept pairs)", "value": round(tf_doc, 2),
+            "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf_doc / PEAK_BF16_TFLOPS, 4),
+            "avg_ms": round(float(ms_doc.mean()), 5), "median_ms": round(float(np.median(ms_doc)), 5),
+            "flops": flops_doc, "kept_pairs": kept, "blocks_kept": int(bk.sum().item()), "blocks_total": bk.numel(),
+            "block_mask_from_bias_ms": round(float(ms_blk.mean()), 5),
+            "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16, packed documents (median 200 tokens) as an fp32 "
+                        "{0, -inf} term shared by the heads, with its derived block mask",
+            "per_head_penalty": {"value": round(tf_pen, 2), "unit": "TFLOP/s",
+                                 "frac_of_bf16_peak": round(tf_pen / PEAK_BF16_TFLOPS, 4),
+                                 "avg_ms": round(float(ms_pen.mean()), 5),
+                                 "term_GB/s": round(pen_bytes / (ms_pen.mean() * 1e-3) / 1e9, 1),
+                                 "workload": "the same prefill with a finite fp32 per-head distance penalty "
+                                             "[4, 32, 2048, 2048] (every causal pair kept)"}}
 
 
 PAGED_CHUNK = 256
