@@ -250,8 +250,8 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
     read[cr], write[cw], fetch[cf] = max(read_d[cr]), max(write_d[cw]), max(fetch_d[cf])
     r_scale, w_scale, f_scale = COPY_BYTES / read[cr], COPY_BYTES / write[cw], COPY_BYTES / fetch[cf]
     kernels = {
-        "prefill": lambda k: "prefill_bf16_kernel<128, false, false, false>" in k,
-        "varlen": lambda k: "prefill_bf16_kernel<64, true, false, false>" in k,
+        "prefill": lambda k: "prefill_bf16_kernel<128, false, false, false, false>" in k,
+        "varlen": lambda k: "prefill_bf16_kernel<64, true, false, false, false>" in k,
         "decode_split": lambda k: "decode_split_kernel" in k,
         "decode_merge": lambda k: "decode_merge_kernel" in k,
         "bwd_dq": lambda k: "bwd_dq_kernel<128>" in k,
@@ -289,6 +289,8 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
         print(f"| {part} | `{k[:60]}` | {n} | {r / 2**20:.1f} | {w / 2**20:.1f} | {f / 2**20:.1f} | {rb / 1e6:.1f} "
               f"| {wb / 1e6:.1f} | {fb / 1e6:.1f} |")
     print()
+    print("Each `source_hash` is the hash of the code of the kernel's sources (comments and layout removed); "
+          "`bench.py` reports a traffic figure only while it matches the current sources.\n")
     print("traffic-json: " + json.dumps(out))
 
 
@@ -308,7 +310,7 @@ def counter_summary(d: str):
                 by.setdefault(key, {})
                 by[key][r["Counter_Name"]] = by[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
                 span[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-    kernels = {"prefill": "prefill_bf16_kernel<128, false, false, false>", "varlen": "prefill_bf16_kernel<64, true, false, false>",
+    kernels = {"prefill": "prefill_bf16_kernel<128, false, false, false, false>", "varlen": "prefill_bf16_kernel<64, true, false, false, false>",
                "decode_split": "decode_split_kernel", "bwd_dq": "bwd_dq_kernel<128>",
                "bwd_dkdv": "bwd_dkdv_kernel<128,"}
     print("# Matrix-core utilisation per launch (SQ / GRBM counters)\n")
@@ -434,7 +436,7 @@ def main():
                      "traffic": None if traffic_prefill is None else round(traffic_prefill),
                      "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
                      "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
-                     "kernel": "prefill_bf16_kernel<128, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
+                     "kernel": "prefill_bf16_kernel<128, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
                      "median_launch_ms": round(med["prefill"], 5), "min_launch_ms": round(mn["prefill"], 5),
                      "measured_ceiling": {"what": "torch.matmul bf16 8192^3 on the same GPU",
                                           "TFLOP/s": ceil["gemm_tflops"],
