@@ -55,7 +55,8 @@ __device__ __forceinline__ int tok_swz(int tok) { return ((tok & 7) << 1) | ((to
 // Wave w of the workgroup owns KV heads 4*HPW*blockIdx.y + HPW*w + [0, HPW).
 // A 16-token chunk of the wave's heads is copied global -> LDS with
 // global_load_lds (rows of HPW*d contiguous elements, so each load
-// instruction reads whole rows), then
+// instruction reads whole rows; bf16 caches use two buffers per wave, the
+// next chunk's copies in flight while this one is computed), then
 //   S^T[token, n] = sum_hh K_hh . Q^T_hh     (16x16x32 MFMA; column n = query
 //                                             head n of the wave; block
 //                                             diagonal: columns of other KV
@@ -77,7 +78,11 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
   constexpr int N_LD = kChunk / TOK_PER_LD;  // load instructions per chunk (K or V)
   constexpr int KSTEPS = D / 32;             // QK k-steps per head
   constexpr int MB = D / 16;                 // 16-row blocks of O^T
-  constexpr int WAVE_LDS = 2 * kChunk * RC * 16;  // bytes: K then V
+  // bf16: two LDS buffers per wave (the next chunk's copies fly while this
+  // one is computed); FP8: one, the next chunk's bytes wait in registers
+  constexpr int NBUF = kFp8 ? 1 : 2;
+  constexpr int BUF_BYTES = 2 * kChunk * RC * 16;  // bytes: K then V
+  constexpr int WAVE_LDS = NBUF * BUF_BYTES;
   static_assert(64 % RC == 0 && kChunk % TOK_PER_LD == 0, "row split");
   __shared__ __attribute__((aligned(16))) char smem[kWavesPerGroup * WAVE_LDS];
 
@@ -88,7 +93,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
   const int kv0 = (blockIdx.y * kWavesPerGroup + wave) * HPW;  // first KV head of this wave
   if (kv0 >= p.A_kv) return;  // no barrier below: waves are independent
   const int nh = min(HPW, p.A_kv - kv0);  // KV heads of this wave
-  char* sK = smem + wave * WAVE_LDS;
+  char* const sK0 = smem + wave * WAVE_LDS;
+  char* sK = sK0;
   char* sV = sK + kChunk * RC * 16;
 
   // ---- this workgroup's chunk range
@@ -204,8 +210,26 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
       ksc_n = p.k_scale[srow];
       vsc_n = p.v_scale[srow];
     };
+    // bf16 with two LDS buffers: chunk c's copies into buffer `buf`
+    [[maybe_unused]] auto bf16_issue = [&](int c, int buf) {
+      int page;
+      const size_t row0 = chunk_row0(c, page);
+      const int nv = min(kChunk, t_end - c);
+      char* dK = sK0 + buf * BUF_BYTES;
+      char* dV = dK + kChunk * RC * 16;
+#pragma unroll
+      for (int i = 0; i < N_LD; ++i) {
+        const size_t e = slot_elem(row0, nv, i);
+        __builtin_amdgcn_global_load_lds((const void*)(kc + e), (__attribute__((address_space(3))) void*)(dK + i * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vc + e), (__attribute__((address_space(3))) void*)(dV + i * 1024),
+                                         16, 0, 0);
+      }
+    };
     if constexpr (kFp8) {
       if (t_begin < t_end) fp8_load(t_begin);
+    } else {
+      if (t_begin < t_end) bf16_issue(t_begin, 0);
     }
 
     for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
@@ -230,22 +254,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
         vsc = vsc_n;
         if (c0 + kChunk < t_end) fp8_load(c0 + kChunk);
       } else {
-        // ---- global -> LDS: instruction i fills token rows i*TOK_PER_LD + [0, TOK_PER_LD)
-        int page;
-        const size_t page_row0 = chunk_row0(c0, page);
-#pragma unroll
-        for (int i = 0; i < N_LD; ++i) {
-          const size_t e = slot_elem(page_row0, n_valid, i);
-          __builtin_amdgcn_global_load_lds((const void*)(kc + e),
-                                           (__attribute__((address_space(3))) void*)(sK + i * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const void*)(vc + e),
-                                           (__attribute__((address_space(3))) void*)(sV + i * 1024), 16, 0, 0);
+        // the next chunk's copies go into the other buffer before this chunk
+        // is waited for; vmcnt counts in issue order, so leaving the newest
+        // 2 N_LD copies outstanding means this chunk's have landed.  The
+        // wait is explicit (the compiler does not place its own before every
+        // read of LDS written this way) and the empty asm keeps the LDS reads
+        // below from moving above it.
+        const int buf = ((c0 - t_begin) / kChunk) & 1;
+        sK = sK0 + buf * BUF_BYTES;
+        sV = sK + kChunk * RC * 16;
+        if (c0 + kChunk < t_end) {
+          bf16_issue(c0 + kChunk, buf ^ 1);
+          constexpr int n = 2 * N_LD;
+          static_assert(n < 64, "vmcnt field");
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
-        // The copies land in LDS asynchronously (tracked by vmcnt).  Wait for all
-        // of them explicitly: the compiler's own wait for LDS written this way is
-        // not placed before every read.  The empty asm keeps LDS accesses from
-        // moving across the wait.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         asm volatile("" ::: "memory");
       }
       // ---- S^T = sum_hh K_hh . Q^T_hh (block diagonal over the wave's heads)
@@ -428,16 +453,28 @@ hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                  hipSuccess || cus < 1)
       cus = 1;
-    const bool two = p.G <= 8;  // two KV heads per wave when 2G <= 16 MFMA columns
+    // FP8: two KV heads per wave when 2G <= 16 MFMA columns (longer rows per
+    // load); bf16: one, so that two LDS buffers per wave still leave room for
+    // two workgroups per CU (measured +1.7% over one buffer at two heads)
+    const bool two = kFp8 && p.G <= 8;
     const int heads_per_group = (two ? 2 : 1) * kWavesPerGroup;
     const int groups = (p.A_kv + heads_per_group - 1) / heads_per_group;
     // one resident wave of workgroups covers the chunk list once
-    long long want = (two ? resident_groups<D, 2, kFp8>(cus) : resident_groups<D, 1, kFp8>(cus)) / groups;
+    long long want = resident_groups<D, 1, kFp8>(cus);
+    if constexpr (kFp8) {
+      if (two) want = resident_groups<D, 2, kFp8>(cus);
+    }
+    want /= groups;
     if (want < 1) want = 1;
     if (want > kMaxDecodeGroups) want = kMaxDecodeGroups;
     if (want > p.n_chunks) want = p.n_chunks;
     p.n_wg = (int)want;
-    hipError_t e = two ? launch_split<D, 2, kFp8>(p, groups, stream) : launch_split<D, 1, kFp8>(p, groups, stream);
+    hipError_t e;
+    if constexpr (kFp8) {
+      e = two ? launch_split<D, 2, kFp8>(p, groups, stream) : launch_split<D, 1, kFp8>(p, groups, stream);
+    } else {
+      e = launch_split<D, 1, kFp8>(p, groups, stream);
+    }
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.B * p.A), dim3(64), 0, stream, p);
