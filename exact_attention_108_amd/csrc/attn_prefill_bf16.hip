@@ -38,6 +38,18 @@
 // 稳定基础").  Query tiles are issued heaviest first (most key tiles) so the
 // tail of the grid holds the short ones (page "快速Transformer（续）",
 // section "Stream-K", wave quantisation).
+//
+// Instantiations (template flags; page "Attention Kernel", sections "Paged 与
+// ragged KV" and "可编程 mask"):
+//   kVarlen  packed sequences described by cumulative lengths;
+//   kPaged   packed query chunks over a paged KV cache (each 16-token part of a
+//            key tile is one page, found through the block table);
+//   kBlocks  the key tiles of a row block listed from a 128 x 128 block mask,
+//            so masked blocks are never loaded;
+//   kBias    a dense additive term M on every score (all tiles take the
+//            per-element step).
+// Sliding windows, keep masks and the causal flag are runtime arguments of
+// every instantiation.
 #include <type_traits>
 
 #include "attn_device.h"
