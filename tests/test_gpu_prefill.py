@@ -591,3 +591,19 @@ def test_bias_full_size_sampled(ea, orc):
     o_ref, l_ref = bias_oracle(orc, p, bias, rows=rows)
     _say("bias full size", int(bk.sum()), "blocks kept",
          gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "bias full size"))
+
+
+def test_block_sparse_longest_key_range(ea, orc):
+    """The largest key range a block mask accepts (S_k = 262144: 4096 listed
+    64-key tiles per workgroup at most), non-causal, one block in ten kept per
+    row block; every row checked against the oracle."""
+    S_q, S_k = 200, 262144
+    p = gen.make_dense(1, 2, 1, S_q, S_k, 128, dtype="bf16", causal=False, seed=1300)
+    rng = np.random.default_rng(1300)
+    bk = (rng.random((1, 1, 2, S_k // 128)) < 0.1).astype(np.uint8)
+    bk[0, 0, 0, -1] = 1                                   # the last block of the range
+    bk[0, 0, 1, :] = 0                                    # a row block with nothing kept
+    _say("block sparse longest range", int(bk.sum()), "blocks kept")
+    o, lse = run_block_sparse(ea, p, bk)
+    assert np.all(np.isneginf(lse[:, :, 128:])) and np.all(o[:, :, 128:] == 0)
+    check_block_sparse(orc, p, bk, o, lse, "block sparse longest range")
