@@ -69,6 +69,36 @@ DENSE_CASES = [
 ]
 
 
+# Grids of more query tiles than one resident round of workgroups holds (512
+# at d = 128, 768 at d = 64 on 256 CUs), compared over every row: with and
+# without the XCD-blocked order (B*A a multiple of 8 or not), GQA, ragged row
+# tiles, non-causal, and keep masks on both sides.
+MULTI_ROUND_CASES = [
+    # B, A, A_kv, S_q, S_k, d, causal, keep masks
+    (16, 8, 2, 1024, 1024, 128, True, False),
+    (4, 16, 16, 1100, 1100, 128, False, False),
+    (4, 16, 4, 2048, 2048, 64, True, False),
+    (12, 7, 7, 1300, 1300, 64, True, False),
+    (9, 8, 4, 1000, 1030, 128, True, True),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_ROUND_CASES,
+                         ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n") + ("k" if c[7] else ""))
+def test_dense_bf16_multi_round(ea, orc, case):
+    B, A, A_kv, S_q, S_k, d, causal, keep = case
+    _say("dense bf16 multi-round grid", case)
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=hash(case) % 10000)
+    qk = kk = None
+    if keep:
+        rng = np.random.default_rng(77)
+        qk = (rng.random((B, S_q)) >= 0.05).astype(np.uint8)
+        kk = (rng.random((B, S_k)) >= 0.2).astype(np.uint8)
+    o, lse = run_dense(ea, p, q_keep=qk, k_keep=kk)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal, q_keep=qk, k_keep=kk)
+    gu.check(o, lse, o_ref, l_ref, "bf16", str(case))
+
+
 @pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "x".join(map(str, c[:6])) + ("c" if c[6] else "n"))
 def test_dense_bf16_small(ea, orc, case):
     B, A, A_kv, S_q, S_k, d, causal = case
