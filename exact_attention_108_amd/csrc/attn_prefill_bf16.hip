@@ -259,18 +259,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // read past the sequence and absent rows arrive as zeros.
   [[maybe_unused]] const uint32_t kv_stride = (uint32_t)(kPaged ? p.A_kv * D * 2 : D * 2);
   [[maybe_unused]] const uint32_t poff = (uint32_t)rowc * kv_stride + (uint32_t)cc * 16;
-  [[maybe_unused]] auto part_rsrc = [&](const char* gbase, int t, int i) -> i32x4 {
+  // Page ids.  The prologue reads them with scalar loads.  In the loop a
+  // scalar load would be costly: scalar loads may return out of order, so
+  // while one is in flight every wait for an LDS operand read becomes a wait
+  // for all of them.  The loop therefore fetches the next iteration's pages
+  // with one vector load (lane i: part i), which the wait for the tile
+  // copies at the top of the next iteration covers, and reads them out of
+  // the lanes there.
+  [[maybe_unused]] auto page_of = [&](int t, int i) -> int {  // page of part i of tile t
     const int row0 = phys(t) * kBc + i * RPC;
-    const int page = load_uniform_i32(rb.bt, min(row0, S_k - 1) >> p.page_shift);
+    return load_uniform_i32(rb.bt, min(row0, S_k - 1) >> p.page_shift);
+  };
+  [[maybe_unused]] auto pages_vec = [&](int t) -> int {  // lane i < LD_PER_T: page of part i of tile t
+    const int row0 = phys(t) * kBc + min(lane, LD_PER_T - 1) * RPC;
+    return rb.bt[min(row0, S_k - 1) >> p.page_shift];
+  };
+  [[maybe_unused]] auto part_rsrc = [&](const char* gbase, int t, int i, int page) -> i32x4 {
+    const int row0 = phys(t) * kBc + i * RPC;
     const int in_page = row0 & ((1 << p.page_shift) - 1);
     const int rows = min(max(S_k - row0, 0), RPC);
     return make_buffer_rsrc(gbase + ((size_t)page << p.page_shift | (size_t)in_page) * kv_stride,
                             (uint32_t)rows * kv_stride);
   };
-  [[maybe_unused]] auto copy_part_paged = [&](const char* gbase, int t, uint32_t dst, int i) {
-    lds_copy16_buf(part_rsrc(gbase, t, i), poff,
+  [[maybe_unused]] auto copy_part_paged = [&](const char* gbase, int t, uint32_t dst, int i, int page) {
+    lds_copy16_buf(part_rsrc(gbase, t, i, page), poff,
                    lds_base + dst + (uint32_t)(i * RPC * D * 2) + (uint32_t)wave_u * 1024u);
   };
+  // pages of the parts of the K tile the current iteration copies (the next
+  // iteration copies V of that same tile), and, in lanes, of the next
+  // iteration's K tile
+  [[maybe_unused]] int pg_k[LD_PER_T] = {};
+  [[maybe_unused]] int pg_n = 0;
   auto copy_keep = [&](int t) {
     if (rb.k_keep && tid < kBc && t < n_tiles) {
       const int key = phys(t) * kBc + tid;
@@ -486,11 +505,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   if (n_tiles > 0) {
     if constexpr (kPaged) {
       const int t1 = min(1, n_tiles - 1);
+      pg_n = pages_vec(min(2, n_tiles - 1));
 #pragma unroll
       for (int i = 0; i < LD_PER_T; ++i) {
-        copy_part_paged(rb.k, 0, 0, i);
-        copy_part_paged(rb.v, 0, 2 * TILE_BYTES, i);
-        copy_part_paged(rb.k, t1, TILE_BYTES, i);
+        const int p0 = page_of(0, i);
+        pg_k[i] = page_of(t1, i);
+        copy_part_paged(rb.k, 0, 0, i, p0);
+        copy_part_paged(rb.v, 0, 2 * TILE_BYTES, i, p0);
+        copy_part_paged(rb.k, t1, TILE_BYTES, i, pg_k[i]);
       }
     } else {
       const i32x4 rk0 = tile_rsrc(gk, 0), rv0 = tile_rsrc(gv, 0);
@@ -534,9 +556,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // and it keeps the body free of branches).
     const int tk = min(j + 2, n_tiles - 1), tv = min(j + 1, n_tiles - 1);
     [[maybe_unused]] i32x4 rk, rv;
+    [[maybe_unused]] int pg_v[LD_PER_T];
     if constexpr (!kPaged) {
       rk = tile_rsrc(gk, tk);
       rv = tile_rsrc(gv, tv);
+    } else {
+      // V of tile tv is the K tile the previous iteration copied; the pages
+      // of K tile tk were loaded during the previous iteration (the copy
+      // wait above covered that load); start loading those of the next one
+      // (the empty asm keeps the reads below the copy wait and the barrier)
+      asm volatile("" : "+v"(pg_n));
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        pg_v[i] = pg_k[i];
+        pg_k[i] = __builtin_amdgcn_readlane(pg_n, i);
+      }
+      pg_n = pages_vec(min(j + 3, n_tiles - 1));
     }
     if constexpr (MASKED) copy_keep(j + 2);
     auto issue = [&](int at) {
@@ -544,8 +579,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int i = 0; i < LD_PER_T; ++i) {
         if (i * 4 / LD_PER_T == at) {
           if constexpr (kPaged) {
-            copy_part_paged(rb.k, tk, BUF * TILE_BYTES, i);
-            copy_part_paged(rb.v, tv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
+            copy_part_paged(rb.k, tk, BUF * TILE_BYTES, i, pg_k[i]);
+            copy_part_paged(rb.v, tv, (2 + (BUF ^ 1)) * TILE_BYTES, i, pg_v[i]);
           } else {
             copy_part(rk, BUF * TILE_BYTES, i);
             copy_part(rv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
