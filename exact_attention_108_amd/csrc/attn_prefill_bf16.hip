@@ -665,16 +665,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   if (g == 0 && qrow < S_q) {
     rb.lse[qrow] = row_ok ? (m_ref + log2_fast(l_tot)) * kLn2 : -INFINITY;
   }
-  __syncthreads();
+  // Each wave reads back only the rows it staged, and the LDS executes one
+  // wave's operations in order, so the reads see the writes without a
+  // workgroup barrier; the fence only keeps the compiler from reordering.
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // all reads first (they are in bounds for every row), then the stores of
+  // the rows that exist, so the LDS round trips overlap
+  constexpr int NST = (32 * NCH) / 64;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 val[NST];
 #pragma unroll
-  for (int i = 0; i < (32 * NCH) / 64; ++i) {
+  for (int i = 0; i < NST; ++i) {
     const int cid = lane + 64 * i;
-    const int row = cid / NCH, c = cid % NCH;
-    const int qr = wave_q0 + row;
-    if (qr < S_q) {
-      const uint4 val = *(const uint4*)(stage + row * PITCH + c * 8);
-      *(uint4*)(go + (size_t)qr * D + c * 8) = val;
-    }
+    val[i] = *(const u32x4*)(stage + (cid / NCH) * PITCH + (cid % NCH) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NST; ++i) asm volatile("" : "+v"(val[i]));  // (keeps the reads out of the branches)
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int cid = lane + 64 * i;
+    const int qr = wave_q0 + cid / NCH;
+    if (qr < S_q) *(u32x4*)(go + (size_t)qr * D + (cid % NCH) * 8) = val[i];
   }
 }
 
