@@ -803,7 +803,7 @@ def bench_paged_prefill(w, steps: int, warmup: int) -> dict:
 def measured_ceilings(stream) -> dict:
     """What this GPU sustains on plain library work, as a second reference
     beside the spec peaks: a bf16 GEMM through torch.matmul, a 2 GiB
-    device-to-device copy and a read-only 4 GiB reduction."""
+    device-to-device copy and a read-only stream (row sums over 4 GiB)."""
     import torch
     out = {}
     n = 8192
