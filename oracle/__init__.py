@@ -50,15 +50,21 @@ class Oracle:
         self.lib = ctypes.CDLL(lib_path)
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         self.lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                             vp, vp, vp, vp, i32, vp, i64, vp, vp]
+                                             vp, vp, vp, vp, i32, vp, i32, vp, i64, vp, vp]
         self.lib.oracle_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32,
                                                     i32, vp, vp, vp, i64, vp, vp]
         self.lib.oracle_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                                  i32, f32, vp, i64, vp, vp]
         self.lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                             vp, vp, vp, vp, vp, vp]
+                                             vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]
+        self.lib.oracle_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32, i32,
+                                                    vp, vp, i32, i32, vp, vp, vp]
+        self.lib.oracle_prefill_paged.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                  i32, f32, i32, i32, i32, vp, i64, vp, vp]
+        self.lib.oracle_block_keep_of_bias.argtypes = [vp, i32, i32, i32, i32, vp]
         for f in (self.lib.oracle_attn_fwd, self.lib.oracle_attn_fwd_varlen, self.lib.oracle_decode_paged,
-                  self.lib.oracle_attn_bwd):
+                  self.lib.oracle_attn_bwd, self.lib.oracle_attn_bwd_varlen, self.lib.oracle_prefill_paged,
+                  self.lib.oracle_block_keep_of_bias):
             f.restype = ctypes.c_int
         self.lib.oracle_num_threads.restype = ctypes.c_int
 
@@ -76,6 +82,25 @@ class Oracle:
         raise ValueError(f"unknown dtype {dtype!r}")
 
     @staticmethod
+    def _blocks(block_keep, B, A, S_q, S_k):
+        if block_keep is None:
+            return None, 0
+        bk = np.ascontiguousarray(block_keep, dtype=np.uint8)
+        want = ((S_q + 127) // 128, (S_k + 127) // 128)
+        if bk.ndim != 4 or bk.shape[0] != B or bk.shape[1] not in (1, A) or bk.shape[2:] != want:
+            raise ValueError(f"block_keep must be [B, 1 or A, {want[0]}, {want[1]}]")
+        return bk, bk.shape[1]
+
+    @staticmethod
+    def _bias(bias, B, A, S_q, S_k):
+        if bias is None:
+            return None, 0
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.ndim != 4 or bias.shape[0] != B or bias.shape[1] not in (1, A) or bias.shape[2:] != (S_q, S_k):
+            raise ValueError("bias must be [B, 1 or A, S_q, S_k]")
+        return bias, bias.shape[1]
+
+    @staticmethod
     def _rows(rows):
         if rows is None:
             return None, 0
@@ -83,11 +108,12 @@ class Oracle:
         return r, r.size
 
     def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None, bias=None,
-                 rows=None):
+                 block_keep=None, rows=None):
         """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d]; m_keep an
         optional dense keep matrix [B,S_q,S_k] (see window_keep); bias an optional
         dense additive term M, fp32 [B,1,S_q,S_k] (every head) or [B,A,S_q,S_k],
-        finite or -inf.
+        finite or -inf; block_keep an optional block mask uint8
+        [B, 1 or A, ceil(S_q/128), ceil(S_k/128)] (0 masks the 128 x 128 block).
 
         Returns (o, lse): o [B,A,S_q,d] / lse [B,A,S_q] in fp64, or [n,d] / [n]
         for the flattened row ids ``rows`` = (b*A + h)*S_q + i.
@@ -104,19 +130,15 @@ class Oracle:
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
         mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
-        bh = 0
-        if bias is not None:
-            bias = np.ascontiguousarray(bias, dtype=np.float32)
-            if bias.ndim != 4 or bias.shape[0] != B or bias.shape[1] not in (1, A) or bias.shape[2:] != (S_q, S_k):
-                raise ValueError("bias must be [B, 1 or A, S_q, S_k]")
-            bh = bias.shape[1]
+        bias, bh = self._bias(bias, B, A, S_q, S_k)
+        bk, bkh = self._blocks(block_keep, B, A, S_q, S_k)
         r, n = self._rows(rows)
         n_out = B * A * S_q if r is None else n
         o = np.empty((n_out, d), dtype=np.float64)
         lse = np.empty(n_out, dtype=np.float64)
         rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, A, A_kv, S_q, S_k, d,
                                       float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(bias),
-                                      bh, _ptr(r), n, _ptr(o), _ptr(lse))
+                                      bh, _ptr(bk), bkh, _ptr(r), n, _ptr(o), _ptr(lse))
         if rc != 0:
             raise ValueError("oracle_attn_fwd rejected its arguments")
         if r is None:
@@ -150,9 +172,11 @@ class Oracle:
             return o.reshape(A, T, d), lse.reshape(A, T)
         return o, lse
 
-    def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None):
-        """Gradient of attn_fwd: q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d].
-        Returns (dq, dk, dv) in fp64 with the shapes of q, k and v."""
+    def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None,
+                 bias=None, block_keep=None):
+        """Gradient of attn_fwd: q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d]; masks
+        as attn_fwd takes them.  Returns (dq, dk, dv) in fp64 with the shapes of
+        q, k and v."""
         q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
         if q.ndim != 4 or k.shape != v.shape or do.shape != q.shape:
             raise ValueError("q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d]")
@@ -163,15 +187,89 @@ class Oracle:
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
         mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
+        bias, bh = self._bias(bias, B, A, S_q, S_k)
+        bk, bkh = self._blocks(block_keep, B, A, S_q, S_k)
         dq = np.empty((B, A, S_q, d), dtype=np.float64)
         dk = np.empty((B, A_kv, S_k, d), dtype=np.float64)
         dv = np.empty((B, A_kv, S_k, d), dtype=np.float64)
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _DT[dtype], B, A, A_kv, S_q, S_k, d,
-                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(dq),
-                                      _ptr(dk), _ptr(dv))
+                                      float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), _ptr(mk), _ptr(bias), bh,
+                                      _ptr(bk), bkh, _ptr(dq), _ptr(dk), _ptr(dv))
         if rc != 0:
             raise ValueError("oracle_attn_bwd rejected its arguments")
         return dq, dk, dv
+
+    def attn_bwd_varlen(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal=True, q_keep=None, k_keep=None,
+                        window=None):
+        """Gradient of the packed varlen prefill: q, do [A,T,d]; k, v [A_kv,T,d];
+        cu_seqlens [n_seq+1]; keep masks [T]; window (left, right) within each
+        sequence (-1 = unbounded).  Returns (dq, dk, dv) in fp64."""
+        q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
+        if q.ndim != 3 or k.shape != v.shape or do.shape != q.shape:
+            raise ValueError("q, do [A,T,d]; k, v [A_kv,T,d]")
+        A, T, d = q.shape
+        A_kv = k.shape[0]
+        if k.shape[1] != T or k.shape[2] != d or A % A_kv:
+            raise ValueError("k/v must be [A_kv, T, d] with A % A_kv == 0")
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(T)
+        kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(T)
+        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        dq = np.empty((A, T, d), dtype=np.float64)
+        dk = np.empty((A_kv, T, d), dtype=np.float64)
+        dv = np.empty((A_kv, T, d), dtype=np.float64)
+        rc = self.lib.oracle_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _DT[dtype], _ptr(cu), cu.size - 1,
+                                             T, A, A_kv, d, float(scale), int(bool(causal)), _ptr(qk), _ptr(kk), wl,
+                                             wr, _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc != 0:
+            raise ValueError("oracle_attn_bwd_varlen rejected its arguments")
+        return dq, dk, dv
+
+    def prefill_paged(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal=True,
+                      window=None, rows=None):
+        """Query chunks over a paged cache: q [A,T_q,d] packed chunks (cu_seqlens_q
+        [n_seq+1]); caches [P, page_size, A_kv, d]; block_table [n_seq, max_pages];
+        seq_lens [n_seq] (chunk included).  Chunk row i of sequence s sits at
+        position seq_lens[s] - q_s + i.  Returns (o [A,T_q,d], lse [A,T_q]) in
+        fp64, or [n,d] / [n] for the flattened ids ``rows`` = h*T_q + r."""
+        q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
+        if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
+            raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
+        A, T_q, d = q.shape
+        num_pages, page_size, A_kv, dk = kc.shape
+        if dk != d or A % A_kv:
+            raise ValueError("cache head dim / head count mismatch")
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+        n_seq = cu.size - 1
+        if bt.ndim != 2 or bt.shape[0] != n_seq or sl.shape != (n_seq,):
+            raise ValueError("block_table [n_seq, max_pages], seq_lens [n_seq]")
+        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        r, n = self._rows(rows)
+        n_out = A * T_q if r is None else n
+        o = np.empty((n_out, d), dtype=np.float64)
+        lse = np.empty(n_out, dtype=np.float64)
+        rc = self.lib.oracle_prefill_paged(_ptr(q), _ptr(kc), _ptr(vc), _DT[dtype], _ptr(bt), _ptr(sl), _ptr(cu),
+                                           n_seq, T_q, A, A_kv, d, page_size, bt.shape[1], num_pages, float(scale),
+                                           int(bool(causal)), wl, wr, _ptr(r), n, _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise ValueError("oracle_prefill_paged rejected its arguments")
+        if r is None:
+            return o.reshape(A, T_q, d), lse.reshape(A, T_q)
+        return o, lse
+
+    def block_keep_of_bias(self, bias):
+        """[B, H, ceil(S_q/128), ceil(S_k/128)] uint8: 1 where some entry of the
+        128 x 128 block of the additive term bias [B, H, S_q, S_k] exceeds -inf."""
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        if b.ndim != 4:
+            raise ValueError("bias must be [B, H, S_q, S_k]")
+        B, H, S_q, S_k = b.shape
+        out = np.empty((B, H, (S_q + 127) // 128, (S_k + 127) // 128), dtype=np.uint8)
+        if self.lib.oracle_block_keep_of_bias(_ptr(b), B, H, S_q, S_k, _ptr(out)) != 0:
+            raise ValueError("oracle_block_keep_of_bias rejected its arguments")
+        return out
 
     def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
                          seqs=None):

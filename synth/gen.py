@@ -298,15 +298,6 @@ def make_paged_prefill(lens, q_lens, A, A_kv, d, page_size, *, dtype="bf16", see
     return pg, q, cu
 
 
-def gather_paged(cache: np.ndarray, block_table: np.ndarray, b: int, length: int) -> np.ndarray:
-    """Tokens 0..length-1 of sequence b as a contiguous [A_kv, length, d] array
-    (token t in page block_table[b, t // page_size] at offset t % page_size)."""
-    ps = cache.shape[1]
-    t = np.arange(length)
-    rows = cache[block_table[b, t // ps], t % ps]       # [length, A_kv, d]
-    return np.ascontiguousarray(rows.transpose(1, 0, 2))
-
-
 def _e4m3_positive_values() -> np.ndarray:
     """Values of the E4M3 codes 0x00..0x7E (sign bit clear, NaN excluded), by
     the OCP FP8 definition: bias 7, 3 mantissa bits, subnormals at exponent 0."""

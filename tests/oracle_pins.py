@@ -752,4 +752,281 @@ def pin_bwd_masked_row_inert(orc):
     assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
 
 
+# ---- block masks (page "Attention Kernel", section "可编程 mask": one flag per
+# 128 x 128 block of (row, key) pairs), the block mask of an additive term,
+# and the masking fill value of a finite term
+
+def _expand_blocks_by_loops(bk_bh, S_q, S_k):
+    """The element rule keep[i][j] = block flag (i // 128, j // 128), one
+    element at a time."""
+    keep = np.zeros((S_q, S_k), np.uint8)
+    for i in range(S_q):
+        for j in range(S_k):
+            keep[i, j] = 1 if bk_bh[i // 128][j // 128] else 0
+    return keep
+
+
+def pin_block_keep_element_rule(orc):
+    """A block mask equals, bit for bit, the dense keep matrix its element rule
+    defines (built here element by element), per head and per batch row, on
+    ragged sizes with more key blocks than row blocks; with causal and key
+    flags combined."""
+    rng = np.random.default_rng(61)
+    B, A, A_kv, S_q, S_k, d = 2, 2, 1, 300, 420, 4
+    q = _f32(rng.standard_normal((B, A, S_q, d)))
+    k = _f32(rng.standard_normal((B, A_kv, S_k, d)))
+    v = _f32(rng.standard_normal((B, A_kv, S_k, d)))
+    kk = (rng.random((B, S_k)) > 0.1).astype(np.uint8)
+    bk = (rng.random((B, A, 3, 4)) < 0.6).astype(np.uint8)
+    bk[0, 0, 0, :] = 1
+    bk[1, 1, 2, :] = 0                     # a row block with no key block kept
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=causal, k_keep=kk, block_keep=bk)
+        for h in range(A):
+            mk = np.stack([_expand_blocks_by_loops(bk[b, h], S_q, S_k) for b in range(B)])
+            o2, l2 = orc.attn_fwd(q[:, h:h + 1], k, v, dtype="f32", scale=0.5, causal=causal, k_keep=kk, m_keep=mk)
+            assert np.array_equal(o[:, h:h + 1], o2) and np.array_equal(lse[:, h:h + 1], l2), (causal, h)
+    assert np.all(np.isneginf(lse[1, 1, 256:]))
+    # one mask shared by the heads
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, block_keep=bk[:, :1])
+    mk = np.stack([_expand_blocks_by_loops(bk[b, 0], S_q, S_k) for b in range(B)])
+    o2, l2 = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, m_keep=mk)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def pin_block_keep_of_bias_brute_force(orc):
+    """The block mask of an additive term: 1 exactly where some entry of the
+    block (clipped to the matrix) exceeds -inf, checked block by block and
+    element by element."""
+    rng = np.random.default_rng(62)
+    B, H, S_q, S_k = 2, 2, 260, 300
+    bias = rng.standard_normal((B, H, S_q, S_k)).astype(np.float32)
+    bias[rng.random(bias.shape) < 0.97] = -np.inf
+    bias[0, 0, :128, :] = -np.inf            # a whole row of blocks masked
+    bias[1, 1, 200:, 256:] = -np.inf         # the ragged corner block masked
+    bias[1, 0, 259, 299] = np.float32(-3e38)  # a finite entry keeps its block
+    bias[1, 0, 256:259, 256:] = -np.inf
+    bias[1, 0, 259, 256:299] = -np.inf
+    got = orc.block_keep_of_bias(bias)
+    assert got.shape == (B, H, 3, 3)
+    for b in range(B):
+        for h in range(H):
+            for qb in range(3):
+                for kb in range(3):
+                    kept = 0
+                    for i in range(128 * qb, min(128 * qb + 128, S_q)):
+                        for j in range(128 * kb, min(128 * kb + 128, S_k)):
+                            if bias[b, h, i, j] > -np.inf:
+                                kept = 1
+                                break
+                        if kept:
+                            break
+                    assert got[b, h, qb, kb] == kept, (b, h, qb, kb)
+    assert got[0, 0, 0].sum() == 0 and got[1, 1, 2, 2] == 0 and got[1, 0, 2, 2] == 1
+
+
+def pin_bias_fill_value(orc):
+    """A finite term below -FLT_MAX * min(scale, ln 2) is a masking fill value:
+    a row filled with the float32 minimum is fully masked (O = 0, LSE = -inf);
+    with one key left at 0 the row sees that key alone (O = v_j exactly,
+    LSE = s_j); a large but representable term (-1e30 on every key) is an
+    ordinary constant shift (mean of V, LSE = -1e30 + ln n)."""
+    rng = np.random.default_rng(63)
+    S_k, d = 6, 3
+    q = _f32(rng.standard_normal((1, 1, 3, d)))
+    k = _f32(rng.standard_normal((1, 1, S_k, d)))
+    v = _f32(rng.standard_normal((1, 1, S_k, d)))
+    fmin = np.finfo(np.float32).min
+    bias = np.zeros((1, 1, 3, S_k), np.float32)
+    bias[0, 0, 0, :] = fmin
+    bias[0, 0, 1, :] = fmin
+    bias[0, 0, 1, 4] = 0.0
+    bias[0, 0, 2, :] = np.float32(-1e30)
+    for scale in (0.125, 2.0):
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=scale, bias=bias)
+        assert np.all(o[0, 0, 0] == 0) and np.isneginf(lse[0, 0, 0])
+        assert np.array_equal(o[0, 0, 1], v[0, 0, 4].astype(np.float64))
+        s4 = float(np.float32(scale)) * float(np.dot(q[0, 0, 1].astype(np.float64), k[0, 0, 4].astype(np.float64)))
+        assert abs(lse[0, 0, 1] - s4) < 1e-12
+        assert np.allclose(o[0, 0, 2], v[0, 0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-12)
+        m = float(np.float32(-1e30))  # the term as stored (fp32)
+        assert abs(lse[0, 0, 2] / m - 1) < 1e-15
+
+
+# ---- prefill of query chunks over a paged cache: each chunk is the tail of
+# its sequence (bottom-right positions); keys through the block table
+
+def _paged_problem(lens, q_lens, A, A_kv, d, ps, seed):
+    rng = np.random.default_rng(seed)
+    npg = [(L + ps - 1) // ps for L in lens]
+    pool = sum(npg) + 2
+    perm = rng.permutation(pool)
+    bt = np.full((len(lens), max(max(npg), 1)), -1, np.int32)
+    at = 0
+    for s, n in enumerate(npg):
+        bt[s, :n] = perm[at:at + n]
+        at += n
+    kc = _f32(rng.standard_normal((pool, ps, A_kv, d)))
+    vc = _f32(rng.standard_normal((pool, ps, A_kv, d)))
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = _f32(rng.standard_normal((A, int(cu[-1]), d)))
+    return q, kc, vc, bt, np.array(lens, np.int32), cu
+
+
+def _contiguous(cache, bt_row, L, ps):
+    """Tokens 0..L-1 of one sequence as [A_kv, L, d], token by token: token t
+    is row t % ps of page bt_row[t // ps]."""
+    out = np.zeros((cache.shape[2], L, cache.shape[3]), cache.dtype)
+    for t in range(L):
+        out[:, t] = cache[bt_row[t // ps], t % ps]
+    return out
+
+
+def pin_prefill_paged_decode_rows(orc):
+    """Chunks of one row are decode steps: bit for bit the paged decode of the
+    same sequences (causal changes nothing for the last position)."""
+    lens = [9, 1, 23, 16]
+    A, A_kv, d, ps = 4, 2, 3, 4
+    q, kc, vc, bt, sl, cu = _paged_problem(lens, [1, 1, 1, 1], A, A_kv, d, ps, 64)
+    for causal in (True, False):
+        o, lse = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=0.75, causal=causal)
+        od, ld = orc.decode_paged(np.ascontiguousarray(q.transpose(1, 0, 2)), kc, vc, bt, sl, dtype="f32",
+                                  scale=0.75)
+        assert np.array_equal(o.transpose(1, 0, 2), od) and np.array_equal(lse.T, ld)
+
+
+def pin_prefill_paged_identity_is_varlen(orc):
+    """With pages laid out in order and each whole sequence as its chunk, the
+    paged prefill is the packed varlen prefill, bit for bit."""
+    rng = np.random.default_rng(65)
+    lens = [7, 0, 12, 5]
+    A, A_kv, d, ps = 4, 2, 3, 4
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = _f32(rng.standard_normal((A, T, d)))
+    k = _f32(rng.standard_normal((A_kv, T, d)))
+    v = _f32(rng.standard_normal((A_kv, T, d)))
+    npg = [(L + ps - 1) // ps for L in lens]
+    kc = np.zeros((sum(npg), ps, A_kv, d), np.float32)
+    vc = np.zeros_like(kc)
+    bt = np.full((len(lens), max(npg)), -1, np.int32)
+    page = 0
+    for s, L in enumerate(lens):
+        for t in range(L):
+            if t % ps == 0:
+                bt[s, t // ps] = page
+                page += 1
+            kc[page - 1, t % ps] = k[:, cu[s] + t]
+            vc[page - 1, t % ps] = v[:, cu[s] + t]
+    for causal in (True, False):
+        o, lse = orc.prefill_paged(q, kc, vc, bt, np.array(lens, np.int32), cu, dtype="f32", scale=0.5,
+                                   causal=causal)
+        o2, l2 = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=0.5, causal=causal)
+        assert np.array_equal(o, o2) and np.array_equal(lse, l2), causal
+
+
+def pin_prefill_paged_chunk_tail(orc):
+    """A chunk of q_s < L rows (scattered pages) equals the last q_s rows of the
+    dense bottom-right-aligned prefill over the sequence's contiguous keys,
+    causal and with a two-sided window; an empty chunk computes nothing."""
+    import oracle as oracle_pkg
+    lens, q_lens = [13, 6, 20], [5, 0, 20]
+    A, A_kv, d, ps = 2, 1, 3, 4
+    q, kc, vc, bt, sl, cu = _paged_problem(lens, q_lens, A, A_kv, d, ps, 66)
+    for causal, window in ((True, None), (False, None), (True, (3, -1)), (False, (2, 4))):
+        o, lse = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=0.625, causal=causal, window=window)
+        for s, (L, n) in enumerate(zip(lens, q_lens)):
+            if n == 0:
+                continue
+            k = _contiguous(kc, bt[s], L, ps)[None]
+            v = _contiguous(vc, bt[s], L, ps)[None]
+            qs = q[None, :, cu[s]:cu[s + 1]]
+            mk = None if window is None else oracle_pkg.window_keep(1, n, L, window[0], window[1])
+            o2, l2 = orc.attn_fwd(qs, k, v, dtype="f32", scale=0.625, causal=causal, m_keep=mk)
+            assert np.array_equal(o[:, cu[s]:cu[s + 1]], o2[0]), (s, causal, window)
+            assert np.array_equal(lse[:, cu[s]:cu[s + 1]], l2[0]), (s, causal, window)
+
+
+# ---- gradient of the packed varlen prefill, and of block / additive masks
+
+def pin_bwd_varlen_equals_separate(orc):
+    """The varlen gradient is the dense gradient of each sequence on its own
+    (bit for bit), with keep flags, GQA, causal or not, and a window given as
+    the dense keep matrix of its definition; tokens of empty or fully masked
+    rows receive exactly zero."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(67)
+    lens = [5, 0, 9, 1, 7]
+    A, A_kv, d = 4, 2, 3
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, do = rng.standard_normal((A, T, d)), rng.standard_normal((A, T, d))
+    k, v = rng.standard_normal((A_kv, T, d)), rng.standard_normal((A_kv, T, d))
+    qk = np.ones(T, np.uint8)
+    kk = np.ones(T, np.uint8)
+    qk[[3, 10]] = 0
+    kk[[2, 8, 15, 21]] = 0
+    for causal, window in ((True, None), (False, None), (True, (2, -1)), (False, (1, 3))):
+        dq, dk, dv = orc.attn_bwd_varlen(q, k, v, do, cu, dtype="f64", scale=0.8, causal=causal, q_keep=qk,
+                                         k_keep=kk, window=window)
+        for s, L in enumerate(lens):
+            a, b = cu[s], cu[s + 1]
+            if L == 0:
+                continue
+            mk = None if window is None else oracle_pkg.window_keep(1, L, L, window[0], window[1])
+            r = orc.attn_bwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], do[None, :, a:b], dtype="f64",
+                             scale=0.8, causal=causal, q_keep=qk[None, a:b], k_keep=kk[None, a:b], m_keep=mk)
+            for g, want in zip((dq, dk, dv), r):
+                assert np.array_equal(g[:, a:b], want[0]), (causal, window, s)
+
+
+def pin_bwd_masks_finite_differences(orc):
+    """Gradients with a block mask, an additive term (finite values and -inf)
+    and both: central differences of L = sum(O * dO) through the forward."""
+    rng = np.random.default_rng(68)
+    B, A, A_kv, S_q, S_k, d = 1, 2, 1, 3, 4, 2
+    q, k, v, do = _bwd_problem(B, A, A_kv, S_q, S_k, d, 69)
+    bias = rng.standard_normal((B, A, S_q, S_k)).astype(np.float32)
+    bias[0, 0, 1, 2] = -np.inf
+    bias[0, 1, 0, :] = -np.inf
+    bk = np.ones((B, 1, 1, 1), np.uint8)
+    h = 1e-6
+    for kw in ({"bias": bias}, {"block_keep": bk}, {"bias": bias[:, :1], "block_keep": bk}):
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.6875, causal=True, **kw)
+
+        def loss(qq, kk_, vv):
+            o, _ = orc.attn_fwd(qq, kk_, vv, dtype="f64", scale=0.6875, causal=True, **kw)
+            return float(np.sum(o * do))
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                ap = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                am = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+            assert np.max(np.abs(num - g)) <= 1e-7, (list(kw), name)
+        if "bias" in kw and kw["bias"].shape[1] == A:
+            assert np.all(dq[0, 1, 0] == 0)  # the row the term masks whole has no gradient
+
+
+def pin_bwd_block_mask_is_keep_matrix(orc):
+    """A block mask in the gradient equals its dense keep matrix (element rule,
+    built element by element), bit for bit, per head."""
+    rng = np.random.default_rng(70)
+    B, A, A_kv, S_q, S_k, d = 1, 2, 2, 200, 300, 2
+    q, k, v, do = _bwd_problem(B, A, A_kv, S_q, S_k, d, 71)
+    bk = (rng.random((B, A, 2, 3)) < 0.6).astype(np.uint8)
+    bk[0, 0, 1, 0] = 1
+    bk[0, 1, 0, 2] = 0
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.5, causal=False, block_keep=bk)
+    for h in range(A):
+        mk = _expand_blocks_by_loops(bk[0, h], S_q, S_k)[None]
+        r = orc.attn_bwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], do[:, h:h + 1], dtype="f64", scale=0.5,
+                         m_keep=mk)
+        for g, want in zip((dq, dk, dv), r):
+            assert np.array_equal(g[:, h:h + 1], want), h
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -121,6 +121,7 @@ def test_attn_fwd_rejects_bad_arguments():
     assert fwd(lib, window=ct.byref(W(-2, 0))) == INVAL     # window sides are >= -1
     assert fwd(lib, window=ct.byref(W(3, -5))) == INVAL
     assert fwd(lib, S_q=0, q=None, o=None, lse=None, window=ct.byref(W(3, -1))) == OK
+    assert fwd(lib, S_q=2 ** 30, S_k=2 ** 30, A=1, A_kv=1, window=ct.byref(W(5, -1))) == UNSUP  # int32 room
 
     M = Mask
     assert fwd(lib, mask=ct.byref(M(None, None, 4096, 3))) == INVAL           # block_heads must be 1 or A
@@ -140,6 +141,78 @@ def test_attn_fwd_rejects_bad_arguments():
     with pytest.raises(ValueError):
         ea.attn_fwd(torch.zeros(1, 1, 5, 8), torch.zeros(1, 1, 5, 8), torch.zeros(1, 1, 6, 8),
                     torch.zeros(1, 1, 5, 8), torch.zeros(1, 1, 5), scale=1.0)
+
+
+def test_misaligned_pointers_are_rejected():
+    """16-byte alignment for bf16 rows and caches, 4 bytes for fp32 data, lse
+    and int32 tables (the kernels copy 16-byte groups and store rows whole)."""
+    lib = _lib()
+    INVAL = 1
+    odd8, odd2 = ctypes.c_void_p(4096 + 8), ctypes.c_void_p(4096 + 2)
+    for name in ("q", "k", "v", "o"):
+        assert fwd(lib, **{name: odd8}) == INVAL, name          # bf16: 16 bytes
+        assert fwd(lib, dt=0, **{name: odd2}) == INVAL, name    # fp32: 4 bytes
+    assert fwd(lib, lse=odd2) == INVAL
+    good = np.array([0, 5, 9], np.int32)
+    gp = good.ctypes.data_as(ctypes.c_void_p)
+    var = lambda q=P, o=P, lse=P, cu=P: lib.attn_fwd_varlen(q, P, P, o, lse, cu, gp, 2, 9, 4, 2, 64, 0.1, 1, None,
+                                                            None, 1, None)
+    assert var(q=odd8) == INVAL and var(o=odd8) == INVAL and var(lse=odd2) == INVAL and var(cu=odd2) == INVAL
+    lens = np.array([10, 40], np.int32)
+    lp = lens.ctypes.data_as(ctypes.c_void_p)
+    dec = lambda q=P, kc=P, bt=P, sl=P, lse=P: lib.attn_decode_paged(q, kc, P, bt, sl, lp, 16, P, lse, 2, 8, 2, 128,
+                                                                     3, 6, 0.1, 1, P, 1 << 30, None)
+    assert dec(q=odd8) == INVAL and dec(kc=odd8) == INVAL and dec(bt=odd2) == INVAL and dec(sl=odd2) == INVAL
+    assert dec(lse=odd2) == INVAL
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_prefill_paged.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 7 + [f, i, vp, i, vp]
+    lib.attn_prefill_paged.restype = i
+    cu = np.array([0, 5, 6], np.int32)
+    pp = lambda q=P, kc=P, lse=P, bt=P: lib.attn_prefill_paged(q, kc, P, bt, P, lp, P, cu.ctypes.data_as(vp), 16, P,
+                                                               lse, 2, 6, 8, 2, 128, 3, 6, 0.1, 1, None, 1, None)
+    assert pp(q=odd8) == INVAL and pp(kc=odd8) == INVAL and pp(lse=odd2) == INVAL and pp(bt=odd2) == INVAL
+    lib.attn_decode_paged_fp8.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 6 + [f, vp, ctypes.c_size_t, vp]
+    lib.attn_decode_paged_fp8.restype = i
+    fp8 = lambda kc=P, ks=P, q=P: lib.attn_decode_paged_fp8(q, kc, P, ks, P, P, P, lp, 16, P, P, 2, 8, 2, 128, 3, 6,
+                                                            0.1, P, 1 << 30, None)
+    assert fp8(kc=ctypes.c_void_p(4096 + 4)) == INVAL and fp8(ks=odd2) == INVAL and fp8(q=odd8) == INVAL
+
+
+WINDOW_CHECK = r'''
+#include <cassert>
+#include <climits>
+#include <cstdio>
+#include "attn_window.h"
+int main() {
+  int l, r;
+  // causal, a left edge wider than every key range: unbounded (no int32 wrap)
+  attn::window_edges(true, INT_MAX, -1, 1, 300, 300, l, r); assert(l == -1 && r == 0);
+  // non-causal, a right edge wider than the rows: unbounded
+  attn::window_edges(true, -1, INT_MAX, 0, 300, 200, l, r); assert(l == -1 && r == -1);
+  // edges that exclude some key are kept exactly
+  attn::window_edges(true, 299, 199, 0, 300, 200, l, r); assert(l == 299 && r == 199);
+  attn::window_edges(true, 300, 200, 0, 300, 200, l, r); assert(l == -1 && r == -1);
+  // causal folds the right edge to the diagonal; no window = unbounded
+  attn::window_edges(true, 7, 5, 1, 300, 300, l, r); assert(l == 7 && r == 0);
+  attn::window_edges(false, 7, 5, 0, 300, 300, l, r); assert(l == -1 && r == -1);
+  assert(attn::window_arith_fits(true, 1000, 1000) && !attn::window_arith_fits(true, 1LL << 30, 1LL << 30));
+  assert(attn::window_arith_fits(false, 1LL << 30, 1LL << 30));
+  std::puts("window edges ok");
+  return 0;
+}
+'''
+
+
+def test_window_edges_clamp(tmp_path):
+    """Window edges that exclude no key become unbounded on the host, so the
+    kernels never add INT_MAX-sized edges to positions (g++, host only)."""
+    src = tmp_path / "w.cpp"
+    src.write_text(WINDOW_CHECK)
+    exe = tmp_path / "w"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", os.path.join(ROOT, "exact_attention_108_amd", "csrc"),
+                    str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and "window edges ok" in r.stdout, r.stderr
 
 
 def test_attn_fwd_varlen_rejects_bad_arguments():

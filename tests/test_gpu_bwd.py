@@ -196,6 +196,8 @@ BWD_WINDOW_CASES = [
     (1, 2, 2, 420, 300, 128, True, (200, -1)),
     (1, 2, 2, 400, 400, 128, False, (40, 90)),
     (1, 4, 1, 350, 350, 64, True, (129, -1)),
+    (1, 2, 1, 300, 300, 128, True, (2147483647, -1)),     # the widest edge: the causal gradient
+    (1, 2, 2, 260, 300, 64, False, (2147483647, 2147483647)),
 ]
 
 

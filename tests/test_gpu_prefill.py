@@ -254,6 +254,9 @@ WINDOW_CASES = [
     (1, 2, 2, 600, 600, 128, False, (200, -1)),    # left edge only
     (2, 4, 4, 400, 400, 64, True, (129, -1)),      # d = 64
     (1, 2, 1, 300, 300, 128, True, (5000, -1)),    # window wider than the sequence = causal
+    (1, 2, 1, 300, 300, 128, True, (2147483647, -1)),   # the widest edge the header accepts (no int32 wrap)
+    (1, 2, 2, 300, 260, 128, False, (-1, 2147483647)),
+    (1, 2, 2, 260, 300, 64, False, (2147483647, 2147483647)),
 ]
 
 
@@ -343,17 +346,10 @@ def run_paged_prefill(ea, pg, q, cu, window=None, causal=True):
 
 
 def check_paged_prefill(orc, pg, q, cu, o, lse, what, window=None, causal=True):
-    for s in range(cu.size - 1):
-        a, b = int(cu[s]), int(cu[s + 1])
-        if a == b:
-            continue
-        L = int(pg.seq_lens[s])
-        k = gen.gather_paged(pg.k_cache, pg.block_table, s, L)[None]
-        v = gen.gather_paged(pg.v_cache, pg.block_table, s, L)[None]
-        mk = None if window is None else oracle.window_keep(1, b - a, L, window[0], 0 if causal else window[1])
-        o_ref, l_ref = orc.attn_fwd(q[None, :, a:b], k, v, dtype=pg.dtype, scale=pg.scale, causal=causal,
-                                    m_keep=mk)
-        gu.check(o[None, :, a:b], lse[None, :, a:b], o_ref, l_ref, pg.dtype, f"{what} seq {s}")
+    w = None if window is None else (window[0], 0 if causal else window[1])
+    o_ref, l_ref = orc.prefill_paged(q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, cu, dtype=pg.dtype,
+                                     scale=pg.scale, causal=causal, window=w)
+    gu.check(o[None], lse[None], o_ref[None], l_ref[None], pg.dtype, what)
 
 
 @pytest.mark.parametrize("d,ps", [(128, 16), (128, 64), (64, 32)])
@@ -417,12 +413,6 @@ def test_paged_prefill_equals_varlen_bitwise(ea):
 # ---- block sparsity (page "Attention Kernel", section "可编程 mask"): the
 # oracle receives the block mask expanded to the dense keep matrix it defines
 
-def block_dense(bk_b, S_q, S_k):
-    """[nqb, nkb] block mask -> [S_q, S_k] keep matrix (block (i, j) covers rows
-    128 i .. and keys 128 j ..)."""
-    return np.repeat(np.repeat(bk_b, 128, axis=0), 128, axis=1)[:S_q, :S_k]
-
-
 def run_block_sparse(ea, p, bk, window=None):
     t = gu.torch()
     q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
@@ -436,14 +426,20 @@ def run_block_sparse(ea, p, bk, window=None):
 
 
 def check_block_sparse(orc, p, bk, o, lse, what, window=None, heads=None):
+    mk = None
+    if window is not None:
+        mk = oracle.window_keep(p.B, p.S_q, p.S_k, window[0], 0 if p.causal else window[1])
+    if heads is None:
+        o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=p.causal, m_keep=mk,
+                                    block_keep=bk)
+        gu.check(o, lse, o_ref, l_ref, "bf16", what)
+        return
     G = p.A // p.A_kv
-    for h in (range(p.A) if heads is None else heads):
+    for h in heads:
         hm = 0 if bk.shape[1] == 1 else h
-        mk = np.stack([block_dense(bk[b, hm], p.S_q, p.S_k) for b in range(p.B)]).astype(np.uint8)
-        if window is not None:
-            mk &= oracle.window_keep(p.B, p.S_q, p.S_k, window[0], 0 if p.causal else window[1])
         o_ref, l_ref = orc.attn_fwd(p.q[:, h:h + 1], p.k[:, h // G:h // G + 1], p.v[:, h // G:h // G + 1],
-                                    dtype="bf16", scale=p.scale, causal=p.causal, m_keep=mk)
+                                    dtype="bf16", scale=p.scale, causal=p.causal, m_keep=mk,
+                                    block_keep=bk[:, hm:hm + 1])
         gu.check(o[:, h:h + 1], lse[:, h:h + 1], o_ref, l_ref, "bf16", f"{what} head {h}")
 
 
@@ -493,9 +489,9 @@ def test_block_sparse_full_size_sampled(ea, orc):
     bk = (rng.random((4, 1, 16, 16)) < 0.5).astype(np.uint8)
     _say("block sparse full size", int(bk.sum()), "blocks kept")
     o, lse = run_block_sparse(ea, p, bk)
-    dead = np.stack([block_dense(bk[b, 0], 2048, 2048) & np.tril(np.ones((2048, 2048), np.uint8))
-                     for b in range(4)]).sum(axis=2) == 0
-    assert np.all(np.isneginf(lse[dead[:, None, :].repeat(32, 1)]))
+    # a row is empty when no kept block of its row block reaches the causal diagonal
+    kept_upto = np.array([[[bk[b, 0, i // 128, :(i // 128) + 1].any()] for i in range(2048)] for b in range(4)])[..., 0]
+    assert np.all(np.isneginf(lse[~kept_upto[:, None, :].repeat(32, 1)]))
     check_block_sparse(orc, p, bk, o, lse, "block sparse full size", heads=[0, 17, 31])
 
 
@@ -532,15 +528,6 @@ def bias_oracle(orc, p, bias_np, *, window=None, q_keep=None, k_keep=None, rows=
                         k_keep=k_keep, m_keep=mk, bias=bias_np, rows=rows)
 
 
-def block_keep_reference(bias_np):
-    """[B, H, ceil(S_q/128), ceil(S_k/128)]: some entry of the block > -inf."""
-    B, H, S_q, S_k = bias_np.shape
-    nq, nk = (S_q + 127) // 128, (S_k + 127) // 128
-    pad = np.full((B, H, nq * 128, nk * 128), -np.inf, np.float32)
-    pad[:, :, :S_q, :S_k] = bias_np
-    return (pad.reshape(B, H, nq, 128, nk, 128) > -np.inf).any(axis=(3, 5)).astype(np.uint8)
-
-
 BIAS_CASES = [
     # B, A, A_kv, S_q, S_k, d, causal, window, heads, kind, blocks, keep masks
     (2, 4, 2, 300, 300, 128, True, None, 1, "document", True, False),
@@ -567,9 +554,30 @@ def test_bias_bf16(ea, orc, case):
     kk = p.k_keep if keeps else None
     o, lse, bk = run_bias(ea, p, bias, window=window, blocks=blocks, q_keep=qk, k_keep=kk)
     if blocks:
-        assert np.array_equal(bk, block_keep_reference(bias))
+        assert np.array_equal(bk, orc.block_keep_of_bias(bias))
     o_ref, l_ref = bias_oracle(orc, p, bias, window=window, q_keep=qk, k_keep=kk)
     _say(gu.check(o, lse, o_ref, l_ref, "bf16", str(case)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bias_fill_value_rows(ea, orc, dtype):
+    """Rows of the additive term filled with the float32 minimum (the usual
+    fill value of additive masks) are fully masked: O = 0, LSE = -inf; a row
+    with the fill value everywhere but one key sees that key alone; other rows
+    mix the fill value with finite terms."""
+    d = 128 if dtype == "bf16" else 64
+    p = gen.make_dense(1, 2, 1, 150, 200, d, dtype=dtype, causal=False, seed=1210)
+    bias = gen.make_bias(1, 2, 150, 200, "random", 1210)
+    fmin = np.finfo(np.float32).min
+    bias[0, 0, 3, :] = fmin
+    bias[0, 1, 7:20, :] = fmin
+    bias[0, 1, 9, 55] = 0.0
+    bias[0, 0, 40:, 100:] = fmin
+    _say("fill value rows", dtype)
+    o, lse, _ = run_bias(ea, p, bias)
+    o_ref, l_ref = bias_oracle(orc, p, bias)
+    assert np.all(o[0, 0, 3] == 0) and np.isneginf(lse[0, 0, 3]) and np.isneginf(lse[0, 1, 8])
+    _say(gu.check(o, lse, o_ref, l_ref, dtype, f"fill value rows {dtype}"))
 
 
 def test_bias_f32(ea, orc):
@@ -615,7 +623,7 @@ def test_bias_full_size_sampled(ea, orc):
     p = gen.make_config(2)
     bias = gen.make_bias(p.B, 1, p.S_q, p.S_k, "document", 1203)
     o, lse, bk = run_bias(ea, p, bias, blocks=True)
-    assert np.array_equal(bk, block_keep_reference(bias))
+    assert np.array_equal(bk, orc.block_keep_of_bias(bias))
     rng = np.random.default_rng(1203)
     rows = _sample_rows(rng, p.B, p.A, p.S_q, 1200)
     o_ref, l_ref = bias_oracle(orc, p, bias, rows=rows)

@@ -79,12 +79,9 @@ def test_sweep_dense_bf16(ea, orc, case):
     mk = None
     if window is not None:
         mk = oracle.window_keep(B, S_q, S_k, window[0], 0 if causal else window[1])
-    if bk is not None:
-        bd = np.stack([np.repeat(np.repeat(bk[b, 0], 128, 0), 128, 1)[:S_q, :S_k] for b in range(B)]).astype(np.uint8)
-        mk = bd if mk is None else (mk & bd)
     o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal,
                                 q_keep=p.q_keep if keeps else None, k_keep=p.k_keep if keeps else None, m_keep=mk,
-                                bias=bias_np)
+                                bias=bias_np, block_keep=bk)
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", str(case)))
 
 

@@ -1,5 +1,4 @@
-"""The seeded input generators (CPU only): the FP8 test-cache quantiser, and
-the paged helpers the paged-prefill reference uses."""
+"""The seeded input generators (CPU only): the FP8 test-cache quantiser."""
 import numpy as np
 
 from synth import gen
@@ -21,10 +20,3 @@ def test_e4m3_round_trip_and_ties():
     mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)                          # exact midpoints (fp32)
     got = gen.quantize_e4m3(mids)
     assert np.all(got % 2 == 0) and np.all((got == codes[:-1]) | (got == codes[1:]))   # ties to the even code
-
-
-def test_gather_paged_follows_block_table():
-    pg = gen.make_paged([40, 3], 2, 2, 8, 16, dtype="f32", seed=5, extra_pages=2)
-    k = gen.gather_paged(pg.k_cache, pg.block_table, 0, 40)
-    for t in (0, 15, 16, 39):
-        assert np.array_equal(k[:, t], pg.k_cache[pg.block_table[0, t // 16], t % 16])

@@ -53,6 +53,35 @@ MUTANTS = [
     ("additive term subtracted", "s[j] += (double)bias_row[j];", "s[j] -= (double)bias_row[j];", 0),
     ("additive term: head ignored", "(bias_heads == 1 ? 0 : h)", "0", 0),
     ("additive term: row ignored", "* S_q + i) * S_k : NULL;", "* S_q + 0) * S_k : NULL;", 0),
+    ("additive term: fill value kept finite", "if ((double)bias_row[j] < fill_limit(scale))", "if (0)", 0),
+    ("additive term: fill limit without the scale", "return -flt_max * (scale < ln2 ? scale : ln2);",
+     "return -flt_max;", 0),
+    ("block mask: 64-wide blocks", "i / 128) * nkb + j / 128]", "i / 64) * nkb + j / 64]", 1),
+    ("block mask: index transposed", "* nqb + i / 128) * nkb + j / 128]", "* nkb + j / 128) * nqb + i / 128]", 1),
+    ("block mask: head ignored", "int hm = block_heads == 1 ? 0 : h;", "int hm = 0;", 0),
+    ("block mask ignored (dense)", "if (!block_kept(block_keep, block_heads, b, h, S_q, S_k, i, j))", "if (0)", 1),
+    ("gradient: block mask ignored", "if (!block_kept(block_keep, block_heads, b, h, S_q, S_k, i, j))", "if (0)", 2),
+    ("gradient: additive term ignored", "w.vis, bias_row, S_k, d, sc, w.s, w.p, o, &lse);",
+     "w.vis, NULL, S_k, d, sc, w.s, w.p, o, &lse);", 0),
+    ("block mask of a bias: 64-wide blocks", "out[(bh * nqb + i / 128) * nkb + j / 128] = 1;",
+     "out[(bh * nqb + i / 64) * nkb + j / 64] = 1;", 0),
+    ("block mask of a bias: finite negatives ignored", "if (row[j] > -INFINITY)", "if (row[j] > -1e30f)", 0),
+    ("block mask of a bias: row stride S_q", "const float *row = bias + (bh * S_q + i) * (int64_t)S_k;",
+     "const float *row = bias + (bh * S_q + i) * (int64_t)S_q;", 0),
+    ("paged prefill: page offset uses page index", "int off = t % page_size;", "int off = (t / page_size) % page_size;", 2),
+    ("paged prefill: chunk aligned top-left", "int pos = L - q_len + (x - cu_q[s]);", "int pos = x - cu_q[s];", 0),
+    ("paged prefill: causal diagonal excluded", "if (causal && t > pos)", "if (causal && t >= pos)", 0),
+    ("paged prefill: window left edge ignored", "if (win_left >= 0 && t < pos - win_left)", "if (0)", 0),
+    ("paged prefill: window right edge ignored", "if (win_right >= 0 && t > pos + win_right)", "if (0)", 0),
+    ("paged prefill: GQA head taken modulo", "int hk = h / G;", "int hk = h % A_kv;", 3),
+    ("varlen gradient: keys not offset to sequence", "int64_t kv_base = ((int64_t)hk * T + start) * d;",
+     "int64_t kv_base = ((int64_t)hk * T) * d;", 0),
+    ("varlen gradient: window left edge ignored", "if (win_left >= 0 && j < i - win_left)", "if (0)", 0),
+    ("varlen gradient: window right edge off by one", "if (win_right >= 0 && j > i + win_right)",
+     "if (win_right >= 0 && j >= i + win_right)", 0),
+    ("varlen gradient: D term dropped", "double ds = w.p[j] * (dp[j] - D);", "double ds = w.p[j] * dp[j];", 2),
+    ("varlen gradient: key flags ignored", "if (k_keep && !k_keep[start + j])\n                            visible = 0;",
+     "if (0)\n                            visible = 0;", 0),
 ]
 
 BATTERY = r"""
