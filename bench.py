@@ -6,7 +6,9 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   2. paged single-query decode, bf16, 64 sequences with lengths ~U{512..32768},
      page 16, A=32 A_kv=8 d=128 (split + LSE merge; KV GB/s),
   3. packed varlen causal prefill, bf16, 16 log-normal sequences, A=16 d=64,
-     5% of query rows fully masked (causal-adjusted TFLOP/s).
+     5% of query rows fully masked (causal-adjusted TFLOP/s),
+  4. long GQA causal prefill, bf16, B=1 A=32 A_kv=8 S_q=S_k=16384 d=128, V~U(-1,1)
+     (causal-adjusted TFLOP/s, with its own roofline object under "gqa_long").
 Inputs are resident in HBM before the timed region.  Each launch is bracketed
 by HIP events recorded on the stream the library launches on.
 
@@ -38,6 +40,12 @@ reported beside them:
 The summary records a hash of the code of each kernel's sources (comments and
 layout excluded); a later bench run reports `traffic` only while that code is
 unchanged (null otherwise).
+
+Per-workload kernel times from one kernel trace of this same command (the
+dense prefill kernel serves three workloads; they are told apart by grid size):
+
+    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline
+    python3 bench.py --trace-summary <dir_t> > profiles/kernel_trace_<...>.md
 
 Matrix-core utilisation of the prefill kernels, from one counter run:
 
@@ -165,6 +173,13 @@ def load_inputs(log_fn=lambda *a: None):
     cu5 = to_dev(p5.cu_seqlens, "i32")
     qk5 = to_dev(p5.q_keep, "u8")
     log_fn(f"varlen inputs ready ({time.time() - t0:.1f}s): T={p5.T}")
+
+    t0 = time.time()
+    p3 = gen.make_config(3)
+    q3, k3, v3 = to_dev(p3.q, "bf16"), to_dev(p3.k, "bf16"), to_dev(p3.v, "bf16")
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty((p3.B, p3.A, p3.S_q), dtype=torch.float32, device="cuda")
+    log_fn(f"long GQA prefill inputs ready ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -178,9 +193,12 @@ def load_inputs(log_fn=lambda *a: None):
         ea.attn_fwd_varlen(q5, k5, v5, o5, l5, cu5, p5.cu_seqlens, scale=p5.scale, causal=True, q_keep=qk5,
                            stream=stream)
 
-    return dict(p2=p2, p4=p4, p5=p5, kv_bytes=kv_bytes, ws_bytes=ws_bytes, stream=stream,
+    def gqa_long():
+        ea.attn_fwd(q3, k3, v3, o3, l3, scale=p3.scale, causal=True, stream=stream)
+
+    return dict(p2=p2, p3=p3, p4=p4, p5=p5, kv_bytes=kv_bytes, ws_bytes=ws_bytes, stream=stream,
                 dev2=(q2, k2, v2, o2, l2), dev4=(kc4, vc4, bt4, sl4),
-                parts=[("prefill", prefill), ("decode", decode), ("varlen", varlen)])
+                parts=[("prefill", prefill), ("decode", decode), ("varlen", varlen), ("gqa_long", gqa_long)])
 
 
 def traffic_workload():
@@ -221,11 +239,11 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
                     w = value_of(r["Counter_Name"])
                     if w is None:
                         continue
-                    key = (r["Kernel_Name"], r["Dispatch_Id"])
+                    key = (r["Kernel_Name"], grid_of(r), r["Dispatch_Id"])
                     by[key] = by.get(key, 0.0) + w * float(r["Counter_Value"])
         out = {}
-        for (kname, _), v in by.items():
-            out.setdefault(kname, []).append(v)
+        for (kname, grid, _), v in by.items():
+            out.setdefault((kname, grid), []).append(v)
         return out
 
     def mean(tab):
@@ -235,8 +253,6 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
     read_d = per_kernel(dir_read, lambda c: sizes.get(c))                          # bytes
     write_d = per_kernel(dir_write, lambda c: 1024.0 if c == "WRITE_SIZE" else None)  # KiB -> bytes
     fetch_d = per_kernel(dir_fetch, lambda c: 1024.0 if c == "FETCH_SIZE" else None)
-    read, write, fetch = mean(read_d), mean(write_d), mean(fetch_d)
-    nr = {k: len(v) for k, v in read_d.items()}
 
     def pick(tab, pred):
         ks = [k for k in tab if pred(k)]
@@ -244,19 +260,21 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
         return ks[0]
 
     # the reference copy: the largest dispatches of the runtime's copy kernel
-    # (the small ones are the input uploads)
-    is_copy = lambda k: "copybuffer" in k.lower()
-    cr, cw, cf = pick(read, is_copy), pick(write, is_copy), pick(fetch, is_copy)
+    # (the small ones are the input uploads), whatever their grid
+    def merge_grids(d):
+        out = {}
+        for (kname, grid), v in d.items():
+            key = ("copy", 0) if "copybuffer" in kname.lower() else (kname, grid)
+            out.setdefault(key, []).extend(v)
+        return out
+    read_d, write_d, fetch_d = merge_grids(read_d), merge_grids(write_d), merge_grids(fetch_d)
+    read, write, fetch = mean(read_d), mean(write_d), mean(fetch_d)
+    nr = {k: len(v) for k, v in read_d.items()}
+    cr = cw = cf = ("copy", 0)
     read[cr], write[cw], fetch[cf] = max(read_d[cr]), max(write_d[cw]), max(fetch_d[cf])
     r_scale, w_scale, f_scale = COPY_BYTES / read[cr], COPY_BYTES / write[cw], COPY_BYTES / fetch[cf]
-    kernels = {
-        "prefill": lambda k: "prefill_bf16_kernel<128, false, false, false, false>" in k,
-        "varlen": lambda k: "prefill_bf16_kernel<64, true, false, false, false>" in k,
-        "decode_split": lambda k: "decode_split_kernel" in k,
-        "decode_merge": lambda k: "decode_merge_kernel" in k,
-        "bwd_dq": lambda k: "bwd_dq_kernel<128>" in k,
-        "bwd_dkdv": lambda k: "bwd_dkdv_kernel<128," in k,
-    }
+    kernels = {part: (lambda k, pat=pat, wgs=wgs: k[0] != "copy" and grid_matches(k[0], k[1], pat, wgs))
+               for part, (pat, wgs) in TRAFFIC_PARTS.items()}
     rows, rec = [], {}
     for part, pred in kernels.items():
         kr, kw, kf = pick(read, pred), pick(write, pred), pick(fetch, pred)
@@ -266,6 +284,8 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
     out = {"copy_read_scale": r_scale, "copy_write_scale": w_scale, "copy_fetch_size_scale": f_scale,
            "prefill": {"bytes_per_launch": sum(rec["prefill"]), "read_bytes": rec["prefill"][0],
                        "write_bytes": rec["prefill"][1], "source_hash": source_hash("prefill")},
+           "gqa_long": {"bytes_per_launch": sum(rec["gqa_long"]), "read_bytes": rec["gqa_long"][0],
+                        "write_bytes": rec["gqa_long"][1], "source_hash": source_hash("prefill")},
            "decode": {"bytes_per_launch": sum(rec["decode_split"]) + sum(rec["decode_merge"]),
                       "source_hash": source_hash("decode")},
            "backward": {"bytes_per_launch": sum(rec["bwd_dq"]) + sum(rec["bwd_dkdv"]),
@@ -278,7 +298,7 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
     print("    rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o p -- python3 bench.py --traffic-workload")
     print("    rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o p -- python3 bench.py --traffic-workload")
     print("    python3 bench.py --traffic-summary <dir_r> <dir_w> <dir_f>\n")
-    print(f"Scale reference: a {COPY_BYTES >> 20} MiB device copy (`{cr[:60]}`) reads "
+    print(f"Scale reference: a {COPY_BYTES >> 20} MiB device copy (the runtime's copy kernel) reads "
           f"{read[cr] / 2**20:.1f} MiB by request size ({r_scale:.4f}x to the true {COPY_BYTES >> 20} MiB), "
           f"writes {write[cw] / 2**20:.1f} MiB by WRITE_SIZE ({w_scale:.4f}x) and shows "
           f"{fetch[cf] / 2**20:.1f} MiB by FETCH_SIZE ({f_scale:.4f}x).\n")
@@ -286,12 +306,92 @@ def traffic_summary(dir_read: str, dir_write: str, dir_fetch: str):
           "| write MB (scaled) | FETCH_SIZE MB (scaled) |")
     print("|---|---|---|---|---|---|---|---|---|")
     for part, k, n, r, w, f, rb, wb, fb in rows:
-        print(f"| {part} | `{k[:60]}` | {n} | {r / 2**20:.1f} | {w / 2**20:.1f} | {f / 2**20:.1f} | {rb / 1e6:.1f} "
-              f"| {wb / 1e6:.1f} | {fb / 1e6:.1f} |")
+        print(f"| {part} | `{k[0][:60]}` (grid {k[1]}) | {n} | {r / 2**20:.1f} | {w / 2**20:.1f} | {f / 2**20:.1f} "
+              f"| {rb / 1e6:.1f} | {wb / 1e6:.1f} | {fb / 1e6:.1f} |")
     print()
     print("Each `source_hash` is the hash of the code of the kernel's sources (comments and layout removed); "
           "`bench.py` reports a traffic figure only while it matches the current sources.\n")
     print("traffic-json: " + json.dumps(out))
+
+
+def grid_of(row) -> int:
+    """Grid size of a dispatch in a rocprofv3 CSV row (work-items)."""
+    for key in ("Grid_Size", "Grid_Size_X"):
+        if row.get(key) not in (None, ""):
+            return int(float(row[key]))
+    return 0
+
+
+def grid_matches(kname: str, grid: int, pattern: str, wgs) -> bool:
+    """Whether a dispatch is `pattern`'s kernel with `wgs` workgroups of 256
+    work-items (None: any grid)."""
+    return pattern in kname and (wgs is None or grid in (wgs, wgs * 256))
+
+
+# Kernel and workgroup count of each workload's launch; the dense prefill
+# kernel serves the MHA workload (16 query tiles x 32 heads x 4 batch rows), the
+# long GQA workload (128 x 32) and the sliding-window leg (256 x 32), so the
+# grid tells them apart.
+DENSE = "prefill_bf16_kernel<128, false, false, false, false>"
+TRAFFIC_PARTS = {
+    "prefill": (DENSE, 2048),
+    "gqa_long": (DENSE, 4096),
+    "varlen": ("prefill_bf16_kernel<64, true, false, false, false>", None),
+    "decode_split": ("decode_split_kernel<128, 1, false>", None),
+    "decode_merge": ("decode_merge_kernel", None),
+    "bwd_dq": ("bwd_dq_kernel<128>", None),
+    "bwd_dkdv": ("bwd_dkdv_kernel<128,", None),
+}
+TRACE_ROWS = [  # (label, kernel pattern, workgroups or None, algorithmic work per launch: (amount, unit) or None)
+    ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, (1.374389534720e11, "TFLOP/s")),
+    ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, (2.199023255552e12, "TFLOP/s")),
+    ("sliding-window GQA causal prefill S=32768, 4096-key window", DENSE, 8192, None),
+    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false>", None, None),
+    ("paged decode split (bf16 cache)", "decode_split_kernel<128, 1, false>", None, None),
+    ("paged decode LSE merge (bf16 and FP8 legs)", "decode_merge_kernel<128>", None, None),
+    ("paged decode split (FP8 cache)", "decode_split_kernel<128, 2, true>", None, None),
+    ("backward dQ pass", "bwd_dq_kernel<128>", None, None),
+    ("backward dK/dV pass", "bwd_dkdv_kernel<128,", None, None),
+    ("paged chunked prefill", "prefill_bf16_kernel<128, true, true, false, false>", None, None),
+    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false>", None, None),
+    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true>", None,
+     None),
+    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true>", None, None),
+    ("block mask of an additive term", "block_keep_kernel", None, None),
+]
+
+
+def trace_summary(d: str):
+    """Markdown table of one kernel trace of the bench: the library's kernels,
+    one row per (kernel, workload), so that no row mixes two workloads."""
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    assert files, f"no kernel_trace.csv under {d}"
+    disp = []
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                disp.append((r["Kernel_Name"], grid_of(r), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    print("# Kernel trace of the bench, per kernel and workload\n")
+    print("Commands (repository root, one MI355X):\n")
+    print("    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 10 --warmup 2 "
+          "--no-cpu-baseline")
+    print("    python3 bench.py --trace-summary <dir_t>\n")
+    print("Each row: the dispatches of one kernel at one workload's grid (warm-up and timed launches).  "
+          "Rate = algorithmic work per launch / average duration.\n")
+    print("| workload | kernel | grid (work-items) | calls | avg us | median us | min us | rate at avg |")
+    print("|---|---|---|---|---|---|---|---|")
+    for label, pat, wgs, work in TRACE_ROWS:
+        ts = sorted(t for k, g, t in disp if grid_matches(k, g, pat, wgs))
+        if not ts:
+            continue
+        grids = sorted({g for k, g, t in disp if grid_matches(k, g, pat, wgs)})
+        avg = sum(ts) / len(ts)
+        rate = ""
+        if work:
+            rate = f"{work[0] / (avg * 1e-9) / 1e12:.1f} {work[1]} ({100 * work[0] / (avg * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of 2500)"
+        print(f"| {label} | `{pat}` | {','.join(map(str, grids))} | {len(ts)} | {avg / 1e3:.1f} | "
+              f"{ts[len(ts) // 2] / 1e3:.1f} | {ts[0] / 1e3:.1f} | {rate} |")
 
 
 N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
@@ -306,13 +406,12 @@ def counter_summary(d: str):
     for path in files:
         with open(path) as fh:
             for r in csv.DictReader(fh):
-                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                key = (r["Kernel_Name"], grid_of(r), r["Dispatch_Id"])
                 by.setdefault(key, {})
                 by[key][r["Counter_Name"]] = by[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
                 span[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-    kernels = {"prefill": "prefill_bf16_kernel<128, false, false, false, false>", "varlen": "prefill_bf16_kernel<64, true, false, false, false>",
-               "decode_split": "decode_split_kernel", "bwd_dq": "bwd_dq_kernel<128>",
-               "bwd_dkdv": "bwd_dkdv_kernel<128,"}
+    kernels = {part: TRAFFIC_PARTS[part] for part in ("prefill", "gqa_long", "varlen", "decode_split", "bwd_dq",
+                                                      "bwd_dkdv")}
     print("# Matrix-core utilisation per launch (SQ / GRBM counters)\n")
     print("Commands (repository root, one MI355X):\n")
     print("    rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
@@ -325,8 +424,8 @@ def counter_summary(d: str):
     print("| part | launches | duration us | kernel cycles | clock GHz | MFMA instr | MFMA busy | VALU instr / MFMA "
           "| exp / MFMA | wave time waiting |")
     print("|---|---|---|---|---|---|---|---|---|---|")
-    for part, pat in kernels.items():
-        rows = [(v, span[k]) for k, v in by.items() if pat in k[0]]
+    for part, (pat, wgs) in kernels.items():
+        rows = [(v, span[k]) for k, v in by.items() if grid_matches(k[0], k[1], pat, wgs)]
         if not rows:
             continue
         n = len(rows)
@@ -352,7 +451,11 @@ def main():
     ap.add_argument("--traffic-summary", nargs=3, metavar=("READ_DIR", "WRITE_DIR", "FETCH_DIR"),
                     help="summarise three counter runs of --traffic-workload and exit")
     ap.add_argument("--counter-summary", metavar="DIR", help="summarise one SQ counter run and exit")
+    ap.add_argument("--trace-summary", metavar="DIR", help="summarise one kernel trace of the bench and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.counter_summary:
         counter_summary(args.counter_summary)
         return
@@ -405,12 +508,16 @@ def main():
     ceil = measured_ceilings(w["stream"])
 
     f2 = p2.flops()
+    f3 = w["p3"].flops()
     f5 = p5.flops()
     tf2 = f2 / (avg["prefill"] * 1e-3) / 1e12
+    tf3 = f3 / (avg["gqa_long"] * 1e-3) / 1e12
     tf5 = f5 / (avg["varlen"] * 1e-3) / 1e12
     gbs4 = kv_bytes / (avg["decode"] * 1e-3) / 1e9
     traffic_prefill, traffic_src = committed_traffic("prefill")
+    traffic_gqa, traffic_gqa_src = committed_traffic("gqa_long")
     traffic_decode, _ = committed_traffic("decode")
+    p3 = w["p3"]
 
     out = {
         "metric": METRIC,
@@ -427,7 +534,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs rounded to bf16; page permutation and lengths seeded)",
         "config": {
             "workload": "causal MHA prefill B=4 A=A_kv=32 S_q=S_k=2048 d=128 bf16 + paged decode 64 seqs "
-                        "A=32 A_kv=8 d=128 page 16 lens~U{512..32768} + varlen causal 16 seqs A=16 d=64",
+                        "A=32 A_kv=8 d=128 page 16 lens~U{512..32768} + varlen causal 16 seqs A=16 d=64 + GQA "
+                        "causal prefill B=1 A=32 A_kv=8 S_q=S_k=16384 d=128",
             "prefill": {"B": p2.B, "A": p2.A, "A_kv": p2.A_kv, "S_q": p2.S_q, "S_k": p2.S_k, "d": p2.d,
                         "causal": True, "flops_causal_adjusted": f2},
         },
@@ -453,6 +561,19 @@ def main():
                    "min_ms": round(mn["decode"], 5),
                    "kv_bytes": kv_bytes, "total_tokens": int(np.sum(p4.seq_lens, dtype=np.int64)),
                    "workspace_bytes": ws_bytes},
+        "gqa_long": {"metric": "GQA causal prefill TFLOP/s (causal-adjusted)", "value": round(tf3, 2),
+                     "unit": "TFLOP/s",
+                     "roofline": {"bound": "mfma", "achieved": round(tf3, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf3 / PEAK_BF16_TFLOPS, 4),
+                                  "traffic": None if traffic_gqa is None else round(traffic_gqa),
+                                  "traffic_unit": "bytes per launch (HBM, counter-scaled)",
+                                  "traffic_source": traffic_gqa_src, "algorithmic_bytes": p3.io_bytes(),
+                                  "kernel": DENSE + " (grid 4096 workgroups)",
+                                  "avg_launch_ms": round(avg["gqa_long"], 5),
+                                  "median_launch_ms": round(med["gqa_long"], 5),
+                                  "min_launch_ms": round(mn["gqa_long"], 5)},
+                     "config": {"B": p3.B, "A": p3.A, "A_kv": p3.A_kv, "S_q": p3.S_q, "S_k": p3.S_k, "d": p3.d,
+                                "causal": True, "flops_causal_adjusted": f3}},
         "varlen": {"metric": "varlen causal prefill TFLOP/s", "value": round(tf5, 2), "unit": "TFLOP/s",
                    "frac_of_bf16_peak": round(tf5 / PEAK_BF16_TFLOPS, 4), "avg_ms": round(avg["varlen"], 5),
                    "median_ms": round(med["varlen"], 5), "min_ms": round(mn["varlen"], 5),
@@ -470,6 +591,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(p4, kv_bytes, args.cpu_seconds / 3)
         out["varlen"]["cpu_baseline"] = cpu_baseline_varlen(p5, args.cpu_seconds / 3)
+        out["gqa_long"]["cpu_baseline"] = cpu_baseline_gqa(p3, args.cpu_seconds / 3)
     print(json.dumps(out), flush=True)
 
 
@@ -545,14 +667,15 @@ def window_pairs(S: int, left: int) -> int:
 
 
 def bench_window(steps: int, warmup: int, stream) -> dict:
-    """Causal sliding-window prefill, GQA B=1 A=32 A_kv=8 S=16384 d=128, each
+    """Causal sliding-window prefill, GQA B=1 A=32 A_kv=8 S=32768 d=128, each
     query sees its own key and the 4095 before it: key tiles outside every
     row's window are skipped whole.  FLOPs = 4 d A x (kept pairs per head),
-    the window analogue of the causal-adjusted count."""
+    the window analogue of the causal-adjusted count.  (S = 32768 also gives
+    this leg a grid of its own in kernel traces: 8192 workgroups.)"""
     import torch
     import exact_attention_108_amd as ea
     from synth import gen
-    B, A, A_kv, S, d, left = 1, 32, 8, 16384, 128, 4095
+    B, A, A_kv, S, d, left = 1, 32, 8, 32768, 128, 4095
     p = gen.make_dense(B, A, A_kv, S, S, d, dtype="bf16", causal=True, seed=1006)
     q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
     o = torch.empty_like(q)
@@ -873,7 +996,8 @@ def cpu_baseline_decode(p4, kv_bytes: float, target_s: float) -> dict:
         work += lens[rows].sum()
     est = spent * lens.sum() / work
     log(f"oracle decode: {done} rows in {spent:.1f}s")
-    return {"value": round(kv_bytes / est / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+    return {"value": round(kv_bytes / est / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} uniformly drawn (sequence, head) rows of the paged decode ({spent:.1f}s), "
                       f"extrapolated by their share of KV tokens to all {total_rows} rows ({est:.0f}s)"}
 
@@ -901,37 +1025,59 @@ def cpu_baseline_varlen(p5, target_s: float) -> dict:
     est = spent * cost.sum() / work
     log(f"oracle varlen: {done} rows in {spent:.1f}s")
     return {"value": round(p5.flops() / est / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} uniformly drawn query rows of the varlen workload ({spent:.1f}s), extrapolated "
                       f"by their share of visible keys to all {total_rows} rows ({est:.0f}s)"}
 
 
-def cpu_baseline(p2, target_s: float) -> dict:
-    """The fp64 oracle on uniformly drawn query rows of the prefill workload,
-    extrapolated to all rows (same causal-adjusted FLOP count as `value`)."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_dense_rows(p, target_s: float, seed: int, what: str) -> dict:
+    """The fp64 oracle on query rows of a causal dense workload drawn without
+    replacement (one seeded permutation, taken in order), extrapolated by the
+    rows' share of visible keys (row i of a causal head sees i + 1 keys)."""
     import oracle
     orc = oracle.default()
-    total_rows = p2.B * p2.A * p2.S_q
-    rng = np.random.default_rng(2024)
-    n = 256
-    spent, done_rows = 0.0, 0
-    while True:
-        rows = rng.choice(total_rows, size=n, replace=False)
+    total_rows = p.B * p.A * p.S_q
+    cost = np.tile(np.arange(1, p.S_q + 1, dtype=np.float64), p.B * p.A)
+    order = np.random.default_rng(seed).permutation(total_rows)
+    n, spent, done, work = 256, 0.0, 0, 0.0
+    while done < total_rows and spent < target_s:
+        rows = np.sort(order[done:done + n])
         t0 = time.perf_counter()
-        orc.attn_fwd(p2.q, p2.k, p2.v, dtype="bf16", scale=p2.scale, causal=True, rows=rows)
+        orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True, rows=rows)
         dt = time.perf_counter() - t0
         spent += dt
-        done_rows += n
-        log(f"oracle: {done_rows} rows in {spent:.1f}s")
-        if spent >= target_s or done_rows >= total_rows:
-            break
-        n = int(min(total_rows - done_rows, max(n, n * (target_s - spent) / max(dt, 1e-3))))
-        n = max(n, 64)
-    est = spent * total_rows / done_rows
-    return {"value": round(p2.flops() / est / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
-            "kind": "oracle",
-            "sample": f"{done_rows} uniformly drawn query rows of the causal B=4 A=32 S=2048 d=128 prefill "
-                      f"({spent:.1f}s), extrapolated to all {total_rows} rows ({est:.0f}s)"}
+        done += rows.size
+        work += cost[rows].sum()
+        log(f"oracle {what}: {done} rows in {spent:.1f}s")
+        n = int(max(64, min(total_rows - done, n * max(1.0, (target_s - spent) / max(dt, 1e-3)))))
+    est = spent * cost.sum() / work
+    return {"value": round(p.flops() / est / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{done} query rows of the {what} drawn without replacement ({spent:.1f}s), extrapolated "
+                      f"by their share of visible keys to all {total_rows} rows ({est:.0f}s)"}
+
+
+def cpu_baseline(p2, target_s: float) -> dict:
+    """The fp64 oracle on sampled query rows of the MHA prefill workload (same
+    causal-adjusted FLOP count as `value`)."""
+    return _oracle_dense_rows(p2, target_s, 2024, "causal B=4 A=32 S=2048 d=128 prefill")
+
+
+def cpu_baseline_gqa(p3, target_s: float) -> dict:
+    """The fp64 oracle on sampled query rows of the long GQA prefill workload."""
+    return _oracle_dense_rows(p3, target_s, 2027, "GQA causal B=1 A=32 A_kv=8 S=16384 d=128 prefill")
 
 
 if __name__ == "__main__":

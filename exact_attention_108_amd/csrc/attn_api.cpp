@@ -5,12 +5,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
 
 #include "attn_bwd.h"
 #include "attn_kernels.h"
+#include "attn_window.h"
 
 #define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -24,17 +26,24 @@ attn_status launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATT
 
 bool valid_window(const attn_window* w) { return w == nullptr || (w->left >= -1 && w->right >= -1); }
 
-// window edges as the kernels take them: -1 = unbounded; causal makes the
-// right edge min(right, 0), which is 0 for every valid right (>= -1)
-void window_edges(const attn_window* w, int causal, int& left, int& right) {
-  left = w ? w->left : -1;
-  right = w ? w->right : -1;
-  if (causal) right = 0;
+void window_edges(const attn_window* w, int causal, long long key_extent, long long row_extent, int& left,
+                  int& right) {
+  attn::window_edges(w != nullptr, w ? w->left : -1, w ? w->right : -1, causal, key_extent, row_extent, left, right);
 }
+
+bool window_arith_fits(const attn_window* w, long long rows, long long keys) {
+  return attn::window_arith_fits(w != nullptr, rows, keys);
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// tensor alignment the kernels' vector loads and stores need: 16 bytes for
+// bf16 rows (16-byte copies into LDS and stores), 4 for fp32 elements
+uintptr_t data_align(attn_dtype dtype) { return dtype == ATTN_BF16 ? 16 : 4; }
 
 attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o, float* lse,
                             int A, int A_kv, int d_h, float scale, int causal, const attn_mask* mask,
-                            const attn_window* window) {
+                            const attn_window* window, long long key_extent, long long row_extent) {
   attn::FwdParams p{};
   p.q = q;
   p.k = k;
@@ -50,7 +59,7 @@ attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  window_edges(window, causal, p.win_left, p.win_right);
+  window_edges(window, causal, key_extent, row_extent, p.win_left, p.win_right);
   return p;
 }
 
@@ -82,8 +91,12 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
   if (S_q > 0 && (!q || !o || !lse)) return ATTN_ERR_INVAL;
   if (S_k > 0 && (!k || !v)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k, v, (const void*)o})
+    if (!aligned(t, data_align(dtype))) return ATTN_ERR_INVAL;
+  if (!aligned(lse, 4)) return ATTN_ERR_INVAL;
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
+  if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
   const bool blocks = mask && mask->block_keep;
   if (blocks) {
     if (mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
@@ -98,7 +111,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   // element offsets inside the kernels are size_t; per-(b,h) row counts are int
   if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
     return ATTN_ERR_UNSUPPORTED;
-  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window);
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window, S_k, S_q);
   p.B = B;
   p.S_q = S_q;
   p.S_k = S_k;
@@ -144,6 +157,9 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   for (int s = 0; s < n_seq; ++s)
     if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return ATTN_ERR_INVAL;
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k, v, (const void*)o})
+    if (!aligned(t, data_align(dtype))) return ATTN_ERR_INVAL;
+  if (!aligned(lse, 4) || !aligned(cu_seqlens, 4)) return ATTN_ERR_INVAL;
   if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // dense attn_fwd only
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
@@ -159,7 +175,10 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
     if (nt > max_tiles) max_tiles = nt;
   }
   if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
-  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window);
+  int max_len = 0;
+  for (int s = 0; s < n_seq; ++s) max_len = std::max(max_len, cu_seqlens_host[s + 1] - cu_seqlens_host[s]);
+  if (!window_arith_fits(window, max_len, max_len)) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window, max_len, max_len);
   p.cu_seqlens = cu_seqlens;
   p.n_seq = n_seq;
   p.T = total_tokens;
@@ -212,6 +231,9 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   long long total_tokens = 0;
   for (int b = 0; b < B; ++b) total_tokens += seq_lens_host[b];
   if (total_tokens > 0 && (!k_cache || !v_cache || !block_table || num_pages < 1)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k_cache, v_cache, (const void*)o})
+    if (!aligned(t, 16)) return ATTN_ERR_INVAL;
+  if (!aligned(lse, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
   const size_t need = attn::decode_workspace_bytes(A, d_h, plan);
@@ -263,6 +285,10 @@ ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, c
   }
   if (total_q > 0 && (!q || !o || !lse)) return ATTN_ERR_INVAL;
   if (total_kv > 0 && (!k_cache || !v_cache || !block_table || num_pages < 1)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k_cache, v_cache, (const void*)o})
+    if (!aligned(t, 16)) return ATTN_ERR_INVAL;
+  for (const void* t : {(const void*)lse, (const void*)seq_lens, (const void*)block_table, (const void*)cu_seqlens_q})
+    if (!aligned(t, 4)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
   const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
   if ((page_size & (page_size - 1)) != 0 || page_size % rows_per_part != 0) return ATTN_ERR_UNSUPPORTED;
@@ -279,7 +305,11 @@ ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, c
     if (nt > max_tiles) max_tiles = nt;
   }
   if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
-  attn::FwdParams p = base_params(q, k_cache, v_cache, o, lse, A, A_kv, d_h, scale, causal, nullptr, window);
+  int max_kv = 0;
+  for (int s = 0; s < n_seq; ++s) max_kv = std::max(max_kv, seq_lens_host[s]);
+  if (!window_arith_fits(window, max_kv, max_kv)) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdParams p = base_params(q, k_cache, v_cache, o, lse, A, A_kv, d_h, scale, causal, nullptr, window, max_kv,
+                                  max_kv);
   p.cu_seqlens = cu_seqlens_q;
   p.n_seq = n_seq;
   p.T = total_q;
@@ -328,6 +358,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // forward only
   if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
     return ATTN_ERR_UNSUPPORTED;
+  if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
   const long long n_qt = (S_q + attn::kBwdQRows - 1) / attn::kBwdQRows;
   const long long n_kt = (S_k + attn::kBwdKRows - 1) / attn::kBwdKRows;
   if (n_qt * A * B > INT_MAX || n_kt * A_kv * B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
@@ -357,7 +388,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  window_edges(window, causal, p.win_left, p.win_right);
+  window_edges(window, causal, S_k, S_q, p.win_left, p.win_right);
   return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
 }
 
@@ -376,7 +407,10 @@ ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_ca
   for (int b = 0; b < B; ++b) total_tokens += seq_lens_host[b];
   if (total_tokens > 0 && (!k_cache || !v_cache || !k_scale || !v_scale || !block_table || num_pages < 1))
     return ATTN_ERR_INVAL;
-  if (((uintptr_t)k_cache & 7) != 0 || ((uintptr_t)v_cache & 7) != 0) return ATTN_ERR_INVAL;
+  if (!aligned(k_cache, 8) || !aligned(v_cache, 8) || !aligned(q, 16) || !aligned(o, 16)) return ATTN_ERR_INVAL;
+  for (const void* t : {(const void*)lse, (const void*)seq_lens, (const void*)block_table, (const void*)k_scale,
+                        (const void*)v_scale})
+    if (!aligned(t, 4)) return ATTN_ERR_INVAL;
   const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
   const size_t need = attn::decode_workspace_bytes(A, d_h, plan);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))

@@ -32,10 +32,14 @@
  *     S_k == 0) returns O = 0 and LSE = -inf (page "Attention Kernel",
  *     section "Online softmax", fully-masked-row contract), never NaN.
  *   - scale must be finite and > 0.  Inputs must be finite.
+ *   - Alignment: bf16 q/k/v/o (and the caches) must be 16-byte aligned (the
+ *     kernels copy and store 16-byte groups of a row), fp32 q/k/v/o and
+ *     every lse, int32 table and fp32 scale array 4-byte aligned; uint8 keep
+ *     masks need none.  A misaligned pointer is ATTN_ERR_INVAL.
  *   - Errors are reported before any launch: ATTN_ERR_INVAL for bad
  *     arguments (NULL required pointer, negative size, A % A_kv != 0,
  *     scale not finite and positive, inconsistent lengths, workspace too
- *     small), ATTN_ERR_UNSUPPORTED for a valid request outside the built
+ *     small, misaligned pointer), ATTN_ERR_UNSUPPORTED for a valid request outside the built
  *     kernels (see each entry point), ATTN_ERR_LAUNCH when the runtime
  *     rejects a launch.  Device-side contract violations (a block-table
  *     entry outside [0, num_pages), cu_seqlens that differ from
@@ -84,6 +88,13 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * may be read; their values are ignored.  Each entry j < S_k is finite or
  * -inf (-inf masks the pair; +inf and NaN are contract violations).  The
  * term is added to scale * q_i . k_j, so it is not multiplied by scale.
+ * Range: with c = min(scale, ln 2), finite entries are supported down to
+ * -FLT_MAX * c / 4 and up to +FLT_MAX * c / 4; an entry below -FLT_MAX * c
+ * is a masking fill value and counts as -inf (the float32 minimum, the
+ * usual fill value of additive masks, is always one: a row filled with it
+ * returns O = 0 and LSE = -inf); entries between the two bounds are outside
+ * the contract.  (The kernels scale scores to base 2 in fp32, where a term
+ * below -FLT_MAX * c has no finite representation.)
  * Requires bias_heads in {1, A}, bias_ld >= S_k and a multiple of 4, and
  * bias 16-byte aligned.  It combines with every other mask; key tiles are
  * skipped only through block_keep, which attn_block_keep_from_bias derives
@@ -105,7 +116,9 @@ typedef struct {
  * sequence for varlen); key j is kept when p_i - left <= j <= p_i + right.
  * -1 leaves a side unbounded; other negative values are ATTN_ERR_INVAL.  With
  * causal = 1 the right edge is min(right, 0) (right = -1 gives the causal
- * diagonal).  NULL = no window. */
+ * diagonal).  NULL = no window.  Any edge value is accepted: an edge wider
+ * than the key range is the same as -1.  A call with a window returns
+ * ATTN_ERR_UNSUPPORTED when its row plus key extent exceeds INT_MAX - 1024. */
 typedef struct {
     int left;
     int right;
@@ -181,8 +194,11 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
  *                 attn_decode_paged_workspace_bytes(...) bytes, 256-byte
  *                 aligned; its contents on entry are ignored
  *
- * The split boundaries depend only on seq_lens, so the result does not
- * depend on which physical pages the block table names.
+ * The split boundaries depend on seq_lens and on the device's compute-unit
+ * count (one resident wave of workgroups covers all tokens), never on page
+ * ids: on one device the result does not depend on which physical pages the
+ * block table names (bit for bit), while devices or partition modes with a
+ * different CU count may round differently, within the stated tolerance.
  * Supported: bf16, d_h in {64, 128}, page_size a multiple of 16.
  */
 attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
