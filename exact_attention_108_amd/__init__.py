@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_decode_paged,
     attn_decode_paged_fp8,
+    attn_decode_paged_noalloc,
+    DECODE_NOALLOC_MAX_BYTES,
     attn_decode_paged_workspace_bytes,
     attn_fwd,
     attn_fwd_varlen,

@@ -44,6 +44,9 @@ _lib.attn_fwd_varlen.restype = _i
 _lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                    _vp, _sz, _vp]
 _lib.attn_decode_paged.restype = _i
+_lib.attn_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                           _i, _vp]
+_lib.attn_decode_paged_noalloc.restype = _i
 _lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _vp]
 _lib.attn_decode_paged_workspace_bytes.restype = _sz
 _lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
@@ -81,7 +84,8 @@ def attn_abi_version() -> int:
 
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
-    return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_bytes",
+    return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
+            "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
 
@@ -305,6 +309,43 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host,
                                 block_table.shape[1], num_pages, float(scale), _dtype_code(q),
                                 _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_decode_paged")
+
+
+DECODE_NOALLOC_MAX_BYTES = 48 << 20
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, *, scale: float,
+                              stream=None):
+    """attn_decode_paged with the split partials in the library's static per-device array (no allocation;
+    calls that overlap on one device race).  Raises AttnError (unsupported) when the workspace the call needs,
+    attn_decode_paged_workspace_bytes(...), exceeds DECODE_NOALLOC_MAX_BYTES."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
+    B, A, d = q.shape
+    num_pages, page_size, A_kv, dk = k_cache.shape
+    if dk != d or o.shape != q.shape or lse.shape != (B, A) or lse.dtype != torch.float32:
+        raise ValueError("shape mismatch")
+    if o.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("dtype mismatch")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if sl.shape != (B,):
+        raise ValueError("seq_lens_host must be [B]")
+    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, o, lse)
+    st = _lib.attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                        sl.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), B, A, A_kv, d,
+                                        block_table.shape[1], num_pages, float(scale), _dtype_code(q),
+                                        _stream(stream, dev))
+    if st == ATTN_ERR_UNSUPPORTED:
+        need = attn_decode_paged_workspace_bytes(B, A, A_kv, d, page_size, sl)
+        if need > DECODE_NOALLOC_MAX_BYTES:
+            raise AttnError(st, f"attn_decode_paged_noalloc: needs {need} bytes of split workspace, more than the "
+                                f"static {DECODE_NOALLOC_MAX_BYTES}")
+    _check(st, "attn_decode_paged_noalloc")
 
 
 def attn_bwd_workspace_bytes(B: int, A: int, S_q: int) -> int:

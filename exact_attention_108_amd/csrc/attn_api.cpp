@@ -216,12 +216,14 @@ ATTN_EXPORT size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int
   return attn::decode_workspace_bytes(A, d_h, plan);
 }
 
-ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                                          const int32_t* block_table, const int32_t* seq_lens,
-                                          const int32_t* seq_lens_host, int page_size, void* o, float* lse,
-                                          int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
-                                          float scale, attn_dtype dtype, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
+namespace {
+
+// validation shared by attn_decode_paged and attn_decode_paged_noalloc; on
+// ATTN_OK `need` holds the split workspace's size
+attn_status check_decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* seq_lens_host, int page_size, void* o,
+                              float* lse, int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                              float scale, attn_dtype dtype, size_t& need) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
   if (max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
   attn_status st = check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, max_pages, true);
@@ -235,11 +237,16 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
     if (!aligned(t, 16)) return ATTN_ERR_INVAL;
   if (!aligned(lse, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
-  const size_t need = attn::decode_workspace_bytes(A, d_h, plan);
-  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
-    return ATTN_ERR_INVAL;
   if ((long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  need = attn::decode_workspace_bytes(A, d_h, attn::plan_decode(B, seq_lens_host));
+  return ATTN_OK;
+}
+
+attn_status launch_decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host, int page_size, void* o,
+                               float* lse, int B, int A, int A_kv, int d_h, int max_pages, float scale,
+                               void* workspace, void* stream) {
+  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
   attn::DecodeParams p{};
   p.q = q;
   p.k_cache = k_cache;
@@ -261,6 +268,40 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return launch_status(attn::launch_decode_bf16(p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                          int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                          float scale, attn_dtype dtype, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  attn_status st = check_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse,
+                                     B, A, A_kv, d_h, max_pages, num_pages, scale, dtype, need);
+  if (st != ATTN_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
+                            A_kv, d_h, max_pages, scale, workspace, stream);
+}
+
+ATTN_EXPORT attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                  const int32_t* block_table, const int32_t* seq_lens,
+                                                  const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                                  int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                                  float scale, attn_dtype dtype, void* stream) {
+  size_t need = 0;
+  attn_status st = check_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse,
+                                     B, A, A_kv, d_h, max_pages, num_pages, scale, dtype, need);
+  if (st != ATTN_OK) return st;
+  if (need > attn::kDecodeStaticScratchBytes) return ATTN_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0 && attn::decode_static_scratch(&ws) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
+                            A_kv, d_h, max_pages, scale, ws, stream);
 }
 
 ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,

@@ -20,6 +20,8 @@
 // "Attention Kernel", section "Prefill 与 decode 是两种 kernel").  The design
 // goal is long, contiguous, row-sized reads with many in flight per CU; the
 // matrix cores only keep the arithmetic off the critical path.
+#include <mutex>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -481,7 +483,36 @@ hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Static split workspace for callers that cannot allocate (attn_decode_paged_noalloc).
+// Each device the library runs on holds its own copy of this array from the
+// first call on that device until the process ends.  In host code the name
+// `scratch` is only a stand-in for the symbol: the device address of each
+// device's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is handed to kernels.
+__device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t decode_static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 DecodePlan plan_decode(int B, const int32_t* seq_lens_host) {
   DecodePlan plan;

@@ -132,6 +132,11 @@ size_t decode_workspace_bytes(int A, int d, const DecodePlan& plan);
 size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan);
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+// Size of the static split workspace of attn_decode_paged_noalloc (one copy per
+// device), and its device address on the current device (looked up once per
+// device; no allocation).
+constexpr size_t kDecodeStaticScratchBytes = size_t(48) << 20;
+hipError_t decode_static_scratch(void** ptr);
 // Same, over FP8 (OCP E4M3) caches with per-(page, KV head) scales.
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream);
 

@@ -14,7 +14,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library neither allocates nor frees memory and keeps no global state.
+ *     library neither allocates nor frees memory and keeps no global state
+ *     (the one exception: the static workspace of attn_decode_paged_noalloc).
  *     Pointers named *_host are HOST pointers read synchronously during the
  *     call.  Everything is contiguous row-major.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
@@ -230,6 +231,30 @@ attn_status attn_decode_paged_fp8(const void *q, const uint8_t *k_cache, const u
                                   const int32_t *seq_lens_host, int page_size, void *o, float *lse,
                                   int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
                                   float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_paged without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses without an allocator).  Same arguments,
+ * semantics, kernels and result as attn_decode_paged (bit for bit), but the
+ * split partials live in a static device array of the library, one copy per
+ * device, 48 MiB (ATTN_DECODE_NOALLOC_MAX_BYTES), held from the first call on a
+ * device until the process ends.  The call allocates nothing.
+ *   - Returns ATTN_ERR_UNSUPPORTED when the workspace the call would need
+ *     (attn_decode_paged_workspace_bytes of the same arguments) exceeds that
+ *     size: e.g. A = 32, d_h = 128 allows up to B = 1000 sequences.
+ *   - Every call on one device shares that device's array: calls that overlap
+ *     in time on one device (several streams or host threads) race and must
+ *     be serialised by the caller.  Calls on different devices do not share.
+ *   - The array keeps the last call's partials; nothing in it needs to start
+ *     at zero (every partial a call reads, that call wrote first).
+ */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)48 << 20)
+attn_status attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_table, const int32_t *seq_lens,
+                                      const int32_t *seq_lens_host, int page_size, void *o, float *lse,
+                                      int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                      float scale, attn_dtype dtype, void *stream);
 
 /* Workspace bytes attn_decode_paged needs for these lengths (0 on bad input). */
 size_t attn_decode_paged_workspace_bytes(int B, int A, int A_kv, int d_h, int page_size,

@@ -19,6 +19,7 @@ def header_functions():
 
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_varlen", "attn_decode_paged",
+                                         "attn_decode_paged_noalloc",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
                                          "attn_block_keep_from_bias", "attn_status_string",
@@ -258,6 +259,26 @@ def test_attn_decode_paged_rejects_bad_arguments():
     assert dec(A=34, A_kv=2) == 2                  # more than 16 query heads per KV head
     neg = np.array([-1, 4], np.int32)
     assert dec(lens=neg.ctypes.data_as(ctypes.c_void_p)) == 1
+
+
+def test_attn_decode_paged_noalloc_rejects_bad_arguments():
+    """Same validation as attn_decode_paged, and a call whose split workspace
+    would exceed the static array is refused before any launch."""
+    lib = _lib()
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_decode_paged_noalloc.argtypes = [vp] * 6 + [i, vp, vp] + [i] * 6 + [f, i, vp]
+    lib.attn_decode_paged_noalloc.restype = i
+    lens = np.array([10, 40], np.int32)
+
+    def dec(lens=lens, B=2, A=8, A_kv=2, d=128, mp=3, scale=0.1, dt=1, q=P):
+        return lib.attn_decode_paged_noalloc(q, P, P, P, P, lens.ctypes.data_as(vp), 16, P, P, B, A, A_kv, d, mp, 6,
+                                             scale, dt, None)
+    assert dec(mp=2) == 1 and dec(A=5) == 1 and dec(scale=0.0) == 1 and dec(q=ctypes.c_void_p(4096 + 8)) == 1
+    assert dec(d=96) == 2 and dec(dt=0) == 2
+    # 1100 sequences of 32 heads at d = 128: (2048 + 1100) slots x 32 x 129 fp32 > 48 MiB
+    many = np.ones(1100, np.int32)
+    assert lib.attn_decode_paged_workspace_bytes(1100, 32, 8, 128, 16, many.ctypes.data_as(vp)) > 48 << 20
+    assert dec(lens=many, B=1100, A=32, A_kv=8, mp=1) == 2
 
 
 def test_workspace_bytes():
