@@ -126,10 +126,11 @@ def source_hash(part: str) -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(part: str):
+def committed_traffic(part: str, sources: str = None):
     """HBM bytes per launch of `part`'s kernel from the newest traffic summary
-    under profiles/ whose recorded source hash matches the current sources."""
-    want = source_hash(part)
+    under profiles/ whose recorded source hash matches the current sources
+    (those of `sources`, by default of `part`)."""
+    want = source_hash(sources or part)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")), reverse=True):
         with open(path) as fh:
             for line in fh:
@@ -515,7 +516,7 @@ def main():
     tf5 = f5 / (avg["varlen"] * 1e-3) / 1e12
     gbs4 = kv_bytes / (avg["decode"] * 1e-3) / 1e9
     traffic_prefill, traffic_src = committed_traffic("prefill")
-    traffic_gqa, traffic_gqa_src = committed_traffic("gqa_long")
+    traffic_gqa, traffic_gqa_src = committed_traffic("gqa_long", "prefill")
     traffic_decode, _ = committed_traffic("decode")
     p3 = w["p3"]
 
