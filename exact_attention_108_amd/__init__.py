@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     attn_abi_version,
     attn_block_keep_from_bias,
     attn_bwd,
+    attn_bwd_varlen,
     attn_bwd_workspace_bytes,
     attn_decode_paged,
     attn_decode_paged_fp8,

@@ -52,6 +52,8 @@ _lib.attn_decode_paged_workspace_bytes.restype = _sz
 _lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                           ctypes.POINTER(_Mask), _WP, _i, _vp, _sz, _vp]
 _lib.attn_bwd.restype = _i
+_lib.attn_bwd_varlen.argtypes = [_vp] * 11 + [_i] * 5 + [_f, _i, ctypes.POINTER(_Mask), _WP, _i, _vp, _sz, _vp]
+_lib.attn_bwd_varlen.restype = _i
 _lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.attn_prefill_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                     _f, _i, _WP, _i, _vp]
@@ -86,7 +88,7 @@ def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
             "attn_decode_paged_workspace_bytes",
-            "attn_bwd", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
+            "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
 
 
@@ -353,9 +355,10 @@ def attn_bwd_workspace_bytes(B: int, A: int, S_q: int) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, causal: bool = False, q_keep=None,
-             k_keep=None, window=None, stream=None):
+             k_keep=None, window=None, block_keep=None, bias=None, stream=None):
     """dQ, dK, dV of attn_fwd.  q/o/dout/dq [B,A,S_q,d], k/v/dk/dv [B,A_kv,S_k,d], lse [B,A,S_q] fp32 (the
-    forward's); workspace a uint8 device tensor of at least attn_bwd_workspace_bytes(B, A, S_q) bytes."""
+    forward's); workspace a uint8 device tensor of at least attn_bwd_workspace_bytes(B, A, S_q) bytes; masks as
+    given to attn_fwd."""
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, heads, S, d]")
@@ -377,12 +380,54 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, caus
         raise ValueError("q_keep must be [B, S_q]")
     if k_keep is not None and k_keep.shape != (B, S_k):
         raise ValueError("k_keep must be [B, S_k]")
+    if block_keep is not None and (block_keep.dim() != 4 or block_keep.shape[0] != B or
+                                   block_keep.shape[1] not in (1, A) or
+                                   tuple(block_keep.shape[2:]) != ((S_q + 127) // 128, (S_k + 127) // 128)):
+        raise ValueError("block_keep must be [B, 1 or A, ceil(S_q/128), ceil(S_k/128)]")
+    bh, ld = _bias_view(bias, B, A, S_q, S_k) if bias is not None else (0, 0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, workspace, q_keep, k_keep)
+    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, workspace, q_keep, k_keep, block_keep, bias)
     st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                       B, A, A_kv, S_q, S_k, d, float(scale), int(bool(causal)), _mask(q_keep, k_keep),
-                       _window(window), _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
+                       B, A, A_kv, S_q, S_k, d, float(scale), int(bool(causal)),
+                       _mask(q_keep, k_keep, block_keep, bias, bh, ld), _window(window), _dtype_code(q),
+                       _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_bwd")
+
+
+def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, cu_seqlens_host, workspace, *, scale: float,
+                    causal: bool = True, q_keep=None, k_keep=None, window=None, stream=None):
+    """dQ, dK, dV of attn_fwd_varlen.  q/o/dout/dq [A,T,d], k/v/dk/dv [A_kv,T,d], lse [A,T] fp32 (the
+    forward's); cu_seqlens int32 device with cu_seqlens_host (numpy); workspace a uint8 device tensor of at
+    least attn_bwd_workspace_bytes(1, A, T) bytes."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
+    A, T, d = q.shape
+    A_kv = k.shape[0]
+    if k.shape[1] != T or k.shape[2] != d:
+        raise ValueError("k/v must be [A_kv, T, d]")
+    for t in (o, dout, dq):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("o, dout, dq must match q")
+    for t in (dk, dv):
+        if t.shape != k.shape or t.dtype != q.dtype:
+            raise ValueError("dk, dv must match k")
+    if k.dtype != q.dtype or v.dtype != q.dtype or lse.shape != (A, T) or lse.dtype != torch.float32:
+        raise ValueError("dtype / lse mismatch")
+    cu_host = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    n_seq = cu_host.size - 1
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.numel() != cu_host.size:
+        raise ValueError("cu_seqlens must be int32 [n_seq + 1] matching cu_seqlens_host")
+    for t in (q_keep, k_keep):
+        if t is not None and t.shape != (T,):
+            raise ValueError("keep-masks must be [T]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace, q_keep, k_keep)
+    st = _lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(cu_seqlens), cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d,
+                              float(scale), int(bool(causal)), _mask(q_keep, k_keep), _window(window),
+                              _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    _check(st, "attn_bwd_varlen")
 
 
 def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host,

@@ -383,29 +383,12 @@ ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int A, int S_q) {
   return bwd_workspace_bytes(B, A, S_q);
 }
 
-ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                                 const float* lse, void* dq, void* dk, void* dv, int B, int A, int A_kv, int S_q,
-                                 int S_k, int d_h, float scale, int causal, const attn_mask* mask,
-                                 const attn_window* window, attn_dtype dtype, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
-  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
-  if (S_q > 0 && (!q || !o || !dout || !lse || !dq)) return ATTN_ERR_INVAL;
-  if (S_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVAL;
-  for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
-    if (!aligned16(t)) return ATTN_ERR_INVAL;
-  if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
-  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // forward only
-  if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
-    return ATTN_ERR_UNSUPPORTED;
-  if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
-  const long long n_qt = (S_q + attn::kBwdQRows - 1) / attn::kBwdQRows;
-  const long long n_kt = (S_k + attn::kBwdKRows - 1) / attn::kBwdKRows;
-  if (n_qt * A * B > INT_MAX || n_kt * A_kv * B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = S_q > 0 ? bwd_workspace_bytes(B, A, S_q) : 0;
-  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
-    return ATTN_ERR_INVAL;
+namespace {
+
+// fields of a backward launch shared by the dense and packed entry points
+attn::BwdParams bwd_params(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int A, int A_kv, int d_h, float scale,
+                           int causal, const attn_mask* mask, void* workspace) {
   attn::BwdParams p{};
   p.q = q;
   p.k = k;
@@ -419,17 +402,109 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   p.dv = dv;
   p.q_keep = mask ? mask->q_keep : nullptr;
   p.k_keep = mask ? mask->k_keep : nullptr;
-  p.B = B;
   p.A = A;
   p.A_kv = A_kv;
   p.G = A / A_kv;
-  p.S_q = S_q;
-  p.S_k = S_k;
   p.d = d_h;
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return p;
+}
+
+}  // namespace
+
+ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, int B, int A, int A_kv, int S_q,
+                                 int S_k, int d_h, float scale, int causal, const attn_mask* mask,
+                                 const attn_window* window, attn_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (S_q > 0 && (!q || !o || !dout || !lse || !dq)) return ATTN_ERR_INVAL;
+  if (S_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(t)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
+  const bool blocks = mask && mask->block_keep;
+  const bool bias = mask && mask->bias;
+  if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
+  if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
+  const long long n_qb = (S_q + 127) / 128, n_kb = (S_k + 127) / 128;
+  if (blocks && (n_kb > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * n_qb > attn::kBwdMaxRowBlocks))
+    return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
+  const long long n_qt = (S_q + attn::kBwdQRows - 1) / attn::kBwdQRows;
+  const long long n_kt = (S_k + attn::kBwdKRows - 1) / attn::kBwdKRows;
+  if (n_qt * A * B > INT_MAX || n_kt * A_kv * B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = S_q > 0 ? bwd_workspace_bytes(B, A, S_q) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  attn::BwdParams p = bwd_params(q, k, v, o, dout, lse, dq, dk, dv, A, A_kv, d_h, scale, causal, mask, workspace);
+  p.B = B;
+  p.S_q = S_q;
+  p.S_k = S_k;
+  if (blocks) {
+    p.block_keep = mask->block_keep;
+    p.block_heads = mask->block_heads;
+    p.n_qb = (int)n_qb;
+    p.n_kb = (int)n_kb;
+  }
+  if (bias) {
+    p.bias = mask->bias;
+    p.bias_heads = mask->bias_heads;
+    p.bias_ld = mask->bias_ld;
+    p.inv_scale = (float)(1.0 / (double)scale);
+  }
   window_edges(window, causal, S_k, S_q, p.win_left, p.win_right);
+  return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
+}
+
+ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int n_seq,
+                                        int total_tokens, int A, int A_kv, int d_h, float scale, int causal,
+                                        const attn_mask* mask, const attn_window* window, attn_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_seq < 0 || total_tokens < 0 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVAL;
+  if (!cu_seqlens || !cu_seqlens_host) return ATTN_ERR_INVAL;
+  if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seq] != total_tokens) return ATTN_ERR_INVAL;
+  for (int s = 0; s < n_seq; ++s)
+    if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return ATTN_ERR_INVAL;
+  if (total_tokens > 0 && (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(t)) return ATTN_ERR_INVAL;
+  if (!aligned(cu_seqlens, 4)) return ATTN_ERR_INVAL;
+  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // dense attn_bwd only
+  if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return ATTN_OK;
+  if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  long long total_tiles = 0;
+  int max_tiles = 0, max_len = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int len = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+    const int nt = (len + attn::kBwdQRows - 1) / attn::kBwdQRows;
+    total_tiles += nt;
+    max_tiles = std::max(max_tiles, nt);
+    max_len = std::max(max_len, len);
+  }
+  if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  if (!window_arith_fits(window, max_len, max_len)) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = bwd_workspace_bytes(1, A, total_tokens);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0) return ATTN_ERR_INVAL;
+  attn::BwdParams p = bwd_params(q, k, v, o, dout, lse, dq, dk, dv, A, A_kv, d_h, scale, causal, mask, workspace);
+  p.B = 1;
+  p.cu_seqlens = cu_seqlens;
+  p.n_seq = n_seq;
+  p.T = total_tokens;
+  p.max_tiles = max_tiles;
+  p.total_tiles = (int)total_tiles;
+  window_edges(window, causal, max_len, max_len, p.win_left, p.win_right);
   return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
 }
 

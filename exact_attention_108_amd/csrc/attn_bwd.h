@@ -30,7 +30,29 @@ struct BwdParams {
   // XCD-blocked grid orders (0 = plain order), set by launch_bwd_bf16
   int dq_units_per_xcd, dq_group;  // units: (batch, query head)
   int kv_units_per_xcd, kv_group;  // units: (batch, KV head)
+  // packed sequences (cu_seqlens != null): q, o, dout, dq are [A, T, d], k, v,
+  // dk, dv [A_kv, T, d], lse [A, T], row_stats [A, T, 2]; sequence s holds
+  // tokens [cu_seqlens[s], cu_seqlens[s+1]) and is its own problem (S_q = S_k
+  // = its length); keep masks are [T].  B = 1.
+  const int32_t* cu_seqlens;
+  int n_seq, T;
+  int max_tiles;    // most 128-row tiles of any sequence
+  int total_tiles;  // 128-row tiles summed over the sequences
+  // block mask (dense only): block_keep[b][hm][qb][kb] for 128 x 128 blocks,
+  // hm = 0 when block_heads == 1, else the query head; n_qb, n_kb blocks
+  const uint8_t* block_keep;
+  int block_heads, n_qb, n_kb;
+  // dense additive term (dense only): bias[((b * bias_heads + hm) * S_q + i) *
+  // bias_ld + j] added to scale * q_i . k_j (as M / scale to the raw product)
+  const float* bias;
+  int bias_heads, bias_ld;
+  float inv_scale;
 };
+// Block-mask limits of the backward: the dQ pass keeps one flag per 128-key
+// block of its row block in LDS, the dK/dV pass one per (query head of the
+// group, 128-row block).
+constexpr int kBwdMaxKeyBlocks = 2048;
+constexpr int kBwdMaxRowBlocks = 4096;
 constexpr int kBwdQRows = 128;   // query rows per dQ workgroup
 constexpr int kBwdKRows = 128;   // keys per dK/dV workgroup
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);

@@ -90,30 +90,97 @@ __device__ __forceinline__ void grid_order(int lin, int n_tiles, int n_units, in
   }
 }
 
+// Packed sequences: the rank-th workgroup of one head when the sequences'
+// 128-row tiles are ordered by tile index t descending, then by sequence.
+// count(t) = sum_s max(0, n_s - t) workgroups have an index >= t; a binary
+// search finds t, a ballot the sequence.  Returns false past the last tile.
+__device__ __forceinline__ bool varlen_tile(const int32_t* cu, int n_seq, int max_tiles, int rank, int& t_out,
+                                            int& seq_out) {
+  const int lane = threadIdx.x & 63;
+  auto ntiles = [&](int s) -> int { return (cu[s + 1] - cu[s] + kBwdQRows - 1) / kBwdQRows; };
+  auto count_ge = [&](int t) -> int {
+    int c = 0;
+    for (int s = lane; s < n_seq; s += 64) c += max(0, ntiles(s) - t);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+    return c;
+  };
+  int lo = 0, hi = max_tiles;  // count_ge(lo) > rank >= count_ge(hi) (= 0)
+  if (count_ge(0) <= rank) return false;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count_ge(mid) > rank) lo = mid; else hi = mid;
+  }
+  int k = rank - count_ge(lo + 1);  // the k-th sequence (in order) with more than lo tiles
+  int seq = -1;
+  for (int base = 0; base < n_seq && seq < 0; base += 64) {
+    const int s = base + lane;
+    const bool has = s < n_seq && ntiles(s) > lo;
+    const uint64_t m = __ballot(has);
+    const int c = __popcll(m);
+    if (k < c) {
+      const uint64_t below = m & (lane == 0 ? 0ull : (~0ull >> (64 - lane)));
+      const uint64_t w = __ballot(has && __popcll(below) == k);
+      seq = base + __ffsll((long long)w) - 1;
+    } else {
+      k -= c;
+    }
+  }
+  if (seq < 0) return false;
+  t_out = __builtin_amdgcn_readfirstlane(lo);
+  seq_out = __builtin_amdgcn_readfirstlane(seq);
+  return true;
+}
+
 template <int N>
 using Slot = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------- dQ
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p,
+// kVarlen: packed sequences (see BwdParams); kMasks: the block mask and the
+// dense additive term (runtime-optional, dense batches only).  Two waves per
+// SIMD, one for the masked form at d = 128 (at two its term loads spill).
+template <int D, bool kMasks>
+constexpr int kDqWavesPerSimd = (D == 128 && kMasks) ? 1 : 2;
+
+template <int D, bool kVarlen, bool kMasks>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D, kMasks>, kDqWavesPerSimd<D, kMasks>))) void bwd_dq_kernel(BwdParams p,
                                                                                                     int n_qt) {
+  static_assert(!(kVarlen && kMasks), "block masks and additive terms are dense-batch only");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int TILE_BYTES = kKeyTile * D * 2;
   constexpr int SLOT_BYTES = 2 * TILE_BYTES;  // [K tile | V tile]
   constexpr int NSLOT = 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * SLOT_BYTES / 2];
+  // block mask: flag of each 128-key block of this row block's key range
+  __shared__ uint8_t sBlk[kMasks ? kBwdMaxKeyBlocks : 1];
 
   // heaviest query tiles first (most causal key tiles)
-  int rank, bh;
-  grid_order(blockIdx.x, n_qt, p.A * p.B, p.dq_units_per_xcd, p.dq_group, rank, bh);
-  const int qt = n_qt - 1 - rank;
-  const int h = bh % p.A, b = bh / p.A, hk = h / p.G;
+  int qt, h, b = 0, S_q, S_k;
+  size_t q_row0, k_row0, tok0 = 0;
+  if constexpr (kVarlen) {
+    h = blockIdx.x % p.A;
+    int seq;
+    if (!varlen_tile(p.cu_seqlens, p.n_seq, p.max_tiles, blockIdx.x / p.A, qt, seq)) return;
+    tok0 = p.cu_seqlens[seq];
+    S_q = S_k = p.cu_seqlens[seq + 1] - (int)tok0;
+    q_row0 = (size_t)h * p.T + tok0;
+    k_row0 = (size_t)(h / p.G) * p.T + tok0;
+  } else {
+    int rank, bh;
+    grid_order(blockIdx.x, n_qt, p.A * p.B, p.dq_units_per_xcd, p.dq_group, rank, bh);
+    qt = n_qt - 1 - rank;
+    h = bh % p.A;
+    b = bh / p.A;
+    S_q = p.S_q;
+    S_k = p.S_k;
+    q_row0 = (size_t)(b * p.A + h) * S_q;
+    k_row0 = (size_t)(b * p.A_kv + h / p.G) * S_k;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int S_q = p.S_q, S_k = p.S_k, off = S_k - S_q;
+  const int off = S_k - S_q;
   const int wl = p.win_left, wr = p.win_right;
-  const size_t q_row0 = (size_t)(b * p.A + h) * S_q;
-  const size_t k_row0 = (size_t)(b * p.A_kv + hk) * S_k;
+  const uint8_t* qkeep = p.q_keep ? p.q_keep + (kVarlen ? tok0 : (size_t)b * S_q) : nullptr;
   const int q0 = qt * kBwdQRows;
   const int qrow = q0 + wave * 32 + l32;
   const bool row_in = qrow < S_q;
@@ -136,7 +203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   float lrow = INFINITY;
   if (row_in) {
     const float lse = p.lse[q_row0 + qrow];
-    const bool keep = p.q_keep == nullptr || p.q_keep[(size_t)b * S_q + qrow] != 0;
+    const bool keep = qkeep == nullptr || qkeep[qrow] != 0;
     if (keep && lse != -INFINITY) lrow = lse * kLog2e;
     if (g == 0) *(float2*)(p.row_stats + 2 * (q_row0 + qrow)) = make_float2(lrow, drow);
   }
@@ -167,7 +234,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float cs = p.scale_log2;
   const uint16_t* kbase = (const uint16_t*)p.k + k_row0 * D;
   const uint16_t* vbase = (const uint16_t*)p.v + k_row0 * D;
-  const uint8_t* kkeep = p.k_keep ? p.k_keep + (size_t)b * S_k : nullptr;
+  const uint8_t* kkeep = p.k_keep ? p.k_keep + (kVarlen ? tok0 : (size_t)b * S_k) : nullptr;
+
+  // Block mask: this row block's flags for the 128-key blocks of its range,
+  // staged in LDS (the loop's first barrier orders them); a tile of a masked
+  // block is skipped whole (its copy still runs: the pipeline stays fixed).
+  // Additive term: this lane's row of M.
+  [[maybe_unused]] const int kb0 = j_lo >> 1;
+  [[maybe_unused]] const float* brow = nullptr;
+  if constexpr (kMasks) {
+    if (p.block_keep) {
+      const int hm = p.block_heads == 1 ? 0 : h;
+      const uint8_t* bk = p.block_keep + ((size_t)(b * p.block_heads + hm) * p.n_qb + qt) * p.n_kb;
+      const int nkb = n_tiles > 0 ? ((j_lo + n_tiles - 1) >> 1) - kb0 + 1 : 0;
+      for (int i = tid; i < nkb; i += kThreads) sBlk[i] = bk[kb0 + i];
+    }
+    if (p.bias) {
+      const int hm = p.bias_heads == 1 ? 0 : h;
+      brow = p.bias + ((size_t)(b * p.bias_heads + hm) * S_q + min(qrow, S_q - 1)) * p.bias_ld;
+    }
+  }
+  auto tile_kept = [&](int j) -> bool {
+    if constexpr (kMasks) {
+      if (p.block_keep) return __builtin_amdgcn_readfirstlane((int)sBlk[((j_lo + j) >> 1) - kb0]) != 0;
+    }
+    return true;
+  };
 
   f32x16 acc[MB];
 #pragma unroll
@@ -188,6 +280,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // 32-key half kb of tile j in `lds`: S^T, dP^T, then P, dS and dQ^T += K^T . dS^T
   const int wave_row0 = q0 + wave * 32;
   auto tile_masked = [&](int j, bool ok) -> bool {
+    if constexpr (kMasks) {
+      if (p.bias) return true;
+    }
     const int k0 = (j_lo + j) * kKeyTile;
     bool full = k0 + kKeyTile <= S_k && __ballot(ok) == ~0ull;
     if (wr >= 0) full = full && k0 + kKeyTile - 1 <= wave_row0 + off + wr;
@@ -196,6 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   auto half = [&](const char* lds, int j, bool ok, int kb, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = (j_lo + j) * kKeyTile;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
@@ -204,7 +300,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       s = mfma32(ka, qf[t], s);
       dp = mfma32(va, dof[t], dp);
     }
-    const int k0 = (j_lo + j) * kKeyTile;
+    // additive term of the 16 keys of this lane in the half: element r is key
+    // k0 + 32 kb + 8 (r / 4) + 4 g + r % 4, four runs of 4 keys (keys at or
+    // past S_k are not read; the predicate masks them)
+    if constexpr (kMasks) {
+      if (brow) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kk = k0 + 32 * kb + 8 * q4 + 4 * g;
+          const f32x4 mt = kk < S_k ? *(const f32x4*)(brow + kk) : f32x4{};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[4 * q4 + i] = fmaf(mt[i], p.inv_scale, s[4 * q4 + i]);
+        }
+      }
+    }
     const uint64_t kvalid = __ballot(ok) >> (4 * g);
     const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
     const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
@@ -235,6 +344,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();  // tile j has landed; every wave is done with tile j - 1
     if (j + 1 < n_tiles) issue(j + 1, SC ^ 1);
     const char* lc = (const char*)smem + SC * SLOT_BYTES;
+    if (!tile_kept(j)) return;
     const bool ok = key_ok(j);
     if (tile_masked(j, ok)) {
       half(lc, j, ok, 0, std::true_type{});
@@ -280,9 +390,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 template <int D, bool KLDS>
 constexpr int kDkdvWavesPerSimd = (D == 64 || KLDS) ? 2 : 1;
 
-template <int D, bool KLDS>
+template <int D, bool KLDS, bool kVarlen, bool kMasks>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS>, kDkdvWavesPerSimd<D, KLDS>))) void bwd_dkdv_kernel(BwdParams p,
                                                                                                       int n_kt) {
+  static_assert(!(kVarlen && kMasks), "block masks and additive terms are dense-batch only");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
@@ -292,18 +403,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   constexpr int KTILE_BYTES = KLDS ? kBwdKRows * D * 2 : 0;  // [slots | K tile]
   constexpr int COPIES = 2 * (kQBlock * D / 8 / kThreads) + 1;  // copy instructions per wave per block
   __shared__ __attribute__((aligned(16))) uint16_t smem[(NSLOT * SLOT_BYTES + KTILE_BYTES) / 2];
+  // block mask: flag of each (query head of the group, 128-row block) for this key block
+  __shared__ uint8_t sBlk[kMasks ? kBwdMaxRowBlocks : 1];
 
   // key tiles in order (the first ones see the most query rows when causal)
-  int kt, bk;
-  grid_order(blockIdx.x, n_kt, p.A_kv * p.B, p.kv_units_per_xcd, p.kv_group, kt, bk);
-  const int hk = bk % p.A_kv, b = bk / p.A_kv;
+  int kt, hk, b = 0, S_q, S_k;
+  size_t k_row0, tok0 = 0;
+  if constexpr (kVarlen) {
+    // packed: the sequences' key tiles counted from each sequence's end, so
+    // that the tiles seeing the most query rows (the first) come first
+    hk = blockIdx.x % p.A_kv;
+    int from_end, seq;
+    if (!varlen_tile(p.cu_seqlens, p.n_seq, p.max_tiles, blockIdx.x / p.A_kv, from_end, seq)) return;
+    tok0 = p.cu_seqlens[seq];
+    S_q = S_k = p.cu_seqlens[seq + 1] - (int)tok0;
+    kt = (S_k + kBwdKRows - 1) / kBwdKRows - 1 - from_end;
+    k_row0 = (size_t)hk * p.T + tok0;
+  } else {
+    int bk;
+    grid_order(blockIdx.x, n_kt, p.A_kv * p.B, p.kv_units_per_xcd, p.kv_group, kt, bk);
+    hk = bk % p.A_kv;
+    b = bk / p.A_kv;
+    S_q = p.S_q;
+    S_k = p.S_k;
+    k_row0 = (size_t)(b * p.A_kv + hk) * S_k;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int S_q = p.S_q, S_k = p.S_k, off = S_k - S_q;
+  const int off = S_k - S_q;
   const int wl = p.win_left, wr = p.win_right;
-  const size_t k_row0 = (size_t)(b * p.A_kv + hk) * S_k;
   const int key = kt * kBwdKRows + wave * 32 + l32;  // this lane's key
   bool key_live = key < S_k;
-  if (key_live && p.k_keep) key_live = p.k_keep[(size_t)b * S_k + key] != 0;
+  if (key_live && p.k_keep) key_live = p.k_keep[(kVarlen ? tok0 : (size_t)b * S_k) + key] != 0;
+  // first row of query head gh of the group (dense: of batch row b)
+  auto q_head_row0 = [&](int gh) -> size_t {
+    const int h = hk * p.G + gh;
+    return kVarlen ? (size_t)h * p.T + tok0 : (size_t)(b * p.A + h) * S_q;
+  };
 
   bf16x8 kres[KLDS ? 1 : KSTEPS], vres[KSTEPS];
 #pragma unroll
@@ -346,9 +481,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   const int nq = qb_end - qb_first;
   const int n_blocks = p.G * nq;
 
+  // Block mask: the flags of this key block for every (query head of the
+  // group, 128-row block) of the row range, staged in LDS (ordered by the
+  // loop's first barrier); a 32-row block of a masked block is skipped whole
+  // (its copy still runs).  Additive term: M[row][this lane's key].
+  [[maybe_unused]] const int rb0 = qb_first / 4;
+  [[maybe_unused]] const int nrb = nq > 0 ? (qb_end - 1) / 4 - rb0 + 1 : 0;
+  if constexpr (kMasks) {
+    if (p.block_keep) {
+      for (int i = tid; i < p.G * nrb; i += kThreads) {
+        const int gh = i / nrb, r = rb0 + i % nrb;
+        const int hm = p.block_heads == 1 ? 0 : hk * p.G + gh;
+        sBlk[i] = p.block_keep[((size_t)(b * p.block_heads + hm) * p.n_qb + r) * p.n_kb + kt];
+      }
+    }
+  }
+  auto block_kept = [&](int idx) -> bool {
+    if constexpr (kMasks) {
+      if (p.block_keep) {
+        const int gh = idx / nq, qb = qb_first + idx % nq;
+        return __builtin_amdgcn_readfirstlane((int)sBlk[gh * nrb + qb / 4 - rb0]) != 0;
+      }
+    }
+    return true;
+  };
+
   auto issue = [&](int idx, int slot) {
     const int gh = idx / nq, qb = qb_first + idx % nq;
-    const size_t q_row0 = (size_t)(b * p.A + hk * p.G + gh) * S_q;
+    const size_t q_row0 = q_head_row0(gh);
     const int r0 = qb * kQBlock;
     const uint32_t dst = lds_base + slot * SLOT_BYTES;
     copy_rows<D, kQBlock>((const uint16_t*)p.q + q_row0 * D, S_q, r0, dst);
@@ -382,10 +542,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   // dead row has L2 = +inf, so its p is 0 without a mask; MASKED adds the
   // per-element predicate (rows past S_q, which arrive zero-filled with L2 =
   // 0, dropped or absent keys, the window's edges).
-  auto grad = [&](const char* lds, int idx, const f32x16& s, const f32x16& dp, auto masked_tag) {
+  auto grad = [&](const char* lds, int idx, const f32x16& s_in, const f32x16& dp, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const float* st = (const float*)(lds + 2 * BLOCK_BYTES);
     const int r0 = (qb_first + idx % nq) * kQBlock;
+    f32x16 s = s_in;
+    if constexpr (kMasks) {
+      if (p.bias) {
+        // M[r0 + m][key], m = 8(r/4) + 4g + r%4: for a fixed m the 32 lanes of a
+        // half-wave read 32 consecutive keys; rows past S_q and keys past S_k
+        // are not read (the predicate masks them)
+        const int gh = idx / nq, hm = p.bias_heads == 1 ? 0 : hk * p.G + gh;
+        const float* bcol = p.bias + (size_t)(b * p.bias_heads + hm) * S_q * p.bias_ld + min(key, S_k - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float m = row < S_q ? bcol[(size_t)row * p.bias_ld] : 0.f;
+          s[r] = fmaf(m, p.inv_scale, s[r]);
+        }
+      }
+    }
     // element r holds query row r0 + m, m = 8(r/4) + 4g + r%4, of this lane's key
     const int m_lo = wr >= 0 ? key - off - wr - r0 - 4 * g : -(1 << 30);
     int m_hi = key_live ? S_q - r0 - 4 * g : -(1 << 30);
@@ -426,6 +602,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   const bool wave_keys_live = __ballot(key_live) == ~0ull;
   const int wave_key_first = kt * kBwdKRows + wave * 32, wave_key_last = wave_key_first + 31;
   auto block_masked = [&](int idx) -> bool {
+    if constexpr (kMasks) {
+      if (p.bias) return true;
+    }
     const int r0 = (qb_first + idx % nq) * kQBlock;
     bool full = wave_keys_live && r0 + kQBlock <= S_q;
     if (wr >= 0) full = full && wave_key_last <= r0 + off + wr;
@@ -454,6 +633,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     const char* lc = (const char*)smem + SC * SLOT_BYTES;
     // at the last block this reads a stale (in-bounds) slot; the result is unused
     const char* ln = (const char*)smem + SN * SLOT_BYTES;
+    if constexpr (kMasks) {
+      // a block the block mask drops contributes nothing: its scores are not
+      // needed and its gradient is not formed
+      const bool keep_cur = block_kept(idx), keep_nxt = idx + 1 < n_blocks && block_kept(idx + 1);
+      if (keep_nxt) scores(ln, nxt.s, nxt.dp);
+      if (keep_cur) grad(lc, idx, cur.s, cur.dp, std::true_type{});
+      return;
+    }
     if (block_masked(idx)) {
       interleave_hint();
       scores(ln, nxt.s, nxt.dp);
@@ -475,6 +662,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
       __syncthreads();  // block idx has landed for every wave; all are done with block idx - 1
       if (idx + 1 < n_blocks) issue(idx + 1, SC ^ 1);
       const char* lc = (const char*)smem + SC * SLOT_BYTES;
+      if (!block_kept(idx)) return;
       SD cur;
       if (block_masked(idx)) {
         interleave_hint();
@@ -508,7 +696,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
       else
         lds_copy_wait_all();
       __syncthreads();
-      scores((const char*)smem, ra.s, ra.dp);
+      if (block_kept(0)) scores((const char*)smem, ra.s, ra.dp);
     }
     int idx = 0;
     for (; idx + 4 <= n_blocks; idx += 4) {
@@ -562,35 +750,59 @@ void plan_order(int units, int group_max, int& per, int& group) {
   group = g;
 }
 
-template <int D>
-hipError_t launch_bwd_d(const BwdParams& p_in, hipStream_t stream) {
+template <int D, bool kVarlen, bool kMasks>
+hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
   BwdParams p = p_in;
-  plan_order(p.A * p.B, kDqGroupMax, p.dq_units_per_xcd, p.dq_group);
-  plan_order(p.A_kv * p.B, kKvGroupMax, p.kv_units_per_xcd, p.kv_group);
-  // the dQ pass writes the row statistics the dK/dV pass reads: same stream, in order
-  if (p.S_q > 0) {
-    const int n_qt = (p.S_q + kBwdQRows - 1) / kBwdQRows;
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_qt * p.A * p.B), dim3(kThreads), 0, stream, p, n_qt);
+  int n_qt, n_units_q, n_units_kv;
+  if constexpr (kVarlen) {
+    n_qt = p.total_tiles;  // 128-row tiles of all sequences (per head); the key tiles are the same
+    n_units_q = p.A;
+    n_units_kv = p.A_kv;
+    p.dq_units_per_xcd = p.dq_group = p.kv_units_per_xcd = p.kv_group = 0;
+  } else {
+    n_qt = (p.S_q + kBwdQRows - 1) / kBwdQRows;
+    n_units_q = p.A * p.B;
+    n_units_kv = p.A_kv * p.B;
+    plan_order(p.A * p.B, kDqGroupMax, p.dq_units_per_xcd, p.dq_group);
+    plan_order(p.A_kv * p.B, kKvGroupMax, p.kv_units_per_xcd, p.kv_group);
   }
-  if (p.S_k > 0) {
+  const int n_kt = kVarlen ? p.total_tiles : (p.S_k + kBwdKRows - 1) / kBwdKRows;
+  // the dQ pass writes the row statistics the dK/dV pass reads: same stream, in order
+  if (n_qt > 0 && (kVarlen || p.S_q > 0)) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kVarlen, kMasks>), dim3(n_qt * n_units_q), dim3(kThreads), 0, stream, p,
+                       n_qt);
+  }
+  if (n_kt > 0 && (kVarlen || p.S_k > 0)) {
     // with no query row every key gradient is zero; the kernel still writes them
-    const int n_kt = (p.S_k + kBwdKRows - 1) / kBwdKRows;
-    const int n_wg = n_kt * p.A_kv * p.B;
+    const int n_wg = n_kt * n_units_kv;
     // The K-in-LDS form doubles the resident workgroups but halves what one
     // of them gets of its SIMD.  Causal key tiles differ in length (the first
     // sees every query row), so with few workgroups per slot the longest one
     // sets the time and the one-wave form is faster (GQA B=1 S=8192: 512
     // workgroups); with several per slot the two-wave form wins (MHA B=4
-    // S=2048: 2048 workgroups, +18%).
+    // S=2048: 2048 workgroups, +18%).  With a block mask or an additive term,
+    // and for packed sequences, the one-wave form runs (its register budget
+    // holds the term loads and the sequence bookkeeping).
     bool two_wave = false;
-    if constexpr (D == 128) two_wave = n_wg >= kKlDsMinWorkgroups;
-    if (two_wave) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
-    } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
+    if constexpr (D == 128 && !kMasks && !kVarlen) two_wave = n_wg >= kKlDsMinWorkgroups;
+    if constexpr (D == 128 && !kMasks && !kVarlen) {
+      if (two_wave) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, kVarlen, false>), dim3(n_wg), dim3(kThreads), 0, stream, p,
+                           n_kt);
+        return hipGetLastError();
+      }
     }
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, kMasks>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
+    (void)two_wave;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  if (p.cu_seqlens) return launch_bwd_v<D, true, false>(p, stream);
+  if (p.block_keep || p.bias) return launch_bwd_v<D, false, true>(p, stream);
+  return launch_bwd_v<D, false, false>(p, stream);
 }
 
 }  // namespace

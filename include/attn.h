@@ -78,8 +78,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * [128 i, 128 i + 128) and key in [128 j, 128 j + 128) (h' = 0 when
  * block_heads == 1, else the query head); those key tiles are never loaded.
  * block_heads is 1 or A (ignored when block_keep is NULL).  Requires
- * S_k <= 262144.  attn_fwd_varlen and attn_bwd return ATTN_ERR_UNSUPPORTED
- * for a non-NULL block_keep.
+ * S_k <= 262144.  attn_fwd and attn_bwd take it; the packed and paged entry
+ * points return ATTN_ERR_UNSUPPORTED for a non-NULL block_keep.
  *
  * bias (attn_fwd only): the general dense additive mask M of the operation
  * (page "Attention Kernel", section "可编程 mask"; the term "+ M" of section
@@ -99,8 +99,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * Requires bias_heads in {1, A}, bias_ld >= S_k and a multiple of 4, and
  * bias 16-byte aligned.  It combines with every other mask; key tiles are
  * skipped only through block_keep, which attn_block_keep_from_bias derives
- * from a bias.  attn_fwd_varlen and attn_bwd return ATTN_ERR_UNSUPPORTED for
- * a non-NULL bias. */
+ * from a bias.  attn_fwd and attn_bwd take it; the packed entry points
+ * return ATTN_ERR_UNSUPPORTED for a non-NULL bias. */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
@@ -310,7 +310,12 @@ attn_status attn_prefill_paged(const void *q, const void *k_cache, const void *v
  *   lse       : [B, A, S_q] fp32, as attn_fwd wrote it for the same q, k, v,
  *               scale, causal and mask; rows with lse = -inf take no part
  *   o         : attn_fwd's output for the same call
- *   mask      : NULL or keep-masks [B, S_q] / [B, S_k], as given to attn_fwd
+ *   mask      : NULL or the attn_fwd mask of the same call: keep-masks
+ *               [B, S_q] / [B, S_k], a block mask (block_keep, block_heads)
+ *               and a dense additive term (bias, bias_heads, bias_ld), with
+ *               the layouts and rules of attn_mask; a block mask requires
+ *               ceil(S_k / 128) <= 2048 and (A / A_kv) * ceil(S_q / 128) <=
+ *               4096 (ATTN_ERR_UNSUPPORTED otherwise)
  *   window    : NULL or the sliding window given to attn_fwd
  *   workspace : device buffer of at least attn_bwd_workspace_bytes(B, A, S_q)
  *               bytes, 256-byte aligned (two fp32 per query row: the base-2
@@ -328,7 +333,32 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                      const attn_window *window, attn_dtype dtype, void *workspace,
                      size_t workspace_bytes, void *stream);
 
-/* Workspace bytes attn_bwd needs (0 on bad input). */
+/*
+ * Backward of attn_fwd_varlen (page "Attention Kernel", section "Backward 与
+ * 重计算": packed-sequence boundaries are part of the backward's contract):
+ * dQ, dK, dV of each packed sequence, every sequence its own problem as in
+ * the forward (a query sees keys of its own sequence only; causal and the
+ * window compare positions within it).
+ *
+ *   q, o, dout, dq : [A, T, d_h]      k, v, dk, dv : [A_kv, T, d_h]
+ *   lse            : [A, T] fp32, attn_fwd_varlen's for the same call
+ *   cu_seqlens, cu_seqlens_host, n_seq, total_tokens : as attn_fwd_varlen
+ *   mask           : NULL or keep-masks q_keep [T], k_keep [T]
+ *   window         : NULL or the sliding window given to attn_fwd_varlen
+ *   workspace      : device buffer of at least attn_bwd_workspace_bytes(1,
+ *                    A, total_tokens) bytes, 256-byte aligned
+ *
+ * Outputs, determinism, alignment and support as attn_bwd; a block mask or
+ * an additive term is ATTN_ERR_UNSUPPORTED (the packed forward takes none).
+ */
+attn_status attn_bwd_varlen(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                            const float *lse, void *dq, void *dk, void *dv, const int32_t *cu_seqlens,
+                            const int32_t *cu_seqlens_host, int n_seq, int total_tokens, int A, int A_kv,
+                            int d_h, float scale, int causal, const attn_mask *mask, const attn_window *window,
+                            attn_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_bwd needs (0 on bad input); attn_bwd_varlen needs
+ * attn_bwd_workspace_bytes(1, A, total_tokens). */
 size_t attn_bwd_workspace_bytes(int B, int A, int S_q);
 
 /* Static text for a status code. */

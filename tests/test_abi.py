@@ -20,7 +20,7 @@ def header_functions():
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_noalloc",
-                                         "attn_decode_paged_workspace_bytes", "attn_bwd",
+                                         "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
                                          "attn_block_keep_from_bias", "attn_status_string",
                                          "attn_abi_version"])
@@ -317,12 +317,40 @@ def test_attn_bwd_rejects_bad_arguments():
     assert bwd(ws=None) == INVAL
     assert bwd(d=96) == UNSUP
     assert bwd(dt=0) == UNSUP                      # the backward is bf16 only
-    bias_mask = ctypes.byref(Mask(None, None, None, 0, 4096, 1, 8))
-    assert lib.attn_bwd(P, P, P, P, P, P, P, P, P, 1, 4, 2, 8, 8, 128, 0.1, 1, bias_mask, None, 1, P, 1 << 20,
-                        None) == UNSUP             # the dense additive mask: forward only
+    mk = lambda *a: ctypes.byref(Mask(*a))
+    call = lambda m, S_q=8, S_k=8: lib.attn_bwd(P, P, P, P, P, P, P, P, P, 1, 4, 2, S_q, S_k, 128, 0.1, 1, m, None,
+                                                1, P, 1 << 30, None)
+    assert call(mk(None, None, None, 0, 4096, 3, 8)) == INVAL           # additive term: heads 1 or A
+    assert call(mk(None, None, None, 0, 4104, 1, 8)) == INVAL           # additive term: 16-byte aligned
+    assert call(mk(None, None, 4096, 3)) == INVAL                       # block mask: heads 1 or A
+    assert call(mk(None, None, 4096, 1), S_k=300000) == UNSUP           # block mask: at most 2048 key blocks
+    assert call(mk(None, None, 4096, 1), S_q=2 * 4096 * 128 + 1) == UNSUP   # G x row blocks > 4096
     assert lib.attn_bwd_workspace_bytes(2, 8, 100) == 12800
     assert lib.attn_bwd_workspace_bytes(1, 1, 1) == 256
     assert lib.attn_bwd_workspace_bytes(0, 8, 100) == 0
+
+
+def test_attn_bwd_varlen_rejects_bad_arguments():
+    lib = _lib()
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_bwd_varlen.argtypes = [vp] * 11 + [i] * 5 + [f, i, vp, vp, i, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd_varlen.restype = i
+    INVAL, UNSUP, OK = 1, 2, 0
+    good = np.array([0, 5, 5, 9], np.int32)
+
+    def call(cu=good, T=9, A=4, A_kv=2, d=128, dt=1, ws=P, ws_bytes=1 << 20, mask=None, q=P, cud=P):
+        return lib.attn_bwd_varlen(q, P, P, P, P, P, P, P, P, cud, cu.ctypes.data_as(vp), cu.size - 1, T, A, A_kv,
+                                   d, 0.1, 1, mask, None, dt, ws, ws_bytes, None)
+    assert call(cu=np.array([0, 5, 3, 9], np.int32)) == INVAL      # decreasing
+    assert call(T=10) == INVAL                                    # cu[n_seq] != T
+    assert call(A=3) == INVAL
+    assert call(ws_bytes=16) == INVAL                             # workspace too small
+    assert call(ws=ctypes.c_void_p(4096 + 16)) == INVAL           # not 256-byte aligned
+    assert call(q=ctypes.c_void_p(4096 + 8)) == INVAL             # 16-byte alignment
+    assert call(cud=ctypes.c_void_p(4096 + 2)) == INVAL
+    assert call(d=96) == UNSUP and call(dt=0) == UNSUP
+    assert call(mask=ctypes.byref(Mask(None, None, 4096, 1))) == UNSUP   # block masks: dense only
+    assert call(cu=np.array([0, 0, 0], np.int32), T=0) == OK       # nothing to do
 
 
 def test_attn_prefill_paged_rejects_bad_arguments():
