@@ -70,6 +70,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (causal-adjusted) + paged-decode KV GB/s, % roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 CSRC = os.path.join(ROOT, "exact_attention_108_amd", "csrc")
 # sources that determine each timed kernel's memory traffic
 KERNEL_SOURCES = {
@@ -333,11 +334,11 @@ def grid_matches(kname: str, grid: int, pattern: str, wgs) -> bool:
 # kernel serves the MHA workload (16 query tiles x 32 heads x 4 batch rows), the
 # long GQA workload (128 x 32) and the sliding-window leg (256 x 32), so the
 # grid tells them apart.
-DENSE = "prefill_bf16_kernel<128, false, false, false, false>"
+DENSE = "prefill_bf16_kernel<128, false, false, false, false, false>"
 TRAFFIC_PARTS = {
     "prefill": (DENSE, 2048),
     "gqa_long": (DENSE, 4096),
-    "varlen": ("prefill_bf16_kernel<64, true, false, false, false>", None),
+    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false>", None),
     "decode_split": ("decode_split_kernel<128, 1, false>", None),
     "decode_merge": ("decode_merge_kernel", None),
     "bwd_dq": ("bwd_dq_kernel<128>", None),
@@ -347,18 +348,22 @@ TRACE_ROWS = [  # (label, kernel pattern, workgroups or None, algorithmic work p
     ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, (1.374389534720e11, "TFLOP/s")),
     ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, (2.199023255552e12, "TFLOP/s")),
     ("sliding-window GQA causal prefill S=32768, 4096-key window", DENSE, 8192, None),
-    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false>", None, None),
+    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false>", None, None),
     ("paged decode split (bf16 cache)", "decode_split_kernel<128, 1, false>", None, None),
     ("paged decode LSE merge (bf16 and FP8 legs)", "decode_merge_kernel<128>", None, None),
     ("paged decode split (FP8 cache)", "decode_split_kernel<128, 2, true>", None, None),
     ("backward dQ pass", "bwd_dq_kernel<128>", None, None),
     ("backward dK/dV pass", "bwd_dkdv_kernel<128,", None, None),
-    ("paged chunked prefill", "prefill_bf16_kernel<128, true, true, false, false>", None, None),
-    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false>", None, None),
-    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true>", None,
+    ("paged chunked prefill", "prefill_bf16_kernel<128, true, true, false, false, false>", None, None),
+    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false>", None, None),
+    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false>", None,
      None),
-    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true>", None, None),
+    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false>", None, None),
     ("block mask of an additive term", "block_keep_kernel", None, None),
+    ("FP8-QK causal prefill, MHA shape", "prefill_bf16_kernel<128, false, false, false, false, true>", 2048,
+     (1.374389534720e11, "TFLOP/s")),
+    ("FP8-QK causal prefill, long GQA shape", "prefill_bf16_kernel<128, false, false, false, false, true>", 4096,
+     (2.199023255552e12, "TFLOP/s")),
 ]
 
 
@@ -545,7 +550,7 @@ def main():
                      "traffic": None if traffic_prefill is None else round(traffic_prefill),
                      "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
                      "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
-                     "kernel": "prefill_bf16_kernel<128, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
+                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
                      "median_launch_ms": round(med["prefill"], 5), "min_launch_ms": round(mn["prefill"], 5),
                      "measured_ceiling": {"what": "torch.matmul bf16 8192^3 on the same GPU",
                                           "TFLOP/s": ceil["gemm_tflops"],
@@ -587,6 +592,7 @@ def main():
     out["block_sparse"] = bench_block_sparse(w, args.steps, args.warmup)
     out["dense_mask"] = bench_dense_mask(w, args.steps, args.warmup)
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
+    out["fp8_prefill"] = bench_fp8_prefill(args.steps, args.warmup, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
@@ -758,6 +764,43 @@ def bench_decode_fp8(w, steps: int, warmup: int, bf16_ms: float) -> dict:
             "speedup_vs_bf16_cache": round(bf16_ms / float(ms.mean()), 3),
             "workload": "the paged decode workload (64 seqs, A=32 A_kv=8 d=128, page 16) with E4M3 caches "
                         "quantised per (page, KV head)"}
+
+
+def bench_fp8_prefill(steps: int, warmup: int, stream) -> dict:
+    """Causal prefill with FP8 (E4M3) queries and keys, one scale per 128 tokens
+    (attn_fwd_fp8): the MHA and long GQA workloads' shapes.  Half of the FLOPs
+    (QK^T) run on the FP8 matrix cores, half (PV) on the bf16 ones, so beside
+    the 5.0 PF fp8 peak the line gives the mixed peak those two halves allow,
+    2 / (1/5.0 + 1/2.5) = 3.33 PF."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    mixed = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+    out = {"metric": "FP8-QK causal prefill TFLOP/s (causal-adjusted)", "unit": "TFLOP/s",
+           "peak_fp8": PEAK_FP8_TFLOPS, "peak_mixed": round(mixed, 1)}
+    for name, (B, A, A_kv, S) in (("mha", (4, 32, 32, 2048)), ("gqa_long", (1, 32, 8, 16384))):
+        t0 = time.time()
+        p = gen.make_dense_fp8(B, A, A_kv, S, S, 128, causal=True, seed=1010 + S)
+        log(f"fp8 prefill {name} inputs ready ({time.time() - t0:.1f}s)")
+        q, k = torch.from_numpy(p.q_codes).cuda(), torch.from_numpy(p.k_codes).cuda()
+        v = to_dev(p.v, "bf16")
+        qs, ks = torch.from_numpy(p.q_scale).cuda(), torch.from_numpy(p.k_scale).cuda()
+        o = torch.empty((B, A, S, 128), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, A, S), dtype=torch.float32, device="cuda")
+        ms = _event_times(lambda: ea.attn_fwd_fp8(q, k, v, o, lse, qs, ks, scale=p.scale, causal=True,
+                                                  stream=stream), steps, warmup, stream)
+        tf = p.flops() / (ms.mean() * 1e-3) / 1e12
+        out[name] = {"value": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "frac_of_mixed_peak": round(tf / mixed, 4), "avg_ms": round(float(ms.mean()), 5),
+                     "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5),
+                     "flops": p.flops(),
+                     "workload": f"causal B={B} A={A} A_kv={A_kv} S={S} d=128, E4M3 Q/K, bf16 V"}
+        del q, k, v, o, lse, qs, ks
+    torch.cuda.empty_cache()
+    out["value"] = out["mha"]["value"]
+    out["roofline"] = {"bound": "mfma", "achieved": out["mha"]["value"], "peak": PEAK_FP8_TFLOPS,
+                       "unit": "TFLOP/s", "frac": out["mha"]["frac_of_fp8_peak"]}
+    return out
 
 
 def bench_block_sparse(w, steps: int, warmup: int) -> dict:

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     DECODE_NOALLOC_MAX_BYTES,
     attn_decode_paged_workspace_bytes,
     attn_fwd,
+    attn_fwd_fp8,
     attn_fwd_varlen,
     attn_prefill_paged,
     attn_status_string,

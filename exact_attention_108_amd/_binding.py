@@ -38,6 +38,8 @@ _WP = ctypes.POINTER(_Window)
 _lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, ctypes.POINTER(_Mask), _WP, _i,
                           _vp]
 _lib.attn_fwd.restype = _i
+_lib.attn_fwd_fp8.argtypes = [_vp] * 7 + [_i] * 6 + [_f, _i, ctypes.POINTER(_Mask), _WP, _vp]
+_lib.attn_fwd_fp8.restype = _i
 _lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                                  ctypes.POINTER(_Mask), _WP, _i, _vp]
 _lib.attn_fwd_varlen.restype = _i
@@ -86,7 +88,7 @@ def attn_abi_version() -> int:
 
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
-    return ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
+    return ["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
             "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
@@ -218,6 +220,37 @@ def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None
                        int(bool(causal)), _mask(q_keep, k_keep, block_keep, bias, bh, ld), _window(window),
                        _dtype_code(q), _stream(stream, dev))
     _check(st, "attn_fwd")
+
+
+def attn_fwd_fp8(q, k, v, o, lse, q_scale, k_scale, *, scale: float, causal: bool = False, q_keep=None,
+                 k_keep=None, window=None, stream=None):
+    """attn_fwd with E4M3 queries and keys: q uint8 [B,A,S_q,128], k uint8 [B,A_kv,S_k,128] (code bytes),
+    q_scale fp32 [B,A,ceil(S_q/128)], k_scale fp32 [B,A_kv,ceil(S_k/128)] (one scale per 128 tokens);
+    v bf16 [B,A_kv,S_k,128]; o bf16 like q; lse fp32 [B,A,S_q]."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, heads, S, d]")
+    B, A, S_q, d = q.shape
+    _, A_kv, S_k, _ = k.shape
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
+        raise ValueError("q, k: uint8 E4M3 codes; v, o: bf16")
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if lse.shape != (B, A, S_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, A, S_q]")
+    if q_scale.dtype != torch.float32 or tuple(q_scale.shape) != (B, A, (S_q + 127) // 128):
+        raise ValueError("q_scale must be fp32 [B, A, ceil(S_q/128)]")
+    if k_scale.dtype != torch.float32 or tuple(k_scale.shape) != (B, A_kv, (S_k + 127) // 128):
+        raise ValueError("k_scale must be fp32 [B, A_kv, ceil(S_k/128)]")
+    if q_keep is not None and q_keep.shape != (B, S_q):
+        raise ValueError("q_keep must be [B, S_q]")
+    if k_keep is not None and k_keep.shape != (B, S_k):
+        raise ValueError("k_keep must be [B, S_k]")
+    dev = _dev(q, k, v, o, lse, q_scale, k_scale, q_keep, k_keep)
+    st = _lib.attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scale), _ptr(k_scale), B, A, A_kv,
+                           S_q, S_k, d, float(scale), int(bool(causal)), _mask(q_keep, k_keep), _window(window),
+                           _stream(stream, dev))
+    _check(st, "attn_fwd_fp8")
 
 
 def pad_bias(bias):

@@ -133,6 +133,38 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   return launch_status(e);
 }
 
+ATTN_EXPORT attn_status attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const void* v, void* o, float* lse,
+                                     const float* q_scale, const float* k_scale, int B, int A, int A_kv, int S_q,
+                                     int S_k, int d_h, float scale, int causal, const attn_mask* mask,
+                                     const attn_window* window, void* stream) {
+  if (B < 1 || A < 1 || A_kv < 1 || S_q < 0 || S_k < 0 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
+  if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
+  if (S_q > 0 && (!q || !o || !lse || !q_scale)) return ATTN_ERR_INVAL;
+  if (S_k > 0 && (!k || !v || !k_scale)) return ATTN_ERR_INVAL;
+  for (const void* t : {(const void*)q, (const void*)k, v, (const void*)o})
+    if (!aligned(t, 16)) return ATTN_ERR_INVAL;
+  for (const void* t : {(const void*)lse, (const void*)q_scale, (const void*)k_scale})
+    if (!aligned(t, 4)) return ATTN_ERR_INVAL;
+  if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
+  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;
+  if (S_k > attn::kFp8MaxKeys) return ATTN_ERR_UNSUPPORTED;
+  if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
+  if (S_q == 0) return ATTN_OK;
+  const long long n_qt = (S_q + attn::kPrefillRows - 1) / attn::kPrefillRows;
+  if (n_qt * (long long)A * (long long)B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * A * (long long)S_q > INT_MAX || (long long)B * A_kv * (long long)S_k > INT_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window, S_k, S_q);
+  p.B = B;
+  p.S_q = S_q;
+  p.S_k = S_k;
+  p.n_qt = (int)n_qt;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  attn::plan_dense_order(p);
+  return launch_status(attn::launch_prefill_fp8(p, (hipStream_t)stream));
+}
+
 ATTN_EXPORT attn_status attn_block_keep_from_bias(const float* bias, int B, int bias_heads, int S_q, int S_k,
                                                   int bias_ld, uint8_t* block_keep, void* stream) {
   if (B < 1 || S_q < 0 || S_k < 0 || bias_heads < 1) return ATTN_ERR_INVAL;

@@ -50,6 +50,11 @@ struct FwdParams {
   const float* bias;
   int bias_heads, bias_ld;
   float inv_scale;
+  // FP8 queries and keys (dense prefill, d = 128): q, k hold OCP E4M3 codes,
+  // one fp32 scale per 128 consecutive tokens of each (batch, head):
+  // q_scale [B, A, ceil(S_q / 128)], k_scale [B, A_kv, ceil(S_k / 128)]
+  const float* q_scale;
+  const float* k_scale;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin
@@ -90,6 +95,10 @@ hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stre
 // bf16 prefill of packed query chunks over a paged KV cache (d in {64, 128};
 // page_size a power of two and a multiple of 2048 / d).
 hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream);
+// prefill with FP8 (E4M3) queries and keys and bf16 values (d = 128, S_k <=
+// kFp8MaxKeys): the QK^T products on the FP8 matrix cores
+constexpr int kFp8MaxKeys = 262144;
+hipError_t launch_prefill_fp8(const FwdParams& p, hipStream_t stream);
 // fp32 prefill (1 <= d <= 128).
 hipError_t launch_prefill_f32(const FwdParams& p, bool varlen, hipStream_t stream);
 // block_keep[b][h][qb][kb] = whether some bias entry of the 128 x 128 block is

@@ -76,22 +76,35 @@ constexpr int kMaxListedTiles = 4096;
 template <int D, bool kPaged, bool kBias>
 constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias) ? 3 : 2;
 
-template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false>
+// kFp8: queries and keys are OCP E4M3 codes with one fp32 scale per 128
+// tokens (FwdParams::q_scale / k_scale); S^T = K . Q^T runs on the FP8 matrix
+// cores (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block exponents) and is
+// scaled by q_scale * k_scale in fp32; values stay bf16 (dense, d = 128).
+template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias>, kWavesPerSimd<D, kPaged, kBias>))) void prefill_bf16_kernel(FwdParams p) {
+  static_assert(!kFp8 || (D == 128 && !kVarlen && !kPaged && !kBlocks && !kBias), "fp8: dense, d = 128");
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
   constexpr int MB = D / 32;               // 32-row blocks of O^T
   constexpr int TILE_CH = kBc * NCH;       // chunks per K (or V) tile
   constexpr int LD_PER_T = TILE_CH / kThreads;  // 16-byte copies per thread per K (or V) tile
   static_assert(TILE_CH % kThreads == 0, "tile load split");
+  // K rows in 2-byte units: an FP8 key row of D bytes is laid out, copied and
+  // swizzled like a bf16 row of D / 2 elements
+  constexpr int DK = kFp8 ? D / 2 : D;
+  constexpr int NCHK = DK / 8;
+  constexpr int LD_K = kBc * NCHK / kThreads;   // copies per thread per K tile
+  constexpr int KTILE_BYTES = kBc * DK * 2;
 
   // [K buf 0 | K buf 1 | V buf 0 | V buf 1]; the epilogue reuses it for staging
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kBc * D];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBc * DK + 2 * kBc * D];
   __shared__ uint8_t sKeep[2][kBc];
   // block-sparse mode: the physical index of each listed key tile, and the
   // per-wave counts of the list-building scans
   __shared__ uint16_t sTiles[kBlocks ? kMaxListedTiles : 1];
   __shared__ int sCnt[kBlocks ? kWaves : 1];
+  // fp8: the key scales of the 128-key blocks of this workgroup's key range
+  __shared__ float sKs[kFp8 ? kFp8MaxKeys / 128 : 1];
 
   RowBlock rb;
   if constexpr (kPaged) {
@@ -99,7 +112,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   } else if constexpr (kVarlen) {
     if (!setup_varlen<kRows>(p, D * 2, rb)) return;
   } else {
-    rb = setup_dense<kRows>(p, D * 2);
+    rb = setup_dense<kRows>(p, D * 2, kFp8 ? D : 0);
   }
 
   const uint16_t* gq = (const uint16_t*)rb.q;
@@ -210,13 +223,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   };
 
   // ---- resident Q operand: lane holds Q[qrow][16t + 8g .. +7] for each t
-  bf16x8 qf[KSTEPS];
+  // (fp8: the 32 code bytes [64t + 32g, +32) of its row for each 64-wide t)
+  [[maybe_unused]] bf16x8 qf[kFp8 ? 1 : KSTEPS];
+  [[maybe_unused]] i32x8 qf8[kFp8 ? D / 64 : 1];
+  if constexpr (kFp8) {
+    const uint8_t* q8 = (const uint8_t*)rb.q;
 #pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    if (qrow < S_q) {
-      qf[t] = *(const bf16x8*)(gq + (size_t)qrow * D + 16 * t + 8 * g);
-    } else {
-      qf[t] = bf16x8{};
+    for (int t = 0; t < D / 64; ++t)
+      qf8[t] = qrow < S_q ? *(const i32x8*)(q8 + (size_t)qrow * D + 64 * t + 32 * g) : i32x8{};
+  } else {
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      if (qrow < S_q) {
+        qf[t] = *(const bf16x8*)(gq + (size_t)qrow * D + 16 * t + 8 * g);
+      } else {
+        qf[t] = bf16x8{};
+      }
     }
   }
 
@@ -236,6 +258,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // buffers iteration j-1 finished with.
   constexpr int RPC = kThreads / NCH;  // rows per copy round (a multiple of 16)
   constexpr int TILE_BYTES = kBc * D * 2;
+  constexpr int VB0 = 2 * KTILE_BYTES;  // LDS byte offset of V buffer 0
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const int rowc = (wave * 64 + lane) / NCH, pcc = (wave * 64 + lane) % NCH;
   const int cc = lds_chunk<D>(rowc, pcc);  // the swizzle is an involution; it depends on row % 16 only
@@ -251,6 +274,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // part i (of LD_PER_T) of one tile of K (or V) into LDS byte offset `dst`
   auto copy_part = [&](const i32x4& rsrc, uint32_t dst, int i) {
     lds_copy16_buf(rsrc, coff[i], lds_base + dst + (uint32_t)(i * RPC * D * 2) + (uint32_t)wave_u * 1024u);
+  };
+  // the same for K tiles in the DK geometry (fp8 keys; = the above for bf16)
+  constexpr int RPCK = kThreads / NCHK;
+  const int rowck = (wave * 64 + lane) / NCHK, pcck = (wave * 64 + lane) % NCHK;
+  const int cck = lds_chunk<DK>(rowck, pcck);
+  uint32_t coffk[LD_K];
+#pragma unroll
+  for (int i = 0; i < LD_K; ++i) coffk[i] = (uint32_t)((i * RPCK + rowck) * DK * 2 + cck * 16);
+  auto tile_rsrc_k = [&](const uint16_t* gsrc, int t) {
+    const int k0 = phys(t) * kBc;
+    const int rows = min(max(S_k - k0, 0), kBc);
+    return make_buffer_rsrc(gsrc + (size_t)k0 * DK, (uint32_t)(rows * DK * 2));
+  };
+  auto copy_part_k = [&](const i32x4& rsrc, uint32_t dst, int i) {
+    lds_copy16_buf(rsrc, coffk[i], lds_base + dst + (uint32_t)(i * RPCK * DK * 2) + (uint32_t)wave_u * 1024u);
   };
   // Paged KV: part i of a tile is RPC consecutive tokens, which the page size
   // (a power of two, a multiple of RPC) keeps inside one page.  Its resource
@@ -313,6 +351,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   for (int mb = 0; mb < MB; ++mb) acc_o[mb] = f32x16{};
 
   const float cs = p.scale_log2;
+  // FP8 keys and queries: tile t's scores scale by q_scale (this row block) *
+  // k_scale (the 128-key block of tile t); the key scales of the workgroup's
+  // range are staged in LDS (the prologue's barrier orders them)
+  [[maybe_unused]] float cs_q = cs;
+  [[maybe_unused]] const int kblk0 = j_lo >> 1;
+  if constexpr (kFp8) {
+    cs_q = cs * p.q_scale[(size_t)(rb.b * p.A + rb.h) * p.n_qt + rb.qt];
+    const int n_kblk = (S_k + 127) / 128;
+    const float* ks = p.k_scale + (size_t)(rb.b * p.A_kv + rb.h / p.G) * n_kblk;
+    const int nkb = n_range > 0 ? ((j_lo + n_range - 1) >> 1) - kblk0 + 1 : 0;
+    for (int i = tid; i < nkb; i += kThreads) sKs[i] = ks[kblk0 + i];
+  }
+  auto cs_of = [&](int t) -> float {
+    if constexpr (kFp8) {
+      const int bits = __builtin_amdgcn_readfirstlane(__float_as_int(sKs[(phys(t) >> 1) - kblk0]));
+      return cs_q * __int_as_float(bits);
+    } else {
+      return cs;
+    }
+  };
   const int wave_q0 = rb.q0 + wave * 32;
   // keys [kbeg_w, kend_w) hold every key some row of this wave keeps; a
   // tile outside them is dead for the whole wave (only edge tiles can be:
@@ -351,10 +409,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // S^T = K . Q^T for the K tile in LDS buffer KBUF: two 32-key blocks, the
   // k-steps interleaved across them.  `issue` is called at two points.
   auto qk = [&](auto kbuf_tag, f32x16 (&s)[2], auto&& issue) {
-    constexpr int KB = decltype(kbuf_tag)::value * TILE_BYTES;
-    constexpr int NQ = 2 * KSTEPS;
+    constexpr int KB = decltype(kbuf_tag)::value * KTILE_BYTES;
     s[0] = f32x16{};
     s[1] = f32x16{};
+    if constexpr (kFp8) {
+      // FP8: steps p = (kb = p % 2, t = p / 2) over 64-wide k-steps; lane reads
+      // row l32 of key block kb, the 32 bytes [64t + 32g, +32) = logical
+      // chunks 4t + 2g and 4t + 2g + 1 of the D-byte row (DK-geometry swizzle)
+      constexpr int NQ8 = 2 * (D / 64);
+      i32x8 ka8[NQ8];
+#pragma unroll
+      for (int q = 0; q < NQ8; ++q) {
+        const int kb = q % 2, t = q / 2;
+        const char* row = lds + KB + kb * 32 * DK * 2 + l32 * DK * 2;
+        const i32x4 lo = *(const i32x4*)(row + lds_chunk<DK>(l32, 4 * t + 2 * g) * 16);
+        const i32x4 hi = *(const i32x4*)(row + lds_chunk<DK>(l32, 4 * t + 2 * g + 1) * 16);
+        ka8[q] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      issue(0);
+#pragma unroll
+      for (int q = 0; q < NQ8; ++q) {
+        s[q % 2] = mfma32_fp8(ka8[q], qf8[q / 2], s[q % 2]);
+        if (q == NQ8 / 2) issue(1);
+      }
+      return;
+    }
+    constexpr int NQ = 2 * KSTEPS;
     bf16x8 ka[NQ];
     auto kread = [&](int p) {  // step p: kb = p % 2, t = p / 2
       ka[p] = *(const bf16x8*)(lds + KB + (p % 2) * 32 * D * 2 + koff[p / 2]);
@@ -425,7 +505,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   };
   // row max of a tile in base-2 units (scale > 0), both lane halves: four
   // chains of three-input maxima
-  auto rowmax = [&](const f32x16 (&s)[2]) {
+  auto rowmax = [&](const f32x16 (&s)[2], float csx) {
     float mx[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -435,7 +515,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       m = fmaxf(m, fmaxf(s[kb][r0 + 5], s[kb][r0 + 6]));
       mx[c] = fmaxf(m, s[kb][r0 + 7]);
     }
-    return max_with_other_half(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * cs;
+    return max_with_other_half(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * csx;
   };
   // move the reference only when some row of the wave needs it
   auto rescale = [&](float mxs) {
@@ -452,17 +532,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // LDS buffer VBUF; the normaliser sums p in fp32, the product takes p
   // rounded to bf16.  PV steps (kb, h, mb) with mb innermost: MB independent
   // accumulator chains.  `issue` is called at two points.
-  auto exps = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) -> float {
+  auto exps = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float csx) -> float {
     const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        const float e0 = exp2_fast(fmaf(s[kb][r + 0], cs, neg));
-        const float e1 = exp2_fast(fmaf(s[kb][r + 1], cs, neg));
-        const float e2 = exp2_fast(fmaf(s[kb][r + 2], cs, neg));
-        const float e3 = exp2_fast(fmaf(s[kb][r + 3], cs, neg));
+        const float e0 = exp2_fast(fmaf(s[kb][r + 0], csx, neg));
+        const float e1 = exp2_fast(fmaf(s[kb][r + 1], csx, neg));
+        const float e2 = exp2_fast(fmaf(s[kb][r + 2], csx, neg));
+        const float e3 = exp2_fast(fmaf(s[kb][r + 3], csx, neg));
         rs[0] += e0;
         rs[1] += e1;
         rs[2] += e2;
@@ -475,10 +555,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
-  auto softmax_pv = [&](auto vbuf_tag, const f32x16 (&s)[2], auto&& issue) {
-    constexpr int VB = (2 + decltype(vbuf_tag)::value) * TILE_BYTES;
+  auto softmax_pv = [&](auto vbuf_tag, const f32x16 (&s)[2], float csx, auto&& issue) {
+    constexpr int VB = VB0 + decltype(vbuf_tag)::value * TILE_BYTES;
     bf16x8 pb[2][2];
-    l_run += exps(s, pb);
+    l_run += exps(s, pb, csx);
     constexpr int NV = 4 * MB;
     bf16x8 va[NV];
     auto vread = [&](int q) {  // step q: mb = q % MB, (kb, h) = q / MB
@@ -502,6 +582,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // ---- prologue: K, V of tile 0 and K of tile 1 in flight; S of tile 0
   f32x16 s_cur[2];
   float mx_cur = -INFINITY;
+  float cs_cur = cs;  // the score scale of the tile in s_cur (fp8: per tile)
   if (n_tiles > 0) {
     if constexpr (kPaged) {
       const int t1 = min(1, n_tiles - 1);
@@ -511,17 +592,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         const int p0 = page_of(0, i);
         pg_k[i] = page_of(t1, i);
         copy_part_paged(rb.k, 0, 0, i, p0);
-        copy_part_paged(rb.v, 0, 2 * TILE_BYTES, i, p0);
-        copy_part_paged(rb.k, t1, TILE_BYTES, i, pg_k[i]);
+        copy_part_paged(rb.v, 0, VB0, i, p0);
+        copy_part_paged(rb.k, t1, KTILE_BYTES, i, pg_k[i]);
       }
     } else {
-      const i32x4 rk0 = tile_rsrc(gk, 0), rv0 = tile_rsrc(gv, 0);
-      const i32x4 rk1 = tile_rsrc(gk, min(1, n_tiles - 1));
+      const i32x4 rk0 = tile_rsrc_k(gk, 0), rv0 = tile_rsrc(gv, 0);
+      const i32x4 rk1 = tile_rsrc_k(gk, min(1, n_tiles - 1));
 #pragma unroll
       for (int i = 0; i < LD_PER_T; ++i) {
-        copy_part(rk0, 0, i);
-        copy_part(rv0, 2 * TILE_BYTES, i);
-        copy_part(rk1, TILE_BYTES, i);
+        if (i < LD_K) copy_part_k(rk0, 0, i);
+        copy_part(rv0, VB0, i);
+        if (i < LD_K) copy_part_k(rk1, KTILE_BYTES, i);
       }
     }
     copy_keep(0);
@@ -532,7 +613,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __syncthreads();
     qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
     if (n_mid == 0) mask(s_cur, 0, m0);
-    mx_cur = rowmax(s_cur);
+    cs_cur = cs_of(0);
+    mx_cur = rowmax(s_cur, cs_cur);
   }
 
   // ---- iteration j (tile j in buffers BUF = j % 2): S of tile j+1, softmax
@@ -558,7 +640,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     [[maybe_unused]] i32x4 rk, rv;
     [[maybe_unused]] int pg_v[LD_PER_T];
     if constexpr (!kPaged) {
-      rk = tile_rsrc(gk, tk);
+      rk = tile_rsrc_k(gk, tk);
       rv = tile_rsrc(gv, tv);
     } else {
       // V of tile tv is the K tile the previous iteration copied; the pages
@@ -577,14 +659,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     auto issue = [&](int at) {
 #pragma unroll
       for (int i = 0; i < LD_PER_T; ++i) {
-        if (i * 4 / LD_PER_T == at) {
-          if constexpr (kPaged) {
-            copy_part_paged(rb.k, tk, BUF * TILE_BYTES, i, pg_k[i]);
-            copy_part_paged(rb.v, tv, (2 + (BUF ^ 1)) * TILE_BYTES, i, pg_v[i]);
-          } else {
-            copy_part(rk, BUF * TILE_BYTES, i);
-            copy_part(rv, (2 + (BUF ^ 1)) * TILE_BYTES, i);
+        if constexpr (kPaged) {
+          if (i * 4 / LD_PER_T == at) {
+            copy_part_paged(rb.k, tk, BUF * KTILE_BYTES, i, pg_k[i]);
+            copy_part_paged(rb.v, tv, VB0 + (BUF ^ 1) * TILE_BYTES, i, pg_v[i]);
           }
+        } else {
+          if (i < LD_K && i * 4 / LD_K == at) copy_part_k(rk, BUF * KTILE_BYTES, i);
+          if (i * 4 / LD_PER_T == at) copy_part(rv, VB0 + (BUF ^ 1) * TILE_BYTES, i);
         }
       }
     };
@@ -593,8 +675,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     interleave_hint();
     if constexpr (!MASKED) {
       qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
-      softmax_pv(buf_tag, s_cur, issue);
-      mx_cur = rowmax(s_next);
+      softmax_pv(buf_tag, s_cur, cs_cur, issue);
+      cs_cur = cs_of(j + 1);
+      mx_cur = rowmax(s_next, cs_cur);
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];
     } else {
@@ -610,14 +693,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       }
       if (has_next) bias_load(j + 1, m_next);  // in flight during the softmax and PV of tile j
       if (wave_sees(j)) {
-        softmax_pv(buf_tag, s_cur, issue);
+        softmax_pv(buf_tag, s_cur, cs_cur, issue);
       } else {
         issue(2);
         issue(3);
       }
       if (has_next) {
         mask(s_next, j + 1, m_next);
-        mx_cur = rowmax(s_next);
+        cs_cur = cs_of(j + 1);
+        mx_cur = rowmax(s_next, cs_cur);
         s_cur[0] = s_next[0];
         s_cur[1] = s_next[1];
       }
@@ -649,7 +733,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
   // stage the wave's 32 x D output through LDS for row-contiguous stores
   constexpr int PITCH = D + 8;  // elements; breaks the row-to-bank alignment
-  static_assert(kWaves * 32 * PITCH <= 4 * kBc * D, "epilogue staging fits");
+  static_assert(kWaves * 32 * PITCH <= 2 * kBc * DK + 2 * kBc * D, "epilogue staging fits");
   uint16_t* stage = smem + wave * 32 * PITCH;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -718,6 +802,15 @@ hipError_t launch_prefill_bf16(const FwdParams& p, bool varlen, hipStream_t stre
   if (p.d == 128) return launch_d<128>(p, varlen, stream);
   if (p.d == 64) return launch_d<64>(p, varlen, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_fp8(const FwdParams& p, hipStream_t stream) {
+  const int grid = p.n_qt * p.A * p.B;
+  if (grid <= 0) return hipSuccess;
+  if (p.d != 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false, false, false, true>), dim3(grid), dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream) {

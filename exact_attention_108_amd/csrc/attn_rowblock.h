@@ -22,7 +22,10 @@ struct RowBlock {
 // Dense batch: query tile index descending (heaviest causal tiles first),
 // then batch*head.
 template <int kRows>
-__device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_bytes) {
+__device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_bytes, int qk_row_bytes = 0) {
+  // qk_row_bytes: row size of q and k when it differs from that of v and o
+  // (FP8 queries and keys beside bf16 values); 0 = row_bytes
+  if (qk_row_bytes == 0) qk_row_bytes = row_bytes;
   const int lin = blockIdx.x;
   const int bh_n = p.A * p.B;
   int qt, bh;
@@ -42,10 +45,10 @@ __device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_byte
   RowBlock r;
   const size_t qoff = (size_t)(b * p.A + h) * p.S_q;
   const size_t koff = (size_t)(b * p.A_kv + hk) * p.S_k;
-  r.q = (const char*)p.q + qoff * row_bytes;
+  r.q = (const char*)p.q + qoff * qk_row_bytes;
   r.o = (char*)p.o + qoff * row_bytes;
   r.lse = p.lse + qoff;
-  r.k = (const char*)p.k + koff * row_bytes;
+  r.k = (const char*)p.k + koff * qk_row_bytes;
   r.v = (const char*)p.v + koff * row_bytes;
   r.q_keep = p.q_keep ? p.q_keep + (size_t)b * p.S_q : nullptr;
   r.k_keep = p.k_keep ? p.k_keep + (size_t)b * p.S_k : nullptr;

@@ -144,6 +144,30 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                      attn_dtype dtype, void *stream);
 
 /*
+ * attn_fwd with FP8 queries and keys (page "Attention 算子加速史", section
+ * 3.3: FP8 attention with block-wise adaptive scaling; the QK^T products run
+ * on gfx950's FP8 matrix instructions).  q and k hold one OCP E4M3 byte per
+ * element (4 exponent bits, bias 7, 3 mantissa bits, largest finite 448, no
+ * infinities; 0x7F / 0xFF are NaN and must not occur), with one fp32 scale per
+ * 128 consecutive tokens of each (batch, head); element value = byte value *
+ * scale of its block:
+ *
+ *   q      : uint8 [B, A, S_q, 128]      q_scale : fp32 [B, A, ceil(S_q / 128)]
+ *   k      : uint8 [B, A_kv, S_k, 128]   k_scale : fp32 [B, A_kv, ceil(S_k / 128)]
+ *   v, o   : bf16 [B, A_kv, S_k, 128] / [B, A, S_q, 128];   lse : fp32 [B, A, S_q]
+ *
+ * Scores are formed exactly from the FP8 products (fp32 accumulation), then
+ * multiplied by scale * q_scale * k_scale; the probabilities are rounded to
+ * bf16 for the bf16 P V product, as in attn_fwd.  Scales must be finite and
+ * > 0.  causal, keep-masks and window as attn_fwd; block masks and additive
+ * terms are ATTN_ERR_UNSUPPORTED.  Supported: d_h = 128, S_k <= 262144.
+ */
+attn_status attn_fwd_fp8(const uint8_t *q, const uint8_t *k, const void *v, void *o, float *lse,
+                         const float *q_scale, const float *k_scale, int B, int A, int A_kv, int S_q, int S_k,
+                         int d_h, float scale, int causal, const attn_mask *mask, const attn_window *window,
+                         void *stream);
+
+/*
  * Block mask of a dense additive mask (page "Attention Kernel", section
  * "可编程 mask": the block level of a mask decides which tiles are skipped
  * whole).  Writes block_keep [B, bias_heads, ceil(S_q / 128), ceil(S_k / 128)]

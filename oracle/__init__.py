@@ -271,6 +271,28 @@ class Oracle:
             raise ValueError("oracle_block_keep_of_bias rejected its arguments")
         return out
 
+    def attn_fwd_fp8(self, q_codes, k_codes, v, q_scale, k_scale, *, scale, causal=False, q_keep=None,
+                     k_keep=None, m_keep=None, rows=None):
+        """Dense prefill with FP8 (E4M3) queries and keys: q_codes [B,A,S_q,d],
+        k_codes [B,A_kv,S_k,d] (uint8 codes), one fp32 scale per 128 consecutive
+        tokens of each (batch, head): q_scale [B,A,ceil(S_q/128)], k_scale
+        [B,A_kv,ceil(S_k/128)]; v bf16 bits [B,A_kv,S_k,d].  Query row i's
+        value is code value * q_scale[.., i // 128], key j's code value *
+        k_scale[.., j // 128] (formed in fp64); the attention is attn_fwd's."""
+        qc, kc = np.asarray(q_codes), np.asarray(k_codes)
+        B, A, S_q, d = qc.shape
+        A_kv, S_k = kc.shape[1], kc.shape[2]
+        qs = np.asarray(q_scale, np.float64)
+        ks = np.asarray(k_scale, np.float64)
+        if qs.shape != (B, A, (S_q + 127) // 128) or ks.shape != (B, A_kv, (S_k + 127) // 128):
+            raise ValueError("q_scale [B, A, ceil(S_q/128)], k_scale [B, A_kv, ceil(S_k/128)]")
+        qv = fp8_e4m3_value(qc) * np.repeat(qs, 128, axis=2)[:, :, :S_q, None]
+        kv = fp8_e4m3_value(kc) * np.repeat(ks, 128, axis=2)[:, :, :S_k, None]
+        vb = self._arr(v, "bf16").astype(np.uint32) << np.uint32(16)   # bf16 bits -> fp32 bits
+        vv = vb.view(np.float32).astype(np.float64)
+        return self.attn_fwd(qv, kv, vv, dtype="f64", scale=scale, causal=causal, q_keep=q_keep, k_keep=k_keep,
+                             m_keep=m_keep, rows=rows)
+
     def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
                          seqs=None):
         """Paged decode over FP8 caches (E4M3 codes [P, page_size, A_kv, d] with

@@ -392,6 +392,58 @@ def make_paged_fp8(lens, A, A_kv, d, page_size, *, seed=0, extra_pages=0) -> Pag
     return PagedFp8(base, out[0], out[2], out[1], out[3])
 
 
+@dataclass
+class DenseFp8:
+    """Dense prefill with FP8 queries and keys: q/k_codes uint8 E4M3 [B, A or
+    A_kv, S, d]; q/k_scale fp32 [B, A or A_kv, ceil(S / 128)] (one scale per 128
+    tokens); v bf16 bits [B, A_kv, S_k, d]."""
+    B: int
+    A: int
+    A_kv: int
+    S_q: int
+    S_k: int
+    d: int
+    causal: bool
+    scale: float
+    q_codes: np.ndarray
+    k_codes: np.ndarray
+    q_scale: np.ndarray
+    k_scale: np.ndarray
+    v: np.ndarray
+
+    def flops(self) -> float:
+        f = 4.0 * self.B * self.A * self.S_q * self.S_k * self.d
+        return f / 2 if self.causal else f
+
+
+def _quantise_blocks(x: np.ndarray) -> tuple:
+    """E4M3 codes of x [B, H, S, d] (fp32) with one scale per 128 rows of each
+    (batch, head): scale = max |x| / 448 over the block (1 for an all-zero
+    block), codes = round-to-nearest-even of x / scale."""
+    B, H, S, d = x.shape
+    nb = (S + 127) // 128
+    pad = np.zeros((B, H, nb * 128, d), np.float32)
+    pad[:, :, :S] = x
+    amax = np.abs(pad.reshape(B, H, nb, 128 * d)).max(axis=3)
+    sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = x / np.repeat(sc, 128, axis=2)[:, :, :S, None]
+    return quantize_e4m3(y).reshape(x.shape), sc
+
+
+def make_dense_fp8(B, A, A_kv, S_q, S_k, d, *, causal=False, seed=0, v_kind="normal") -> DenseFp8:
+    """Q, K ~ N(0, 1) drawn in fp32 and quantised to E4M3 per 128-token block;
+    V ~ N(0, 1) (or U(-1, 1)) rounded to bf16; scale = fp32(1 / sqrt(d))."""
+    q = draw((B, A, S_q, d), seed, S_Q, "normal", "f32")
+    k = draw((B, A_kv, S_k, d), seed, S_K, "normal", "f32")
+    if v_kind == "uniform":
+        v = draw((B, A_kv, S_k, d), seed, S_V, "uniform", "bf16", -1.0, 1.0)
+    else:
+        v = draw((B, A_kv, S_k, d), seed, S_V, "normal", "bf16")
+    qc, qs = _quantise_blocks(q)
+    kc, ks = _quantise_blocks(k)
+    return DenseFp8(B, A, A_kv, S_q, S_k, d, causal, float(np.float32(1.0 / math.sqrt(d))), qc, kc, qs, ks, v)
+
+
 # --- the five named workloads -------------------------------------------------
 
 CONFIG_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}

@@ -620,6 +620,38 @@ def pin_fp8_decode_brute_force(orc):
             assert (wl == -math.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - wl) < 1e-13
 
 
+def pin_fp8_prefill_brute_force(orc):
+    """FP8 dense prefill (E4M3 codes, one scale per 128 tokens of each head)
+    against math.fsum over the dequantised rows: S = 300 queries and keys span
+    three scale blocks, each with its own scale, so a block size or index
+    mistake moves rows of the later blocks."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(52)
+    B, A, A_kv, S_q, S_k, d = 1, 2, 1, 300, 280, 4
+    qc = rng.integers(0, 0x7F, size=(B, A, S_q, d)).astype(np.uint8) | (rng.integers(0, 2, size=(B, A, S_q, d)) * 0x80).astype(np.uint8)
+    kc = rng.integers(0, 0x7F, size=(B, A_kv, S_k, d)).astype(np.uint8) | (rng.integers(0, 2, size=(B, A_kv, S_k, d)) * 0x80).astype(np.uint8)
+    qs = rng.uniform(0.001, 0.004, size=(B, A, 3)).astype(np.float32)
+    ks = rng.uniform(0.001, 0.004, size=(B, A_kv, 3)).astype(np.float32)
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, A_kv, S_k, d)).astype(np.float32))
+    o, lse = orc.attn_fwd_fp8(qc, kc, v, qs, ks, scale=0.5, causal=True)
+    vv = gen.bf16_bits_to_f32(v).astype(np.float64)
+    off = S_k - S_q
+    for h in range(A):
+        for i in (0, 21, 127, 128, 200, 255, 256, 299):
+            qrow = [float(x) * float(qs[0, h, i // 128]) for x in oracle_pkg.fp8_e4m3_value(qc[0, h, i])]
+            keys, vals, vis = [], [], []
+            for j in range(S_k):
+                keys.append([float(x) * float(ks[0, 0, j // 128]) for x in oracle_pkg.fp8_e4m3_value(kc[0, 0, j])])
+                vals.append([float(x) for x in vv[0, 0, j]])
+                vis.append(j <= i + off)
+            want, wl = _brute(qrow, keys, vals, 0.5, vis)
+            if wl == -math.inf:
+                assert np.all(o[0, h, i] == 0) and np.isneginf(lse[0, h, i]), (h, i)
+                continue
+            assert np.allclose(o[0, h, i], want, rtol=0, atol=1e-12), (h, i)
+            assert abs(lse[0, h, i] - wl) < 1e-12, (h, i)
+
+
 # ---- gradient (oracle_attn_bwd): the exact derivative of the forward above.
 # Pinned against central finite differences of the (already pinned) forward
 # in fp64, closed forms and invariants of the softmax Jacobian.

@@ -18,7 +18,7 @@ def header_functions():
 
 
 def test_header_declares_entry_points():
-    assert header_functions() == sorted(["attn_fwd", "attn_fwd_varlen", "attn_decode_paged",
+    assert header_functions() == sorted(["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_noalloc",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
@@ -214,6 +214,24 @@ def test_window_edges_clamp(tmp_path):
                     str(src), "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and "window edges ok" in r.stdout, r.stderr
+
+
+def test_attn_fwd_fp8_rejects_bad_arguments():
+    lib = _lib()
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd_fp8.argtypes = [vp] * 7 + [i] * 6 + [f, i, vp, vp, vp]
+    lib.attn_fwd_fp8.restype = i
+    INVAL, UNSUP, OK = 1, 2, 0
+
+    def call(q=P, k=P, qs=P, ks=P, A=4, A_kv=2, S_q=8, S_k=8, d=128, scale=0.1, mask=None):
+        return lib.attn_fwd_fp8(q, k, P, P, P, qs, ks, 1, A, A_kv, S_q, S_k, d, scale, 1, mask, None, None)
+    assert call(A=3) == INVAL and call(scale=0.0) == INVAL
+    assert call(qs=None) == INVAL and call(ks=None) == INVAL
+    assert call(q=ctypes.c_void_p(4096 + 8)) == INVAL and call(qs=ctypes.c_void_p(4096 + 2)) == INVAL
+    assert call(d=64) == UNSUP                                            # d = 128 only
+    assert call(S_k=300000) == UNSUP                                      # key scales staged per workgroup
+    assert call(mask=ctypes.byref(Mask(None, None, 4096, 1))) == UNSUP    # no block masks
+    assert call(S_q=0, q=None, qs=None) == OK
 
 
 def test_attn_fwd_varlen_rejects_bad_arguments():
