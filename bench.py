@@ -593,6 +593,7 @@ def main():
     out["dense_mask"] = bench_dense_mask(w, args.steps, args.warmup)
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
     out["fp8_prefill"] = bench_fp8_prefill(args.steps, args.warmup, stream)
+    out["decode_low_kv"] = bench_decode_low_kv(w, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
@@ -800,6 +801,39 @@ def bench_fp8_prefill(steps: int, warmup: int, stream) -> dict:
     out["value"] = out["mha"]["value"]
     out["roofline"] = {"bound": "mfma", "achieved": out["mha"]["value"], "peak": PEAK_FP8_TFLOPS,
                        "unit": "TFLOP/s", "frac": out["mha"]["frac_of_fp8_peak"]}
+    return out
+
+
+def bench_decode_low_kv(w, steps: int, warmup: int) -> dict:
+    """Paged decode with few KV heads: the decode workload's 64 lengths and
+    page size with A = 32 query heads on A_kv = 1 (MQA: 32 query-head columns
+    per KV head, two column groups) and on A_kv = 2 (one-wave workgroups).
+    KV GB/s = 2 A_kv d 2 bytes x total tokens / time (split + merge)."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p4, stream = w["p4"], w["stream"]
+    out = {"metric": "paged-decode KV GB/s at few KV heads", "unit": "GB/s"}
+    for A_kv in (1, 2):
+        t0 = time.time()
+        p = gen.make_paged(p4.seq_lens, 32, A_kv, 128, 16, dtype="bf16", seed=1030 + A_kv)
+        log(f"decode A_kv={A_kv} inputs ready ({time.time() - t0:.1f}s)")
+        q, kc, vc = to_dev(p.q, "bf16"), to_dev(p.k_cache, "bf16"), to_dev(p.v_cache, "bf16")
+        bt, sl = to_dev(p.block_table, "i32"), to_dev(p.seq_lens, "i32")
+        o = torch.empty_like(q)
+        lse = torch.empty((p.B, p.A), dtype=torch.float32, device="cuda")
+        nb = ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        ms = _event_times(lambda: ea.attn_decode_paged(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale,
+                                                       stream=stream), steps, warmup, stream)
+        kvb = p.kv_bytes()
+        gbs = kvb / (ms.mean() * 1e-3) / 1e9
+        out[f"A_kv={A_kv}"] = {"value": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBPS, 4),
+                               "avg_ms": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
+                               "kv_bytes": kvb, "workload": f"64 seqs, A=32 A_kv={A_kv} d=128 page 16, "
+                                                            "lengths ~U{512..32768}"}
+        del q, kc, vc, bt, sl, o, lse, ws
+    torch.cuda.empty_cache()
     return out
 
 

@@ -235,7 +235,7 @@ attn_status check_decode(int B, int A, int A_kv, int d_h, int page_size, const i
   }
   if (d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
   if (page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
-  if (A / A_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (A / A_kv > 64) return ATTN_ERR_UNSUPPORTED;  // query-head column groups of the split kernel
   return ATTN_OK;
 }
 

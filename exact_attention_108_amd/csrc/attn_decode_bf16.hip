@@ -73,8 +73,15 @@ __device__ __forceinline__ int tok_swz(int tok) { return ((tok & 7) << 1) | ((to
 // path's copy would have put them, so the MFMA code is shared.  The scales
 // stay in fp32: a key's scale multiplies its scores, a value's scale its
 // probabilities before the PV product (the normaliser sums the unscaled ones).
-template <int D, int HPW, bool kFp8 = false>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(DecodeParams p) {
+//
+// Query heads per KV head (G) beyond the 16 columns of one MFMA: NCG column
+// groups of 16 (G <= 16 NCG), each with its own operand, state and products;
+// the K and V operands read from LDS serve every group (MQA: G up to 64).
+// WPG waves per workgroup: 4, or 1 when the workgroup would have fewer KV
+// heads than waves (A_kv < 4 HPW), so that no wave of a resident workgroup
+// sits idle.
+template <int D, int HPW, bool kFp8, int NCG, int WPG>
+__global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) {
   constexpr int RC = HPW * D / 8;            // 16-byte chunks per token row
   constexpr int TOK_PER_LD = 64 / RC;        // tokens per load instruction
   constexpr int N_LD = kChunk / TOK_PER_LD;  // load instructions per chunk (K or V)
@@ -86,13 +93,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
   constexpr int BUF_BYTES = 2 * kChunk * RC * 16;  // bytes: K then V
   constexpr int WAVE_LDS = NBUF * BUF_BYTES;
   static_assert(64 % RC == 0 && kChunk % TOK_PER_LD == 0, "row split");
-  __shared__ __attribute__((aligned(16))) char smem[kWavesPerGroup * WAVE_LDS];
+  __shared__ __attribute__((aligned(16))) char smem[WPG * WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int G = p.G;
-  const int kv0 = (blockIdx.y * kWavesPerGroup + wave) * HPW;  // first KV head of this wave
+  const int kv0 = (blockIdx.y * WPG + wave) * HPW;  // first KV head of this wave
   if (kv0 >= p.A_kv) return;  // no barrier below: waves are independent
   const int nh = min(HPW, p.A_kv - kv0);  // KV heads of this wave
   char* const sK0 = smem + wave * WAVE_LDS;
@@ -138,9 +145,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
   const int ld_tok = lane / RC, ld_pc = lane % RC;
   const int ld_hh = min(ld_pc / (D / 8), nh - 1);
   const int ld_c = ld_pc % (D / 8);
-  const int n_col = l16;
-  const int hh_col = n_col / G;  // which of the wave's KV heads this column belongs to
-  const bool col_live = n_col < nh * G;
+  // column l16 of group cg is query head kv0 * G + 16 cg + l16
+  int hh_col[NCG];  // which of the wave's KV heads the column belongs to
+  bool col_live[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    hh_col[cg] = (16 * cg + l16) / G;
+    col_live[cg] = 16 * cg + l16 < nh * G;
+  }
   const float cs = p.scale_log2;
   const int tr_r = l16 >> 2, tr_q = l16 & 3;
 
@@ -153,20 +165,29 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
 
     // ---- Q^T operand: column n = query head kv0*G + n (n < nh*G), 8 d per lane
     const uint16_t* qb = (const uint16_t*)p.q + ((size_t)b * p.A + (size_t)kv0 * G) * D;
-    bf16x8 qf[KSTEPS];
+    bf16x8 qf[NCG][KSTEPS];
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      qf[t] = col_live ? *(const bf16x8*)(qb + (size_t)n_col * D + 32 * t + 8 * grp) : bf16x8{};
+    for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) {
+        qf[cg][t] = col_live[cg] ? *(const bf16x8*)(qb + (size_t)(16 * cg + l16) * D + 32 * t + 8 * grp)
+                                 : bf16x8{};
+      }
     }
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
     const int last_page = (t_end - 1) / ps;
     int pbase = t_begin / ps;  // lane i holds block-table entry pbase + i
     int page_of_lane = pbase + lane <= last_page ? bt[pbase + lane] : 0;
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[MB];
+    float m_run[NCG], l_run[NCG];
+    f32x4 acc[NCG][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{};
+    for (int cg = 0; cg < NCG; ++cg) {
+      m_run[cg] = -INFINITY;
+      l_run[cg] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[cg][mb] = f32x4{};
+    }
 
     // first token row of chunk c in the cache (for this wave's first KV head).
     // A 16-token chunk lies inside one page (page_size is a multiple of 16);
@@ -208,7 +229,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
         kr[i] = *(const uint2*)(kc8 + e);
         vr[i] = *(const uint2*)(vc8 + e);
       }
-      const size_t srow = (size_t)page * p.A_kv + kv0 + min(hh_col, nh - 1);
+      const size_t srow = (size_t)page * p.A_kv + kv0 + min(hh_col[0], nh - 1);
       ksc_n = p.k_scale[srow];
       vsc_n = p.v_scale[srow];
     };
@@ -276,7 +297,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
         asm volatile("" ::: "memory");
       }
       // ---- S^T = sum_hh K_hh . Q^T_hh (block diagonal over the wave's heads)
-      f32x4 sc = f32x4{};
+      f32x4 sc[NCG];
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) sc[cg] = f32x4{};
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
@@ -284,49 +307,59 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
           const int c = 4 * t + grp;  // logical chunk of lane's 8 d
           const char* ka = sK + (l16 * RC + hh * (D / 8) + (c ^ (tok_swz(l16) & (D / 8 - 1)))) * 16;
           const bf16x8 a = *(const bf16x8*)ka;
-          const bf16x8 bq = (col_live && hh_col == hh) ? qf[t] : bf16x8{};
-          sc = mfma16(a, bq, sc);
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            const bf16x8 bq = (col_live[cg] && hh_col[cg] == hh) ? qf[cg][t] : bf16x8{};
+            sc[cg] = mfma16(a, bq, sc[cg]);
+          }
         }
       }
-      // lane holds tokens c0 + 4 grp + r of column n_col
-      float mx = -INFINITY;
+      // lane holds tokens c0 + 4 grp + r of column l16 of each group
+      bf16x4 pb[NCG];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (kFp8) sc[r] *= ksc;
-        if (4 * grp + r >= n_valid) sc[r] = -INFINITY;
-        mx = fmaxf(mx, sc[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = max_with_other_half(mx);
-      const float m_new = fmaxf(m_run, mx * cs);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
-      float rs = 0.f;
-      bf16x4 pb;
+      for (int cg = 0; cg < NCG; ++cg) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = exp2_fast(fmaf(sc[r], cs, -m_use));
-        rs += e;
-        if constexpr (kFp8)
-          pb[r] = (__bf16)(e * vsc);
-        else
-          pb[r] = (__bf16)e;
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (kFp8) sc[cg][r] *= ksc;
+          if (4 * grp + r >= n_valid) sc[cg][r] = -INFINITY;
+          mx = fmaxf(mx, sc[cg][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = max_with_other_half(mx);
+        const float m_new = fmaxf(m_run[cg], mx * cs);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run[cg] - m_use);
+        m_run[cg] = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2_fast(fmaf(sc[cg][r], cs, -m_use));
+          rs += e;
+          if constexpr (kFp8)
+            pb[cg][r] = (__bf16)(e * vsc);
+          else
+            pb[cg][r] = (__bf16)e;
+        }
+        l_run[cg] = fmaf(l_run[cg], alpha, rs);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[cg][mb] *= alpha;
       }
-      l_run = fmaf(l_run, alpha, rs);
       // ---- O^T += sum_hh V_hh^T . P^T_hh ; V^T slot s of lane group grp = token 4 grp + s
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
-#pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        const bf16x4 bp = (col_live && hh_col == hh) ? pb : bf16x4{};
         const int row = 4 * grp + tr_r;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int c = 2 * mb + (tr_q >> 1);
           const char* va =
               sV + (row * RC + hh * (D / 8) + (c ^ (tok_swz(row) & (D / 8 - 1)))) * 16 + (tr_q & 1) * 8;
-          acc[mb] = mfma16_k16(__builtin_bit_cast(bf16x4, lds_read_tr16(va)), bp, acc[mb]);
+          const bf16x4 vt = __builtin_bit_cast(bf16x4, lds_read_tr16(va));
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            const bf16x4 bp = (col_live[cg] && hh_col[cg] == hh) ? pb[cg] : bf16x4{};
+            acc[cg][mb] = mfma16_k16(vt, bp, acc[cg][mb]);
+          }
         }
       }
       // the next chunk's copies overwrite this chunk's LDS rows: all reads above
@@ -336,17 +369,20 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_split_kernel(Decod
     }
 
     // ---- partial of (workgroup, sequence b): normalised O and base-2 LSE per column
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot = sum_with_other_half(l_tot);
-    const bool ok = l_tot > 0.f;
-    const float inv = ok ? 1.f / l_tot : 0.f;
-    if (col_live) {
-      const int h = kv0 * G + n_col;
-      const size_t slot = (size_t)(wg + b) * p.A + h;
-      float* po = p.part_o + slot * D;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) *(f32x4*)(po + 16 * mb + 4 * grp) = acc[mb] * inv;
-      if (grp == 0) p.part_lse[slot] = ok ? m_run + log2_fast(l_tot) : -INFINITY;
+    for (int cg = 0; cg < NCG; ++cg) {
+      float l_tot = l_run[cg] + __shfl_xor(l_run[cg], 16);
+      l_tot = sum_with_other_half(l_tot);
+      const bool ok = l_tot > 0.f;
+      const float inv = ok ? 1.f / l_tot : 0.f;
+      if (col_live[cg]) {
+        const int h = kv0 * G + 16 * cg + l16;
+        const size_t slot = (size_t)(wg + b) * p.A + h;
+        float* po = p.part_o + slot * D;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) *(f32x4*)(po + 16 * mb + 4 * grp) = acc[cg][mb] * inv;
+        if (grp == 0) p.part_lse[slot] = ok ? m_run[cg] + log2_fast(l_tot) : -INFINITY;
+      }
     }
 
     remaining -= k_end - k;
@@ -431,56 +467,72 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   if (lane == 0) p.lse[(size_t)b * p.A + h] = ok ? (mx + log2_fast(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int D, int HPW, bool kFp8>
-hipError_t launch_split(const DecodeParams& p, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, HPW, kFp8>), dim3(p.n_wg, groups), dim3(64 * kWavesPerGroup), 0, stream,
-                     p);
-  return hipGetLastError();
-}
-
-template <int D, int HPW, bool kFp8>
+template <int D, int HPW, bool kFp8, int NCG, int WPG>
 int resident_groups(int cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, HPW, kFp8>, 64 * kWavesPerGroup,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, HPW, kFp8, NCG, WPG>, 64 * WPG,
                                                    0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   return cus * per_cu;
 }
 
-template <int D, bool kFp8>
-hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
-  if (p.n_chunks > 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus < 1)
-      cus = 1;
-    // FP8: two KV heads per wave when 2G <= 16 MFMA columns (longer rows per
-    // load); bf16: one, so that two LDS buffers per wave still leave room for
-    // two workgroups per CU (measured +1.7% over one buffer at two heads)
-    const bool two = kFp8 && p.G <= 8;
-    const int heads_per_group = (two ? 2 : 1) * kWavesPerGroup;
-    const int groups = (p.A_kv + heads_per_group - 1) / heads_per_group;
-    // one resident wave of workgroups covers the chunk list once
-    long long want = resident_groups<D, 1, kFp8>(cus);
-    if constexpr (kFp8) {
-      if (two) want = resident_groups<D, 2, kFp8>(cus);
-    }
-    want /= groups;
-    if (want < 1) want = 1;
-    if (want > kMaxDecodeGroups) want = kMaxDecodeGroups;
-    if (want > p.n_chunks) want = p.n_chunks;
-    p.n_wg = (int)want;
-    hipError_t e;
-    if constexpr (kFp8) {
-      e = two ? launch_split<D, 2, kFp8>(p, groups, stream) : launch_split<D, 1, kFp8>(p, groups, stream);
-    } else {
-      e = launch_split<D, 1, kFp8>(p, groups, stream);
-    }
-    if (e != hipSuccess) return e;
-  }
+// Split kernel for this (head dim, heads per wave, column groups, waves per
+// workgroup) choice: one resident wave of workgroups covers the chunk list
+// once; then the merge.
+template <int D, int HPW, bool kFp8, int NCG, int WPG>
+hipError_t launch_split(DecodeParams p, int cus, hipStream_t stream) {
+  const int heads_per_group = HPW * WPG;
+  const int groups = (p.A_kv + heads_per_group - 1) / heads_per_group;
+  long long want = resident_groups<D, HPW, kFp8, NCG, WPG>(cus) / groups;
+  if (want < 1) want = 1;
+  if (want > kMaxDecodeGroups) want = kMaxDecodeGroups;
+  if (want > p.n_chunks) want = p.n_chunks;
+  p.n_wg = (int)want;
+  hipLaunchKernelGGL((decode_split_kernel<D, HPW, kFp8, NCG, WPG>), dim3(p.n_wg, groups), dim3(64 * WPG), 0, stream,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.B * p.A), dim3(64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int HPW, bool kFp8, int NCG>
+hipError_t launch_wpg(const DecodeParams& p, int cus, hipStream_t stream) {
+  if (p.A_kv < kWavesPerGroup * HPW) return launch_split<D, HPW, kFp8, NCG, 1>(p, cus, stream);
+  return launch_split<D, HPW, kFp8, NCG, kWavesPerGroup>(p, cus, stream);
+}
+
+template <int D, int HPW, bool kFp8>
+hipError_t launch_ncg(const DecodeParams& p, int cus, hipStream_t stream) {
+  const int cols = HPW * p.G;  // query-head columns of one wave
+  if (cols <= 16) return launch_wpg<D, HPW, kFp8, 1>(p, cus, stream);
+  if constexpr (HPW == 1) {
+    if (cols <= 32) return launch_wpg<D, 1, kFp8, 2>(p, cus, stream);
+    if (cols <= 64) return launch_wpg<D, 1, kFp8, 4>(p, cus, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool kFp8>
+hipError_t launch_decode_d(DecodeParams p, hipStream_t stream) {
+  if (p.n_chunks <= 0) {
+    // no token at all: the merge alone writes O = 0 and LSE = -inf
+    p.n_wg = 1;
+    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.B * p.A), dim3(64), 0, stream, p);
+    return hipGetLastError();
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    cus = 1;
+  // FP8: two KV heads per wave when 2G <= 16 MFMA columns (longer rows per
+  // load); bf16: one, so that two LDS buffers per wave still leave room for
+  // two workgroups per CU (measured +1.7% over one buffer at two heads)
+  if constexpr (kFp8) {
+    if (p.G <= 8) return launch_ncg<D, 2, kFp8>(p, cus, stream);
+  }
+  return launch_ncg<D, 1, kFp8>(p, cus, stream);
 }
 
 // Static split workspace for callers that cannot allocate (attn_decode_paged_noalloc).

@@ -224,7 +224,8 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
  * ids: on one device the result does not depend on which physical pages the
  * block table names (bit for bit), while devices or partition modes with a
  * different CU count may round differently, within the stated tolerance.
- * Supported: bf16, d_h in {64, 128}, page_size a multiple of 16.
+ * Supported: bf16, d_h in {64, 128}, page_size a multiple of 16, A / A_kv <= 64
+ * (MQA included).
  */
 attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                               const int32_t *block_table, const int32_t *seq_lens,
@@ -247,7 +248,7 @@ attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_
  *
  * q, o, lse, block table, lengths and workspace are as in attn_decode_paged
  * (q, o bf16; same workspace size, from attn_decode_paged_workspace_bytes).
- * Supported: d_h in {64, 128}, page_size a multiple of 16.
+ * Supported: d_h in {64, 128}, page_size a multiple of 16, A / A_kv <= 64.
  */
 attn_status attn_decode_paged_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
                                   const float *k_scale, const float *v_scale,

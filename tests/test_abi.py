@@ -274,7 +274,7 @@ def test_attn_decode_paged_rejects_bad_arguments():
     assert dec(ps=8, max_pages=8) == 2             # page size must be a multiple of 16
     assert dec(d=96) == 2
     assert dec(dt=0) == 2                          # decode is bf16 only
-    assert dec(A=34, A_kv=2) == 2                  # more than 16 query heads per KV head
+    assert dec(A=130, A_kv=2) == 2                 # more than 64 query heads per KV head
     neg = np.array([-1, 4], np.int32)
     assert dec(lens=neg.ctypes.data_as(ctypes.c_void_p)) == 1
 

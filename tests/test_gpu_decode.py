@@ -54,6 +54,11 @@ DECODE_CASES = [
     ([2000, 1, 31], 32, 8, 128, 16),
     ([0, 0], 4, 1, 128, 16),
     ([4097], 8, 8, 64, 48),
+    ([700, 3, 2049], 32, 1, 128, 16),      # MQA: 32 query heads on one KV head (two column groups)
+    ([1500, 40], 64, 1, 128, 32),          # 64 query heads on one KV head (four column groups)
+    ([300, 999, 17], 24, 1, 64, 16),       # a ragged second column group
+    ([1200, 5, 640], 32, 2, 128, 16),      # two KV heads: one-wave workgroups
+    ([800, 1600], 24, 3, 128, 16),         # three KV heads
 ]
 
 
@@ -160,6 +165,22 @@ def test_decode_fp8_small(ea, orc, case):
     o_ref, l_ref = orc.decode_paged_fp8(p.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, p.block_table,
                                         p.seq_lens, scale=p.scale)
     gu.check(o, lse, o_ref, l_ref, "bf16", f"fp8 {case}")
+
+
+@pytest.mark.parametrize("A_kv", [1, 2])
+def test_decode_low_kv_heads_full_size_sampled(ea, orc, A_kv):
+    """The paged decode workload's lengths with A = 32 query heads on 1 or 2
+    KV heads (MQA-width groups, one-wave workgroups): sampled sequences
+    against the oracle, every output finite."""
+    lens = gen.make_config(4).seq_lens
+    _say("decode low kv heads", A_kv, int(lens.sum()), "tokens")
+    p = gen.make_paged(lens, 32, A_kv, 128, 16, dtype="bf16", seed=1020 + A_kv)
+    o, lse = run_decode(ea, p)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = np.array([b * 32 + h for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), 63) for h in (0, 17, 31)])
+    o_ref, l_ref = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="bf16",
+                                    scale=p.scale, rows=rows)
+    _say(gu.check(o.reshape(-1, 128)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", f"low kv {A_kv}"))
 
 
 def test_decode_fp8_full_size_sampled(ea, orc):

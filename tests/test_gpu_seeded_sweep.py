@@ -137,7 +137,7 @@ def test_sweep_decode(ea, orc, seed):
     lens = [int(x) for x in rng.integers(0, 3000, size=int(rng.integers(1, 9)))]
     d = int(rng.choice([64, 128]))
     A_kv = int(rng.choice([1, 2, 4, 8]))
-    A = A_kv * int(rng.choice([1, 2, 4, 8, 16]))
+    A = A_kv * int(rng.choice([1, 2, 4, 8, 16, 32] if A_kv <= 2 else [1, 2, 4, 8, 16]))
     ps = int(rng.choice([16, 32, 64]))
     _say("sweep decode", (seed, lens, A, A_kv, d, ps))
     p = gen.make_paged(lens, A, A_kv, d, ps, dtype="bf16", seed=6000 + seed, extra_pages=3)

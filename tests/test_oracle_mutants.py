@@ -84,6 +84,23 @@ MUTANTS = [
      "if (0)\n                            visible = 0;", 0),
 ]
 
+# Mutants of the package's Python side (oracle/__init__.py): the E4M3 code
+# values, the FP8 block scales, the window keep matrix.  (name, text to find,
+# replacement, which occurrence (0 = all))
+PY_MUTANTS = [
+    ("E4M3 exponent bias 8", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)", 0),
+    ("E4M3 sign bit ignored", "sign = np.where(c & 0x80, -1.0, 1.0)", "sign = 1.0", 0),
+    ("E4M3 subnormals without the 2^-6 factor", "(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7", 0),
+    ("FP8 prefill: 64-token query scale blocks", "np.repeat(qs, 128, axis=2)", "np.repeat(qs, 64, axis=2)", 0),
+    ("FP8 prefill: key scales ignored", "kv = fp8_e4m3_value(kc) * np.repeat(ks, 128, axis=2)[:, :, :S_k, None]",
+     "kv = fp8_e4m3_value(kc) * 1.0", 0),
+    ("FP8 decode: value scale of the key", "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale",
+     "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(k_scale", 0),
+    ("window: left edge off by one", "keep &= j >= i - left", "keep &= j > i - left", 0),
+    ("window: aligned top-left", "off = S_k - S_q\n    i = np.arange(S_q, dtype=np.int64)[:, None] + off",
+     "off = 0\n    i = np.arange(S_q, dtype=np.int64)[:, None] + off", 0),
+]
+
 BATTERY = r"""
 import sys
 sys.path.insert(0, {root!r})
@@ -130,3 +147,31 @@ def test_mutants_fail_a_pin(tmp_path):
     for n, (f, crashed) in results.items():
         print(f"{n:40s} caught by {len(f):2d} pins{' (crashed)' if crashed else ''}: {','.join(f)}")
     assert not undetected, f"mutants no pin catches: {undetected}"
+
+
+def test_python_mutants_fail_a_pin(tmp_path):
+    """The same for the package's Python side: each mutant is a copy of the
+    oracle package whose __init__.py carries the mistake, imported ahead of the
+    real one by the pin battery's child process."""
+    import shutil
+    src = open(os.path.join(os.path.dirname(oracle.SRC), "__init__.py")).read()
+    undetected = []
+    for n, (name, old, new, which) in enumerate([("control", "", "", -1)] + PY_MUTANTS):
+        root = tmp_path / f"p{n}"
+        pkg = root / "oracle"
+        pkg.mkdir(parents=True)
+        for f in ("attn_oracle.c", "blockwise.py", "liboracle.so"):
+            shutil.copy(os.path.join(os.path.dirname(oracle.SRC), f), pkg / f)
+        (pkg / "__init__.py").write_text(src if which == -1 else _mutate(src, old, new, which))
+        code = BATTERY.format(root=ROOT, lib=str(pkg / "liboracle.so")).replace(
+            "sys.path.insert(0, {!r})".format(ROOT), "sys.path.insert(0, {!r}); sys.path.insert(0, {!r})".format(
+                ROOT, str(root)))
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=str(root))
+        line = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED_PINS")]
+        failed = line[0].split(" ", 1)[1].split(",") if line and line[0].strip() != "FAILED_PINS" else []
+        print(f"{name:45s} caught by {len(failed):2d} pins{' (crashed)' if r.returncode else ''}: {','.join(failed)}")
+        if which == -1:
+            assert failed == [] and r.returncode == 0, (failed, r.stderr[-2000:])
+        elif not failed and r.returncode == 0:
+            undetected.append(name)
+    assert not undetected, f"Python mutants no pin catches: {undetected}"
