@@ -334,11 +334,11 @@ def grid_matches(kname: str, grid: int, pattern: str, wgs) -> bool:
 # kernel serves the MHA workload (16 query tiles x 32 heads x 4 batch rows), the
 # long GQA workload (128 x 32) and the sliding-window leg (256 x 32), so the
 # grid tells them apart.
-DENSE = "prefill_bf16_kernel<128, false, false, false, false, false>"
+DENSE = "prefill_bf16_kernel<128, false, false, false, false, false, false>"
 TRAFFIC_PARTS = {
     "prefill": (DENSE, 2048),
     "gqa_long": (DENSE, 4096),
-    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false>", None),
+    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false, false>", None),
     "decode_split": ("decode_split_kernel<128, 1, false>", None),
     "decode_merge": ("decode_merge_kernel", None),
     "bwd_dq": ("bwd_dq_kernel<128>", None),
@@ -348,22 +348,24 @@ TRACE_ROWS = [  # (label, kernel pattern, workgroups or None, algorithmic work p
     ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, (1.374389534720e11, "TFLOP/s")),
     ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, (2.199023255552e12, "TFLOP/s")),
     ("sliding-window GQA causal prefill S=32768, 4096-key window", DENSE, 8192, None),
-    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false>", None, None),
+    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false>", None, None),
     ("paged decode split (bf16 cache)", "decode_split_kernel<128, 1, false>", None, None),
     ("paged decode LSE merge (bf16 and FP8 legs)", "decode_merge_kernel<128>", None, None),
     ("paged decode split (FP8 cache)", "decode_split_kernel<128, 2, true>", None, None),
     ("backward dQ pass", "bwd_dq_kernel<128>", None, None),
     ("backward dK/dV pass", "bwd_dkdv_kernel<128,", None, None),
-    ("paged chunked prefill", "prefill_bf16_kernel<128, true, true, false, false, false>", None, None),
-    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false>", None, None),
-    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false>", None,
+    ("paged chunked prefill", "prefill_bf16_kernel<128, true, true, false, false, false, false>", None, None),
+    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false, false>", None, None),
+    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false>", None,
      None),
-    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false>", None, None),
+    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false>", None, None),
     ("block mask of an additive term", "block_keep_kernel", None, None),
-    ("FP8-QK causal prefill, MHA shape", "prefill_bf16_kernel<128, false, false, false, false, true>", 2048,
+    ("FP8-QK causal prefill, MHA shape", "prefill_bf16_kernel<128, false, false, false, false, true, false>", 2048,
      (1.374389534720e11, "TFLOP/s")),
-    ("FP8-QK causal prefill, long GQA shape", "prefill_bf16_kernel<128, false, false, false, false, true>", 4096,
+    ("FP8-QK causal prefill, long GQA shape", "prefill_bf16_kernel<128, false, false, false, false, true, false>", 4096,
      (2.199023255552e12, "TFLOP/s")),
+    ("paged chunked prefill over the E4M3 cache", "prefill_bf16_kernel<128, true, true, false, false, false, true>",
+     None, None),
 ]
 
 
@@ -550,7 +552,7 @@ def main():
                      "traffic": None if traffic_prefill is None else round(traffic_prefill),
                      "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
                      "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
-                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
+                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
                      "median_launch_ms": round(med["prefill"], 5), "min_launch_ms": round(mn["prefill"], 5),
                      "measured_ceiling": {"what": "torch.matmul bf16 8192^3 on the same GPU",
                                           "TFLOP/s": ceil["gemm_tflops"],
@@ -589,6 +591,7 @@ def main():
     out["backward"] = bench_backward(w, args.steps, args.warmup)
     out["window"] = bench_window(args.steps, args.warmup, stream)
     out["paged_prefill"] = bench_paged_prefill(w, args.steps, args.warmup)
+    out["paged_prefill_fp8"] = bench_paged_prefill_fp8(w, args.steps, args.warmup)
     out["block_sparse"] = bench_block_sparse(w, args.steps, args.warmup)
     out["dense_mask"] = bench_dense_mask(w, args.steps, args.warmup)
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
@@ -999,6 +1002,43 @@ def bench_paged_prefill(w, steps: int, warmup: int) -> dict:
             "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5), "flops": flops,
             "workload": f"{n} sequences of the paged decode cache (A=32 A_kv=8 d=128 page 16, lengths "
                         f"~U{{512..32768}}), each with its last {PAGED_CHUNK} tokens as the query chunk"}
+
+
+def bench_paged_prefill_fp8(w, steps: int, warmup: int) -> dict:
+    """The chunked-prefill leg over the E4M3 form of the decode workload's cache
+    (per-(page, KV head) scales; the same lengths, block table and 256-token
+    chunks, seeded queries): the FP8 bytes are widened to bf16 on the way into
+    LDS.  FLOPs as the bf16 leg."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p4, stream = w["p4"], w["stream"]
+    n = p4.B
+    q_lens = np.full(n, PAGED_CHUNK, np.int32)
+    t0 = time.time()
+    pf, qh, cu = gen.make_paged_prefill_fp8(p4.seq_lens, q_lens, p4.A, p4.A_kv, p4.d, p4.page_size, seed=1012)
+    log(f"fp8 paged prefill inputs ready ({time.time() - t0:.1f}s)")
+    p = pf.base
+    q = to_dev(qh, "bf16")
+    kc, vc = torch.from_numpy(pf.k_codes).cuda(), torch.from_numpy(pf.v_codes).cuda()
+    ks, vs = torch.from_numpy(pf.k_scale).cuda(), torch.from_numpy(pf.v_scale).cuda()
+    bt, sl, cud = to_dev(p.block_table, "i32"), to_dev(p.seq_lens, "i32"), to_dev(cu, "i32")
+    o = torch.empty_like(q)
+    lse = torch.empty((p.A, int(cu[-1])), dtype=torch.float32, device="cuda")
+    ms = _event_times(lambda: ea.attn_prefill_paged_fp8(q, kc, vc, ks, vs, bt, sl, p.seq_lens, cud, cu, o, lse,
+                                                        scale=p.scale, causal=True, stream=stream),
+                      steps, warmup, stream)
+    L = p.seq_lens.astype(np.int64)
+    ql = q_lens.astype(np.int64)
+    pairs = int(np.sum(ql * (L - ql) + ql * (ql + 1) // 2))
+    flops = 4.0 * p.d * p.A * pairs
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    del q, kc, vc, ks, vs, o, lse
+    torch.cuda.empty_cache()
+    return {"metric": "paged chunked prefill over an E4M3 cache TFLOP/s (causal pairs)", "value": round(tf, 2),
+            "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "avg_ms": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5), "flops": flops,
+            "workload": f"{n} sequences of the paged decode workload's E4M3 cache, last {PAGED_CHUNK} tokens each"}
 
 
 def measured_ceilings(stream) -> dict:

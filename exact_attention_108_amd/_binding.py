@@ -60,6 +60,8 @@ _lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.attn_prefill_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                     _f, _i, _WP, _i, _vp]
 _lib.attn_prefill_paged.restype = _i
+_lib.attn_prefill_paged_fp8.argtypes = [_vp] * 10 + [_i, _vp, _vp] + [_i] * 7 + [_f, _i, _WP, _vp]
+_lib.attn_prefill_paged_fp8.restype = _i
 _lib.attn_bwd_workspace_bytes.restype = _sz
 _lib.attn_decode_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                        _f, _vp, _sz, _vp]
@@ -90,7 +92,7 @@ def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
             "attn_decode_paged_workspace_bytes",
-            "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
+            "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8", "attn_decode_paged_fp8",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
 
 
@@ -493,6 +495,43 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host
                                  float(scale), int(bool(causal)), _window(window), _dtype_code(q),
                                  _stream(stream, dev))
     _check(st, "attn_prefill_paged")
+
+
+def attn_prefill_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host,
+                           cu_seqlens_q, cu_seqlens_q_host, o, lse, *, scale: float, causal: bool = True, window=None,
+                           stream=None):
+    """attn_prefill_paged over E4M3 caches: caches uint8 [num_pages, page_size, A_kv, d] of code bytes,
+    k_scale/v_scale fp32 [num_pages, A_kv]; q/o bf16 [A,T_q,d]; the rest as attn_prefill_paged."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
+    A, T_q, d = q.shape
+    num_pages, page_size, A_kv, dk = k_cache.shape
+    if dk != d or o.shape != q.shape or lse.shape != (A, T_q) or lse.dtype != torch.float32:
+        raise ValueError("shape mismatch")
+    if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
+        raise ValueError("q and o must be bf16")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches are passed as uint8 tensors of E4M3 bytes")
+    for sc in (k_scale, v_scale):
+        if sc.dtype != torch.float32 or sc.shape != (num_pages, A_kv):
+            raise ValueError("scales must be fp32 [num_pages, A_kv]")
+    cu_host = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
+    n_seq = cu_host.size - 1
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if sl.shape != (n_seq,) or seq_lens.dtype != torch.int32 or seq_lens.shape != (n_seq,):
+        raise ValueError("seq_lens must be int32 [n_seq]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_q.numel() != cu_host.size:
+        raise ValueError("cu_seqlens_q must be int32 [n_seq + 1]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != n_seq:
+        raise ValueError("block_table must be int32 [n_seq, max_pages]")
+    dev = _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, cu_seqlens_q, o, lse)
+    st = _lib.attn_prefill_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                     _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp), _ptr(cu_seqlens_q),
+                                     cu_host.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), n_seq, T_q, A, A_kv,
+                                     d, block_table.shape[1], num_pages, float(scale), int(bool(causal)),
+                                     _window(window), _stream(stream, dev))
+    _check(st, "attn_prefill_paged_fp8")
 
 
 def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse,

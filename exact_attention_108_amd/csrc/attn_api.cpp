@@ -336,13 +336,15 @@ ATTN_EXPORT attn_status attn_decode_paged_noalloc(const void* q, const void* k_c
                             A_kv, d_h, max_pages, scale, ws, stream);
 }
 
-ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
-                                           const int32_t* block_table, const int32_t* seq_lens,
-                                           const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
-                                           const int32_t* cu_seqlens_q_host, int page_size, void* o, float* lse,
-                                           int n_seq, int total_q, int A, int A_kv, int d_h, int max_pages,
-                                           int num_pages, float scale, int causal, const attn_window* window,
-                                           attn_dtype dtype, void* stream) {
+namespace {
+
+// attn_prefill_paged and its E4M3-cache form: validation, planning, launch
+attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, bool fp8, const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_q_host, int page_size, void* o, float* lse, int n_seq,
+                               int total_q, int A, int A_kv, int d_h, int max_pages, int num_pages, float scale,
+                               int causal, const attn_window* window, attn_dtype dtype, void* stream) {
   if (n_seq < 0 || total_q < 0 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
   if (page_size < 1 || max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
   if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
@@ -358,9 +360,13 @@ ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, c
   }
   if (total_q > 0 && (!q || !o || !lse)) return ATTN_ERR_INVAL;
   if (total_kv > 0 && (!k_cache || !v_cache || !block_table || num_pages < 1)) return ATTN_ERR_INVAL;
-  for (const void* t : {q, k_cache, v_cache, (const void*)o})
+  if (fp8 && total_kv > 0 && (!k_scale || !v_scale)) return ATTN_ERR_INVAL;
+  for (const void* t : {q, (const void*)o})
     if (!aligned(t, 16)) return ATTN_ERR_INVAL;
-  for (const void* t : {(const void*)lse, (const void*)seq_lens, (const void*)block_table, (const void*)cu_seqlens_q})
+  for (const void* t : {k_cache, v_cache})
+    if (!aligned(t, fp8 ? 8 : 16)) return ATTN_ERR_INVAL;
+  for (const void* t : {(const void*)lse, (const void*)seq_lens, (const void*)block_table, (const void*)cu_seqlens_q,
+                        (const void*)k_scale, (const void*)v_scale})
     if (!aligned(t, 4)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
   const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
@@ -392,11 +398,41 @@ ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, c
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.max_pages = max_pages;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
   p.page_shift = shift;
   attn::plan_varlen_order(p);
-  return launch_status(attn::launch_prefill_paged_bf16(p, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  return launch_status(fp8 ? attn::launch_prefill_paged_fp8(p, st) : attn::launch_prefill_paged_bf16(p, st));
+}
+
+}  // namespace
+
+ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table, const int32_t* seq_lens,
+                                           const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_q_host, int page_size, void* o, float* lse,
+                                           int n_seq, int total_q, int A, int A_kv, int d_h, int max_pages,
+                                           int num_pages, float scale, int causal, const attn_window* window,
+                                           attn_dtype dtype, void* stream) {
+  return prefill_paged_call(q, k_cache, v_cache, nullptr, nullptr, false, block_table, seq_lens, seq_lens_host,
+                            cu_seqlens_q, cu_seqlens_q_host, page_size, o, lse, n_seq, total_q, A, A_kv, d_h,
+                            max_pages, num_pages, scale, causal, window, dtype, stream);
+}
+
+ATTN_EXPORT attn_status attn_prefill_paged_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                               const float* k_scale, const float* v_scale,
+                                               const int32_t* block_table, const int32_t* seq_lens,
+                                               const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
+                                               const int32_t* cu_seqlens_q_host, int page_size, void* o, float* lse,
+                                               int n_seq, int total_q, int A, int A_kv, int d_h, int max_pages,
+                                               int num_pages, float scale, int causal, const attn_window* window,
+                                               void* stream) {
+  return prefill_paged_call(q, k_cache, v_cache, k_scale, v_scale, true, block_table, seq_lens, seq_lens_host,
+                            cu_seqlens_q, cu_seqlens_q_host, page_size, o, lse, n_seq, total_q, A, A_kv, d_h,
+                            max_pages, num_pages, scale, causal, window, ATTN_BF16, stream);
 }
 
 namespace {

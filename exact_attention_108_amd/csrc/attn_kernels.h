@@ -55,6 +55,8 @@ struct FwdParams {
   // q_scale [B, A, ceil(S_q / 128)], k_scale [B, A_kv, ceil(S_k / 128)]
   const float* q_scale;
   const float* k_scale;
+  // E4M3 paged cache (paged prefill): k_scale, v_scale [num_pages, A_kv]
+  const float* v_scale;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin
@@ -99,6 +101,9 @@ hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream);
 // kFp8MaxKeys): the QK^T products on the FP8 matrix cores
 constexpr int kFp8MaxKeys = 262144;
 hipError_t launch_prefill_fp8(const FwdParams& p, hipStream_t stream);
+// bf16 prefill of packed query chunks over an E4M3 paged cache with
+// per-(page, KV head) scales (same page-size rules as the bf16 cache)
+hipError_t launch_prefill_paged_fp8(const FwdParams& p, hipStream_t stream);
 // fp32 prefill (1 <= d <= 128).
 hipError_t launch_prefill_f32(const FwdParams& p, bool varlen, hipStream_t stream);
 // block_keep[b][h][qb][kb] = whether some bias entry of the 128 x 128 block is

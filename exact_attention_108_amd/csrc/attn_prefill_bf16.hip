@@ -80,9 +80,17 @@ constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias) ? 3 : 2;
 // tokens (FwdParams::q_scale / k_scale); S^T = K . Q^T runs on the FP8 matrix
 // cores (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block exponents) and is
 // scaled by q_scale * k_scale in fp32; values stay bf16 (dense, d = 128).
-template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false, bool kFp8 = false>
+// kCache8 (paged only): the cache holds OCP E4M3 codes with one fp32 scale
+// per (page, KV head) (FwdParams::k_scale / v_scale, [num_pages, A_kv]).  The
+// tile parts are loaded into registers, widened exactly to bf16 and written
+// where the bf16 copy would land; a key's scale multiplies its scores, a
+// value's scale its probabilities before the PV product (the normaliser sums
+// the unscaled ones).
+template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false, bool kFp8 = false,
+          bool kCache8 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias>, kWavesPerSimd<D, kPaged, kBias>))) void prefill_bf16_kernel(FwdParams p) {
   static_assert(!kFp8 || (D == 128 && !kVarlen && !kPaged && !kBlocks && !kBias), "fp8: dense, d = 128");
+  static_assert(!kCache8 || kPaged, "E4M3 caches: paged prefill only");
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
   constexpr int MB = D / 32;               // 32-row blocks of O^T
@@ -105,10 +113,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   __shared__ int sCnt[kBlocks ? kWaves : 1];
   // fp8: the key scales of the 128-key blocks of this workgroup's key range
   __shared__ float sKs[kFp8 ? kFp8MaxKeys / 128 : 1];
+  // E4M3 cache: the scales of the parts of each K and V buffer's tile
+  __shared__ f32x4 sKsc[kCache8 ? 2 : 1];
+  __shared__ f32x4 sVsc[kCache8 ? 2 : 1];
 
   RowBlock rb;
   if constexpr (kPaged) {
-    if (!setup_paged<kRows>(p, D * 2, rb)) return;
+    if (!setup_paged<kRows>(p, D * 2, rb, kCache8 ? D : 0)) return;
   } else if constexpr (kVarlen) {
     if (!setup_varlen<kRows>(p, D * 2, rb)) return;
   } else {
@@ -323,6 +334,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     lds_copy16_buf(part_rsrc(gbase, t, i, page), poff,
                    lds_base + dst + (uint32_t)(i * RPC * D * 2) + (uint32_t)wave_u * 1024u);
   };
+  // E4M3 cache: this lane's 8 code bytes of part i of tile t (the logical
+  // chunk cc of its row, as the bf16 copy moves), zero past S_k; widened to
+  // bf16 and stored at the slot that copy would fill
+  [[maybe_unused]] const uint32_t kv_stride8 = (uint32_t)(p.A_kv * D);
+  [[maybe_unused]] auto load_part8 = [&](const char* gbase8, int t, int i, int page) -> uint2 {
+    const int row0 = phys(t) * kBc + i * RPC;
+    const int in_page = row0 & ((1 << p.page_shift) - 1);
+    const char* src = gbase8 + ((size_t)page << p.page_shift | (size_t)in_page) * kv_stride8 +
+                      (size_t)rowc * kv_stride8 + (size_t)cc * 8;
+    return row0 + rowc < S_k ? *(const uint2*)src : uint2{0u, 0u};
+  };
+  [[maybe_unused]] auto store_part8 = [&](uint2 w, uint32_t dst, int i) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false);
+    const b2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true);
+    const b2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false);
+    const b2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true);
+    *(bf16x8*)((char*)smem + dst + i * RPC * D * 2 + wave * 1024 + lane * 16) =
+        bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  };
+  // scale of (page, this KV head) from lane `i` (< LD_PER_T) of a page vector
+  [[maybe_unused]] const int hk_c = rb.h / p.G;
+  [[maybe_unused]] auto scale_of = [&](const float* tab, int page) -> float {
+    return tab[(size_t)page * p.A_kv + hk_c];
+  };
   // pages of the parts of the K tile the current iteration copies (the next
   // iteration copies V of that same tile), and, in lanes, of the next
   // iteration's K tile
@@ -449,6 +485,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       if (p == NQ / 2) issue(1);
     }
   };
+  // E4M3 cache: multiply the scores of the tile in K buffer kbuf by their
+  // keys' scales (element (kb, r) is key 32 kb + 8 (r / 4) + 4 g + r % 4 of the
+  // tile, in part (32 kb + 8 (r / 4)) / RPC)
+  auto part_of = [](int kb, int r) -> int { return (32 * kb + 8 * (r >> 2)) / RPC; };
+  auto kscale = [&](f32x16 (&s)[2], int kbuf) {
+    if constexpr (kCache8) {
+      const f32x4 ksc = sKsc[kbuf];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] *= ksc[part_of(kb, r)];
+      }
+    }
+  };
   // per-element predicate of tile t (keys past S_k, the window's edges -- the
   // causal diagonal is its right edge --, the key keep-mask): dead scores
   // become -inf
@@ -532,8 +582,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // LDS buffer VBUF; the normaliser sums p in fp32, the product takes p
   // rounded to bf16.  PV steps (kb, h, mb) with mb innermost: MB independent
   // accumulator chains.  `issue` is called at two points.
-  auto exps = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float csx) -> float {
+  auto exps = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float csx, int vbuf) -> float {
     const float neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    [[maybe_unused]] f32x4 vsc;
+    if constexpr (kCache8) vsc = sVsc[vbuf];
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -547,10 +599,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         rs[1] += e1;
         rs[2] += e2;
         rs[3] += e3;
-        pb[kb][r >> 3][(r & 7) + 0] = (__bf16)e0;
-        pb[kb][r >> 3][(r & 7) + 1] = (__bf16)e1;
-        pb[kb][r >> 3][(r & 7) + 2] = (__bf16)e2;
-        pb[kb][r >> 3][(r & 7) + 3] = (__bf16)e3;
+        if constexpr (kCache8) {
+          const float v = vsc[part_of(kb, r)];
+          pb[kb][r >> 3][(r & 7) + 0] = (__bf16)(e0 * v);
+          pb[kb][r >> 3][(r & 7) + 1] = (__bf16)(e1 * v);
+          pb[kb][r >> 3][(r & 7) + 2] = (__bf16)(e2 * v);
+          pb[kb][r >> 3][(r & 7) + 3] = (__bf16)(e3 * v);
+        } else {
+          pb[kb][r >> 3][(r & 7) + 0] = (__bf16)e0;
+          pb[kb][r >> 3][(r & 7) + 1] = (__bf16)e1;
+          pb[kb][r >> 3][(r & 7) + 2] = (__bf16)e2;
+          pb[kb][r >> 3][(r & 7) + 3] = (__bf16)e3;
+        }
       }
     }
     return (rs[0] + rs[1]) + (rs[2] + rs[3]);
@@ -558,7 +618,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   auto softmax_pv = [&](auto vbuf_tag, const f32x16 (&s)[2], float csx, auto&& issue) {
     constexpr int VB = VB0 + decltype(vbuf_tag)::value * TILE_BYTES;
     bf16x8 pb[2][2];
-    l_run += exps(s, pb, csx);
+    l_run += exps(s, pb, csx, decltype(vbuf_tag)::value);
     constexpr int NV = 4 * MB;
     bf16x8 va[NV];
     auto vread = [&](int q) {  // step q: mb = q % MB, (kb, h) = q / MB
@@ -584,7 +644,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   float mx_cur = -INFINITY;
   float cs_cur = cs;  // the score scale of the tile in s_cur (fp8: per tile)
   if (n_tiles > 0) {
-    if constexpr (kPaged) {
+    if constexpr (kPaged && kCache8) {
+      const int t1 = min(1, n_tiles - 1);
+      pg_n = pages_vec(min(2, n_tiles - 1));
+      uint2 k0r[LD_PER_T], v0r[LD_PER_T], k1r[LD_PER_T];
+      f32x4 ks0, vs0, ks1;
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        const int p0 = page_of(0, i);
+        pg_k[i] = page_of(t1, i);
+        k0r[i] = load_part8(rb.k, 0, i, p0);
+        v0r[i] = load_part8(rb.v, 0, i, p0);
+        k1r[i] = load_part8(rb.k, t1, i, pg_k[i]);
+        ks0[i] = scale_of(p.k_scale, p0);
+        vs0[i] = scale_of(p.v_scale, p0);
+        ks1[i] = scale_of(p.k_scale, pg_k[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        store_part8(k0r[i], 0, i);
+        store_part8(v0r[i], VB0, i);
+        store_part8(k1r[i], KTILE_BYTES, i);
+      }
+      if (tid == 0) {
+        sKsc[0] = ks0;
+        sVsc[0] = vs0;
+        sKsc[1] = ks1;
+      }
+    } else if constexpr (kPaged) {
       const int t1 = min(1, n_tiles - 1);
       pg_n = pages_vec(min(2, n_tiles - 1));
 #pragma unroll
@@ -612,6 +699,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     lds_copy_wait_all();
     __syncthreads();
     qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
+    kscale(s_cur, 0);
     if (n_mid == 0) mask(s_cur, 0, m0);
     cs_cur = cs_of(0);
     mx_cur = rowmax(s_cur, cs_cur);
@@ -656,10 +744,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       pg_n = pages_vec(min(j + 3, n_tiles - 1));
     }
     if constexpr (MASKED) copy_keep(j + 2);
+    // E4M3 cache: the parts of K tile tk and V tile tv, and their scales, are
+    // loaded into registers now and widened into the LDS buffers at the end
+    // of the iteration (the buffers iteration j-1 finished with)
+    [[maybe_unused]] uint2 kr8[LD_PER_T], vr8[LD_PER_T];
+    [[maybe_unused]] float ks8 = 0.f, vs8 = 0.f;
+    if constexpr (kCache8) {
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        kr8[i] = load_part8(rb.k, tk, i, pg_k[i]);
+        vr8[i] = load_part8(rb.v, tv, i, pg_v[i]);
+      }
+      // lane i < LD_PER_T: the scales of part i
+      int pk = pg_k[0], pv = pg_v[0];
+#pragma unroll
+      for (int i = 1; i < LD_PER_T; ++i) {
+        if (lane == i) {
+          pk = pg_k[i];
+          pv = pg_v[i];
+        }
+      }
+      ks8 = scale_of(p.k_scale, pk);
+      vs8 = scale_of(p.v_scale, pv);
+    }
     auto issue = [&](int at) {
 #pragma unroll
       for (int i = 0; i < LD_PER_T; ++i) {
-        if constexpr (kPaged) {
+        if constexpr (kCache8) {
+          (void)at;
+        } else if constexpr (kPaged) {
           if (i * 4 / LD_PER_T == at) {
             copy_part_paged(rb.k, tk, BUF * KTILE_BYTES, i, pg_k[i]);
             copy_part_paged(rb.v, tv, VB0 + (BUF ^ 1) * TILE_BYTES, i, pg_v[i]);
@@ -675,6 +788,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     interleave_hint();
     if constexpr (!MASKED) {
       qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
+      kscale(s_next, BUF ^ 1);
       softmax_pv(buf_tag, s_cur, cs_cur, issue);
       cs_cur = cs_of(j + 1);
       mx_cur = rowmax(s_next, cs_cur);
@@ -687,6 +801,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       f32x4 m_next[2][4];
       if (has_next) {
         qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
+        kscale(s_next, BUF ^ 1);
       } else {
         issue(0);
         issue(1);
@@ -704,6 +819,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         mx_cur = rowmax(s_next, cs_cur);
         s_cur[0] = s_next[0];
         s_cur[1] = s_next[1];
+      }
+    }
+    if constexpr (kCache8) {
+#pragma unroll
+      for (int i = 0; i < LD_PER_T; ++i) {
+        store_part8(kr8[i], BUF * KTILE_BYTES, i);
+        store_part8(vr8[i], VB0 + (BUF ^ 1) * TILE_BYTES, i);
+      }
+      if (tid < LD_PER_T) {
+        ((float*)&sKsc[BUF])[tid] = ks8;
+        ((float*)&sVsc[BUF ^ 1])[tid] = vs8;
       }
     }
   };
@@ -820,6 +946,21 @@ hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_bf16_kernel<128, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else if (p.d == 64) {
     hipLaunchKernelGGL((prefill_bf16_kernel<64, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_paged_fp8(const FwdParams& p, hipStream_t stream) {
+  const int grid = p.total_tiles * p.A;
+  if (grid <= 0) return hipSuccess;
+  if (p.d == 128) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, true, false, false, false, true>), dim3(grid), dim3(kThreads),
+                       0, stream, p);
+  } else if (p.d == 64) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, true, true, false, false, false, true>), dim3(grid), dim3(kThreads),
+                       0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

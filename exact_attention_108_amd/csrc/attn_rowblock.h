@@ -140,6 +140,9 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
   r.S_q = len;
   r.S_k = len;
   r.q0 = t_u * kRows;
+  r.b = 0;
+  r.h = h;
+  r.qt = t_u;
   if (seq_out) *seq_out = seq;
   if (head_out) *head_out = h;
   return true;
@@ -149,12 +152,15 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
 // one (cu_seqlens over the chunks); sequence s's keys are its seq_lens[s]
 // cached tokens, the chunk being the last of them (bottom-right alignment).
 template <int kRows>
-__device__ __forceinline__ bool setup_paged(const FwdParams& p, int row_bytes, RowBlock& r) {
+__device__ __forceinline__ bool setup_paged(const FwdParams& p, int row_bytes, RowBlock& r, int kv_row_bytes = 0) {
+  // kv_row_bytes: bytes of one KV head's row in the cache when they differ
+  // from the queries' (an E4M3 cache beside bf16 queries); 0 = row_bytes
+  if (kv_row_bytes == 0) kv_row_bytes = row_bytes;
   int seq = 0, h = 0;
   if (!setup_varlen<kRows>(p, row_bytes, r, &seq, &h)) return false;
   const int hk = h / p.G;
-  r.k = (const char*)p.k + (size_t)hk * row_bytes;
-  r.v = (const char*)p.v + (size_t)hk * row_bytes;
+  r.k = (const char*)p.k + (size_t)hk * kv_row_bytes;
+  r.v = (const char*)p.v + (size_t)hk * kv_row_bytes;
   r.bt = p.block_table + (size_t)seq * p.max_pages;
   r.S_k = p.seq_lens[seq];
   r.q_keep = nullptr;

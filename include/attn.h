@@ -321,6 +321,29 @@ attn_status attn_prefill_paged(const void *q, const void *k_cache, const void *v
                                attn_dtype dtype, void *stream);
 
 /*
+ * attn_prefill_paged over FP8 caches (page "Attention Kernel", sections "Paged
+ * 与 ragged KV" and "正确性契约": the cache dtype and its scale metadata are
+ * part of the contract; page "Attention 算子加速史", section 3.3).  The caches
+ * hold one OCP E4M3 byte per element with the layout [num_pages, page_size,
+ * A_kv, d_h] and the scales of attn_decode_paged_fp8 (element value = byte
+ * value * scale[page, kv head]):
+ *
+ *   k_scale, v_scale : device fp32 [num_pages, A_kv], finite
+ *
+ * Every other argument, the result's definition and the support are those of
+ * attn_prefill_paged (q, o bf16); the caches must be 8-byte aligned.  The
+ * bytes are widened exactly to bf16; key scales multiply scores, value scales
+ * the probabilities before the PV product.
+ */
+attn_status attn_prefill_paged_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                   const float *k_scale, const float *v_scale, const int32_t *block_table,
+                                   const int32_t *seq_lens, const int32_t *seq_lens_host,
+                                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_q_host, int page_size,
+                                   void *o, float *lse, int n_seq, int total_q, int A, int A_kv, int d_h,
+                                   int max_pages, int num_pages, float scale, int causal,
+                                   const attn_window *window, void *stream);
+
+/*
  * Backward of attn_fwd (dense batch): dQ, dK, dV of O = softmax(Q K^T *
  * scale + M) V for an incoming dO, with the probabilities recomputed tile by
  * tile from Q, K and the forward's LSE instead of being stored (page

@@ -293,6 +293,19 @@ class Oracle:
         return self.attn_fwd(qv, kv, vv, dtype="f64", scale=scale, causal=causal, q_keep=q_keep, k_keep=k_keep,
                              m_keep=m_keep, rows=rows)
 
+    def prefill_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, cu_seqlens_q, *,
+                          scale, causal=True, window=None, rows=None):
+        """prefill_paged over FP8 caches: E4M3 codes [P, page_size, A_kv, d]
+        with per-(page, KV head) scales [P, A_kv]; q bf16 bits [A, T_q, d].  The
+        cache values code value * scale are formed in fp64 and the chunks run
+        through prefill_paged."""
+        kc = fp8_e4m3_value(k_codes) * np.asarray(k_scale, np.float64)[:, None, :, None]
+        vc = fp8_e4m3_value(v_codes) * np.asarray(v_scale, np.float64)[:, None, :, None]
+        qb = self._arr(q, "bf16").astype(np.uint32) << np.uint32(16)   # bf16 bits -> fp32 bits
+        qf = qb.view(np.float32).astype(np.float64)
+        return self.prefill_paged(qf, kc, vc, block_table, seq_lens, cu_seqlens_q, dtype="f64", scale=scale,
+                                  causal=causal, window=window, rows=rows)
+
     def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
                          seqs=None):
         """Paged decode over FP8 caches (E4M3 codes [P, page_size, A_kv, d] with

@@ -444,6 +444,18 @@ def make_dense_fp8(B, A, A_kv, S_q, S_k, d, *, causal=False, seed=0, v_kind="nor
     return DenseFp8(B, A, A_kv, S_q, S_k, d, causal, float(np.float32(1.0 / math.sqrt(d))), qc, kc, qs, ks, v)
 
 
+def make_paged_prefill_fp8(lens, q_lens, A, A_kv, d, page_size, *, seed=0, extra_pages=0):
+    """Query chunks over FP8 caches: make_paged_fp8's caches, scales, block
+    table and lengths (``lens`` = KV length per sequence, chunk included) plus
+    packed bf16 chunk queries q [A, sum(q_lens), d] and cu_seqlens_q."""
+    pf = make_paged_fp8(lens, A, A_kv, d, page_size, seed=seed, extra_pages=extra_pages)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    cu = np.zeros(q_lens.size + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    q = draw((A, int(cu[-1]), d), seed, S_DOUT + 1, "normal", "bf16")
+    return pf, q, cu
+
+
 # --- the five named workloads -------------------------------------------------
 
 CONFIG_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}

@@ -979,6 +979,42 @@ def pin_prefill_paged_chunk_tail(orc):
             assert np.array_equal(lse[:, cu[s]:cu[s + 1]], l2[0]), (s, causal, window)
 
 
+def pin_prefill_paged_fp8(orc):
+    """Over FP8 caches: one-row chunks equal the FP8 paged decode (bit for
+    bit), and a chunk of 5 rows matches math.fsum over the dequantised keys
+    (code value x its page's scale) at the bottom-right positions."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(72)
+    ps, A, A_kv, d = 4, 4, 2, 3
+    lens = np.array([9, 6, 1], np.int32)
+    bt = np.array([[3, 0, 5], [1, 4, -1], [2, -1, -1]], np.int32)
+    kc = rng.integers(0, 0x7F, size=(6, ps, A_kv, d)).astype(np.uint8) | (rng.integers(0, 2, size=(6, ps, A_kv, d)) * 0x80).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, size=(6, ps, A_kv, d)).astype(np.uint8)
+    ksc = rng.uniform(0.001, 0.01, size=(6, A_kv)).astype(np.float32)
+    vsc = rng.uniform(0.001, 0.01, size=(6, A_kv)).astype(np.float32)
+    q1 = gen.f32_to_bf16_bits(rng.standard_normal((A, 3, d)).astype(np.float32))
+    cu1 = np.array([0, 1, 2, 3], np.int32)
+    o, lse = orc.prefill_paged_fp8(q1, kc, vc, ksc, vsc, bt, lens, cu1, scale=0.75)
+    od, ld = orc.decode_paged_fp8(np.ascontiguousarray(q1.transpose(1, 0, 2)), kc, vc, ksc, vsc, bt, lens,
+                                  scale=0.75)
+    assert np.array_equal(o.transpose(1, 0, 2), od) and np.array_equal(lse.T, ld)
+    q5 = gen.f32_to_bf16_bits(rng.standard_normal((A, 5, d)).astype(np.float32))
+    cu5 = np.array([0, 5, 5, 5], np.int32)
+    o, lse = orc.prefill_paged_fp8(q5, kc, vc, ksc, vsc, bt, lens, cu5, scale=0.75)
+    qv = gen.bf16_bits_to_f32(q5).astype(np.float64)
+    G = A // A_kv
+    for h in range(A):
+        hk = h // G
+        keys = [[float(x) * float(ksc[bt[0, t // ps], hk]) for x in oracle_pkg.fp8_e4m3_value(kc[bt[0, t // ps], t % ps, hk])]
+                for t in range(9)]
+        vals = [[float(x) * float(vsc[bt[0, t // ps], hk]) for x in oracle_pkg.fp8_e4m3_value(vc[bt[0, t // ps], t % ps, hk])]
+                for t in range(9)]
+        for i in range(5):
+            pos = 9 - 5 + i
+            want, wl = _brute([float(x) for x in qv[h, i]], keys, vals, 0.75, [t <= pos for t in range(9)])
+            assert np.allclose(o[h, i], want, rtol=0, atol=1e-13) and abs(lse[h, i] - wl) < 1e-13, (h, i)
+
+
 # ---- gradient of the packed varlen prefill, and of block / additive masks
 
 def pin_bwd_varlen_equals_separate(orc):

@@ -21,7 +21,8 @@ def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_noalloc",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
-                                         "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_decode_paged_fp8",
+                                         "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8",
+                                         "attn_decode_paged_fp8",
                                          "attn_block_keep_from_bias", "attn_status_string",
                                          "attn_abi_version"])
 
@@ -393,6 +394,24 @@ def test_attn_prefill_paged_rejects_bad_arguments():
     assert call(dt=0) == UNSUP
     zero = np.array([0, 0, 0], np.int32)
     assert call(cu=zero, T=0) == OK                              # no query rows: nothing to launch
+
+
+def test_attn_prefill_paged_fp8_rejects_bad_arguments():
+    lib = _lib()
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_prefill_paged_fp8.argtypes = [vp] * 10 + [i, vp, vp] + [i] * 7 + [f, i, vp, vp]
+    lib.attn_prefill_paged_fp8.restype = i
+    INVAL, UNSUP = 1, 2
+    cu = np.array([0, 5, 6], np.int32)
+    lens = np.array([40, 9], np.int32)
+
+    def call(ks=P, vs=P, kc=P, ps=16, d=128):
+        return lib.attn_prefill_paged_fp8(P, kc, P, ks, vs, P, P, lens.ctypes.data_as(vp), P, cu.ctypes.data_as(vp),
+                                          ps, P, P, cu.size - 1, 6, 8, 2, d, 3, 6, 0.1, 1, None, None)
+    assert call(ks=None) == INVAL and call(vs=None) == INVAL
+    assert call(kc=ctypes.c_void_p(4096 + 4)) == INVAL              # 8-byte aligned caches
+    assert call(ks=ctypes.c_void_p(4096 + 2)) == INVAL
+    assert call(ps=24) == UNSUP and call(d=96) == UNSUP
 
 
 def test_attn_block_keep_from_bias_rejects_bad_arguments():

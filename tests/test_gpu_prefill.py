@@ -373,6 +373,58 @@ def test_paged_prefill_window_and_noncausal(ea, orc):
     check_paged_prefill(orc, pg, q, cu, o, lse, "paged non-causal", causal=False)
 
 
+def run_paged_prefill_fp8(ea, pf, q, cu, window=None, causal=True):
+    t = gu.torch()
+    p = pf.base
+    qd = gu.dev(q, "bf16")
+    kc, vc = t.from_numpy(pf.k_codes).cuda(), t.from_numpy(pf.v_codes).cuda()
+    ks, vs = t.from_numpy(pf.k_scale).cuda(), t.from_numpy(pf.v_scale).cuda()
+    bt, sl, cud = gu.dev(p.block_table, "i32"), gu.dev(p.seq_lens, "i32"), gu.dev(cu, "i32")
+    o = gu.empty_out(qd.shape, "bf16")
+    lse = t.empty((qd.shape[0], qd.shape[1]), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    ea.attn_prefill_paged_fp8(qd, kc, vc, ks, vs, bt, sl, p.seq_lens, cud, cu, o, lse, scale=p.scale, causal=causal,
+                              window=window)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("d,ps", [(128, 16), (128, 64), (64, 32)])
+def test_paged_prefill_fp8_cache(ea, orc, d, ps):
+    """Prefill chunks and decode rows over E4M3 caches with per-(page, KV head)
+    scales; causal, then a window and non-causal (the bf16 tolerances: the
+    codes widen exactly and the scales stay fp32)."""
+    lens = [300, 1, 129, 700, 64, 5, 1000, 17]
+    q_lens = [300, 1, 1, 200, 64, 5, 129, 0]
+    _say("paged prefill fp8 cache", d, ps)
+    pf, q, cu = gen.make_paged_prefill_fp8(lens, q_lens, 8, 2, d, ps, seed=1900 + d + ps, extra_pages=3)
+    p = pf.base
+    for causal, window in ((True, None), (True, (77, -1)), (False, None)):
+        o, lse = run_paged_prefill_fp8(ea, pf, q, cu, window=window, causal=causal)
+        w = None if window is None else (window[0], 0 if causal else window[1])
+        o_ref, l_ref = orc.prefill_paged_fp8(q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, p.block_table,
+                                             p.seq_lens, cu, scale=p.scale, causal=causal, window=w)
+        _say(gu.check(o[None], lse[None], o_ref[None], l_ref[None], "bf16", f"fp8 cache d={d} ps={ps} {causal} {window}"))
+
+
+def test_paged_prefill_fp8_cache_full_size_sampled(ea, orc):
+    """The decode workload's FP8 cache (64 sequences, lengths ~U{512..32768},
+    A = 32, A_kv = 8, page 16) with each sequence's last 256 tokens as the
+    chunk: sampled rows against the oracle, all outputs finite."""
+    lens = gen.make_config(4).seq_lens
+    q_lens = np.full(lens.size, 256, np.int32)
+    _say("paged prefill fp8 cache full size", int(lens.sum()))
+    pf, q, cu = gen.make_paged_prefill_fp8(lens, q_lens, 32, 8, 128, 16, seed=1950)
+    o, lse = run_paged_prefill_fp8(ea, pf, q, cu)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(1951)
+    rows = np.unique(rng.integers(0, 32 * int(cu[-1]), size=300))
+    o_ref, l_ref = orc.prefill_paged_fp8(q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, pf.base.block_table,
+                                         lens, cu, scale=pf.base.scale, rows=rows)
+    _say(gu.check(o.reshape(-1, 128)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "fp8 cache full size"))
+
+
 def test_paged_prefill_equals_varlen_bitwise(ea):
     """With identity pages and the whole sequence as the chunk, the paged call
     computes exactly the packed varlen prefill (same tiles, same order)."""

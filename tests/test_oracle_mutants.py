@@ -96,6 +96,8 @@ PY_MUTANTS = [
      "kv = fp8_e4m3_value(kc) * 1.0", 0),
     ("FP8 decode: value scale of the key", "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale",
      "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(k_scale", 0),
+    ("FP8 paged prefill: value scale of the key", "vc = fp8_e4m3_value(v_codes) * np.asarray(v_scale",
+     "vc = fp8_e4m3_value(v_codes) * np.asarray(k_scale", 0),
     ("window: left edge off by one", "keep &= j >= i - left", "keep &= j > i - left", 0),
     ("window: aligned top-left", "off = S_k - S_q\n    i = np.arange(S_q, dtype=np.int64)[:, None] + off",
      "off = 0\n    i = np.arange(S_q, dtype=np.int64)[:, None] + off", 0),
