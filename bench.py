@@ -335,37 +335,73 @@ def grid_matches(kname: str, grid: int, pattern: str, wgs) -> bool:
 # long GQA workload (128 x 32) and the sliding-window leg (256 x 32), so the
 # grid tells them apart.
 DENSE = "prefill_bf16_kernel<128, false, false, false, false, false, false>"
+FP8_DENSE = "prefill_bf16_kernel<128, false, false, false, false, true, false>"
 TRAFFIC_PARTS = {
     "prefill": (DENSE, 2048),
     "gqa_long": (DENSE, 4096),
     "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false, false>", None),
-    "decode_split": ("decode_split_kernel<128, 1, false>", None),
+    "decode_split": ("decode_split_kernel<128, 1, false, 1, 4>", None),
     "decode_merge": ("decode_merge_kernel", None),
-    "bwd_dq": ("bwd_dq_kernel<128>", None),
-    "bwd_dkdv": ("bwd_dkdv_kernel<128,", None),
+    "bwd_dq": ("bwd_dq_kernel<128, false, false>", None),
+    "bwd_dkdv": ("bwd_dkdv_kernel<128, true, false, false>", None),
 }
-TRACE_ROWS = [  # (label, kernel pattern, workgroups or None, algorithmic work per launch: (amount, unit) or None)
-    ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, (1.374389534720e11, "TFLOP/s")),
-    ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, (2.199023255552e12, "TFLOP/s")),
-    ("sliding-window GQA causal prefill S=32768, 4096-key window", DENSE, 8192, None),
-    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false>", None, None),
-    ("paged decode split (bf16 cache)", "decode_split_kernel<128, 1, false>", None, None),
-    ("paged decode LSE merge (bf16 and FP8 legs)", "decode_merge_kernel<128>", None, None),
-    ("paged decode split (FP8 cache)", "decode_split_kernel<128, 2, true>", None, None),
-    ("backward dQ pass", "bwd_dq_kernel<128>", None, None),
-    ("backward dK/dV pass", "bwd_dkdv_kernel<128,", None, None),
-    ("paged chunked prefill", "prefill_bf16_kernel<128, true, true, false, false, false, false>", None, None),
+
+
+def _trace_work():
+    """Algorithmic work per launch of each trace row that has a fixed one:
+    (amount, unit, peak), from the workloads' seeded lengths alone."""
+    from synth import gen
+    mha = 4.0 * 4 * 32 * 2048 * 2048 * 128 / 2
+    gqa = 4.0 * 1 * 32 * 16384 * 16384 * 128 / 2
+    lv = gen.lognormal_lengths(16, 1024.0, 1.0, 64, 8192, gen.CONFIG_SEEDS[5]).astype(np.float64)
+    varlen = float(np.sum(4.0 * 16 * lv ** 2 * 64)) / 2
+    ld = gen.config_lengths_decode().astype(np.int64)
+    tokens, pages = int(ld.sum()), int(np.sum((ld + 15) // 16))
+    kv16 = 2.0 * 8 * 128 * 2 * tokens
+    kv8 = 2.0 * 8 * 128 * tokens + 2.0 * 4 * 8 * pages
+    win = 4.0 * 128 * 32 * window_pairs(32768, 4095)
+    q = PAGED_CHUNK
+    paged = 4.0 * 128 * 32 * float(np.sum(q * (ld - q) + q * (q + 1) // 2))
+    tf, gb = "TFLOP/s", "GB/s"
+    return {"mha": (mha, tf, PEAK_BF16_TFLOPS), "gqa": (gqa, tf, PEAK_BF16_TFLOPS),
+            "window": (win, tf, PEAK_BF16_TFLOPS), "varlen": (varlen, tf, PEAK_BF16_TFLOPS),
+            "decode": (kv16, gb, PEAK_HBM_GBPS), "decode_fp8": (kv8, gb, PEAK_HBM_GBPS),
+            "lowkv1": (2.0 * 1 * 128 * 2 * tokens, gb, PEAK_HBM_GBPS),
+            "lowkv2": (2.0 * 2 * 128 * 2 * tokens, gb, PEAK_HBM_GBPS),
+            "bwd": (2.5 * mha, tf, PEAK_BF16_TFLOPS),
+            "paged": (paged, tf, PEAK_BF16_TFLOPS),
+            "fp8_mha": (mha, tf, PEAK_FP8_TFLOPS), "fp8_gqa": (gqa, tf, PEAK_FP8_TFLOPS)}
+
+
+TRACE_ROWS = [  # (label, kernel pattern, workgroups or None, key of _trace_work() or None)
+    ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, "mha"),
+    ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, "gqa"),
+    ("sliding-window GQA causal prefill S=32768, 4096-key window (kept pairs)", DENSE, 8192, "window"),
+    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false>",
+     None, "varlen"),
+    ("paged decode split, bf16 cache (KV bytes / split time)", "decode_split_kernel<128, 1, false, 1, 4>", None,
+     "decode"),
+    ("paged decode LSE merge (all decode legs)", "decode_merge_kernel<128>", None, None),
+    ("paged decode split, FP8 cache (KV bytes / split time)", "decode_split_kernel<128, 2, true, 1, 4>", None,
+     "decode_fp8"),
+    ("paged decode split, A=32 on A_kv=1 (two column groups)", "decode_split_kernel<128, 1, false, 2, 1>", None,
+     "lowkv1"),
+    ("paged decode split, A=32 on A_kv=2 (one-wave workgroups)", "decode_split_kernel<128, 1, false, 1, 1>", None,
+     "lowkv2"),
+    ("backward dQ pass", "bwd_dq_kernel<128, false, false>", None, None),
+    ("backward dK/dV pass", "bwd_dkdv_kernel<128, true, false, false>", None, None),
+    ("paged chunked prefill, 256-token chunks (causal pairs)",
+     "prefill_bf16_kernel<128, true, true, false, false, false, false>", None, "paged"),
     ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false, false>", None, None),
-    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false>", None,
-     None),
-    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false>", None, None),
-    ("block mask of an additive term", "block_keep_kernel", None, None),
-    ("FP8-QK causal prefill, MHA shape", "prefill_bf16_kernel<128, false, false, false, false, true, false>", 2048,
-     (1.374389534720e11, "TFLOP/s")),
-    ("FP8-QK causal prefill, long GQA shape", "prefill_bf16_kernel<128, false, false, false, false, true, false>", 4096,
-     (2.199023255552e12, "TFLOP/s")),
-    ("paged chunked prefill over the E4M3 cache", "prefill_bf16_kernel<128, true, true, false, false, false, true>",
+    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false>",
      None, None),
+    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false>", None,
+     None),
+    ("block mask of an additive term", "block_keep_kernel", None, None),
+    ("FP8-QK causal prefill, MHA shape", FP8_DENSE, 2048, "fp8_mha"),
+    ("FP8-QK causal prefill, long GQA shape", FP8_DENSE, 4096, "fp8_gqa"),
+    ("paged chunked prefill over the E4M3 cache (causal pairs)",
+     "prefill_bf16_kernel<128, true, true, false, false, false, true>", None, "paged"),
 ]
 
 
@@ -389,17 +425,37 @@ def trace_summary(d: str):
           "Rate = algorithmic work per launch / average duration.\n")
     print("| workload | kernel | grid (work-items) | calls | avg us | median us | min us | rate at avg |")
     print("|---|---|---|---|---|---|---|---|")
-    for label, pat, wgs, work in TRACE_ROWS:
+    works = _trace_work()
+    for label, pat, wgs, wkey in TRACE_ROWS:
         ts = sorted(t for k, g, t in disp if grid_matches(k, g, pat, wgs))
         if not ts:
             continue
         grids = sorted({g for k, g, t in disp if grid_matches(k, g, pat, wgs)})
         avg = sum(ts) / len(ts)
         rate = ""
-        if work:
-            rate = f"{work[0] / (avg * 1e-9) / 1e12:.1f} {work[1]} ({100 * work[0] / (avg * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of 2500)"
+        if wkey:
+            amount, unit, peak = works[wkey]
+            r = amount / (avg * 1e-9) / (1e12 if unit == "TFLOP/s" else 1e9)
+            rate = f"{r:.1f} {unit} ({100 * r / peak:.1f}% of {peak:.0f})"
         print(f"| {label} | `{pat}` | {','.join(map(str, grids))} | {len(ts)} | {avg / 1e3:.1f} | "
               f"{ts[len(ts) // 2] / 1e3:.1f} | {ts[0] / 1e3:.1f} | {rate} |")
+    print("\nThe backward's two passes together do 2.5x the forward's FLOPs of the MHA workload; the bench reports "
+          "their combined rate.")
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        print("\n`--stats` output of the same run (per kernel name, all grids together; the library's kernels, then "
+              "the five longest others: the measured ceilings, uploads and fills):\n")
+        print("| kernel | calls | avg us | min us | max us | share |")
+        print("|---|---|---|---|---|---|")
+        with open(stats[0]) as fh:
+            rows = list(csv.DictReader(fh))
+        ours = [r for r in rows if "attn::" in r["Name"]]
+        others = [r for r in rows if "attn::" not in r["Name"]][:5]
+        for r in ours + others:
+            name = r["Name"].replace("void ", "").replace("attn::(anonymous namespace)::", "")
+            name = name.split("(")[0] if "attn::" in r["Name"] else name[:70]
+            print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                  f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
 
 
 N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
@@ -665,7 +721,7 @@ def bench_backward(w, steps: int, warmup: int) -> dict:
             "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5),
             "flops": flops,
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 (the prefill workload)",
-            "kernels": "bwd_dq_kernel<128> then bwd_dkdv_kernel<128, true> (K rows in LDS; one call)"}
+            "kernels": "bwd_dq_kernel<128, false, false> then bwd_dkdv_kernel<128, true, false, false> (K rows in LDS; one call)"}
 
 
 def window_pairs(S: int, left: int) -> int:
