@@ -46,8 +46,8 @@
 //            key tile is one page, found through the block table);
 //   kBlocks  the key tiles of a row block listed from a 128 x 128 block mask,
 //            so masked blocks are never loaded;
-//   kBias    a dense additive term M on every score (all tiles take the
-//            per-element step).
+//   kBias    a dense additive term M on every score (loaded a tile ahead as
+//            the initial value of the score accumulators).
 // Sliding windows, keep masks and the causal flag are runtime arguments of
 // every instantiation.
 #include <type_traits>
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // after them (the online softmax does not depend on the order).  Logical
   // tile t is physical tile phys(t).
   int j_ul = j_lo, j_uh = j_lo;
-  if (rb.k_keep == nullptr && !kBias && n_range > 0) {
+  if (rb.k_keep == nullptr && n_range > 0) {
     int ul = wl >= 0 ? (max(q_last + off - wl, 0) + kBc - 1) / kBc : 0;
     int uh = S_k / kBc;
     if (wr >= 0) uh = min(uh, max(q_first + off + wr + 1, 0) / kBc);
@@ -444,10 +444,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
   // S^T = K . Q^T for the K tile in LDS buffer KBUF: two 32-key blocks, the
   // k-steps interleaved across them.  `issue` is called at two points.
+  // (with an additive term, s arrives holding M / scale of the tile's scores)
   auto qk = [&](auto kbuf_tag, f32x16 (&s)[2], auto&& issue) {
     constexpr int KB = decltype(kbuf_tag)::value * KTILE_BYTES;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    if constexpr (!kBias) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
     if constexpr (kFp8) {
       // FP8: steps p = (kb = p % 2, t = p / 2) over 64-wide k-steps; lane reads
       // row l32 of key block kb, the 32 bytes [64t + 32g, +32) = logical
@@ -505,36 +508,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // Dense additive mask: this lane's row of M, and the 32 terms of its keys
   // in tile t (element (kb, r) of the score tile is key k0 + 32kb + 8(r/4) +
   // 4g + r%4, so keys come in runs of 4: one 16-byte load per run).  Keys at
-  // or past S_k are not read (their scores are masked below).  The term is
-  // added to the raw product as M / scale, so that the base-2 scaling by
-  // scale * log2(e) applies to both.
-  [[maybe_unused]] const float* brow = nullptr;
+  // or past S_k are not read (their scores are masked below).  The term
+  // enters the raw product as M / scale, so that the base-2 scaling by
+  // scale * log2(e) applies to both: it is the initial value of the score
+  // accumulators.  A tile's terms are loaded an iteration ahead, so that the
+  // wait for the tile copies at the top of the iteration covers them.
+  // The terms of this workgroup's rows come through one buffer resource that
+  // starts at its first row and ends at key S_k of its last row: rows past
+  // S_q read zeros, and keys past S_k (padding, or the next row's terms)
+  // belong to masked tiles, whose predicate discards them.  A lane's offset
+  // holds its row; the tile's first key goes in the scalar offset.
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t bias_rsrc;
+  [[maybe_unused]] uint32_t bias_voff = 0;
   if constexpr (kBias) {
     const int hm = p.bias_heads == 1 ? 0 : rb.h;
-    brow = p.bias + ((size_t)(rb.b * p.bias_heads + hm) * S_q + min(qrow, S_q - 1)) * p.bias_ld;
+    const int rows = min(kRows, S_q - rb.q0);
+    const float* plane = p.bias + ((size_t)(rb.b * p.bias_heads + hm) * S_q + rb.q0) * p.bias_ld;
+    const uint32_t nbytes = ((uint32_t)(rows - 1) * p.bias_ld + S_k) * 4u;
+    bias_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)plane, 0, (int)nbytes, 0x00020000);
+    bias_voff = ((uint32_t)(qrow - rb.q0) * p.bias_ld + 4 * g) * 4u;
   }
   auto bias_load = [&](int t, f32x4 (&m)[2][4]) {
     if constexpr (kBias) {
-      const int k0 = phys(t) * kBc;
+      const int k0b = __builtin_amdgcn_readfirstlane(phys(t) * kBc * 4);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int kk = k0 + 32 * kb + 8 * q4 + 4 * g;
-          m[kb][q4] = kk < S_k ? *(const f32x4*)(brow + kk) : f32x4{};
+          // (the run's offset goes in the scalar operand: one offset register
+          // serves all eight loads)
+          m[kb][q4] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(bias_rsrc, bias_voff, k0b + (32 * kb + 8 * q4) * 4, 0));
         }
       }
     }
   };
-  auto mask = [&](f32x16 (&s)[2], int t, const f32x4 (&m)[2][4]) {
-    const int k0 = phys(t) * kBc;
+  auto term_init = [&](f32x16 (&s)[2], const f32x4 (&m)[2][4]) {
     if constexpr (kBias) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(m[kb][r >> 2][r & 3], p.inv_scale, s[kb][r]);
+        for (int r = 0; r < 16; ++r) s[kb][r] = m[kb][r >> 2][r & 3] * p.inv_scale;
       }
     }
+  };
+  auto mask = [&](f32x16 (&s)[2], int t) {
+    const int k0 = phys(t) * kBc;
     // bit k of kvalid: key k0 + k exists and is kept (same for every lane)
     bool valid = k0 + lane < S_k;
     if (rb.k_keep) valid = valid && sKeep[t & 1][lane] != 0;
@@ -642,6 +661,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // ---- prologue: K, V of tile 0 and K of tile 1 in flight; S of tile 0
   f32x16 s_cur[2];
   float mx_cur = -INFINITY;
+  [[maybe_unused]] f32x4 m_nx[2][4];  // additive term: the terms of the next tile's scores
   float cs_cur = cs;  // the score scale of the tile in s_cur (fp8: per tile)
   if (n_tiles > 0) {
     if constexpr (kPaged && kCache8) {
@@ -696,11 +716,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     copy_keep(1);
     f32x4 m0[2][4];
     bias_load(0, m0);
+    bias_load(min(1, n_tiles - 1), m_nx);
     lds_copy_wait_all();
     __syncthreads();
+    term_init(s_cur, m0);
     qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
     kscale(s_cur, 0);
-    if (n_mid == 0) mask(s_cur, 0, m0);
+    if (n_mid == 0) mask(s_cur, 0);
     cs_cur = cs_of(0);
     mx_cur = rowmax(s_cur, cs_cur);
   }
@@ -787,8 +809,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     f32x16 s_next[2];
     interleave_hint();
     if constexpr (!MASKED) {
+      term_init(s_next, m_nx);
       qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
       kscale(s_next, BUF ^ 1);
+      bias_load(min(j + 2, n_tiles - 1), m_nx);  // in flight until the next iteration's copy wait
       softmax_pv(buf_tag, s_cur, cs_cur, issue);
       cs_cur = cs_of(j + 1);
       mx_cur = rowmax(s_next, cs_cur);
@@ -798,15 +822,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       // a wave skips the work of a tile none of its rows can see (it still
       // takes part in the copies and barriers)
       const bool has_next = j + 1 < n_tiles && wave_sees(j + 1);
-      f32x4 m_next[2][4];
       if (has_next) {
+        term_init(s_next, m_nx);
         qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
         kscale(s_next, BUF ^ 1);
       } else {
         issue(0);
         issue(1);
       }
-      if (has_next) bias_load(j + 1, m_next);  // in flight during the softmax and PV of tile j
+      bias_load(min(j + 2, n_tiles - 1), m_nx);  // in flight until the next iteration's copy wait
       if (wave_sees(j)) {
         softmax_pv(buf_tag, s_cur, cs_cur, issue);
       } else {
@@ -814,7 +838,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         issue(3);
       }
       if (has_next) {
-        mask(s_next, j + 1, m_next);
+        mask(s_next, j + 1);
         cs_cur = cs_of(j + 1);
         mx_cur = rowmax(s_next, cs_cur);
         s_cur[0] = s_next[0];
