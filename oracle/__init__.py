@@ -54,7 +54,7 @@ class Oracle:
         self.lib.oracle_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32,
                                                     i32, vp, vp, vp, i64, vp, vp]
         self.lib.oracle_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                 i32, f32, vp, i64, vp, vp]
+                                                 i32, f32, i32, vp, i64, vp, vp]
         self.lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]
         self.lib.oracle_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32, i32,
@@ -332,8 +332,10 @@ class Oracle:
             lses.append(lse.reshape(A))
         return np.stack(outs), np.stack(lses)
 
-    def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None):
-        """Paged decode.  q [B,A,d]; caches [P, page_size, A_kv, d]; rows = b*A + h."""
+    def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None, window_left=None):
+        """Paged decode.  q [B,A,d]; caches [P, page_size, A_kv, d]; rows = b*A + h.
+        window_left: the query (position seq_lens[b] - 1) sees keys t >=
+        seq_lens[b] - 1 - window_left; None = every key."""
         q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
         if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
             raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
@@ -349,8 +351,9 @@ class Oracle:
         n_out = B * A if r is None else n
         o = np.empty((n_out, d), dtype=np.float64)
         lse = np.empty(n_out, dtype=np.float64)
+        wl = -1 if window_left is None else int(window_left)
         rc = self.lib.oracle_decode_paged(_ptr(q), _ptr(kc), _ptr(vc), _DT[dtype], _ptr(bt), _ptr(sl), B, A,
-                                          A_kv, d, page_size, bt.shape[1], num_pages, float(scale), _ptr(r), n,
+                                          A_kv, d, page_size, bt.shape[1], num_pages, float(scale), wl, _ptr(r), n,
                                           _ptr(o), _ptr(lse))
         if rc != 0:
             raise ValueError("oracle_decode_paged rejected its arguments")

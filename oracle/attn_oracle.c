@@ -454,16 +454,20 @@ int oracle_attn_fwd_varlen(const void *q, const void *k, const void *v, int dt,
  * Single-query decode over a paged KV cache.  q, o: [B, A, d];
  * k_cache, v_cache: [num_pages, page_size, A_kv, d];
  * block_table: [B, max_pages]; seq_lens: [B].
+ * The query of sequence b sits at position seq_lens[b] - 1 (it is the last
+ * token).  win_left >= 0 is a sliding window ("Attention Kernel", section
+ * 可编程 mask): key t is visible when t >= seq_lens[b] - 1 - win_left;
+ * win_left = -1 leaves every key visible.
  * rows: flattened ids b*A + h, or NULL for all.
  */
 int oracle_decode_paged(const void *q, const void *k_cache, const void *v_cache, int dt,
                         const int32_t *block_table, const int32_t *seq_lens,
                         int B, int A, int A_kv, int d, int page_size, int max_pages,
-                        int num_pages, float scale,
+                        int num_pages, float scale, int win_left,
                         const int64_t *rows, int64_t n_rows, double *o, double *lse)
 {
     if (B <= 0 || A <= 0 || A_kv <= 0 || d <= 0 || A % A_kv != 0 || page_size <= 0 ||
-        max_pages < 0 || num_pages < 0)
+        max_pages < 0 || num_pages < 0 || win_left < -1)
         return -1;
     if (!dt_ok(dt))
         return -1;
@@ -504,7 +508,7 @@ int oracle_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                 int64_t page = block_table[(int64_t)b * max_pages + t / page_size];
                 int off = t % page_size;
                 w.off[t] = ((page * page_size + off) * A_kv + hk) * (int64_t)d;
-                w.vis[t] = 1;
+                w.vis[t] = win_left < 0 || (int64_t)t >= (int64_t)n - 1 - win_left;
             }
             attend_row(q, id * d, k_cache, v_cache, dt, w.off, w.vis, NULL, n, d, (double)scale,
                        w.s, w.p, o + r * d, lse + r);

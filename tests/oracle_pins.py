@@ -927,6 +927,48 @@ def pin_prefill_paged_decode_rows(orc):
         assert np.array_equal(o.transpose(1, 0, 2), od) and np.array_equal(lse.T, ld)
 
 
+def pin_decode_window_rows(orc):
+    """A decode step with a sliding window of w keys before the query is the
+    one-row chunk of the paged prefill under the window (w, unbounded right),
+    bit for bit ("Attention Kernel", 可编程 mask: sliding window), for windows
+    shorter and longer than the sequences."""
+    lens = [9, 1, 23, 16, 5]
+    A, A_kv, d, ps = 4, 2, 3, 4
+    q, kc, vc, bt, sl, cu = _paged_problem(lens, [1] * len(lens), A, A_kv, d, ps, 66)
+    qd = np.ascontiguousarray(q.transpose(1, 0, 2))
+    for w in (0, 3, 8, 40):
+        o, lse = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=0.75, causal=True, window=(w, -1))
+        od, ld = orc.decode_paged(qd, kc, vc, bt, sl, dtype="f32", scale=0.75, window_left=w)
+        assert np.array_equal(o.transpose(1, 0, 2), od) and np.array_equal(lse.T, ld), w
+
+
+def pin_decode_window_closed_forms(orc):
+    """Window 0: the query sees only itself, O = v of the last token exactly and
+    LSE = scale q . k_last.  Window 1: the two-key softmax written out.  A
+    window reaching the first token: the decode without a window, bit for bit."""
+    lens = [7, 12, 2]
+    A, A_kv, d, ps = 2, 1, 5, 4
+    q, kc, vc, bt, sl, cu = _paged_problem(lens, [1] * len(lens), A, A_kv, d, ps, 67)
+    qd = np.ascontiguousarray(q.transpose(1, 0, 2)).astype(np.float64)
+    o0, l0 = orc.decode_paged(qd.astype(np.float32), kc, vc, bt, sl, dtype="f32", scale=0.5, window_left=0)
+    o1, l1 = orc.decode_paged(qd.astype(np.float32), kc, vc, bt, sl, dtype="f32", scale=0.5, window_left=1)
+    for b, L in enumerate(lens):
+        kk = _contiguous(kc, bt[b], L, ps).astype(np.float64)
+        vv = _contiguous(vc, bt[b], L, ps).astype(np.float64)
+        for h in range(A):
+            s_last = 0.5 * float(qd[b, h] @ kk[0, L - 1])
+            assert np.array_equal(o0[b, h], vv[0, L - 1]) and abs(l0[b, h] - s_last) < 1e-12
+            s_prev = 0.5 * float(qd[b, h] @ kk[0, L - 2])
+            m = max(s_last, s_prev)
+            e1, e2 = math.exp(s_prev - m), math.exp(s_last - m)
+            want = (e1 * vv[0, L - 2] + e2 * vv[0, L - 1]) / (e1 + e2)
+            assert np.allclose(o1[b, h], want, rtol=0, atol=1e-12)
+            assert abs(l1[b, h] - (m + math.log(e1 + e2))) < 1e-12
+    on, ln = orc.decode_paged(qd.astype(np.float32), kc, vc, bt, sl, dtype="f32", scale=0.5)
+    ow, lw = orc.decode_paged(qd.astype(np.float32), kc, vc, bt, sl, dtype="f32", scale=0.5, window_left=11)
+    assert np.array_equal(on, ow) and np.array_equal(ln, lw)
+
+
 def pin_prefill_paged_identity_is_varlen(orc):
     """With pages laid out in order and each whole sequence as its chunk, the
     paged prefill is the packed varlen prefill, bit for bit."""

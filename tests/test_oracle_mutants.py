@@ -28,6 +28,11 @@ MUTANTS = [
     ("q_keep ignored (dense)", "int row_masked = q_keep && !q_keep[(int64_t)b * S_q + i];", "int row_masked = 0;", 0),
     ("k_keep ignored (dense)", "if (k_keep && !k_keep[(int64_t)b * S_k + j])", "if (0)", 0),
     ("k_keep ignored (varlen)", "if (k_keep && !k_keep[start + j])", "if (0)", 0),
+    ("decode window excludes its left edge", "(int64_t)t >= (int64_t)n - 1 - win_left", "(int64_t)t > (int64_t)n - 1 - win_left",
+     0),
+    ("decode window ignored", "w.vis[t] = win_left < 0 ||", "w.vis[t] = 1 ||", 0),
+    ("decode window anchored at the first token", "(int64_t)t >= (int64_t)n - 1 - win_left", "(int64_t)t <= (int64_t)win_left",
+     0),
     ("varlen causal diagonal excluded", "if (causal && j > i)", "if (causal && j >= i)", 0),
     ("varlen keys not offset to sequence", "int64_t kv_base = ((int64_t)(h / G) * T + start) * d;",
      "int64_t kv_base = ((int64_t)(h / G) * T) * d;", 0),
