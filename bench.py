@@ -368,19 +368,26 @@ def _trace_work():
             "decode": (kv16, gb, PEAK_HBM_GBPS), "decode_fp8": (kv8, gb, PEAK_HBM_GBPS),
             "lowkv1": (2.0 * 1 * 128 * 2 * tokens, gb, PEAK_HBM_GBPS),
             "lowkv2": (2.0 * 2 * 128 * 2 * tokens, gb, PEAK_HBM_GBPS),
+            "decode_window": (2.0 * 8 * 128 * 2 * int(np.minimum(ld, DECODE_WINDOW).sum()), gb, PEAK_HBM_GBPS),
             "bwd": (2.5 * mha, tf, PEAK_BF16_TFLOPS),
             "paged": (paged, tf, PEAK_BF16_TFLOPS),
             "fp8_mha": (mha, tf, PEAK_FP8_TFLOPS), "fp8_gqa": (gqa, tf, PEAK_FP8_TFLOPS)}
 
 
-TRACE_ROWS = [  # (label, kernel pattern, workgroups or None, key of _trace_work() or None)
+# (label, kernel pattern, workgroups or None, key of _trace_work() or None).  A
+# pattern (name, part) names a kernel and grid that two legs share: their
+# dispatches split at the largest gap in dispatch order (the legs run one
+# after the other), part 0 the earlier leg, 1 the later.
+TRACE_ROWS = [
     ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, "mha"),
     ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, "gqa"),
     ("sliding-window GQA causal prefill S=32768, 4096-key window (kept pairs)", DENSE, 8192, "window"),
     ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false>",
      None, "varlen"),
-    ("paged decode split, bf16 cache (KV bytes / split time)", "decode_split_kernel<128, 1, false, 1, 4>", None,
+    ("paged decode split, bf16 cache (KV bytes / split time)", ("decode_split_kernel<128, 1, false, 1, 4>", 0), None,
      "decode"),
+    ("paged decode split, 4096-token window (visible KV bytes / split time)",
+     ("decode_split_kernel<128, 1, false, 1, 4>", 1), None, "decode_window"),
     ("paged decode LSE merge (all decode legs)", "decode_merge_kernel<128>", None, None),
     ("paged decode split, FP8 cache (KV bytes / split time)", "decode_split_kernel<128, 2, true, 1, 4>", None,
      "decode_fp8"),
@@ -415,7 +422,8 @@ def trace_summary(d: str):
     for path in files:
         with open(path) as fh:
             for r in csv.DictReader(fh):
-                disp.append((r["Kernel_Name"], grid_of(r), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+                disp.append((r["Kernel_Name"], grid_of(r), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                             int(r["Dispatch_Id"])))
     print("# Kernel trace of the bench, per kernel and workload\n")
     print("Commands (repository root, one MI355X):\n")
     print("    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 10 --warmup 2 "
@@ -427,10 +435,18 @@ def trace_summary(d: str):
     print("|---|---|---|---|---|---|---|---|")
     works = _trace_work()
     for label, pat, wgs, wkey in TRACE_ROWS:
-        ts = sorted(t for k, g, t in disp if grid_matches(k, g, pat, wgs))
+        part = None
+        if isinstance(pat, tuple):
+            pat, part = pat
+        sel = sorted((i, g, t) for k, g, t, i in disp if grid_matches(k, g, pat, wgs))
+        if part is not None and len(sel) > 1:
+            gaps = [sel[j + 1][0] - sel[j][0] for j in range(len(sel) - 1)]
+            cut = gaps.index(max(gaps)) + 1
+            sel = sel[:cut] if part == 0 else sel[cut:]
+        ts = sorted(t for _, _, t in sel)
         if not ts:
             continue
-        grids = sorted({g for k, g, t in disp if grid_matches(k, g, pat, wgs)})
+        grids = sorted({g for _, g, _ in sel})
         avg = sum(ts) / len(ts)
         rate = ""
         if wkey:
@@ -653,6 +669,7 @@ def main():
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
     out["fp8_prefill"] = bench_fp8_prefill(args.steps, args.warmup, stream)
     out["decode_low_kv"] = bench_decode_low_kv(w, args.steps, args.warmup)
+    out["decode_window"] = bench_decode_window(w, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p2, args.cpu_seconds)
@@ -894,6 +911,35 @@ def bench_decode_low_kv(w, steps: int, warmup: int) -> dict:
         del q, kc, vc, bt, sl, o, lse, ws
     torch.cuda.empty_cache()
     return out
+
+
+DECODE_WINDOW = 4096
+
+
+def bench_decode_window(w, steps: int, warmup: int) -> dict:
+    """The paged decode workload with a sliding window: each query sees its own
+    token and the 4095 before it.  KV GB/s = 2 A_kv d 2 bytes x visible tokens
+    / time (split + merge)."""
+    import torch
+    import exact_attention_108_amd as ea
+    p4, stream = w["p4"], w["stream"]
+    kc, vc, bt, sl = w["dev4"]
+    q = to_dev(p4.q, "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty((p4.B, p4.A), dtype=torch.float32, device="cuda")
+    nb = ea.attn_decode_paged_workspace_bytes(p4.B, p4.A, p4.A_kv, p4.d, p4.page_size, p4.seq_lens)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    ms = _event_times(lambda: ea.attn_decode_paged_window(q, kc, vc, bt, sl, p4.seq_lens, o, lse, ws, scale=p4.scale,
+                                                          window_left=DECODE_WINDOW - 1, stream=stream),
+                      steps, warmup, stream)
+    visible = int(np.minimum(p4.seq_lens.astype(np.int64), DECODE_WINDOW).sum())
+    kvb = 2.0 * p4.A_kv * p4.d * 2 * visible
+    gbs = kvb / (ms.mean() * 1e-3) / 1e9
+    return {"metric": "sliding-window paged-decode KV GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBPS, 4), "avg_ms": round(float(ms.mean()), 5),
+            "median_ms": round(float(np.median(ms)), 5), "kv_bytes": kvb, "visible_tokens": visible,
+            "workload": f"the paged decode workload (64 seqs, A=32 A_kv=8 d=128 page 16) with a {DECODE_WINDOW}-token "
+                        "window (each query sees its own token and the ones before it)"}
 
 
 def bench_block_sparse(w, steps: int, warmup: int) -> dict:

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     attn_decode_paged,
     attn_decode_paged_fp8,
     attn_decode_paged_noalloc,
+    attn_decode_paged_window,
     DECODE_NOALLOC_MAX_BYTES,
     attn_decode_paged_workspace_bytes,
     attn_fwd,

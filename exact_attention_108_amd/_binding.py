@@ -46,6 +46,9 @@ _lib.attn_fwd_varlen.restype = _i
 _lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                    _vp, _sz, _vp]
 _lib.attn_decode_paged.restype = _i
+_lib.attn_decode_paged_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                          _i, _i, _vp, _sz, _vp]
+_lib.attn_decode_paged_window.restype = _i
 _lib.attn_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                            _i, _vp]
 _lib.attn_decode_paged_noalloc.restype = _i
@@ -91,6 +94,7 @@ def attn_abi_version() -> int:
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
+            "attn_decode_paged_window",
             "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8", "attn_decode_paged_fp8",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
@@ -323,6 +327,20 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host,
     """Paged decode.  q/o [B,A,d]; caches [num_pages, page_size, A_kv, d]; block_table int32 [B, max_pages];
     seq_lens int32 [B] (device) and seq_lens_host (numpy); workspace a uint8 device tensor of at least
     attn_decode_paged_workspace_bytes(...) bytes."""
+    _decode_call("attn_decode_paged", q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, workspace,
+                 scale, None, stream)
+
+
+def attn_decode_paged_window(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, workspace, *,
+                             scale: float, window_left: int, stream=None):
+    """attn_decode_paged where the query (position seq_lens[b] - 1) sees the keys t >= seq_lens[b] - 1 -
+    window_left; window_left = -1 sees every key."""
+    _decode_call("attn_decode_paged_window", q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse,
+                 workspace, scale, int(window_left), stream)
+
+
+def _decode_call(name, q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, workspace, scale,
+                 window_left, stream):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
@@ -341,11 +359,12 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host,
         raise ValueError("seq_lens_host must be [B]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace)
-    st = _lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
-                                sl.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), B, A, A_kv, d,
-                                block_table.shape[1], num_pages, float(scale), _dtype_code(q),
-                                _ptr(workspace), ws_bytes, _stream(stream, dev))
-    _check(st, "attn_decode_paged")
+    args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp),
+            page_size, _ptr(o), _ptr(lse), B, A, A_kv, d, block_table.shape[1], num_pages, float(scale)]
+    if window_left is not None:
+        args.append(window_left)
+    st = getattr(_lib, name)(*args, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    _check(st, name)
 
 
 DECODE_NOALLOC_MAX_BYTES = 48 << 20

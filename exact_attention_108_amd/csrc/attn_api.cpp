@@ -277,9 +277,10 @@ attn_status check_decode_call(const void* q, const void* k_cache, const void* v_
 attn_status launch_decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* seq_lens_host, int page_size, void* o,
                                float* lse, int B, int A, int A_kv, int d_h, int max_pages, float scale,
-                               void* workspace, void* stream) {
-  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
+                               int window_left, void* workspace, void* stream) {
+  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host, window_left);
   attn::DecodeParams p{};
+  p.win_left = window_left;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -317,7 +318,24 @@ ATTN_EXPORT attn_status attn_decode_paged(const void* q, const void* k_cache, co
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
     return ATTN_ERR_INVAL;
   return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
-                            A_kv, d_h, max_pages, scale, workspace, stream);
+                            A_kv, d_h, max_pages, scale, -1, workspace, stream);
+}
+
+ATTN_EXPORT attn_status attn_decode_paged_window(const void* q, const void* k_cache, const void* v_cache,
+                                                 const int32_t* block_table, const int32_t* seq_lens,
+                                                 const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                                 int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                                 float scale, int window_left, attn_dtype dtype, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  if (window_left < -1) return ATTN_ERR_INVAL;
+  size_t need = 0;
+  attn_status st = check_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse,
+                                     B, A, A_kv, d_h, max_pages, num_pages, scale, dtype, need);
+  if (st != ATTN_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
+                            A_kv, d_h, max_pages, scale, window_left, workspace, stream);
 }
 
 ATTN_EXPORT attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
@@ -333,7 +351,7 @@ ATTN_EXPORT attn_status attn_decode_paged_noalloc(const void* q, const void* k_c
   void* ws = nullptr;
   if (need > 0 && attn::decode_static_scratch(&ws) != hipSuccess) return ATTN_ERR_LAUNCH;
   return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
-                            A_kv, d_h, max_pages, scale, ws, stream);
+                            A_kv, d_h, max_pages, scale, -1, ws, stream);
 }
 
 namespace {
@@ -601,6 +619,7 @@ ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_ca
     return ATTN_ERR_INVAL;
   if ((long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   attn::DecodeParams p{};
+  p.win_left = -1;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;

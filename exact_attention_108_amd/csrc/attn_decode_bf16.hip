@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
     for (int base = 0; base < p.B; base += 64) {
       const int bb = base + lane;
       const int lb = bb < p.B ? p.seq_lens[bb] : 0;
-      const int nc = (lb + kChunk - 1) / kChunk;
+      const int nc = decode_chunks(lb, p.win_left);
       const long long incl = base_chunks + wave_incl_scan(nc, lane);
       const long long total = __shfl(incl, 63);
       if (c_lo < total) {
@@ -156,12 +156,15 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
   const float cs = p.scale_log2;
   const int tr_r = l16 >> 2, tr_q = l16 & 3;
 
-  int k = (int)(c_lo - cex);     // chunk index within sequence b
+  int k = (int)(c_lo - cex);     // chunk index within sequence b's list
   long long remaining = c_hi - c_lo;
   while (true) {
-    const int nch = (len + kChunk - 1) / kChunk;
+    // the list of sequence b starts at the chunk of its first visible key
+    const int t_first = decode_first_key(len, p.win_left);
+    const int ck0 = t_first / kChunk;
+    const int nch = decode_chunks(len, p.win_left);
     const int k_end = (int)min((long long)nch, k + remaining);
-    const int t_begin = k * kChunk, t_end = min(len, k_end * kChunk);
+    const int t_begin = (ck0 + k) * kChunk, t_end = min(len, (ck0 + k_end) * kChunk);
 
     // ---- Q^T operand: column n = query head kv0*G + n (n < nh*G), 8 d per lane
     const uint16_t* qb = (const uint16_t*)p.q + ((size_t)b * p.A + (size_t)kv0 * G) * D;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (kFp8) sc[cg][r] *= ksc;
-          if (4 * grp + r >= n_valid) sc[cg][r] = -INFINITY;
+          if (4 * grp + r >= n_valid || c0 + 4 * grp + r < t_first) sc[cg][r] = -INFINITY;
           mx = fmaxf(mx, sc[cg][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -418,12 +421,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
     for (int base = 0; base < b; base += 64) {
       const int bb = base + lane;
       const int lb = bb < b ? p.seq_lens[bb] : 0;
-      long long nc = (lb + kChunk - 1) / kChunk;
+      long long nc = decode_chunks(lb, p.win_left);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) nc += __shfl_xor(nc, off);
       cex += nc;
     }
-    const long long nch = (len + kChunk - 1) / kChunk;
+    const long long nch = decode_chunks(len, p.win_left);
     const long long NC = p.n_chunks, P = p.n_wg;
     // owner of chunk c: the largest i with floor(i * NC / P) <= c
     const int first = (int)(((cex + 1) * P - 1) / NC);
@@ -566,10 +569,11 @@ hipError_t decode_static_scratch(void** ptr) {
   return hipSuccess;
 }
 
-DecodePlan plan_decode(int B, const int32_t* seq_lens_host) {
+DecodePlan plan_decode(int B, const int32_t* seq_lens_host, int win_left) {
+  static_assert(kChunk == 16, "decode_chunks counts 16-token chunks");
   DecodePlan plan;
   long long nc = 0;
-  for (int b = 0; b < B; ++b) nc += (seq_lens_host[b] + kChunk - 1) / kChunk;
+  for (int b = 0; b < B; ++b) nc += decode_chunks(seq_lens_host[b], win_left);
   plan.n_chunks = nc;
   plan.n_slots = kMaxDecodeGroups + B;  // slot wg + b < n_wg + B
   return plan;

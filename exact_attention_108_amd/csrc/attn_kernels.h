@@ -129,7 +129,11 @@ struct DecodeParams {
   const float* v_scale;
   int B, A, A_kv, G, d;
   int page_size, max_pages;
-  long long n_chunks;  // sum over sequences of ceil(len / 16)
+  // sliding window: the query (position len - 1) sees keys t >= len - 1 -
+  // win_left; -1 = every key.  A sequence's chunk list covers the 16-token
+  // chunks from the one holding its first visible key.
+  int win_left;
+  long long n_chunks;  // sum over sequences of decode_chunks(len, win_left)
   int n_wg;            // workgroups along the chunk list (set at launch)
   float scale, scale_log2;
 };
@@ -141,7 +145,14 @@ struct DecodePlan {
   long long n_chunks;
   int n_slots;  // partial slots: workgroup + sequence < kMaxDecodeGroups + B
 };
-DecodePlan plan_decode(int B, const int32_t* seq_lens_host);
+// first visible key of a sequence of len tokens, and its chunks in the list
+__host__ __device__ inline int decode_first_key(int len, int win_left) {
+  return (win_left < 0 || len - 1 - win_left <= 0) ? 0 : len - 1 - win_left;
+}
+__host__ __device__ inline int decode_chunks(int len, int win_left) {
+  return len <= 0 ? 0 : (len + 15) / 16 - decode_first_key(len, win_left) / 16;
+}
+DecodePlan plan_decode(int B, const int32_t* seq_lens_host, int win_left = -1);
 size_t decode_workspace_bytes(int A, int d, const DecodePlan& plan);
 size_t decode_workspace_lse_offset(int A, int d, const DecodePlan& plan);
 

@@ -235,6 +235,26 @@ attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_
                               size_t workspace_bytes, void *stream);
 
 /*
+ * attn_decode_paged with a sliding window (page "Attention Kernel", section
+ * "可编程 mask": a sliding window bounds how far back a query looks).  The
+ * query of sequence b sits at position seq_lens[b] - 1 and sees the keys t
+ * with t >= seq_lens[b] - 1 - window_left: its own and the window_left before
+ * it.  window_left = -1 is attn_decode_paged (every key; bit for bit).  Only
+ * the 16-token chunks from the one holding the first visible key are read
+ * and split, so the work per sequence is min(len, window_left + 1) tokens
+ * rounded out to chunks.  Arguments, workspace (attn_decode_paged_workspace_
+ * bytes suffices), support and errors as attn_decode_paged; window_left <
+ * -1 is ATTN_ERR_INVAL.
+ */
+attn_status attn_decode_paged_window(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     const int32_t *seq_lens_host, int page_size, void *o,
+                                     float *lse, int B, int A, int A_kv, int d_h, int max_pages,
+                                     int num_pages, float scale, int window_left,
+                                     attn_dtype dtype, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
  * attn_decode_paged over an FP8 KV cache (page "Attention Kernel", sections
  * "Paged 与 ragged KV" and "正确性契约": the cache dtype and its scale
  * metadata are part of the contract; page "Attention 算子加速史", section

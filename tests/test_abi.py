@@ -20,6 +20,7 @@ def header_functions():
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_noalloc",
+                                         "attn_decode_paged_window",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8",
                                          "attn_decode_paged_fp8",
@@ -428,3 +429,22 @@ def test_attn_block_keep_from_bias_rejects_bad_arguments():
     assert blk(bias=ctypes.c_void_p(4096 + 4)) == INVAL
     assert blk(S_q=0) == OK                         # empty block mask, no launch
     assert blk(S_k=0, ld=4) == OK
+
+
+def test_decode_window_rejects_bad_arguments():
+    """attn_decode_paged_window: window_left >= -1, and otherwise the checks of
+    attn_decode_paged (host-side, before any device call)."""
+    lib = _lib()
+    INVAL = 1
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_decode_paged_window.argtypes = [vp] * 6 + [i, vp, vp] + [i] * 6 + [f, i, i, vp, sz, vp]
+    lens = np.array([10, 40], np.int32)
+    lp = lens.ctypes.data_as(ctypes.c_void_p)
+    odd8 = ctypes.c_void_p(4096 + 8)
+    call = lambda wl, q=P, kc=P: lib.attn_decode_paged_window(q, kc, P, P, P, lp, 16, P, P, 2, 8, 2, 128, 3, 6, 0.1,
+                                                              wl, 1, P, 1 << 30, None)
+    assert call(-2) == INVAL
+    assert call(-7) == INVAL
+    assert call(4, q=odd8) == INVAL and call(4, kc=odd8) == INVAL
+    assert lib.attn_decode_paged_window(P, P, P, P, P, lp, 16, P, P, 2, 8, 3, 128, 3, 6, 0.1, 4, 1, P, 1 << 30,
+                                        None) == INVAL   # A % A_kv

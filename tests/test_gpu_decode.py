@@ -27,7 +27,7 @@ def orc():
     return oracle.default()
 
 
-def run_decode(ea, p, k_cache=None, v_cache=None, block_table=None):
+def run_decode(ea, p, k_cache=None, v_cache=None, block_table=None, window_left=None):
     t = gu.torch()
     q = gu.dev(p.q, "bf16")
     kc = gu.dev(p.k_cache if k_cache is None else k_cache, "bf16")
@@ -41,7 +41,10 @@ def run_decode(ea, p, k_cache=None, v_cache=None, block_table=None):
     nbytes = ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens)
     ws = t.empty(max(nbytes, 1), dtype=t.uint8, device="cuda")
     ws.fill_(0xFF)  # stale contents must not matter
-    ea.attn_decode_paged(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale)
+    if window_left is None:
+        ea.attn_decode_paged(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale)
+    else:
+        ea.attn_decode_paged_window(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale, window_left=window_left)
     t.cuda.synchronize()
     return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
 
@@ -196,3 +199,64 @@ def test_decode_fp8_full_size_sampled(ea, orc):
     o_ref, l_ref = orc.decode_paged_fp8(pf.base.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale,
                                         pf.base.block_table, lens, scale=pf.base.scale, seqs=seqs)
     _say(gu.check(o[seqs], lse[seqs], o_ref, l_ref, "bf16", "fp8 full size"))
+
+
+WINDOW_CASES = [
+    # lens, A, A_kv, d, page_size, window_left
+    ([1, 15, 16, 17, 33, 0, 500, 1000], 8, 2, 128, 16, 0),      # the query alone
+    ([1, 15, 16, 17, 33, 0, 500, 1000], 8, 2, 128, 16, 16),     # window edge on a chunk boundary for len 17, 33
+    ([64, 65, 3000, 129], 4, 4, 128, 16, 100),                  # edge inside a chunk
+    ([5, 77, 1025], 16, 1, 64, 32, 40),
+    ([2000, 1, 31, 4097], 32, 8, 128, 16, 1023),
+    ([700, 3, 2049], 32, 1, 128, 16, 511),                      # MQA column groups
+    ([1200, 5, 640], 32, 2, 128, 16, 200),                      # one-wave workgroups
+    ([300, 400], 8, 2, 128, 16, 5000),                          # window past the first token: every key
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: f"{len(c[0])}seq-A{c[1]}-kv{c[2]}-d{c[3]}-ps{c[4]}-w{c[5]}")
+def test_decode_window(ea, orc, case):
+    """Sliding-window decode ("Attention Kernel", 可编程 mask) against the
+    oracle's decode under the same window."""
+    lens, A, A_kv, d, ps, w = case
+    _say("decode window", case)
+    p = gen.make_paged(lens, A, A_kv, d, ps, dtype="bf16", seed=len(lens) * 100 + A + w, extra_pages=3)
+    o, lse = run_decode(ea, p, window_left=w)
+    o_ref, l_ref = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="bf16",
+                                    scale=p.scale, window_left=w)
+    gu.check(o, lse, o_ref, l_ref, "bf16", str(case))
+
+
+def test_decode_window_edges(ea):
+    """Window -1 is attn_decode_paged bit for bit; a window reaching the first
+    token of every sequence reads the same chunks and gives the same bits;
+    window 0 returns the last token's value row (the weight is exactly 1)."""
+    lens = [700, 33, 1500, 16, 1]
+    _say("decode window edges", lens)
+    p = gen.make_paged(lens, 8, 2, 128, 16, dtype="bf16", seed=93)
+    o0, l0 = run_decode(ea, p)
+    o1, l1 = run_decode(ea, p, window_left=-1)
+    o2, l2 = run_decode(ea, p, window_left=max(lens))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    assert np.array_equal(o0, o2) and np.array_equal(l0, l2)
+    o3, _ = run_decode(ea, p, window_left=0)
+    vf = gen.bf16_bits_to_f32(p.v_cache).astype(np.float64)
+    for b, n in enumerate(lens):
+        last = vf[p.block_table[b, (n - 1) // 16], (n - 1) % 16]  # [A_kv, d]
+        for h in range(p.A):
+            assert np.array_equal(o3[b, h], last[h // (p.A // p.A_kv)]), (b, h)
+
+
+def test_config4_window_full_size_sampled(ea, orc):
+    """The decode workload with a 4096-token window, sampled rows."""
+    _say("config 4 paged decode, 4096-token window (sampled rows)")
+    p = gen.make_config(4)
+    o, lse = run_decode(ea, p, window_left=4095)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([rng.choice(p.B * p.A, size=64, replace=False),
+                                     [int(np.argmax(p.seq_lens)) * p.A, int(np.argmin(p.seq_lens)) * p.A + 3]]))
+    o_ref, l_ref = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="bf16",
+                                    scale=p.scale, rows=rows, window_left=4095)
+    stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "config4 window")
+    _say("config 4 window", stats)
