@@ -146,8 +146,23 @@ class Oracle:
         return o, lse
 
     def attn_fwd_varlen(self, q, k, v, cu_seqlens, *, dtype, scale, causal=True, q_keep=None,
-                        k_keep=None, rows=None):
-        """Packed varlen attention.  q [A,T,d], k/v [A_kv,T,d]; rows = h*T + t."""
+                        k_keep=None, rows=None, bias=None, block_keep=None, window=None):
+        """Packed varlen attention.  q [A,T,d], k/v [A_kv,T,d]; rows = h*T + t.
+
+        bias: fp32 [1 or A, T, ld] -- row t (token i of its sequence) holds the
+        additive term of its keys j < len at columns j (positions within the
+        sequence); block_keep: uint8 [n_seq, 1 or A, nb, nb], nb = ceil(longest
+        length / 128), the 128 x 128 block flags of each sequence's own
+        (row, key) grid; window: (left, right) around each row's position in
+        its sequence.  With any of these, each sequence is its own dense problem
+        ("Attention Kernel", Paged 与 ragged KV: packed sequences never attend
+        across boundaries) and goes through attn_fwd with its slices."""
+        if bias is not None or block_keep is not None or window is not None:
+            if rows is not None:
+                raise ValueError("rows are not taken with bias / block_keep / window")
+            return self._varlen_by_sequence(q, k, v, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
+                                            q_keep=q_keep, k_keep=k_keep, bias=bias, block_keep=block_keep,
+                                            window=window)
         q, k, v = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype)
         if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape != v.shape:
             raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
@@ -170,6 +185,47 @@ class Oracle:
             raise ValueError("oracle_attn_fwd_varlen rejected its arguments")
         if r is None:
             return o.reshape(A, T, d), lse.reshape(A, T)
+        return o, lse
+
+    def _varlen_by_sequence(self, q, k, v, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, bias, block_keep,
+                            window):
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        A, T, d = q.shape
+        n_seq = cu.size - 1
+        lens = np.diff(cu)
+        nb = int((lens.max() + 127) // 128) if n_seq else 0
+        if bias is not None:
+            bias = np.asarray(bias, dtype=np.float32)
+            if bias.ndim != 3 or bias.shape[0] not in (1, A) or bias.shape[1] != T or bias.shape[2] < lens.max(initial=0):
+                raise ValueError("bias must be [1 or A, T, ld >= longest length]")
+        if block_keep is not None:
+            block_keep = np.asarray(block_keep, dtype=np.uint8)
+            if block_keep.ndim != 4 or block_keep.shape[0] != n_seq or block_keep.shape[1] not in (1, A) or \
+                    block_keep.shape[2:] != (nb, nb):
+                raise ValueError(f"block_keep must be [n_seq, 1 or A, {nb}, {nb}]")
+        o = np.zeros((A, T, d), dtype=np.float64)
+        lse = np.full((A, T), -np.inf, dtype=np.float64)
+        for s in range(n_seq):
+            s0, s1 = int(cu[s]), int(cu[s + 1])
+            L = s1 - s0
+            if L == 0:
+                continue
+            kw = {}
+            if q_keep is not None:
+                kw["q_keep"] = np.asarray(q_keep).reshape(T)[s0:s1][None]
+            if k_keep is not None:
+                kw["k_keep"] = np.asarray(k_keep).reshape(T)[s0:s1][None]
+            if window is not None:
+                kw["m_keep"] = window_keep(1, L, L, int(window[0]), int(window[1]))
+            if bias is not None:
+                kw["bias"] = bias[:, s0:s1, :L][None]
+            if block_keep is not None:
+                nbs = (L + 127) // 128
+                kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]
+            os_, ls_ = self.attn_fwd(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], dtype=dtype,
+                                     scale=scale, causal=causal, **kw)
+            o[:, s0:s1] = os_[0]
+            lse[:, s0:s1] = ls_[0]
         return o, lse
 
     def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None,

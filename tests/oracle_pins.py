@@ -969,6 +969,57 @@ def pin_decode_window_closed_forms(orc):
     assert np.array_equal(on, ow) and np.array_equal(ln, lw)
 
 
+def pin_varlen_masks_brute_force(orc):
+    """Packed sequences with a per-token additive term, per-sequence block
+    masks and a window, against a direct fp64 softmax of each sequence's own
+    score matrix (tiny sizes; the term's row t and column j are token t and the
+    key at position j of t's sequence; block (qb, kb) of sequence s covers its
+    rows and keys 128 qb.., 128 kb..)."""
+    rng = np.random.default_rng(68)
+    lens = [130, 0, 200, 7]
+    A, A_kv, d, scale = 2, 1, 4, 0.625   # (a float32 value: the oracle takes the scale as float)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, nb = int(cu[-1]), 2
+    q = _f32(rng.standard_normal((A, T, d)))
+    k = _f32(rng.standard_normal((A_kv, T, d)))
+    v = _f32(rng.standard_normal((A_kv, T, d)))
+    bias = _f32(rng.standard_normal((A, T, 204)))
+    bias[rng.random(bias.shape) < 0.1] = -np.inf
+    bk = (rng.random((len(lens), A, nb, nb)) < 0.7).astype(np.uint8)
+    bk[0, :, 1, 0] = 1
+    for causal, window in ((True, None), (False, (50, 20)), (True, (90, -1))):
+        o, lse = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=scale, causal=causal, bias=bias,
+                                     block_keep=bk, window=window)
+        for s, L in enumerate(lens):
+            s0 = int(cu[s])
+            for h in range(A):
+                qq = q[h, s0:s0 + L].astype(np.float64)
+                kk = k[h // (A // A_kv), s0:s0 + L].astype(np.float64)
+                vv = v[h // (A // A_kv), s0:s0 + L].astype(np.float64)
+                sc = scale * qq @ kk.T + bias[h, s0:s0 + L, :L].astype(np.float64)
+                i = np.arange(L)[:, None]
+                j = np.arange(L)[None, :]
+                keep = bk[s, h][i // 128, j // 128] != 0
+                if causal:
+                    keep &= j <= i
+                if window is not None:
+                    if window[0] >= 0:
+                        keep &= j >= i - window[0]
+                    if window[1] >= 0:
+                        keep &= j <= i + window[1]
+                sc = np.where(keep, sc, -np.inf)
+                for r in range(L):
+                    row = sc[r]
+                    if not np.isfinite(row).any():
+                        assert np.all(o[h, s0 + r] == 0) and np.isneginf(lse[h, s0 + r])
+                        continue
+                    m = row[np.isfinite(row)].max()
+                    e = np.exp(row - m)
+                    want = e @ vv / e.sum()
+                    assert np.allclose(o[h, s0 + r], want, rtol=0, atol=1e-12), (s, h, r)
+                    assert abs(lse[h, s0 + r] - (m + math.log(e.sum()))) < 1e-12
+
+
 def pin_prefill_paged_identity_is_varlen(orc):
     """With pages laid out in order and each whole sequence as its chunk, the
     paged prefill is the packed varlen prefill, bit for bit."""

@@ -106,6 +106,14 @@ PY_MUTANTS = [
     ("window: left edge off by one", "keep &= j >= i - left", "keep &= j > i - left", 0),
     ("window: aligned top-left", "off = S_k - S_q\n    i = np.arange(S_q, dtype=np.int64)[:, None] + off",
      "off = 0\n    i = np.arange(S_q, dtype=np.int64)[:, None] + off", 0),
+    ("varlen term rows not offset to the sequence", 'kw["bias"] = bias[:, s0:s1, :L][None]',
+     'kw["bias"] = bias[:, 0:L, :L][None]', 0),
+    ("varlen term columns offset to the sequence", 'kw["bias"] = bias[:, s0:s1, :L][None]',
+     'kw["bias"] = bias[:, s0:s1, s0:s0 + L][None]', 0),
+    ("varlen block mask of the first sequence", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
+     'kw["block_keep"] = block_keep[0][None, :, :nbs, :nbs]', 0),
+    ("varlen block mask transposed", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
+     'kw["block_keep"] = np.ascontiguousarray(block_keep[s][None, :, :nbs, :nbs].transpose(0, 1, 3, 2))', 0),
 ]
 
 BATTERY = r"""
