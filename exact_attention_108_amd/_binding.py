@@ -289,9 +289,12 @@ def attn_block_keep_from_bias(bias, block_keep, *, stream=None):
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: float, causal: bool = True,
-                    q_keep=None, k_keep=None, window=None, stream=None):
+                    q_keep=None, k_keep=None, window=None, block_keep=None, bias=None, stream=None):
     """Packed varlen prefill.  q/o [A,T,d], k/v [A_kv,T,d], lse [A,T]; cu_seqlens int32 device,
-    cu_seqlens_host the same values on the host (numpy int32)."""
+    cu_seqlens_host the same values on the host (numpy int32).  bf16 only: block_keep uint8
+    [n_seq, 1 or A, nb, nb] (nb = ceil(longest length / 128)), each sequence's own 128 x 128 blocks;
+    bias fp32 [1 or A, T, L] (L = the longest length; row t = token t against the keys at positions
+    j < len of its sequence; rows unit-stride and a multiple of 4 elements apart)."""
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
         raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
@@ -308,10 +311,24 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: floa
     for t in (q_keep, k_keep):
         if t is not None and t.shape != (T,):
             raise ValueError("keep-masks must be [T]")
-    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep)
+    max_len = int(np.diff(cu_host).max()) if n_seq > 0 else 0
+    nb = (max_len + 127) // 128
+    if block_keep is not None and (block_keep.dim() != 4 or block_keep.shape[0] != n_seq or
+                                   block_keep.shape[1] not in (1, A) or tuple(block_keep.shape[2:]) != (nb, nb)):
+        raise ValueError(f"block_keep must be [n_seq, 1 or A, {nb}, {nb}]")
+    bh, ld = 0, 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.dim() != 3 or bias.shape[0] not in (1, A) or \
+                tuple(bias.shape[1:]) != (T, max_len):
+            raise ValueError(f"bias must be fp32 [1 or A, T, {max_len}]")
+        bh, ld = int(bias.shape[0]), int(bias.stride(1))
+        if (max_len > 1 and bias.stride(2) != 1) or ld % 4 or ld < max_len or (bh > 1 and bias.stride(0) != T * ld):
+            raise ValueError("bias rows must be unit-stride, a multiple of 4 elements apart, heads packed")
+    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep, block_keep, bias)
     st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                               cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d, float(scale), int(bool(causal)),
-                              _mask(q_keep, k_keep), _window(window), _dtype_code(q), _stream(stream, dev))
+                              _mask(q_keep, k_keep, block_keep, bias, bh, ld), _window(window), _dtype_code(q),
+                              _stream(stream, dev))
     _check(st, "attn_fwd_varlen")
 
 

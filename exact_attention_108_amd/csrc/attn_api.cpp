@@ -72,6 +72,9 @@ bool valid_bias(const float* bias, int heads, int A, int S_q, int S_k, int ld) {
   (void)S_q;
   return true;
 }
+// the bf16 kernels read a workgroup's 128 rows of terms through one buffer
+// resource, whose byte range is 32 bits
+bool bias_rows_fit(int ld) { return (long long)attn::kPrefillRows * ld * 4 < (1LL << 32); }
 
 // dtype / head-dim combinations the kernels are built for
 attn_status check_prefill_support(attn_dtype dtype, int d_h) {
@@ -104,6 +107,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   }
   const bool bias = mask && mask->bias;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if (bias && dtype == ATTN_BF16 && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   if (S_q == 0) return ATTN_OK;
   const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
   const long long n_qt = (S_q + rows - 1) / rows;
@@ -192,9 +196,19 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   for (const void* t : {q, k, v, (const void*)o})
     if (!aligned(t, data_align(dtype))) return ATTN_ERR_INVAL;
   if (!aligned(lse, 4) || !aligned(cu_seqlens, 4)) return ATTN_ERR_INVAL;
-  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // dense attn_fwd only
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
+  int max_len = 0;
+  for (int s = 0; s < n_seq; ++s) max_len = std::max(max_len, cu_seqlens_host[s + 1] - cu_seqlens_host[s]);
+  // block masks [n_seq, block_heads, nb, nb] (nb = ceil(max_len / 128)) and
+  // terms [bias_heads, T, bias_ld] (row t: keys at positions of t's sequence)
+  const bool blocks = mask && mask->block_keep;
+  const bool bias = mask && mask->bias;
+  if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
+  if (bias && !valid_bias(mask->bias, mask->bias_heads, A, max_len, max_len, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if ((blocks || bias) && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (blocks && max_len > 262144) return ATTN_ERR_UNSUPPORTED;
+  if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;
   if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
@@ -207,8 +221,6 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
     if (nt > max_tiles) max_tiles = nt;
   }
   if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
-  int max_len = 0;
-  for (int s = 0; s < n_seq; ++s) max_len = std::max(max_len, cu_seqlens_host[s + 1] - cu_seqlens_host[s]);
   if (!window_arith_fits(window, max_len, max_len)) return ATTN_ERR_UNSUPPORTED;
   attn::FwdParams p = base_params(q, k, v, o, lse, A, A_kv, d_h, scale, causal, mask, window, max_len, max_len);
   p.cu_seqlens = cu_seqlens;
@@ -217,6 +229,17 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   p.B = 1;
   p.n_qt = max_tiles;
   p.total_tiles = (int)total_tiles;
+  if (blocks) {
+    p.block_keep = mask->block_keep;
+    p.block_heads = mask->block_heads;
+    p.n_kb = max_tiles;  // bf16 row tiles are 128 rows: nb = max_tiles
+  }
+  if (bias) {
+    p.bias = mask->bias;
+    p.bias_heads = mask->bias_heads;
+    p.bias_ld = mask->bias_ld;
+    p.inv_scale = (float)(1.0 / (double)scale);
+  }
   if (dtype == ATTN_BF16) attn::plan_varlen_order(p);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, true, st) : attn::launch_prefill_f32(p, true, st);

@@ -523,7 +523,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   if constexpr (kBias) {
     const int hm = p.bias_heads == 1 ? 0 : rb.h;
     const int rows = min(kRows, S_q - rb.q0);
-    const float* plane = p.bias + ((size_t)(rb.b * p.bias_heads + hm) * S_q + rb.q0) * p.bias_ld;
+    // dense [B, heads, S_q, ld]; packed [heads, T, ld] (row t: token t of its sequence)
+    const float* plane = kVarlen ? p.bias + ((size_t)hm * p.T + rb.t0 + rb.q0) * p.bias_ld
+                                 : p.bias + ((size_t)(rb.b * p.bias_heads + hm) * S_q + rb.q0) * p.bias_ld;
     const uint32_t nbytes = ((uint32_t)(rows - 1) * p.bias_ld + S_k) * 4u;
     bias_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)plane, 0, (int)nbytes, 0x00020000);
     bias_voff = ((uint32_t)(qrow - rb.q0) * p.bias_ld + 4 * g) * 4u;
@@ -938,6 +940,12 @@ hipError_t launch_d(const FwdParams& p, bool varlen, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else if (!varlen && p.block_keep) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (varlen && p.bias && p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (varlen && p.bias) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (varlen && p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else if (varlen) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else {

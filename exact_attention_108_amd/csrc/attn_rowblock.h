@@ -16,7 +16,8 @@ struct RowBlock {
   const uint8_t* k_keep;  // or null
   int S_q, S_k;
   int q0;                 // first query row of this workgroup
-  int b, h, qt;           // dense: batch, head and query tile of this workgroup
+  int b, h, qt;           // batch (packed: sequence), head and query tile of this workgroup
+  int t0;                 // packed: the sequence's first token (dense: 0)
 };
 
 // Dense batch: query tile index descending (heaviest causal tiles first),
@@ -58,6 +59,7 @@ __device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_byte
   r.b = b;
   r.h = h;
   r.qt = qt;
+  r.t0 = 0;
   return r;
 }
 
@@ -140,9 +142,10 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
   r.S_q = len;
   r.S_k = len;
   r.q0 = t_u * kRows;
-  r.b = 0;
+  r.b = seq;
   r.h = h;
   r.qt = t_u;
+  r.t0 = start;
   if (seq_out) *seq_out = seq;
   if (head_out) *head_out = h;
   return true;

@@ -71,17 +71,21 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 /* Optional keep-masks (uint8, 1 = keep, 0 = mask to -inf); any may be NULL.
  * Layout: attn_fwd q_keep [B, S_q], k_keep [B, S_k]; attn_fwd_varlen [T].
  *
- * block_keep (attn_fwd only, bf16): block sparsity (page "Attention Kernel",
+ * block_keep (bf16): block sparsity (page "Attention Kernel",
  * section "可编程 mask": the block level decides which tiles are skipped
  * whole).  uint8 [B, block_heads, ceil(S_q / 128), ceil(S_k / 128)];
  * block_keep[b][h'][i][j] = 0 masks every (row, key) pair with row in
  * [128 i, 128 i + 128) and key in [128 j, 128 j + 128) (h' = 0 when
  * block_heads == 1, else the query head); those key tiles are never loaded.
  * block_heads is 1 or A (ignored when block_keep is NULL).  Requires
- * S_k <= 262144.  attn_fwd and attn_bwd take it; the packed and paged entry
- * points return ATTN_ERR_UNSUPPORTED for a non-NULL block_keep.
+ * S_k <= 262144.  attn_fwd, attn_fwd_varlen and attn_bwd take it; the
+ * paged entry points and attn_bwd_varlen return ATTN_ERR_UNSUPPORTED for a
+ * non-NULL block_keep.  attn_fwd_varlen: uint8 [n_seq, block_heads, nb, nb]
+ * with nb = ceil(longest sequence / 128); entry [s][h'][i][j] is block (i, j)
+ * of sequence s's own rows and keys (positions within the sequence); entries
+ * past a shorter sequence's blocks are never read.
  *
- * bias (attn_fwd only): the general dense additive mask M of the operation
+ * bias: the general dense additive mask M of the operation
  * (page "Attention Kernel", section "可编程 mask"; the term "+ M" of section
  * "问题与成本").  fp32 [B, bias_heads, S_q, bias_ld], row (b, h', i) holding
  * M_ij for keys j < S_k (h' = 0 when bias_heads == 1, else the query head).
@@ -97,10 +101,15 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * the contract.  (The kernels scale scores to base 2 in fp32, where a term
  * below -FLT_MAX * c has no finite representation.)
  * Requires bias_heads in {1, A}, bias_ld >= S_k and a multiple of 4, and
- * bias 16-byte aligned.  It combines with every other mask; key tiles are
- * skipped only through block_keep, which attn_block_keep_from_bias derives
- * from a bias.  attn_fwd and attn_bwd take it; the packed entry points
- * return ATTN_ERR_UNSUPPORTED for a non-NULL bias. */
+ * bias 16-byte aligned; bf16 calls also need 128 * bias_ld * 4 < 2^32
+ * (ATTN_ERR_UNSUPPORTED otherwise).  It combines with every other mask; key
+ * tiles are skipped only through block_keep, which attn_block_keep_from_bias
+ * derives from a bias.  attn_fwd, attn_fwd_varlen (bf16) and attn_bwd take
+ * it; the paged entry points and attn_bwd_varlen return ATTN_ERR_UNSUPPORTED
+ * for a non-NULL bias.  attn_fwd_varlen: fp32 [bias_heads, T, bias_ld], row
+ * (h', t) holding M for token t (position i in its sequence) against the
+ * keys at positions j < len of the same sequence (bias_ld >= the longest
+ * sequence). */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
@@ -190,10 +199,12 @@ attn_status attn_block_keep_from_bias(const float *bias, int B, int bias_heads, 
  *   cu_seqlens      : device int32 [n_seq + 1], cu[0] = 0, non-decreasing,
  *                     cu[n_seq] = T (= total_tokens); empty sequences allowed
  *   cu_seqlens_host : host copy of the same values (used for launch planning)
- *   mask            : NULL or q_keep [T], k_keep [T]
+ *   mask            : NULL or q_keep [T], k_keep [T]; bf16 also a block mask
+ *                     [n_seq, block_heads, nb, nb] and an additive term
+ *                     [bias_heads, T, bias_ld] per sequence (see attn_mask)
  *   window          : NULL or a sliding window (positions within a sequence)
  *
- * Supported: as attn_fwd.
+ * Supported: as attn_fwd (block masks and terms: bf16 only).
  */
 attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                             const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,

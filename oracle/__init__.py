@@ -158,11 +158,9 @@ class Oracle:
         ("Attention Kernel", Paged 与 ragged KV: packed sequences never attend
         across boundaries) and goes through attn_fwd with its slices."""
         if bias is not None or block_keep is not None or window is not None:
-            if rows is not None:
-                raise ValueError("rows are not taken with bias / block_keep / window")
             return self._varlen_by_sequence(q, k, v, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
                                             q_keep=q_keep, k_keep=k_keep, bias=bias, block_keep=block_keep,
-                                            window=window)
+                                            window=window, rows=rows)
         q, k, v = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype)
         if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape != v.shape:
             raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
@@ -188,7 +186,7 @@ class Oracle:
         return o, lse
 
     def _varlen_by_sequence(self, q, k, v, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, bias, block_keep,
-                            window):
+                            window, rows=None):
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         A, T, d = q.shape
         n_seq = cu.size - 1
@@ -205,12 +203,21 @@ class Oracle:
                 raise ValueError(f"block_keep must be [n_seq, 1 or A, {nb}, {nb}]")
         o = np.zeros((A, T, d), dtype=np.float64)
         lse = np.full((A, T), -np.inf, dtype=np.float64)
+        want = None
+        if rows is not None:  # flattened ids h*T + t: only those rows are formed
+            r = np.asarray(rows, dtype=np.int64).reshape(-1)
+            want = (r // T, r % T)
         for s in range(n_seq):
             s0, s1 = int(cu[s]), int(cu[s + 1])
             L = s1 - s0
             if L == 0:
                 continue
             kw = {}
+            if want is not None:
+                sel = (want[1] >= s0) & (want[1] < s1)
+                if not sel.any():
+                    continue
+                kw["rows"] = want[0][sel] * L + (want[1][sel] - s0)   # (b = 0, h, i) of the one-sequence call
             if q_keep is not None:
                 kw["q_keep"] = np.asarray(q_keep).reshape(T)[s0:s1][None]
             if k_keep is not None:
@@ -224,8 +231,14 @@ class Oracle:
                 kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]
             os_, ls_ = self.attn_fwd(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], dtype=dtype,
                                      scale=scale, causal=causal, **kw)
-            o[:, s0:s1] = os_[0]
-            lse[:, s0:s1] = ls_[0]
+            if want is not None:
+                o[want[0][sel], want[1][sel]] = os_
+                lse[want[0][sel], want[1][sel]] = ls_
+            else:
+                o[:, s0:s1] = os_[0]
+                lse[:, s0:s1] = ls_[0]
+        if want is not None:
+            return o[want], lse[want]
         return o, lse
 
     def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None,

@@ -990,6 +990,10 @@ def pin_varlen_masks_brute_force(orc):
     for causal, window in ((True, None), (False, (50, 20)), (True, (90, -1))):
         o, lse = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=scale, causal=causal, bias=bias,
                                      block_keep=bk, window=window)
+        ids = np.array([0 * T + 3, 1 * T + 140, 0 * T + T - 1, 1 * T + 131], np.int64)
+        o_r, l_r = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=scale, causal=causal, bias=bias,
+                                       block_keep=bk, window=window, rows=ids)
+        assert np.array_equal(o_r, o.reshape(-1, d)[ids]) and np.array_equal(l_r, lse.reshape(-1)[ids])
         for s, L in enumerate(lens):
             s0 = int(cu[s])
             for h in range(A):

@@ -697,3 +697,115 @@ def test_block_sparse_longest_key_range(ea, orc):
     o, lse = run_block_sparse(ea, p, bk)
     assert np.all(np.isneginf(lse[:, :, 128:])) and np.all(o[:, :, 128:] == 0)
     check_block_sparse(orc, p, bk, o, lse, "block sparse longest range")
+
+
+# ---------------------------------------------------------------- packed sequences with block masks and terms
+def _varlen_term(rng, A_heads, T, L, p_inf=0.1):
+    """fp32 [heads, T, L] term: N(0, 1/2) with a fraction of -inf entries."""
+    b = (0.5 * rng.standard_normal((A_heads, T, L))).astype(np.float32)
+    b[rng.random(b.shape) < p_inf] = -np.inf
+    return b
+
+
+def run_varlen_masks(ea, p, *, bias_np=None, bk_np=None, window=None, k_keep=None):
+    t = gu.torch()
+    q, k, v = gu.dev(p.q, p.dtype), gu.dev(p.k, p.dtype), gu.dev(p.v, p.dtype)
+    o = gu.empty_out(q.shape, p.dtype)
+    lse = t.empty((p.A, p.T), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    cu = gu.dev(p.cu_seqlens, "i32")
+    bias = None
+    if bias_np is not None:
+        H, T, L = bias_np.shape
+        ld = max(4, (L + 3) // 4 * 4)
+        full = t.full((H, T, ld), float("nan"), dtype=t.float32, device="cuda")   # padding is never used
+        full[..., :L] = t.from_numpy(bias_np).cuda()
+        bias = full[..., :L]
+    bk = None if bk_np is None else t.from_numpy(bk_np).cuda()
+    qk = None if p.q_keep is None else gu.dev(p.q_keep, "u8")
+    kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    ea.attn_fwd_varlen(q, k, v, o, lse, cu, p.cu_seqlens, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk,
+                       window=window, block_keep=bk, bias=bias)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+VARLEN_MASK_CASES = [
+    # lens, A, A_kv, d, causal, window, term heads (0 = none), block heads (0 = none), keep masks
+    ([1, 0, 130, 17, 256, 0, 64, 300, 5], 4, 2, 128, True, None, 1, 0, False),
+    ([300, 129, 7], 4, 4, 64, False, None, 4, 4, True),
+    ([500, 40, 260], 8, 2, 128, True, (100, -1), 0, 1, False),
+    ([257, 0, 513], 2, 1, 128, True, None, 2, 2, True),
+    ([70, 700], 4, 2, 64, True, None, 1, 1, False),
+    ([129, 384, 1], 4, 1, 128, False, (60, 30), 1, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_MASK_CASES,
+                         ids=lambda c: f"{len(c[0])}seq-A{c[1]}-kv{c[2]}-d{c[3]}-{'c' if c[4] else 'n'}"
+                                       f"-t{c[6]}-b{c[7]}" + ("-keep" if c[8] else "")
+                                       + ("" if c[5] is None else f"-w{c[5][0]}_{c[5][1]}"))
+def test_varlen_block_mask_and_term(ea, orc, case):
+    """Packed sequences with per-sequence block masks [n_seq, heads, nb, nb] and
+    per-token terms [heads, T, longest] ("Attention Kernel", 可编程 mask, over
+    the ragged batches of Paged 与 ragged KV) against the oracle."""
+    lens, A, A_kv, d, causal, window, th, bh, keeps = case
+    _say("varlen block mask + term", case)
+    p = gen.make_varlen(lens, A, A_kv, d, dtype="bf16", causal=causal, seed=sum(lens) + A,
+                        q_mask_frac=0.05 if keeps else 0.0, k_mask_frac=0.1 if keeps else 0.0)
+    rng = np.random.default_rng(sum(lens) + 7)
+    L = max(lens)
+    nb = (L + 127) // 128
+    bias = _varlen_term(rng, th, p.T, L) if th else None
+    if bias is not None and th == 1:
+        bias[0, int(p.cu_seqlens[np.argmax(lens)]) + 3, :] = np.finfo(np.float32).min   # a fully filled row
+    bk = (rng.random((len(lens), bh, nb, nb)) < 0.6).astype(np.uint8) if bh else None
+    k_keep = p.k_keep if keeps else None
+    o, lse = run_varlen_masks(ea, p, bias_np=bias, bk_np=bk, window=window, k_keep=k_keep)
+    o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=causal,
+                                       q_keep=p.q_keep, k_keep=k_keep, bias=bias, block_keep=bk, window=window)
+    gu.check(o, lse, o_ref, l_ref, "bf16", str(case))
+
+
+def test_varlen_masks_one_sequence_is_dense_bitwise(ea):
+    """One packed sequence with a block mask and a term gives the dense call's
+    bits (same arithmetic; only the workgroup-to-tile map differs)."""
+    t = gu.torch()
+    L, A, A_kv, d = 333, 4, 2, 128
+    _say("varlen masks one sequence == dense", L)
+    p = gen.make_varlen([L], A, A_kv, d, dtype="bf16", causal=True, seed=511)
+    rng = np.random.default_rng(512)
+    bias = _varlen_term(rng, A, L, L)
+    bk = (rng.random((1, A, 3, 3)) < 0.7).astype(np.uint8)
+    o1, l1 = run_varlen_masks(ea, p, bias_np=bias, bk_np=bk)
+    q = gu.dev(p.q, "bf16")[None]
+    k = gu.dev(p.k, "bf16")[None]
+    v = gu.dev(p.v, "bf16")[None]
+    o = t.empty_like(q)
+    lse = t.empty((1, A, L), dtype=t.float32, device="cuda")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=True, bias=ea.pad_bias(t.from_numpy(bias[None]).cuda()),
+                block_keep=t.from_numpy(bk).cuda())
+    t.cuda.synchronize()
+    assert np.array_equal(o1, gu.host_f64(o)[0]) and np.array_equal(l1, lse.cpu().numpy()[0].astype(np.float64))
+
+
+def test_config5_block_mask_full_size_sampled(ea, orc):
+    """The varlen workload (16 sequences, A = 16, d = 64) with a seeded block
+    mask per sequence and a per-token term shared by the heads; sampled rows."""
+    _say("config 5 with block mask and term (sampled rows)")
+    p = gen.make_config(5)
+    rng = np.random.default_rng(555)
+    L = int(np.diff(p.cu_seqlens).max())
+    nb = (L + 127) // 128
+    bk = (rng.random((p.n_seq, 1, nb, nb)) < 0.5).astype(np.uint8)
+    for s in range(p.n_seq):
+        np.fill_diagonal(bk[s, 0], 1)
+    bias = _varlen_term(rng, 1, p.T, L, p_inf=0.05)
+    o, lse = run_varlen_masks(ea, p, bias_np=bias, bk_np=bk)
+    rows = np.unique(np.concatenate([rng.choice(p.A * p.T, size=300, replace=False),
+                                     [int(p.cu_seqlens[-1]) - 1, p.T + int(p.cu_seqlens[1])]]))
+    o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=True,
+                                       q_keep=p.q_keep, bias=bias, block_keep=bk, rows=rows)
+    stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "config5 masks")
+    _say("config 5 masks", stats)
