@@ -115,19 +115,38 @@ def test_sweep_varlen(ea, orc, seed):
     A_kv = int(rng.choice([1, 2, 4]))
     A = A_kv * int(rng.choice([1, 2, 4]))
     causal = bool(rng.random() < 0.7)
-    _say("sweep varlen", (seed, lens, A, A_kv, d, causal))
+    # per-sequence block masks, per-token terms and windows on some seeds
+    L = max(lens)
+    nb = (L + 127) // 128
+    bh = int(rng.choice([0, 1, A])) if L > 0 else 0
+    th = int(rng.choice([0, 1, A])) if L > 0 else 0
+    window = None
+    if rng.random() < 0.35:
+        window = (int(rng.choice([-1, rng.integers(0, 300)])), int(rng.choice([-1, rng.integers(0, 300)])))
+    _say("sweep varlen", (seed, lens, A, A_kv, d, causal, "blocks", bh, "term", th, window))
     p = gen.make_varlen(lens, A, A_kv, d, dtype="bf16", causal=causal, seed=5000 + seed, q_mask_frac=0.05,
                         k_mask_frac=0.1)
+    bk = (rng.random((len(lens), bh, nb, nb)) < 0.7).astype(np.uint8) if bh else None
+    bias = None
+    if th:
+        bias = (0.5 * rng.standard_normal((th, p.T, L))).astype(np.float32)
+        bias[rng.random(bias.shape) < 0.05] = -np.inf
     t = gu.torch()
     q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
     o = gu.empty_out(q.shape, "bf16")
     lse = t.empty((A, p.T), dtype=t.float32, device="cuda")
     u8 = lambda x: None if x is None else gu.dev(x, "u8")
+    bias_d = None
+    if bias is not None:
+        ld = max(4, (L + 3) // 4 * 4)
+        full = t.zeros((th, p.T, ld), dtype=t.float32, device="cuda")
+        full[..., :L] = t.from_numpy(bias).cuda()
+        bias_d = full[..., :L]
     ea.attn_fwd_varlen(q, k, v, o, lse, gu.dev(p.cu_seqlens, "i32"), p.cu_seqlens, scale=p.scale, causal=causal,
-                       q_keep=u8(p.q_keep), k_keep=u8(p.k_keep))
+                       q_keep=u8(p.q_keep), k_keep=u8(p.k_keep), window=window, block_keep=u8(bk), bias=bias_d)
     t.cuda.synchronize()
     o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=causal,
-                                       q_keep=p.q_keep, k_keep=p.k_keep)
+                                       q_keep=p.q_keep, k_keep=p.k_keep, bias=bias, block_keep=bk, window=window)
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"varlen {seed}"))
 
 
@@ -139,7 +158,8 @@ def test_sweep_decode(ea, orc, seed):
     A_kv = int(rng.choice([1, 2, 4, 8]))
     A = A_kv * int(rng.choice([1, 2, 4, 8, 16, 32] if A_kv <= 2 else [1, 2, 4, 8, 16]))
     ps = int(rng.choice([16, 32, 64]))
-    _say("sweep decode", (seed, lens, A, A_kv, d, ps))
+    wl = int(rng.choice([-1, rng.integers(0, 2000)])) if rng.random() < 0.5 else None
+    _say("sweep decode", (seed, lens, A, A_kv, d, ps, "window", wl))
     p = gen.make_paged(lens, A, A_kv, d, ps, dtype="bf16", seed=6000 + seed, extra_pages=3)
     t = gu.torch()
     q = gu.dev(p.q, "bf16")
@@ -147,11 +167,15 @@ def test_sweep_decode(ea, orc, seed):
     lse = t.empty((p.B, A), dtype=t.float32, device="cuda")
     nbytes = ea.attn_decode_paged_workspace_bytes(p.B, A, A_kv, d, ps, p.seq_lens)
     ws = t.empty(max(nbytes, 1), dtype=t.uint8, device="cuda")
-    ea.attn_decode_paged(q, gu.dev(p.k_cache, "bf16"), gu.dev(p.v_cache, "bf16"), gu.dev(p.block_table, "i32"),
-                         gu.dev(p.seq_lens, "i32"), p.seq_lens, o, lse, ws, scale=p.scale)
+    args = (q, gu.dev(p.k_cache, "bf16"), gu.dev(p.v_cache, "bf16"), gu.dev(p.block_table, "i32"),
+            gu.dev(p.seq_lens, "i32"), p.seq_lens, o, lse, ws)
+    if wl is None:
+        ea.attn_decode_paged(*args, scale=p.scale)
+    else:
+        ea.attn_decode_paged_window(*args, scale=p.scale, window_left=wl)
     t.cuda.synchronize()
     o_ref, l_ref = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="bf16",
-                                    scale=p.scale)
+                                    scale=p.scale, window_left=wl)
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"decode {seed}"))
 
 
