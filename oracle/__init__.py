@@ -295,12 +295,25 @@ class Oracle:
         return dq, dk, dv
 
     def prefill_paged(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal=True,
-                      window=None, rows=None):
+                      window=None, rows=None, bias=None, block_keep=None):
         """Query chunks over a paged cache: q [A,T_q,d] packed chunks (cu_seqlens_q
         [n_seq+1]); caches [P, page_size, A_kv, d]; block_table [n_seq, max_pages];
         seq_lens [n_seq] (chunk included).  Chunk row i of sequence s sits at
         position seq_lens[s] - q_s + i.  Returns (o [A,T_q,d], lse [A,T_q]) in
-        fp64, or [n,d] / [n] for the flattened ids ``rows`` = h*T_q + r."""
+        fp64, or [n,d] / [n] for the flattened ids ``rows`` = h*T_q + r.
+
+        bias: fp32 [1 or A, T_q, ld] -- row t (a chunk token) holds the term of
+        the keys at positions j < seq_lens of its sequence; block_keep: uint8
+        [n_seq, 1 or A, ceil(longest chunk/128), ceil(longest seq_lens/128)] over
+        (chunk row, key position).  With either, each sequence's keys are
+        gathered token by token through its block table (token t: row t %
+        page_size of page block_table[s][t // page_size]) and the chunk is the
+        dense problem of its rows against them ("Attention Kernel", Paged 与
+        ragged KV and 可编程 mask)."""
+        if bias is not None or block_keep is not None:
+            return self._paged_by_sequence(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, dtype=dtype,
+                                           scale=scale, causal=causal, window=window, rows=rows, bias=bias,
+                                           block_keep=block_keep)
         q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
         if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
             raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
@@ -326,6 +339,65 @@ class Oracle:
             raise ValueError("oracle_prefill_paged rejected its arguments")
         if r is None:
             return o.reshape(A, T_q, d), lse.reshape(A, T_q)
+        return o, lse
+
+    def _paged_by_sequence(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal,
+                           window, rows, bias, block_keep):
+        A, T_q, d = q.shape
+        page_size, A_kv = k_cache.shape[1], k_cache.shape[2]
+        cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+        sl = np.asarray(seq_lens, dtype=np.int64)
+        bt = np.asarray(block_table)
+        n_seq = cu.size - 1
+        qlens = np.diff(cu)
+        nqb = int((qlens.max(initial=0) + 127) // 128)
+        nkb = int((sl.max(initial=0) + 127) // 128)
+        if bias is not None:
+            bias = np.asarray(bias, dtype=np.float32)
+            if bias.ndim != 3 or bias.shape[0] not in (1, A) or bias.shape[1] != T_q or bias.shape[2] < sl.max(initial=0):
+                raise ValueError("bias must be [1 or A, T_q, ld >= longest seq_lens]")
+        if block_keep is not None:
+            block_keep = np.asarray(block_keep, dtype=np.uint8)
+            if block_keep.ndim != 4 or block_keep.shape[0] != n_seq or block_keep.shape[1] not in (1, A) or \
+                    block_keep.shape[2:] != (nqb, nkb):
+                raise ValueError(f"block_keep must be [n_seq, 1 or A, {nqb}, {nkb}]")
+        o = np.zeros((A, T_q, d), dtype=np.float64)
+        lse = np.full((A, T_q), -np.inf, dtype=np.float64)
+        want = None
+        if rows is not None:
+            r = np.asarray(rows, dtype=np.int64).reshape(-1)
+            want = (r // T_q, r % T_q)
+        for s in range(n_seq):
+            s0, s1, L = int(cu[s]), int(cu[s + 1]), int(sl[s])
+            ql = s1 - s0
+            if ql == 0:
+                continue
+            kw = {}
+            if want is not None:
+                sel = (want[1] >= s0) & (want[1] < s1)
+                if not sel.any():
+                    continue
+                kw["rows"] = want[0][sel] * ql + (want[1][sel] - s0)
+            pages = bt[s, np.arange(L) // page_size]
+            offs = np.arange(L) % page_size
+            ks = np.ascontiguousarray(np.asarray(k_cache)[pages, offs].transpose(1, 0, 2))   # [A_kv, L, d]
+            vs = np.ascontiguousarray(np.asarray(v_cache)[pages, offs].transpose(1, 0, 2))
+            if window is not None:
+                kw["m_keep"] = window_keep(1, ql, L, int(window[0]), int(window[1]))
+            if bias is not None:
+                kw["bias"] = bias[:, s0:s1, :L][None]
+            if block_keep is not None:
+                kw["block_keep"] = block_keep[s][None, :, :(ql + 127) // 128, :(L + 127) // 128]
+            os_, ls_ = self.attn_fwd(q[None, :, s0:s1], ks[None], vs[None], dtype=dtype, scale=scale, causal=causal,
+                                     **kw)
+            if want is not None:
+                o[want[0][sel], want[1][sel]] = os_
+                lse[want[0][sel], want[1][sel]] = ls_
+            else:
+                o[:, s0:s1] = os_[0]
+                lse[:, s0:s1] = ls_[0]
+        if want is not None:
+            return o[want], lse[want]
         return o, lse
 
     def block_keep_of_bias(self, bias):

@@ -1024,6 +1024,65 @@ def pin_varlen_masks_brute_force(orc):
                     assert abs(lse[h, s0 + r] - (m + math.log(e.sum()))) < 1e-12
 
 
+def pin_prefill_paged_masks_neutral(orc):
+    """A zero term and an all-ones block mask change nothing: the masked paged
+    prefill (keys gathered per sequence, the dense definition per chunk) is the
+    paged prefill bit for bit, with and without a window."""
+    lens, q_lens = [9, 130, 23, 260], [3, 130, 1, 129]
+    A, A_kv, d, ps = 4, 2, 3, 4
+    q, kc, vc, bt, sl, cu = _paged_problem(lens, q_lens, A, A_kv, d, ps, 69)
+    T_q = int(cu[-1])
+    zero = np.zeros((A, T_q, max(lens)), np.float32)
+    ones = np.ones((len(lens), 1, 2, 3), np.uint8)
+    for causal, window in ((True, None), (False, None), (True, (40, -1))):
+        o, lse = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=0.75, causal=causal, window=window)
+        o2, l2 = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=0.75, causal=causal, window=window,
+                                   bias=zero, block_keep=ones)
+        assert np.array_equal(o, o2) and np.array_equal(lse, l2), (causal, window)
+
+
+def pin_prefill_paged_masks_brute_force(orc):
+    """Chunks with a per-token term and per-sequence block masks against a
+    direct fp64 softmax over keys read token by token from the pages."""
+    rng = np.random.default_rng(70)
+    lens, q_lens = [150, 20, 300], [140, 1, 150]
+    A, A_kv, d, ps, scale = 2, 1, 4, 8, 0.625
+    q, kc, vc, bt, sl, cu = _paged_problem(lens, q_lens, A, A_kv, d, ps, 71)
+    T_q = int(cu[-1])
+    bias = _f32(rng.standard_normal((A, T_q, 304)))
+    bias[rng.random(bias.shape) < 0.1] = -np.inf
+    bk = (rng.random((len(lens), A, 2, 3)) < 0.7).astype(np.uint8)
+    ids = np.array([0 * T_q + 5, 1 * T_q + T_q - 1, 1 * T_q + 141], np.int64)
+    for causal in (True, False):
+        o, lse = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=scale, causal=causal, bias=bias,
+                                   block_keep=bk)
+        o_r, l_r = orc.prefill_paged(q, kc, vc, bt, sl, cu, dtype="f32", scale=scale, causal=causal, bias=bias,
+                                     block_keep=bk, rows=ids)
+        assert np.array_equal(o_r, o.reshape(-1, d)[ids]) and np.array_equal(l_r, lse.reshape(-1)[ids])
+        for s, (L, ql) in enumerate(zip(lens, q_lens)):
+            s0 = int(cu[s])
+            kk = _contiguous(kc, bt[s], L, ps).astype(np.float64)
+            vv = _contiguous(vc, bt[s], L, ps).astype(np.float64)
+            for h in range(A):
+                qq = q[h, s0:s0 + ql].astype(np.float64)
+                sc = scale * qq @ kk[0].T + bias[h, s0:s0 + ql, :L].astype(np.float64)
+                i = np.arange(ql)[:, None]
+                j = np.arange(L)[None, :]
+                keep = bk[s, h][i // 128, j // 128] != 0
+                if causal:
+                    keep &= j <= i + (L - ql)
+                sc = np.where(keep, sc, -np.inf)
+                for r in range(ql):
+                    row = sc[r]
+                    if not np.isfinite(row).any():
+                        assert np.all(o[h, s0 + r] == 0) and np.isneginf(lse[h, s0 + r])
+                        continue
+                    m = row[np.isfinite(row)].max()
+                    e = np.exp(row - m)
+                    assert np.allclose(o[h, s0 + r], e @ vv[0] / e.sum(), rtol=0, atol=1e-12), (s, h, r)
+                    assert abs(lse[h, s0 + r] - (m + math.log(e.sum()))) < 1e-12
+
+
 def pin_prefill_paged_identity_is_varlen(orc):
     """With pages laid out in order and each whole sequence as its chunk, the
     paged prefill is the packed varlen prefill, bit for bit."""

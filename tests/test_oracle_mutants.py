@@ -112,6 +112,15 @@ PY_MUTANTS = [
      'kw["bias"] = bias[:, s0:s1, s0:s0 + L][None]', 0),
     ("varlen block mask of the first sequence", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
      'kw["block_keep"] = block_keep[0][None, :, :nbs, :nbs]', 0),
+    ("paged term rows not offset to the chunk", 'kw["bias"] = bias[:, s0:s1, :L][None]', 'kw["bias"] = bias[:, 0:ql, :L][None]',
+     1),
+    ("paged block mask of the first sequence",
+     'kw["block_keep"] = block_keep[s][None, :, :(ql + 127) // 128, :(L + 127) // 128]',
+     'kw["block_keep"] = block_keep[0][None, :, :(ql + 127) // 128, :(L + 127) // 128]', 0),
+    ("paged keys gathered page-major (t // ps as the row)", "offs = np.arange(L) % page_size",
+     "offs = (np.arange(L) // page_size) % page_size", 0),
+    ("paged causal diagonal aligned top-left", 'kw["m_keep"] = window_keep(1, ql, L, int(window[0]), int(window[1]))',
+     'kw["m_keep"] = window_keep(1, ql, ql, int(window[0]), int(window[1]))', 0),
     ("varlen block mask transposed", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
      'kw["block_keep"] = np.ascontiguousarray(block_keep[s][None, :, :nbs, :nbs].transpose(0, 1, 3, 2))', 0),
 ]
