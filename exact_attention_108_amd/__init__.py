@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     attn_fwd_fp8,
     attn_fwd_varlen,
     attn_prefill_paged,
+    attn_prefill_paged_masked,
     attn_prefill_paged_fp8,
     attn_status_string,
     exported_symbols,

@@ -63,6 +63,9 @@ _lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.attn_prefill_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                     _f, _i, _WP, _i, _vp]
 _lib.attn_prefill_paged.restype = _i
+_lib.attn_prefill_paged_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                                           _i, _i, _f, _i, ctypes.POINTER(_Mask), _WP, _i, _vp]
+_lib.attn_prefill_paged_masked.restype = _i
 _lib.attn_prefill_paged_fp8.argtypes = [_vp] * 10 + [_i, _vp, _vp] + [_i] * 7 + [_f, _i, _WP, _vp]
 _lib.attn_prefill_paged_fp8.restype = _i
 _lib.attn_bwd_workspace_bytes.restype = _sz
@@ -94,7 +97,7 @@ def attn_abi_version() -> int:
 def exported_symbols():
     """Names of the C entry points this binding resolves (one per header declaration)."""
     return ["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
-            "attn_decode_paged_window",
+            "attn_decode_paged_window", "attn_prefill_paged_masked",
             "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8", "attn_decode_paged_fp8",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
@@ -506,6 +509,23 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host
     """Prefill of packed query chunks q/o [A,T_q,d] (lse [A,T_q]) over a paged cache [num_pages, page_size,
     A_kv, d]; block_table int32 [n_seq, max_pages]; seq_lens int32 [n_seq] (device) with seq_lens_host; chunk
     boundaries cu_seqlens_q int32 [n_seq+1] (device) with cu_seqlens_q_host."""
+    _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host, o, lse,
+                scale, causal, window, stream, None, None)
+
+
+def attn_prefill_paged_masked(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q,
+                              cu_seqlens_q_host, o, lse, *, scale: float, causal: bool = True, window=None,
+                              block_keep=None, bias=None, stream=None):
+    """attn_prefill_paged with block_keep uint8 [n_seq, 1 or A, ceil(longest chunk/128), ceil(longest
+    seq_len/128)] over (chunk rows, key positions) and bias fp32 [1 or A, T_q, L] (L = the longest
+    seq_len; row t = chunk token t against the key positions of its sequence; rows unit-stride and a
+    multiple of 4 elements apart)."""
+    _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host, o, lse,
+                scale, causal, window, stream, block_keep, bias)
+
+
+def _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host, o, lse,
+                scale, causal, window, stream, block_keep, bias):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
@@ -524,13 +544,31 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host
         raise ValueError("cu_seqlens_q must be int32 [n_seq + 1]")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != n_seq:
         raise ValueError("block_table must be int32 [n_seq, max_pages]")
-    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse)
-    st = _lib.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
-                                 sl.ctypes.data_as(_vp), _ptr(cu_seqlens_q), cu_host.ctypes.data_as(_vp), page_size,
-                                 _ptr(o), _ptr(lse), n_seq, T_q, A, A_kv, d, block_table.shape[1], num_pages,
-                                 float(scale), int(bool(causal)), _window(window), _dtype_code(q),
-                                 _stream(stream, dev))
-    _check(st, "attn_prefill_paged")
+    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse, block_keep, bias)
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp),
+            _ptr(cu_seqlens_q), cu_host.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), n_seq, T_q, A, A_kv, d,
+            block_table.shape[1], num_pages, float(scale), int(bool(causal)))
+    if block_keep is None and bias is None:
+        st = _lib.attn_prefill_paged(*head, _window(window), _dtype_code(q), _stream(stream, dev))
+        _check(st, "attn_prefill_paged")
+        return
+    max_q = int(np.diff(cu_host).max()) if n_seq > 0 else 0
+    max_l = int(sl.max()) if n_seq > 0 else 0
+    want = (n_seq, (max_q + 127) // 128, (max_l + 127) // 128)
+    if block_keep is not None and (block_keep.dim() != 4 or block_keep.shape[0] != n_seq or
+                                   block_keep.shape[1] not in (1, A) or tuple(block_keep.shape[2:]) != want[1:]):
+        raise ValueError(f"block_keep must be [n_seq, 1 or A, {want[1]}, {want[2]}]")
+    bh, ld = 0, 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.dim() != 3 or bias.shape[0] not in (1, A) or \
+                tuple(bias.shape[1:]) != (T_q, max_l):
+            raise ValueError(f"bias must be fp32 [1 or A, T_q, {max_l}]")
+        bh, ld = int(bias.shape[0]), int(bias.stride(1))
+        if (max_l > 1 and bias.stride(2) != 1) or ld % 4 or ld < max_l or (bh > 1 and bias.stride(0) != T_q * ld):
+            raise ValueError("bias rows must be unit-stride, a multiple of 4 elements apart, heads packed")
+    st = _lib.attn_prefill_paged_masked(*head, _mask(None, None, block_keep, bias, bh, ld), _window(window),
+                                        _dtype_code(q), _stream(stream, dev))
+    _check(st, "attn_prefill_paged_masked")
 
 
 def attn_prefill_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host,

@@ -385,7 +385,8 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
                                const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_q_host, int page_size, void* o, float* lse, int n_seq,
                                int total_q, int A, int A_kv, int d_h, int max_pages, int num_pages, float scale,
-                               int causal, const attn_window* window, attn_dtype dtype, void* stream) {
+                               int causal, const attn_window* window, attn_dtype dtype, void* stream,
+                               const attn_mask* mask = nullptr) {
   if (n_seq < 0 || total_q < 0 || A < 1 || A_kv < 1 || d_h < 1 || A % A_kv != 0) return ATTN_ERR_INVAL;
   if (page_size < 1 || max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
   if (!valid_scale(scale) || !valid_window(window)) return ATTN_ERR_INVAL;
@@ -410,6 +411,22 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
                         (const void*)k_scale, (const void*)v_scale})
     if (!aligned(t, 4)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
+  // masks: block flags [n_seq, block_heads, nqb, nkb] over (chunk row, key
+  // position) and terms [bias_heads, total_q, bias_ld] (row: chunk token;
+  // columns: key positions of its sequence); no keep-masks here
+  const bool blocks = mask && mask->block_keep;
+  const bool bias = mask && mask->bias;
+  int max_q = 0, max_kv_len = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    max_q = std::max(max_q, cu_seqlens_q_host[s + 1] - cu_seqlens_q_host[s]);
+    max_kv_len = std::max(max_kv_len, seq_lens_host[s]);
+  }
+  if (mask && (mask->q_keep || mask->k_keep)) return ATTN_ERR_UNSUPPORTED;
+  if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
+  if (bias && !valid_bias(mask->bias, mask->bias_heads, A, max_q, max_kv_len, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if ((blocks || bias) && fp8) return ATTN_ERR_UNSUPPORTED;
+  if (blocks && max_kv_len > 262144) return ATTN_ERR_UNSUPPORTED;
+  if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
   if ((page_size & (page_size - 1)) != 0 || page_size % rows_per_part != 0) return ATTN_ERR_UNSUPPORTED;
   if (total_q == 0) return ATTN_OK;
@@ -441,6 +458,17 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   p.max_pages = max_pages;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  if (blocks) {
+    p.block_keep = mask->block_keep;
+    p.block_heads = mask->block_heads;
+    p.n_kb = (max_kv_len + 127) / 128;
+  }
+  if (bias) {
+    p.bias = mask->bias;
+    p.bias_heads = mask->bias_heads;
+    p.bias_ld = mask->bias_ld;
+    p.inv_scale = (float)(1.0 / (double)scale);
+  }
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
   p.page_shift = shift;
@@ -461,6 +489,19 @@ ATTN_EXPORT attn_status attn_prefill_paged(const void* q, const void* k_cache, c
   return prefill_paged_call(q, k_cache, v_cache, nullptr, nullptr, false, block_table, seq_lens, seq_lens_host,
                             cu_seqlens_q, cu_seqlens_q_host, page_size, o, lse, n_seq, total_q, A, A_kv, d_h,
                             max_pages, num_pages, scale, causal, window, dtype, stream);
+}
+
+ATTN_EXPORT attn_status attn_prefill_paged_masked(const void* q, const void* k_cache, const void* v_cache,
+                                                  const int32_t* block_table, const int32_t* seq_lens,
+                                                  const int32_t* seq_lens_host, const int32_t* cu_seqlens_q,
+                                                  const int32_t* cu_seqlens_q_host, int page_size, void* o,
+                                                  float* lse, int n_seq, int total_q, int A, int A_kv, int d_h,
+                                                  int max_pages, int num_pages, float scale, int causal,
+                                                  const attn_mask* mask, const attn_window* window,
+                                                  attn_dtype dtype, void* stream) {
+  return prefill_paged_call(q, k_cache, v_cache, nullptr, nullptr, false, block_table, seq_lens, seq_lens_host,
+                            cu_seqlens_q, cu_seqlens_q_host, page_size, o, lse, n_seq, total_q, A, A_kv, d_h,
+                            max_pages, num_pages, scale, causal, window, dtype, stream, mask);
 }
 
 ATTN_EXPORT attn_status attn_prefill_paged_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,

@@ -971,17 +971,26 @@ hipError_t launch_prefill_fp8(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_paged_d(const FwdParams& p, int grid, hipStream_t stream) {
+  if (p.bias && p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (p.bias) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_paged_bf16(const FwdParams& p, hipStream_t stream) {
   const int grid = p.total_tiles * p.A;
   if (grid <= 0) return hipSuccess;
-  if (p.d == 128) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-  } else if (p.d == 64) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (p.d == 128) return launch_paged_d<128>(p, grid, stream);
+  if (p.d == 64) return launch_paged_d<64>(p, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_paged_fp8(const FwdParams& p, hipStream_t stream) {

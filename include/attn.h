@@ -78,9 +78,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * [128 i, 128 i + 128) and key in [128 j, 128 j + 128) (h' = 0 when
  * block_heads == 1, else the query head); those key tiles are never loaded.
  * block_heads is 1 or A (ignored when block_keep is NULL).  Requires
- * S_k <= 262144.  attn_fwd, attn_fwd_varlen and attn_bwd take it; the
- * paged entry points and attn_bwd_varlen return ATTN_ERR_UNSUPPORTED for a
- * non-NULL block_keep.  attn_fwd_varlen: uint8 [n_seq, block_heads, nb, nb]
+ * S_k <= 262144.  attn_fwd, attn_fwd_varlen, attn_prefill_paged_masked and
+ * attn_bwd take it; the other paged entry points have no mask argument and
+ * attn_bwd_varlen returns ATTN_ERR_UNSUPPORTED for a non-NULL block_keep.  attn_fwd_varlen: uint8 [n_seq, block_heads, nb, nb]
  * with nb = ceil(longest sequence / 128); entry [s][h'][i][j] is block (i, j)
  * of sequence s's own rows and keys (positions within the sequence); entries
  * past a shorter sequence's blocks are never read.
@@ -104,9 +104,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * bias 16-byte aligned; bf16 calls also need 128 * bias_ld * 4 < 2^32
  * (ATTN_ERR_UNSUPPORTED otherwise).  It combines with every other mask; key
  * tiles are skipped only through block_keep, which attn_block_keep_from_bias
- * derives from a bias.  attn_fwd, attn_fwd_varlen (bf16) and attn_bwd take
- * it; the paged entry points and attn_bwd_varlen return ATTN_ERR_UNSUPPORTED
- * for a non-NULL bias.  attn_fwd_varlen: fp32 [bias_heads, T, bias_ld], row
+ * derives from a bias.  attn_fwd, attn_fwd_varlen (bf16),
+ * attn_prefill_paged_masked and attn_bwd take it; attn_bwd_varlen returns
+ * ATTN_ERR_UNSUPPORTED for a non-NULL bias.  attn_fwd_varlen: fp32 [bias_heads, T, bias_ld], row
  * (h', t) holding M for token t (position i in its sequence) against the
  * keys at positions j < len of the same sequence (bias_ld >= the longest
  * sequence). */
@@ -350,6 +350,37 @@ attn_status attn_prefill_paged(const void *q, const void *k_cache, const void *v
                                int n_seq, int total_q, int A, int A_kv, int d_h, int max_pages,
                                int num_pages, float scale, int causal, const attn_window *window,
                                attn_dtype dtype, void *stream);
+
+/*
+ * attn_prefill_paged with a block mask and a dense additive term (page
+ * "Attention Kernel", section "可编程 mask": block-level skipping, then an
+ * element rule, over the paged chunks of section "Paged 与 ragged KV").  Each
+ * sequence's chunk rows (index i within the chunk, at position
+ * seq_lens[s] - q_len + i) face its keys at positions j < seq_lens[s]:
+ *
+ *   mask->block_keep : NULL or uint8 [n_seq, block_heads, nqb, nkb] with nqb =
+ *                      ceil(longest chunk / 128), nkb = ceil(longest
+ *                      seq_lens / 128); entry [s][h'][i][j] = 0 masks chunk
+ *                      rows [128 i, 128 i + 128) against keys [128 j, 128 j +
+ *                      128) of sequence s; those key tiles are never loaded
+ *   mask->bias       : NULL or fp32 [bias_heads, total_q, bias_ld]; row (h', t)
+ *                      holds the term of chunk token t against the keys at
+ *                      positions j < seq_lens of its sequence (bias_ld >= the
+ *                      longest seq_lens, a multiple of 4); values and range as
+ *                      in attn_mask
+ *   mask->q_keep, k_keep : must be NULL (ATTN_ERR_UNSUPPORTED otherwise)
+ *
+ * Everything else as attn_prefill_paged (bf16 caches only).  A NULL mask is
+ * attn_prefill_paged.
+ */
+attn_status attn_prefill_paged_masked(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_table, const int32_t *seq_lens,
+                                      const int32_t *seq_lens_host, const int32_t *cu_seqlens_q,
+                                      const int32_t *cu_seqlens_q_host, int page_size, void *o,
+                                      float *lse, int n_seq, int total_q, int A, int A_kv, int d_h,
+                                      int max_pages, int num_pages, float scale, int causal,
+                                      const attn_mask *mask, const attn_window *window,
+                                      attn_dtype dtype, void *stream);
 
 /*
  * attn_prefill_paged over FP8 caches (page "Attention Kernel", sections "Paged

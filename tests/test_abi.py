@@ -20,7 +20,7 @@ def header_functions():
 def test_header_declares_entry_points():
     assert header_functions() == sorted(["attn_fwd", "attn_fwd_fp8", "attn_fwd_varlen", "attn_decode_paged",
                                          "attn_decode_paged_noalloc",
-                                         "attn_decode_paged_window",
+                                         "attn_decode_paged_window", "attn_prefill_paged_masked",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8",
                                          "attn_decode_paged_fp8",
@@ -249,7 +249,16 @@ def test_attn_fwd_varlen_rejects_bad_arguments():
     assert args(gp, 3, 9, A=3) == 1                # A % A_kv
     assert args(gp, 3, 9, scale=-1.0) == 1
     assert args(None, 3, 9) == 1
-    assert args(gp, 3, 9, mask=ctypes.byref(Mask(None, None, None, 0, 4096, 1, 12))) == 2   # additive mask: dense only
+    # packed-sequence masks (longest sequence 5): block heads in {1, A}; term heads in {1, A}, rows >= 5 and a
+    # multiple of 4 elements apart, 16-byte aligned; fp32 calls take neither
+    M = lambda *f: ctypes.byref(Mask(*f))
+    assert args(gp, 3, 9, mask=M(None, None, P, 3, None, 0, 0)) == 1
+    assert args(gp, 3, 9, mask=M(None, None, None, 0, 4096, 3, 8)) == 1
+    assert args(gp, 3, 9, mask=M(None, None, None, 0, 4096, 1, 4)) == 1
+    assert args(gp, 3, 9, mask=M(None, None, None, 0, 4096, 1, 6)) == 1
+    assert args(gp, 3, 9, mask=M(None, None, None, 0, 4096 + 4, 1, 8)) == 1
+    assert lib.attn_fwd_varlen(P, P, P, P, P, P, gp, 3, 9, 4, 2, 64, 0.1, 1, M(None, None, None, 0, 4096, 1, 8),
+                               None, 0, None) == 2
     zero = np.array([0, 0, 0], np.int32)
     assert args(zero.ctypes.data_as(ctypes.c_void_p), 2, 0) == 0   # all sequences empty: no launch
 
@@ -448,3 +457,24 @@ def test_decode_window_rejects_bad_arguments():
     assert call(4, q=odd8) == INVAL and call(4, kc=odd8) == INVAL
     assert lib.attn_decode_paged_window(P, P, P, P, P, lp, 16, P, P, 2, 8, 3, 128, 3, 6, 0.1, 4, 1, P, 1 << 30,
                                         None) == INVAL   # A % A_kv
+
+
+def test_prefill_paged_masked_rejects_bad_arguments():
+    """attn_prefill_paged_masked: no keep-masks; block heads and term heads in
+    {1, A}; term rows at least the longest sequence and a multiple of 4 apart;
+    bf16 caches only (host-side checks, before any device call)."""
+    lib = _lib()
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_prefill_paged_masked.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 7 + [f, i, ctypes.POINTER(Mask), vp, i, vp]
+    lens = np.array([40, 20], np.int32)
+    cu = np.array([0, 16, 17], np.int32)
+    lp, cp = lens.ctypes.data_as(vp), cu.ctypes.data_as(vp)
+    call = lambda m, dt=1: lib.attn_prefill_paged_masked(P, P, P, P, P, lp, P, cp, 16, P, P, 2, 17, 4, 2, 128, 3, 6,
+                                                         0.1, 1, ctypes.byref(m), None, dt, None)
+    assert call(Mask(P, None, None, 0, None, 0, 0)) == 2            # keep-masks: unsupported here
+    assert call(Mask(None, P, None, 0, None, 0, 0)) == 2
+    assert call(Mask(None, None, P, 3, None, 0, 0)) == 1            # block heads 3 with A = 4
+    assert call(Mask(None, None, None, 0, 4096, 2, 40)) == 1        # term heads 2 with A = 4
+    assert call(Mask(None, None, None, 0, 4096, 1, 36)) == 1        # rows shorter than the longest sequence (40)
+    assert call(Mask(None, None, None, 0, 4096, 1, 42)) == 1        # not a multiple of 4
+    assert call(Mask(None, None, P, 1, None, 0, 0), dt=0) == 2      # fp32: unsupported

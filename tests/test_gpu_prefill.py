@@ -809,3 +809,73 @@ def test_config5_block_mask_full_size_sampled(ea, orc):
                                        q_keep=p.q_keep, bias=bias, block_keep=bk, rows=rows)
     stats = gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "config5 masks")
     _say("config 5 masks", stats)
+
+
+# ---------------------------------------------------------------- paged chunks with block masks and terms
+def run_paged_masked(ea, pg, q, cu, *, bias_np=None, bk_np=None, window=None, causal=True):
+    t = gu.torch()
+    qd = gu.dev(q, pg.dtype)
+    kc, vc = gu.dev(pg.k_cache, pg.dtype), gu.dev(pg.v_cache, pg.dtype)
+    bt, sl, cud = gu.dev(pg.block_table, "i32"), gu.dev(pg.seq_lens, "i32"), gu.dev(cu, "i32")
+    o = gu.empty_out(qd.shape, pg.dtype)
+    lse = t.empty((qd.shape[0], qd.shape[1]), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    bias = None
+    if bias_np is not None:
+        H, T, L = bias_np.shape
+        ld = max(4, (L + 3) // 4 * 4)
+        full = t.full((H, T, ld), float("nan"), dtype=t.float32, device="cuda")
+        full[..., :L] = t.from_numpy(bias_np).cuda()
+        bias = full[..., :L]
+    bk = None if bk_np is None else t.from_numpy(bk_np).cuda()
+    ea.attn_prefill_paged_masked(qd, kc, vc, bt, sl, pg.seq_lens, cud, cu, o, lse, scale=pg.scale, causal=causal,
+                                 window=window, block_keep=bk, bias=bias)
+    t.cuda.synchronize()
+    return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+PAGED_MASK_CASES = [
+    # KV lengths, chunk lengths, A, A_kv, d, page size, causal, window, term heads, block heads
+    ([300, 1, 129, 700, 64, 5, 1000, 17], [300, 1, 1, 200, 64, 5, 129, 0], 8, 2, 128, 16, True, None, 1, 1),
+    ([400, 260, 33], [150, 260, 3], 4, 4, 128, 64, True, (77, -1), 4, 0),
+    ([520, 90], [260, 90], 4, 2, 64, 32, False, None, 0, 4),
+    ([1000, 300], [129, 300], 8, 1, 128, 16, True, None, 1, 8),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_MASK_CASES,
+                         ids=lambda c: f"{len(c[0])}seq-A{c[2]}-kv{c[3]}-d{c[4]}-ps{c[5]}-{'c' if c[6] else 'n'}"
+                                       f"-t{c[8]}-b{c[9]}" + ("" if c[7] is None else f"-w{c[7][0]}"))
+def test_paged_prefill_block_mask_and_term(ea, orc, case):
+    """Paged chunks with per-sequence block masks over (chunk row, key
+    position) and per-token terms ("Attention Kernel", 可编程 mask over Paged 与
+    ragged KV) against the oracle, mixed with decode rows and an empty chunk."""
+    lens, q_lens, A, A_kv, d, ps, causal, window, th, bh = case
+    _say("paged prefill block mask + term", case)
+    pg, q, cu = gen.make_paged_prefill(lens, q_lens, A, A_kv, d, ps, seed=sum(lens) + A, extra_pages=3)
+    rng = np.random.default_rng(sum(q_lens) + 11)
+    T_q, L = int(cu[-1]), max(lens)
+    nqb, nkb = (max(q_lens) + 127) // 128, (L + 127) // 128
+    bias = None
+    if th:
+        bias = (0.5 * rng.standard_normal((th, T_q, L))).astype(np.float32)
+        bias[rng.random(bias.shape) < 0.1] = -np.inf
+    bk = (rng.random((len(lens), bh, nqb, nkb)) < 0.6).astype(np.uint8) if bh else None
+    w = None if window is None else (window[0], 0 if causal else window[1])
+    o, lse = run_paged_masked(ea, pg, q, cu, bias_np=bias, bk_np=bk, window=window, causal=causal)
+    o_ref, l_ref = orc.prefill_paged(q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, cu, dtype=pg.dtype,
+                                     scale=pg.scale, causal=causal, window=w, bias=bias, block_keep=bk)
+    gu.check(o[None], lse[None], o_ref[None], l_ref[None], pg.dtype, str(case))
+
+
+def test_paged_masked_neutral_is_paged_bitwise(ea):
+    """An all-ones block mask gives attn_prefill_paged's bits (the listed tiles
+    are all the tiles; a zero term differs only by the term's path)."""
+    lens, q_lens = [700, 33, 260], [200, 3, 260]
+    _say("paged masked, all-ones blocks == paged", lens, q_lens)
+    pg, q, cu = gen.make_paged_prefill(lens, q_lens, 8, 2, 128, 16, seed=977)
+    bk = np.ones((3, 1, 3, 6), np.uint8)
+    o1, l1 = run_paged_prefill(ea, pg, q, cu)
+    o2, l2 = run_paged_masked(ea, pg, q, cu, bk_np=bk)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
