@@ -269,10 +269,18 @@ class Oracle:
         return dq, dk, dv
 
     def attn_bwd_varlen(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal=True, q_keep=None, k_keep=None,
-                        window=None):
+                        window=None, bias=None, block_keep=None):
         """Gradient of the packed varlen prefill: q, do [A,T,d]; k, v [A_kv,T,d];
         cu_seqlens [n_seq+1]; keep masks [T]; window (left, right) within each
-        sequence (-1 = unbounded).  Returns (dq, dk, dv) in fp64."""
+        sequence (-1 = unbounded).  Returns (dq, dk, dv) in fp64.  bias and
+        block_keep as attn_fwd_varlen takes them; with either, each sequence's
+        gradient is the dense gradient of its own problem (its slices of the
+        masks) -- the backward uses the forward's mask ("Attention Kernel",
+        Backward 与重计算)."""
+        if bias is not None or block_keep is not None:
+            return self._bwd_varlen_by_sequence(q, k, v, do, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
+                                                q_keep=q_keep, k_keep=k_keep, window=window, bias=bias,
+                                                block_keep=block_keep)
         q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
         if q.ndim != 3 or k.shape != v.shape or do.shape != q.shape:
             raise ValueError("q, do [A,T,d]; k, v [A_kv,T,d]")
@@ -292,6 +300,48 @@ class Oracle:
                                              wr, _ptr(dq), _ptr(dk), _ptr(dv))
         if rc != 0:
             raise ValueError("oracle_attn_bwd_varlen rejected its arguments")
+        return dq, dk, dv
+
+    def _bwd_varlen_by_sequence(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, window, bias,
+                                block_keep):
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        A, T, d = q.shape
+        A_kv = k.shape[0]
+        n_seq = cu.size - 1
+        lens = np.diff(cu)
+        nb = int((lens.max(initial=0) + 127) // 128)
+        if bias is not None:
+            bias = np.asarray(bias, dtype=np.float32)
+            if bias.ndim != 3 or bias.shape[0] not in (1, A) or bias.shape[1] != T or bias.shape[2] < lens.max(initial=0):
+                raise ValueError("bias must be [1 or A, T, ld >= longest length]")
+        if block_keep is not None:
+            block_keep = np.asarray(block_keep, dtype=np.uint8)
+            if block_keep.ndim != 4 or block_keep.shape[0] != n_seq or block_keep.shape[1] not in (1, A) or \
+                    block_keep.shape[2:] != (nb, nb):
+                raise ValueError(f"block_keep must be [n_seq, 1 or A, {nb}, {nb}]")
+        dq = np.zeros((A, T, d), dtype=np.float64)
+        dk = np.zeros((A_kv, T, d), dtype=np.float64)
+        dv = np.zeros((A_kv, T, d), dtype=np.float64)
+        for s in range(n_seq):
+            s0, s1 = int(cu[s]), int(cu[s + 1])
+            L = s1 - s0
+            if L == 0:
+                continue
+            kw = {}
+            if q_keep is not None:
+                kw["q_keep"] = np.asarray(q_keep).reshape(T)[s0:s1][None]
+            if k_keep is not None:
+                kw["k_keep"] = np.asarray(k_keep).reshape(T)[s0:s1][None]
+            if window is not None:
+                kw["m_keep"] = window_keep(1, L, L, int(window[0]), int(window[1]))
+            if bias is not None:
+                kw["bias"] = bias[:, s0:s1, :L][None]
+            if block_keep is not None:
+                nbs = (L + 127) // 128
+                kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]
+            g = self.attn_bwd(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], do[None, :, s0:s1],
+                              dtype=dtype, scale=scale, causal=causal, **kw)
+            dq[:, s0:s1], dk[:, s0:s1], dv[:, s0:s1] = g[0][0], g[1][0], g[2][0]
         return dq, dk, dv
 
     def prefill_paged(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal=True,

@@ -1204,6 +1204,51 @@ def pin_bwd_varlen_equals_separate(orc):
                 assert np.array_equal(g[:, a:b], want[0]), (causal, window, s)
 
 
+def pin_bwd_varlen_masks(orc):
+    """The packed-sequence gradient with per-sequence blocks and per-token
+    terms: neutral masks give the unmasked packed gradient bit for bit, and
+    with real masks it matches central differences of the packed forward under
+    the same masks (the forward's and the backward's slicing are separate
+    code)."""
+    rng = np.random.default_rng(72)
+    lens = [4, 0, 6, 3]
+    A, A_kv, d, scale = 2, 1, 3, 0.7
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, do = rng.standard_normal((A, T, d)), rng.standard_normal((A, T, d))
+    k, v = rng.standard_normal((A_kv, T, d)), rng.standard_normal((A_kv, T, d))
+    zero = np.zeros((A, T, 8), np.float32)
+    ones = np.ones((len(lens), 1, 1, 1), np.uint8)
+    ref = orc.attn_bwd_varlen(q, k, v, do, cu, dtype="f64", scale=scale, causal=True)
+    neu = orc.attn_bwd_varlen(q, k, v, do, cu, dtype="f64", scale=scale, causal=True, bias=zero, block_keep=ones)
+    for g, want in zip(neu, ref):
+        assert np.array_equal(g, want)
+    bias = (0.5 * rng.standard_normal((A, T, 6))).astype(np.float32)
+    bias[0, 5, 1] = -np.inf
+    bias[1, 11, 0] = -np.inf
+    bk = np.ones((len(lens), A, 1, 1), np.uint8)
+    bk[3, 1] = 0                     # head 1 of the last sequence fully masked
+    dq, dk, dv = orc.attn_bwd_varlen(q, k, v, do, cu, dtype="f64", scale=scale, causal=False, bias=bias,
+                                     block_keep=bk)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attn_fwd_varlen(qq, kk, vv, cu, dtype="f64", scale=scale, causal=False, bias=bias, block_keep=bk)
+        return float(np.sum(o * do))
+    eps = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for h, t, e in [(0, 0, 0), (1, 5, 2), (0, 9, 1), (1, T - 1, 0), (0, 12, 2)]:
+            idx = (h % arr.shape[0], t, e)
+            saved = arr[idx]
+            arr[idx] = saved + eps
+            lp = loss(q, k, v)
+            arr[idx] = saved - eps
+            lm = loss(q, k, v)
+            arr[idx] = saved
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+    assert np.all(dq[1, 10:13] == 0)  # the fully masked head and sequence
+
+
 def pin_bwd_masks_finite_differences(orc):
     """Gradients with a block mask, an additive term (finite values and -inf)
     and both: central differences of L = sum(O * dO) through the forward."""

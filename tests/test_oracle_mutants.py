@@ -112,8 +112,12 @@ PY_MUTANTS = [
      'kw["bias"] = bias[:, s0:s1, s0:s0 + L][None]', 0),
     ("varlen block mask of the first sequence", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
      'kw["block_keep"] = block_keep[0][None, :, :nbs, :nbs]', 0),
+    ("packed gradient: term rows not offset to the sequence", 'kw["bias"] = bias[:, s0:s1, :L][None]',
+     'kw["bias"] = bias[:, 0:L, :L][None]', 1),
+    ("packed gradient: block mask of the first sequence", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
+     'kw["block_keep"] = block_keep[0][None, :, :nbs, :nbs]', 1),
     ("paged term rows not offset to the chunk", 'kw["bias"] = bias[:, s0:s1, :L][None]', 'kw["bias"] = bias[:, 0:ql, :L][None]',
-     1),
+     2),
     ("paged block mask of the first sequence",
      'kw["block_keep"] = block_keep[s][None, :, :(ql + 127) // 128, :(L + 127) // 128]',
      'kw["block_keep"] = block_keep[0][None, :, :(ql + 127) // 128, :(L + 127) // 128]', 0),
