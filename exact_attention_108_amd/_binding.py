@@ -314,6 +314,20 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: floa
     for t in (q_keep, k_keep):
         if t is not None and t.shape != (T,):
             raise ValueError("keep-masks must be [T]")
+    bh, ld = _packed_masks(block_keep, bias, cu_host, A, T)
+    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep, block_keep, bias)
+    st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                              cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d, float(scale), int(bool(causal)),
+                              _mask(q_keep, k_keep, block_keep, bias, bh, ld), _window(window), _dtype_code(q),
+                              _stream(stream, dev))
+    _check(st, "attn_fwd_varlen")
+
+
+def _packed_masks(block_keep, bias, cu_host, A, T):
+    """Checks the packed-sequence block mask [n_seq, 1 or A, nb, nb] and term
+    [1 or A, T, longest length]; returns the term's (heads, row stride)."""
+    torch = _torch()
+    n_seq = cu_host.size - 1
     max_len = int(np.diff(cu_host).max()) if n_seq > 0 else 0
     nb = (max_len + 127) // 128
     if block_keep is not None and (block_keep.dim() != 4 or block_keep.shape[0] != n_seq or
@@ -327,12 +341,7 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: floa
         bh, ld = int(bias.shape[0]), int(bias.stride(1))
         if (max_len > 1 and bias.stride(2) != 1) or ld % 4 or ld < max_len or (bh > 1 and bias.stride(0) != T * ld):
             raise ValueError("bias rows must be unit-stride, a multiple of 4 elements apart, heads packed")
-    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep, block_keep, bias)
-    st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
-                              cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d, float(scale), int(bool(causal)),
-                              _mask(q_keep, k_keep, block_keep, bias, bh, ld), _window(window), _dtype_code(q),
-                              _stream(stream, dev))
-    _check(st, "attn_fwd_varlen")
+    return bh, ld
 
 
 def attn_decode_paged_workspace_bytes(B: int, A: int, A_kv: int, d: int, page_size: int, seq_lens_host) -> int:
@@ -469,10 +478,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, caus
 
 
 def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, cu_seqlens_host, workspace, *, scale: float,
-                    causal: bool = True, q_keep=None, k_keep=None, window=None, stream=None):
+                    causal: bool = True, q_keep=None, k_keep=None, window=None, block_keep=None, bias=None,
+                    stream=None):
     """dQ, dK, dV of attn_fwd_varlen.  q/o/dout/dq [A,T,d], k/v/dk/dv [A_kv,T,d], lse [A,T] fp32 (the
     forward's); cu_seqlens int32 device with cu_seqlens_host (numpy); workspace a uint8 device tensor of at
-    least attn_bwd_workspace_bytes(1, A, T) bytes."""
+    least attn_bwd_workspace_bytes(1, A, T) bytes; block_keep and bias as attn_fwd_varlen takes them."""
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
         raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
@@ -495,11 +505,13 @@ def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, cu_seqlens_ho
     for t in (q_keep, k_keep):
         if t is not None and t.shape != (T,):
             raise ValueError("keep-masks must be [T]")
+    bh, ld = _packed_masks(block_keep, bias, cu_host, A, T)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace, q_keep, k_keep)
+    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace, q_keep, k_keep, block_keep, bias)
     st = _lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                               _ptr(dv), _ptr(cu_seqlens), cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d,
-                              float(scale), int(bool(causal)), _mask(q_keep, k_keep), _window(window),
+                              float(scale), int(bool(causal)), _mask(q_keep, k_keep, block_keep, bias, bh, ld),
+                              _window(window),
                               _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_bwd_varlen")
 

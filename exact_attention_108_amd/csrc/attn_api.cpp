@@ -630,10 +630,7 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(t)) return ATTN_ERR_INVAL;
   if (!aligned(cu_seqlens, 4)) return ATTN_ERR_INVAL;
-  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;  // dense attn_bwd only
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
-  if (total_tokens == 0) return ATTN_OK;
-  if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   long long total_tiles = 0;
   int max_tiles = 0, max_len = 0;
   for (int s = 0; s < n_seq; ++s) {
@@ -643,6 +640,16 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
     max_tiles = std::max(max_tiles, nt);
     max_len = std::max(max_len, len);
   }
+  // the forward's packed masks: block flags [n_seq, block_heads, nb, nb]
+  // (nb = max_tiles: 128-row tiles), terms [bias_heads, T, bias_ld]
+  const bool blocks = mask && mask->block_keep;
+  const bool bias = mask && mask->bias;
+  if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
+  if (bias && !valid_bias(mask->bias, mask->bias_heads, A, max_len, max_len, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if (blocks && (max_tiles > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * max_tiles > attn::kBwdMaxRowBlocks))
+    return ATTN_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return ATTN_OK;
+  if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   if (!window_arith_fits(window, max_len, max_len)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = bwd_workspace_bytes(1, A, total_tokens);
@@ -654,6 +661,17 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   p.T = total_tokens;
   p.max_tiles = max_tiles;
   p.total_tiles = (int)total_tiles;
+  if (blocks) {
+    p.block_keep = mask->block_keep;
+    p.block_heads = mask->block_heads;
+    p.n_qb = p.n_kb = max_tiles;
+  }
+  if (bias) {
+    p.bias = mask->bias;
+    p.bias_heads = mask->bias_heads;
+    p.bias_ld = mask->bias_ld;
+    p.inv_scale = (float)(1.0 / (double)scale);
+  }
   window_edges(window, causal, max_len, max_len, p.win_left, p.win_right);
   return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
 }

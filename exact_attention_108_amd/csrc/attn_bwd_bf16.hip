@@ -145,7 +145,6 @@ constexpr int kDqWavesPerSimd = (D == 128 && kMasks) ? 1 : 2;
 template <int D, bool kVarlen, bool kMasks>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D, kMasks>, kDqWavesPerSimd<D, kMasks>))) void bwd_dq_kernel(BwdParams p,
                                                                                                     int n_qt) {
-  static_assert(!(kVarlen && kMasks), "block masks and additive terms are dense-batch only");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int TILE_BYTES = kKeyTile * D * 2;
@@ -162,6 +161,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     h = blockIdx.x % p.A;
     int seq;
     if (!varlen_tile(p.cu_seqlens, p.n_seq, p.max_tiles, blockIdx.x / p.A, qt, seq)) return;
+    b = seq;  // packed masks: block flags [n_seq, heads, nb, nb]
     tok0 = p.cu_seqlens[seq];
     S_q = S_k = p.cu_seqlens[seq + 1] - (int)tok0;
     q_row0 = (size_t)h * p.T + tok0;
@@ -250,8 +250,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
       for (int i = tid; i < nkb; i += kThreads) sBlk[i] = bk[kb0 + i];
     }
     if (p.bias) {
+      // dense [B, heads, S_q, ld]; packed [heads, T, ld] (row t: token t of its sequence)
       const int hm = p.bias_heads == 1 ? 0 : h;
-      brow = p.bias + ((size_t)(b * p.bias_heads + hm) * S_q + min(qrow, S_q - 1)) * p.bias_ld;
+      brow = kVarlen ? p.bias + ((size_t)hm * p.T + tok0 + min(qrow, S_q - 1)) * p.bias_ld
+                     : p.bias + ((size_t)(b * p.bias_heads + hm) * S_q + min(qrow, S_q - 1)) * p.bias_ld;
     }
   }
   auto tile_kept = [&](int j) -> bool {
@@ -393,7 +395,6 @@ constexpr int kDkdvWavesPerSimd = (D == 64 || KLDS) ? 2 : 1;
 template <int D, bool KLDS, bool kVarlen, bool kMasks>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS>, kDkdvWavesPerSimd<D, KLDS>))) void bwd_dkdv_kernel(BwdParams p,
                                                                                                       int n_kt) {
-  static_assert(!(kVarlen && kMasks), "block masks and additive terms are dense-batch only");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
@@ -415,6 +416,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     hk = blockIdx.x % p.A_kv;
     int from_end, seq;
     if (!varlen_tile(p.cu_seqlens, p.n_seq, p.max_tiles, blockIdx.x / p.A_kv, from_end, seq)) return;
+    b = seq;  // packed masks: block flags [n_seq, heads, nb, nb]
     tok0 = p.cu_seqlens[seq];
     S_q = S_k = p.cu_seqlens[seq + 1] - (int)tok0;
     kt = (S_k + kBwdKRows - 1) / kBwdKRows - 1 - from_end;
@@ -553,7 +555,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
         // half-wave read 32 consecutive keys; rows past S_q and keys past S_k
         // are not read (the predicate masks them)
         const int gh = idx / nq, hm = p.bias_heads == 1 ? 0 : hk * p.G + gh;
-        const float* bcol = p.bias + (size_t)(b * p.bias_heads + hm) * S_q * p.bias_ld + min(key, S_k - 1);
+        const float* bcol = (kVarlen ? p.bias + ((size_t)hm * p.T + tok0) * p.bias_ld
+                                     : p.bias + (size_t)(b * p.bias_heads + hm) * S_q * p.bias_ld) +
+                            min(key, S_k - 1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = r0 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -800,6 +804,7 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  if (p.cu_seqlens && (p.block_keep || p.bias)) return launch_bwd_v<D, true, true>(p, stream);
   if (p.cu_seqlens) return launch_bwd_v<D, true, false>(p, stream);
   if (p.block_keep || p.bias) return launch_bwd_v<D, false, true>(p, stream);
   return launch_bwd_v<D, false, false>(p, stream);

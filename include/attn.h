@@ -78,12 +78,13 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * [128 i, 128 i + 128) and key in [128 j, 128 j + 128) (h' = 0 when
  * block_heads == 1, else the query head); those key tiles are never loaded.
  * block_heads is 1 or A (ignored when block_keep is NULL).  Requires
- * S_k <= 262144.  attn_fwd, attn_fwd_varlen, attn_prefill_paged_masked and
- * attn_bwd take it; the other paged entry points have no mask argument and
- * attn_bwd_varlen returns ATTN_ERR_UNSUPPORTED for a non-NULL block_keep.  attn_fwd_varlen: uint8 [n_seq, block_heads, nb, nb]
- * with nb = ceil(longest sequence / 128); entry [s][h'][i][j] is block (i, j)
- * of sequence s's own rows and keys (positions within the sequence); entries
- * past a shorter sequence's blocks are never read.
+ * S_k <= 262144.  attn_fwd, attn_fwd_varlen, attn_prefill_paged_masked,
+ * attn_bwd and attn_bwd_varlen take it; the other paged entry points have
+ * no mask argument.  attn_fwd_varlen and attn_bwd_varlen: uint8 [n_seq,
+ * block_heads, nb, nb] with nb = ceil(longest sequence / 128); entry
+ * [s][h'][i][j] is block (i, j) of sequence s's own rows and keys (positions
+ * within the sequence); entries past a shorter sequence's blocks are never
+ * read.
  *
  * bias: the general dense additive mask M of the operation
  * (page "Attention Kernel", section "可编程 mask"; the term "+ M" of section
@@ -105,8 +106,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * (ATTN_ERR_UNSUPPORTED otherwise).  It combines with every other mask; key
  * tiles are skipped only through block_keep, which attn_block_keep_from_bias
  * derives from a bias.  attn_fwd, attn_fwd_varlen (bf16),
- * attn_prefill_paged_masked and attn_bwd take it; attn_bwd_varlen returns
- * ATTN_ERR_UNSUPPORTED for a non-NULL bias.  attn_fwd_varlen: fp32 [bias_heads, T, bias_ld], row
+ * attn_prefill_paged_masked, attn_bwd and attn_bwd_varlen take it.
+ * attn_fwd_varlen and attn_bwd_varlen: fp32 [bias_heads, T, bias_ld], row
  * (h', t) holding M for token t (position i in its sequence) against the
  * keys at positions j < len of the same sequence (bias_ld >= the longest
  * sequence). */
@@ -453,13 +454,16 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
  *   q, o, dout, dq : [A, T, d_h]      k, v, dk, dv : [A_kv, T, d_h]
  *   lse            : [A, T] fp32, attn_fwd_varlen's for the same call
  *   cu_seqlens, cu_seqlens_host, n_seq, total_tokens : as attn_fwd_varlen
- *   mask           : NULL or keep-masks q_keep [T], k_keep [T]
+ *   mask           : NULL or the forward's: keep-masks q_keep [T], k_keep
+ *                    [T], a block mask [n_seq, block_heads, nb, nb] and an
+ *                    additive term [bias_heads, T, bias_ld] as attn_fwd_varlen
+ *                    takes them (see attn_mask)
  *   window         : NULL or the sliding window given to attn_fwd_varlen
  *   workspace      : device buffer of at least attn_bwd_workspace_bytes(1,
  *                    A, total_tokens) bytes, 256-byte aligned
  *
- * Outputs, determinism, alignment and support as attn_bwd; a block mask or
- * an additive term is ATTN_ERR_UNSUPPORTED (the packed forward takes none).
+ * Outputs, determinism, alignment and support as attn_bwd (block masks: nb <=
+ * 2048 and (A / A_kv) * nb <= 4096, else ATTN_ERR_UNSUPPORTED).
  */
 attn_status attn_bwd_varlen(const void *q, const void *k, const void *v, const void *o, const void *dout,
                             const float *lse, void *dq, void *dk, void *dv, const int32_t *cu_seqlens,

@@ -38,22 +38,30 @@ def orc():
 
 # ---- packed sequences
 
-def run_bwd_varlen(ea, p, dout, q_keep=None, k_keep=None, window=None):
+def run_bwd_varlen(ea, p, dout, q_keep=None, k_keep=None, window=None, bias_np=None, bk_np=None):
     t = gu.torch()
     q, k, v, do = (gu.dev(x, "bf16") for x in (p.q, p.k, p.v, dout))
     cu = gu.dev(p.cu_seqlens, "i32")
     qk = None if q_keep is None else gu.dev(q_keep, "u8")
     kk = None if k_keep is None else gu.dev(k_keep, "u8")
+    bias = None
+    if bias_np is not None:
+        H, T, L = bias_np.shape
+        ld = max(4, (L + 3) // 4 * 4)
+        full = t.zeros((H, T, ld), dtype=t.float32, device="cuda")
+        full[..., :L] = t.from_numpy(bias_np).cuda()
+        bias = full[..., :L]
+    bk = None if bk_np is None else t.from_numpy(bk_np).cuda()
     o = gu.empty_out(q.shape, "bf16")
     lse = t.empty((p.A, p.T), dtype=t.float32, device="cuda")
     ea.attn_fwd_varlen(q, k, v, o, lse, cu, p.cu_seqlens, scale=p.scale, causal=p.causal, q_keep=qk, k_keep=kk,
-                       window=window)
+                       window=window, block_keep=bk, bias=bias)
     dq, dk, dv = (gu.empty_out(x.shape, "bf16") for x in (q, k, v))
     for x in (dq, dk, dv):
         x.fill_(float("nan"))
     ws = t.empty(max(ea.attn_bwd_workspace_bytes(1, p.A, p.T), 1), dtype=t.uint8, device="cuda")
     ea.attn_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, cu, p.cu_seqlens, ws, scale=p.scale, causal=p.causal,
-                       q_keep=qk, k_keep=kk, window=window)
+                       q_keep=qk, k_keep=kk, window=window, block_keep=bk, bias=bias)
     t.cuda.synchronize()
     return gu.host_f64(dq), gu.host_f64(dk), gu.host_f64(dv)
 
@@ -203,3 +211,44 @@ def test_bwd_block_mask_all_on_equals_dense_bitwise(ea):
     b = run_bwd_masked(ea, p, dout, block_keep=np.ones((1, 1, 3, 3), np.uint8))
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+VARLEN_MASK_CASES = [
+    # lens, A, A_kv, d, causal, window, term heads (0 = none), block heads (0 = none)
+    ([1, 0, 130, 17, 400, 64, 300], 4, 2, 128, True, None, 1, 1),
+    ([257, 1, 128, 129, 5], 2, 2, 128, False, None, 2, 0),
+    ([300, 77, 513], 4, 1, 64, True, (70, -1), 0, 4),
+    ([190, 260], 2, 1, 64, False, (40, 30), 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_MASK_CASES, ids=lambda c: f"n{len(c[0])}A{c[1]}:{c[2]}d{c[3]}"
+                         + ("c" if c[4] else "n") + ("w" if c[5] else "") + f"t{c[6]}b{c[7]}")
+def test_bwd_varlen_block_mask_and_term(ea, orc, case):
+    """Gradient of packed sequences under the forward's per-sequence block
+    masks and per-token terms ("Attention Kernel", Backward 与重计算: the
+    backward uses the forward's mask) against the oracle's."""
+    lens, A, A_kv, d, causal, window, th, bh = case
+    _say("bwd varlen block mask + term", case)
+    seed = 1500 + sum(lens) + A + d
+    p = gen.make_varlen(lens, A, A_kv, d, dtype="bf16", causal=causal, seed=seed)
+    dout = gen.draw((A, p.T, d), seed, gen.S_DOUT, "normal", "bf16")
+    rng = np.random.default_rng(seed)
+    L = max(lens)
+    nb = (L + 127) // 128
+    bias = None
+    if th:
+        bias = (0.5 * rng.standard_normal((th, p.T, L))).astype(np.float32)
+        bias[rng.random(bias.shape) < 0.05] = -np.inf
+    bk = None
+    if bh:
+        bk = (rng.random((len(lens), bh, nb, nb)) < 0.6).astype(np.uint8)
+        for s_ in range(len(lens)):
+            for h_ in range(bh):
+                np.fill_diagonal(bk[s_, h_], 1)   # keep rows that see more than a key or two
+    got = run_bwd_varlen(ea, p, dout, window=window, bias_np=bias, bk_np=bk)
+    w = None if window is None else (window[0], 0 if causal else window[1])
+    ref = orc.attn_bwd_varlen(p.q, p.k, p.v, dout, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=causal,
+                              window=w, bias=bias, block_keep=bk)
+    out = {n: gu.check_grad(g, r, f"{case} {n}") for n, g, r in zip(("dq", "dk", "dv"), got, ref)}
+    _say(out)
