@@ -378,7 +378,12 @@ def test_attn_bwd_varlen_rejects_bad_arguments():
     assert call(q=ctypes.c_void_p(4096 + 8)) == INVAL             # 16-byte alignment
     assert call(cud=ctypes.c_void_p(4096 + 2)) == INVAL
     assert call(d=96) == UNSUP and call(dt=0) == UNSUP
-    assert call(mask=ctypes.byref(Mask(None, None, 4096, 1))) == UNSUP   # block masks: dense only
+    # the forward's packed masks: block heads and term heads in {1, A}; term rows >= the longest sequence (5),
+    # a multiple of 4 elements apart
+    assert call(mask=ctypes.byref(Mask(None, None, 4096, 3))) == INVAL
+    assert call(mask=ctypes.byref(Mask(None, None, None, 0, 4096, 3, 8))) == INVAL
+    assert call(mask=ctypes.byref(Mask(None, None, None, 0, 4096, 1, 4))) == INVAL
+    assert call(mask=ctypes.byref(Mask(None, None, None, 0, 4096, 1, 10))) == INVAL
     assert call(cu=np.array([0, 0, 0], np.int32), T=0) == OK       # nothing to do
 
 
