@@ -669,6 +669,74 @@ def test_bias_block_skip_bitwise(ea):
     assert t.equal(o1.view(t.int16), o2.view(t.int16)) and t.equal(l1, l2)
 
 
+# More dense-term shapes without block or key masks: one, two and three key
+# tiles, long key ranges, rows and keys past the last full tile, shared and
+# per-head terms, GQA and windows.
+TERM_CASES = [
+    # B, A, A_kv, S_q, S_k, causal, window, heads, kind
+    (1, 4, 4, 1000, 1000, True, None, 4, "alibi"),
+    (2, 4, 1, 300, 777, False, None, 1, "random"),
+    (1, 2, 2, 129, 50, False, None, 2, "random"),
+    (1, 2, 2, 64, 130, True, None, 2, "random"),
+    (1, 2, 2, 100, 190, False, None, 1, "alibi"),
+    (1, 2, 1, 700, 1300, True, (200, -1), 2, "alibi"),
+    (1, 2, 2, 256, 640, False, (100, 100), 1, "random"),
+]
+
+
+@pytest.mark.parametrize("case", TERM_CASES, ids=lambda c: "x".join(map(str, c[:5])) + ("c" if c[5] else "n")
+                         + f"_{c[8]}{c[7]}" + ("" if c[6] is None else f"_w{c[6][0]}_{c[6][1]}"))
+def test_bias_shapes(ea, orc, case):
+    B, A, A_kv, S_q, S_k, causal, window, heads, kind = case
+    _say("dense additive term", case)
+    seed = 1400 + S_q + S_k
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, 128, dtype="bf16", causal=causal, seed=seed)
+    bias = gen.make_bias(B, heads, S_q, S_k, kind, seed)
+    o, lse, _ = run_bias(ea, p, bias, window=window)
+    o_ref, l_ref = bias_oracle(orc, p, bias, window=window)
+    _say(gu.check(o, lse, o_ref, l_ref, "bf16", str(case)))
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 300, 512), (2, 2, 2, 128, 1024), (1, 2, 1, 77, 64)])
+def test_bias_all_kept_key_mask_bitwise(ea, shape):
+    """A key mask that keeps every key changes nothing: non-causal with whole
+    key tiles, the call with it (every tile through the masked body) and the
+    call without it (every tile predicate-free) visit the tiles in the same
+    order and agree bit for bit."""
+    t = gu.torch()
+    B, A, A_kv, S_q, S_k = shape
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, 128, dtype="bf16", causal=False, seed=1450 + S_k)
+    bias = ea.pad_bias(t.from_numpy(gen.make_bias(B, A, S_q, S_k, "random", 1450 + S_k)).cuda())
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    ones = t.ones((B, S_k), dtype=t.uint8, device="cuda")
+    o1, o2 = gu.empty_out(q.shape, "bf16"), gu.empty_out(q.shape, "bf16")
+    l1 = t.empty((B, A, S_q), dtype=t.float32, device="cuda")
+    l2 = t.empty_like(l1)
+    _say("all-kept key mask bitwise", shape)
+    ea.attn_fwd(q, k, v, o1, l1, scale=p.scale, causal=False, bias=bias)
+    ea.attn_fwd(q, k, v, o2, l2, scale=p.scale, causal=False, bias=bias, k_keep=ones)
+    t.cuda.synchronize()
+    assert t.equal(o1.view(t.int16), o2.view(t.int16))
+    assert t.equal(l1.isneginf(), l2.isneginf())
+    fin = l1.isfinite()
+    assert t.equal(l1[fin], l2[fin])
+
+
+def test_bias_penalty_full_size_sampled(ea, orc):
+    """The MHA workload's shape, causal, with a per-head distance penalty
+    [4, 32, 2048, 2048] (the timed additive-term launch), sampled rows against
+    the oracle."""
+    p = gen.make_config(2)
+    bias = gen.make_bias(p.B, p.A, p.S_q, p.S_k, "alibi", 1460)
+    _say("per-head penalty full size")
+    o, lse, _ = run_bias(ea, p, bias)
+    rng = np.random.default_rng(1460)
+    rows = _sample_rows(rng, p.B, p.A, p.S_q, 1200)
+    o_ref, l_ref = bias_oracle(orc, p, bias, rows=rows)
+    _say("per-head penalty full size",
+         gu.check(o.reshape(-1, p.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, "bf16", "penalty full size"))
+
+
 def test_bias_full_size_sampled(ea, orc):
     """The MHA workload's shape, causal, with a packed-document mask given as
     the additive term (and its block mask), sampled rows against the oracle."""
