@@ -29,6 +29,7 @@ namespace attn {
 namespace {
 
 constexpr int kChunk = 16;       // tokens per inner step (one MFMA M block)
+constexpr int kDecodeBufsOneWave = 3;  // LDS buffers per wave in 1-wave workgroups (bf16)
 constexpr int kWavesPerGroup = 4;  // waves per workgroup, each with its own KV heads
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
@@ -87,9 +88,13 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
   constexpr int N_LD = kChunk / TOK_PER_LD;  // load instructions per chunk (K or V)
   constexpr int KSTEPS = D / 32;             // QK k-steps per head
   constexpr int MB = D / 16;                 // 16-row blocks of O^T
-  // bf16: two LDS buffers per wave (the next chunk's copies fly while this
-  // one is computed); FP8: one, the next chunk's bytes wait in registers
-  constexpr int NBUF = kFp8 ? 1 : 2;
+  // bf16: NBUF LDS buffers per wave, the copies of the next NBUF - 1 chunks
+  // in flight while one is computed -- two in 4-wave workgroups (two of
+  // them fit a CU), three in 1-wave workgroups (few KV heads: measured +22%
+  // at A_kv = 2, +2% at A_kv = 1 over two; four cost more waves per CU than
+  // the deeper prefetch gains); FP8: one, the next chunk's bytes wait in
+  // registers
+  constexpr int NBUF = kFp8 ? 1 : (WPG == 1 ? kDecodeBufsOneWave : 2);
   constexpr int BUF_BYTES = 2 * kChunk * RC * 16;  // bytes: K then V
   constexpr int WAVE_LDS = NBUF * BUF_BYTES;
   static_assert(64 % RC == 0 && kChunk % TOK_PER_LD == 0, "row split");
@@ -255,7 +260,9 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
     if constexpr (kFp8) {
       if (t_begin < t_end) fp8_load(t_begin);
     } else {
-      if (t_begin < t_end) bf16_issue(t_begin, 0);
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i)
+        if (t_begin + i * kChunk < t_end) bf16_issue(t_begin + i * kChunk, i);
     }
 
     for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
@@ -280,22 +287,30 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
         vsc = vsc_n;
         if (c0 + kChunk < t_end) fp8_load(c0 + kChunk);
       } else {
-        // the next chunk's copies go into the other buffer before this chunk
-        // is waited for; vmcnt counts in issue order, so leaving the newest
-        // 2 N_LD copies outstanding means this chunk's have landed.  The
-        // wait is explicit (the compiler does not place its own before every
-        // read of LDS written this way) and the empty asm keeps the LDS reads
-        // below from moving above it.
-        const int buf = ((c0 - t_begin) / kChunk) & 1;
+        // the copies of chunk c0 + (NBUF - 1) 16 go into the buffer the
+        // previous step computed before this chunk is waited for; vmcnt
+        // counts in issue order, so leaving the copies of the chunks issued
+        // after this one outstanding (2 N_LD per chunk) means this chunk's
+        // have landed.  The wait is explicit (the compiler does not place
+        // its own before every read of LDS written this way) and the empty
+        // asm keeps the LDS reads below from moving above it.
+        const int step = (c0 - t_begin) / kChunk;
+        const int buf = step % NBUF;
         sK = sK0 + buf * BUF_BYTES;
         sV = sK + kChunk * RC * 16;
-        if (c0 + kChunk < t_end) {
-          bf16_issue(c0 + kChunk, buf ^ 1);
-          constexpr int n = 2 * N_LD;
-          static_assert(n < 64, "vmcnt field");
-          __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+        const int c_new = c0 + (NBUF - 1) * kChunk;
+        if (c_new < t_end) bf16_issue(c_new, (step + NBUF - 1) % NBUF);
+        // chunks after this one already issued: min(NBUF - 1, those left)
+        const int after = min(NBUF - 1, (t_end - c0 - 1) / kChunk);
+        static_assert(2 * N_LD * (NBUF - 1) < 64, "vmcnt field");
+        if (after >= 3) {
+          lds_copy_wait<2 * N_LD * 3>();
+        } else if (after == 2) {
+          lds_copy_wait<2 * N_LD * 2>();
+        } else if (after == 1) {
+          lds_copy_wait<2 * N_LD>();
         } else {
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+          lds_copy_wait<0>();
         }
         asm volatile("" ::: "memory");
       }
