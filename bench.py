@@ -44,7 +44,7 @@ unchanged (null otherwise).
 Per-workload kernel times from one kernel trace of this same command (the
 dense prefill kernel serves three workloads; they are told apart by grid size):
 
-    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline
+    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline
     python3 bench.py --trace-summary <dir_t> > profiles/kernel_trace_<...>.md
 
 Matrix-core utilisation of the prefill kernels, from one counter run:
@@ -426,7 +426,7 @@ def trace_summary(d: str):
                              int(r["Dispatch_Id"])))
     print("# Kernel trace of the bench, per kernel and workload\n")
     print("Commands (repository root, one MI355X):\n")
-    print("    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 10 --warmup 2 "
+    print("    rocprofv3 --kernel-trace --stats -f csv -d <dir_t> -o bench -- python3 bench.py --steps 20 --warmup 5 "
           "--no-cpu-baseline")
     print("    python3 bench.py --trace-summary <dir_t>\n")
     print("Each row: the dispatches of one kernel at one workload's grid (warm-up and timed launches).  "
