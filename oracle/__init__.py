@@ -498,12 +498,13 @@ class Oracle:
                                   causal=causal, window=window, rows=rows)
 
     def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
-                         seqs=None):
+                         seqs=None, window_left=None):
         """Paged decode over FP8 caches (E4M3 codes [P, page_size, A_kv, d] with
         per-(page, KV head) scales [P, A_kv]); q bf16 bits [B, A, d].  The cache
         values code value * scale are formed in fp64 for the pages each sequence
-        uses, and the sequence runs through decode_paged.  Returns (o [n, A, d],
-        lse [n, A]) for the sequences ``seqs`` (default: all)."""
+        uses, and the sequence runs through decode_paged (with its window,
+        window_left as there).  Returns (o [n, A, d], lse [n, A]) for the
+        sequences ``seqs`` (default: all)."""
         B, A, d = q.shape
         bt = np.asarray(block_table)
         sl = np.asarray(seq_lens)
@@ -518,7 +519,8 @@ class Oracle:
             kc = fp8_e4m3_value(k_codes[pages]) * np.asarray(k_scale, np.float64)[pages][:, None, :, None]
             vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale, np.float64)[pages][:, None, :, None]
             o, lse = self.decode_paged(qf[b:b + 1], kc, vc, np.arange(pages.size, dtype=np.int32)[None],
-                                       np.array([sl[b]], np.int32), dtype="f64", scale=scale)
+                                       np.array([sl[b]], np.int32), dtype="f64", scale=scale,
+                                       window_left=window_left)
             outs.append(o.reshape(A, d))
             lses.append(lse.reshape(A))
         return np.stack(outs), np.stack(lses)

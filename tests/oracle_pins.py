@@ -620,6 +620,41 @@ def pin_fp8_decode_brute_force(orc):
             assert (wl == -math.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - wl) < 1e-13
 
 
+def pin_fp8_decode_window_brute_force(orc):
+    """FP8 paged decode under a sliding window ("Attention Kernel", 可编程 mask:
+    the query at position len - 1 sees the keys t >= len - 1 - w) against
+    math.fsum over the visible dequantised keys alone, for windows of 0, 2
+    and 9 keys and one reaching past the first token."""
+    import oracle as oracle_pkg
+    rng = np.random.default_rng(52)
+    ps, A, A_kv, d = 4, 4, 2, 3
+    lens = np.array([11, 1, 0, 6], np.int32)
+    bt = np.array([[3, 0, 5], [1, -1, -1], [-1, -1, -1], [2, 4, -1]], np.int32)
+    kc = rng.integers(0, 0x7F, size=(6, ps, A_kv, d)).astype(np.uint8) | (rng.integers(0, 2, size=(6, ps, A_kv, d)) * 0x80).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, size=(6, ps, A_kv, d)).astype(np.uint8)
+    ksc = rng.uniform(0.001, 0.01, size=(6, A_kv)).astype(np.float32)
+    vsc = rng.uniform(0.001, 0.01, size=(6, A_kv)).astype(np.float32)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((4, A, d)).astype(np.float32))
+    qv = gen.bf16_bits_to_f32(q).astype(np.float64)
+    G = A // A_kv
+    for w in (0, 2, 9, 50):
+        o, lse = orc.decode_paged_fp8(q, kc, vc, ksc, vsc, bt, lens, scale=0.75, window_left=w)
+        for b in range(4):
+            L = int(lens[b])
+            for h in range(A):
+                hk = h // G
+                keys, vals = [], []
+                for t in range(max(0, L - 1 - w), L):
+                    pg, off = int(bt[b, t // ps]), t % ps
+                    keys.append([float(x) * float(ksc[pg, hk]) for x in oracle_pkg.fp8_e4m3_value(kc[pg, off, hk])])
+                    vals.append([float(x) * float(vsc[pg, hk]) for x in oracle_pkg.fp8_e4m3_value(vc[pg, off, hk])])
+                want, wl = _brute([float(x) for x in qv[b, h]], keys, vals, 0.75, [True] * len(keys))
+                if not keys:
+                    want = [0.0] * d
+                assert np.allclose(o[b, h], want, rtol=0, atol=1e-13), (w, b, h)
+                assert (wl == -math.inf and lse[b, h] == -np.inf) or abs(lse[b, h] - wl) < 1e-13, (w, b, h)
+
+
 def pin_fp8_prefill_brute_force(orc):
     """FP8 dense prefill (E4M3 codes, one scale per 128 tokens of each head)
     against math.fsum over the dequantised rows: S = 300 queries and keys span

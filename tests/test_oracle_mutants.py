@@ -99,6 +99,7 @@ PY_MUTANTS = [
     ("FP8 prefill: 64-token query scale blocks", "np.repeat(qs, 128, axis=2)", "np.repeat(qs, 64, axis=2)", 0),
     ("FP8 prefill: key scales ignored", "kv = fp8_e4m3_value(kc) * np.repeat(ks, 128, axis=2)[:, :, :S_k, None]",
      "kv = fp8_e4m3_value(kc) * 1.0", 0),
+    ("FP8 decode: window ignored", "window_left=window_left)", "window_left=None)", 0),
     ("FP8 decode: value scale of the key", "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale",
      "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(k_scale", 0),
     ("FP8 paged prefill: value scale of the key", "vc = fp8_e4m3_value(v_codes) * np.asarray(v_scale",
