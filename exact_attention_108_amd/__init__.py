@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_decode_paged,
     attn_decode_paged_fp8,
+    attn_decode_paged_fp8_window,
     attn_decode_paged_noalloc,
     attn_decode_paged_window,
     DECODE_NOALLOC_MAX_BYTES,

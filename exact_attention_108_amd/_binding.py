@@ -72,6 +72,9 @@ _lib.attn_bwd_workspace_bytes.restype = _sz
 _lib.attn_decode_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                        _f, _vp, _sz, _vp]
 _lib.attn_decode_paged_fp8.restype = _i
+_lib.attn_decode_paged_fp8_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                                              _i, _f, _i, _vp, _sz, _vp]
+_lib.attn_decode_paged_fp8_window.restype = _i
 _lib.attn_status_string.argtypes = [_i]
 _lib.attn_status_string.restype = ctypes.c_char_p
 _lib.attn_abi_version.argtypes = []
@@ -100,6 +103,7 @@ def exported_symbols():
             "attn_decode_paged_window", "attn_prefill_paged_masked",
             "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8", "attn_decode_paged_fp8",
+            "attn_decode_paged_fp8_window",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
 
 
@@ -624,6 +628,20 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, se
                           workspace, *, scale: float, stream=None):
     """Paged decode over FP8 (E4M3) caches: q/o bf16 [B,A,d]; caches uint8 [num_pages, page_size, A_kv, d];
     k_scale/v_scale fp32 [num_pages, A_kv]; the rest as attn_decode_paged."""
+    _fp8_decode_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse, workspace,
+                     scale, None, stream)
+
+
+def attn_decode_paged_fp8_window(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o,
+                                 lse, workspace, *, scale: float, window_left: int, stream=None):
+    """attn_decode_paged_fp8 where the query of sequence b sees only the keys t >= seq_lens[b] - 1 - window_left
+    (-1: every key)."""
+    _fp8_decode_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse, workspace,
+                     scale, int(window_left), stream)
+
+
+def _fp8_decode_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse, workspace,
+                     scale, window_left, stream):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
@@ -647,8 +665,11 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, se
         raise ValueError("seq_lens_host must be [B]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse, workspace)
-    st = _lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-                                    _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp), page_size, _ptr(o),
-                                    _ptr(lse), B, A, A_kv, d, block_table.shape[1], num_pages, float(scale),
-                                    _ptr(workspace), ws_bytes, _stream(stream, dev))
-    _check(st, "attn_decode_paged_fp8")
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+            sl.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), B, A, A_kv, d, block_table.shape[1], num_pages,
+            float(scale))
+    tail = (_ptr(workspace), ws_bytes, _stream(stream, dev))
+    if window_left is None:
+        _check(_lib.attn_decode_paged_fp8(*args, *tail), "attn_decode_paged_fp8")
+    else:
+        _check(_lib.attn_decode_paged_fp8_window(*args, window_left, *tail), "attn_decode_paged_fp8_window")

@@ -676,12 +676,13 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   return launch_status(attn::launch_bwd_bf16(p, (hipStream_t)stream));
 }
 
-ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
-                                              const float* k_scale, const float* v_scale,
-                                              const int32_t* block_table, const int32_t* seq_lens,
-                                              const int32_t* seq_lens_host, int page_size, void* o, float* lse,
-                                              int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
-                                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+attn_status decode_fp8_call(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, const float* k_scale,
+                            const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* seq_lens_host, int page_size, void* o, float* lse, int B, int A,
+                            int A_kv, int d_h, int max_pages, int num_pages, float scale, int window_left,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
   attn_status st = check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, max_pages, true);
   if (st != ATTN_OK) return st;
@@ -695,13 +696,13 @@ ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_ca
   for (const void* t : {(const void*)lse, (const void*)seq_lens, (const void*)block_table, (const void*)k_scale,
                         (const void*)v_scale})
     if (!aligned(t, 4)) return ATTN_ERR_INVAL;
-  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host);
+  const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host, window_left);
   const size_t need = attn::decode_workspace_bytes(A, d_h, plan);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
     return ATTN_ERR_INVAL;
   if ((long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   attn::DecodeParams p{};
-  p.win_left = -1;
+  p.win_left = window_left;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -724,6 +725,31 @@ ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_ca
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return launch_status(attn::launch_decode_fp8(p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+ATTN_EXPORT attn_status attn_decode_paged_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                              const float* k_scale, const float* v_scale,
+                                              const int32_t* block_table, const int32_t* seq_lens,
+                                              const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                              int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_fp8_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, page_size, o,
+                         lse, B, A, A_kv, d_h, max_pages, num_pages, scale, -1, workspace, workspace_bytes, stream);
+}
+
+ATTN_EXPORT attn_status attn_decode_paged_fp8_window(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                                     const float* k_scale, const float* v_scale,
+                                                     const int32_t* block_table, const int32_t* seq_lens,
+                                                     const int32_t* seq_lens_host, int page_size, void* o,
+                                                     float* lse, int B, int A, int A_kv, int d_h, int max_pages,
+                                                     int num_pages, float scale, int window_left, void* workspace,
+                                                     size_t workspace_bytes, void* stream) {
+  if (window_left < -1) return ATTN_ERR_INVAL;
+  return decode_fp8_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, page_size, o,
+                         lse, B, A, A_kv, d_h, max_pages, num_pages, scale, window_left, workspace,
+                         workspace_bytes, stream);
 }
 
 ATTN_EXPORT const char* attn_status_string(attn_status s) {

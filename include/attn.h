@@ -53,7 +53,7 @@
 #include <stdint.h>
 
 /* The value attn_abi_version() returns for this header. */
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 #ifdef __cplusplus
 extern "C" {
@@ -288,6 +288,23 @@ attn_status attn_decode_paged_fp8(const void *q, const uint8_t *k_cache, const u
                                   const int32_t *seq_lens_host, int page_size, void *o, float *lse,
                                   int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
                                   float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_paged_fp8 with a sliding window (page "Attention Kernel",
+ * section "可编程 mask"), defined as for attn_decode_paged_window: the query
+ * of sequence b sees the keys t >= seq_lens[b] - 1 - window_left, and only
+ * the 16-token chunks from the one holding the first visible key are read.
+ * window_left = -1 is attn_decode_paged_fp8 (every key; bit for bit).
+ * Arguments, workspace, support and errors as attn_decode_paged_fp8;
+ * window_left < -1 is ATTN_ERR_INVAL.
+ */
+attn_status attn_decode_paged_fp8_window(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                         const float *k_scale, const float *v_scale,
+                                         const int32_t *block_table, const int32_t *seq_lens,
+                                         const int32_t *seq_lens_host, int page_size, void *o, float *lse,
+                                         int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                         float scale, int window_left, void *workspace,
+                                         size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode_paged without a caller workspace, for callers that cannot

@@ -23,7 +23,7 @@ def test_header_declares_entry_points():
                                          "attn_decode_paged_window", "attn_prefill_paged_masked",
                                          "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8",
-                                         "attn_decode_paged_fp8",
+                                         "attn_decode_paged_fp8", "attn_decode_paged_fp8_window",
                                          "attn_block_keep_from_bias", "attn_status_string",
                                          "attn_abi_version"])
 
@@ -42,7 +42,7 @@ def test_library_exports_exactly_the_header():
 
 def test_status_strings_and_version():
     import exact_attention_108_amd as ea
-    assert ea.attn_abi_version() == 4
+    assert ea.attn_abi_version() == 5
     assert ea.attn_status_string(0) == "ok"
     assert ea.attn_status_string(1) == "invalid argument"
     assert ea.attn_status_string(2) == "unsupported configuration"
@@ -462,6 +462,26 @@ def test_decode_window_rejects_bad_arguments():
     assert call(4, q=odd8) == INVAL and call(4, kc=odd8) == INVAL
     assert lib.attn_decode_paged_window(P, P, P, P, P, lp, 16, P, P, 2, 8, 3, 128, 3, 6, 0.1, 4, 1, P, 1 << 30,
                                         None) == INVAL   # A % A_kv
+
+
+def test_decode_fp8_window_rejects_bad_arguments():
+    """attn_decode_paged_fp8_window: window_left >= -1, and otherwise the checks
+    of attn_decode_paged_fp8 (host-side, before any device call)."""
+    lib = _lib()
+    INVAL = 1
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_decode_paged_fp8_window.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 6 + [f, i, vp, sz, vp]
+    lens = np.array([10, 40], np.int32)
+    lp = lens.ctypes.data_as(ctypes.c_void_p)
+    odd = ctypes.c_void_p(4096 + 4)
+    call = lambda wl, q=P, kc=P, ks=P, A_kv=2: lib.attn_decode_paged_fp8_window(
+        q, kc, P, ks, P, P, P, lp, 16, P, P, 2, 8, A_kv, 128, 3, 6, 0.1, wl, P, 1 << 30, None)
+    assert call(-2) == INVAL
+    assert call(-9) == INVAL
+    assert call(3, kc=odd) == INVAL                 # caches 8-byte aligned
+    assert call(3, q=ctypes.c_void_p(4096 + 8)) == INVAL
+    assert call(3, ks=ctypes.c_void_p(4096 + 2)) == INVAL
+    assert call(3, A_kv=3) == INVAL                 # A % A_kv
 
 
 def test_prefill_paged_masked_rejects_bad_arguments():

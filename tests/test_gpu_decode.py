@@ -136,7 +136,7 @@ def test_config4_full(ea, orc):
 # so the rounding budget (bf16 P, bf16 O) is the same; the oracle decodes the
 # same codes exactly.
 
-def run_decode_fp8(ea, pf):
+def run_decode_fp8(ea, pf, window_left=None):
     t = gu.torch()
     p = pf.base
     q = gu.dev(p.q, "bf16")
@@ -153,7 +153,11 @@ def run_decode_fp8(ea, pf):
     nbytes = ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens)
     ws = t.empty(max(nbytes, 1), dtype=t.uint8, device="cuda")
     ws.fill_(0xFF)
-    ea.attn_decode_paged_fp8(q, kc, vc, ks, vs, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale)
+    if window_left is None:
+        ea.attn_decode_paged_fp8(q, kc, vc, ks, vs, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale)
+    else:
+        ea.attn_decode_paged_fp8_window(q, kc, vc, ks, vs, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale,
+                                        window_left=window_left)
     t.cuda.synchronize()
     return gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
 
@@ -245,6 +249,36 @@ def test_decode_window_edges(ea):
         last = vf[p.block_table[b, (n - 1) // 16], (n - 1) % 16]  # [A_kv, d]
         for h in range(p.A):
             assert np.array_equal(o3[b, h], last[h // (p.A // p.A_kv)]), (b, h)
+
+
+FP8_WINDOW_CASES = [
+    # lens, A, A_kv, d, page_size, window_left
+    ([1, 15, 16, 17, 33, 0, 500, 1000], 8, 2, 128, 16, 16),
+    ([64, 65, 3000, 129], 4, 4, 128, 16, 100),
+    ([5, 77, 1025], 16, 1, 64, 32, 40),
+    ([700, 3, 2049], 32, 1, 128, 16, 511),
+    ([1200, 5, 640], 32, 2, 128, 16, 0),
+]
+
+
+@pytest.mark.parametrize("case", FP8_WINDOW_CASES,
+                         ids=lambda c: f"{len(c[0])}seq-A{c[1]}-kv{c[2]}-d{c[3]}-ps{c[4]}-w{c[5]}")
+def test_decode_fp8_window(ea, orc, case):
+    """Sliding-window decode over E4M3 caches against the oracle's FP8 decode
+    under the same window; window -1 and a window reaching every first token
+    give attn_decode_paged_fp8's bits."""
+    lens, A, A_kv, d, ps, w = case
+    _say("decode fp8 window", case)
+    pf = gen.make_paged_fp8(lens, A, A_kv, d, ps, seed=71 + sum(lens) + w, extra_pages=2)
+    o, lse = run_decode_fp8(ea, pf, window_left=w)
+    p = pf.base
+    o_ref, l_ref = orc.decode_paged_fp8(p.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, p.block_table,
+                                        p.seq_lens, scale=p.scale, window_left=w)
+    gu.check(o, lse, o_ref, l_ref, "bf16", f"fp8 window {case}")
+    o0, l0 = run_decode_fp8(ea, pf)
+    for wl in (-1, max(lens)):
+        o1, l1 = run_decode_fp8(ea, pf, window_left=wl)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1), wl
 
 
 def test_config4_window_full_size_sampled(ea, orc):

@@ -179,6 +179,40 @@ def test_sweep_decode(ea, orc, seed):
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"decode {seed}"))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_decode_fp8(ea, orc, seed):
+    """Seeded E4M3-cache decodes: lengths, heads, head dim, page size and an
+    optional window drawn per seed."""
+    rng = np.random.default_rng(6500 + seed)
+    lens = [int(x) for x in rng.integers(0, 3000, size=int(rng.integers(1, 9)))]
+    d = int(rng.choice([64, 128]))
+    A_kv = int(rng.choice([1, 2, 4, 8]))
+    A = A_kv * int(rng.choice([1, 2, 4, 8, 16, 32] if A_kv <= 2 else [1, 2, 4, 8, 16]))
+    ps = int(rng.choice([16, 32, 64]))
+    wl = int(rng.choice([-1, rng.integers(0, 2000)])) if rng.random() < 0.5 else None
+    _say("sweep decode fp8", (seed, lens, A, A_kv, d, ps, "window", wl))
+    pf = gen.make_paged_fp8(lens, A, A_kv, d, ps, seed=6500 + seed, extra_pages=3)
+    p = pf.base
+    t = gu.torch()
+    q = gu.dev(p.q, "bf16")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, A), dtype=t.float32, device="cuda")
+    nbytes = ea.attn_decode_paged_workspace_bytes(p.B, A, A_kv, d, ps, p.seq_lens)
+    ws = t.empty(max(nbytes, 1), dtype=t.uint8, device="cuda")
+    args = (q, t.from_numpy(pf.k_codes).cuda(), t.from_numpy(pf.v_codes).cuda(), t.from_numpy(pf.k_scale).cuda(),
+            t.from_numpy(pf.v_scale).cuda(), gu.dev(p.block_table, "i32"), gu.dev(p.seq_lens, "i32"), p.seq_lens,
+            o, lse, ws)
+    if wl is None:
+        ea.attn_decode_paged_fp8(*args, scale=p.scale)
+    else:
+        ea.attn_decode_paged_fp8_window(*args, scale=p.scale, window_left=wl)
+    t.cuda.synchronize()
+    o_ref, l_ref = orc.decode_paged_fp8(p.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, p.block_table,
+                                        p.seq_lens, scale=p.scale, window_left=wl)
+    _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16",
+                  f"decode fp8 {seed}"))
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_sweep_backward(ea, orc, seed):
     rng = np.random.default_rng(7000 + seed)
