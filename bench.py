@@ -532,6 +532,8 @@ def main():
                     help="summarise three counter runs of --traffic-workload and exit")
     ap.add_argument("--counter-summary", metavar="DIR", help="summarise one SQ counter run and exit")
     ap.add_argument("--trace-summary", metavar="DIR", help="summarise one kernel trace of the bench and exit")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="time the paged decode at other page sizes, batch sizes and length mixes and exit")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary)
@@ -544,6 +546,9 @@ def main():
         return
     if args.traffic_workload:
         traffic_workload()
+        return
+    if args.decode_sweep:
+        decode_sweep(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on a single device "
@@ -983,6 +988,80 @@ def bench_block_sparse(w, steps: int, warmup: int) -> dict:
             "min_ms": round(float(ms.min()), 5), "flops": flops, "blocks_kept": int(bk.sum()),
             "blocks_total": int(bk.size),
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 with a seeded 50% block mask (128 x 128 blocks)"}
+
+
+def decode_sweep_configs():
+    """(label, lengths, page size) of the decode sweep: the decode workload's
+    shape (A = 32, A_kv = 8, d = 128, bf16 cache) at other page sizes, batch
+    sizes and length mixes, all lengths seeded."""
+    from synth import gen
+    ld = gen.config_lengths_decode()
+    rng = np.random.default_rng(1041)
+    return [
+        ("page 16, the decode workload's 64 lengths U{512..32768}", ld, 16),
+        ("page 64, the same lengths", ld, 64),
+        ("page 256, the same lengths", ld, 256),
+        ("8 sequences, lengths U{512..32768}", rng.integers(512, 32769, 8).astype(np.int32), 16),
+        ("256 sequences, lengths U{512..8192}", rng.integers(512, 8193, 256).astype(np.int32), 16),
+        ("256 sequences of 1024 tokens", np.full(256, 1024, np.int32), 16),
+        ("16 sequences, log-normal lengths (median 8192, sigma 1, 512..131072)",
+         gen.lognormal_lengths(16, 8192.0, 1.0, 512, 131072, 1042).astype(np.int32), 16),
+    ]
+
+
+def decode_sweep(steps: int, warmup: int):
+    """The paged decode by page size, batch size and length mix (the pages ask
+    for these reported separately): KV GB/s = 2 A_kv d 2 bytes x tokens / time
+    (split + merge).  Caches and queries are seeded N(0, 1) drawn on the GPU,
+    pages a seeded permutation of the pool.  Prints a markdown table, then one
+    JSON line."""
+    import torch
+    import exact_attention_108_amd as ea
+    assert torch.cuda.is_available(), "the decode sweep needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    A, A_kv, d = 32, 8, 128
+    g = torch.Generator(device="cuda").manual_seed(1043)
+    rows = []
+    for label, lens, ps in decode_sweep_configs():
+        lens = np.asarray(lens, np.int32)
+        B = len(lens)
+        n_pages = (lens.astype(np.int64) + ps - 1) // ps
+        P = int(n_pages.sum())
+        perm = np.random.default_rng(1044).permutation(P).astype(np.int32)
+        bt = np.full((B, int(n_pages.max())), -1, np.int32)
+        at = 0
+        for b in range(B):
+            bt[b, :n_pages[b]] = perm[at:at + n_pages[b]]
+            at += int(n_pages[b])
+        kc = torch.randn((P, ps, A_kv, d), generator=g, device="cuda").to(torch.bfloat16)
+        vc = torch.randn((P, ps, A_kv, d), generator=g, device="cuda").to(torch.bfloat16)
+        q = torch.randn((B, A, d), generator=g, device="cuda").to(torch.bfloat16)
+        btd, sld = torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+        o = torch.empty_like(q)
+        lse = torch.empty((B, A), dtype=torch.float32, device="cuda")
+        nb = ea.attn_decode_paged_workspace_bytes(B, A, A_kv, d, ps, lens)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        ms = _event_times(lambda: ea.attn_decode_paged(q, kc, vc, btd, sld, lens, o, lse, ws, scale=d ** -0.5,
+                                                       stream=stream), steps, warmup, stream)
+        tokens = int(lens.astype(np.int64).sum())
+        kvb = 2.0 * A_kv * d * 2 * tokens
+        gbs = kvb / (ms.mean() * 1e-3) / 1e9
+        rows.append({"workload": label, "sequences": B, "tokens": tokens, "page_size": ps,
+                     "value": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBPS, 4),
+                     "avg_ms": round(float(ms.mean()), 5), "median_ms": round(float(np.median(ms)), 5),
+                     "kv_bytes": kvb})
+        log(f"decode sweep: {label}: {gbs:.0f} GB/s")
+        del kc, vc, q, o, lse, ws, btd, sld
+        torch.cuda.empty_cache()
+    print(f"| workload (A = 32, A_kv = 8, d = 128, bf16 cache) | sequences | tokens | page | avg ms | KV GB/s | of "
+          f"{PEAK_HBM_GBPS:.0f} |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['workload']} | {r['sequences']} | {r['tokens']} | {r['page_size']} | {r['avg_ms']:.3f} | "
+              f"{r['value']:.0f} | {100 * r['frac_of_hbm_peak']:.1f}% |")
+    print(json.dumps({"metric": "paged-decode KV GB/s by page size, batch size and length mix", "unit": "GB/s",
+                      "steps": steps, "warmup": warmup, "rows": rows}), flush=True)
 
 
 def _event_times(run, steps: int, warmup: int, stream) -> np.ndarray:
