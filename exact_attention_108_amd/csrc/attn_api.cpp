@@ -255,6 +255,8 @@ attn_status check_decode(int B, int A, int A_kv, int d_h, int page_size, const i
   for (int b = 0; b < B; ++b) {
     if (seq_lens_host[b] < 0) return ATTN_ERR_INVAL;
     if (check_pages && (long long)seq_lens_host[b] > (long long)max_pages * page_size) return ATTN_ERR_INVAL;
+    // the split kernels count positions in int32, up to a few chunks past a length
+    if (seq_lens_host[b] > INT_MAX - 256) return ATTN_ERR_UNSUPPORTED;
   }
   if (d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
   if (page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;

@@ -237,7 +237,7 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
  * block table names (bit for bit), while devices or partition modes with a
  * different CU count may round differently, within the stated tolerance.
  * Supported: bf16, d_h in {64, 128}, page_size a multiple of 16, A / A_kv <= 64
- * (MQA included).
+ * (MQA included), lengths up to 2^31 - 257 (longer: ATTN_ERR_UNSUPPORTED).
  */
 attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                               const int32_t *block_table, const int32_t *seq_lens,

@@ -464,6 +464,30 @@ def test_decode_window_rejects_bad_arguments():
                                         None) == INVAL   # A % A_kv
 
 
+def test_decode_rejects_lengths_near_int32_max():
+    """Lengths above 2^31 - 257 are unsupported by every paged decode (the
+    split kernels count positions in int32); the check runs before any
+    pointer is used."""
+    lib = _lib()
+    UNSUP = 2
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_decode_paged.argtypes = [vp] * 6 + [i, vp, vp] + [i] * 6 + [f, i, vp, sz, vp]
+    lib.attn_decode_paged_fp8.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 6 + [f, vp, sz, vp]
+    lib.attn_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, vp]
+    lib.attn_decode_paged_workspace_bytes.restype = sz
+    big = (1 << 31) - 200
+    lens = np.array([10, big], np.int32)
+    lp = lens.ctypes.data_as(ctypes.c_void_p)
+    max_pages = big // 16 + 1
+    assert lib.attn_decode_paged(P, P, P, P, P, lp, 16, P, P, 2, 8, 2, 128, max_pages, 6, 0.1, 1, P, 1 << 40,
+                                 None) == UNSUP
+    assert lib.attn_decode_paged_fp8(P, P, P, P, P, P, P, lp, 16, P, P, 2, 8, 2, 128, max_pages, 6, 0.1, P,
+                                     1 << 40, None) == UNSUP
+    assert lib.attn_decode_paged_workspace_bytes(2, 8, 2, 128, 16, lp) == 0
+    lens[1] = (1 << 31) - 257
+    assert lib.attn_decode_paged_workspace_bytes(2, 8, 2, 128, 16, lp) > 0
+
+
 def test_decode_fp8_window_rejects_bad_arguments():
     """attn_decode_paged_fp8_window: window_left >= -1, and otherwise the checks
     of attn_decode_paged_fp8 (host-side, before any device call)."""
