@@ -37,6 +37,10 @@ bool window_arith_fits(const attn_window* w, long long rows, long long keys) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Longest sequence (rows or keys) any call takes: the kernels count positions
+// in int32 and round up to a tile or chunk past a length.
+constexpr int kMaxLen = INT_MAX - 1024;
+
 // tensor alignment the kernels' vector loads and stores need: 16 bytes for
 // bf16 rows (16-byte copies into LDS and stores), 4 for fp32 elements
 uintptr_t data_align(attn_dtype dtype) { return dtype == ATTN_BF16 ? 16 : 4; }
@@ -108,6 +112,8 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   const bool bias = mask && mask->bias;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
   if (bias && dtype == ATTN_BF16 && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
+  // the kernels count rows and key positions in int32, up to a tile past a length
+  if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (S_q == 0) return ATTN_OK;
   const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
   const long long n_qt = (S_q + rows - 1) / rows;
@@ -153,6 +159,7 @@ ATTN_EXPORT attn_status attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const v
   if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;
   if (S_k > attn::kFp8MaxKeys) return ATTN_ERR_UNSUPPORTED;
   if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
+  if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (S_q == 0) return ATTN_OK;
   const long long n_qt = (S_q + attn::kPrefillRows - 1) / attn::kPrefillRows;
   if (n_qt * (long long)A * (long long)B > INT_MAX) return ATTN_ERR_UNSUPPORTED;
@@ -174,6 +181,7 @@ ATTN_EXPORT attn_status attn_block_keep_from_bias(const float* bias, int B, int 
   if (B < 1 || S_q < 0 || S_k < 0 || bias_heads < 1) return ATTN_ERR_INVAL;
   if (!bias || !block_keep || !valid_bias(bias, bias_heads, bias_heads, S_q, S_k, bias_ld)) return ATTN_ERR_INVAL;
   if (S_q == 0 || S_k == 0) return ATTN_OK;  // the block mask is empty
+  if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   const long long n_qb = (S_q + 127) / 128, n_kb = (S_k + 127) / 128;
   if ((long long)B * bias_heads * n_qb > INT_MAX || n_kb > 65535) return ATTN_ERR_UNSUPPORTED;
   return launch_status(attn::launch_block_keep_from_bias(bias, B, bias_heads, S_q, S_k, bias_ld, block_keep,
@@ -209,6 +217,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   if ((blocks || bias) && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (blocks && max_len > 262144) return ATTN_ERR_UNSUPPORTED;
   if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
+  if (max_len > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;
   if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   const int rows = dtype == ATTN_BF16 ? attn::kPrefillRows : attn::kPrefillRowsF32;
@@ -256,7 +265,7 @@ attn_status check_decode(int B, int A, int A_kv, int d_h, int page_size, const i
     if (seq_lens_host[b] < 0) return ATTN_ERR_INVAL;
     if (check_pages && (long long)seq_lens_host[b] > (long long)max_pages * page_size) return ATTN_ERR_INVAL;
     // the split kernels count positions in int32, up to a few chunks past a length
-    if (seq_lens_host[b] > INT_MAX - 256) return ATTN_ERR_UNSUPPORTED;
+    if (seq_lens_host[b] > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   }
   if (d_h != 64 && d_h != 128) return ATTN_ERR_UNSUPPORTED;
   if (page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
@@ -427,6 +436,7 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, max_q, max_kv_len, mask->bias_ld)) return ATTN_ERR_INVAL;
   if ((blocks || bias) && fp8) return ATTN_ERR_UNSUPPORTED;
+  if (max_q > kMaxLen || max_kv_len > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (blocks && max_kv_len > 262144) return ATTN_ERR_UNSUPPORTED;
   if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
@@ -583,6 +593,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   const bool bias = mask && mask->bias;
   if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   const long long n_qb = (S_q + 127) / 128, n_kb = (S_k + 127) / 128;
   if (blocks && (n_kb > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * n_qb > attn::kBwdMaxRowBlocks))
     return ATTN_ERR_UNSUPPORTED;
@@ -651,7 +662,7 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   if (blocks && (max_tiles > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * max_tiles > attn::kBwdMaxRowBlocks))
     return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;
-  if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+  if (max_len > kMaxLen || (long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   if (total_tiles * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   if (!window_arith_fits(window, max_len, max_len)) return ATTN_ERR_UNSUPPORTED;
   const size_t need = bwd_workspace_bytes(1, A, total_tokens);

@@ -26,8 +26,11 @@
  *     ATTN_F32: q/k/v/o are fp32.  lse is always fp32, natural log.
  *   - GQA: query head h reads KV head h / (A / A_kv) (contiguous groups; page
  *     "Attention Kernel", section "问题与成本", GQA paragraph).
- *   - Mask: M_ij is the optional dense additive term bias[i][j] (attn_fwd
- *     only, see attn_mask) plus -inf when: causal and j > i + (S_k - S_q)
+ *   - Lengths: a sequence (S_q, S_k, a packed sequence, a chunk or a cached
+ *     length) of more than 2^31 - 1025 positions is ATTN_ERR_UNSUPPORTED
+ *     (the kernels count positions in int32, up to a tile past a length).
+ *   - Mask: M_ij is the optional dense additive term bias[i][j] (see
+ *     attn_mask) plus -inf when: causal and j > i + (S_k - S_q)
  *     (bottom-right alignment), q_keep[i] == 0, k_keep[j] == 0, a window or
  *     a block mask excludes (i, j).  A row with every key masked (including
  *     S_k == 0) returns O = 0 and LSE = -inf (page "Attention Kernel",
@@ -237,7 +240,7 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
  * block table names (bit for bit), while devices or partition modes with a
  * different CU count may round differently, within the stated tolerance.
  * Supported: bf16, d_h in {64, 128}, page_size a multiple of 16, A / A_kv <= 64
- * (MQA included), lengths up to 2^31 - 257 (longer: ATTN_ERR_UNSUPPORTED).
+ * (MQA included).
  */
 attn_status attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                               const int32_t *block_table, const int32_t *seq_lens,

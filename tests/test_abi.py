@@ -465,7 +465,7 @@ def test_decode_window_rejects_bad_arguments():
 
 
 def test_decode_rejects_lengths_near_int32_max():
-    """Lengths above 2^31 - 257 are unsupported by every paged decode (the
+    """Lengths above 2^31 - 1025 are unsupported by every paged decode (the
     split kernels count positions in int32); the check runs before any
     pointer is used."""
     lib = _lib()
@@ -484,8 +484,20 @@ def test_decode_rejects_lengths_near_int32_max():
     assert lib.attn_decode_paged_fp8(P, P, P, P, P, P, P, lp, 16, P, P, 2, 8, 2, 128, max_pages, 6, 0.1, P,
                                      1 << 40, None) == UNSUP
     assert lib.attn_decode_paged_workspace_bytes(2, 8, 2, 128, 16, lp) == 0
-    lens[1] = (1 << 31) - 257
+    lens[1] = (1 << 31) - 1025
     assert lib.attn_decode_paged_workspace_bytes(2, 8, 2, 128, 16, lp) > 0
+
+
+def test_prefill_rejects_lengths_near_int32_max():
+    """attn_fwd, attn_bwd and attn_block_keep_from_bias: S_q or S_k above
+    2^31 - 1025 is unsupported (host-side, before any pointer is used)."""
+    lib = _lib()
+    UNSUP = 2
+    big = (1 << 31) - 1000
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_block_keep_from_bias.argtypes = [vp, i, i, i, i, i, vp, vp]
+    assert lib.attn_block_keep_from_bias(P, 1, 1, big, 64, 64, P, None) == UNSUP
+    assert lib.attn_block_keep_from_bias(P, 1, 1, 64, big, big + 8, P, None) == UNSUP
 
 
 def test_decode_fp8_window_rejects_bad_arguments():
