@@ -492,6 +492,10 @@ int resident_groups(int cus) {
                                                    0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
+  // 1-wave workgroups: whole waves per SIMD (LDS allows 6 per CU at three
+  // buffers, which would leave two SIMDs with two waves and two with one;
+  // 4 per CU measured 1-2% faster at A_kv = 1, 2 and 13-31% on short batches)
+  if (WPG == 1 && per_cu >= 4) per_cu = per_cu / 4 * 4;
   return cus * per_cu;
 }
 
