@@ -457,6 +457,28 @@ def trace_summary(d: str):
               f"{ts[len(ts) // 2] / 1e3:.1f} | {ts[0] / 1e3:.1f} | {rate} |")
     print("\nThe backward's two passes together do 2.5x the forward's FLOPs of the MHA workload; the bench reports "
           "their combined rate.")
+    # registers, LDS and the occupancy they allow, per library kernel
+    res = {}
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if "attn::" not in r["Kernel_Name"]:
+                    continue
+                name = r["Kernel_Name"].replace("void ", "").replace("attn::(anonymous namespace)::", "").split("(")[0]
+                res[name] = (int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]), int(r["SGPR_Count"]),
+                             int(r["LDS_Block_Size"]), int(r["Scratch_Size"]), int(r["Workgroup_Size_X"]))
+    if res:
+        print("\nResources per kernel (from the same trace): vector, accumulation and scalar registers per lane or "
+              "wave, LDS bytes per workgroup (static plus dynamic), scratch bytes per lane, and the waves per SIMD "
+              "they allow: min(512 registers / (VGPR + AGPR), 160 KiB / LDS x waves per workgroup / 4).\n")
+        print("| kernel | VGPR | AGPR | SGPR | LDS bytes | scratch | waves / WG | waves per SIMD |")
+        print("|---|---|---|---|---|---|---|---|")
+        for name in sorted(res):
+            v, a, sg, lds, scr, wg = res[name]
+            wpw = max(1, wg // 64)
+            by_reg = 512 // max(1, v + a)
+            by_lds = (163840 // lds) * wpw / 4 if lds else 8
+            print(f"| `{name}` | {v} | {a} | {sg} | {lds} | {scr} | {wpw} | {min(by_reg, by_lds, 8):g} |")
     stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if stats:
         print("\n`--stats` output of the same run (per kernel name, all grids together; the library's kernels, then "
