@@ -468,17 +468,18 @@ def trace_summary(d: str):
                 res[name] = (int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]), int(r["SGPR_Count"]),
                              int(r["LDS_Block_Size"]), int(r["Scratch_Size"]), int(r["Workgroup_Size_X"]))
     if res:
-        print("\nResources per kernel (from the same trace): vector, accumulation and scalar registers per lane or "
-              "wave, LDS bytes per workgroup (static plus dynamic), scratch bytes per lane, and the waves per SIMD "
-              "they allow: min(512 registers / (VGPR + AGPR), 160 KiB / LDS x waves per workgroup / 4).\n")
-        print("| kernel | VGPR | AGPR | SGPR | LDS bytes | scratch | waves / WG | waves per SIMD |")
+        print("\nResources per kernel, as the trace records them: `VGPR_Count`, `Accum_VGPR_Count` and `SGPR_Count` "
+              "(on gfx950 the VGPR field reads half the registers the kernel allocates: 237 allocated read as 120), "
+              "LDS bytes per workgroup (static plus dynamic), scratch bytes per lane, and the waves per SIMD the LDS "
+              "allows (160 KiB / LDS x waves per workgroup / 4); the register budget each kernel is built for is "
+              "its `amdgpu_waves_per_eu` attribute.\n")
+        print("| kernel | VGPR field | AGPR | SGPR | LDS bytes | scratch | waves / WG | waves per SIMD (LDS) |")
         print("|---|---|---|---|---|---|---|---|")
         for name in sorted(res):
             v, a, sg, lds, scr, wg = res[name]
             wpw = max(1, wg // 64)
-            by_reg = 512 // max(1, v + a)
             by_lds = (163840 // lds) * wpw / 4 if lds else 8
-            print(f"| `{name}` | {v} | {a} | {sg} | {lds} | {scr} | {wpw} | {min(by_reg, by_lds, 8):g} |")
+            print(f"| `{name}` | {v} | {a} | {sg} | {lds} | {scr} | {wpw} | {min(by_lds, 8):g} |")
     stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if stats:
         print("\n`--stats` output of the same run (per kernel name, all grids together; the library's kernels, then "
