@@ -101,6 +101,17 @@ class Oracle:
         return bias, bias.shape[1]
 
     @staticmethod
+    def _keep_matrix(m_keep, key_range, B, S_q, S_k):
+        mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
+        if key_range is not None:
+            kr = np.asarray(key_range)
+            if kr.shape != (B, S_q, 2):
+                raise ValueError("key_range must be [B, S_q, 2]")
+            rk = key_range_keep(kr, S_k)
+            mk = rk if mk is None else mk & rk
+        return mk
+
+    @staticmethod
     def _rows(rows):
         if rows is None:
             return None, 0
@@ -108,9 +119,11 @@ class Oracle:
         return r, r.size
 
     def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None, bias=None,
-                 block_keep=None, rows=None):
+                 block_keep=None, rows=None, key_range=None):
         """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d]; m_keep an
-        optional dense keep matrix [B,S_q,S_k] (see window_keep); bias an optional
+        optional dense keep matrix [B,S_q,S_k] (see window_keep); key_range
+        optional per-row key ranges int [B,S_q,2] (see key_range_keep), applied
+        together with m_keep; bias an optional
         dense additive term M, fp32 [B,1,S_q,S_k] (every head) or [B,A,S_q,S_k],
         finite or -inf; block_keep an optional block mask uint8
         [B, 1 or A, ceil(S_q/128), ceil(S_k/128)] (0 masks the 128 x 128 block).
@@ -129,7 +142,7 @@ class Oracle:
             raise ValueError("A must be a multiple of A_kv")
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
-        mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
+        mk = self._keep_matrix(m_keep, key_range, B, S_q, S_k)
         bias, bh = self._bias(bias, B, A, S_q, S_k)
         bk, bkh = self._blocks(block_keep, B, A, S_q, S_k)
         r, n = self._rows(rows)
@@ -146,7 +159,7 @@ class Oracle:
         return o, lse
 
     def attn_fwd_varlen(self, q, k, v, cu_seqlens, *, dtype, scale, causal=True, q_keep=None,
-                        k_keep=None, rows=None, bias=None, block_keep=None, window=None):
+                        k_keep=None, rows=None, bias=None, block_keep=None, window=None, key_range=None):
         """Packed varlen attention.  q [A,T,d], k/v [A_kv,T,d]; rows = h*T + t.
 
         bias: fp32 [1 or A, T, ld] -- row t (token i of its sequence) holds the
@@ -154,13 +167,14 @@ class Oracle:
         sequence); block_keep: uint8 [n_seq, 1 or A, nb, nb], nb = ceil(longest
         length / 128), the 128 x 128 block flags of each sequence's own
         (row, key) grid; window: (left, right) around each row's position in
-        its sequence.  With any of these, each sequence is its own dense problem
+        its sequence; key_range: int [T, 2], token t's key range as positions
+        within its sequence.  With any of these, each sequence is its own dense problem
         ("Attention Kernel", Paged 与 ragged KV: packed sequences never attend
         across boundaries) and goes through attn_fwd with its slices."""
-        if bias is not None or block_keep is not None or window is not None:
+        if bias is not None or block_keep is not None or window is not None or key_range is not None:
             return self._varlen_by_sequence(q, k, v, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
                                             q_keep=q_keep, k_keep=k_keep, bias=bias, block_keep=block_keep,
-                                            window=window, rows=rows)
+                                            window=window, rows=rows, key_range=key_range)
         q, k, v = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype)
         if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape != v.shape:
             raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
@@ -186,7 +200,7 @@ class Oracle:
         return o, lse
 
     def _varlen_by_sequence(self, q, k, v, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, bias, block_keep,
-                            window, rows=None):
+                            window, rows=None, key_range=None):
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         A, T, d = q.shape
         n_seq = cu.size - 1
@@ -224,6 +238,8 @@ class Oracle:
                 kw["k_keep"] = np.asarray(k_keep).reshape(T)[s0:s1][None]
             if window is not None:
                 kw["m_keep"] = window_keep(1, L, L, int(window[0]), int(window[1]))
+            if key_range is not None:
+                kw["key_range"] = np.asarray(key_range).reshape(T, 2)[s0:s1][None]
             if bias is not None:
                 kw["bias"] = bias[:, s0:s1, :L][None]
             if block_keep is not None:
@@ -242,7 +258,7 @@ class Oracle:
         return o, lse
 
     def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None,
-                 bias=None, block_keep=None):
+                 bias=None, block_keep=None, key_range=None):
         """Gradient of attn_fwd: q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d]; masks
         as attn_fwd takes them.  Returns (dq, dk, dv) in fp64 with the shapes of
         q, k and v."""
@@ -255,7 +271,7 @@ class Oracle:
             raise ValueError("k/v must be [B, A_kv, S_k, d] with A % A_kv == 0")
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
-        mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
+        mk = self._keep_matrix(m_keep, key_range, B, S_q, S_k)
         bias, bh = self._bias(bias, B, A, S_q, S_k)
         bk, bkh = self._blocks(block_keep, B, A, S_q, S_k)
         dq = np.empty((B, A, S_q, d), dtype=np.float64)
@@ -269,18 +285,18 @@ class Oracle:
         return dq, dk, dv
 
     def attn_bwd_varlen(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal=True, q_keep=None, k_keep=None,
-                        window=None, bias=None, block_keep=None):
+                        window=None, bias=None, block_keep=None, key_range=None):
         """Gradient of the packed varlen prefill: q, do [A,T,d]; k, v [A_kv,T,d];
         cu_seqlens [n_seq+1]; keep masks [T]; window (left, right) within each
-        sequence (-1 = unbounded).  Returns (dq, dk, dv) in fp64.  bias and
-        block_keep as attn_fwd_varlen takes them; with either, each sequence's
+        sequence (-1 = unbounded).  Returns (dq, dk, dv) in fp64.  bias,
+        block_keep and key_range as attn_fwd_varlen takes them; with any, each sequence's
         gradient is the dense gradient of its own problem (its slices of the
         masks) -- the backward uses the forward's mask ("Attention Kernel",
         Backward 与重计算)."""
-        if bias is not None or block_keep is not None:
+        if bias is not None or block_keep is not None or key_range is not None:
             return self._bwd_varlen_by_sequence(q, k, v, do, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
                                                 q_keep=q_keep, k_keep=k_keep, window=window, bias=bias,
-                                                block_keep=block_keep)
+                                                block_keep=block_keep, key_range=key_range)
         q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
         if q.ndim != 3 or k.shape != v.shape or do.shape != q.shape:
             raise ValueError("q, do [A,T,d]; k, v [A_kv,T,d]")
@@ -303,7 +319,7 @@ class Oracle:
         return dq, dk, dv
 
     def _bwd_varlen_by_sequence(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, window, bias,
-                                block_keep):
+                                block_keep, key_range=None):
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         A, T, d = q.shape
         A_kv = k.shape[0]
@@ -334,6 +350,8 @@ class Oracle:
                 kw["k_keep"] = np.asarray(k_keep).reshape(T)[s0:s1][None]
             if window is not None:
                 kw["m_keep"] = window_keep(1, L, L, int(window[0]), int(window[1]))
+            if key_range is not None:
+                kw["key_range"] = np.asarray(key_range).reshape(T, 2)[s0:s1][None]
             if bias is not None:
                 kw["bias"] = bias[:, s0:s1, :L][None]
             if block_keep is not None:
@@ -345,7 +363,7 @@ class Oracle:
         return dq, dk, dv
 
     def prefill_paged(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal=True,
-                      window=None, rows=None, bias=None, block_keep=None):
+                      window=None, rows=None, bias=None, block_keep=None, key_range=None):
         """Query chunks over a paged cache: q [A,T_q,d] packed chunks (cu_seqlens_q
         [n_seq+1]); caches [P, page_size, A_kv, d]; block_table [n_seq, max_pages];
         seq_lens [n_seq] (chunk included).  Chunk row i of sequence s sits at
@@ -355,15 +373,16 @@ class Oracle:
         bias: fp32 [1 or A, T_q, ld] -- row t (a chunk token) holds the term of
         the keys at positions j < seq_lens of its sequence; block_keep: uint8
         [n_seq, 1 or A, ceil(longest chunk/128), ceil(longest seq_lens/128)] over
-        (chunk row, key position).  With either, each sequence's keys are
+        (chunk row, key position); key_range: int [T_q, 2], chunk token t's key
+        range as positions in its sequence.  With any of these, each sequence's keys are
         gathered token by token through its block table (token t: row t %
         page_size of page block_table[s][t // page_size]) and the chunk is the
         dense problem of its rows against them ("Attention Kernel", Paged 与
         ragged KV and 可编程 mask)."""
-        if bias is not None or block_keep is not None:
+        if bias is not None or block_keep is not None or key_range is not None:
             return self._paged_by_sequence(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, dtype=dtype,
                                            scale=scale, causal=causal, window=window, rows=rows, bias=bias,
-                                           block_keep=block_keep)
+                                           block_keep=block_keep, key_range=key_range)
         q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
         if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
             raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
@@ -392,7 +411,7 @@ class Oracle:
         return o, lse
 
     def _paged_by_sequence(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal,
-                           window, rows, bias, block_keep):
+                           window, rows, bias, block_keep, key_range=None):
         A, T_q, d = q.shape
         page_size, A_kv = k_cache.shape[1], k_cache.shape[2]
         cu = np.asarray(cu_seqlens_q, dtype=np.int64)
@@ -434,6 +453,8 @@ class Oracle:
             vs = np.ascontiguousarray(np.asarray(v_cache)[pages, offs].transpose(1, 0, 2))
             if window is not None:
                 kw["m_keep"] = window_keep(1, ql, L, int(window[0]), int(window[1]))
+            if key_range is not None:
+                kw["key_range"] = np.asarray(key_range).reshape(T_q, 2)[s0:s1][None]
             if bias is not None:
                 kw["bias"] = bias[:, s0:s1, :L][None]
             if block_keep is not None:
@@ -463,7 +484,7 @@ class Oracle:
         return out
 
     def attn_fwd_fp8(self, q_codes, k_codes, v, q_scale, k_scale, *, scale, causal=False, q_keep=None,
-                     k_keep=None, m_keep=None, rows=None):
+                     k_keep=None, m_keep=None, rows=None, key_range=None):
         """Dense prefill with FP8 (E4M3) queries and keys: q_codes [B,A,S_q,d],
         k_codes [B,A_kv,S_k,d] (uint8 codes), one fp32 scale per 128 consecutive
         tokens of each (batch, head): q_scale [B,A,ceil(S_q/128)], k_scale
@@ -482,10 +503,10 @@ class Oracle:
         vb = self._arr(v, "bf16").astype(np.uint32) << np.uint32(16)   # bf16 bits -> fp32 bits
         vv = vb.view(np.float32).astype(np.float64)
         return self.attn_fwd(qv, kv, vv, dtype="f64", scale=scale, causal=causal, q_keep=q_keep, k_keep=k_keep,
-                             m_keep=m_keep, rows=rows)
+                             m_keep=m_keep, rows=rows, key_range=key_range)
 
     def prefill_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, cu_seqlens_q, *,
-                          scale, causal=True, window=None, rows=None):
+                          scale, causal=True, window=None, rows=None, key_range=None):
         """prefill_paged over FP8 caches: E4M3 codes [P, page_size, A_kv, d]
         with per-(page, KV head) scales [P, A_kv]; q bf16 bits [A, T_q, d].  The
         cache values code value * scale are formed in fp64 and the chunks run
@@ -495,7 +516,7 @@ class Oracle:
         qb = self._arr(q, "bf16").astype(np.uint32) << np.uint32(16)   # bf16 bits -> fp32 bits
         qf = qb.view(np.float32).astype(np.float64)
         return self.prefill_paged(qf, kc, vc, block_table, seq_lens, cu_seqlens_q, dtype="f64", scale=scale,
-                                  causal=causal, window=window, rows=rows)
+                                  causal=causal, window=window, rows=rows, key_range=key_range)
 
     def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
                          seqs=None, window_left=None):
@@ -584,6 +605,18 @@ def window_keep(B: int, S_q: int, S_k: int, left: int, right: int) -> np.ndarray
     if right >= 0:
         keep &= j <= i + right
     return np.broadcast_to(keep.astype(np.uint8), (B, S_q, S_k)).copy()
+
+
+def key_range_keep(key_range, S_k: int) -> np.ndarray:
+    """Dense keep matrix [..., S_q, S_k] of per-row key ranges: row i keeps
+    key j when key_range[..., i, 0] <= j <= key_range[..., i, 1] (both ends
+    included; a first end past the last keeps no key).  Page "Attention
+    Kernel", section "可编程 mask": document boundaries (a row keeps the keys
+    of its own document) and prefix-LM (rows of the prefix see the whole
+    prefix) are element rules of this form."""
+    r = np.asarray(key_range, dtype=np.int64)
+    j = np.arange(S_k, dtype=np.int64)
+    return ((j >= r[..., 0:1]) & (j <= r[..., 1:2])).astype(np.uint8)
 
 
 def default() -> Oracle:

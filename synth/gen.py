@@ -491,6 +491,51 @@ def make_config(k: int, seed: int | None = None):
     raise ValueError(f"no config {k}")
 
 
+def document_ids(S: int, seed: int, b: int, doc_median: int = 200) -> np.ndarray:
+    """Document index of each of S packed positions of batch row b: documents
+    with log-normal lengths (median doc_median, sigma 0.8) laid end to end."""
+    lens = lognormal_lengths(max(1, S // max(doc_median // 4, 1)) + 1, doc_median, 0.8, 1, max(S, 1), seed * 1000 + b)
+    return np.searchsorted(np.cumsum(lens), np.arange(S), side="right")
+
+
+def make_key_ranges(B: int, S_q: int, S_k: int, kind: str, seed: int, *, doc_median: int = 200,
+                    prefix: int = 0) -> np.ndarray:
+    """Per-row key ranges int32 [B, S_q, 2]: query i (at position i + S_k - S_q)
+    keeps keys first..last (both included).
+
+    kind "document": the keys of the query's own document, the documents of
+        document_ids (the same ones make_bias "document" draws for this seed);
+        rows at negative positions keep none (first > last).
+    kind "prefix": prefix-LM, 0..max(position, prefix - 1).
+    kind "random": seeded intervals, some empty, some with first < 0 or last
+        >= S_k.
+    """
+    off = S_k - S_q
+    pos = np.arange(S_q, dtype=np.int64) + off
+    out = np.empty((B, S_q, 2), np.int64)
+    if kind == "document":
+        for b in range(B):
+            doc = document_ids(S_k, seed, b, doc_median)
+            first = np.searchsorted(doc, doc, side="left")
+            last = np.searchsorted(doc, doc, side="right") - 1
+            p = np.clip(pos, 0, max(S_k - 1, 0))
+            ok = (pos >= 0) & (S_k > 0)
+            out[b, :, 0] = np.where(ok, first[p] if S_k else 0, 1)
+            out[b, :, 1] = np.where(ok, last[p] if S_k else 0, 0)
+    elif kind == "prefix":
+        out[:, :, 0] = 0
+        out[:, :, 1] = np.maximum(pos, prefix - 1)[None]
+    elif kind == "random":
+        u = draw((B, S_q, 3), seed, S_BIAS + 200, "uniform", "f32").astype(np.float64)
+        a = np.floor(u[..., 0] * (S_k + 8)).astype(np.int64) - 4
+        w = np.floor(u[..., 1] * (S_k // 2 + 2)).astype(np.int64)
+        out[..., 0] = a
+        out[..., 1] = np.where(u[..., 2] < 0.05, a - 1, a + w)   # about 5% of the rows keep nothing
+    else:
+        raise ValueError(kind)
+    return out.astype(np.int32)
+
+
 def make_bias(B: int, H: int, S_q: int, S_k: int, kind: str, seed: int, *, doc_median: int = 200) -> np.ndarray:
     """A dense additive mask M, fp32 [B, H, S_q, S_k] (query i at position
     i + S_k - S_q, as for causal alignment).
@@ -510,10 +555,7 @@ def make_bias(B: int, H: int, S_q: int, S_k: int, kind: str, seed: int, *, doc_m
     if kind == "document":
         assert H == 1
         for b in range(B):
-            lens = lognormal_lengths(max(1, S_k // max(doc_median // 4, 1)) + 1, doc_median, 0.8, 1, S_k,
-                                     seed * 1000 + b)
-            edges = np.cumsum(lens)
-            doc = np.searchsorted(edges, np.arange(S_k), side="right")
+            doc = document_ids(S_k, seed, b, doc_median)
             same = doc[np.clip(pos, 0, S_k - 1)] == doc[j]
             same &= (pos >= 0)
             out[b, 0] = np.where(same, 0.0, -np.inf).astype(np.float32)

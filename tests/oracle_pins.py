@@ -572,6 +572,155 @@ def pin_window_equals_key_slice(orc):
             assert np.array_equal(lse[0, :, i], ls[0, :, 0]), (S_q, S_k, left, right, i)
 
 
+# ---- per-row key ranges (document boundaries, prefix-LM)
+
+def pin_key_range_equals_key_slice(orc):
+    """A row with key range [first, last] equals plain attention over the
+    contiguous slice of keys max(first, 0) .. min(last, S_k - 1) (cut at the
+    causal diagonal when causal; same keys in the same order: bit for bit); a
+    row whose range holds no key is fully masked."""
+    from synth import gen
+    rng = np.random.default_rng(44)
+    for S_q, S_k, causal in [(9, 12, False), (12, 12, True), (7, 10, True), (10, 6, False)]:
+        q = _f32(rng.standard_normal((1, 2, S_q, 4)))
+        k = _f32(rng.standard_normal((1, 1, S_k, 4)))
+        v = _f32(rng.standard_normal((1, 1, S_k, 4)))
+        kr = gen.make_key_ranges(1, S_q, S_k, "random", 5 + S_q)
+        kr[0, 0] = (-3, S_k + 5)   # both ends past the keys
+        kr[0, 1] = (4, 3)          # empty
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.625, causal=causal, key_range=kr)
+        off = S_k - S_q
+        for i in range(S_q):
+            lo = max(int(kr[0, i, 0]), 0)
+            hi = min(int(kr[0, i, 1]), S_k - 1, i + off if causal else S_k - 1)
+            if lo > hi:
+                assert np.all(o[0, :, i] == 0) and np.all(np.isneginf(lse[0, :, i])), (S_q, S_k, i)
+                continue
+            os_, ls = orc.attn_fwd(q[:, :, i:i + 1], k[:, :, lo:hi + 1], v[:, :, lo:hi + 1], dtype="f32",
+                                   scale=0.625)
+            assert np.array_equal(o[0, :, i], os_[0, :, 0]), (S_q, S_k, causal, i)
+            assert np.array_equal(lse[0, :, i], ls[0, :, 0]), (S_q, S_k, causal, i)
+
+
+def pin_key_range_documents_are_varlen(orc):
+    """Packed documents as key ranges (each row keeps its own document, cut at
+    the causal diagonal) equal the packed-sequence attention with the
+    documents as sequences: the same rows see the same keys."""
+    from synth import gen
+    rng = np.random.default_rng(45)
+    S, A, A_kv, d = 300, 2, 1, 4
+    kr = gen.make_key_ranges(1, S, S, "document", 3, doc_median=40)
+    doc = gen.document_ids(S, 3, 0, 40)
+    cu = np.concatenate([[0], np.cumsum(np.bincount(doc))]).astype(np.int32)
+    cu = np.unique(cu)
+    assert cu.size > 4
+    q = _f32(rng.standard_normal((1, A, S, d)))
+    k = _f32(rng.standard_normal((1, A_kv, S, d)))
+    v = _f32(rng.standard_normal((1, A_kv, S, d)))
+    for causal in (True, False):
+        o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=causal, key_range=kr)
+        ov, lv = orc.attn_fwd_varlen(q[0], k[0], v[0], cu, dtype="f32", scale=0.5, causal=causal)
+        assert np.allclose(o[0], ov, rtol=0, atol=1e-12) and np.allclose(lse[0], lv, rtol=0, atol=1e-12), causal
+
+
+def pin_key_range_prefix_lm(orc):
+    """Prefix-LM ranges: prefix 0 or 1 is causal attention, a prefix covering
+    every key is full (non-causal) attention, and a row inside a prefix of P
+    keys attends to exactly the first P keys."""
+    from synth import gen
+    rng = np.random.default_rng(46)
+    S, d = 40, 4
+    q = _f32(rng.standard_normal((1, 1, S, d)))
+    k = _f32(rng.standard_normal((1, 1, S, d)))
+    v = _f32(rng.standard_normal((1, 1, S, d)))
+    causal = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=True)
+    full = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5)
+    for P, want in ((0, causal), (1, causal), (S, full), (S + 7, full)):
+        got = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, key_range=gen.make_key_ranges(1, S, S, "prefix", 0, prefix=P))
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), P
+    P = 13
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, key_range=gen.make_key_ranges(1, S, S, "prefix", 0, prefix=P))
+    pre = orc.attn_fwd(q[:, :, :P], k[:, :, :P], v[:, :, :P], dtype="f32", scale=0.5)
+    assert np.array_equal(o[:, :, :P], pre[0]) and np.array_equal(lse[:, :, :P], pre[1])
+    assert np.array_equal(o[:, :, P:], causal[0][:, :, P:])
+
+
+def _window_ranges(positions, left, right):
+    first = positions - left if left >= 0 else np.full_like(positions, -1)
+    last = positions + right if right >= 0 else np.full_like(positions, 1 << 30)
+    return np.stack([first, last], axis=-1).astype(np.int32)
+
+
+def pin_key_range_packed_paths_equal_windows(orc):
+    """Key ranges that describe a sliding window give the window's result in
+    the packed prefill, the paged prefill (whose window is applied inside the
+    C oracle) and the packed gradient (likewise): the ranges are indexed by
+    token and read as positions within each sequence."""
+    lens = [70, 0, 33, 101]
+    A, A_kv, d = 2, 1, 4
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    rng = np.random.default_rng(47)
+    q = _f32(rng.standard_normal((A, T, d)))
+    k = _f32(rng.standard_normal((A_kv, T, d)))
+    v = _f32(rng.standard_normal((A_kv, T, d)))
+    do = _f32(rng.standard_normal((A, T, d)))
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int64)
+    for left, right, causal in ((9, 3, False), (20, -1, True), (-1, 5, False)):
+        kr = _window_ranges(pos, left, right)
+        a = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=0.5, causal=causal, key_range=kr)
+        b = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=0.5, causal=causal, window=(left, right))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), (left, right)
+        ga = orc.attn_bwd_varlen(q, k, v, do, cu, dtype="f32", scale=0.5, causal=causal, key_range=kr)
+        gb = orc.attn_bwd_varlen(q, k, v, do, cu, dtype="f32", scale=0.5, causal=causal, window=(left, right))
+        for x, y in zip(ga, gb):
+            assert np.allclose(x, y, rtol=0, atol=1e-12), (left, right)
+    # ranges together with a window: the intersection of the two intervals
+    from synth import gen
+    kr2 = gen.make_key_ranges(1, T, max(lens), "random", 8)[0]
+    win = _window_ranges(pos, 9, 3)
+    both = np.stack([np.maximum(kr2[:, 0], win[:, 0]), np.minimum(kr2[:, 1], win[:, 1])], axis=-1)
+    a = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=0.5, causal=False, key_range=kr2, window=(9, 3))
+    b = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=0.5, causal=False, key_range=both)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    q_lens = [5, 0, 17, 30]
+    qp, kc, vc, bt, sl, cuq = _paged_problem([40, 9, 64, 77], q_lens, A, A_kv, d, 16, 48)
+    posq = np.concatenate([np.arange(int(L) - ql, int(L)) for L, ql in zip(sl, q_lens)]).astype(np.int64)
+    for left, right in ((6, 0), (-1, 0), (12, -1)):
+        kr = _window_ranges(posq, left, right)
+        a = orc.prefill_paged(qp, kc, vc, bt, sl, cuq, dtype="f32", scale=0.5, causal=False, key_range=kr)
+        b = orc.prefill_paged(qp, kc, vc, bt, sl, cuq, dtype="f32", scale=0.5, causal=False, window=(left, right))
+        assert np.allclose(a[0], b[0], rtol=0, atol=1e-12) and np.allclose(a[1], b[1], rtol=0, atol=1e-12)
+
+
+def pin_bwd_key_range_finite_differences(orc):
+    """The gradient under document key ranges against central differences of
+    the loss sum(O * dO) (fp64 inputs)."""
+    from synth import gen
+    B, A, A_kv, S_q, S_k, d = 1, 2, 1, 24, 24, 3
+    q, k, v, do = _bwd_problem(B, A, A_kv, S_q, S_k, d, 49)
+    kr = gen.make_key_ranges(B, S_q, S_k, "document", 9, doc_median=6)
+    kr[0, 5] = (7, 2)   # a row that keeps nothing
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.7, causal=True, key_range=kr)
+    assert np.all(dq[0, :, 5] == 0)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attn_fwd(qq, kk, vv, dtype="f64", scale=0.7, causal=True, key_range=kr)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            am = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert np.max(np.abs(num - g)) <= 1e-7, name
+
+
 # ---- FP8 (OCP E4M3) caches: code values, and decode over dequantised pages
 
 def pin_fp8_e4m3_published_values(orc):

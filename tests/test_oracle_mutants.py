@@ -126,6 +126,15 @@ PY_MUTANTS = [
      "offs = (np.arange(L) // page_size) % page_size", 0),
     ("paged causal diagonal aligned top-left", 'kw["m_keep"] = window_keep(1, ql, L, int(window[0]), int(window[1]))',
      'kw["m_keep"] = window_keep(1, ql, ql, int(window[0]), int(window[1]))', 0),
+    ("key range: last key excluded", "(j <= r[..., 1:2])", "(j < r[..., 1:2])", 0),
+    ("key range: first key excluded", "(j >= r[..., 0:1])", "(j > r[..., 0:1])", 0),
+    ("key range: last key ignored", "((j >= r[..., 0:1]) & (j <= r[..., 1:2]))", "(j >= r[..., 0:1])", 0),
+    ("key ranges ignored beside a keep matrix", "mk = rk if mk is None else mk & rk", "mk = rk if mk is None else mk", 0),
+    ("key ranges ignored", "mk = rk if mk is None else mk & rk", "mk = mk", 0),
+    ("varlen key ranges of the first tokens", 'kw["key_range"] = np.asarray(key_range).reshape(T, 2)[s0:s1][None]',
+     'kw["key_range"] = np.asarray(key_range).reshape(T, 2)[0:L][None]', 0),
+    ("paged key ranges of the first tokens", 'kw["key_range"] = np.asarray(key_range).reshape(T_q, 2)[s0:s1][None]',
+     'kw["key_range"] = np.asarray(key_range).reshape(T_q, 2)[0:ql][None]', 0),
     ("varlen block mask transposed", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
      'kw["block_keep"] = np.ascontiguousarray(block_keep[s][None, :, :nbs, :nbs].transpose(0, 1, 3, 2))', 0),
 ]
