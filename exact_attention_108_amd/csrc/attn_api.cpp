@@ -37,6 +37,9 @@ bool window_arith_fits(const attn_window* w, long long rows, long long keys) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// per-row key ranges are read as int32 pairs (8-byte loads)
+bool key_range_aligned(const attn_mask* m) { return m == nullptr || aligned(m->key_range, 8); }
+
 // Longest sequence (rows or keys) any call takes: the kernels count positions
 // in int32 and round up to a tile or chunk past a length.
 constexpr int kMaxLen = INT_MAX - 1024;
@@ -56,6 +59,7 @@ attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   p.lse = lse;
   p.q_keep = mask ? mask->q_keep : nullptr;
   p.k_keep = mask ? mask->k_keep : nullptr;
+  p.key_range = mask ? mask->key_range : nullptr;
   p.A = A;
   p.A_kv = A_kv;
   p.G = A / A_kv;
@@ -100,7 +104,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   if (S_k > 0 && (!k || !v)) return ATTN_ERR_INVAL;
   for (const void* t : {q, k, v, (const void*)o})
     if (!aligned(t, data_align(dtype))) return ATTN_ERR_INVAL;
-  if (!aligned(lse, 4)) return ATTN_ERR_INVAL;
+  if (!aligned(lse, 4) || !key_range_aligned(mask)) return ATTN_ERR_INVAL;
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
   if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
@@ -112,6 +116,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   const bool bias = mask && mask->bias;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
   if (bias && dtype == ATTN_BF16 && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
+  if (bias && mask->key_range && dtype == ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   // the kernels count rows and key positions in int32, up to a tile past a length
   if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (S_q == 0) return ATTN_OK;
@@ -155,6 +160,7 @@ ATTN_EXPORT attn_status attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const v
     if (!aligned(t, 16)) return ATTN_ERR_INVAL;
   for (const void* t : {(const void*)lse, (const void*)q_scale, (const void*)k_scale})
     if (!aligned(t, 4)) return ATTN_ERR_INVAL;
+  if (!key_range_aligned(mask)) return ATTN_ERR_INVAL;
   if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
   if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;
   if (S_k > attn::kFp8MaxKeys) return ATTN_ERR_UNSUPPORTED;
@@ -203,7 +209,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse)) return ATTN_ERR_INVAL;
   for (const void* t : {q, k, v, (const void*)o})
     if (!aligned(t, data_align(dtype))) return ATTN_ERR_INVAL;
-  if (!aligned(lse, 4) || !aligned(cu_seqlens, 4)) return ATTN_ERR_INVAL;
+  if (!aligned(lse, 4) || !aligned(cu_seqlens, 4) || !key_range_aligned(mask)) return ATTN_ERR_INVAL;
   attn_status sup = check_prefill_support(dtype, d_h);
   if (sup != ATTN_OK) return sup;
   int max_len = 0;
@@ -217,6 +223,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   if ((blocks || bias) && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (blocks && max_len > 262144) return ATTN_ERR_UNSUPPORTED;
   if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
+  if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;
   if (max_len > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;
   if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
@@ -421,6 +428,7 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   for (const void* t : {(const void*)lse, (const void*)seq_lens, (const void*)block_table, (const void*)cu_seqlens_q,
                         (const void*)k_scale, (const void*)v_scale})
     if (!aligned(t, 4)) return ATTN_ERR_INVAL;
+  if (!key_range_aligned(mask)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
   // masks: block flags [n_seq, block_heads, nqb, nkb] over (chunk row, key
   // position) and terms [bias_heads, total_q, bias_ld] (row: chunk token;
@@ -439,6 +447,7 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   if (max_q > kMaxLen || max_kv_len > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (blocks && max_kv_len > 262144) return ATTN_ERR_UNSUPPORTED;
   if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
+  if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;
   const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
   if ((page_size & (page_size - 1)) != 0 || page_size % rows_per_part != 0) return ATTN_ERR_UNSUPPORTED;
   if (total_q == 0) return ATTN_OK;
@@ -470,6 +479,7 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   p.max_pages = max_pages;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.key_range = mask ? mask->key_range : nullptr;
   if (blocks) {
     p.block_keep = mask->block_keep;
     p.block_heads = mask->block_heads;
@@ -564,6 +574,7 @@ attn::BwdParams bwd_params(const void* q, const void* k, const void* v, const vo
   p.dv = dv;
   p.q_keep = mask ? mask->q_keep : nullptr;
   p.k_keep = mask ? mask->k_keep : nullptr;
+  p.key_range = mask ? mask->key_range : nullptr;
   p.A = A;
   p.A_kv = A_kv;
   p.G = A / A_kv;
@@ -588,11 +599,13 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   if (S_k > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVAL;
   for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(t)) return ATTN_ERR_INVAL;
+  if (!key_range_aligned(mask)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
   const bool blocks = mask && mask->block_keep;
   const bool bias = mask && mask->bias;
   if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;  // as the forward
   if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   const long long n_qb = (S_q + 127) / 128, n_kb = (S_k + 127) / 128;
   if (blocks && (n_kb > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * n_qb > attn::kBwdMaxRowBlocks))
@@ -642,7 +655,7 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   if (total_tokens > 0 && (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)) return ATTN_ERR_INVAL;
   for (const void* t : {q, k, v, o, dout, (const void*)lse, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(t)) return ATTN_ERR_INVAL;
-  if (!aligned(cu_seqlens, 4)) return ATTN_ERR_INVAL;
+  if (!aligned(cu_seqlens, 4) || !key_range_aligned(mask)) return ATTN_ERR_INVAL;
   if (dtype != ATTN_BF16 || (d_h != 64 && d_h != 128)) return ATTN_ERR_UNSUPPORTED;
   long long total_tiles = 0;
   int max_tiles = 0, max_len = 0;
@@ -659,6 +672,7 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   const bool bias = mask && mask->bias;
   if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, max_len, max_len, mask->bias_ld)) return ATTN_ERR_INVAL;
+  if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;  // as the forward
   if (blocks && (max_tiles > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * max_tiles > attn::kBwdMaxRowBlocks))
     return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;

@@ -47,6 +47,10 @@ struct BwdParams {
   const float* bias;
   int bias_heads, bias_ld;
   float inv_scale;
+  // per-row key ranges: row i keeps key j only when key_range[2 i] <= j <=
+  // key_range[2 i + 1]; dense [B, S_q, 2], packed [T, 2] (positions within
+  // the sequence); or null
+  const int32_t* key_range;
 };
 // Block-mask limits of the backward: the dQ pass keeps one flag per 128-key
 // block of its row block in LDS, the dK/dV pass one per (query head of the

@@ -34,6 +34,7 @@
 // The per-element predicate (sliding window whose right edge is the causal
 // bottom-right diagonal, keep masks, rows and keys past the ends) is the
 // forward's; rows whose LSE is -inf (fully masked) take no part.
+#include <climits>
 #include <type_traits>
 
 #include "attn_bwd.h"
@@ -136,8 +137,8 @@ template <int N>
 using Slot = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------- dQ
-// kVarlen: packed sequences (see BwdParams); kMasks: the block mask and the
-// dense additive term (runtime-optional, dense batches only).  Two waves per
+// kVarlen: packed sequences (see BwdParams); kMasks: the block mask, the
+// dense additive term and the per-row key ranges (each runtime-optional).  Two waves per
 // SIMD, one for the masked form at d = 128 (at two its term loads spill).
 template <int D, bool kMasks>
 constexpr int kDqWavesPerSimd = (D == 128 && kMasks) ? 1 : 2;
@@ -153,6 +154,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * SLOT_BYTES / 2];
   // block mask: flag of each 128-key block of this row block's key range
   __shared__ uint8_t sBlk[kMasks ? kBwdMaxKeyBlocks : 1];
+  // per-row key ranges: the key bounds of each wave's rows
+  __shared__ KeyBounds sKb[kMasks ? 4 : 1];
 
   // heaviest query tiles first (most causal key tiles)
   int qt, h, b = 0, S_q, S_k;
@@ -208,10 +211,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     if (g == 0) *(float2*)(p.row_stats + 2 * (q_row0 + qrow)) = make_float2(lrow, drow);
   }
 
+  // per-row key ranges (the forward's mask): this lane's row keeps keys
+  // [rng.x, rng.y] (clamped into [-1, S_k]); the bounds of the wave's and the
+  // workgroup's rows narrow the tile range and pick the whole tiles
+  [[maybe_unused]] int2 rng = make_int2(-1, S_k);
+  [[maybe_unused]] KeyBounds kb_wave{0, S_k, 0, S_k}, kb_wg{0, S_k, 0, S_k};
+  if constexpr (kMasks) {
+    if (p.key_range) {
+      const int32_t* kr = p.key_range + 2 * (kVarlen ? tok0 : (size_t)b * S_q);
+      rng = row_in ? load_key_range(kr, qrow, S_k) : make_int2(0, -1);
+      kb_wave = wave_key_bounds(row_in, rng.x, rng.y);
+      kb_wg = workgroup_key_bounds<4>(kb_wave, sKb, wave, lane);
+    }
+  }
+
   // key tiles some row of the workgroup keeps: j_lo + [0, n_tiles)
   int kbeg = 0, kend = S_k;
   if (wr >= 0) kend = min(kend, q0 + kBwdQRows - 1 + off + wr + 1);
   if (wl >= 0) kbeg = max(q0 + off - wl, 0);
+  if constexpr (kMasks) {
+    kbeg = max(kbeg, kb_wg.any_lo);
+    kend = min(kend, kb_wg.any_hi);
+  }
   const int j_lo = kbeg / kKeyTile;
   const int n_tiles = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile - j_lo : 0;
 
@@ -289,6 +310,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     bool full = k0 + kKeyTile <= S_k && __ballot(ok) == ~0ull;
     if (wr >= 0) full = full && k0 + kKeyTile - 1 <= wave_row0 + off + wr;
     if (wl >= 0) full = full && k0 >= wave_row0 + 31 + off - wl;
+    if constexpr (kMasks) full = full && k0 >= kb_wave.all_lo && k0 + kKeyTile <= kb_wave.all_hi;
     return !full;
   };
   auto half = [&](const char* lds, int j, bool ok, int kb, auto masked_tag) {
@@ -317,8 +339,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
       }
     }
     const uint64_t kvalid = __ballot(ok) >> (4 * g);
-    const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
-    const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
+    int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
+    int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
+    if constexpr (kMasks) {
+      lim = min(lim, rng.y - k0 - 4 * g);
+      lo = max(lo, rng.x - k0 - 4 * g);
+    }
     bf16x8 dsb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -389,23 +415,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
 // double-buffered, which fits 256 registers: two waves per SIMD, twice the
 // resident workgroups.  The launch picks it when the grid has enough
 // workgroups to fill those slots several times over.
-template <int D, bool KLDS>
-constexpr int kDkdvWavesPerSimd = (D == 64 || KLDS) ? 2 : 1;
+// kRange (with kMasks): per-row key ranges, a form of its own (the ranges of
+// a block are staged beside its statistics); one wave per SIMD at both head
+// dimensions (at d = 64 two spill).
+template <int D, bool KLDS, bool kRange>
+constexpr int kDkdvWavesPerSimd = ((D == 64 && !kRange) || KLDS) ? 2 : 1;
 
-template <int D, bool KLDS, bool kVarlen, bool kMasks>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS>, kDkdvWavesPerSimd<D, KLDS>))) void bwd_dkdv_kernel(BwdParams p,
+template <int D, bool KLDS, bool kVarlen, bool kMasks, bool kRange = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS, kRange>, kDkdvWavesPerSimd<D, KLDS, kRange>))) void bwd_dkdv_kernel(BwdParams p,
                                                                                                       int n_kt) {
+  static_assert(!kRange || (kMasks && !KLDS), "key ranges: the masked one-wave form");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
   constexpr int STATS_BYTES = kQBlock * 8;                    // (L2, D) per row
-  constexpr int SLOT_BYTES = 2 * BLOCK_BYTES + STATS_BYTES;   // [Q block | dO block | stats]
+  constexpr int RANGE_BYTES = kRange ? kQBlock * 8 : 0;       // per-row key ranges
+  constexpr int SLOT_BYTES = 2 * BLOCK_BYTES + STATS_BYTES + RANGE_BYTES;  // [Q block | dO block | stats | ranges]
   constexpr int NSLOT = KLDS ? 2 : 4;
   constexpr int KTILE_BYTES = KLDS ? kBwdKRows * D * 2 : 0;  // [slots | K tile]
-  constexpr int COPIES = 2 * (kQBlock * D / 8 / kThreads) + 1;  // copy instructions per wave per block
+  // copy instructions per wave per block
+  constexpr int COPIES = 2 * (kQBlock * D / 8 / kThreads) + 1 + (kRange ? 1 : 0);
   __shared__ __attribute__((aligned(16))) uint16_t smem[(NSLOT * SLOT_BYTES + KTILE_BYTES) / 2];
   // block mask: flag of each (query head of the group, 128-row block) for this key block
   __shared__ uint8_t sBlk[kMasks ? kBwdMaxRowBlocks : 1];
+  // per-row key ranges: the first and last row (per wave) that keep a key of this workgroup
+  __shared__ int sHull[kRange ? 8 : 1];
 
   // key tiles in order (the first ones see the most query rows when causal)
   int kt, hk, b = 0, S_q, S_k;
@@ -476,8 +510,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   // blocks run over (query head of the group, 32-row block)
   // (row i keeps key j when i + off - wl <= j <= i + off + wr)
   const int k_first = kt * kBwdKRows, k_last = k_first + kBwdKRows - 1;
-  const int i_first = wr >= 0 ? max(k_first - off - wr, 0) : 0;
-  const int i_end = wl >= 0 ? min(k_last - off + wl + 1, S_q) : S_q;
+  int i_first = wr >= 0 ? max(k_first - off - wr, 0) : 0;
+  int i_end = wl >= 0 ? min(k_last - off + wl + 1, S_q) : S_q;
+  // Per-row key ranges (the forward's mask): only rows whose range reaches a
+  // key of this workgroup take part; a scan of every row's range gives the
+  // first and last of them (rows past the window's range stay out as well).
+  if constexpr (kRange) {
+    {
+      const int32_t* kr = p.key_range + 2 * (kVarlen ? tok0 : (size_t)b * S_q);
+      int lo_row = INT_MAX, hi_row = -1;
+      for (int i = tid; i < S_q; i += kThreads) {
+        const int2 r = *(const int2*)(kr + 2 * (size_t)i);
+        if (r.x <= r.y && r.x <= k_last && r.y >= k_first) {
+          lo_row = min(lo_row, i);
+          hi_row = max(hi_row, i);
+        }
+      }
+      lo_row = wave_min_i32(lo_row);
+      hi_row = wave_max_i32(hi_row);
+      if (lane == 0) {
+        sHull[wave] = lo_row;
+        sHull[4 + wave] = hi_row;
+      }
+      __syncthreads();
+      lo_row = min(min(sHull[0], sHull[1]), min(sHull[2], sHull[3]));
+      hi_row = max(max(sHull[4], sHull[5]), max(sHull[6], sHull[7]));
+      i_first = max(i_first, lo_row);
+      i_end = min(i_end, hi_row + 1);
+    }
+  }
   const int qb_first = i_first / kQBlock;
   const int qb_end = i_end > i_first ? (i_end + kQBlock - 1) / kQBlock : qb_first;
   const int nq = qb_end - qb_first;
@@ -520,6 +581,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     const i32x4 rsrc = make_buffer_rsrc(p.row_stats + 2 * (q_row0 + r0), (uint32_t)(rows * 8));
     const uint32_t sdst = dst + 2 * BLOCK_BYTES + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
     if (lane < 4) lds_copy16_buf(rsrc, (uint32_t)(wave * 64 + lane * 16), sdst);
+    if constexpr (kRange) {
+      // the rows' key ranges
+      const i32x4 rrng = make_buffer_rsrc(p.key_range + 2 * ((kVarlen ? tok0 : (size_t)b * S_q) + r0),
+                                          (uint32_t)(rows * 8));
+      if (lane < 4) lds_copy16_buf(rrng, (uint32_t)(wave * 64 + lane * 16), sdst + STATS_BYTES);
+    }
   };
 
   // S and dP of the block in `lds` for this wave's 32 keys
@@ -570,19 +637,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     const int m_lo = wr >= 0 ? key - off - wr - r0 - 4 * g : -(1 << 30);
     int m_hi = key_live ? S_q - r0 - 4 * g : -(1 << 30);
     if (wl >= 0) m_hi = min(m_hi, key - off + wl - r0 - 4 * g + 1);
+    [[maybe_unused]] const int* rg = (const int*)(st + 2 * kQBlock);  // the rows' key ranges
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4 a = *(const f32x4*)(st + 2 * (8 * r4 + 4 * g));
       const f32x4 c = *(const f32x4*)(st + 2 * (8 * r4 + 4 * g) + 4);
       const float lv[4] = {a[0], a[2], c[0], c[2]}, dv[4] = {a[1], a[3], c[1], c[3]};
+      [[maybe_unused]] i32x4 ra, rc;
+      if constexpr (kRange && MASKED) {
+        ra = *(const i32x4*)(rg + 2 * (8 * r4 + 4 * g));
+        rc = *(const i32x4*)(rg + 2 * (8 * r4 + 4 * g) + 4);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * r4 + i;
         float x = fmaf(s[r], cs, -lv[i]);
         if constexpr (MASKED) {
           const int m = 8 * r4 + i;
-          x = (m >= m_lo && m < m_hi) ? x : -INFINITY;
+          bool live = m >= m_lo && m < m_hi;
+          if constexpr (kRange) {
+            const int lo_i = i < 2 ? ra[2 * i] : rc[2 * (i - 2)];
+            const int hi_i = i < 2 ? ra[2 * i + 1] : rc[2 * (i - 2) + 1];
+            live = live && key >= lo_i && key <= hi_i;
+          }
+          x = live ? x : -INFINITY;
         }
         const float pr = exp2_fast(x);
         pb[r >> 3][r & 7] = (__bf16)pr;
@@ -606,6 +685,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   const bool wave_keys_live = __ballot(key_live) == ~0ull;
   const int wave_key_first = kt * kBwdKRows + wave * 32, wave_key_last = wave_key_first + 31;
   auto block_masked = [&](int idx) -> bool {
+    if constexpr (kRange) return true;
     if constexpr (kMasks) {
       if (p.bias) return true;
     }
@@ -796,6 +876,13 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
         return hipGetLastError();
       }
     }
+    if constexpr (kMasks) {
+      if (p.key_range) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, true, true>), dim3(n_wg), dim3(kThreads), 0, stream, p,
+                           n_kt);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, kMasks>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
     (void)two_wave;
   }
@@ -804,9 +891,10 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  if (p.cu_seqlens && (p.block_keep || p.bias)) return launch_bwd_v<D, true, true>(p, stream);
+  const bool masks = p.block_keep || p.bias || p.key_range;
+  if (p.cu_seqlens && masks) return launch_bwd_v<D, true, true>(p, stream);
   if (p.cu_seqlens) return launch_bwd_v<D, true, false>(p, stream);
-  if (p.block_keep || p.bias) return launch_bwd_v<D, false, true>(p, stream);
+  if (masks) return launch_bwd_v<D, false, true>(p, stream);
   return launch_bwd_v<D, false, false>(p, stream);
 }
 

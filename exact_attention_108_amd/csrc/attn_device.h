@@ -128,6 +128,59 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t* base, int idx) {
   return *(const_i32_ptr)(((uint64_t)hi << 32) | lo);
 }
 
+// Per-row key ranges (the mask rule first <= j <= last).  A row's pair is
+// clamped to [-1, n_keys]: the same keys of 0 .. n_keys - 1 stay kept, and
+// position arithmetic on the ends stays far from int32 overflow.
+__device__ __forceinline__ int2 load_key_range(const int32_t* kr, int row, int n_keys) {
+  const int2 r = *(const int2*)(kr + 2 * (size_t)row);
+  return make_int2(min(max(r.x, -1), n_keys), min(max(r.y, -1), n_keys));
+}
+__device__ __forceinline__ int wave_min_i32(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+// Key bounds of a group of rows under key ranges: [any_lo, any_hi) holds
+// every key some row keeps (empty when none keeps a key), [all_lo, all_hi)
+// the keys every row keeps (empty when some row keeps none).
+struct KeyBounds {
+  int any_lo, any_hi, all_lo, all_hi;
+};
+constexpr int kNoKey = 1 << 30;
+// the bounds of this wave's rows: `row` says whether the lane holds a row that
+// exists, (lo, hi) its clamped range; the result is wave-uniform
+__device__ __forceinline__ KeyBounds wave_key_bounds(bool row, int lo, int hi) {
+  const bool some = row && lo <= hi;
+  KeyBounds b;
+  b.any_lo = __builtin_amdgcn_readfirstlane(wave_min_i32(some ? lo : kNoKey));
+  b.any_hi = __builtin_amdgcn_readfirstlane(wave_max_i32(some ? hi + 1 : -kNoKey));
+  b.all_lo = __builtin_amdgcn_readfirstlane(wave_max_i32(row ? lo : -kNoKey));
+  b.all_hi = __builtin_amdgcn_readfirstlane(wave_min_i32(row ? hi + 1 : kNoKey));
+  return b;
+}
+// combine the bounds of a workgroup's waves through `slots` (one per wave,
+// in LDS); every thread of the workgroup must call it (it holds a barrier)
+template <int kWaves>
+__device__ __forceinline__ KeyBounds workgroup_key_bounds(const KeyBounds& w, KeyBounds* slots, int wave, int lane) {
+  if (lane == 0) slots[wave] = w;
+  __syncthreads();
+  KeyBounds b = slots[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) {
+    const KeyBounds o = slots[i];
+    b.any_lo = min(b.any_lo, o.any_lo);
+    b.any_hi = max(b.any_hi, o.any_hi);
+    b.all_lo = max(b.all_lo, o.all_lo);
+    b.all_hi = min(b.all_hi, o.all_hi);
+  }
+  return b;
+}
+
 __device__ __forceinline__ bf16x8 concat(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

@@ -57,6 +57,10 @@ struct FwdParams {
   const float* k_scale;
   // E4M3 paged cache (paged prefill): k_scale, v_scale [num_pages, A_kv]
   const float* v_scale;
+  // per-row key ranges: row i keeps key j only when key_range[2 i] <= j <=
+  // key_range[2 i + 1]; dense [B, S_q, 2], packed [T, 2] (positions within
+  // the sequence), paged [T_q, 2] (positions in the sequence's cache); or null
+  const int32_t* key_range;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin

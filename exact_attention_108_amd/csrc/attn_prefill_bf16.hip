@@ -47,9 +47,11 @@
 //   kBlocks  the key tiles of a row block listed from a 128 x 128 block mask,
 //            so masked blocks are never loaded;
 //   kBias    a dense additive term M on every score (loaded a tile ahead as
-//            the initial value of the score accumulators).
-// Sliding windows, keep masks and the causal flag are runtime arguments of
-// every instantiation.
+//            the initial value of the score accumulators);
+//   kRange   per-row key ranges (kept apart so that the other forms keep
+//            their register allocation; not combined with kBias).
+// Sliding windows, per-row key ranges, keep masks and the causal flag are
+// runtime arguments of every instantiation.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -71,10 +73,10 @@ constexpr int kMaxListedTiles = 4096;
 // Waves per SIMD: two at d = 128 (the kernel needs up to 256 VGPRs); three
 // at d = 64, whose accumulators and operands fit the 168-VGPR budget that
 // needs, with three workgroups' 32 KB of tiles in LDS (measured +9% on a
-// causal S = 2048 batch, +16% on ragged varlen batches).  The paged and
-// dense-additive-mask variants stay at two: at three they spill.
-template <int D, bool kPaged, bool kBias>
-constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias) ? 3 : 2;
+// causal S = 2048 batch, +16% on ragged varlen batches).  The paged,
+// dense-additive-mask and key-range variants stay at two: at three they spill.
+template <int D, bool kPaged, bool kBias, bool kRange>
+constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias && !kRange) ? 3 : 2;
 
 // kFp8: queries and keys are OCP E4M3 codes with one fp32 scale per 128
 // tokens (FwdParams::q_scale / k_scale); S^T = K . Q^T runs on the FP8 matrix
@@ -87,10 +89,11 @@ constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias) ? 3 : 2;
 // value's scale its probabilities before the PV product (the normaliser sums
 // the unscaled ones).
 template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false, bool kFp8 = false,
-          bool kCache8 = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias>, kWavesPerSimd<D, kPaged, kBias>))) void prefill_bf16_kernel(FwdParams p) {
+          bool kCache8 = false, bool kRange = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias, kRange>, kWavesPerSimd<D, kPaged, kBias, kRange>))) void prefill_bf16_kernel(FwdParams p) {
   static_assert(!kFp8 || (D == 128 && !kVarlen && !kPaged && !kBlocks && !kBias), "fp8: dense, d = 128");
   static_assert(!kCache8 || kPaged, "E4M3 caches: paged prefill only");
+  static_assert(!kRange || (!kBias && !kCache8), "key ranges: not with a dense additive term or an E4M3 cache");
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
   constexpr int MB = D / 32;               // 32-row blocks of O^T
@@ -116,6 +119,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // E4M3 cache: the scales of the parts of each K and V buffer's tile
   __shared__ f32x4 sKsc[kCache8 ? 2 : 1];
   __shared__ f32x4 sVsc[kCache8 ? 2 : 1];
+  // per-row key ranges: each row's clamped (first, last), read back only by
+  // the wave that owns the row, and the key bounds of each wave's rows
+  __shared__ int2 sRange[kRange ? kRows : 1];
+  __shared__ KeyBounds sKb[kRange ? kWaves : 1];
 
   RowBlock rb;
   if constexpr (kPaged) {
@@ -139,13 +146,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int off = S_k - S_q;                 // causal: query i sits at position i + off
   const int qrow = rb.q0 + wave * 32 + l32;  // this lane's query row
 
-  // ---- key tiles this workgroup needs: [j_lo, j_hi), the keys some row of
-  // it keeps under the window (the causal diagonal is its right edge)
+  // ---- per-row key ranges (page "Attention Kernel", section "可编程 mask":
+  // document boundaries and prefix-LM as per-row ranges): each row's range,
+  // clamped into [-1, S_k] so that offsets stay in int32, is kept in LDS for
+  // the predicate of the masked tiles (registers are scarce here), and the
+  // bounds of the wave's and the workgroup's rows narrow the tile range
   const int wl = p.win_left, wr = p.win_right;
+  KeyBounds kb_wave{0, S_k, 0, S_k}, kb_wg{0, S_k, 0, S_k};
+  if constexpr (kRange) {
+    const int2 r = qrow < S_q ? load_key_range(rb.key_range, qrow, S_k) : make_int2(0, -1);
+    if (g == 0) sRange[wave * 32 + l32] = r;
+    kb_wave = wave_key_bounds(qrow < S_q, r.x, r.y);
+    kb_wg = workgroup_key_bounds<kWaves>(kb_wave, sKb, wave, lane);
+  }
+
+  // ---- key tiles this workgroup needs: [j_lo, j_hi), the keys some row of
+  // it keeps under the window and the key ranges
   const int q_first = rb.q0, q_last = rb.q0 + kRows - 1;
   int kbeg = 0, kend = S_k;
   if (wr >= 0) kend = min(kend, q_last + off + wr + 1);
   if (wl >= 0) kbeg = max(q_first + off - wl, 0);
+  if constexpr (kRange) {
+    kbeg = max(kbeg, kb_wg.any_lo);
+    kend = min(kend, kb_wg.any_hi);
+  }
   const int j_lo = kbeg / kBc;
   const int n_range = kend > kbeg ? (kend + kBc - 1) / kBc - j_lo : 0;
 
@@ -159,6 +183,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     int ul = wl >= 0 ? (max(q_last + off - wl, 0) + kBc - 1) / kBc : 0;
     int uh = S_k / kBc;
     if (wr >= 0) uh = min(uh, max(q_first + off + wr + 1, 0) / kBc);
+    if constexpr (kRange) {
+      ul = max(ul, (max(kb_wg.all_lo, 0) + kBc - 1) / kBc);
+      uh = min(uh, max(kb_wg.all_hi, 0) / kBc);
+    }
     ul = max(ul, j_lo);
     uh = min(uh, j_lo + n_range);
     if (ul < uh) {
@@ -414,6 +442,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   int kbeg_w = 0, kend_w = S_k;
   if (wr >= 0) kend_w = min(kend_w, wave_q0 + 31 + off + wr + 1);
   if (wl >= 0) kbeg_w = max(wave_q0 + off - wl, 0);
+  if constexpr (kRange) {
+    kbeg_w = max(kbeg_w, kb_wave.any_lo);
+    kend_w = min(kend_w, kb_wave.any_hi);
+  }
   kbeg_w = __builtin_amdgcn_readfirstlane(kbeg_w);
   kend_w = __builtin_amdgcn_readfirstlane(kend_w);
   auto wave_sees = [&](int t) -> bool {
@@ -503,8 +535,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
   };
   // per-element predicate of tile t (keys past S_k, the window's edges -- the
-  // causal diagonal is its right edge --, the key keep-mask): dead scores
-  // become -inf
+  // causal diagonal is its right edge --, the row's key range, the key
+  // keep-mask): dead scores become -inf
   // Dense additive mask: this lane's row of M, and the 32 terms of its keys
   // in tile t (element (kb, r) of the score tile is key k0 + 32kb + 8(r/4) +
   // 4g + r%4, so keys come in runs of 4: one 16-byte load per run).  Keys at
@@ -561,9 +593,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (rb.k_keep) valid = valid && sKeep[t & 1][lane] != 0;
     const uint64_t kvalid = __ballot(valid) >> (4 * g);
     // element (kb, r) holds key k0 + kl, kl = 32kb + 8(r/4) + 4g + r%4;
-    // dead when kl > qrow + off + wr - k0 or kl < qrow + off - wl - k0
-    const int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
-    const int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
+    // dead when kl > qrow + off + wr - k0 or kl < qrow + off - wl - k0, or
+    // outside the row's key range
+    [[maybe_unused]] int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
+    [[maybe_unused]] int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
+    if constexpr (kRange) {
+      const int2 r = sRange[wave * 32 + l32];
+      lim = min(lim, r.y - k0 - 4 * g);
+      lo = max(lo, r.x - k0 - 4 * g);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -934,6 +972,23 @@ hipError_t launch_d(const FwdParams& p, bool varlen, hipStream_t stream) {
     grid = p.n_qt * p.A * p.B;
   }
   if (grid <= 0) return hipSuccess;
+  if (p.key_range) {
+    // (a dense additive term with key ranges is rejected before the launch)
+    if (varlen && p.block_keep) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true, false, false, false, true>), dim3(grid),
+                         dim3(kThreads), 0, stream, p);
+    } else if (varlen) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false, false, false, false, true>), dim3(grid),
+                         dim3(kThreads), 0, stream, p);
+    } else if (p.block_keep) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, false, false, false, true>), dim3(grid),
+                         dim3(kThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, false, false, false, true>), dim3(grid),
+                         dim3(kThreads), 0, stream, p);
+    }
+    return hipGetLastError();
+  }
   if (!varlen && p.bias && p.block_keep) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else if (!varlen && p.bias) {
@@ -966,14 +1021,25 @@ hipError_t launch_prefill_fp8(const FwdParams& p, hipStream_t stream) {
   const int grid = p.n_qt * p.A * p.B;
   if (grid <= 0) return hipSuccess;
   if (p.d != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false, false, false, true>), dim3(grid), dim3(kThreads), 0,
-                     stream, p);
+  if (p.key_range) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false, false, false, true, false, true>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false, false, false, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_paged_d(const FwdParams& p, int grid, hipStream_t stream) {
-  if (p.bias && p.block_keep) {
+  if (p.key_range && p.block_keep) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true, false, false, false, true>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
+  } else if (p.key_range) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, false, false, false, true>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
+  } else if (p.bias && p.block_keep) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else if (p.bias) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);

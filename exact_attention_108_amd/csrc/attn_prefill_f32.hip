@@ -8,7 +8,9 @@
 // fp32 FMAs on the vector ALUs, so this path is exact to fp32 rounding.
 //
 // A dense additive mask M (dense batches) enters each score as M / scale
-// before the scaling, i.e. s * scale + M.
+// before the scaling, i.e. s * scale + M.  Per-row key ranges (page
+// "Attention Kernel", section "可编程 mask") mask the keys outside each row's
+// range.
 //
 // A workgroup owns 16 query rows; wave w owns rows 4w..4w+3.  In the score
 // step lane j computes the scores of key j of the tile for the wave's 4 rows;
@@ -83,6 +85,17 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
     }
   }
 
+  // this wave's rows keep keys [r_lo, r_hi] under their key ranges
+  int r_lo[kRowsPerWave], r_hi[kRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerWave; ++rr) {
+    const int row = rb.q0 + wave * kRowsPerWave + rr;
+    int2 r = make_int2(-1, S_k);
+    if (rb.key_range && row < S_q) r = load_key_range(rb.key_range, row, S_k);
+    r_lo[rr] = r.x;
+    r_hi[rr] = r.y;
+  }
+
   float m_run[kRowsPerWave], l_run[kRowsPerWave], acc[kRowsPerWave][2];
 #pragma unroll
   for (int rr = 0; rr < kRowsPerWave; ++rr) {
@@ -116,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
       float s = 0.f;
       for (int e = 0; e < D; ++e) s = fmaf(sQ[qr][e], sK[lane][e], s);
       if (bias_rows && key < S_k && row < S_q) s = fmaf(bias_rows[(size_t)row * p.bias_ld + key], p.inv_scale, s);
-      const bool dead = sKeep[lane] == 0 || (wr >= 0 && key > row + off + wr) || (wl >= 0 && key < row + off - wl);
+      const bool dead = sKeep[lane] == 0 || (wr >= 0 && key > row + off + wr) || (wl >= 0 && key < row + off - wl) ||
+                        key < r_lo[rr] || key > r_hi[rr];
       s = dead ? -INFINITY : s;
       const float mx = wave_max(s);
       const float m_new = fmaxf(m_run[rr], mx * cs);

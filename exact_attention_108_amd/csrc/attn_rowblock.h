@@ -14,6 +14,7 @@ struct RowBlock {
   float* lse;
   const uint8_t* q_keep;  // or null
   const uint8_t* k_keep;  // or null
+  const int32_t* key_range;  // this sequence's row 0 of the per-row key ranges, or null
   int S_q, S_k;
   int q0;                 // first query row of this workgroup
   int b, h, qt;           // batch (packed: sequence), head and query tile of this workgroup
@@ -53,6 +54,7 @@ __device__ __forceinline__ RowBlock setup_dense(const FwdParams& p, int row_byte
   r.v = (const char*)p.v + koff * row_bytes;
   r.q_keep = p.q_keep ? p.q_keep + (size_t)b * p.S_q : nullptr;
   r.k_keep = p.k_keep ? p.k_keep + (size_t)b * p.S_k : nullptr;
+  r.key_range = p.key_range ? p.key_range + 2 * (size_t)b * p.S_q : nullptr;
   r.S_q = p.S_q;
   r.S_k = p.S_k;
   r.q0 = qt * kRows;
@@ -139,6 +141,7 @@ __device__ __forceinline__ bool setup_varlen(const FwdParams& p, int row_bytes, 
   r.v = (const char*)p.v + ((size_t)hk * p.T + start) * row_bytes;
   r.q_keep = p.q_keep ? p.q_keep + start : nullptr;
   r.k_keep = p.k_keep ? p.k_keep + start : nullptr;
+  r.key_range = p.key_range ? p.key_range + 2 * (size_t)start : nullptr;
   r.S_q = len;
   r.S_k = len;
   r.q0 = t_u * kRows;

@@ -31,8 +31,8 @@
  *     (the kernels count positions in int32, up to a tile past a length).
  *   - Mask: M_ij is the optional dense additive term bias[i][j] (see
  *     attn_mask) plus -inf when: causal and j > i + (S_k - S_q)
- *     (bottom-right alignment), q_keep[i] == 0, k_keep[j] == 0, a window or
- *     a block mask excludes (i, j).  A row with every key masked (including
+ *     (bottom-right alignment), q_keep[i] == 0, k_keep[j] == 0, a window,
+ *     a key range or a block mask excludes (i, j).  A row with every key masked (including
  *     S_k == 0) returns O = 0 and LSE = -inf (page "Attention Kernel",
  *     section "Online softmax", fully-masked-row contract), never NaN.
  *   - scale must be finite and > 0.  Inputs must be finite.
@@ -56,7 +56,7 @@
 #include <stdint.h>
 
 /* The value attn_abi_version() returns for this header. */
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 #ifdef __cplusplus
 extern "C" {
@@ -109,11 +109,32 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * (ATTN_ERR_UNSUPPORTED otherwise).  It combines with every other mask; key
  * tiles are skipped only through block_keep, which attn_block_keep_from_bias
  * derives from a bias.  attn_fwd, attn_fwd_varlen (bf16),
- * attn_prefill_paged_masked, attn_bwd and attn_bwd_varlen take it.
+ * attn_prefill_paged_masked, attn_bwd and attn_bwd_varlen take it; in bf16
+ * calls it does not combine with key_range (ATTN_ERR_UNSUPPORTED: fold the
+ * ranges into the term).
  * attn_fwd_varlen and attn_bwd_varlen: fp32 [bias_heads, T, bias_ld], row
  * (h', t) holding M for token t (position i in its sequence) against the
  * keys at positions j < len of the same sequence (bias_ld >= the longest
- * sequence). */
+ * sequence).
+ *
+ * key_range: per-row key ranges (page "Attention Kernel", section
+ * "可编程 mask": document boundaries and prefix-LM are element rules; the
+ * block level skips the key tiles no row of a tile keeps).  int32 pairs
+ * (first, last): query row i keeps key j only when first_i <= j <= last_i
+ * (both ends included; first_i > last_i keeps no key, and any int32 value is
+ * accepted).  Shared by every head; combined with every other mask.
+ * Packed documents: each row's range is its own document (with causal = 1
+ * the diagonal cuts it); prefix-LM: (0, max(i, prefix - 1)) with causal = 0.
+ * Layouts: attn_fwd, attn_fwd_fp8 and attn_bwd [B, S_q, 2] over keys
+ * 0 .. S_k - 1; attn_fwd_varlen and attn_bwd_varlen [T, 2], the pair of
+ * token t counting key positions within its sequence;
+ * attn_prefill_paged_masked [T_q, 2], the pair of chunk token t counting
+ * key positions of its sequence's cache (0 .. seq_lens[s] - 1).  Must be
+ * 8-byte aligned (ATTN_ERR_INVAL otherwise).  The forward loads only the key
+ * tiles between the smallest first and the largest last of a 128-row tile
+ * and applies no per-element test to tiles inside every row's range; the
+ * dK/dV pass of the gradient visits only the query rows whose ranges reach
+ * its keys. */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
@@ -122,6 +143,7 @@ typedef struct {
     const float *bias;
     int bias_heads;
     int bias_ld;
+    const int32_t *key_range;
 } attn_mask;
 
 /* Optional sliding window (page "Attention Kernel", section "可编程 mask":
@@ -172,8 +194,8 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
  * Scores are formed exactly from the FP8 products (fp32 accumulation), then
  * multiplied by scale * q_scale * k_scale; the probabilities are rounded to
  * bf16 for the bf16 P V product, as in attn_fwd.  Scales must be finite and
- * > 0.  causal, keep-masks and window as attn_fwd; block masks and additive
- * terms are ATTN_ERR_UNSUPPORTED.  Supported: d_h = 128, S_k <= 262144.
+ * > 0.  causal, keep-masks, key ranges and window as attn_fwd; block masks
+ * and additive terms are ATTN_ERR_UNSUPPORTED.  Supported: d_h = 128, S_k <= 262144.
  */
 attn_status attn_fwd_fp8(const uint8_t *q, const uint8_t *k, const void *v, void *o, float *lse,
                          const float *q_scale, const float *k_scale, int B, int A, int A_kv, int S_q, int S_k,

@@ -42,7 +42,7 @@ def test_library_exports_exactly_the_header():
 
 def test_status_strings_and_version():
     import exact_attention_108_amd as ea
-    assert ea.attn_abi_version() == 5
+    assert ea.attn_abi_version() == 6
     assert ea.attn_status_string(0) == "ok"
     assert ea.attn_status_string(1) == "invalid argument"
     assert ea.attn_status_string(2) == "unsupported configuration"
@@ -85,7 +85,7 @@ class Mask(ctypes.Structure):
     """attn_mask of include/attn.h."""
     _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p), ("block_keep", ctypes.c_void_p),
                 ("block_heads", ctypes.c_int), ("bias", ctypes.c_void_p), ("bias_heads", ctypes.c_int),
-                ("bias_ld", ctypes.c_int)]
+                ("bias_ld", ctypes.c_int), ("key_range", ctypes.c_void_p)]
 
 
 P = ctypes.c_void_p(4096)  # never dereferenced: every call below is rejected (or empty) on the host
@@ -357,6 +357,28 @@ def test_attn_bwd_rejects_bad_arguments():
     assert lib.attn_bwd_workspace_bytes(2, 8, 100) == 12800
     assert lib.attn_bwd_workspace_bytes(1, 1, 1) == 256
     assert lib.attn_bwd_workspace_bytes(0, 8, 100) == 0
+
+
+def test_key_range_arguments():
+    """Per-row key ranges: 8-byte aligned int32 pairs, and (bf16) not together
+    with a dense additive term; the Python struct matches the header's."""
+    lib = _lib()
+    INVAL, UNSUP, OK = 1, 2, 0
+    mk = lambda *a: ctypes.byref(Mask(*a))
+    rng = lambda addr: mk(None, None, None, 0, None, 0, 0, addr)
+    assert fwd(lib, mask=rng(4096 + 4)) == INVAL                         # pairs are read as 8-byte loads
+    assert fwd(lib, mask=rng(4096 + 4), dt=0) == INVAL
+    assert fwd(lib, mask=rng(4096), S_q=0, q=None, o=None, lse=None) == OK
+    assert fwd(lib, mask=mk(None, None, None, 0, 4096, 1, 8, 4096)) == UNSUP   # bf16: not with a term
+    call = lambda m: lib.attn_bwd(P, P, P, P, P, P, P, P, P, 1, 4, 2, 8, 8, 128, 0.1, 1, m, None, 1, P, 1 << 30,
+                                  None)
+    assert call(rng(4096 + 4)) == INVAL
+    assert call(mk(None, None, None, 0, 4096, 1, 8, 4096)) == UNSUP
+    cu = np.array([0, 8], np.int32)
+    assert lib.attn_fwd_varlen(P, P, P, P, P, P, cu.ctypes.data_as(ctypes.c_void_p), 1, 8, 4, 2, 128, 0.1, 1,
+                               rng(4096 + 4), None, 1, None) == INVAL
+    import exact_attention_108_amd._binding as b
+    assert [f[0] for f in b._Mask._fields_] == [f[0] for f in Mask._fields_]
 
 
 def test_attn_bwd_varlen_rejects_bad_arguments():
