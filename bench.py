@@ -18,7 +18,9 @@ workload 1 recomputed from the forward's LSE), "window" (GQA causal S=16384
 with a 4096-key sliding window), "paged_prefill" (256-token chunks over the
 decode workload's paged cache), "block_sparse" (workload 1 with a 50% block
 mask), "dense_mask" (workload 1 with a general dense additive mask: packed
-documents with their derived block mask, and a per-head distance penalty) and
+documents with their derived block mask, and a per-head distance penalty),
+"key_range" (workload 1 with per-row key ranges: the same documents, forward
+and backward, and prefix-LM) and
 "decode_fp8" (workload 2 over E4M3 caches with per-(page, head) scales).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -694,6 +696,7 @@ def main():
     out["paged_prefill_fp8"] = bench_paged_prefill_fp8(w, args.steps, args.warmup)
     out["block_sparse"] = bench_block_sparse(w, args.steps, args.warmup)
     out["dense_mask"] = bench_dense_mask(w, args.steps, args.warmup)
+    out["key_range"] = bench_key_range(w, args.steps, args.warmup, out["dense_mask"]["avg_ms"])
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
     out["fp8_prefill"] = bench_fp8_prefill(args.steps, args.warmup, stream)
     out["decode_low_kv"] = bench_decode_low_kv(w, args.steps, args.warmup)
@@ -1155,6 +1158,60 @@ def bench_dense_mask(w, steps: int, warmup: int) -> dict:
                                  "term_GB/s": round(pen_bytes / (ms_pen.mean() * 1e-3) / 1e9, 1),
                                  "workload": "the same prefill with a finite fp32 per-head distance penalty "
                                              "[4, 32, 2048, 2048] (every causal pair kept)"}}
+
+
+def bench_key_range(w, steps: int, warmup: int, doc_term_ms: float) -> dict:
+    """The MHA causal prefill workload with per-row key ranges:
+      - packed documents as ranges (each row keeps its own document, the
+        causal flag cuts it; the same documents as the dense-mask leg, seed
+        1011), forward and backward; FLOPs = 4 d A x (kept causal pairs), the
+        backward 2.5x that;
+      - prefix-LM with a 512-token prefix (rows keep 0 .. max(i, 511), no
+        causal flag); FLOPs over the kept pairs."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p2, stream = w["p2"], w["stream"]
+    q, k, v, o, lse = w["dev2"]
+    B, A, S, d = p2.B, p2.A, p2.S_q, p2.d
+    kr_np = gen.make_key_ranges(B, S, S, "document", 1011)
+    i = np.arange(S)
+    last = np.minimum(kr_np[..., 1], i[None])                       # causal cut
+    kept = int(np.maximum(last - kr_np[..., 0] + 1, 0).sum())
+    kr = torch.from_numpy(kr_np).cuda()
+    ms_doc = _event_times(lambda: ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, key_range=kr,
+                                              stream=stream), steps, warmup, stream)
+    flops_doc = 4.0 * d * A * kept
+    tf_doc = flops_doc / (ms_doc.mean() * 1e-3) / 1e12
+    # backward of the documents forward
+    ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, key_range=kr, stream=stream)
+    do = to_dev(gen.make_dout(p2, 2002), "bf16")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(B, A, S), dtype=torch.uint8, device="cuda")
+    ms_bwd = _event_times(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p2.scale, causal=True,
+                                              key_range=kr, stream=stream), steps, warmup, stream)
+    tf_bwd = 2.5 * flops_doc / (ms_bwd.mean() * 1e-3) / 1e12
+    del do, dq, dk, dv, ws
+    P = 512
+    pre_np = gen.make_key_ranges(B, S, S, "prefix", 0, prefix=P)
+    kept_pre = int((np.maximum(i, P - 1) + 1).sum()) * B
+    pre = torch.from_numpy(pre_np).cuda()
+    ms_pre = _event_times(lambda: ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=False, key_range=pre,
+                                              stream=stream), steps, warmup, stream)
+    tf_pre = 4.0 * d * A * kept_pre / (ms_pre.mean() * 1e-3) / 1e12
+    return {"metric": "key-range causal prefill TFLOP/s (kept pairs)", "value": round(tf_doc, 2), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(tf_doc / PEAK_BF16_TFLOPS, 4), "avg_ms": round(float(ms_doc.mean()), 5),
+            "median_ms": round(float(np.median(ms_doc)), 5), "flops": flops_doc, "kept_pairs": kept,
+            "speedup_over_dense_term": round(doc_term_ms / float(ms_doc.mean()), 2),
+            "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16, packed documents (median 200 tokens) as per-row "
+                        "key ranges (the dense-mask leg's documents)",
+            "backward": {"value": round(tf_bwd, 2), "unit": "TFLOP/s (2.5x the kept-pair forward FLOPs)",
+                         "frac_of_bf16_peak": round(tf_bwd / PEAK_BF16_TFLOPS, 4),
+                         "avg_ms": round(float(ms_bwd.mean()), 5)},
+            "prefix_lm": {"value": round(tf_pre, 2), "unit": "TFLOP/s (kept pairs)",
+                          "frac_of_bf16_peak": round(tf_pre / PEAK_BF16_TFLOPS, 4),
+                          "avg_ms": round(float(ms_pre.mean()), 5), "kept_pairs": kept_pre,
+                          "workload": "the same prefill, prefix-LM with a 512-token prefix (no causal flag)"}}
 
 
 PAGED_CHUNK = 256

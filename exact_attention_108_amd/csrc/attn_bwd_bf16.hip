@@ -138,12 +138,13 @@ using Slot = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------- dQ
 // kVarlen: packed sequences (see BwdParams); kMasks: the block mask, the
-// dense additive term and the per-row key ranges (each runtime-optional).  Two waves per
+// dense additive term and the per-row key ranges (each runtime-optional);
+// kRange (without kMasks): per-row key ranges alone, at two waves per SIMD.  Two waves per
 // SIMD, one for the masked form at d = 128 (at two its term loads spill).
 template <int D, bool kMasks>
 constexpr int kDqWavesPerSimd = (D == 128 && kMasks) ? 1 : 2;
 
-template <int D, bool kVarlen, bool kMasks>
+template <int D, bool kVarlen, bool kMasks, bool kRange = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D, kMasks>, kDqWavesPerSimd<D, kMasks>))) void bwd_dq_kernel(BwdParams p,
                                                                                                     int n_qt) {
   constexpr int KSTEPS = D / 16;
@@ -155,7 +156,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   // block mask: flag of each 128-key block of this row block's key range
   __shared__ uint8_t sBlk[kMasks ? kBwdMaxKeyBlocks : 1];
   // per-row key ranges: the key bounds of each wave's rows
-  __shared__ KeyBounds sKb[kMasks ? 4 : 1];
+  static_assert(!(kMasks && kRange), "the masked form takes key ranges at run time");
+  // key ranges: compiled in (kRange), or optional at run time (kMasks)
+  constexpr bool kRng = kMasks || kRange;
+  __shared__ KeyBounds sKb[kRng ? 4 : 1];
+  // each row's clamped range, read back only by the wave that owns the row
+  // (for the masked tiles; registers are scarce here)
+  __shared__ int2 sRange[kRng ? kBwdQRows : 1];
 
   // heaviest query tiles first (most causal key tiles)
   int qt, h, b = 0, S_q, S_k;
@@ -214,12 +221,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   // per-row key ranges (the forward's mask): this lane's row keeps keys
   // [rng.x, rng.y] (clamped into [-1, S_k]); the bounds of the wave's and the
   // workgroup's rows narrow the tile range and pick the whole tiles
-  [[maybe_unused]] int2 rng = make_int2(-1, S_k);
   [[maybe_unused]] KeyBounds kb_wave{0, S_k, 0, S_k}, kb_wg{0, S_k, 0, S_k};
-  if constexpr (kMasks) {
-    if (p.key_range) {
+  if constexpr (kRng) {
+    int2 rng = make_int2(-1, S_k);
+    if (kRange || p.key_range) {
       const int32_t* kr = p.key_range + 2 * (kVarlen ? tok0 : (size_t)b * S_q);
       rng = row_in ? load_key_range(kr, qrow, S_k) : make_int2(0, -1);
+    }
+    if (g == 0) sRange[wave * 32 + l32] = rng;
+    if (kRange || p.key_range) {
       kb_wave = wave_key_bounds(row_in, rng.x, rng.y);
       kb_wg = workgroup_key_bounds<4>(kb_wave, sKb, wave, lane);
     }
@@ -229,12 +239,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   int kbeg = 0, kend = S_k;
   if (wr >= 0) kend = min(kend, q0 + kBwdQRows - 1 + off + wr + 1);
   if (wl >= 0) kbeg = max(q0 + off - wl, 0);
-  if constexpr (kMasks) {
+  if constexpr (kRng) {
     kbeg = max(kbeg, kb_wg.any_lo);
     kend = min(kend, kb_wg.any_hi);
   }
   const int j_lo = kbeg / kKeyTile;
   const int n_tiles = kend > kbeg ? (kend + kKeyTile - 1) / kKeyTile - j_lo : 0;
+  // key ranges: tiles j_lo + [jw_lo, jw_hi) lie inside the range of every row
+  // of this wave
+  [[maybe_unused]] int jw_lo = 0, jw_hi = n_tiles;
+  if constexpr (kRng) {
+    jw_lo = (max(kb_wave.all_lo, 0) + kKeyTile - 1) / kKeyTile - j_lo;
+    jw_hi = max(kb_wave.all_hi, 0) / kKeyTile - j_lo;
+  }
 
   int koff[KSTEPS];  // row-major operand read: row l32, chunk 2t + g
 #pragma unroll
@@ -310,7 +327,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     bool full = k0 + kKeyTile <= S_k && __ballot(ok) == ~0ull;
     if (wr >= 0) full = full && k0 + kKeyTile - 1 <= wave_row0 + off + wr;
     if (wl >= 0) full = full && k0 >= wave_row0 + 31 + off - wl;
-    if constexpr (kMasks) full = full && k0 >= kb_wave.all_lo && k0 + kKeyTile <= kb_wave.all_hi;
+    // (the key-range form takes the per-element step on every tile: with a
+    // whole-tile test the compiler's allocation spills over a hundred registers)
+    if constexpr (kRange) return true;
+    if constexpr (kRng) full = full && j >= jw_lo && j < jw_hi;
     return !full;
   };
   auto half = [&](const char* lds, int j, bool ok, int kb, auto masked_tag) {
@@ -341,7 +361,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     const uint64_t kvalid = __ballot(ok) >> (4 * g);
     int lim = wr >= 0 ? qrow + off + wr - k0 - 4 * g : (1 << 30);
     int lo = wl >= 0 ? qrow + off - wl - k0 - 4 * g : -(1 << 30);
-    if constexpr (kMasks) {
+    if constexpr (kRng) {
+      const int2 rng = sRange[wave * 32 + l32];
       lim = min(lim, rng.y - k0 - 4 * g);
       lo = max(lo, rng.x - k0 - 4 * g);
     }
@@ -415,16 +436,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
 // double-buffered, which fits 256 registers: two waves per SIMD, twice the
 // resident workgroups.  The launch picks it when the grid has enough
 // workgroups to fill those slots several times over.
-// kRange (with kMasks): per-row key ranges, a form of its own (the ranges of
-// a block are staged beside its statistics); one wave per SIMD at both head
-// dimensions (at d = 64 two spill).
+// kRange: per-row key ranges, forms of their own (the ranges of a block are
+// staged beside its statistics, every block takes the per-element step);
+// the register form runs one wave per SIMD at both head dimensions (at
+// d = 64 two spill), the K-in-LDS form two.
 template <int D, bool KLDS, bool kRange>
 constexpr int kDkdvWavesPerSimd = ((D == 64 && !kRange) || KLDS) ? 2 : 1;
 
 template <int D, bool KLDS, bool kVarlen, bool kMasks, bool kRange = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS, kRange>, kDkdvWavesPerSimd<D, KLDS, kRange>))) void bwd_dkdv_kernel(BwdParams p,
                                                                                                       int n_kt) {
-  static_assert(!kRange || (kMasks && !KLDS), "key ranges: the masked one-wave form");
+  static_assert(!(KLDS && kMasks), "the K-in-LDS form takes no block mask or term");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
@@ -519,11 +541,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
     {
       const int32_t* kr = p.key_range + 2 * (kVarlen ? tok0 : (size_t)b * S_q);
       int lo_row = INT_MAX, hi_row = -1;
-      for (int i = tid; i < S_q; i += kThreads) {
-        const int2 r = *(const int2*)(kr + 2 * (size_t)i);
-        if (r.x <= r.y && r.x <= k_last && r.y >= k_first) {
-          lo_row = min(lo_row, i);
-          hi_row = max(hi_row, i);
+      // rows outside [i_first, i_end) are out already (window, causal
+      // diagonal); four loads in flight per thread
+      for (int i0 = i_first + tid; i0 < i_end; i0 += 4 * kThreads) {
+        int2 r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * kThreads;
+          r[u] = i < i_end ? *(const int2*)(kr + 2 * (size_t)i) : make_int2(1, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * kThreads;
+          if (r[u].x <= r[u].y && r[u].x <= k_last && r[u].y >= k_first) {
+            lo_row = min(lo_row, i);
+            hi_row = max(hi_row, i);
+          }
         }
       }
       lo_row = wave_min_i32(lo_row);
@@ -644,11 +677,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
       const f32x4 a = *(const f32x4*)(st + 2 * (8 * r4 + 4 * g));
       const f32x4 c = *(const f32x4*)(st + 2 * (8 * r4 + 4 * g) + 4);
       const float lv[4] = {a[0], a[2], c[0], c[2]}, dv[4] = {a[1], a[3], c[1], c[3]};
-      [[maybe_unused]] i32x4 ra, rc;
-      if constexpr (kRange && MASKED) {
-        ra = *(const i32x4*)(rg + 2 * (8 * r4 + 4 * g));
-        rc = *(const i32x4*)(rg + 2 * (8 * r4 + 4 * g) + 4);
-      }
+
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * r4 + i;
@@ -657,9 +686,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
           const int m = 8 * r4 + i;
           bool live = m >= m_lo && m < m_hi;
           if constexpr (kRange) {
-            const int lo_i = i < 2 ? ra[2 * i] : rc[2 * (i - 2)];
-            const int hi_i = i < 2 ? ra[2 * i + 1] : rc[2 * (i - 2) + 1];
-            live = live && key >= lo_i && key <= hi_i;
+            const int2 r = *(const int2*)(rg + 2 * m + 8 * g);
+            live = live && key >= r.x && key <= r.y;
           }
           x = live ? x : -INFINITY;
         }
@@ -834,7 +862,7 @@ void plan_order(int units, int group_max, int& per, int& group) {
   group = g;
 }
 
-template <int D, bool kVarlen, bool kMasks>
+template <int D, bool kVarlen, bool kMasks, bool kRange>
 hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
   BwdParams p = p_in;
   int n_qt, n_units_q, n_units_kv;
@@ -853,8 +881,8 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
   const int n_kt = kVarlen ? p.total_tiles : (p.S_k + kBwdKRows - 1) / kBwdKRows;
   // the dQ pass writes the row statistics the dK/dV pass reads: same stream, in order
   if (n_qt > 0 && (kVarlen || p.S_q > 0)) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kVarlen, kMasks>), dim3(n_qt * n_units_q), dim3(kThreads), 0, stream, p,
-                       n_qt);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kVarlen, kMasks, kRange && !kMasks>), dim3(n_qt * n_units_q),
+                       dim3(kThreads), 0, stream, p, n_qt);
   }
   if (n_kt > 0 && (kVarlen || p.S_k > 0)) {
     // with no query row every key gradient is zero; the kernel still writes them
@@ -871,19 +899,13 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
     if constexpr (D == 128 && !kMasks && !kVarlen) two_wave = n_wg >= kKlDsMinWorkgroups;
     if constexpr (D == 128 && !kMasks && !kVarlen) {
       if (two_wave) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, kVarlen, false>), dim3(n_wg), dim3(kThreads), 0, stream, p,
-                           n_kt);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, kVarlen, false, kRange>), dim3(n_wg), dim3(kThreads), 0,
+                           stream, p, n_kt);
         return hipGetLastError();
       }
     }
-    if constexpr (kMasks) {
-      if (p.key_range) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, true, true>), dim3(n_wg), dim3(kThreads), 0, stream, p,
-                           n_kt);
-        return hipGetLastError();
-      }
-    }
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, kMasks>), dim3(n_wg), dim3(kThreads), 0, stream, p, n_kt);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, kMasks, kRange>), dim3(n_wg), dim3(kThreads), 0, stream, p,
+                       n_kt);
     (void)two_wave;
   }
   return hipGetLastError();
@@ -891,11 +913,18 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  const bool masks = p.block_keep || p.bias || p.key_range;
-  if (p.cu_seqlens && masks) return launch_bwd_v<D, true, true>(p, stream);
-  if (p.cu_seqlens) return launch_bwd_v<D, true, false>(p, stream);
-  if (masks) return launch_bwd_v<D, false, true>(p, stream);
-  return launch_bwd_v<D, false, false>(p, stream);
+  // (key ranges with a term are rejected before the launch)
+  const bool masks = p.block_keep || p.bias, rng = p.key_range != nullptr;
+  if (p.cu_seqlens) {
+    if (masks && rng) return launch_bwd_v<D, true, true, true>(p, stream);
+    if (masks) return launch_bwd_v<D, true, true, false>(p, stream);
+    if (rng) return launch_bwd_v<D, true, false, true>(p, stream);
+    return launch_bwd_v<D, true, false, false>(p, stream);
+  }
+  if (masks && rng) return launch_bwd_v<D, false, true, true>(p, stream);
+  if (masks) return launch_bwd_v<D, false, true, false>(p, stream);
+  if (rng) return launch_bwd_v<D, false, false, true>(p, stream);
+  return launch_bwd_v<D, false, false, false>(p, stream);
 }
 
 }  // namespace
