@@ -336,16 +336,16 @@ def grid_matches(kname: str, grid: int, pattern: str, wgs) -> bool:
 # kernel serves the MHA workload (16 query tiles x 32 heads x 4 batch rows), the
 # long GQA workload (128 x 32) and the sliding-window leg (256 x 32), so the
 # grid tells them apart.
-DENSE = "prefill_bf16_kernel<128, false, false, false, false, false, false>"
-FP8_DENSE = "prefill_bf16_kernel<128, false, false, false, false, true, false>"
+DENSE = "prefill_bf16_kernel<128, false, false, false, false, false, false, false>"
+FP8_DENSE = "prefill_bf16_kernel<128, false, false, false, false, true, false, false>"
 TRAFFIC_PARTS = {
     "prefill": (DENSE, 2048),
     "gqa_long": (DENSE, 4096),
-    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false, false>", None),
+    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false, false, false>", None),
     "decode_split": ("decode_split_kernel<128, 1, false, 1, 4>", None),
     "decode_merge": ("decode_merge_kernel", None),
-    "bwd_dq": ("bwd_dq_kernel<128, false, false>", None),
-    "bwd_dkdv": ("bwd_dkdv_kernel<128, true, false, false>", None),
+    "bwd_dq": ("bwd_dq_kernel<128, false, false, false>", None),
+    "bwd_dkdv": ("bwd_dkdv_kernel<128, true, false, false, false>", None),
 }
 
 
@@ -384,7 +384,7 @@ TRACE_ROWS = [
     ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, "mha"),
     ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, "gqa"),
     ("sliding-window GQA causal prefill S=32768, 4096-key window (kept pairs)", DENSE, 8192, "window"),
-    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false>",
+    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false, false>",
      None, "varlen"),
     ("paged decode split, bf16 cache (KV bytes / split time)", ("decode_split_kernel<128, 1, false, 1, 4>", 0), None,
      "decode"),
@@ -397,20 +397,26 @@ TRACE_ROWS = [
      "lowkv1"),
     ("paged decode split, A=32 on A_kv=2 (one-wave workgroups)", "decode_split_kernel<128, 1, false, 1, 1>", None,
      "lowkv2"),
-    ("backward dQ pass", "bwd_dq_kernel<128, false, false>", None, None),
-    ("backward dK/dV pass", "bwd_dkdv_kernel<128, true, false, false>", None, None),
+    ("backward dQ pass", "bwd_dq_kernel<128, false, false, false>", None, None),
+    ("backward dK/dV pass", "bwd_dkdv_kernel<128, true, false, false, false>", None, None),
     ("paged chunked prefill, 256-token chunks (causal pairs)",
-     "prefill_bf16_kernel<128, true, true, false, false, false, false>", None, "paged"),
-    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false, false>", None, None),
-    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false>",
+     "prefill_bf16_kernel<128, true, true, false, false, false, false, false>", None, "paged"),
+    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false, false, false>", None, None),
+    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false, false>",
      None, None),
-    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false>", None,
+    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false, false>", None,
      None),
     ("block mask of an additive term", "block_keep_kernel", None, None),
+    ("key ranges: packed documents, causal prefill",
+     ("prefill_bf16_kernel<128, false, false, false, false, false, false, true>", 0), None, None),
+    ("key ranges: prefix-LM prefill (512-token prefix)",
+     ("prefill_bf16_kernel<128, false, false, false, false, false, false, true>", 1), None, None),
+    ("key ranges: backward dQ pass (documents)", "bwd_dq_kernel<128, false, false, true>", None, None),
+    ("key ranges: backward dK/dV pass (documents)", "bwd_dkdv_kernel<128, true, false, false, true>", None, None),
     ("FP8-QK causal prefill, MHA shape", FP8_DENSE, 2048, "fp8_mha"),
     ("FP8-QK causal prefill, long GQA shape", FP8_DENSE, 4096, "fp8_gqa"),
     ("paged chunked prefill over the E4M3 cache (causal pairs)",
-     "prefill_bf16_kernel<128, true, true, false, false, false, true>", None, "paged"),
+     "prefill_bf16_kernel<128, true, true, false, false, false, true, false>", None, "paged"),
 ]
 
 
@@ -654,7 +660,7 @@ def main():
                      "traffic": None if traffic_prefill is None else round(traffic_prefill),
                      "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
                      "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
-                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
+                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
                      "median_launch_ms": round(med["prefill"], 5), "min_launch_ms": round(mn["prefill"], 5),
                      "measured_ceiling": {"what": "torch.matmul bf16 8192^3 on the same GPU",
                                           "TFLOP/s": ceil["gemm_tflops"],
@@ -769,7 +775,7 @@ def bench_backward(w, steps: int, warmup: int) -> dict:
             "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5),
             "flops": flops,
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 (the prefill workload)",
-            "kernels": "bwd_dq_kernel<128, false, false> then bwd_dkdv_kernel<128, true, false, false> (K rows in LDS; one call)"}
+            "kernels": "bwd_dq_kernel<128, false, false, false> then bwd_dkdv_kernel<128, true, false, false, false> (K rows in LDS; one call)"}
 
 
 def window_pairs(S: int, left: int) -> int:
