@@ -101,6 +101,15 @@ class Oracle:
         return bias, bias.shape[1]
 
     @staticmethod
+    def _with_alibi(bias, alibi_slopes, B, A, S_q, S_k):
+        if alibi_slopes is None:
+            return bias
+        if np.asarray(alibi_slopes).reshape(-1).size != A:
+            raise ValueError("alibi_slopes must hold one slope per query head")
+        a = alibi_term(alibi_slopes, B, S_q, S_k)
+        return a if bias is None else (np.asarray(bias, np.float32) + a).astype(np.float32)
+
+    @staticmethod
     def _keep_matrix(m_keep, key_range, B, S_q, S_k):
         mk = None if m_keep is None else np.ascontiguousarray(m_keep, dtype=np.uint8).reshape(B, S_q, S_k)
         if key_range is not None:
@@ -119,8 +128,9 @@ class Oracle:
         return r, r.size
 
     def attn_fwd(self, q, k, v, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None, bias=None,
-                 block_keep=None, rows=None, key_range=None):
-        """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d]; m_keep an
+                 block_keep=None, rows=None, key_range=None, alibi_slopes=None):
+        """Dense batched attention.  q [B,A,S_q,d], k/v [B,A_kv,S_k,d]; alibi_slopes
+        optional per-head ALiBi slopes [A] (see alibi_term), added to bias; m_keep an
         optional dense keep matrix [B,S_q,S_k] (see window_keep); key_range
         optional per-row key ranges int [B,S_q,2] (see key_range_keep), applied
         together with m_keep; bias an optional
@@ -143,6 +153,7 @@ class Oracle:
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
         mk = self._keep_matrix(m_keep, key_range, B, S_q, S_k)
+        bias = self._with_alibi(bias, alibi_slopes, B, A, S_q, S_k)
         bias, bh = self._bias(bias, B, A, S_q, S_k)
         bk, bkh = self._blocks(block_keep, B, A, S_q, S_k)
         r, n = self._rows(rows)
@@ -159,7 +170,8 @@ class Oracle:
         return o, lse
 
     def attn_fwd_varlen(self, q, k, v, cu_seqlens, *, dtype, scale, causal=True, q_keep=None,
-                        k_keep=None, rows=None, bias=None, block_keep=None, window=None, key_range=None):
+                        k_keep=None, rows=None, bias=None, block_keep=None, window=None, key_range=None,
+                        alibi_slopes=None):
         """Packed varlen attention.  q [A,T,d], k/v [A_kv,T,d]; rows = h*T + t.
 
         bias: fp32 [1 or A, T, ld] -- row t (token i of its sequence) holds the
@@ -168,13 +180,15 @@ class Oracle:
         length / 128), the 128 x 128 block flags of each sequence's own
         (row, key) grid; window: (left, right) around each row's position in
         its sequence; key_range: int [T, 2], token t's key range as positions
-        within its sequence.  With any of these, each sequence is its own dense problem
+        within its sequence; alibi_slopes: [A], distances within each sequence.
+        With any of these, each sequence is its own dense problem
         ("Attention Kernel", Paged 与 ragged KV: packed sequences never attend
         across boundaries) and goes through attn_fwd with its slices."""
-        if bias is not None or block_keep is not None or window is not None or key_range is not None:
+        if bias is not None or block_keep is not None or window is not None or key_range is not None or \
+                alibi_slopes is not None:
             return self._varlen_by_sequence(q, k, v, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
                                             q_keep=q_keep, k_keep=k_keep, bias=bias, block_keep=block_keep,
-                                            window=window, rows=rows, key_range=key_range)
+                                            window=window, rows=rows, key_range=key_range, alibi_slopes=alibi_slopes)
         q, k, v = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype)
         if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape != v.shape:
             raise ValueError("q [A,T,d], k/v [A_kv,T,d]")
@@ -200,7 +214,7 @@ class Oracle:
         return o, lse
 
     def _varlen_by_sequence(self, q, k, v, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, bias, block_keep,
-                            window, rows=None, key_range=None):
+                            window, rows=None, key_range=None, alibi_slopes=None):
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         A, T, d = q.shape
         n_seq = cu.size - 1
@@ -240,6 +254,8 @@ class Oracle:
                 kw["m_keep"] = window_keep(1, L, L, int(window[0]), int(window[1]))
             if key_range is not None:
                 kw["key_range"] = np.asarray(key_range).reshape(T, 2)[s0:s1][None]
+            if alibi_slopes is not None:
+                kw["alibi_slopes"] = alibi_slopes
             if bias is not None:
                 kw["bias"] = bias[:, s0:s1, :L][None]
             if block_keep is not None:
@@ -258,9 +274,9 @@ class Oracle:
         return o, lse
 
     def attn_bwd(self, q, k, v, do, *, dtype, scale, causal=False, q_keep=None, k_keep=None, m_keep=None,
-                 bias=None, block_keep=None, key_range=None):
+                 bias=None, block_keep=None, key_range=None, alibi_slopes=None):
         """Gradient of attn_fwd: q, do [B,A,S_q,d]; k, v [B,A_kv,S_k,d]; masks
-        as attn_fwd takes them.  Returns (dq, dk, dv) in fp64 with the shapes of
+        and ALiBi slopes as attn_fwd takes them.  Returns (dq, dk, dv) in fp64 with the shapes of
         q, k and v."""
         q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
         if q.ndim != 4 or k.shape != v.shape or do.shape != q.shape:
@@ -272,6 +288,7 @@ class Oracle:
         qk = None if q_keep is None else np.ascontiguousarray(q_keep, dtype=np.uint8).reshape(B, S_q)
         kk = None if k_keep is None else np.ascontiguousarray(k_keep, dtype=np.uint8).reshape(B, S_k)
         mk = self._keep_matrix(m_keep, key_range, B, S_q, S_k)
+        bias = self._with_alibi(bias, alibi_slopes, B, A, S_q, S_k)
         bias, bh = self._bias(bias, B, A, S_q, S_k)
         bk, bkh = self._blocks(block_keep, B, A, S_q, S_k)
         dq = np.empty((B, A, S_q, d), dtype=np.float64)
@@ -285,7 +302,7 @@ class Oracle:
         return dq, dk, dv
 
     def attn_bwd_varlen(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal=True, q_keep=None, k_keep=None,
-                        window=None, bias=None, block_keep=None, key_range=None):
+                        window=None, bias=None, block_keep=None, key_range=None, alibi_slopes=None):
         """Gradient of the packed varlen prefill: q, do [A,T,d]; k, v [A_kv,T,d];
         cu_seqlens [n_seq+1]; keep masks [T]; window (left, right) within each
         sequence (-1 = unbounded).  Returns (dq, dk, dv) in fp64.  bias,
@@ -293,10 +310,11 @@ class Oracle:
         gradient is the dense gradient of its own problem (its slices of the
         masks) -- the backward uses the forward's mask ("Attention Kernel",
         Backward 与重计算)."""
-        if bias is not None or block_keep is not None or key_range is not None:
+        if bias is not None or block_keep is not None or key_range is not None or alibi_slopes is not None:
             return self._bwd_varlen_by_sequence(q, k, v, do, cu_seqlens, dtype=dtype, scale=scale, causal=causal,
                                                 q_keep=q_keep, k_keep=k_keep, window=window, bias=bias,
-                                                block_keep=block_keep, key_range=key_range)
+                                                block_keep=block_keep, key_range=key_range,
+                                                alibi_slopes=alibi_slopes)
         q, k, v, do = self._arr(q, dtype), self._arr(k, dtype), self._arr(v, dtype), self._arr(do, dtype)
         if q.ndim != 3 or k.shape != v.shape or do.shape != q.shape:
             raise ValueError("q, do [A,T,d]; k, v [A_kv,T,d]")
@@ -319,7 +337,7 @@ class Oracle:
         return dq, dk, dv
 
     def _bwd_varlen_by_sequence(self, q, k, v, do, cu_seqlens, *, dtype, scale, causal, q_keep, k_keep, window, bias,
-                                block_keep, key_range=None):
+                                block_keep, key_range=None, alibi_slopes=None):
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         A, T, d = q.shape
         A_kv = k.shape[0]
@@ -352,6 +370,8 @@ class Oracle:
                 kw["m_keep"] = window_keep(1, L, L, int(window[0]), int(window[1]))
             if key_range is not None:
                 kw["key_range"] = np.asarray(key_range).reshape(T, 2)[s0:s1][None]
+            if alibi_slopes is not None:
+                kw["alibi_slopes"] = alibi_slopes
             if bias is not None:
                 kw["bias"] = bias[:, s0:s1, :L][None]
             if block_keep is not None:
@@ -363,7 +383,7 @@ class Oracle:
         return dq, dk, dv
 
     def prefill_paged(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal=True,
-                      window=None, rows=None, bias=None, block_keep=None, key_range=None):
+                      window=None, rows=None, bias=None, block_keep=None, key_range=None, alibi_slopes=None):
         """Query chunks over a paged cache: q [A,T_q,d] packed chunks (cu_seqlens_q
         [n_seq+1]); caches [P, page_size, A_kv, d]; block_table [n_seq, max_pages];
         seq_lens [n_seq] (chunk included).  Chunk row i of sequence s sits at
@@ -374,15 +394,16 @@ class Oracle:
         the keys at positions j < seq_lens of its sequence; block_keep: uint8
         [n_seq, 1 or A, ceil(longest chunk/128), ceil(longest seq_lens/128)] over
         (chunk row, key position); key_range: int [T_q, 2], chunk token t's key
-        range as positions in its sequence.  With any of these, each sequence's keys are
+        range as positions in its sequence; alibi_slopes: [A], chunk row i at
+        position seq_lens - q_s + i.  With any of these, each sequence's keys are
         gathered token by token through its block table (token t: row t %
         page_size of page block_table[s][t // page_size]) and the chunk is the
         dense problem of its rows against them ("Attention Kernel", Paged 与
         ragged KV and 可编程 mask)."""
-        if bias is not None or block_keep is not None or key_range is not None:
+        if bias is not None or block_keep is not None or key_range is not None or alibi_slopes is not None:
             return self._paged_by_sequence(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, dtype=dtype,
                                            scale=scale, causal=causal, window=window, rows=rows, bias=bias,
-                                           block_keep=block_keep, key_range=key_range)
+                                           block_keep=block_keep, key_range=key_range, alibi_slopes=alibi_slopes)
         q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
         if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
             raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
@@ -411,7 +432,7 @@ class Oracle:
         return o, lse
 
     def _paged_by_sequence(self, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, *, dtype, scale, causal,
-                           window, rows, bias, block_keep, key_range=None):
+                           window, rows, bias, block_keep, key_range=None, alibi_slopes=None):
         A, T_q, d = q.shape
         page_size, A_kv = k_cache.shape[1], k_cache.shape[2]
         cu = np.asarray(cu_seqlens_q, dtype=np.int64)
@@ -455,6 +476,8 @@ class Oracle:
                 kw["m_keep"] = window_keep(1, ql, L, int(window[0]), int(window[1]))
             if key_range is not None:
                 kw["key_range"] = np.asarray(key_range).reshape(T_q, 2)[s0:s1][None]
+            if alibi_slopes is not None:
+                kw["alibi_slopes"] = alibi_slopes
             if bias is not None:
                 kw["bias"] = bias[:, s0:s1, :L][None]
             if block_keep is not None:
@@ -605,6 +628,21 @@ def window_keep(B: int, S_q: int, S_k: int, left: int, right: int) -> np.ndarray
     if right >= 0:
         keep &= j <= i + right
     return np.broadcast_to(keep.astype(np.uint8), (B, S_q, S_k)).copy()
+
+
+def alibi_term(slopes, B: int, S_q: int, S_k: int, positions=None) -> np.ndarray:
+    """ALiBi as the additive term M, fp32 [B, A, S_q, S_k]: M[b, h, i, j] =
+    -slopes[h] * |p_i - j|, with query i at the bottom-right aligned position
+    p_i = i + S_k - S_q (as for causal), or at positions[i] when given (a
+    packed chunk's positions in its sequence).  Page "Attention Kernel",
+    section "正确性契约": ALiBi is one of the transforms fused into the score
+    (a linear penalty on the query-key distance, per head); it enters the
+    score like any additive term, after the scaling of q . k."""
+    sl = np.asarray(slopes, dtype=np.float64).reshape(-1)
+    p = (np.arange(S_q, dtype=np.int64) + (S_k - S_q)) if positions is None else np.asarray(positions, np.int64)
+    dist = np.abs(p[:, None] - np.arange(S_k, dtype=np.int64)[None, :]).astype(np.float64)
+    m = -sl[:, None, None] * dist[None]
+    return np.broadcast_to(m.astype(np.float32)[None], (B, sl.size, S_q, S_k)).copy()
 
 
 def key_range_keep(key_range, S_k: int) -> np.ndarray:

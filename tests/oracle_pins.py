@@ -721,6 +721,133 @@ def pin_bwd_key_range_finite_differences(orc):
         assert np.max(np.abs(num - g)) <= 1e-7, name
 
 
+# ---- ALiBi (a per-head linear distance penalty as the additive term)
+
+def pin_alibi_causal_is_a_per_key_term(orc):
+    """Under causal masking row i's ALiBi term -s (p_i - j) is s j plus a row
+    constant, so O equals attention with the per-key term s j alone and the
+    LSE moves by -s p_i (softmax shift invariance); per head, its own slope."""
+    rng = np.random.default_rng(81)
+    B, A, S_q, S_k, d = 1, 3, 7, 11, 4
+    slopes = np.array([0.5, 0.125, 2.0])
+    q = _f32(rng.standard_normal((B, A, S_q, d)))
+    k = _f32(rng.standard_normal((B, A, S_k, d)))
+    v = _f32(rng.standard_normal((B, A, S_k, d)))
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, causal=True, alibi_slopes=slopes)
+    p = np.arange(S_q) + (S_k - S_q)
+    for h, sl in enumerate(slopes):
+        term = np.broadcast_to((sl * np.arange(S_k))[None, None, None, :], (B, 1, S_q, S_k)).astype(np.float32)
+        o2, l2 = orc.attn_fwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], dtype="f32", scale=0.5, causal=True,
+                              bias=term)
+        assert np.allclose(o[:, h], o2[:, 0], rtol=0, atol=1e-10), h
+        assert np.allclose(lse[:, h], l2[:, 0] - sl * p, rtol=0, atol=1e-9), h
+
+
+def pin_alibi_closed_forms(orc):
+    """Slope 0 is no term (bitwise); two keys give the logistic of the logit
+    difference including the distance penalty; a huge slope leaves only the
+    key at the query's own position (O = that value row); non-causal ALiBi is
+    mirror-symmetric: row i over keys reversed = row S - 1 - i over the
+    original keys."""
+    rng = np.random.default_rng(82)
+    S, d = 9, 4
+    q = _f32(rng.standard_normal((1, 1, S, d)))
+    k = _f32(rng.standard_normal((1, 1, S, d)))
+    v = _f32(rng.standard_normal((1, 1, S, d)))
+    a = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, alibi_slopes=[0.0])
+    b = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # two keys at positions 0 and 1, query rows at positions 0 and 1 (S_q = S_k = 2)
+    s2 = 0.75
+    o, lse = orc.attn_fwd(q[:, :, :2], k[:, :, :2], v[:, :, :2], dtype="f32", scale=0.5, alibi_slopes=[s2])
+    qq, kk, vv = (x[0, 0, :2].astype(np.float64) for x in (q, k, v))
+    for i in range(2):
+        z = 0.5 * (qq[i] @ kk.T) - s2 * np.abs(i - np.arange(2))
+        w = expit(z[0] - z[1])
+        assert np.allclose(o[0, 0, i], w * vv[0] + (1 - w) * vv[1], rtol=0, atol=1e-12)
+        assert abs(lse[0, 0, i] - np.logaddexp(z[0], z[1])) < 1e-12
+    o, _ = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, alibi_slopes=[1e4])
+    assert np.array_equal(o[0, 0], v[0, 0].astype(np.float64))
+    o, lse = orc.attn_fwd(q, k, v, dtype="f32", scale=0.5, alibi_slopes=[0.3])
+    om, lm = orc.attn_fwd(q[:, :, ::-1], k[:, :, ::-1], v[:, :, ::-1], dtype="f32", scale=0.5, alibi_slopes=[0.3])
+    assert np.allclose(o[0, 0], om[0, 0, ::-1], rtol=0, atol=1e-12)
+    assert np.allclose(lse[0, 0], lm[0, 0, ::-1], rtol=0, atol=1e-12)
+
+
+def pin_alibi_packed_and_paged_positions(orc):
+    """Packed sequences measure distances within each sequence (one sequence
+    = the dense call, bitwise), and a paged chunk's rows sit at the bottom of
+    their sequence: they equal the last rows of the dense call over the whole
+    sequence, ALiBi included."""
+    rng = np.random.default_rng(83)
+    A, A_kv, d = 2, 1, 4
+    slopes = np.array([0.25, 1.0])
+    lens = [9, 0, 14]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = _f32(rng.standard_normal((A, T, d)))
+    k = _f32(rng.standard_normal((A_kv, T, d)))
+    v = _f32(rng.standard_normal((A_kv, T, d)))
+    o, lse = orc.attn_fwd_varlen(q, k, v, cu, dtype="f32", scale=0.5, causal=False, alibi_slopes=slopes)
+    for s0, s1 in ((0, 9), (9, 23)):
+        o2, l2 = orc.attn_fwd(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], dtype="f32", scale=0.5,
+                              alibi_slopes=slopes)
+        assert np.array_equal(o[:, s0:s1], o2[0]) and np.array_equal(lse[:, s0:s1], l2[0])
+    q_lens = [3, 0, 5]
+    qp, kc, vc, bt, sl, cuq = _paged_problem([20, 4, 33], q_lens, A, A_kv, d, 16, 84)
+    for causal in (True, False):
+        op, lp = orc.prefill_paged(qp, kc, vc, bt, sl, cuq, dtype="f32", scale=0.5, causal=causal,
+                                   alibi_slopes=slopes)
+        for sidx, (L, ql) in enumerate(zip(sl, q_lens)):
+            if ql == 0:
+                continue
+            c0 = int(cuq[sidx])
+            kk = _contiguous(kc, bt[sidx], int(L), 16)[None]
+            vv = _contiguous(vc, bt[sidx], int(L), 16)[None]
+            # the chunk's rows are the last ql of a dense call with S_q = S_k = L
+            qfull = np.zeros((1, A, int(L), d), np.float32)
+            qfull[0, :, L - ql:] = qp[:, c0:c0 + ql]
+            o2, l2 = orc.attn_fwd(qfull, kk, vv, dtype="f32", scale=0.5, causal=causal, alibi_slopes=slopes)
+            assert np.allclose(op[:, c0:c0 + ql], o2[0, :, L - ql:], rtol=0, atol=1e-12), (sidx, causal)
+            assert np.allclose(lp[:, c0:c0 + ql], l2[0, :, L - ql:], rtol=0, atol=1e-12), (sidx, causal)
+
+
+def pin_bwd_alibi_finite_differences(orc):
+    """The gradient with ALiBi (non-causal, two heads with their own slopes,
+    packed and dense) against central differences of the loss sum(O * dO)."""
+    B, A, A_kv, S_q, S_k, d = 1, 2, 1, 6, 9, 3
+    q, k, v, do = _bwd_problem(B, A, A_kv, S_q, S_k, d, 85)
+    slopes = [0.4, 1.5]
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, dtype="f64", scale=0.7, alibi_slopes=slopes)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attn_fwd(qq, kk, vv, dtype="f64", scale=0.7, alibi_slopes=slopes)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            am = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert np.max(np.abs(num - g)) <= 1e-7, name
+    # packed: one sequence's gradient is the dense gradient of that sequence
+    cu = np.array([0, 4, 9], np.int32)
+    qp, kp, vp, dop = q[0, :, :S_q], k[0, :, :S_k], v[0, :, :S_k], do[0, :, :S_q]
+    qp = np.concatenate([qp, qp[:, :3]], axis=1)[:, :9]
+    dop = np.concatenate([dop, dop[:, :3]], axis=1)[:, :9]
+    g = orc.attn_bwd_varlen(qp, kp, vp, dop, cu, dtype="f64", scale=0.7, causal=True, alibi_slopes=slopes)
+    for s0, s1 in ((0, 4), (4, 9)):
+        r = orc.attn_bwd(qp[None, :, s0:s1], kp[None, :, s0:s1], vp[None, :, s0:s1], dop[None, :, s0:s1],
+                         dtype="f64", scale=0.7, causal=True, alibi_slopes=slopes)
+        for x, y in zip(g, r):
+            assert np.array_equal(x[:, s0:s1], y[0])
+
+
 # ---- FP8 (OCP E4M3) caches: code values, and decode over dequantised pages
 
 def pin_fp8_e4m3_published_values(orc):

@@ -135,6 +135,15 @@ PY_MUTANTS = [
      'kw["key_range"] = np.asarray(key_range).reshape(T, 2)[0:L][None]', 0),
     ("paged key ranges of the first tokens", 'kw["key_range"] = np.asarray(key_range).reshape(T_q, 2)[s0:s1][None]',
      'kw["key_range"] = np.asarray(key_range).reshape(T_q, 2)[0:ql][None]', 0),
+    ("ALiBi: penalty sign flipped", "m = -sl[:, None, None] * dist[None]", "m = sl[:, None, None] * dist[None]", 0),
+    ("ALiBi: signed distance", "dist = np.abs(p[:, None] - np.arange(S_k, dtype=np.int64)[None, :])",
+     "dist = (p[:, None] - np.arange(S_k, dtype=np.int64)[None, :])", 0),
+    ("ALiBi: queries aligned top-left", "(np.arange(S_q, dtype=np.int64) + (S_k - S_q))",
+     "np.arange(S_q, dtype=np.int64)", 0),
+    ("ALiBi: the first head's slope for every head", "m = -sl[:, None, None] * dist[None]",
+     "m = -sl[:1, None, None] * dist[None]", 0),
+    ("ALiBi ignored in packed and paged calls", 'kw["alibi_slopes"] = alibi_slopes', 'kw["alibi_slopes"] = None', 0),
+    ("ALiBi ignored", "return a if bias is None else", "return bias if bias is None else", 0),
     ("varlen block mask transposed", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
      'kw["block_keep"] = np.ascontiguousarray(block_keep[s][None, :, :nbs, :nbs].transpose(0, 1, 3, 2))', 0),
 ]
