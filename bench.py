@@ -20,7 +20,8 @@ decode workload's paged cache), "block_sparse" (workload 1 with a 50% block
 mask), "dense_mask" (workload 1 with a general dense additive mask: packed
 documents with their derived block mask, and a per-head distance penalty),
 "key_range" (workload 1 with per-row key ranges: the same documents, forward
-and backward, and prefix-LM) and
+and backward, and prefix-LM), "alibi" (workload 1 with ALiBi computed in the
+kernels, forward and backward) and
 "decode_fp8" (workload 2 over E4M3 caches with per-(page, head) scales).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -336,16 +337,16 @@ def grid_matches(kname: str, grid: int, pattern: str, wgs) -> bool:
 # kernel serves the MHA workload (16 query tiles x 32 heads x 4 batch rows), the
 # long GQA workload (128 x 32) and the sliding-window leg (256 x 32), so the
 # grid tells them apart.
-DENSE = "prefill_bf16_kernel<128, false, false, false, false, false, false, false>"
-FP8_DENSE = "prefill_bf16_kernel<128, false, false, false, false, true, false, false>"
+DENSE = "prefill_bf16_kernel<128, false, false, false, false, false, false, false, false>"
+FP8_DENSE = "prefill_bf16_kernel<128, false, false, false, false, true, false, false, false>"
 TRAFFIC_PARTS = {
     "prefill": (DENSE, 2048),
     "gqa_long": (DENSE, 4096),
-    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false, false, false>", None),
+    "varlen": ("prefill_bf16_kernel<64, true, false, false, false, false, false, false, false>", None),
     "decode_split": ("decode_split_kernel<128, 1, false, 1, 4>", None),
     "decode_merge": ("decode_merge_kernel", None),
-    "bwd_dq": ("bwd_dq_kernel<128, false, false, false>", None),
-    "bwd_dkdv": ("bwd_dkdv_kernel<128, true, false, false, false>", None),
+    "bwd_dq": ("bwd_dq_kernel<128, false, false, false, false>", None),
+    "bwd_dkdv": ("bwd_dkdv_kernel<128, true, false, false, false, false>", None),
 }
 
 
@@ -384,7 +385,7 @@ TRACE_ROWS = [
     ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, "mha"),
     ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, "gqa"),
     ("sliding-window GQA causal prefill S=32768, 4096-key window (kept pairs)", DENSE, 8192, "window"),
-    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false, false>",
+    ("varlen causal prefill, 16 seqs A=16 d=64", "prefill_bf16_kernel<64, true, false, false, false, false, false, false, false>",
      None, "varlen"),
     ("paged decode split, bf16 cache (KV bytes / split time)", ("decode_split_kernel<128, 1, false, 1, 4>", 0), None,
      "decode"),
@@ -397,26 +398,30 @@ TRACE_ROWS = [
      "lowkv1"),
     ("paged decode split, A=32 on A_kv=2 (one-wave workgroups)", "decode_split_kernel<128, 1, false, 1, 1>", None,
      "lowkv2"),
-    ("backward dQ pass", "bwd_dq_kernel<128, false, false, false>", None, None),
-    ("backward dK/dV pass", "bwd_dkdv_kernel<128, true, false, false, false>", None, None),
+    ("backward dQ pass", "bwd_dq_kernel<128, false, false, false, false>", None, None),
+    ("backward dK/dV pass", "bwd_dkdv_kernel<128, true, false, false, false, false>", None, None),
     ("paged chunked prefill, 256-token chunks (causal pairs)",
-     "prefill_bf16_kernel<128, true, true, false, false, false, false, false>", None, "paged"),
-    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false, false, false>", None, None),
-    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false, false>",
+     "prefill_bf16_kernel<128, true, true, false, false, false, false, false, false>", None, "paged"),
+    ("block-sparse causal prefill", "prefill_bf16_kernel<128, false, false, true, false, false, false, false, false>", None, None),
+    ("dense additive mask: documents + block mask", "prefill_bf16_kernel<128, false, false, true, true, false, false, false, false>",
      None, None),
-    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false, false>", None,
+    ("dense additive mask: per-head penalty", "prefill_bf16_kernel<128, false, false, false, true, false, false, false, false>", None,
      None),
     ("block mask of an additive term", "block_keep_kernel", None, None),
     ("key ranges: packed documents, causal prefill",
-     ("prefill_bf16_kernel<128, false, false, false, false, false, false, true>", 0), None, None),
+     ("prefill_bf16_kernel<128, false, false, false, false, false, false, true, false>", 0), None, None),
     ("key ranges: prefix-LM prefill (512-token prefix)",
-     ("prefill_bf16_kernel<128, false, false, false, false, false, false, true>", 1), None, None),
-    ("key ranges: backward dQ pass (documents)", "bwd_dq_kernel<128, false, false, true>", None, None),
-    ("key ranges: backward dK/dV pass (documents)", "bwd_dkdv_kernel<128, true, false, false, true>", None, None),
+     ("prefill_bf16_kernel<128, false, false, false, false, false, false, true, false>", 1), None, None),
+    ("key ranges: backward dQ pass (documents)", "bwd_dq_kernel<128, false, false, true, false>", None, None),
+    ("key ranges: backward dK/dV pass (documents)", "bwd_dkdv_kernel<128, true, false, false, true, false>", None, None),
+    ("ALiBi causal prefill", "prefill_bf16_kernel<128, false, false, false, false, false, false, false, true>",
+     None, "mha"),
+    ("ALiBi backward dQ pass", "bwd_dq_kernel<128, false, false, false, true>", None, None),
+    ("ALiBi backward dK/dV pass", "bwd_dkdv_kernel<128, true, false, false, false, true>", None, None),
     ("FP8-QK causal prefill, MHA shape", FP8_DENSE, 2048, "fp8_mha"),
     ("FP8-QK causal prefill, long GQA shape", FP8_DENSE, 4096, "fp8_gqa"),
     ("paged chunked prefill over the E4M3 cache (causal pairs)",
-     "prefill_bf16_kernel<128, true, true, false, false, false, true, false>", None, "paged"),
+     "prefill_bf16_kernel<128, true, true, false, false, false, true, false, false>", None, "paged"),
 ]
 
 
@@ -660,7 +665,7 @@ def main():
                      "traffic": None if traffic_prefill is None else round(traffic_prefill),
                      "traffic_unit": "bytes per launch (HBM, counter-scaled)", "traffic_source": traffic_src,
                      "algorithmic_bytes": p2.io_bytes() if hasattr(p2, "io_bytes") else None,
-                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
+                     "kernel": "prefill_bf16_kernel<128, false, false, false, false, false, false, false, false>", "avg_launch_ms": round(avg["prefill"], 5),
                      "median_launch_ms": round(med["prefill"], 5), "min_launch_ms": round(mn["prefill"], 5),
                      "measured_ceiling": {"what": "torch.matmul bf16 8192^3 on the same GPU",
                                           "TFLOP/s": ceil["gemm_tflops"],
@@ -703,6 +708,8 @@ def main():
     out["block_sparse"] = bench_block_sparse(w, args.steps, args.warmup)
     out["dense_mask"] = bench_dense_mask(w, args.steps, args.warmup)
     out["key_range"] = bench_key_range(w, args.steps, args.warmup, out["dense_mask"]["avg_ms"])
+    out["alibi"] = bench_alibi(w, args.steps, args.warmup, out["dense_mask"]["per_head_penalty"]["avg_ms"],
+                               out["backward"]["avg_ms"])
     out["decode_fp8"] = bench_decode_fp8(w, args.steps, args.warmup, avg["decode"])
     out["fp8_prefill"] = bench_fp8_prefill(args.steps, args.warmup, stream)
     out["decode_low_kv"] = bench_decode_low_kv(w, args.steps, args.warmup)
@@ -775,7 +782,7 @@ def bench_backward(w, steps: int, warmup: int) -> dict:
             "median_ms": round(float(np.median(ms)), 5), "min_ms": round(float(ms.min()), 5),
             "flops": flops,
             "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 (the prefill workload)",
-            "kernels": "bwd_dq_kernel<128, false, false, false> then bwd_dkdv_kernel<128, true, false, false, false> (K rows in LDS; one call)"}
+            "kernels": "bwd_dq_kernel<128, false, false, false, false> then bwd_dkdv_kernel<128, true, false, false, false, false> (K rows in LDS; one call)"}
 
 
 def window_pairs(S: int, left: int) -> int:
@@ -1218,6 +1225,41 @@ def bench_key_range(w, steps: int, warmup: int, doc_term_ms: float) -> dict:
                           "frac_of_bf16_peak": round(tf_pre / PEAK_BF16_TFLOPS, 4),
                           "avg_ms": round(float(ms_pre.mean()), 5), "kept_pairs": kept_pre,
                           "workload": "the same prefill, prefix-LM with a 512-token prefix (no causal flag)"}}
+
+
+def bench_alibi(w, steps: int, warmup: int, term_ms: float, plain_bwd_ms: float) -> dict:
+    """The MHA causal prefill workload with ALiBi computed in the kernels: the
+    per-head distance penalty of the dense-mask leg (slopes 2^(-8 (h + 1) / A))
+    without its 2.1 GB term, forward and backward; FLOPs = the causal count
+    (every causal pair kept), the backward 2.5x that."""
+    import torch
+    import exact_attention_108_amd as ea
+    from synth import gen
+    p2, stream = w["p2"], w["stream"]
+    q, k, v, o, lse = w["dev2"]
+    B, A, S, d = p2.B, p2.A, p2.S_q, p2.d
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / A) for h in range(A)], dtype=torch.float32, device="cuda")
+    ms = _event_times(lambda: ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, alibi_slopes=slopes,
+                                          stream=stream), steps, warmup, stream)
+    flops = p2.flops()
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    ea.attn_fwd(q, k, v, o, lse, scale=p2.scale, causal=True, alibi_slopes=slopes, stream=stream)
+    do = to_dev(gen.make_dout(p2, 2002), "bf16")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(B, A, S), dtype=torch.uint8, device="cuda")
+    ms_b = _event_times(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p2.scale, causal=True,
+                                            alibi_slopes=slopes, stream=stream), steps, warmup, stream)
+    tf_b = 2.5 * flops / (ms_b.mean() * 1e-3) / 1e12
+    return {"metric": "ALiBi causal prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(float(ms.mean()), 5),
+            "median_ms": round(float(np.median(ms)), 5), "flops": flops,
+            "speedup_over_dense_term": round(term_ms / float(ms.mean()), 2),
+            "workload": "causal MHA B=4 A=32 S=2048 d=128 bf16 with ALiBi, slopes 2^(-8(h+1)/32) (the dense-mask "
+                        "leg's per-head penalty, computed in the kernel)",
+            "backward": {"value": round(tf_b, 2), "unit": "TFLOP/s (2.5x the forward FLOPs)",
+                         "frac_of_bf16_peak": round(tf_b / PEAK_BF16_TFLOPS, 4),
+                         "avg_ms": round(float(ms_b.mean()), 5),
+                         "plain_backward_avg_ms": plain_bwd_ms}}
 
 
 PAGED_CHUNK = 256

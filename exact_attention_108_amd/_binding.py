@@ -26,7 +26,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 class _Mask(ctypes.Structure):
     _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p), ("block_keep", ctypes.c_void_p),
                 ("block_heads", ctypes.c_int), ("bias", ctypes.c_void_p), ("bias_heads", ctypes.c_int),
-                ("bias_ld", ctypes.c_int), ("key_range", ctypes.c_void_p)]
+                ("bias_ld", ctypes.c_int), ("key_range", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p)]
 
 
 class _Window(ctypes.Structure):
@@ -176,18 +176,26 @@ def _bias_view(bias, B, A, S_q, S_k):
     return heads, ld
 
 
-def _mask(q_keep, k_keep, block_keep=None, bias=None, bias_heads=0, bias_ld=0, key_range=None):
+def _mask(q_keep, k_keep, block_keep=None, bias=None, bias_heads=0, bias_ld=0, key_range=None, alibi_slopes=None):
     torch = _torch()
     for t in (q_keep, k_keep, block_keep):
         if t is not None and t.dtype != torch.uint8:
             raise ValueError("keep-masks must be uint8")
     if key_range is not None and key_range.dtype != torch.int32:
         raise ValueError("key_range must be int32 (first, last) pairs")
-    if q_keep is None and k_keep is None and block_keep is None and bias is None and key_range is None:
+    if alibi_slopes is not None and alibi_slopes.dtype != torch.float32:
+        raise ValueError("alibi_slopes must be fp32 [A]")
+    if q_keep is None and k_keep is None and block_keep is None and bias is None and key_range is None and \
+            alibi_slopes is None:
         return None
     heads = 0 if block_keep is None else int(block_keep.shape[1])
     return ctypes.byref(_Mask(_ptr(q_keep), _ptr(k_keep), _ptr(block_keep), heads, _view_ptr(bias), bias_heads,
-                             bias_ld, _ptr(key_range)))
+                             bias_ld, _ptr(key_range), _ptr(alibi_slopes)))
+
+
+def _check_slopes(alibi_slopes, A):
+    if alibi_slopes is not None and tuple(alibi_slopes.shape) != (A,):
+        raise ValueError(f"alibi_slopes must be fp32 [{A}]")
 
 
 def _check_key_range(key_range, shape):
@@ -209,10 +217,11 @@ def _check(status: int, where: str) -> None:
 
 
 def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None, k_keep=None, window=None,
-             block_keep=None, bias=None, key_range=None, stream=None):
+             block_keep=None, bias=None, key_range=None, alibi_slopes=None, stream=None):
     """O, LSE of softmax(Q K^T * scale + M) V.  q/o [B,A,S_q,d], k/v [B,A_kv,S_k,d], lse [B,A,S_q] fp32;
     window = (left, right) sliding window around each query's position, -1 = unbounded side;
     key_range = int32 [B, S_q, 2]: row i keeps keys first..last only (documents, prefix-LM);
+    alibi_slopes = fp32 [A]: ALiBi, -slope_h |p_i - j| joins M;
     block_keep = uint8 [B, 1 or A, ceil(S_q/128), ceil(S_k/128)] block mask (bf16 only);
     bias = the dense additive term M, fp32 [B, 1 or A, S_q, S_k] (finite or -inf; rows unit-stride and
     a multiple of 4 elements apart, see pad_bias)."""
@@ -237,10 +246,11 @@ def attn_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, q_keep=None
         raise ValueError("block_keep must be [B, 1 or A, ceil(S_q/128), ceil(S_k/128)]")
     bh, ld = _bias_view(bias, B, A, S_q, S_k) if bias is not None else (0, 0)
     _check_key_range(key_range, (B, S_q, 2))
-    dev = _dev(q, k, v, o, lse, q_keep, k_keep, block_keep, bias, key_range)
+    _check_slopes(alibi_slopes, A)
+    dev = _dev(q, k, v, o, lse, q_keep, k_keep, block_keep, bias, key_range, alibi_slopes)
     st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, A, A_kv, S_q, S_k, d, float(scale),
-                       int(bool(causal)), _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range), _window(window),
-                       _dtype_code(q), _stream(stream, dev))
+                       int(bool(causal)), _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range, alibi_slopes),
+                       _window(window), _dtype_code(q), _stream(stream, dev))
     _check(st, "attn_fwd")
 
 
@@ -306,7 +316,8 @@ def attn_block_keep_from_bias(bias, block_keep, *, stream=None):
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: float, causal: bool = True,
-                    q_keep=None, k_keep=None, window=None, block_keep=None, bias=None, key_range=None, stream=None):
+                    q_keep=None, k_keep=None, window=None, block_keep=None, bias=None, key_range=None,
+                    alibi_slopes=None, stream=None):
     """Packed varlen prefill.  q/o [A,T,d], k/v [A_kv,T,d], lse [A,T]; cu_seqlens int32 device,
     cu_seqlens_host the same values on the host (numpy int32).  bf16 only: block_keep uint8
     [n_seq, 1 or A, nb, nb] (nb = ceil(longest length / 128)), each sequence's own 128 x 128 blocks;
@@ -331,11 +342,12 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens_host, *, scale: floa
             raise ValueError("keep-masks must be [T]")
     bh, ld = _packed_masks(block_keep, bias, cu_host, A, T)
     _check_key_range(key_range, (T, 2))
-    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep, block_keep, bias, key_range)
+    _check_slopes(alibi_slopes, A)
+    dev = _dev(q, k, v, o, lse, cu_seqlens, q_keep, k_keep, block_keep, bias, key_range, alibi_slopes)
     st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                               cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d, float(scale), int(bool(causal)),
-                              _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range), _window(window),
-                              _dtype_code(q), _stream(stream, dev))
+                              _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range, alibi_slopes),
+                              _window(window), _dtype_code(q), _stream(stream, dev))
     _check(st, "attn_fwd_varlen")
 
 
@@ -454,7 +466,7 @@ def attn_bwd_workspace_bytes(B: int, A: int, S_q: int) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, causal: bool = False, q_keep=None,
-             k_keep=None, window=None, block_keep=None, bias=None, key_range=None, stream=None):
+             k_keep=None, window=None, block_keep=None, bias=None, key_range=None, alibi_slopes=None, stream=None):
     """dQ, dK, dV of attn_fwd.  q/o/dout/dq [B,A,S_q,d], k/v/dk/dv [B,A_kv,S_k,d], lse [B,A,S_q] fp32 (the
     forward's); workspace a uint8 device tensor of at least attn_bwd_workspace_bytes(B, A, S_q) bytes; masks as
     given to attn_fwd."""
@@ -485,18 +497,19 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float, caus
         raise ValueError("block_keep must be [B, 1 or A, ceil(S_q/128), ceil(S_k/128)]")
     bh, ld = _bias_view(bias, B, A, S_q, S_k) if bias is not None else (0, 0)
     _check_key_range(key_range, (B, S_q, 2))
+    _check_slopes(alibi_slopes, A)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, workspace, q_keep, k_keep, block_keep, bias, key_range)
+    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, workspace, q_keep, k_keep, block_keep, bias, key_range, alibi_slopes)
     st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                        B, A, A_kv, S_q, S_k, d, float(scale), int(bool(causal)),
-                       _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range), _window(window), _dtype_code(q),
-                       _ptr(workspace), ws_bytes, _stream(stream, dev))
+                       _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range, alibi_slopes), _window(window),
+                       _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_bwd")
 
 
 def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, cu_seqlens_host, workspace, *, scale: float,
                     causal: bool = True, q_keep=None, k_keep=None, window=None, block_keep=None, bias=None,
-                    key_range=None, stream=None):
+                    key_range=None, alibi_slopes=None, stream=None):
     """dQ, dK, dV of attn_fwd_varlen.  q/o/dout/dq [A,T,d], k/v/dk/dv [A_kv,T,d], lse [A,T] fp32 (the
     forward's); cu_seqlens int32 device with cu_seqlens_host (numpy); workspace a uint8 device tensor of at
     least attn_bwd_workspace_bytes(1, A, T) bytes; block_keep, bias and key_range as attn_fwd_varlen takes
@@ -525,12 +538,14 @@ def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, cu_seqlens_ho
             raise ValueError("keep-masks must be [T]")
     bh, ld = _packed_masks(block_keep, bias, cu_host, A, T)
     _check_key_range(key_range, (T, 2))
+    _check_slopes(alibi_slopes, A)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace, q_keep, k_keep, block_keep, bias, key_range)
+    dev = _dev(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, workspace, q_keep, k_keep, block_keep, bias, key_range,
+               alibi_slopes)
     st = _lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                               _ptr(dv), _ptr(cu_seqlens), cu_host.ctypes.data_as(_vp), n_seq, T, A, A_kv, d,
                               float(scale), int(bool(causal)),
-                              _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range),
+                              _mask(q_keep, k_keep, block_keep, bias, bh, ld, key_range, alibi_slopes),
                               _window(window),
                               _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, "attn_bwd_varlen")
@@ -547,18 +562,18 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host
 
 def attn_prefill_paged_masked(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q,
                               cu_seqlens_q_host, o, lse, *, scale: float, causal: bool = True, window=None,
-                              block_keep=None, bias=None, key_range=None, stream=None):
+                              block_keep=None, bias=None, key_range=None, alibi_slopes=None, stream=None):
     """attn_prefill_paged with block_keep uint8 [n_seq, 1 or A, ceil(longest chunk/128), ceil(longest
     seq_len/128)] over (chunk rows, key positions) and bias fp32 [1 or A, T_q, L] (L = the longest
     seq_len; row t = chunk token t against the key positions of its sequence; rows unit-stride and a
     multiple of 4 elements apart); key_range int32 [T_q, 2], chunk token t's (first, last) key positions
-    in its sequence's cache."""
+    in its sequence's cache; alibi_slopes fp32 [A] (chunk rows at the bottom of their sequence)."""
     _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host, o, lse,
-                scale, causal, window, stream, block_keep, bias, key_range)
+                scale, causal, window, stream, block_keep, bias, key_range, alibi_slopes)
 
 
 def _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_seqlens_q, cu_seqlens_q_host, o, lse,
-                scale, causal, window, stream, block_keep, bias, key_range=None):
+                scale, causal, window, stream, block_keep, bias, key_range=None, alibi_slopes=None):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q [A,T_q,d]; caches [num_pages, page_size, A_kv, d]")
@@ -578,11 +593,13 @@ def _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_se
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != n_seq:
         raise ValueError("block_table must be int32 [n_seq, max_pages]")
     _check_key_range(key_range, (T_q, 2))
-    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse, block_keep, bias, key_range)
+    _check_slopes(alibi_slopes, A)
+    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, o, lse, block_keep, bias, key_range,
+               alibi_slopes)
     head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp),
             _ptr(cu_seqlens_q), cu_host.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), n_seq, T_q, A, A_kv, d,
             block_table.shape[1], num_pages, float(scale), int(bool(causal)))
-    if block_keep is None and bias is None and key_range is None:
+    if block_keep is None and bias is None and key_range is None and alibi_slopes is None:
         st = _lib.attn_prefill_paged(*head, _window(window), _dtype_code(q), _stream(stream, dev))
         _check(st, "attn_prefill_paged")
         return
@@ -600,7 +617,8 @@ def _paged_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, cu_se
         bh, ld = int(bias.shape[0]), int(bias.stride(1))
         if (max_l > 1 and bias.stride(2) != 1) or ld % 4 or ld < max_l or (bh > 1 and bias.stride(0) != T_q * ld):
             raise ValueError("bias rows must be unit-stride, a multiple of 4 elements apart, heads packed")
-    st = _lib.attn_prefill_paged_masked(*head, _mask(None, None, block_keep, bias, bh, ld, key_range), _window(window),
+    st = _lib.attn_prefill_paged_masked(*head, _mask(None, None, block_keep, bias, bh, ld, key_range, alibi_slopes),
+                                        _window(window),
                                         _dtype_code(q), _stream(stream, dev))
     _check(st, "attn_prefill_paged_masked")
 

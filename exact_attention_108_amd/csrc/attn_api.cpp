@@ -37,8 +37,15 @@ bool window_arith_fits(const attn_window* w, long long rows, long long keys) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// per-row key ranges are read as int32 pairs (8-byte loads)
-bool key_range_aligned(const attn_mask* m) { return m == nullptr || aligned(m->key_range, 8); }
+// per-row key ranges are read as int32 pairs (8-byte loads), ALiBi slopes as floats
+bool key_range_aligned(const attn_mask* m) {
+  return m == nullptr || (aligned(m->key_range, 8) && aligned(m->alibi_slopes, 4));
+}
+// the bf16 kernels' ALiBi forms take keep masks and windows beside it, no
+// other mask form
+bool alibi_alone(const attn_mask* m) {
+  return m == nullptr || m->alibi_slopes == nullptr || (!m->block_keep && !m->bias && !m->key_range);
+}
 
 // Longest sequence (rows or keys) any call takes: the kernels count positions
 // in int32 and round up to a tile or chunk past a length.
@@ -60,6 +67,7 @@ attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   p.q_keep = mask ? mask->q_keep : nullptr;
   p.k_keep = mask ? mask->k_keep : nullptr;
   p.key_range = mask ? mask->key_range : nullptr;
+  p.alibi_slopes = mask ? mask->alibi_slopes : nullptr;
   p.A = A;
   p.A_kv = A_kv;
   p.G = A / A_kv;
@@ -67,6 +75,7 @@ attn::FwdParams base_params(const void* q, const void* k, const void* v, void* o
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.inv_scale = (float)(1.0 / (double)scale);
   window_edges(window, causal, key_extent, row_extent, p.win_left, p.win_right);
   return p;
 }
@@ -117,6 +126,7 @@ ATTN_EXPORT attn_status attn_fwd(const void* q, const void* k, const void* v, vo
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
   if (bias && dtype == ATTN_BF16 && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   if (bias && mask->key_range && dtype == ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_BF16 && !alibi_alone(mask)) return ATTN_ERR_UNSUPPORTED;
   // the kernels count rows and key positions in int32, up to a tile past a length
   if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (S_q == 0) return ATTN_OK;
@@ -162,7 +172,7 @@ ATTN_EXPORT attn_status attn_fwd_fp8(const uint8_t* q, const uint8_t* k, const v
     if (!aligned(t, 4)) return ATTN_ERR_INVAL;
   if (!key_range_aligned(mask)) return ATTN_ERR_INVAL;
   if (d_h != 128) return ATTN_ERR_UNSUPPORTED;
-  if (mask && (mask->block_keep || mask->bias)) return ATTN_ERR_UNSUPPORTED;
+  if (mask && (mask->block_keep || mask->bias || mask->alibi_slopes)) return ATTN_ERR_UNSUPPORTED;
   if (S_k > attn::kFp8MaxKeys) return ATTN_ERR_UNSUPPORTED;
   if (!window_arith_fits(window, S_q, S_k)) return ATTN_ERR_UNSUPPORTED;
   if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
@@ -224,6 +234,7 @@ ATTN_EXPORT attn_status attn_fwd_varlen(const void* q, const void* k, const void
   if (blocks && max_len > 262144) return ATTN_ERR_UNSUPPORTED;
   if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_BF16 && !alibi_alone(mask)) return ATTN_ERR_UNSUPPORTED;
   if (max_len > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;
   if ((long long)A * total_tokens > INT_MAX) return ATTN_ERR_UNSUPPORTED;
@@ -448,6 +459,8 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   if (blocks && max_kv_len > 262144) return ATTN_ERR_UNSUPPORTED;
   if (bias && !bias_rows_fit(mask->bias_ld)) return ATTN_ERR_UNSUPPORTED;
   if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;
+  if (!alibi_alone(mask)) return ATTN_ERR_UNSUPPORTED;
+  if (fp8 && mask && mask->alibi_slopes) return ATTN_ERR_UNSUPPORTED;
   const int rows_per_part = 2048 / d_h;  // tokens one copy round of a workgroup moves
   if ((page_size & (page_size - 1)) != 0 || page_size % rows_per_part != 0) return ATTN_ERR_UNSUPPORTED;
   if (total_q == 0) return ATTN_OK;
@@ -480,6 +493,7 @@ attn_status prefill_paged_call(const void* q, const void* k_cache, const void* v
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   p.key_range = mask ? mask->key_range : nullptr;
+  p.alibi_slopes = mask ? mask->alibi_slopes : nullptr;
   if (blocks) {
     p.block_keep = mask->block_keep;
     p.block_heads = mask->block_heads;
@@ -575,6 +589,7 @@ attn::BwdParams bwd_params(const void* q, const void* k, const void* v, const vo
   p.q_keep = mask ? mask->q_keep : nullptr;
   p.k_keep = mask ? mask->k_keep : nullptr;
   p.key_range = mask ? mask->key_range : nullptr;
+  p.alibi_slopes = mask ? mask->alibi_slopes : nullptr;
   p.A = A;
   p.A_kv = A_kv;
   p.G = A / A_kv;
@@ -582,6 +597,7 @@ attn::BwdParams bwd_params(const void* q, const void* k, const void* v, const vo
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.inv_scale = (float)(1.0 / (double)scale);
   return p;
 }
 
@@ -606,6 +622,7 @@ ATTN_EXPORT attn_status attn_bwd(const void* q, const void* k, const void* v, co
   if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, S_q, S_k, mask->bias_ld)) return ATTN_ERR_INVAL;
   if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;  // as the forward
+  if (!alibi_alone(mask)) return ATTN_ERR_UNSUPPORTED;
   if (S_q > kMaxLen || S_k > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   const long long n_qb = (S_q + 127) / 128, n_kb = (S_k + 127) / 128;
   if (blocks && (n_kb > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * n_qb > attn::kBwdMaxRowBlocks))
@@ -673,6 +690,7 @@ ATTN_EXPORT attn_status attn_bwd_varlen(const void* q, const void* k, const void
   if (blocks && mask->block_heads != 1 && mask->block_heads != A) return ATTN_ERR_INVAL;
   if (bias && !valid_bias(mask->bias, mask->bias_heads, A, max_len, max_len, mask->bias_ld)) return ATTN_ERR_INVAL;
   if (bias && mask->key_range) return ATTN_ERR_UNSUPPORTED;  // as the forward
+  if (!alibi_alone(mask)) return ATTN_ERR_UNSUPPORTED;
   if (blocks && (max_tiles > attn::kBwdMaxKeyBlocks || (long long)(A / A_kv) * max_tiles > attn::kBwdMaxRowBlocks))
     return ATTN_ERR_UNSUPPORTED;
   if (total_tokens == 0) return ATTN_OK;

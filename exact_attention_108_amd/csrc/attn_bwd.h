@@ -51,6 +51,8 @@ struct BwdParams {
   // key_range[2 i + 1]; dense [B, S_q, 2], packed [T, 2] (positions within
   // the sequence); or null
   const int32_t* key_range;
+  // ALiBi: slope per query head [A] (the forward's); uses inv_scale; or null
+  const float* alibi_slopes;
 };
 // Block-mask limits of the backward: the dQ pass keeps one flag per 128-key
 // block of its row block in LDS, the dK/dV pass one per (query head of the

@@ -144,7 +144,7 @@ using Slot = std::integral_constant<int, N>;
 template <int D, bool kMasks>
 constexpr int kDqWavesPerSimd = (D == 128 && kMasks) ? 1 : 2;
 
-template <int D, bool kVarlen, bool kMasks, bool kRange = false>
+template <int D, bool kVarlen, bool kMasks, bool kRange = false, bool kAlibi = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D, kMasks>, kDqWavesPerSimd<D, kMasks>))) void bwd_dq_kernel(BwdParams p,
                                                                                                     int n_qt) {
   constexpr int KSTEPS = D / 16;
@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   __shared__ uint8_t sBlk[kMasks ? kBwdMaxKeyBlocks : 1];
   // per-row key ranges: the key bounds of each wave's rows
   static_assert(!(kMasks && kRange), "the masked form takes key ranges at run time");
+  static_assert(!kAlibi || (!kMasks && !kRange), "ALiBi: no other term or range");
   // key ranges: compiled in (kRange), or optional at run time (kMasks)
   constexpr bool kRng = kMasks || kRange;
   __shared__ KeyBounds sKb[kRng ? 4 : 1];
@@ -270,6 +271,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const float cs = p.scale_log2;
+  [[maybe_unused]] float alibi_b = 0.f;  // ALiBi: this head's slope over the scale
+  if constexpr (kAlibi) alibi_b = p.alibi_slopes[h] * p.inv_scale;
   const uint16_t* kbase = (const uint16_t*)p.k + k_row0 * D;
   const uint16_t* vbase = (const uint16_t*)p.v + k_row0 * D;
   const uint8_t* kkeep = p.k_keep ? p.k_keep + (kVarlen ? tok0 : (size_t)b * S_k) : nullptr;
@@ -337,6 +340,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = (j_lo + j) * kKeyTile;
     f32x16 s = f32x16{}, dp = f32x16{};
+    if constexpr (kAlibi) {
+      // the forward's ALiBi term as the accumulators' initial value: element
+      // r is key k0 + 32 kb + 8 (r / 4) + 4 g + r % 4 of this lane's row
+      const float x0 = (float)(k0 + 32 * kb + 4 * g - (qrow + off));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = -fabsf(x0 + (float)(8 * (r >> 2) + (r & 3))) * alibi_b;
+    }
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
       const bf16x8 ka = *(const bf16x8*)(lds + kb * 32 * D * 2 + koff[t]);
@@ -443,10 +453,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
 template <int D, bool KLDS, bool kRange>
 constexpr int kDkdvWavesPerSimd = ((D == 64 && !kRange) || KLDS) ? 2 : 1;
 
-template <int D, bool KLDS, bool kVarlen, bool kMasks, bool kRange = false>
+template <int D, bool KLDS, bool kVarlen, bool kMasks, bool kRange = false, bool kAlibi = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerSimd<D, KLDS, kRange>, kDkdvWavesPerSimd<D, KLDS, kRange>))) void bwd_dkdv_kernel(BwdParams p,
                                                                                                       int n_kt) {
   static_assert(!(KLDS && kMasks), "the K-in-LDS form takes no block mask or term");
+  static_assert(!kAlibi || (!kMasks && !kRange), "ALiBi: no other term or range");
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int BLOCK_BYTES = kQBlock * D * 2;
@@ -625,9 +636,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
   // S and dP of the block in `lds` for this wave's 32 keys
   // (K tile in LDS: this wave's rows 32 wave + l32 have the swizzle of rows l32)
   const char* lds_k = (const char*)smem + NSLOT * SLOT_BYTES + wave * 32 * D * 2;
-  auto scores = [&](const char* lds, f32x16& s, f32x16& dp) {
+  auto scores = [&](const char* lds, int idx, f32x16& s, f32x16& dp) {
     s = f32x16{};
     dp = f32x16{};
+    if constexpr (kAlibi) {
+      // the forward's ALiBi term (the slope of the block's query head) as the
+      // accumulators' initial value: element r is row r0 + 8 (r / 4) + 4 g +
+      // r % 4 against this lane's key
+      const int gh = idx / nq, r0 = (qb_first + idx % nq) * kQBlock;
+      const float ab = p.alibi_slopes[hk * p.G + gh] * p.inv_scale;
+      const float x0 = (float)(key - off - r0 - 4 * g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = -fabsf(x0 - (float)(8 * (r >> 2) + (r & 3))) * ab;
+    }
+    (void)idx;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
       const bf16x8 qa = *(const bf16x8*)(lds + koff[t]);
@@ -749,17 +771,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
       // a block the block mask drops contributes nothing: its scores are not
       // needed and its gradient is not formed
       const bool keep_cur = block_kept(idx), keep_nxt = idx + 1 < n_blocks && block_kept(idx + 1);
-      if (keep_nxt) scores(ln, nxt.s, nxt.dp);
+      if (keep_nxt) scores(ln, idx + 1, nxt.s, nxt.dp);
       if (keep_cur) grad(lc, idx, cur.s, cur.dp, std::true_type{});
       return;
     }
     if (block_masked(idx)) {
       interleave_hint();
-      scores(ln, nxt.s, nxt.dp);
+      scores(ln, idx + 1, nxt.s, nxt.dp);
       grad(lc, idx, cur.s, cur.dp, std::true_type{});
     } else {
       interleave_hint();
-      scores(ln, nxt.s, nxt.dp);
+      scores(ln, idx + 1, nxt.s, nxt.dp);
       grad(lc, idx, cur.s, cur.dp, std::false_type{});
     }
   };
@@ -778,11 +800,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
       SD cur;
       if (block_masked(idx)) {
         interleave_hint();
-        scores(lc, cur.s, cur.dp);
+        scores(lc, idx, cur.s, cur.dp);
         grad(lc, idx, cur.s, cur.dp, std::true_type{});
       } else {
         interleave_hint();
-        scores(lc, cur.s, cur.dp);
+        scores(lc, idx, cur.s, cur.dp);
         grad(lc, idx, cur.s, cur.dp, std::false_type{});
       }
     };
@@ -808,7 +830,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDkdvW
       else
         lds_copy_wait_all();
       __syncthreads();
-      if (block_kept(0)) scores((const char*)smem, ra.s, ra.dp);
+      if (block_kept(0)) scores((const char*)smem, 0, ra.s, ra.dp);
     }
     int idx = 0;
     for (; idx + 4 <= n_blocks; idx += 4) {
@@ -862,7 +884,7 @@ void plan_order(int units, int group_max, int& per, int& group) {
   group = g;
 }
 
-template <int D, bool kVarlen, bool kMasks, bool kRange>
+template <int D, bool kVarlen, bool kMasks, bool kRange, bool kAlibi = false>
 hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
   BwdParams p = p_in;
   int n_qt, n_units_q, n_units_kv;
@@ -881,7 +903,7 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
   const int n_kt = kVarlen ? p.total_tiles : (p.S_k + kBwdKRows - 1) / kBwdKRows;
   // the dQ pass writes the row statistics the dK/dV pass reads: same stream, in order
   if (n_qt > 0 && (kVarlen || p.S_q > 0)) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kVarlen, kMasks, kRange && !kMasks>), dim3(n_qt * n_units_q),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kVarlen, kMasks, kRange && !kMasks, kAlibi>), dim3(n_qt * n_units_q),
                        dim3(kThreads), 0, stream, p, n_qt);
   }
   if (n_kt > 0 && (kVarlen || p.S_k > 0)) {
@@ -899,13 +921,13 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
     if constexpr (D == 128 && !kMasks && !kVarlen) two_wave = n_wg >= kKlDsMinWorkgroups;
     if constexpr (D == 128 && !kMasks && !kVarlen) {
       if (two_wave) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, kVarlen, false, kRange>), dim3(n_wg), dim3(kThreads), 0,
-                           stream, p, n_kt);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, kVarlen, false, kRange, kAlibi>), dim3(n_wg), dim3(kThreads),
+                           0, stream, p, n_kt);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, kMasks, kRange>), dim3(n_wg), dim3(kThreads), 0, stream, p,
-                       n_kt);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kVarlen, kMasks, kRange, kAlibi>), dim3(n_wg), dim3(kThreads), 0,
+                       stream, p, n_kt);
     (void)two_wave;
   }
   return hipGetLastError();
@@ -913,8 +935,13 @@ hipError_t launch_bwd_v(const BwdParams& p_in, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  // (key ranges with a term are rejected before the launch)
+  // (key ranges with a term, and ALiBi with any mask form but keep masks and
+  // windows, are rejected before the launch)
   const bool masks = p.block_keep || p.bias, rng = p.key_range != nullptr;
+  if (p.alibi_slopes) {
+    if (p.cu_seqlens) return launch_bwd_v<D, true, false, false, true>(p, stream);
+    return launch_bwd_v<D, false, false, false, true>(p, stream);
+  }
   if (p.cu_seqlens) {
     if (masks && rng) return launch_bwd_v<D, true, true, true>(p, stream);
     if (masks) return launch_bwd_v<D, true, true, false>(p, stream);

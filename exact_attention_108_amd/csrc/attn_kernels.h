@@ -61,6 +61,9 @@ struct FwdParams {
   // key_range[2 i + 1]; dense [B, S_q, 2], packed [T, 2] (positions within
   // the sequence), paged [T_q, 2] (positions in the sequence's cache); or null
   const int32_t* key_range;
+  // ALiBi: slope per query head [A]; the term -slope_h |p_i - j| joins the
+  // score (p_i: row i's bottom-right aligned position); or null.  Uses inv_scale.
+  const float* alibi_slopes;
 };
 
 // Dense prefill grid order.  Workgroups are dealt to the 8 XCDs round-robin

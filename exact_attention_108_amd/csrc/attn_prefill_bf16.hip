@@ -49,7 +49,9 @@
 //   kBias    a dense additive term M on every score (loaded a tile ahead as
 //            the initial value of the score accumulators);
 //   kRange   per-row key ranges (kept apart so that the other forms keep
-//            their register allocation; not combined with kBias).
+//            their register allocation; not combined with kBias);
+//   kAlibi   ALiBi, the per-head distance penalty computed in the kernel (no
+//            block mask, term or key ranges beside it).
 // Sliding windows, per-row key ranges, keep masks and the causal flag are
 // runtime arguments of every instantiation.
 #include <type_traits>
@@ -75,8 +77,8 @@ constexpr int kMaxListedTiles = 4096;
 // needs, with three workgroups' 32 KB of tiles in LDS (measured +9% on a
 // causal S = 2048 batch, +16% on ragged varlen batches).  The paged,
 // dense-additive-mask and key-range variants stay at two: at three they spill.
-template <int D, bool kPaged, bool kBias, bool kRange>
-constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias && !kRange) ? 3 : 2;
+template <int D, bool kPaged, bool kBias, bool kRange, bool kAlibi>
+constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias && !kRange && !kAlibi) ? 3 : 2;
 
 // kFp8: queries and keys are OCP E4M3 codes with one fp32 scale per 128
 // tokens (FwdParams::q_scale / k_scale); S^T = K . Q^T runs on the FP8 matrix
@@ -89,11 +91,12 @@ constexpr int kWavesPerSimd = (D == 64 && !kPaged && !kBias && !kRange) ? 3 : 2;
 // value's scale its probabilities before the PV product (the normaliser sums
 // the unscaled ones).
 template <int D, bool kVarlen, bool kPaged = false, bool kBlocks = false, bool kBias = false, bool kFp8 = false,
-          bool kCache8 = false, bool kRange = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias, kRange>, kWavesPerSimd<D, kPaged, kBias, kRange>))) void prefill_bf16_kernel(FwdParams p) {
+          bool kCache8 = false, bool kRange = false, bool kAlibi = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, kPaged, kBias, kRange, kAlibi>, kWavesPerSimd<D, kPaged, kBias, kRange, kAlibi>))) void prefill_bf16_kernel(FwdParams p) {
   static_assert(!kFp8 || (D == 128 && !kVarlen && !kPaged && !kBlocks && !kBias), "fp8: dense, d = 128");
   static_assert(!kCache8 || kPaged, "E4M3 caches: paged prefill only");
   static_assert(!kRange || (!kBias && !kCache8), "key ranges: not with a dense additive term or an E4M3 cache");
+  static_assert(!kAlibi || (!kBias && !kBlocks && !kRange && !kFp8 && !kCache8), "ALiBi: bf16 values, no other term");
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // k-steps of the QK^T MFMA
   constexpr int MB = D / 32;               // 32-row blocks of O^T
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // (with an additive term, s arrives holding M / scale of the tile's scores)
   auto qk = [&](auto kbuf_tag, f32x16 (&s)[2], auto&& issue) {
     constexpr int KB = decltype(kbuf_tag)::value * KTILE_BYTES;
-    if constexpr (!kBias) {
+    if constexpr (!kBias && !kAlibi) {  // (with a term, the accumulators start from it)
       s[0] = f32x16{};
       s[1] = f32x16{};
     }
@@ -577,7 +580,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       }
     }
   };
-  auto term_init = [&](f32x16 (&s)[2], const f32x4 (&m)[2][4]) {
+  // ALiBi (page "Attention Kernel", section "正确性契约": a per-head linear
+  // penalty on the query-key distance, fused into the score): the term
+  // -slope_h |p - j| (p = qrow + off, this lane's position) enters the raw
+  // product divided by the scale, as the initial value of the accumulators;
+  // key j - p is formed exactly in fp32 (one add per score), the magnitude,
+  // sign and slope in one multiply
+  [[maybe_unused]] float alibi_b = 0.f;
+  if constexpr (kAlibi) alibi_b = p.alibi_slopes[rb.h] * p.inv_scale;
+  auto term_init = [&](f32x16 (&s)[2], const f32x4 (&m)[2][4], int t) {
     if constexpr (kBias) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -585,6 +596,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         for (int r = 0; r < 16; ++r) s[kb][r] = m[kb][r >> 2][r & 3] * p.inv_scale;
       }
     }
+    if constexpr (kAlibi) {
+      const float x0 = (float)(phys(t) * kBc + 4 * g - (qrow + off));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = x0 + (float)(32 * kb + 8 * (r >> 2) + (r & 3));
+          s[kb][r] = -fabsf(x) * alibi_b;
+        }
+      }
+    }
+    (void)t;
   };
   auto mask = [&](f32x16 (&s)[2], int t) {
     const int k0 = phys(t) * kBc;
@@ -759,7 +782,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     bias_load(min(1, n_tiles - 1), m_nx);
     lds_copy_wait_all();
     __syncthreads();
-    term_init(s_cur, m0);
+    term_init(s_cur, m0, 0);
     qk(std::integral_constant<int, 0>{}, s_cur, [](int) {});
     kscale(s_cur, 0);
     if (n_mid == 0) mask(s_cur, 0);
@@ -849,7 +872,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     f32x16 s_next[2];
     interleave_hint();
     if constexpr (!MASKED) {
-      term_init(s_next, m_nx);
+      term_init(s_next, m_nx, j + 1);
       qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
       kscale(s_next, BUF ^ 1);
       bias_load(min(j + 2, n_tiles - 1), m_nx);  // in flight until the next iteration's copy wait
@@ -863,7 +886,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       // takes part in the copies and barriers)
       const bool has_next = j + 1 < n_tiles && wave_sees(j + 1);
       if (has_next) {
-        term_init(s_next, m_nx);
+        term_init(s_next, m_nx, j + 1);
         qk(std::integral_constant<int, BUF ^ 1>{}, s_next, issue);
         kscale(s_next, BUF ^ 1);
       } else {
@@ -972,6 +995,17 @@ hipError_t launch_d(const FwdParams& p, bool varlen, hipStream_t stream) {
     grid = p.n_qt * p.A * p.B;
   }
   if (grid <= 0) return hipSuccess;
+  if (p.alibi_slopes) {
+    // (block masks, terms and key ranges with ALiBi are rejected before the launch)
+    if (varlen) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false, false, false, false, false, true>), dim3(grid),
+                         dim3(kThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, false, false, false, false, true>), dim3(grid),
+                         dim3(kThreads), 0, stream, p);
+    }
+    return hipGetLastError();
+  }
   if (p.key_range) {
     // (a dense additive term with key ranges is rejected before the launch)
     if (varlen && p.block_keep) {
@@ -1033,7 +1067,10 @@ hipError_t launch_prefill_fp8(const FwdParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_paged_d(const FwdParams& p, int grid, hipStream_t stream) {
-  if (p.key_range && p.block_keep) {
+  if (p.alibi_slopes) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, false, false, false, false, true>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
+  } else if (p.key_range && p.block_keep) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true, false, false, false, true>), dim3(grid),
                        dim3(kThreads), 0, stream, p);
   } else if (p.key_range) {

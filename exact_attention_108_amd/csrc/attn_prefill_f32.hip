@@ -10,7 +10,8 @@
 // A dense additive mask M (dense batches) enters each score as M / scale
 // before the scaling, i.e. s * scale + M.  Per-row key ranges (page
 // "Attention Kernel", section "可编程 mask") mask the keys outside each row's
-// range.
+// range.  ALiBi adds -slope_h |p_i - j| the same way (as -slope_h |p_i - j| /
+// scale to the raw product).
 //
 // A workgroup owns 16 query rows; wave w owns rows 4w..4w+3.  In the score
 // step lane j computes the scores of key j of the tile for the wave's 4 rows;
@@ -85,6 +86,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
     }
   }
 
+  // ALiBi: this head's slope over the scale (0 without ALiBi)
+  const float alibi_b = p.alibi_slopes ? p.alibi_slopes[rb.h] * p.inv_scale : 0.f;
   // this wave's rows keep keys [r_lo, r_hi] under their key ranges
   int r_lo[kRowsPerWave], r_hi[kRowsPerWave];
 #pragma unroll
@@ -129,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(FwdParams p) {
       float s = 0.f;
       for (int e = 0; e < D; ++e) s = fmaf(sQ[qr][e], sK[lane][e], s);
       if (bias_rows && key < S_k && row < S_q) s = fmaf(bias_rows[(size_t)row * p.bias_ld + key], p.inv_scale, s);
+      s = fmaf(-fabsf((float)(key - (row + off))), alibi_b, s);
       const bool dead = sKeep[lane] == 0 || (wr >= 0 && key > row + off + wr) || (wl >= 0 && key < row + off - wl) ||
                         key < r_lo[rr] || key > r_hi[rr];
       s = dead ? -INFINITY : s;

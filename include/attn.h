@@ -29,8 +29,8 @@
  *   - Lengths: a sequence (S_q, S_k, a packed sequence, a chunk or a cached
  *     length) of more than 2^31 - 1025 positions is ATTN_ERR_UNSUPPORTED
  *     (the kernels count positions in int32, up to a tile past a length).
- *   - Mask: M_ij is the optional dense additive term bias[i][j] (see
- *     attn_mask) plus -inf when: causal and j > i + (S_k - S_q)
+ *   - Mask: M_ij is the optional dense additive term bias[i][j] and the
+ *     optional ALiBi term (see attn_mask) plus -inf when: causal and j > i + (S_k - S_q)
  *     (bottom-right alignment), q_keep[i] == 0, k_keep[j] == 0, a window,
  *     a key range or a block mask excludes (i, j).  A row with every key masked (including
  *     S_k == 0) returns O = 0 and LSE = -inf (page "Attention Kernel",
@@ -56,7 +56,7 @@
 #include <stdint.h>
 
 /* The value attn_abi_version() returns for this header. */
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 #ifdef __cplusplus
 extern "C" {
@@ -134,7 +134,18 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * tiles between the smallest first and the largest last of a 128-row tile
  * and applies no per-element test to tiles inside every row's range; the
  * dK/dV pass of the gradient visits only the query rows whose ranges reach
- * its keys. */
+ * its keys.
+ *
+ * alibi_slopes: ALiBi (page "Attention Kernel", section "正确性契约" names it
+ * among the transforms fused into the score).  fp32 [A], one slope per query
+ * head; the term -alibi_slopes[h] * |p_i - j| joins M (it is added to
+ * scale * q_i . k_j, like bias), with p_i query i's bottom-right aligned
+ * position (i + S_k - S_q; packed calls: within the sequence; paged chunks:
+ * seq_lens[s] - q_len + i over cache positions j).  Computed in the kernels
+ * (no term is read).  attn_fwd, attn_fwd_varlen, attn_prefill_paged_masked,
+ * attn_bwd and attn_bwd_varlen take it; in bf16 calls it combines with the
+ * causal flag, windows and keep-masks but not with block masks, bias or
+ * key_range (ATTN_ERR_UNSUPPORTED), nor with attn_fwd_fp8.  4-byte aligned. */
 typedef struct {
     const uint8_t *q_keep;
     const uint8_t *k_keep;
@@ -144,6 +155,7 @@ typedef struct {
     int bias_heads;
     int bias_ld;
     const int32_t *key_range;
+    const float *alibi_slopes;
 } attn_mask;
 
 /* Optional sliding window (page "Attention Kernel", section "可编程 mask":

@@ -42,7 +42,7 @@ def test_library_exports_exactly_the_header():
 
 def test_status_strings_and_version():
     import exact_attention_108_amd as ea
-    assert ea.attn_abi_version() == 6
+    assert ea.attn_abi_version() == 7
     assert ea.attn_status_string(0) == "ok"
     assert ea.attn_status_string(1) == "invalid argument"
     assert ea.attn_status_string(2) == "unsupported configuration"
@@ -85,7 +85,7 @@ class Mask(ctypes.Structure):
     """attn_mask of include/attn.h."""
     _fields_ = [("q_keep", ctypes.c_void_p), ("k_keep", ctypes.c_void_p), ("block_keep", ctypes.c_void_p),
                 ("block_heads", ctypes.c_int), ("bias", ctypes.c_void_p), ("bias_heads", ctypes.c_int),
-                ("bias_ld", ctypes.c_int), ("key_range", ctypes.c_void_p)]
+                ("bias_ld", ctypes.c_int), ("key_range", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p)]
 
 
 P = ctypes.c_void_p(4096)  # never dereferenced: every call below is rejected (or empty) on the host
@@ -379,6 +379,26 @@ def test_key_range_arguments():
                                rng(4096 + 4), None, 1, None) == INVAL
     import exact_attention_108_amd._binding as b
     assert [f[0] for f in b._Mask._fields_] == [f[0] for f in Mask._fields_]
+
+
+def test_alibi_arguments():
+    """ALiBi slopes: 4-byte aligned; in bf16 calls not with a block mask, a
+    term or key ranges; never with the FP8 forward."""
+    lib = _lib()
+    INVAL, UNSUP, OK = 1, 2, 0
+    mk = lambda *a: ctypes.byref(Mask(*a))
+    al = lambda addr, **kw: mk(kw.get("q"), None, kw.get("blk"), 1 if kw.get("blk") else 0, kw.get("bias"),
+                               1 if kw.get("bias") else 0, 8 if kw.get("bias") else 0, kw.get("kr"), addr)
+    assert fwd(lib, mask=al(4096 + 2)) == INVAL
+    assert fwd(lib, mask=al(4096), S_q=0, q=None, o=None, lse=None) == OK
+    assert fwd(lib, mask=al(4096, blk=4096)) == UNSUP
+    assert fwd(lib, mask=al(4096, bias=4096)) == UNSUP
+    assert fwd(lib, mask=al(4096, kr=4096)) == UNSUP
+    assert fwd(lib, mask=al(4096, bias=4096), dt=0, S_q=0, q=None, o=None, lse=None) == OK   # fp32 takes both
+    call = lambda m: lib.attn_bwd(P, P, P, P, P, P, P, P, P, 1, 4, 2, 8, 8, 128, 0.1, 1, m, None, 1, P, 1 << 30,
+                                  None)
+    assert call(al(4096, kr=4096)) == UNSUP
+    assert call(al(4096 + 2)) == INVAL
 
 
 def test_attn_bwd_varlen_rejects_bad_arguments():
