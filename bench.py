@@ -414,6 +414,8 @@ TRACE_ROWS = [
      ("prefill_bf16_kernel<128, false, false, false, false, false, false, true, false>", 1), None, None),
     ("key ranges: backward dQ pass (documents)", "bwd_dq_kernel<128, false, false, true, false>", None, None),
     ("key ranges: backward dK/dV pass (documents)", "bwd_dkdv_kernel<128, true, false, false, true, false>", None, None),
+    ("key ranges: the documents as packed sequences (varlen d=128)",
+     "prefill_bf16_kernel<128, true, false, false, false, false, false, false, false>", None, None),
     ("ALiBi causal prefill", "prefill_bf16_kernel<128, false, false, false, false, false, false, false, true>",
      None, "mha"),
     ("ALiBi backward dQ pass", "bwd_dq_kernel<128, false, false, false, true>", None, None),
@@ -1205,6 +1207,18 @@ def bench_key_range(w, steps: int, warmup: int, doc_term_ms: float) -> dict:
                                               key_range=kr, stream=stream), steps, warmup, stream)
     tf_bwd = 2.5 * flops_doc / (ms_bwd.mean() * 1e-3) / 1e12
     del do, dq, dk, dv, ws
+    # the same documents as packed sequences (each document of each batch row
+    # its own sequence; q, k, v copied into the packed [A, T, d] layout
+    # outside the timed region)
+    lens = np.concatenate([np.bincount(gen.document_ids(S, 1011, b)) for b in range(B)])
+    lens = lens[lens > 0]
+    cu_host = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    qp, kp, vp = (x.permute(1, 0, 2, 3).reshape(A, B * S, d).contiguous() for x in (q, k, v))
+    op, lp = torch.empty_like(qp), torch.empty((A, B * S), dtype=torch.float32, device="cuda")
+    cu = torch.from_numpy(cu_host).cuda()
+    ms_pk = _event_times(lambda: ea.attn_fwd_varlen(qp, kp, vp, op, lp, cu, cu_host, scale=p2.scale, causal=True,
+                                                    stream=stream), steps, warmup, stream)
+    del qp, kp, vp, op, lp
     P = 512
     pre_np = gen.make_key_ranges(B, S, S, "prefix", 0, prefix=P)
     kept_pre = int((np.maximum(i, P - 1) + 1).sum()) * B
@@ -1221,6 +1235,10 @@ def bench_key_range(w, steps: int, warmup: int, doc_term_ms: float) -> dict:
             "backward": {"value": round(tf_bwd, 2), "unit": "TFLOP/s (2.5x the kept-pair forward FLOPs)",
                          "frac_of_bf16_peak": round(tf_bwd / PEAK_BF16_TFLOPS, 4),
                          "avg_ms": round(float(ms_bwd.mean()), 5)},
+            "as_packed_sequences": {"value": round(flops_doc / (ms_pk.mean() * 1e-3) / 1e12, 2),
+                                    "unit": "TFLOP/s (kept pairs)", "avg_ms": round(float(ms_pk.mean()), 5),
+                                    "sequences": int(lens.size),
+                                    "workload": "the same documents through attn_fwd_varlen, one sequence each"},
             "prefix_lm": {"value": round(tf_pre, 2), "unit": "TFLOP/s (kept pairs)",
                           "frac_of_bf16_peak": round(tf_pre / PEAK_BF16_TFLOPS, 4),
                           "avg_ms": round(float(ms_pre.mean()), 5), "kept_pairs": kept_pre,
