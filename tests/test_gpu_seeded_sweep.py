@@ -247,3 +247,60 @@ def test_sweep_backward(ea, orc, seed):
     out = {n: gu.check_grad(gu.host_f64(g), r, f"backward {seed} {n}")
            for n, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), refs)}
     _say(out)
+
+
+def _rule_cases(n, seed):
+    """Seeded configurations of the two computed mask rules: per-row key
+    ranges (with windows, keep masks and block masks) and ALiBi (with windows
+    and keep masks)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        d = int(rng.choice([64, 128]))
+        A_kv = int(rng.choice([1, 2]))
+        A = A_kv * int(rng.choice([1, 2, 4]))
+        S_q = int(rng.integers(1, 600))
+        S_k = int(rng.integers(1, 600))
+        causal = bool(rng.random() < 0.6)
+        window = None
+        if rng.random() < 0.3:
+            window = (int(rng.choice([-1, rng.integers(0, 250)])), int(rng.choice([-1, rng.integers(0, 250)])))
+        keeps = bool(rng.random() < 0.3)
+        rule = "alibi" if c % 2 else str(rng.choice(["document", "prefix", "random"]))
+        blocks = rule != "alibi" and bool(rng.random() < 0.3)
+        out.append((c, int(rng.integers(1, 3)), A, A_kv, S_q, S_k, d, causal, window, keeps, rule, blocks))
+    return out
+
+
+@pytest.mark.parametrize("case", _rule_cases(16, 2026), ids=lambda c: f"rule{c[0]}{c[10]}")
+def test_sweep_key_ranges_and_alibi(ea, orc, case):
+    _, B, A, A_kv, S_q, S_k, d, causal, window, keeps, rule, blocks = case
+    _say("sweep rules", case)
+    t = gu.torch()
+    seed = 5000 + case[0]
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=causal, seed=seed,
+                       q_masked=S_q // 9 if keeps else 0, k_masked=S_k // 7 if keeps else 0)
+    kr = slopes = bk = None
+    if rule == "alibi":
+        slopes = (2.0 ** -np.arange(1, A + 1, dtype=np.float64) * 4.0).astype(np.float32)
+    else:
+        kr = gen.make_key_ranges(B, S_q, S_k, rule, seed, doc_median=60, prefix=S_k // 3)
+    if blocks:
+        bk = (np.random.default_rng(seed).random((B, A, (S_q + 127) // 128, (S_k + 127) // 128)) < 0.7).astype(np.uint8)
+    q, k, v = gu.dev(p.q, "bf16"), gu.dev(p.k, "bf16"), gu.dev(p.v, "bf16")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((B, A, S_q), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=causal, window=window,
+                q_keep=gu.dev(p.q_keep, "u8") if keeps else None, k_keep=gu.dev(p.k_keep, "u8") if keeps else None,
+                key_range=None if kr is None else gu.dev(kr, "i32"),
+                alibi_slopes=None if slopes is None else gu.dev(slopes, "f32"),
+                block_keep=None if bk is None else t.from_numpy(bk).cuda())
+    t.cuda.synchronize()
+    mk = None
+    if window is not None:
+        mk = oracle.window_keep(B, S_q, S_k, window[0], 0 if causal else window[1])
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal,
+                                q_keep=p.q_keep if keeps else None, k_keep=p.k_keep if keeps else None, m_keep=mk,
+                                key_range=kr, alibi_slopes=slopes, block_keep=bk)
+    _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"rules {case}"))
