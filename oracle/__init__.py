@@ -542,7 +542,7 @@ class Oracle:
                                   causal=causal, window=window, rows=rows, key_range=key_range)
 
     def decode_paged_fp8(self, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, *, scale,
-                         seqs=None, window_left=None):
+                         seqs=None, window_left=None, alibi_slopes=None):
         """Paged decode over FP8 caches (E4M3 codes [P, page_size, A_kv, d] with
         per-(page, KV head) scales [P, A_kv]); q bf16 bits [B, A, d].  The cache
         values code value * scale are formed in fp64 for the pages each sequence
@@ -564,15 +564,21 @@ class Oracle:
             vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale, np.float64)[pages][:, None, :, None]
             o, lse = self.decode_paged(qf[b:b + 1], kc, vc, np.arange(pages.size, dtype=np.int32)[None],
                                        np.array([sl[b]], np.int32), dtype="f64", scale=scale,
-                                       window_left=window_left)
+                                       window_left=window_left, alibi_slopes=alibi_slopes)
             outs.append(o.reshape(A, d))
             lses.append(lse.reshape(A))
         return np.stack(outs), np.stack(lses)
 
-    def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None, window_left=None):
+    def decode_paged(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows=None, window_left=None,
+                     alibi_slopes=None):
         """Paged decode.  q [B,A,d]; caches [P, page_size, A_kv, d]; rows = b*A + h.
         window_left: the query (position seq_lens[b] - 1) sees keys t >=
-        seq_lens[b] - 1 - window_left; None = every key."""
+        seq_lens[b] - 1 - window_left; None = every key.  alibi_slopes: [A]; the
+        decode row is then the one-row chunk of each sequence in prefill_paged
+        (the query at position seq_lens[b] - 1)."""
+        if alibi_slopes is not None:
+            return self._decode_as_chunks(q, k_cache, v_cache, block_table, seq_lens, dtype=dtype, scale=scale,
+                                          rows=rows, window_left=window_left, alibi_slopes=alibi_slopes)
         q, kc, vc = self._arr(q, dtype), self._arr(k_cache, dtype), self._arr(v_cache, dtype)
         if q.ndim != 3 or kc.ndim != 4 or kc.shape != vc.shape:
             raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
@@ -596,6 +602,27 @@ class Oracle:
             raise ValueError("oracle_decode_paged rejected its arguments")
         if r is None:
             return o.reshape(B, A, d), lse.reshape(B, A)
+        return o, lse
+
+
+    def _decode_as_chunks(self, q, k_cache, v_cache, block_table, seq_lens, *, dtype, scale, rows, window_left,
+                          alibi_slopes):
+        B, A, d = np.asarray(q).shape
+        sl = np.asarray(seq_lens, dtype=np.int32)
+        live = sl > 0
+        cu = np.concatenate([[0], np.cumsum(live.astype(np.int32))]).astype(np.int32)
+        qc = np.ascontiguousarray(np.asarray(q)[live].transpose(1, 0, 2))   # [A, chunk rows, d]
+        window = None if window_left is None else (int(window_left), 0)
+        o = np.zeros((B, A, d), np.float64)
+        lse = np.full((B, A), -np.inf, np.float64)
+        if qc.shape[1]:
+            oc, lc = self.prefill_paged(qc, k_cache, v_cache, block_table, sl, cu, dtype=dtype, scale=scale,
+                                        causal=True, window=window, alibi_slopes=alibi_slopes)
+            o[live] = oc.transpose(1, 0, 2)
+            lse[live] = lc.T
+        if rows is not None:
+            r = np.asarray(rows, np.int64).reshape(-1)
+            return o.reshape(B * A, d)[r], lse.reshape(-1)[r]
         return o, lse
 
 

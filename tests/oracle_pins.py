@@ -848,6 +848,49 @@ def pin_bwd_alibi_finite_differences(orc):
             assert np.array_equal(x[:, s0:s1], y[0])
 
 
+def pin_decode_alibi_is_last_dense_row(orc):
+    """Paged decode with ALiBi (and with a window) = the last row of the
+    dense causal prefill with ALiBi over the sequence's keys gathered token by
+    token; an empty sequence is a fully masked row; the FP8-cache decode
+    takes the same slopes."""
+    rng = np.random.default_rng(86)
+    lens, A, A_kv, d, ps = [40, 0, 17, 33], 4, 2, 4, 16
+    slopes = np.array([0.5, 0.25, 1.0, 0.0])
+    q, kc, vc, bt, sl, _ = _paged_problem(lens, [0] * len(lens), A, A_kv, d, ps, 87)
+    qd = _f32(rng.standard_normal((len(lens), A, d)))
+    for wl in (None, 5):
+        o, lse = orc.decode_paged(qd, kc, vc, bt, sl, dtype="f32", scale=0.5, alibi_slopes=slopes, window_left=wl)
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+                continue
+            kk = _contiguous(kc, bt[b], L, ps)[None]
+            vv = _contiguous(vc, bt[b], L, ps)[None]
+            qq = np.zeros((1, A, L, d), np.float32)
+            qq[0, :, L - 1] = qd[b]
+            mk = None if wl is None else oracle_window(L, wl)
+            o2, l2 = orc.attn_fwd(qq, kk, vv, dtype="f32", scale=0.5, causal=True, alibi_slopes=slopes, m_keep=mk)
+            assert np.allclose(o[b], o2[0, :, L - 1], rtol=0, atol=1e-12), (b, wl)
+            assert np.allclose(lse[b], l2[0, :, L - 1], rtol=0, atol=1e-12), (b, wl)
+    # FP8 caches: the same decode over the dequantised pages
+    import oracle as oracle_pkg
+    codes = lambda shape: (rng.integers(0, 0x7E, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+    k8, v8 = codes(kc.shape), codes(vc.shape)
+    ks, vs = rng.uniform(0.01, 0.1, kc.shape[::2]), rng.uniform(0.01, 0.1, kc.shape[::2])
+    qb = gen.f32_to_bf16_bits(qd)
+    o8, l8 = orc.decode_paged_fp8(qb, k8, v8, ks, vs, bt, sl, scale=0.5, alibi_slopes=slopes)
+    kd = oracle_pkg.fp8_e4m3_value(k8) * ks[:, None, :, None]
+    vd = oracle_pkg.fp8_e4m3_value(v8) * vs[:, None, :, None]
+    qf = gen.bf16_bits_to_f32(qb).astype(np.float64)
+    o9, l9 = orc.decode_paged(qf, kd, vd, bt, sl, dtype="f64", scale=0.5, alibi_slopes=slopes)
+    assert np.allclose(o8, o9, rtol=0, atol=1e-12) and np.allclose(l8[np.isfinite(l9)], l9[np.isfinite(l9)], atol=1e-12)
+
+
+def oracle_window(L, wl):
+    import oracle as oracle_pkg
+    return oracle_pkg.window_keep(1, L, L, wl, 0)
+
+
 # ---- FP8 (OCP E4M3) caches: code values, and decode over dequantised pages
 
 def pin_fp8_e4m3_published_values(orc):

@@ -99,7 +99,8 @@ PY_MUTANTS = [
     ("FP8 prefill: 64-token query scale blocks", "np.repeat(qs, 128, axis=2)", "np.repeat(qs, 64, axis=2)", 0),
     ("FP8 prefill: key scales ignored", "kv = fp8_e4m3_value(kc) * np.repeat(ks, 128, axis=2)[:, :, :S_k, None]",
      "kv = fp8_e4m3_value(kc) * 1.0", 0),
-    ("FP8 decode: window ignored", "window_left=window_left)", "window_left=None)", 0),
+    ("FP8 decode: window ignored", "window_left=window_left, alibi_slopes=alibi_slopes)",
+     "window_left=None, alibi_slopes=alibi_slopes)", 0),
     ("FP8 decode: value scale of the key", "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(v_scale",
      "vc = fp8_e4m3_value(v_codes[pages]) * np.asarray(k_scale", 0),
     ("FP8 paged prefill: value scale of the key", "vc = fp8_e4m3_value(v_codes) * np.asarray(v_scale",
@@ -144,6 +145,11 @@ PY_MUTANTS = [
      "m = -sl[:1, None, None] * dist[None]", 0),
     ("ALiBi ignored in packed and paged calls", 'kw["alibi_slopes"] = alibi_slopes', 'kw["alibi_slopes"] = None', 0),
     ("ALiBi ignored", "return a if bias is None else", "return bias if bias is None else", 0),
+    ("decode ALiBi: window dropped", "window = None if window_left is None else (int(window_left), 0)",
+     "window = None", 0),
+    ("decode ALiBi: sequences' rows shifted", "o[live] = oc.transpose(1, 0, 2)", "o[live] = oc.transpose(1, 0, 2)[::-1]", 0),
+    ("FP8 decode: ALiBi ignored", "window_left=window_left, alibi_slopes=alibi_slopes)",
+     "window_left=window_left, alibi_slopes=None)", 0),
     ("varlen block mask transposed", 'kw["block_keep"] = block_keep[s][None, :, :nbs, :nbs]',
      'kw["block_keep"] = np.ascontiguousarray(block_keep[s][None, :, :nbs, :nbs].transpose(0, 1, 3, 2))', 0),
 ]
