@@ -378,9 +378,10 @@ def _trace_work():
 
 
 # (label, kernel pattern, workgroups or None, key of _trace_work() or None).  A
-# pattern (name, part) names a kernel and grid that two legs share: their
-# dispatches split at the largest gap in dispatch order (the legs run one
-# after the other), part 0 the earlier leg, 1 the later.
+# pattern (name, part) names a kernel and grid that several legs share (as many
+# as TRACE_PARTS gives, else two): their dispatches split at the largest gaps
+# in dispatch order (the legs run one after the other), part 0 the earliest.
+TRACE_PARTS = {"decode_split_kernel<128, 1, false, 1, 4>": 3}
 TRACE_ROWS = [
     ("MHA causal prefill B=4 A=32 S=2048 d=128 (headline)", DENSE, 2048, "mha"),
     ("GQA causal prefill B=1 A=32 A_kv=8 S=16384 d=128", DENSE, 4096, "gqa"),
@@ -389,8 +390,10 @@ TRACE_ROWS = [
      None, "varlen"),
     ("paged decode split, bf16 cache (KV bytes / split time)", ("decode_split_kernel<128, 1, false, 1, 4>", 0), None,
      "decode"),
+    ("paged decode split with ALiBi (KV bytes / split time)", ("decode_split_kernel<128, 1, false, 1, 4>", 1), None,
+     "decode"),
     ("paged decode split, 4096-token window (visible KV bytes / split time)",
-     ("decode_split_kernel<128, 1, false, 1, 4>", 1), None, "decode_window"),
+     ("decode_split_kernel<128, 1, false, 1, 4>", 2), None, "decode_window"),
     ("paged decode LSE merge (all decode legs)", "decode_merge_kernel<128>", None, None),
     ("paged decode split, FP8 cache (KV bytes / split time)", "decode_split_kernel<128, 2, true, 1, 4>", None,
      "decode_fp8"),
@@ -450,14 +453,19 @@ def trace_summary(d: str):
     print("|---|---|---|---|---|---|---|---|")
     works = _trace_work()
     for label, pat, wgs, wkey in TRACE_ROWS:
-        part = None
+        part, nparts = None, 2
         if isinstance(pat, tuple):
-            pat, part = pat
+            pat, part = pat[0], pat[1]
+        if isinstance(TRACE_PARTS.get(pat), int):
+            nparts = TRACE_PARTS[pat]
         sel = sorted((i, g, t) for k, g, t, i in disp if grid_matches(k, g, pat, wgs))
         if part is not None and len(sel) > 1:
-            gaps = [sel[j + 1][0] - sel[j][0] for j in range(len(sel) - 1)]
-            cut = gaps.index(max(gaps)) + 1
-            sel = sel[:cut] if part == 0 else sel[cut:]
+            # the legs run one after the other: cut at the nparts - 1 largest
+            # gaps in dispatch order
+            gaps = sorted(range(len(sel) - 1), key=lambda j: sel[j + 1][0] - sel[j][0], reverse=True)
+            cuts = sorted(j + 1 for j in gaps[:nparts - 1])
+            bounds = [0] + cuts + [len(sel)]
+            sel = sel[bounds[part]:bounds[part + 1]] if part + 1 < len(bounds) else []
         ts = sorted(t for _, _, t in sel)
         if not ts:
             continue
@@ -1268,6 +1276,20 @@ def bench_alibi(w, steps: int, warmup: int, term_ms: float, plain_bwd_ms: float)
     ms_b = _event_times(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p2.scale, causal=True,
                                             alibi_slopes=slopes, stream=stream), steps, warmup, stream)
     tf_b = 2.5 * flops / (ms_b.mean() * 1e-3) / 1e12
+    del do, dq, dk, dv, ws
+    # the paged decode workload with the same slopes
+    p4 = w["p4"]
+    kc, vc, bt, sl = w["dev4"]
+    q4 = to_dev(p4.q, "bf16")
+    o4 = torch.empty_like(q4)
+    lse4 = torch.empty((p4.B, p4.A), dtype=torch.float32, device="cuda")
+    nb = ea.attn_decode_paged_workspace_bytes(p4.B, p4.A, p4.A_kv, p4.d, p4.page_size, p4.seq_lens)
+    ws4 = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    ms_d = _event_times(lambda: ea.attn_decode_paged_alibi(q4, kc, vc, bt, sl, p4.seq_lens, o4, lse4, ws4,
+                                                           scale=p4.scale, alibi_slopes=slopes, stream=stream),
+                        steps, warmup, stream)
+    kvb = p4.kv_bytes()
+    gbs = kvb / (ms_d.mean() * 1e-3) / 1e9
     return {"metric": "ALiBi causal prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(float(ms.mean()), 5),
             "median_ms": round(float(np.median(ms)), 5), "flops": flops,
@@ -1277,7 +1299,11 @@ def bench_alibi(w, steps: int, warmup: int, term_ms: float, plain_bwd_ms: float)
             "backward": {"value": round(tf_b, 2), "unit": "TFLOP/s (2.5x the forward FLOPs)",
                          "frac_of_bf16_peak": round(tf_b / PEAK_BF16_TFLOPS, 4),
                          "avg_ms": round(float(ms_b.mean()), 5),
-                         "plain_backward_avg_ms": plain_bwd_ms}}
+                         "plain_backward_avg_ms": plain_bwd_ms},
+            "decode": {"value": round(gbs, 1), "unit": "GB/s of KV", "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBPS, 4),
+                       "avg_ms": round(float(ms_d.mean()), 5),
+                       "workload": "the paged decode workload (64 seqs, A=32 A_kv=8 d=128 page 16) with the same "
+                                   "slopes (attn_decode_paged_alibi, split + merge)"}}
 
 
 PAGED_CHUNK = 256

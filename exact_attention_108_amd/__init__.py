@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     attn_decode_paged,
     attn_decode_paged_fp8,
     attn_decode_paged_fp8_window,
+    attn_decode_paged_alibi,
+    attn_decode_paged_fp8_alibi,
     attn_decode_paged_noalloc,
     attn_decode_paged_window,
     DECODE_NOALLOC_MAX_BYTES,

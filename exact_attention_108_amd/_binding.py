@@ -49,6 +49,9 @@ _lib.attn_decode_paged.restype = _i
 _lib.attn_decode_paged_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                           _i, _i, _vp, _sz, _vp]
 _lib.attn_decode_paged_window.restype = _i
+_lib.attn_decode_paged_alibi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                         _i, _vp, _i, _vp, _sz, _vp]
+_lib.attn_decode_paged_alibi.restype = _i
 _lib.attn_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                                            _i, _vp]
 _lib.attn_decode_paged_noalloc.restype = _i
@@ -75,6 +78,9 @@ _lib.attn_decode_paged_fp8.restype = _i
 _lib.attn_decode_paged_fp8_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
                                               _i, _f, _i, _vp, _sz, _vp]
 _lib.attn_decode_paged_fp8_window.restype = _i
+_lib.attn_decode_paged_fp8_alibi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                                             _i, _f, _i, _vp, _vp, _sz, _vp]
+_lib.attn_decode_paged_fp8_alibi.restype = _i
 _lib.attn_status_string.argtypes = [_i]
 _lib.attn_status_string.restype = ctypes.c_char_p
 _lib.attn_abi_version.argtypes = []
@@ -103,7 +109,7 @@ def exported_symbols():
             "attn_decode_paged_window", "attn_prefill_paged_masked",
             "attn_decode_paged_workspace_bytes",
             "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8", "attn_decode_paged_fp8",
-            "attn_decode_paged_fp8_window",
+            "attn_decode_paged_fp8_window", "attn_decode_paged_alibi", "attn_decode_paged_fp8_alibi",
             "attn_block_keep_from_bias", "attn_status_string", "attn_abi_version"]
 
 
@@ -396,8 +402,16 @@ def attn_decode_paged_window(q, k_cache, v_cache, block_table, seq_lens, seq_len
                  workspace, scale, int(window_left), stream)
 
 
+def attn_decode_paged_alibi(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, workspace, *,
+                            scale: float, alibi_slopes, window_left: int = -1, stream=None):
+    """attn_decode_paged_window with ALiBi: alibi_slopes fp32 [A]; key t of sequence b gets
+    -slope_h (seq_lens[b] - 1 - t) on its score."""
+    _decode_call("attn_decode_paged_alibi", q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse,
+                 workspace, scale, int(window_left), stream, alibi_slopes)
+
+
 def _decode_call(name, q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, o, lse, workspace, scale,
-                 window_left, stream):
+                 window_left, stream, alibi_slopes=None):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
@@ -415,11 +429,15 @@ def _decode_call(name, q, k_cache, v_cache, block_table, seq_lens, seq_lens_host
     if sl.shape != (B,):
         raise ValueError("seq_lens_host must be [B]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace)
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (A,)):
+        raise ValueError(f"alibi_slopes must be fp32 [{A}]")
+    dev = _dev(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, alibi_slopes)
     args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), sl.ctypes.data_as(_vp),
             page_size, _ptr(o), _ptr(lse), B, A, A_kv, d, block_table.shape[1], num_pages, float(scale)]
     if window_left is not None:
         args.append(window_left)
+    if alibi_slopes is not None:
+        args.append(_ptr(alibi_slopes))
     st = getattr(_lib, name)(*args, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream, dev))
     _check(st, name)
 
@@ -676,8 +694,15 @@ def attn_decode_paged_fp8_window(q, k_cache, v_cache, k_scale, v_scale, block_ta
                      scale, int(window_left), stream)
 
 
+def attn_decode_paged_fp8_alibi(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o,
+                                lse, workspace, *, scale: float, alibi_slopes, window_left: int = -1, stream=None):
+    """attn_decode_paged_fp8_window with ALiBi (alibi_slopes fp32 [A], as attn_decode_paged_alibi)."""
+    _fp8_decode_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse, workspace,
+                     scale, int(window_left), stream, alibi_slopes)
+
+
 def _fp8_decode_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, o, lse, workspace,
-                     scale, window_left, stream):
+                     scale, window_left, stream, alibi_slopes=None):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q [B,A,d]; caches [num_pages, page_size, A_kv, d]")
@@ -700,12 +725,17 @@ def _fp8_decode_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_len
     if sl.shape != (B,):
         raise ValueError("seq_lens_host must be [B]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    dev = _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse, workspace)
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (A,)):
+        raise ValueError(f"alibi_slopes must be fp32 [{A}]")
+    dev = _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse, workspace, alibi_slopes)
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
             sl.ctypes.data_as(_vp), page_size, _ptr(o), _ptr(lse), B, A, A_kv, d, block_table.shape[1], num_pages,
             float(scale))
     tail = (_ptr(workspace), ws_bytes, _stream(stream, dev))
-    if window_left is None:
+    if alibi_slopes is not None:
+        _check(_lib.attn_decode_paged_fp8_alibi(*args, window_left, _ptr(alibi_slopes), *tail),
+               "attn_decode_paged_fp8_alibi")
+    elif window_left is None:
         _check(_lib.attn_decode_paged_fp8(*args, *tail), "attn_decode_paged_fp8")
     else:
         _check(_lib.attn_decode_paged_fp8_window(*args, window_left, *tail), "attn_decode_paged_fp8_window")

@@ -329,10 +329,13 @@ attn_status check_decode_call(const void* q, const void* k_cache, const void* v_
 attn_status launch_decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* seq_lens_host, int page_size, void* o,
                                float* lse, int B, int A, int A_kv, int d_h, int max_pages, float scale,
-                               int window_left, void* workspace, void* stream) {
+                               int window_left, void* workspace, void* stream,
+                               const float* alibi_slopes = nullptr) {
   const attn::DecodePlan plan = attn::plan_decode(B, seq_lens_host, window_left);
   attn::DecodeParams p{};
   p.win_left = window_left;
+  p.alibi_slopes = alibi_slopes;
+  p.inv_scale = (float)(1.0 / (double)scale);
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -388,6 +391,24 @@ ATTN_EXPORT attn_status attn_decode_paged_window(const void* q, const void* k_ca
     return ATTN_ERR_INVAL;
   return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
                             A_kv, d_h, max_pages, scale, window_left, workspace, stream);
+}
+
+ATTN_EXPORT attn_status attn_decode_paged_alibi(const void* q, const void* k_cache, const void* v_cache,
+                                                const int32_t* block_table, const int32_t* seq_lens,
+                                                const int32_t* seq_lens_host, int page_size, void* o, float* lse,
+                                                int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                                float scale, int window_left, const float* alibi_slopes,
+                                                attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  if (window_left < -1 || !alibi_slopes || !aligned(alibi_slopes, 4)) return ATTN_ERR_INVAL;
+  size_t need = 0;
+  attn_status st = check_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse,
+                                     B, A, A_kv, d_h, max_pages, num_pages, scale, dtype, need);
+  if (st != ATTN_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_ERR_INVAL;
+  return launch_decode_call(q, k_cache, v_cache, block_table, seq_lens, seq_lens_host, page_size, o, lse, B, A,
+                            A_kv, d_h, max_pages, scale, window_left, workspace, stream, alibi_slopes);
 }
 
 ATTN_EXPORT attn_status attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
@@ -727,7 +748,8 @@ attn_status decode_fp8_call(const void* q, const uint8_t* k_cache, const uint8_t
                             const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* seq_lens_host, int page_size, void* o, float* lse, int B, int A,
                             int A_kv, int d_h, int max_pages, int num_pages, float scale, int window_left,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            const float* alibi_slopes = nullptr) {
   if (max_pages < 0 || num_pages < 0) return ATTN_ERR_INVAL;
   attn_status st = check_decode(B, A, A_kv, d_h, page_size, seq_lens_host, max_pages, true);
   if (st != ATTN_OK) return st;
@@ -748,6 +770,8 @@ attn_status decode_fp8_call(const void* q, const uint8_t* k_cache, const uint8_t
   if ((long long)B * A > INT_MAX) return ATTN_ERR_UNSUPPORTED;
   attn::DecodeParams p{};
   p.win_left = window_left;
+  p.alibi_slopes = alibi_slopes;
+  p.inv_scale = (float)(1.0 / (double)scale);
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -795,6 +819,20 @@ ATTN_EXPORT attn_status attn_decode_paged_fp8_window(const void* q, const uint8_
   return decode_fp8_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, page_size, o,
                          lse, B, A, A_kv, d_h, max_pages, num_pages, scale, window_left, workspace,
                          workspace_bytes, stream);
+}
+
+ATTN_EXPORT attn_status attn_decode_paged_fp8_alibi(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                                    const float* k_scale, const float* v_scale,
+                                                    const int32_t* block_table, const int32_t* seq_lens,
+                                                    const int32_t* seq_lens_host, int page_size, void* o,
+                                                    float* lse, int B, int A, int A_kv, int d_h, int max_pages,
+                                                    int num_pages, float scale, int window_left,
+                                                    const float* alibi_slopes, void* workspace,
+                                                    size_t workspace_bytes, void* stream) {
+  if (window_left < -1 || !alibi_slopes || !aligned(alibi_slopes, 4)) return ATTN_ERR_INVAL;
+  return decode_fp8_call(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, seq_lens_host, page_size, o,
+                         lse, B, A, A_kv, d_h, max_pages, num_pages, scale, window_left, workspace,
+                         workspace_bytes, stream, alibi_slopes);
 }
 
 ATTN_EXPORT const char* attn_status_string(attn_status s) {

@@ -160,6 +160,14 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
   }
   const float cs = p.scale_log2;
   const int tr_r = l16 >> 2, tr_q = l16 & 3;
+  // ALiBi (page "Attention Kernel", section "正确性契约"): each column's slope
+  // over the scale; key t of a sequence of len tokens is len - 1 - t before
+  // the query, and its raw product gets -slope (len - 1 - t) / scale
+  const bool alibi = p.alibi_slopes != nullptr;
+  float ab[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg)
+    ab[cg] = alibi && col_live[cg] ? p.alibi_slopes[kv0 * G + 16 * cg + l16] * p.inv_scale : 0.f;
 
   int k = (int)(c_lo - cex);     // chunk index within sequence b's list
   long long remaining = c_hi - c_lo;
@@ -334,12 +342,14 @@ __global__ __launch_bounds__(64 * WPG) void decode_split_kernel(DecodeParams p) 
       }
       // lane holds tokens c0 + 4 grp + r of column l16 of each group
       bf16x4 pb[NCG];
+      const float dist0 = (float)(len - 1 - c0 - 4 * grp);  // distance of token c0 + 4 grp to the query
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (kFp8) sc[cg][r] *= ksc;
+          if (alibi) sc[cg][r] = fmaf((float)r - dist0, ab[cg], sc[cg][r]);
           if (4 * grp + r >= n_valid || c0 + 4 * grp + r < t_first) sc[cg][r] = -INFINITY;
           mx = fmaxf(mx, sc[cg][r]);
         }

@@ -143,6 +143,10 @@ struct DecodeParams {
   long long n_chunks;  // sum over sequences of decode_chunks(len, win_left)
   int n_wg;            // workgroups along the chunk list (set at launch)
   float scale, scale_log2;
+  // ALiBi: slope per query head [A]; key t of a sequence of len tokens gets
+  // -slope_h (len - 1 - t) (divided by the scale, on the raw product); or null
+  const float* alibi_slopes;
+  float inv_scale;
 };
 
 // upper bound on workgroups along the chunk list; sizes the workspace

@@ -56,7 +56,7 @@
 #include <stdint.h>
 
 /* The value attn_abi_version() returns for this header. */
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 #ifdef __cplusplus
 extern "C" {
@@ -342,6 +342,38 @@ attn_status attn_decode_paged_fp8_window(const void *q, const uint8_t *k_cache, 
                                          int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
                                          float scale, int window_left, void *workspace,
                                          size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_paged_window with ALiBi (page "Attention Kernel", section
+ * "正确性契约" names ALiBi among the transforms fused into the score): key t
+ * of sequence b, len = seq_lens[b] tokens, gets the term
+ * -alibi_slopes[h] * (len - 1 - t) added to scale * q . k_t, the decode row's
+ * part of attn_fwd's ALiBi (the query sits at position len - 1).
+ * alibi_slopes: device fp32 [A], 4-byte aligned, non-NULL (ATTN_ERR_INVAL
+ * otherwise).  window_left as attn_decode_paged_window.  Arguments,
+ * workspace, support and errors as attn_decode_paged_window.
+ */
+attn_status attn_decode_paged_alibi(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens,
+                                    const int32_t *seq_lens_host, int page_size, void *o, float *lse,
+                                    int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                    float scale, int window_left, const float *alibi_slopes,
+                                    attn_dtype dtype, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
+ * attn_decode_paged_fp8_window with ALiBi, defined as for
+ * attn_decode_paged_alibi (the term joins the score after the key scale).
+ * Arguments, workspace, support and errors as attn_decode_paged_fp8_window;
+ * alibi_slopes as attn_decode_paged_alibi.
+ */
+attn_status attn_decode_paged_fp8_alibi(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                        const float *k_scale, const float *v_scale,
+                                        const int32_t *block_table, const int32_t *seq_lens,
+                                        const int32_t *seq_lens_host, int page_size, void *o, float *lse,
+                                        int B, int A, int A_kv, int d_h, int max_pages, int num_pages,
+                                        float scale, int window_left, const float *alibi_slopes,
+                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode_paged without a caller workspace, for callers that cannot

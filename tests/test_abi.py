@@ -24,6 +24,7 @@ def test_header_declares_entry_points():
                                          "attn_decode_paged_workspace_bytes", "attn_bwd", "attn_bwd_varlen",
                                          "attn_bwd_workspace_bytes", "attn_prefill_paged", "attn_prefill_paged_fp8",
                                          "attn_decode_paged_fp8", "attn_decode_paged_fp8_window",
+                                         "attn_decode_paged_alibi", "attn_decode_paged_fp8_alibi",
                                          "attn_block_keep_from_bias", "attn_status_string",
                                          "attn_abi_version"])
 
@@ -42,7 +43,7 @@ def test_library_exports_exactly_the_header():
 
 def test_status_strings_and_version():
     import exact_attention_108_amd as ea
-    assert ea.attn_abi_version() == 7
+    assert ea.attn_abi_version() == 8
     assert ea.attn_status_string(0) == "ok"
     assert ea.attn_status_string(1) == "invalid argument"
     assert ea.attn_status_string(2) == "unsupported configuration"
@@ -560,6 +561,29 @@ def test_decode_fp8_window_rejects_bad_arguments():
     assert call(3, q=ctypes.c_void_p(4096 + 8)) == INVAL
     assert call(3, ks=ctypes.c_void_p(4096 + 2)) == INVAL
     assert call(3, A_kv=3) == INVAL                 # A % A_kv
+
+
+def test_decode_alibi_rejects_bad_arguments():
+    """attn_decode_paged_alibi and attn_decode_paged_fp8_alibi: slopes
+    non-NULL and 4-byte aligned, window_left >= -1, and otherwise the checks of
+    the window forms (host-side, before any device call)."""
+    lib = _lib()
+    INVAL = 1
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_decode_paged_alibi.argtypes = [vp] * 6 + [i, vp, vp] + [i] * 6 + [f, i, vp, i, vp, sz, vp]
+    lib.attn_decode_paged_fp8_alibi.argtypes = [vp] * 8 + [i, vp, vp] + [i] * 6 + [f, i, vp, vp, sz, vp]
+    lens = np.array([10, 40], np.int32)
+    lp = lens.ctypes.data_as(ctypes.c_void_p)
+    bf = lambda wl, sl, q=P: lib.attn_decode_paged_alibi(q, P, P, P, P, lp, 16, P, P, 2, 8, 2, 128, 3, 6, 0.1, wl, sl,
+                                                          1, P, 1 << 30, None)
+    f8 = lambda wl, sl, kc=P: lib.attn_decode_paged_fp8_alibi(P, kc, P, P, P, P, P, lp, 16, P, P, 2, 8, 2, 128, 3,
+                                                              6, 0.1, wl, sl, P, 1 << 30, None)
+    for call in (bf, f8):
+        assert call(-1, None) == INVAL                     # slopes required
+        assert call(-1, ctypes.c_void_p(4096 + 2)) == INVAL
+        assert call(-2, P) == INVAL
+    assert bf(-1, P, q=ctypes.c_void_p(4096 + 8)) == INVAL
+    assert f8(-1, P, kc=ctypes.c_void_p(4096 + 4)) == INVAL
 
 
 def test_prefill_paged_masked_rejects_bad_arguments():

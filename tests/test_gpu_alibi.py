@@ -227,3 +227,90 @@ def test_bwd_varlen_alibi(ea, orc, d):
     ref = orc.attn_bwd_varlen(p.q, p.k, p.v, dout, p.cu_seqlens, dtype="bf16", scale=p.scale, causal=True,
                               alibi_slopes=sl)
     _say({n: gu.check_grad(g, r, f"varlen alibi {n}") for n, g, r in zip(("dq", "dk", "dv"), got, ref)})
+
+
+# ---- paged decode
+
+DECODE_CASES = [
+    # lens, A, A_kv, d, page_size, window_left
+    ([1, 15, 17, 33, 0, 500, 1000], 8, 2, 128, 16, None),
+    ([64, 3000], 4, 4, 128, 16, 700),
+    ([5, 77, 1025], 16, 1, 64, 32, None),
+    ([700, 3, 2049], 32, 1, 128, 16, 100),     # MQA: two column groups
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{len(c[0])}seq-A{c[1]}-kv{c[2]}-d{c[3]}-w{c[5]}")
+def test_decode_alibi(ea, orc, case):
+    t = gu.torch()
+    lens, A, A_kv, d, ps, wl = case
+    _say("decode alibi", case)
+    p = gen.make_paged(lens, A, A_kv, d, ps, seed=3900 + sum(lens), extra_pages=2)
+    sl_np = slopes_of(A)
+    q, kc, vc = gu.dev(p.q, "bf16"), gu.dev(p.k_cache, "bf16"), gu.dev(p.v_cache, "bf16")
+    bt, sl = gu.dev(p.block_table, "i32"), gu.dev(p.seq_lens, "i32")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    ws = t.empty(max(ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens), 1),
+                 dtype=t.uint8, device="cuda")
+    ws.fill_(0xFF)
+    ea.attn_decode_paged_alibi(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale,
+                               alibi_slopes=gu.dev(sl_np, "f32"), window_left=-1 if wl is None else wl)
+    t.cuda.synchronize()
+    o_ref, l_ref = orc.decode_paged(p.q, p.k_cache, p.v_cache, p.block_table, p.seq_lens, dtype="bf16",
+                                    scale=p.scale, window_left=wl, alibi_slopes=sl_np)
+    _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"decode {case}"))
+
+
+@pytest.mark.parametrize("wl", [None, 300])
+def test_decode_fp8_alibi(ea, orc, wl):
+    t = gu.torch()
+    lens, A, A_kv, d, ps = [1, 33, 500, 1000, 0], 8, 2, 128, 16
+    _say("decode fp8 alibi", lens, wl)
+    pf = gen.make_paged_fp8(lens, A, A_kv, d, ps, seed=3950, extra_pages=2)
+    p = pf.base
+    sl_np = slopes_of(A)
+    q = gu.dev(p.q, "bf16")
+    kc, vc = t.from_numpy(pf.k_codes).cuda(), t.from_numpy(pf.v_codes).cuda()
+    ks, vs = t.from_numpy(pf.k_scale).cuda(), t.from_numpy(pf.v_scale).cuda()
+    bt, sl = gu.dev(p.block_table, "i32"), gu.dev(p.seq_lens, "i32")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A), dtype=t.float32, device="cuda")
+    ws = t.empty(max(ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens), 1),
+                 dtype=t.uint8, device="cuda")
+    ea.attn_decode_paged_fp8_alibi(q, kc, vc, ks, vs, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale,
+                                   alibi_slopes=gu.dev(sl_np, "f32"), window_left=-1 if wl is None else wl)
+    t.cuda.synchronize()
+    o_ref, l_ref = orc.decode_paged_fp8(p.q, pf.k_codes, pf.v_codes, pf.k_scale, pf.v_scale, p.block_table,
+                                        p.seq_lens, scale=p.scale, window_left=wl, alibi_slopes=sl_np)
+    _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", "decode fp8 alibi"))
+
+
+def test_decode_alibi_is_the_prefill_last_row(ea):
+    """A sequence's decode with ALiBi equals the last row of the paged
+    prefill of that sequence with the same slopes (both on the GPU; within
+    the bf16 tolerance, the two kernels accumulate in different orders)."""
+    t = gu.torch()
+    lens, A, A_kv, d, ps = [300, 1000], 8, 2, 128, 16
+    _say("decode alibi vs prefill last row", lens)
+    p = gen.make_paged(lens, A, A_kv, d, ps, seed=3960)
+    sl_np = slopes_of(A)
+    q, kc, vc = gu.dev(p.q, "bf16"), gu.dev(p.k_cache, "bf16"), gu.dev(p.v_cache, "bf16")
+    bt, sl = gu.dev(p.block_table, "i32"), gu.dev(p.seq_lens, "i32")
+    sld = gu.dev(sl_np, "f32")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A), dtype=t.float32, device="cuda")
+    ws = t.empty(ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens),
+                 dtype=t.uint8, device="cuda")
+    ea.attn_decode_paged_alibi(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale, alibi_slopes=sld)
+    cu_np = np.arange(p.B + 1, dtype=np.int32)
+    qc = q.permute(1, 0, 2).contiguous()   # [A, B one-row chunks, d]
+    oc = t.empty_like(qc)
+    lc = t.empty((A, p.B), dtype=t.float32, device="cuda")
+    ea.attn_prefill_paged_masked(qc, kc, vc, bt, sl, p.seq_lens, gu.dev(cu_np, "i32"), cu_np, oc, lc, scale=p.scale,
+                                 causal=True, alibi_slopes=sld)
+    t.cuda.synchronize()
+    a = gu.host_f64(o)
+    b = gu.host_f64(oc).transpose(1, 0, 2)
+    assert np.max(np.abs(a - b)) <= 2e-2 and np.max(np.abs(lse.cpu().numpy() - lc.cpu().numpy().T)) <= 1e-3
