@@ -139,8 +139,9 @@ using Slot = std::integral_constant<int, N>;
 // ---------------------------------------------------------------- dQ
 // kVarlen: packed sequences (see BwdParams); kMasks: the block mask, the
 // dense additive term and the per-row key ranges (each runtime-optional);
-// kRange (without kMasks): per-row key ranges alone, at two waves per SIMD.  Two waves per
-// SIMD, one for the masked form at d = 128 (at two its term loads spill).
+// kRange (without kMasks): per-row key ranges alone; kAlibi: ALiBi.  Two
+// waves per SIMD, one for the masked form at d = 128 (at two its term loads
+// spill).
 template <int D, bool kMasks>
 constexpr int kDqWavesPerSimd = (D == 128 && kMasks) ? 1 : 2;
 
