@@ -142,7 +142,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * scale * q_i . k_j, like bias), with p_i query i's bottom-right aligned
  * position (i + S_k - S_q; packed calls: within the sequence; paged chunks:
  * seq_lens[s] - q_len + i over cache positions j).  Computed in the kernels
- * (no term is read).  attn_fwd, attn_fwd_varlen, attn_prefill_paged_masked,
+ * (no term is read); bf16 calls form the distance in fp32, exact below 2^24
+ * and rounded to fp32 (relative 2^-24) beyond.  attn_fwd, attn_fwd_varlen, attn_prefill_paged_masked,
  * attn_bwd and attn_bwd_varlen take it; in bf16 calls it combines with the
  * causal flag, windows and keep-masks but not with block masks, bias or
  * key_range (ATTN_ERR_UNSUPPORTED), nor with attn_fwd_fp8.  4-byte aligned. */
@@ -348,7 +349,8 @@ attn_status attn_decode_paged_fp8_window(const void *q, const uint8_t *k_cache, 
  * "正确性契约" names ALiBi among the transforms fused into the score): key t
  * of sequence b, len = seq_lens[b] tokens, gets the term
  * -alibi_slopes[h] * (len - 1 - t) added to scale * q . k_t, the decode row's
- * part of attn_fwd's ALiBi (the query sits at position len - 1).
+ * part of attn_fwd's ALiBi (the query sits at position len - 1).  The
+ * distance is formed in fp32: exact below 2^24, rounded to fp32 beyond.
  * alibi_slopes: device fp32 [A], 4-byte aligned, non-NULL (ATTN_ERR_INVAL
  * otherwise).  window_left as attn_decode_paged_window.  Arguments,
  * workspace, support and errors as attn_decode_paged_window.
