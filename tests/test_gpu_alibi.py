@@ -287,6 +287,35 @@ def test_decode_fp8_alibi(ea, orc, wl):
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", "decode fp8 alibi"))
 
 
+def test_config4_alibi_full_size_sampled(ea, orc):
+    """The decode workload (64 sequences, lengths U[512, 32768], page 16,
+    A = 32, A_kv = 8, d = 128) with the geometric slopes, in the launch
+    configuration the bench times; the oracle takes six sequences (the
+    longest, the shortest and four seeded ones) with their block-table rows."""
+    t = gu.torch()
+    _say("config 4 paged decode with ALiBi (sampled sequences)")
+    p = gen.make_config(4)
+    sl_np = slopes_of(p.A)
+    q, kc, vc = gu.dev(p.q, "bf16"), gu.dev(p.k_cache, "bf16"), gu.dev(p.v_cache, "bf16")
+    bt, sl = gu.dev(p.block_table, "i32"), gu.dev(p.seq_lens, "i32")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((p.B, p.A), dtype=t.float32, device="cuda")
+    o.fill_(float("nan"))
+    ws = t.empty(max(ea.attn_decode_paged_workspace_bytes(p.B, p.A, p.A_kv, p.d, p.page_size, p.seq_lens), 1),
+                 dtype=t.uint8, device="cuda")
+    ea.attn_decode_paged_alibi(q, kc, vc, bt, sl, p.seq_lens, o, lse, ws, scale=p.scale,
+                               alibi_slopes=gu.dev(sl_np, "f32"))
+    t.cuda.synchronize()
+    o_h, l_h = gu.host_f64(o), lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(l_h))
+    rng = np.random.default_rng(3970)
+    seqs = np.unique(np.concatenate([rng.choice(p.B, size=4, replace=False),
+                                     [int(np.argmax(p.seq_lens)), int(np.argmin(p.seq_lens))]]))
+    o_ref, l_ref = orc.decode_paged(p.q[seqs], p.k_cache, p.v_cache, p.block_table[seqs], p.seq_lens[seqs],
+                                    dtype="bf16", scale=p.scale, alibi_slopes=sl_np)
+    _say(gu.check(o_h[seqs], l_h[seqs], o_ref, l_ref, "bf16", "config4 alibi"))
+
+
 def test_decode_alibi_is_the_prefill_last_row(ea):
     """A sequence's decode with ALiBi equals the last row of the paged
     prefill of that sequence with the same slopes (both on the GPU; within
