@@ -205,6 +205,46 @@ def test_bwd_alibi(ea, orc, case):
     _say({n: gu.check_grad(g, r, f"{case} {n}") for n, g, r in zip(("dq", "dk", "dv"), got, ref)})
 
 
+@pytest.mark.parametrize("case", [
+    # B, A, A_kv, S_q, S_k, d, window left (causal, right edge at the diagonal)
+    (1, 4, 2, 320, 320, 128, 100),
+    (2, 2, 2, 300, 200, 64, None),     # rows 0..99 see no key (bottom-right causal)
+], ids=lambda c: f"{c[3]}x{c[4]}d{c[5]}w{c[6]}")
+def test_bwd_alibi_window_keeps(ea, orc, case):
+    """ALiBi beside a causal window and both keep masks, and at S_q > S_k
+    (rows with no visible key): gradients against the oracle."""
+    t = gu.torch()
+    B, A, A_kv, S_q, S_k, d, wl = case
+    _say("bwd alibi with window and keeps", case)
+    seed = 3750 + S_q + S_k + d
+    p = gen.make_dense(B, A, A_kv, S_q, S_k, d, dtype="bf16", causal=True, seed=seed)
+    rng = np.random.default_rng(seed)
+    qk = (rng.random((B, S_q)) > 0.1).astype(np.uint8)
+    kk = (rng.random((B, S_k)) > 0.1).astype(np.uint8)
+    sl = slopes_of(A)
+    dout = gen.make_dout(p, seed)
+    q, k, v, do = (gu.dev(x, "bf16") for x in (p.q, p.k, p.v, dout))
+    sld, qkd, kkd = gu.dev(sl, "f32"), gu.dev(qk, "u8"), gu.dev(kk, "u8")
+    window = None if wl is None else (wl, -1)
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((B, A, S_q), dtype=t.float32, device="cuda")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=True, window=window, q_keep=qkd, k_keep=kkd,
+                alibi_slopes=sld)
+    dq, dk, dv = (gu.empty_out(x.shape, "bf16") for x in (q, k, v))
+    ws = t.empty(max(ea.attn_bwd_workspace_bytes(B, A, S_q), 1), dtype=t.uint8, device="cuda")
+    ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p.scale, causal=True, window=window, q_keep=qkd,
+                k_keep=kkd, alibi_slopes=sld)
+    t.cuda.synchronize()
+    mk = None if wl is None else oracle.window_keep(B, S_q, S_k, wl, 0)
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=True, q_keep=qk, k_keep=kk,
+                                m_keep=mk, alibi_slopes=sl)
+    _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"{case} fwd"))
+    got = (gu.host_f64(dq), gu.host_f64(dk), gu.host_f64(dv))
+    ref = orc.attn_bwd(p.q, p.k, p.v, dout, dtype="bf16", scale=p.scale, causal=True, q_keep=qk, k_keep=kk,
+                       m_keep=mk, alibi_slopes=sl)
+    _say({n: gu.check_grad(g, r, f"{case} {n}") for n, g, r in zip(("dq", "dk", "dv"), got, ref)})
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_bwd_varlen_alibi(ea, orc, d):
     t = gu.torch()
