@@ -286,6 +286,44 @@ def test_bwd_key_ranges(ea, orc, case):
     _say({n: gu.check_grad(g, r, f"{case} {n}") for n, g, r in zip(("dq", "dk", "dv"), got, ref)})
 
 
+@pytest.mark.parametrize("case", [
+    # B, A, A_kv, S, d, causal, window (left, right), kind
+    (1, 4, 2, 320, 128, True, (100, -1), "document"),
+    (2, 2, 1, 290, 64, False, (60, 40), "random"),
+], ids=lambda c: f"{c[3]}d{c[4]}" + ("c" if c[5] else "n") + c[7])
+def test_bwd_key_ranges_with_window_and_keeps(ea, orc, case):
+    """Key ranges beside a window and both keep masks: forward and
+    gradients against the oracle (the window as its keep matrix)."""
+    t = gu.torch()
+    B, A, A_kv, S, d, causal, window, kind = case
+    _say("bwd key ranges + window + keeps", case)
+    seed = 2970 + S + d
+    p = gen.make_dense(B, A, A_kv, S, S, d, dtype="bf16", causal=causal, seed=seed)
+    kr = ranges(B, S, S, kind, seed, doc_median=60)
+    rng = np.random.default_rng(seed)
+    qk = (rng.random((B, S)) > 0.1).astype(np.uint8)
+    kk = (rng.random((B, S)) > 0.1).astype(np.uint8)
+    dout = gen.make_dout(p, seed)
+    q, k, v, do = (gu.dev(x, "bf16") for x in (p.q, p.k, p.v, dout))
+    krd, qkd, kkd = gu.dev(kr, "i32"), gu.dev(qk, "u8"), gu.dev(kk, "u8")
+    o = gu.empty_out(q.shape, "bf16")
+    lse = t.empty((B, A, S), dtype=t.float32, device="cuda")
+    ea.attn_fwd(q, k, v, o, lse, scale=p.scale, causal=causal, window=window, q_keep=qkd, k_keep=kkd, key_range=krd)
+    dq, dk, dv = (gu.empty_out(x.shape, "bf16") for x in (q, k, v))
+    ws = t.empty(max(ea.attn_bwd_workspace_bytes(B, A, S), 1), dtype=t.uint8, device="cuda")
+    ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=p.scale, causal=causal, window=window, q_keep=qkd,
+                k_keep=kkd, key_range=krd)
+    t.cuda.synchronize()
+    mk = oracle.window_keep(B, S, S, window[0], 0 if causal else window[1])
+    o_ref, l_ref = orc.attn_fwd(p.q, p.k, p.v, dtype="bf16", scale=p.scale, causal=causal, q_keep=qk, k_keep=kk,
+                                m_keep=mk, key_range=kr)
+    _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16", f"{case} fwd"))
+    got = (gu.host_f64(dq), gu.host_f64(dk), gu.host_f64(dv))
+    ref = orc.attn_bwd(p.q, p.k, p.v, dout, dtype="bf16", scale=p.scale, causal=causal, q_keep=qk, k_keep=kk,
+                       m_keep=mk, key_range=kr)
+    _say({n: gu.check_grad(g, r, f"{case} {n}") for n, g, r in zip(("dq", "dk", "dv"), got, ref)})
+
+
 def test_bwd_key_ranges_with_block_mask(ea, orc):
     B, A, A_kv, S, d = 1, 4, 2, 400, 128
     _say("bwd key ranges + block mask", B, A, S, d)
