@@ -131,12 +131,12 @@ def test_varlen_alibi(ea, orc, dtype, d, causal):
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, dtype, "varlen alibi"))
 
 
-@pytest.mark.parametrize("d,ps", [(128, 16), (64, 32)])
-def test_paged_prefill_alibi(ea, orc, d, ps):
+@pytest.mark.parametrize("d,ps,window", [(128, 16, None), (64, 32, None), (128, 16, (150, -1))])
+def test_paged_prefill_alibi(ea, orc, d, ps, window):
     t = gu.torch()
     lens = [300, 1, 129, 700, 64, 1000]
     q_lens = [300, 1, 1, 200, 64, 129]
-    _say("paged prefill alibi", d, ps, lens, q_lens)
+    _say("paged prefill alibi", d, ps, window, lens, q_lens)
     pg, q, cu = gen.make_paged_prefill(lens, q_lens, 8, 2, d, ps, seed=3500 + d, extra_pages=2)
     sl = slopes_of(8)
     qd = gu.dev(q, pg.dtype)
@@ -145,12 +145,12 @@ def test_paged_prefill_alibi(ea, orc, d, ps):
     o = gu.empty_out(qd.shape, pg.dtype)
     lse = t.empty((qd.shape[0], qd.shape[1]), dtype=t.float32, device="cuda")
     ea.attn_prefill_paged_masked(qd, kc, vc, bt, sld, pg.seq_lens, cud, cu, o, lse, scale=pg.scale, causal=True,
-                                 alibi_slopes=gu.dev(sl, "f32"))
+                                 window=window, alibi_slopes=gu.dev(sl, "f32"))
     t.cuda.synchronize()
     o_ref, l_ref = orc.prefill_paged(q, pg.k_cache, pg.v_cache, pg.block_table, pg.seq_lens, cu, dtype=pg.dtype,
-                                     scale=pg.scale, causal=True, alibi_slopes=sl)
+                                     scale=pg.scale, causal=True, window=window, alibi_slopes=sl)
     _say(gu.check(gu.host_f64(o)[None], lse.cpu().numpy()[None].astype(np.float64), o_ref[None], l_ref[None],
-                  "bf16", f"paged alibi d={d}"))
+                  "bf16", f"paged alibi d={d} window={window}"))
 
 
 def test_alibi_full_size_sampled(ea, orc):
