@@ -113,21 +113,30 @@ def test_f32_alibi(ea, orc):
         _say(gu.check(o, lse, o_ref, l_ref, "f32", "fp32 alibi"))
 
 
-@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("f32", 64, True)])
-def test_varlen_alibi(ea, orc, dtype, d, causal):
+@pytest.mark.parametrize("dtype,d,causal,keeps", [("bf16", 128, True, False), ("bf16", 64, False, False),
+                                                  ("f32", 64, True, False), ("bf16", 64, True, True)])
+def test_varlen_alibi(ea, orc, dtype, d, causal, keeps):
+    """Packed sequences with ALiBi (positions within each sequence); the
+    last case adds query and key flags (5% and 10% of the tokens dropped)."""
     t = gu.torch()
     lens = [300, 0, 77, 513, 1, 129]
-    _say("varlen alibi", dtype, d, causal, lens)
+    _say("varlen alibi", dtype, d, causal, keeps, lens)
     p = gen.make_varlen(lens, 4, 2, d, dtype=dtype, causal=causal, seed=3400 + d)
     sl = slopes_of(4)
+    qk = kk = None
+    if keeps:
+        rng = np.random.default_rng(3450 + d)
+        qk = (rng.random(p.T) > 0.05).astype(np.uint8)
+        kk = (rng.random(p.T) > 0.10).astype(np.uint8)
     q, k, v = gu.dev(p.q, dtype), gu.dev(p.k, dtype), gu.dev(p.v, dtype)
     cu = gu.dev(p.cu_seqlens, "i32")
     o = gu.empty_out(q.shape, dtype)
     lse = t.empty((p.A, p.T), dtype=t.float32, device="cuda")
-    ea.attn_fwd_varlen(q, k, v, o, lse, cu, p.cu_seqlens, scale=p.scale, causal=causal, alibi_slopes=gu.dev(sl, "f32"))
+    ea.attn_fwd_varlen(q, k, v, o, lse, cu, p.cu_seqlens, scale=p.scale, causal=causal, alibi_slopes=gu.dev(sl, "f32"),
+                       q_keep=None if qk is None else gu.dev(qk, "u8"), k_keep=None if kk is None else gu.dev(kk, "u8"))
     t.cuda.synchronize()
     o_ref, l_ref = orc.attn_fwd_varlen(p.q, p.k, p.v, p.cu_seqlens, dtype=dtype, scale=p.scale, causal=causal,
-                                       alibi_slopes=sl)
+                                       q_keep=qk, k_keep=kk, alibi_slopes=sl)
     _say(gu.check(gu.host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, dtype, "varlen alibi"))
 
 
